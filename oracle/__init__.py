@@ -1,0 +1,10 @@
+"""CPU oracle (test infrastructure only): see ``oracle/lapnys_oracle.py``."""
+
+from .lapnys_oracle import (  # noqa: F401
+    attention_problem,
+    forward,
+    laplacian_kernel,
+    newton_schulz_inverse,
+    pool_landmarks,
+    whiten_columns,
+)

@@ -1,0 +1,409 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each ``pin_*`` function checks the oracle against something that does not come
+from the oracle itself: hand-worked values (tests/golden), closed forms,
+library routines (LU inverse, eigendecomposition, numpy mean/std), brute force
+on tiny inputs, and invariants the mathematics fixes.  ``test_planted_mistakes``
+then plants plausible mistakes in the oracle (on the CPU) and checks that at
+least one pin fails for each, so the pins are known to have teeth.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle.lapnys_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "laplacian_kernel_hand.txt")
+
+
+def _rng(seed=0):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _heavy(rng, shape):
+    return rng.standard_t(3.0, size=shape) * 0.25
+
+
+def _golden_rows():
+    rows = []
+    with open(GOLDEN) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            x, y, lam, dist, _ = [s.strip() for s in line.split(";")]
+            rows.append((np.array([float(t) for t in x.split(",")]),
+                         np.array([float(t) for t in y.split(",")]), float(lam), float(dist)))
+    return rows
+
+
+# ----------------------------------------------------------------------------- pins
+
+
+def pin_kernel_hand(orc):
+    for x, y, lam, dist in _golden_rows():
+        got = orc.laplacian_kernel(x[None, :], y[None, :], lam)[0, 0]
+        want = math.exp(-dist / lam)
+        assert abs(got - want) <= 1e-15 * want, (x, y, lam, got, want)
+
+
+def pin_kernel_invariants(orc):
+    rng = _rng(1)
+    x = _heavy(rng, (9, 6))
+    kxx = orc.laplacian_kernel(x, x, 4.0)
+    assert np.all(np.diag(kxx) == 1.0)
+    assert np.array_equal(kxx, kxx.T)
+    assert np.all(kxx > 0) and np.all(kxx <= 1)
+    # The Laplacian kernel is a product of one-dimensional Laplace kernels, each
+    # positive definite, so its Gram matrix on distinct points is positive definite.
+    assert np.linalg.eigvalsh(kxx).min() > 0
+    y = _heavy(rng, (4, 6))
+    assert np.array_equal(orc.laplacian_kernel(x, y, 4.0), orc.laplacian_kernel(y, x, 4.0).T)
+
+
+def pin_pool_ramp(orc):
+    # K[n, t] = n + 1000 t on a row-major grid: the window mean has a closed form.
+    for gh, gw, p in [(6, 10, 2), (9, 6, 3), (4, 8, 4), (5, 5, 1)]:
+        n = np.arange(gh * gw, dtype=np.float64)
+        d = 3
+        k = n[:, None] + 1000.0 * np.arange(d)[None, :]
+        kt = orc.pool_landmarks(k, gh, gw, p)
+        R, C = np.divmod(np.arange((gh // p) * (gw // p)), gw // p)
+        centre = (R * p + (p - 1) / 2.0) * gw + (C * p + (p - 1) / 2.0)
+        want = centre[:, None] + 1000.0 * np.arange(d)[None, :]
+        assert kt.shape == want.shape
+        assert np.allclose(kt, want, rtol=0, atol=1e-9), (gh, gw, p)
+
+
+def pin_pool_special_cases(orc):
+    rng = _rng(2)
+    k = _heavy(rng, (30, 4))
+    assert np.array_equal(orc.pool_landmarks(k, 5, 6, 1), k)           # pool 1: identity
+    g = _heavy(rng, (36, 4))
+    assert np.allclose(orc.pool_landmarks(g, 6, 6, 6)[0], g.mean(axis=0), rtol=0, atol=1e-15)
+
+
+def pin_pool_fixed_order(orc):
+    # The GPU reproduces the landmarks bit for bit, so the float64 summation order
+    # is part of the definition: window row outer, window column inner.
+    # Values with exponents spread over 2^-40..2^40 make float64 window sums
+    # depend on their order, so a different order shows up as a bit change.
+    rng = _rng(3)
+    gh, gw, p, d = 6, 8, 2, 5
+    mant = rng.uniform(1.0, 2.0, size=(gh * gw, d)) * rng.choice([-1.0, 1.0], size=(gh * gw, d))
+    k = (mant * np.exp2(rng.integers(-40, 41, size=(gh * gw, d)))).astype(np.float32).astype(np.float64)
+    k[0, 0], k[1, 0], k[gw, 0], k[gw + 1, 0] = 2.0 ** 60, 1.0, -(2.0 ** 60), 0.5
+    kt = orc.pool_landmarks(k, gh, gw, p)
+    assert kt[0, 0] == 0.125  # ((2^60 + 1) - 2^60 + 0.5) / 4 in float64
+    for j in range((gh // p) * (gw // p)):
+        R, C = divmod(j, gw // p)
+        for t in range(d):
+            acc = 0.0
+            for r in range(p):
+                for c in range(p):
+                    acc += k[(R * p + r) * gw + (C * p + c), t]
+            assert kt[j, t] == acc / (p * p)
+
+
+def _w_of(rng, m=7, d=4, eps=1e-3):
+    kt = _heavy(rng, (m, d))
+    return O.laplacian_kernel(kt, kt, 4.0) + eps * np.eye(m)
+
+
+def pin_ns_closed_form(orc):
+    # For symmetric W with X0 = W / alpha, the residual squares each step, so
+    # X_T = W^-1 (I - (I - W^2 / alpha)^(2^T)); evaluate it on W's eigenbasis.
+    rng = _rng(4)
+    w = _w_of(rng)
+    alpha = np.linalg.norm(w, 1) * np.linalg.norm(w, np.inf)
+    s, u = np.linalg.eigh(w)
+    for t in [0, 1, 3, 8]:
+        want = (u * ((1.0 - (1.0 - s * s / alpha) ** (2 ** t)) / s)) @ u.T
+        got = orc.newton_schulz_inverse(w, t)
+        assert np.abs(got - want).max() <= 1e-12 * np.abs(want).max(), t
+
+
+def pin_ns_lu(orc):
+    rng = _rng(5)
+    w = _w_of(rng, m=5)
+    got = orc.newton_schulz_inverse(w, 60)
+    want = np.linalg.solve(w, np.eye(5))
+    assert np.abs(got - want).max() <= 1e-12 * np.abs(want).max()
+
+
+def pin_ns_residual_squares(orc):
+    rng = _rng(6)
+    w = _w_of(rng, m=6)
+    prev = None
+    for t in range(6):
+        r = np.linalg.norm(np.eye(6) - w @ orc.newton_schulz_inverse(w, t), 2)
+        if prev is not None:
+            assert abs(r - prev * prev) <= 1e-9 * max(prev * prev, 1e-300) + 1e-15
+        prev = r
+
+
+def pin_whiten_moments(orc):
+    rng = _rng(7)
+    c = np.exp(-np.abs(_heavy(rng, (50, 6))) * 3)
+    z, mu, sigma = orc.whiten_columns(c)
+    assert np.allclose(mu, np.mean(c, axis=0), rtol=1e-14, atol=0)
+    assert np.allclose(sigma, np.std(c, axis=0, ddof=0), rtol=1e-13, atol=0)
+    assert np.abs(z.mean(axis=0)).max() <= 1e-12
+    assert np.abs((z * z).mean(axis=0) - 1.0).max() <= 1e-12
+    c2 = c.copy()
+    c2[:, 2] = 0.25
+    z2, _, s2 = orc.whiten_columns(c2)
+    assert s2[2] == 0 and np.all(z2[:, 2] == 0)
+
+
+def _brute_kernel(x, y, lam):
+    out = np.empty((x.shape[0], y.shape[0]))
+    for i in range(x.shape[0]):
+        for j in range(y.shape[0]):
+            out[i, j] = math.exp(-sum(abs(a - b) for a, b in zip(x[i], y[j])) / lam)
+    return out
+
+
+def pin_nystrom_pool1(orc):
+    # pool = 1 makes every key a landmark.  With an exact inverse the Nystrom
+    # product then equals C - eps C (k(K,K) + eps I)^-1 exactly, and tends to
+    # the brute-force O(N^2) Laplacian attention k(Q, K) V as eps -> 0.
+    rng = _rng(8)
+    gh, gw, d, lam = 4, 4, 3, 4.0
+    q, k, v = (_heavy(rng, (gh * gw, d)) for _ in range(3))
+    g_qk = _brute_kernel(q, k, lam)
+    g_kk = _brute_kernel(k, k, lam)
+    errs = []
+    for eps in [1e-2, 1e-4, 1e-6]:
+        res = orc.attention_problem(q, k, v, grid_h=gh, grid_w=gw, pool=1, lam=lam, eps=eps,
+                                    ns_iters=80, whiten=False)
+        a = g_kk + eps * np.eye(gh * gw)
+        want = (g_qk - eps * g_qk @ np.linalg.solve(a, np.eye(gh * gw))) @ v
+        assert np.abs(res["O"] - want).max() <= 1e-9 * np.abs(want).max(), eps
+        errs.append(np.abs(res["O"] - g_qk @ v).max())
+    assert errs[0] > errs[1] > errs[2]
+    assert errs[2] < 1e-3 * np.abs(g_qk @ v).max()
+
+
+def pin_single_landmark(orc):
+    # pool = whole grid: one landmark (the mean key), W = 1 + eps, X_T = 1/(1+eps),
+    # so O_i = z_i / (1 + eps) * sum_n b_n v_n.
+    rng = _rng(9)
+    g, d, lam, eps = 5, 4, 4.0, 1e-3
+    q, k, v = (_heavy(rng, (g * g, d)) for _ in range(3))
+    res = orc.attention_problem(q, k, v, grid_h=g, grid_w=g, pool=g, lam=lam, eps=eps,
+                                ns_iters=20, whiten=True)
+    kbar = k.mean(axis=0)
+    c = np.array([math.exp(-np.abs(qi - kbar).sum() / lam) for qi in q])
+    b = np.array([math.exp(-np.abs(kbar - kn).sum() / lam) for kn in k])
+    z = (c - c.mean()) / c.std()
+    want = np.outer(z / (1.0 + eps), (b[:, None] * v).sum(axis=0))
+    assert np.abs(res["O"] - want).max() <= 1e-12 * np.abs(want).max()
+
+
+def _problem(orc, q, k, v, **kw):
+    base = dict(grid_h=6, grid_w=6, pool=2, lam=4.0, eps=1e-3, ns_iters=20, whiten=True)
+    base.update(kw)
+    return orc.attention_problem(q, k, v, **base)
+
+
+def pin_metamorphic(orc):
+    rng = _rng(10)
+    q, k, v, v2 = (_heavy(rng, (36, 5)) for _ in range(4))
+    r = _problem(orc, q, k, v)
+    # Linear in V.
+    r2 = _problem(orc, q, k, v2)
+    r3 = _problem(orc, q, k, 2.0 * v - 3.0 * v2)
+    assert np.allclose(r3["O"], 2.0 * r["O"] - 3.0 * r2["O"], rtol=0, atol=1e-12 * np.abs(r["O"]).max())
+    # Permuting the queries permutes the output rows (whitening statistics are
+    # symmetric in the tokens).
+    perm = rng.permutation(36)
+    rp = _problem(orc, q[perm], k, v)
+    assert np.allclose(rp["O"], r["O"][perm], rtol=0, atol=1e-12 * np.abs(r["O"]).max())
+    # (Q, K, lambda) -> (2Q, 2K, 2 lambda) leaves every kernel value bit-identical.
+    rs = _problem(orc, 2 * q, 2 * k, v, lam=8.0)
+    for key in ["C", "B", "W", "X", "O"]:
+        assert np.array_equal(rs[key], r[key]), key
+    assert np.array_equal(rs["landmarks"], 2 * r["landmarks"])
+
+
+def pin_forward_layout(orc):
+    # forward() runs each (b, h) problem independently on its own slice.
+    rng = _rng(11)
+    q, k, v = (_heavy(rng, (2, 3, 16, 4)) for _ in range(3))
+    kw = dict(grid_h=4, grid_w=4, pool=2, lam=4.0, eps=1e-3, ns_iters=20)
+    res = orc.forward(q, k, v, **kw)
+    assert res["O"].shape == (2, 3, 16, 4)
+    one = orc.attention_problem(q[1, 2], k[1, 2], v[1, 2], **kw)
+    assert np.array_equal(res["O"][1, 2], one["O"])
+    samp = orc.forward(q, k, v, problems=[(1, 2)], **kw)
+    assert np.array_equal(samp["O"][0], one["O"])
+
+
+PINS = [pin_kernel_hand, pin_kernel_invariants, pin_pool_ramp, pin_pool_special_cases,
+        pin_pool_fixed_order, pin_ns_closed_form, pin_ns_lu, pin_ns_residual_squares,
+        pin_whiten_moments, pin_nystrom_pool1, pin_single_landmark, pin_metamorphic,
+        pin_forward_layout]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(pin):
+    pin(O)
+
+
+def test_headline_shapes_converge_in_fp64():
+    """At the 14x14 tiny shape, 20 float64 steps reach the inverse to ~1e-14."""
+    from lapnys_inputs import WORKLOADS, make_inputs
+    w = WORKLOADS["tiny_f32"]
+    x = make_inputs(w)
+    res = O.attention_problem(x.qf[0, 0], x.kf[0, 0], x.vf[0, 0], grid_h=w.grid_h, grid_w=w.grid_w,
+                              pool=w.pool, lam=w.lam, eps=w.eps, ns_iters=w.ns_iters)
+    r = np.linalg.norm(res["W"] @ res["X"] - np.eye(w.m))
+    assert r < 1e-12
+    assert np.all(res["C"] > 0) and np.all(res["C"] <= 1)
+
+
+# ----------------------------------------------------------------- planted mistakes
+
+
+def _k_signed(x, y, lam):
+    x, y = np.asarray(x, float), np.asarray(y, float)
+    return np.exp(-(x[:, None, :] - y[None, :, :]).sum(axis=2) / lam)
+
+
+def _k_l2sq(x, y, lam):
+    x, y = np.asarray(x, float), np.asarray(y, float)
+    return np.exp(-((x[:, None, :] - y[None, :, :]) ** 2).sum(axis=2) / lam)
+
+
+def _k_times_lam(x, y, lam):
+    x, y = np.asarray(x, float), np.asarray(y, float)
+    return np.exp(-np.abs(x[:, None, :] - y[None, :, :]).sum(axis=2) * lam / 16.0)
+
+
+def _pool_colmajor(k, gh, gw, p):
+    k = np.asarray(k, float)
+    g = k.reshape(gw, gh, -1).transpose(1, 0, 2)
+    acc = sum(g[r::p, c::p] for r in range(p) for c in range(p))
+    return (acc / (p * p)).reshape((gh // p) * (gw // p), -1)
+
+
+def _pool_colmajor_landmarks(k, gh, gw, p):
+    k = np.asarray(k, float)
+    g = k.reshape(gh, gw, -1)
+    acc = sum(g[r::p, c::p] for r in range(p) for c in range(p))
+    return (acc / (p * p)).transpose(1, 0, 2).reshape((gh // p) * (gw // p), -1)
+
+
+def _pool_sum(k, gh, gw, p):
+    k = np.asarray(k, float)
+    g = k.reshape(gh, gw, -1)
+    return sum(g[r::p, c::p] for r in range(p) for c in range(p)).reshape((gh // p) * (gw // p), -1)
+
+
+def _pool_reversed_order(k, gh, gw, p):
+    k = np.asarray(k, float)
+    g = k.reshape(gh, gw, -1)
+    acc = np.zeros((gh // p, gw // p, g.shape[2]))
+    for c in range(p):
+        for r in range(p):
+            acc = acc + g[r::p, c::p]
+    return (acc / (p * p)).reshape((gh // p) * (gw // p), -1)
+
+
+def _ns_no_alpha(w, iters):
+    x = np.asarray(w, float).T.copy()
+    for _ in range(iters):
+        x = x @ (2 * np.eye(len(w)) - w @ x)
+    return x
+
+
+def _ns_frob_alpha(w, iters):
+    x = np.asarray(w, float).T / (np.linalg.norm(w) ** 2)
+    for _ in range(iters):
+        x = x @ (2 * np.eye(len(w)) - w @ x)
+    return x
+
+
+def _ns_extra_step(w, iters):
+    return O.__dict__["_orig_ns"](w, iters + 1)
+
+
+def _ns_missing_two(w, iters):
+    w = np.asarray(w, float)
+    x = w.T / (np.abs(w).sum(0).max() * np.abs(w).sum(1).max())
+    for _ in range(iters):
+        x = x @ (np.eye(len(w)) - w @ x)
+    return x
+
+
+def _whiten_sample_var(c):
+    mu = c.mean(axis=0)
+    sigma = c.std(axis=0, ddof=1)
+    return (c - mu) / sigma, mu, sigma
+
+
+def _whiten_rows(c):
+    mu = c.mean(axis=1, keepdims=True)
+    sigma = c.std(axis=1, keepdims=True)
+    return (c - mu) / sigma, mu[:, 0], sigma[:, 0]
+
+
+def _attention_variant(variant):
+    def f(q, k, v, *, grid_h, grid_w, pool, lam, eps, ns_iters, whiten=True):
+        kt = O.pool_landmarks(k, grid_h, grid_w, pool)
+        m = kt.shape[0]
+        c = O.laplacian_kernel(q, kt, lam)
+        b = O.laplacian_kernel(kt, q if variant == "b_from_q" else k, lam)
+        w = O.laplacian_kernel(kt, kt, lam) + (0.0 if variant == "no_eps" else eps) * np.eye(m)
+        x = O.newton_schulz_inverse(w, ns_iters)
+        if variant == "skip_inverse":
+            x = np.eye(m)
+        if whiten:
+            z, mu, sigma = O.whiten_columns(c)
+        else:
+            z, mu, sigma = c, np.zeros(m), np.ones(m)
+        bv = b @ v
+        y = x @ bv
+        o = z @ y
+        return {"landmarks": kt, "C": c, "B": b, "W": w, "X": x, "Z": z,
+                "mu": mu, "sigma": sigma, "BV": bv, "Y": y, "O": o}
+    return f
+
+
+MUTANTS = {
+    "kernel_signed_difference": ("laplacian_kernel", _k_signed),
+    "kernel_squared_l2": ("laplacian_kernel", _k_l2sq),
+    "kernel_scale_by_lambda": ("laplacian_kernel", _k_times_lam),
+    "pool_column_major_tokens": ("pool_landmarks", _pool_colmajor),
+    "pool_column_major_landmarks": ("pool_landmarks", _pool_colmajor_landmarks),
+    "pool_sum_not_mean": ("pool_landmarks", _pool_sum),
+    "pool_reversed_sum_order": ("pool_landmarks", _pool_reversed_order),
+    "ns_no_scaling": ("newton_schulz_inverse", _ns_no_alpha),
+    "ns_frobenius_scaling": ("newton_schulz_inverse", _ns_frob_alpha),
+    "ns_one_extra_step": ("newton_schulz_inverse", _ns_extra_step),
+    "ns_update_missing_two": ("newton_schulz_inverse", _ns_missing_two),
+    "whiten_sample_variance": ("whiten_columns", _whiten_sample_var),
+    "whiten_per_token": ("whiten_columns", _whiten_rows),
+    "key_factor_from_queries": ("attention_problem", _attention_variant("b_from_q")),
+    "no_diagonal_shift": ("attention_problem", _attention_variant("no_eps")),
+    "inverse_skipped": ("attention_problem", _attention_variant("skip_inverse")),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistakes(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setitem(O.__dict__, "_orig_ns", O.newton_schulz_inverse)
+    monkeypatch.setattr(O, attr, fn)
+    failed = []
+    for pin in PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(O)
+        except (AssertionError, ValueError, FloatingPointError, np.linalg.LinAlgError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches the planted mistake {name}"

@@ -1,0 +1,174 @@
+"""Throughput of the Laplacian-kernel Nystrom attention forward on one MI355X.
+
+One step = one full forward (landmark pooling, W + Newton-Schulz, fused
+L1+exp kernel matrices with statistics and B V, reductions and Y = X (B V),
+whitened output) over the whole synthetic workload, through the C ABI with
+inputs already resident in device memory.
+
+Default workload: B=32, H=1, 56x56 token grid (N=3136), d=64, 8x8 pooling
+(m=49), lambda=4, eps=1e-3, 20 Newton-Schulz steps, bf16 inputs (float32
+arithmetic).  Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from lapnys_inputs import HEADLINE, WORKLOADS, make_inputs  # noqa: E402
+
+HEADLINE_METRIC = "attention tokens/s (N=3136,d=64,m=49 bf16) + % VALU/MFMA/HBM roofline"
+
+# MI355X figures: 256 CUs at 2.4 GHz; a non-packed fp32 VALU instruction
+# covers 64 lanes per CU per clock (4 SIMDs x 16 lanes), i.e.
+# 256 * 64 * 2.4e9 = 39.3e12 lane-ops/s.  (Packed fp32 would double it; it is
+# disabled in this build.)  HBM3E 8 TB/s; fp32 MFMA 157.3 TFLOP/s.
+CUS, CLOCK_HZ = 256, 2.4e9
+VALU_F32_LANE_OPS = CUS * 64 * CLOCK_HZ
+HBM_BYTES_S = 8.0e12
+
+
+def kernel_stage_ops(w) -> float:
+    """Algorithmic VALU ops of one launch of the fused L1+exp kernel: C = k(Q, K~)
+    and B = k(K~, K) are N*m pair-dims each per feature, and every pair-dim is one
+    subtract plus one add of the absolute value."""
+    pair_dims = 2.0 * w.N * w.m * w.d * w.P
+    return 2.0 * pair_dims
+
+
+def cpu_baseline(w, x, budget_s: float):
+    """The oracle, single-threaded, over as many (batch, head) problems as fit in
+    the budget; scaled to tokens/s."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        limit = None
+    done = 0
+    t0 = time.perf_counter()
+    for p in range(w.P):
+        b, h = divmod(p, w.H)
+        oracle.attention_problem(x.qf[b, h], x.kf[b, h], x.vf[b, h], grid_h=w.grid_h, grid_w=w.grid_w,
+                                 pool=w.pool, lam=float(np.float32(w.lam)), eps=float(np.float32(w.eps)),
+                                 ns_iters=w.ns_iters, whiten=w.whiten)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    if limit is not None:
+        limit.restore_original_limits()
+    return {"value": done * w.N / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {w.P} (batch, head) problems of the same workload (N={w.N} tokens each), "
+                      f"float64 numpy, one thread, {el:.1f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0: skip)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this forward has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        return 2
+    w = WORKLOADS[args.workload]
+    x = make_inputs(w)
+
+    # The CPU leg runs before the GPU is touched.
+    cpu = cpu_baseline(w, x, args.cpu_budget) if args.cpu_budget > 0 else None
+
+    import torch
+
+    import laplacian_nystr_approximation_amd as L
+    from laplacian_nystr_approximation_amd.lapnys import LAPNYS_NUM_STAGES, STAGE_NAMES
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if w.dtype == "bf16" else a).to(dev)
+
+    q, k, v = up(x.q), up(x.k), up(x.v)
+    params = L.params_for(w)
+    out = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
+    ws = torch.empty(L.lapnys_workspace_size(params), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    K, W = args.steps, args.warmup
+    ev = L.HipEvents(2 * LAPNYS_NUM_STAGES * K)
+    per_step = 2 * LAPNYS_NUM_STAGES
+
+    for _ in range(W):
+        L.lapnys_forward_ws(q, k, v, out, params, ws, stream)
+    torch.cuda.synchronize()
+
+    # Timed region: K steps, each through the profiled entry point, which
+    # records a HIP event before and after every stage on the stream that runs it.
+    t0 = time.perf_counter()
+    for i in range(K):
+        L.lapnys_forward_profiled(q, k, v, out, params, ws, ev.handles[i * per_step:(i + 1) * per_step], stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / K
+    stage_ms = {name: float(np.mean([ev.elapsed_ms(i * per_step + 2 * s, i * per_step + 2 * s + 1)
+                                     for i in range(K)]))
+                for s, name in enumerate(STAGE_NAMES)}
+    device_ms = float(np.mean([ev.elapsed_ms(i * per_step, (i + 1) * per_step - 1) for i in range(K)]))
+    ev.close()
+
+    # Same loop without the stage events, for the overhead of the markers.
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(K):
+        L.lapnys_forward_ws(q, k, v, out, params, ws, stream)
+    torch.cuda.synchronize()
+    plain_ms = (time.perf_counter() - t2) * 1e3 / K
+
+    tokens = w.P * w.N
+    kern_s = stage_ms["kernel"] * 1e-3
+    achieved = kernel_stage_ops(w) / kern_s / 1e12
+    peak = VALU_F32_LANE_OPS / 1e12
+    metric = HEADLINE_METRIC if w.name == HEADLINE else f"attention tokens/s ({w.name})"
+    line = {
+        "metric": metric,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "grid": [w.grid_h, w.grid_w], "N": w.N, "d": w.d,
+                   "pool": w.pool, "m": w.m, "input_dtype": w.dtype, "lambda": w.lam, "eps": w.eps,
+                   "ns_iters": w.ns_iters, "whiten": w.whiten},
+        "roofline": {"kernel": "l1exp_kernel (fused L1 + exp, C store, column statistics, B V)",
+                     "bound": "alu", "achieved": achieved, "peak": peak, "unit": "TOP/s",
+                     "frac": achieved / peak, "traffic": None},
+        "cpu_baseline": cpu,
+        "stage_ms": stage_ms,
+        "device_ms_per_step": device_ms,
+        "ms_per_step_without_stage_events": plain_ms,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,167 @@
+/*
+ * liblapnys -- forward pass of LaplacianFormer's Laplacian-kernel Nystrom
+ * linear attention on AMD Instinct MI355X (gfx950).
+ *
+ * Sources: the summary pages of "LaplacianFormer: Rethinking Linear Attention
+ * with Laplacian Kernel" (gist.science; English page cited as EN, others by
+ * language).  Per independent (batch, head) problem with N tokens on a
+ * grid_h x grid_w token grid and head dimension d, one call computes:
+ *
+ *   K~ = average pool of K over pool x pool windows        (EN 2.C.1)
+ *   C  = k(Q, K~)  [N x m],  B = k(K~, K)  [m x N],
+ *   W  = k(K~, K~) + eps I  [m x m],
+ *        with k(x, y) = exp(-||x - y||_1 / lambda)          (EN 2.A)
+ *   X  = Newton-Schulz inverse of W: X0 = W^T/(||W||_1 ||W||_inf),
+ *        then ns_iters steps X <- X (2I - W X)             (EN 2.C.2)
+ *   Z  = C with each landmark column centred and divided by its standard
+ *        deviation over the N tokens (population variance) (EN 2.B)
+ *   O  = Z (X (B V))
+ *
+ * m = (grid_h / pool) * (grid_w / pool).  Tokens are the row-major cells of
+ * the grid (token n = r * grid_w + c); landmark j = R * (grid_w / pool) + C.
+ *
+ * Layouts: q, k, v and out are dense, C-order [B, H, N, d] arrays; problem
+ * (b, h) is the contiguous block starting at element (b * H + h) * N * d.
+ * q, k and v are float32 or bfloat16 (dtype); out is always float32.  All
+ * arithmetic after the input load is float32 (landmark pooling sums in
+ * float64 and rounds once), so results do not depend on the input storage
+ * type beyond the input values themselves.
+ *
+ * Ownership and threading: every pointer argument belongs to the caller.  The
+ * library keeps no pointer after a call returns.  Device pointers must point
+ * to memory of the current HIP device.  Work is enqueued on `stream` (0 means
+ * the null stream); no call synchronises the stream except
+ * lapnys_forward_debug, which returns after its copies are complete.  Calls
+ * do not throw; every call returns LAPNYS_OK (0) or a negative status, and on
+ * any validation error nothing is enqueued.  Faults inside kernels surface as
+ * HIP errors at the caller's next synchronisation.
+ */
+#ifndef LAPNYS_H_
+#define LAPNYS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage type of q, k and v. */
+typedef enum { LAPNYS_F32 = 0, LAPNYS_BF16 = 1 } lapnys_dtype;
+
+/* flags: apply the diagonal whitening to C (EN 2.B).  Without it Z = C. */
+enum { LAPNYS_WHITEN = 1u };
+
+/* Status codes. */
+enum {
+  LAPNYS_OK = 0,
+  LAPNYS_ERR_INVALID_ARG = -1, /* null/misaligned pointer, non-positive size,
+                                  lambda <= 0, eps < 0, ns_iters < 0, unknown
+                                  flag bits, non-finite lambda/eps, or out
+                                  overlapping an input */
+  LAPNYS_ERR_SHAPE = -2,       /* N != grid_h * grid_w, or pool does not divide
+                                  grid_h and grid_w */
+  LAPNYS_ERR_UNSUPPORTED = -3, /* d not in {32, 64}, m > 256, unknown dtype, or
+                                  sizes beyond 32-bit element counts */
+  LAPNYS_ERR_WORKSPACE = -4,   /* workspace null, smaller than
+                                  lapnys_workspace_size, or not 256-B aligned */
+  LAPNYS_ERR_HIP = -5          /* a HIP runtime call or kernel launch failed */
+};
+
+/* Problem description.  lambda is the kernel scale (the pages find 4 best,
+ * EN section 4), eps the diagonal shift of W (EN 2.C.2). */
+typedef struct {
+  int32_t B, H;          /* batch and heads: B * H independent problems */
+  int32_t N;             /* tokens per problem, = grid_h * grid_w */
+  int32_t d;             /* head dimension: 32 or 64 */
+  int32_t grid_h, grid_w;
+  int32_t pool;          /* landmark pooling window (pool x pool, stride pool) */
+  float lambda;          /* > 0 */
+  float eps;             /* >= 0 */
+  int32_t ns_iters;      /* Newton-Schulz steps, >= 0 */
+  int32_t dtype;         /* lapnys_dtype */
+  uint32_t flags;        /* LAPNYS_WHITEN or 0 */
+} lapnys_params;
+
+/* Optional device buffers for the intermediates of one call (debug form).
+ * Each pointer may be NULL (not written).  Shapes per problem p = b * H + h,
+ * all float32, C order:
+ *   landmarks [B*H, m, d]   C_t [B*H, m, N] (C transposed: landmark-major)
+ *   W, X      [B*H, m, m]   BV, Y [B*H, m, d]   mu, sigma [B*H, m]
+ * With whitening off, mu = 0 and sigma = 1. */
+typedef struct {
+  float* landmarks;
+  float* C_t;
+  float* W;
+  float* X;
+  float* BV;
+  float* Y;
+  float* mu;
+  float* sigma;
+} lapnys_debug;
+
+/* Stage indices for lapnys_forward_profiled. */
+enum {
+  LAPNYS_STAGE_POOL = 0,     /* landmark average pooling */
+  LAPNYS_STAGE_NS = 1,       /* W build, scaling, Newton-Schulz */
+  LAPNYS_STAGE_KERNEL = 2,   /* fused L1 + exp: C, column statistics, B V */
+  LAPNYS_STAGE_FINALIZE = 3, /* statistics and B V reductions, Y = X (B V) */
+  LAPNYS_STAGE_OUTPUT = 4,   /* O = whiten(C) Y */
+  LAPNYS_NUM_STAGES = 5
+};
+
+/* Number of landmarks m for valid params, else a negative status. */
+int lapnys_landmark_count(const lapnys_params* p);
+
+/* Device workspace (bytes) that lapnys_forward_ws needs for params p.
+ * Host-only arithmetic: touches no device.  Returns a status; *bytes is
+ * written only on success. */
+int lapnys_workspace_size(const lapnys_params* p, size_t* bytes);
+
+/* Forward with a caller-provided device workspace (allocates nothing).
+ * q, k, v: device, [B,H,N,d] of dtype, 16-byte aligned.  out: device float32
+ * [B,H,N,d], 16-byte aligned, not overlapping q, k, v or ws.  ws: device,
+ * 256-byte aligned, at least lapnys_workspace_size bytes; its contents on
+ * entry do not matter and on return are unspecified.  Two calls that share a
+ * workspace must be ordered (same stream or synchronised). */
+int lapnys_forward_ws(const void* q, const void* k, const void* v, float* out,
+                      const lapnys_params* p, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
+
+/* Forward with a library-owned workspace: the call form
+ * lapnys_forward(q, k, v, out, params, stream).  The library keeps one
+ * workspace per device, grown with hipMalloc on demand (the first call for a
+ * size may allocate and synchronise the device), and reuses it; calls on one
+ * device must therefore be ordered on a single stream.  lapnys_release frees
+ * it.  Arguments as for lapnys_forward_ws. */
+int lapnys_forward(const void* q, const void* k, const void* v, float* out,
+                   const lapnys_params* p, hipStream_t stream);
+
+/* lapnys_forward_ws, then copies of the intermediates into the non-NULL
+ * buffers of dbg (layouts above); synchronises `stream` before returning. */
+int lapnys_forward_debug(const void* q, const void* k, const void* v, float* out,
+                         const lapnys_params* p, void* ws, size_t ws_bytes,
+                         const lapnys_debug* dbg, hipStream_t stream);
+
+/* lapnys_forward_ws that also records stage_events[2*s] before and
+ * stage_events[2*s+1] after stage s (LAPNYS_STAGE_*) on the stream that runs
+ * that stage, so hipEventElapsedTime gives per-stage device time.
+ * stage_events: 2 * LAPNYS_NUM_STAGES events created by the caller. */
+int lapnys_forward_profiled(const void* q, const void* k, const void* v, float* out,
+                            const lapnys_params* p, void* ws, size_t ws_bytes,
+                            hipEvent_t* stage_events, hipStream_t stream);
+
+/* Frees the library-owned workspaces of lapnys_forward (all devices).
+ * Synchronises each device that had one. */
+void lapnys_release(void);
+
+/* Static, human-readable text for a status code. */
+const char* lapnys_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LAPNYS_H_ */

@@ -1,0 +1,307 @@
+// C ABI of liblapnys (declared in include/lapnys.h): parameter validation,
+// the per-call plan and workspace layout, the stage sequence, the
+// library-owned workspace of lapnys_forward, and the debug/profiled forms.
+//
+// Stage sequence on the caller's stream (no host synchronisation):
+//   pool      K -> K~                                  (pool.hip)
+//   ns        K~ -> W, X = NS inverse of W             (ns.hip)
+//   kernel    Q, K, V, K~ -> C^T, tile statistics, B V partials (l1exp.hip)
+//   finalize  statistics -> mu, sigma; partials -> B V; Y = X (B V) (finalize.hip)
+//   output    O = whiten(C) Y                          (output.hip)
+#include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "lapnys.h"
+#include "lapnys_internal.hpp"
+
+using lapnys::Plan;
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// LAPNYS_LOG=1 in the environment prints each failing HIP call to stderr.
+bool log_enabled() {
+  static const bool on = [] {
+    const char* e = getenv("LAPNYS_LOG");
+    return e && *e && *e != '0';
+  }();
+  return on;
+}
+
+bool ok(hipError_t e, const char* what) {
+  if (e == hipSuccess) return true;
+  if (log_enabled()) fprintf(stderr, "liblapnys: %s failed: %s (%d)\n", what, hipGetErrorString(e), (int)e);
+  return false;
+}
+
+int validate(const lapnys_params* p) {
+  if (!p) return LAPNYS_ERR_INVALID_ARG;
+  if (p->B <= 0 || p->H <= 0 || p->N <= 0 || p->d <= 0 || p->grid_h <= 0 || p->grid_w <= 0 || p->pool <= 0)
+    return LAPNYS_ERR_INVALID_ARG;
+  if (!(isfinite(p->lambda) && p->lambda > 0.f)) return LAPNYS_ERR_INVALID_ARG;
+  if (!(isfinite(p->eps) && p->eps >= 0.f)) return LAPNYS_ERR_INVALID_ARG;
+  if (p->ns_iters < 0) return LAPNYS_ERR_INVALID_ARG;
+  if (p->flags & ~(uint32_t)LAPNYS_WHITEN) return LAPNYS_ERR_INVALID_ARG;
+  if (p->dtype != LAPNYS_F32 && p->dtype != LAPNYS_BF16) return LAPNYS_ERR_UNSUPPORTED;
+  if ((int64_t)p->grid_h * p->grid_w != (int64_t)p->N) return LAPNYS_ERR_SHAPE;
+  if (p->grid_h % p->pool || p->grid_w % p->pool) return LAPNYS_ERR_SHAPE;
+  if (p->d != 32 && p->d != 64) return LAPNYS_ERR_UNSUPPORTED;
+  const int64_t m = (int64_t)(p->grid_h / p->pool) * (p->grid_w / p->pool);
+  if (m > lapnys::kMaxM) return LAPNYS_ERR_UNSUPPORTED;
+  if ((int64_t)p->B * p->H > 65535) return LAPNYS_ERR_UNSUPPORTED;  // problems map to one grid axis
+  return LAPNYS_OK;
+}
+
+int make_plan(const lapnys_params* p, Plan* pl) {
+  const int st = validate(p);
+  if (st != LAPNYS_OK) return st;
+  Plan& P = *pl;
+  memset(&P, 0, sizeof(P));
+  P.P = p->B * p->H;
+  P.N = p->N;
+  P.d = p->d;
+  P.grid_w = p->grid_w;
+  P.pool = p->pool;
+  P.gw = p->grid_w / p->pool;
+  P.m = (p->grid_h / p->pool) * P.gw;
+  P.dtype = p->dtype;
+  P.whiten = (p->flags & LAPNYS_WHITEN) != 0;
+  P.ns_iters = p->ns_iters;
+  // exp(-s / lambda) = exp2(s * scale)
+  P.scale = (float)(-1.4426950408889634074 / (double)p->lambda);
+  P.eps = p->eps;
+  P.fused_ns = P.m <= lapnys::kFusedNsMaxM;
+  P.mp = P.fused_ns ? 64 : ((P.m + 63) / 64) * 64;
+  P.tt = 256;
+  P.ntiles = (P.N + P.tt - 1) / P.tt;
+  P.lb = P.m <= lapnys::kLandmarkBlock ? P.m : 32;
+  P.jblocks = (P.m + P.lb - 1) / P.lb;
+  // Tiles per workgroup: enough workgroups to fill the chip several times,
+  // few enough that the B V partials stay small.
+  const int64_t jobs = (int64_t)P.ntiles * P.jblocks * P.P;
+  P.tpg = (int)(jobs / 4096 > 1 ? jobs / 4096 : 1);
+  P.groups = (P.ntiles + P.tpg - 1) / P.tpg;
+  const size_t f = sizeof(float);
+  const size_t Pn = (size_t)P.P;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  P.off_kt = take(Pn * P.m * P.d * f);
+  P.off_w = take(Pn * P.mp * P.mp * f);
+  P.off_x = take(Pn * P.mp * P.mp * f);
+  P.off_x2 = take(P.fused_ns ? 0 : Pn * P.mp * P.mp * f);
+  P.off_pm = take(P.fused_ns ? 0 : Pn * P.mp * P.mp * f);
+  P.off_ct = take(Pn * P.m * (size_t)P.N * f);
+  P.off_stats = take(Pn * P.ntiles * P.m * 2 * f);
+  P.off_bvpart = take(Pn * P.groups * P.m * P.d * f);
+  P.off_bv = take(Pn * P.m * P.d * f);
+  P.off_mu = take(Pn * P.m * f);
+  P.off_sigma = take(Pn * P.m * f);
+  P.off_rs = take(Pn * P.m * f);
+  P.off_y = take(Pn * P.m * P.d * f);
+  P.total = off;
+  return LAPNYS_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+int check_buffers(const void* q, const void* k, const void* v, const float* out, const Plan& pl, const void* ws,
+                  size_t ws_bytes) {
+  if (!q || !k || !v || !out) return LAPNYS_ERR_INVALID_ARG;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15) return LAPNYS_ERR_INVALID_ARG;
+  const size_t elems = (size_t)pl.P * pl.N * pl.d;
+  const size_t in_bytes = elems * (pl.dtype == LAPNYS_BF16 ? 2 : 4);
+  const size_t out_bytes = elems * 4;
+  if (overlaps(out, out_bytes, q, in_bytes) || overlaps(out, out_bytes, k, in_bytes) ||
+      overlaps(out, out_bytes, v, in_bytes))
+    return LAPNYS_ERR_INVALID_ARG;
+  if (!ws || ((uintptr_t)ws & 255) || ws_bytes < pl.total) return LAPNYS_ERR_WORKSPACE;
+  if (overlaps(out, out_bytes, ws, pl.total)) return LAPNYS_ERR_INVALID_ARG;
+  return LAPNYS_OK;
+}
+
+struct Buffers {
+  float *kt, *w, *x, *x2, *pm, *ct, *stats, *bvpart, *bv, *mu, *sigma, *rs, *y;
+  float* x_final;
+};
+
+Buffers carve(const Plan& pl, void* ws) {
+  char* b = (char*)ws;
+  Buffers B;
+  B.kt = (float*)(b + pl.off_kt);
+  B.w = (float*)(b + pl.off_w);
+  B.x = (float*)(b + pl.off_x);
+  B.x2 = (float*)(b + pl.off_x2);
+  B.pm = (float*)(b + pl.off_pm);
+  B.ct = (float*)(b + pl.off_ct);
+  B.stats = (float*)(b + pl.off_stats);
+  B.bvpart = (float*)(b + pl.off_bvpart);
+  B.bv = (float*)(b + pl.off_bv);
+  B.mu = (float*)(b + pl.off_mu);
+  B.sigma = (float*)(b + pl.off_sigma);
+  B.rs = (float*)(b + pl.off_rs);
+  B.y = (float*)(b + pl.off_y);
+  B.x_final = B.x;
+  return B;
+}
+
+int run(const Plan& pl, const void* q, const void* k, const void* v, float* out, Buffers& B, hipEvent_t* ev,
+        hipStream_t s) {
+  // An error left by an earlier, unrelated runtime call would otherwise be
+  // reported by the first launch check below.
+  (void)hipGetLastError();
+  auto mark = [&](int idx) { return !ev || ok(hipEventRecord(ev[idx], s), "hipEventRecord"); };
+  if (!mark(2 * LAPNYS_STAGE_POOL)) return LAPNYS_ERR_HIP;
+  if (!ok(lapnys::launch_pool(pl, k, B.kt, s), "pool launch")) return LAPNYS_ERR_HIP;
+  if (!mark(2 * LAPNYS_STAGE_POOL + 1) || !mark(2 * LAPNYS_STAGE_NS)) return LAPNYS_ERR_HIP;
+  if (!ok(lapnys::launch_ns(pl, B.kt, B.w, B.x, B.x2, B.pm, &B.x_final, s), "Newton-Schulz launch"))
+    return LAPNYS_ERR_HIP;
+  if (!mark(2 * LAPNYS_STAGE_NS + 1) || !mark(2 * LAPNYS_STAGE_KERNEL)) return LAPNYS_ERR_HIP;
+  if (!ok(lapnys::launch_l1exp(pl, q, k, v, B.kt, B.ct, B.stats, B.bvpart, s), "kernel-matrix launch"))
+    return LAPNYS_ERR_HIP;
+  if (!mark(2 * LAPNYS_STAGE_KERNEL + 1) || !mark(2 * LAPNYS_STAGE_FINALIZE)) return LAPNYS_ERR_HIP;
+  if (!ok(lapnys::launch_finalize(pl, B.stats, B.bvpart, B.x_final, B.bv, B.mu, B.sigma, B.rs, B.y, s),
+          "finalize launch"))
+    return LAPNYS_ERR_HIP;
+  if (!mark(2 * LAPNYS_STAGE_FINALIZE + 1) || !mark(2 * LAPNYS_STAGE_OUTPUT)) return LAPNYS_ERR_HIP;
+  if (!ok(lapnys::launch_output(pl, B.ct, B.y, B.mu, B.rs, out, s), "output launch")) return LAPNYS_ERR_HIP;
+  if (!mark(2 * LAPNYS_STAGE_OUTPUT + 1)) return LAPNYS_ERR_HIP;
+  return LAPNYS_OK;
+}
+
+int forward_impl(const void* q, const void* k, const void* v, float* out, const lapnys_params* p, void* ws,
+                 size_t ws_bytes, hipEvent_t* ev, const lapnys_debug* dbg, hipStream_t s) {
+  Plan pl;
+  int st = make_plan(p, &pl);
+  if (st != LAPNYS_OK) return st;
+  st = check_buffers(q, k, v, out, pl, ws, ws_bytes);
+  if (st != LAPNYS_OK) return st;
+  Buffers B = carve(pl, ws);
+  st = run(pl, q, k, v, out, B, ev, s);
+  if (st != LAPNYS_OK || !dbg) return st;
+  const size_t f = sizeof(float);
+  const size_t Pm = (size_t)pl.P * pl.m;
+  auto cp = [&](float* dst, const float* src, size_t bytes) {
+    return !dst || ok(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s), "debug copy");
+  };
+  bool good = cp(dbg->landmarks, B.kt, Pm * pl.d * f) && cp(dbg->C_t, B.ct, Pm * pl.N * f) &&
+            cp(dbg->BV, B.bv, Pm * pl.d * f) && cp(dbg->Y, B.y, Pm * pl.d * f) && cp(dbg->mu, B.mu, Pm * f) &&
+            cp(dbg->sigma, B.sigma, Pm * f);
+  if (good && dbg->W) good = ok(lapnys::launch_extract_square(B.w, pl.mp, dbg->W, pl.m, pl.P, s), "W extract");
+  if (good && dbg->X)
+    good = ok(lapnys::launch_extract_square(B.x_final, pl.mp, dbg->X, pl.m, pl.P, s), "X extract");
+  if (!good || !ok(hipStreamSynchronize(s), "hipStreamSynchronize")) return LAPNYS_ERR_HIP;
+  return LAPNYS_OK;
+}
+
+struct Cached {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_cache_mu;
+std::vector<Cached> g_cache;
+
+}  // namespace
+
+extern "C" {
+
+int lapnys_landmark_count(const lapnys_params* p) {
+  const int st = validate(p);
+  if (st != LAPNYS_OK) return st;
+  return (p->grid_h / p->pool) * (p->grid_w / p->pool);
+}
+
+int lapnys_workspace_size(const lapnys_params* p, size_t* bytes) {
+  if (!bytes) return LAPNYS_ERR_INVALID_ARG;
+  Plan pl;
+  const int st = make_plan(p, &pl);
+  if (st != LAPNYS_OK) return st;
+  *bytes = pl.total;
+  return LAPNYS_OK;
+}
+
+int lapnys_forward_ws(const void* q, const void* k, const void* v, float* out, const lapnys_params* p, void* ws,
+                      size_t ws_bytes, hipStream_t stream) {
+  return forward_impl(q, k, v, out, p, ws, ws_bytes, nullptr, nullptr, stream);
+}
+
+int lapnys_forward_profiled(const void* q, const void* k, const void* v, float* out, const lapnys_params* p,
+                            void* ws, size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream) {
+  if (!stage_events) return LAPNYS_ERR_INVALID_ARG;
+  for (int i = 0; i < 2 * LAPNYS_NUM_STAGES; ++i)
+    if (!stage_events[i]) return LAPNYS_ERR_INVALID_ARG;
+  return forward_impl(q, k, v, out, p, ws, ws_bytes, stage_events, nullptr, stream);
+}
+
+int lapnys_forward_debug(const void* q, const void* k, const void* v, float* out, const lapnys_params* p, void* ws,
+                         size_t ws_bytes, const lapnys_debug* dbg, hipStream_t stream) {
+  if (!dbg) return LAPNYS_ERR_INVALID_ARG;
+  return forward_impl(q, k, v, out, p, ws, ws_bytes, nullptr, dbg, stream);
+}
+
+int lapnys_forward(const void* q, const void* k, const void* v, float* out, const lapnys_params* p,
+                   hipStream_t stream) {
+  Plan pl;
+  int st = make_plan(p, &pl);
+  if (st != LAPNYS_OK) return st;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return LAPNYS_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_cache_mu);
+  if ((int)g_cache.size() <= dev) g_cache.resize(dev + 1);
+  Cached& c = g_cache[dev];
+  if (c.bytes < pl.total) {
+    if (c.ptr) {
+      if (hipDeviceSynchronize() != hipSuccess) return LAPNYS_ERR_HIP;
+      hipFree(c.ptr);
+      c.ptr = nullptr;
+      c.bytes = 0;
+    }
+    if (hipMalloc(&c.ptr, pl.total) != hipSuccess) {
+      c.ptr = nullptr;
+      return LAPNYS_ERR_HIP;
+    }
+    c.bytes = pl.total;
+  }
+  return forward_impl(q, k, v, out, p, c.ptr, c.bytes, nullptr, nullptr, stream);
+}
+
+void lapnys_release(void) {
+  std::lock_guard<std::mutex> lock(g_cache_mu);
+  int cur = 0;
+  const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  for (size_t dev = 0; dev < g_cache.size(); ++dev) {
+    if (!g_cache[dev].ptr) continue;
+    if (hipSetDevice((int)dev) == hipSuccess) {
+      hipDeviceSynchronize();
+      hipFree(g_cache[dev].ptr);
+    }
+    g_cache[dev] = Cached();
+  }
+  if (have_cur) hipSetDevice(cur);
+}
+
+const char* lapnys_status_string(int status) {
+  switch (status) {
+    case LAPNYS_OK: return "ok";
+    case LAPNYS_ERR_INVALID_ARG: return "invalid argument";
+    case LAPNYS_ERR_SHAPE: return "shape mismatch: N != grid_h*grid_w or pool does not divide the grid";
+    case LAPNYS_ERR_UNSUPPORTED: return "unsupported: d must be 32 or 64, m <= 256, dtype f32 or bf16";
+    case LAPNYS_ERR_WORKSPACE: return "workspace null, too small or not 256-byte aligned";
+    case LAPNYS_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,297 @@
+// Landmark Gram matrix and its Newton-Schulz inverse (EN page, section 2.C.2;
+// DE section 2; ZH section 2.2; KO section 2.3; JA section 2.3).
+//
+//   W  = k(K~, K~) + eps I,   k(x, y) = exp(-||x - y||_1 / lambda)
+//   X0 = W^T / (||W||_1 ||W||_inf)
+//   X <- X (2I - W X), a fixed number of times, matrix products only.
+//
+// W is built so that it is bit-symmetric: entry (a, b) and entry (b, a) sum
+// the same |differences| in the same feature order, and the diagonal is
+// exp(0) + eps = 1 + eps exactly as float32 arithmetic gives it.
+//
+// Two schedules:
+//  * m <= 64: one workgroup per problem keeps W, X and W X in LDS (64 x 64,
+//    zero padded) and runs every step in one launch.  Each of the four
+//    wavefronts owns a 32 x 32 block of a product and issues fp32 MFMA
+//    (32x32x2) along the reduction; padding rows and columns stay exactly zero.
+//  * 64 < m <= 256: the products are too large for one LDS; W and the iterates
+//    live in the workspace (L2-resident) and each product is one batched launch
+//    of 64 x 64 output tiles, two launches per step.
+#include "lapnys_internal.hpp"
+
+namespace lapnys {
+
+namespace {
+
+constexpr int kMP = 64;   // padded size of the in-LDS schedule
+constexpr int kLD = 65;   // LDS row stride: column reads hit 32 distinct banks
+
+template <int D>
+__global__ __launch_bounds__(256) void ns_fused_kernel(const float* __restrict__ kt, float* __restrict__ wout,
+                                                       float* __restrict__ xout, int m, float scale, float eps,
+                                                       int iters) {
+  constexpr int KLD = D + 1;
+  __shared__ float kl[kMP * KLD];
+  __shared__ float wl[kMP * kLD];
+  __shared__ float xa[kMP * kLD];
+  __shared__ float xb[kMP * kLD];
+  __shared__ float pl[kMP * kLD];
+  __shared__ float red[128];
+  __shared__ float alpha_s;
+
+  const int p = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const float* ktp = kt + (size_t)p * m * D;
+  for (int e = tid; e < m * D; e += 256) kl[(e / D) * KLD + (e % D)] = ktp[e];
+  __syncthreads();
+
+  // W = k(K~, K~) + eps I, zero padded.
+  for (int e = tid; e < kMP * kMP; e += 256) {
+    const int a = e >> 6, b = e & 63;
+    float val = 0.f;
+    if (a < m && b < m) {
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int t = 0; t < D; t += 2) {
+        s0 += fabsf(kl[a * KLD + t] - kl[b * KLD + t]);
+        s1 += fabsf(kl[a * KLD + t + 1] - kl[b * KLD + t + 1]);
+      }
+      val = exp2f((s0 + s1) * scale);
+      if (a == b) val += eps;
+    }
+    wl[a * kLD + b] = val;
+  }
+  __syncthreads();
+
+  // alpha = ||W||_1 * ||W||_inf (largest absolute column sum times largest row sum).
+  if (tid < kMP) {
+    float r = 0.f;
+    for (int b = 0; b < kMP; ++b) r += fabsf(wl[tid * kLD + b]);
+    red[tid] = r;
+  } else if (tid < 2 * kMP) {
+    const int c = tid - kMP;
+    float s = 0.f;
+    for (int a = 0; a < kMP; ++a) s += fabsf(wl[a * kLD + c]);
+    red[tid] = s;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float rm = 0.f, cm = 0.f;
+    for (int i = 0; i < kMP; ++i) {
+      rm = fmaxf(rm, red[i]);
+      cm = fmaxf(cm, red[kMP + i]);
+    }
+    alpha_s = cm * rm;
+  }
+  __syncthreads();
+  const float alpha = alpha_s;
+  for (int e = tid; e < kMP * kMP; e += 256) {
+    const int a = e >> 6, b = e & 63;
+    xa[a * kLD + b] = wl[b * kLD + a] / alpha;
+  }
+  __syncthreads();
+
+  const int bi = w >> 1, bj = w & 1;
+  const int li = lane & 31, lk = lane >> 5;
+  const int kext = (m + 1) & ~1;  // reduction extent: m rounded up to the MFMA depth
+  float* xc = xa;
+  float* xn = xb;
+  for (int it = 0; it < iters; ++it) {
+    // P = W X
+    f32x16 acc = {0.f};
+    for (int k0 = 0; k0 < kext; k0 += 2) {
+      const float a = wl[(32 * bi + li) * kLD + k0 + lk];
+      const float b = xc[(k0 + lk) * kLD + 32 * bj + li];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      pl[(32 * bi + 8 * (r >> 2) + 4 * lk + (r & 3)) * kLD + 32 * bj + li] = acc[r];
+    __syncthreads();
+    // X_next = X (2I - P)
+    acc = f32x16{0.f};
+    for (int k0 = 0; k0 < kext; k0 += 2) {
+      const int kk = k0 + lk, col = 32 * bj + li;
+      const float a = xc[(32 * bi + li) * kLD + kk];
+      const float b = (kk == col ? 2.f : 0.f) - pl[kk * kLD + col];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      xn[(32 * bi + 8 * (r >> 2) + 4 * lk + (r & 3)) * kLD + 32 * bj + li] = acc[r];
+    __syncthreads();
+    float* t = xc;
+    xc = xn;
+    xn = t;
+  }
+
+  float* wp = wout + (size_t)p * kMP * kMP;
+  float* xp = xout + (size_t)p * kMP * kMP;
+  for (int e = tid; e < kMP * kMP; e += 256) {
+    wp[e] = wl[(e >> 6) * kLD + (e & 63)];
+    xp[e] = xc[(e >> 6) * kLD + (e & 63)];
+  }
+}
+
+// ---- 64 < m <= 256 -------------------------------------------------------
+
+// W rows [16*blockIdx.x, +16) of problem blockIdx.y; thread b owns column b.
+template <int D>
+__global__ __launch_bounds__(256) void wbuild_big_kernel(const float* __restrict__ kt, float* __restrict__ w, int m,
+                                                         int mp, float scale, float eps) {
+  __shared__ float kl[16 * D];
+  const int p = blockIdx.y, a0 = blockIdx.x * 16, b = threadIdx.x;
+  const float* ktp = kt + (size_t)p * m * D;
+  for (int e = threadIdx.x; e < 16 * D; e += 256) {
+    const int a = a0 + e / D;
+    kl[e] = (a < m) ? ktp[(size_t)a * D + e % D] : 0.f;
+  }
+  float xb[D];
+#pragma unroll
+  for (int t = 0; t < D; ++t) xb[t] = (b < m) ? ktp[(size_t)b * D + t] : 0.f;
+  __syncthreads();
+  if (b >= mp) return;
+  for (int r = 0; r < 16; ++r) {
+    const int a = a0 + r;
+    float val = 0.f;
+    if (a < m && b < m) {
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int t = 0; t < D; t += 2) {
+        s0 += fabsf(kl[r * D + t] - xb[t]);
+        s1 += fabsf(kl[r * D + t + 1] - xb[t + 1]);
+      }
+      val = exp2f((s0 + s1) * scale);
+      if (a == b) val += eps;
+    }
+    w[((size_t)p * mp + a) * mp + b] = val;
+  }
+}
+
+// alpha and X0 = W^T / alpha for problem blockIdx.x.
+__global__ __launch_bounds__(256) void alpha_x0_kernel(const float* __restrict__ w, float* __restrict__ x, int mp) {
+  __shared__ float red[512];
+  __shared__ float alpha_s;
+  const int p = blockIdx.x, tid = threadIdx.x;
+  const float* wp = w + (size_t)p * mp * mp;
+  float rs = 0.f, cs = 0.f;
+  if (tid < mp) {
+    for (int b = 0; b < mp; ++b) rs += fabsf(wp[(size_t)tid * mp + b]);
+    for (int a = 0; a < mp; ++a) cs += fabsf(wp[(size_t)a * mp + tid]);
+  }
+  red[tid] = rs;
+  red[256 + tid] = cs;
+  __syncthreads();
+  if (tid == 0) {
+    float rm = 0.f, cm = 0.f;
+    for (int i = 0; i < 256; ++i) {
+      rm = fmaxf(rm, red[i]);
+      cm = fmaxf(cm, red[256 + i]);
+    }
+    alpha_s = cm * rm;
+  }
+  __syncthreads();
+  const float alpha = alpha_s;
+  float* xp = x + (size_t)p * mp * mp;
+  for (int e = tid; e < mp * mp; e += 256) {
+    const int a = e / mp, b = e % mp;
+    xp[e] = wp[(size_t)b * mp + a] / alpha;
+  }
+}
+
+// out = A B (mode 0) or out = A (2I - B) (mode 1), 64 x 64 output tile
+// (blockIdx.x, blockIdx.y) of problem blockIdx.z; reduction over [0, kext).
+__global__ __launch_bounds__(256) void ns_gemm_kernel(const float* __restrict__ amat, const float* __restrict__ bmat,
+                                                      float* __restrict__ out, int mp, int kext, int mode) {
+  __shared__ float as[64 * 33];
+  __shared__ float bs[32 * 64];
+  const int p = blockIdx.z, r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wr = w >> 1, wc = w & 1, li = lane & 31, lk = lane >> 5;
+  const float* A = amat + (size_t)p * mp * mp;
+  const float* B = bmat + (size_t)p * mp * mp;
+  f32x16 acc = {0.f};
+  for (int kc = 0; kc < kext; kc += 32) {
+    for (int e = tid; e < 64 * 32; e += 256) {
+      const int r = e >> 5, c = e & 31;
+      as[r * 33 + c] = A[(size_t)(r0 + r) * mp + kc + c];
+    }
+    for (int e = tid; e < 32 * 64; e += 256) {
+      const int r = e >> 6, c = e & 63;
+      float bv = B[(size_t)(kc + r) * mp + c0 + c];
+      if (mode) bv = ((kc + r == c0 + c) ? 2.f : 0.f) - bv;
+      bs[r * 64 + c] = bv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k0 = 0; k0 < 32; k0 += 2) {
+      const float a = as[(32 * wr + li) * 33 + k0 + lk];
+      const float b = bs[(k0 + lk) * 64 + 32 * wc + li];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  float* O = out + (size_t)p * mp * mp;
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    O[(size_t)(r0 + 32 * wr + 8 * (r >> 2) + 4 * lk + (r & 3)) * mp + c0 + 32 * wc + li] = acc[r];
+}
+
+__global__ __launch_bounds__(256) void extract_square_kernel(const float* __restrict__ src, int src_ld,
+                                                             float* __restrict__ dst, int n, long long total) {
+  const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= total) return;
+  const long long p = e / ((long long)n * n);
+  const int rem = (int)(e % ((long long)n * n));
+  const int a = rem / n, b = rem % n;
+  dst[e] = src[(p * src_ld + a) * src_ld + b];
+}
+
+}  // namespace
+
+hipError_t launch_ns(const Plan& pl, const float* kt, float* w, float* x, float* x2, float* pm, float** x_final,
+                     hipStream_t s) {
+  if (pl.fused_ns) {
+    if (pl.d == 64)
+      hipLaunchKernelGGL(ns_fused_kernel<64>, dim3(pl.P), dim3(256), 0, s, kt, w, x, pl.m, pl.scale, pl.eps,
+                         pl.ns_iters);
+    else
+      hipLaunchKernelGGL(ns_fused_kernel<32>, dim3(pl.P), dim3(256), 0, s, kt, w, x, pl.m, pl.scale, pl.eps,
+                         pl.ns_iters);
+    *x_final = x;
+    return hipGetLastError();
+  }
+  const int mp = pl.mp;
+  if (pl.d == 64)
+    hipLaunchKernelGGL(wbuild_big_kernel<64>, dim3(mp / 16, pl.P), dim3(256), 0, s, kt, w, pl.m, mp, pl.scale,
+                       pl.eps);
+  else
+    hipLaunchKernelGGL(wbuild_big_kernel<32>, dim3(mp / 16, pl.P), dim3(256), 0, s, kt, w, pl.m, mp, pl.scale,
+                       pl.eps);
+  hipLaunchKernelGGL(alpha_x0_kernel, dim3(pl.P), dim3(256), 0, s, w, x, mp);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int kext = (pl.m + 31) & ~31;
+  float* xc = x;
+  float* xn = x2;
+  for (int it = 0; it < pl.ns_iters; ++it) {
+    hipLaunchKernelGGL(ns_gemm_kernel, dim3(mp / 64, mp / 64, pl.P), dim3(256), 0, s, w, xc, pm, mp, kext, 0);
+    hipLaunchKernelGGL(ns_gemm_kernel, dim3(mp / 64, mp / 64, pl.P), dim3(256), 0, s, xc, pm, xn, mp, kext, 1);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    float* t = xc;
+    xc = xn;
+    xn = t;
+  }
+  *x_final = xc;
+  return hipSuccess;
+}
+
+hipError_t launch_extract_square(const float* src, int src_ld, float* dst, int n, int P, hipStream_t s) {
+  const long long total = (long long)P * n * n;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(extract_square_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, src, src_ld,
+                     dst, n, total);
+  return hipGetLastError();
+}
+
+}  // namespace lapnys

@@ -1,0 +1,222 @@
+"""ctypes binding of liblapnys (include/lapnys.h): argument marshalling only.
+
+Every function carries the name of the C entry point it calls and returns what
+that call returns, raising ``LapnysError`` on a negative status.  Tensors are
+passed as device pointers (``torch.Tensor.data_ptr()``); plain integers are
+accepted as raw pointers.  All computation happens in the HIP library: if
+``liblapnys.so`` has not been built, importing this module fails.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblapnys.so")
+
+LAPNYS_F32 = 0
+LAPNYS_BF16 = 1
+LAPNYS_WHITEN = 1
+
+LAPNYS_OK = 0
+LAPNYS_ERR_INVALID_ARG = -1
+LAPNYS_ERR_SHAPE = -2
+LAPNYS_ERR_UNSUPPORTED = -3
+LAPNYS_ERR_WORKSPACE = -4
+LAPNYS_ERR_HIP = -5
+
+LAPNYS_STAGE_POOL = 0
+LAPNYS_STAGE_NS = 1
+LAPNYS_STAGE_KERNEL = 2
+LAPNYS_STAGE_FINALIZE = 3
+LAPNYS_STAGE_OUTPUT = 4
+LAPNYS_NUM_STAGES = 5
+STAGE_NAMES = ["pool", "ns", "kernel", "finalize", "output"]
+
+
+class lapnys_params(ctypes.Structure):
+    """Mirror of the C struct (the C field ``lambda`` is ``lambda_`` here)."""
+
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32), ("pool", ctypes.c_int32),
+        ("lambda_", ctypes.c_float), ("eps", ctypes.c_float), ("ns_iters", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
+    ]
+
+
+class lapnys_debug(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in
+                ["landmarks", "C_t", "W", "X", "BV", "Y", "mu", "sigma"]]
+
+
+DEBUG_FIELDS = [f[0] for f in lapnys_debug._fields_]
+
+
+class LapnysError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {lapnys_status_string(code)} (status {code})")
+
+
+def _load():
+    # PyTorch-ROCm loads its own HIP runtime under the name libamdhip64.so;
+    # liblapnys depends on that name, so loading torch first leaves exactly one
+    # HIP runtime in the process (the one whose streams and memory we are given).
+    import torch  # noqa: F401
+
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m laplacian_nystr_approximation_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(lapnys_params)
+    vp = ctypes.c_void_p
+    lib.lapnys_landmark_count.argtypes = [P]
+    lib.lapnys_landmark_count.restype = ctypes.c_int
+    lib.lapnys_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.lapnys_workspace_size.restype = ctypes.c_int
+    lib.lapnys_forward_ws.argtypes = [vp, vp, vp, vp, P, vp, ctypes.c_size_t, vp]
+    lib.lapnys_forward_ws.restype = ctypes.c_int
+    lib.lapnys_forward.argtypes = [vp, vp, vp, vp, P, vp]
+    lib.lapnys_forward.restype = ctypes.c_int
+    lib.lapnys_forward_debug.argtypes = [vp, vp, vp, vp, P, vp, ctypes.c_size_t,
+                                         ctypes.POINTER(lapnys_debug), vp]
+    lib.lapnys_forward_debug.restype = ctypes.c_int
+    lib.lapnys_forward_profiled.argtypes = [vp, vp, vp, vp, P, vp, ctypes.c_size_t,
+                                            ctypes.POINTER(ctypes.c_void_p), vp]
+    lib.lapnys_forward_profiled.restype = ctypes.c_int
+    lib.lapnys_release.argtypes = []
+    lib.lapnys_release.restype = None
+    lib.lapnys_status_string.argtypes = [ctypes.c_int]
+    lib.lapnys_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def library():
+    """The loaded ctypes library handle."""
+    return _lib
+
+
+def make_params(*, B, H, grid_h, grid_w, d, pool, lam=4.0, eps=1e-3, ns_iters=20, dtype="f32",
+                whiten=True, N=None) -> lapnys_params:
+    """Build a lapnys_params; ``dtype`` is "f32"/"bf16" or the enum value."""
+    dt = {"f32": LAPNYS_F32, "bf16": LAPNYS_BF16}.get(dtype, dtype)
+    return lapnys_params(B, H, grid_h * grid_w if N is None else N, d, grid_h, grid_w, pool,
+                         lam, eps, ns_iters, dt, LAPNYS_WHITEN if whiten else 0)
+
+
+def params_for(w) -> lapnys_params:
+    """lapnys_params for a ``lapnys_inputs.Workload``."""
+    return make_params(B=w.B, H=w.H, grid_h=w.grid_h, grid_w=w.grid_w, d=w.d, pool=w.pool, lam=w.lam,
+                       eps=w.eps, ns_iters=w.ns_iters, dtype=w.dtype, whiten=w.whiten)
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if not x.is_contiguous():
+        raise ValueError("tensor arguments must be contiguous")
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ws(ws):
+    if ws is None:
+        return None, 0
+    if isinstance(ws, tuple):
+        return ws
+    return _ptr(ws), ws.numel() * ws.element_size()
+
+
+def _check(code: int, where: str) -> int:
+    if code < 0:
+        raise LapnysError(code, where)
+    return code
+
+
+def lapnys_status_string(code: int) -> str:
+    return _lib.lapnys_status_string(code).decode()
+
+
+def lapnys_landmark_count(params: lapnys_params) -> int:
+    return _check(_lib.lapnys_landmark_count(ctypes.byref(params)), "lapnys_landmark_count")
+
+
+def lapnys_workspace_size(params: lapnys_params) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.lapnys_workspace_size(ctypes.byref(params), ctypes.byref(n)), "lapnys_workspace_size")
+    return n.value
+
+
+def lapnys_forward_ws(q, k, v, out, params: lapnys_params, ws, stream=None) -> None:
+    wp, wn = _ws(ws)
+    _check(_lib.lapnys_forward_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.byref(params), wp, wn,
+                                  _stream(stream)), "lapnys_forward_ws")
+
+
+def lapnys_forward(q, k, v, out, params: lapnys_params, stream=None) -> None:
+    _check(_lib.lapnys_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.byref(params), _stream(stream)),
+           "lapnys_forward")
+
+
+def lapnys_forward_debug(q, k, v, out, params: lapnys_params, ws, dbg: Dict[str, object], stream=None) -> None:
+    """``dbg`` maps lapnys_debug field names to device tensors (missing = not written)."""
+    d = lapnys_debug(*[_ptr(dbg.get(name)) for name in DEBUG_FIELDS])
+    wp, wn = _ws(ws)
+    _check(_lib.lapnys_forward_debug(_ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.byref(params), wp, wn,
+                                     ctypes.byref(d), _stream(stream)), "lapnys_forward_debug")
+
+
+def lapnys_forward_profiled(q, k, v, out, params: lapnys_params, ws, events: Sequence[int], stream=None) -> None:
+    """``events``: 2 * LAPNYS_NUM_STAGES raw hipEvent_t handles (see HipEvents)."""
+    arr = (ctypes.c_void_p * len(events))(*events)
+    wp, wn = _ws(ws)
+    _check(_lib.lapnys_forward_profiled(_ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.byref(params), wp, wn,
+                                        arr, _stream(stream)), "lapnys_forward_profiled")
+
+
+def lapnys_release() -> None:
+    _lib.lapnys_release()
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime (timing events for the profiled form)."""
+
+    def __init__(self, n: int):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                  ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.handles = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self._hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.handles.append(h.value)
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.handles[a], self.handles[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def close(self):
+        for h in self.handles:
+            self._hip.hipEventDestroy(h)
+        self.handles = []

@@ -1,0 +1,147 @@
+"""Shared helpers for the GPU parity tests: upload seeded inputs, run the HIP
+path through the C ABI (debug form, which also returns the intermediates),
+run the oracle on the same values, and compare with the stated tolerances.
+
+Tolerances (per (batch, head) problem):
+  * landmarks: bit-exact (float32 rounding of the float64 window mean taken in
+    a fixed order, on both sides);
+  * output, float32 inputs: normwise max relative error
+    max|O_gpu - O_ref| / max|O_ref| <= 1e-4;
+  * output, bf16 inputs (float32 arithmetic): relative L2 error
+    ||O_gpu - O_ref||_2 / ||O_ref||_2 <= 2e-2, and the float32 bound above
+    is also reported;
+  * Newton-Schulz residual ||W X - I||_F <= 1e-4, evaluated in float64 from the
+    GPU's own float32 W and X.
+Elementwise relative error is not used for O: outputs pass through zero, so
+it is unbounded for a correct float32 result.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from lapnys_inputs import Workload, make_inputs
+
+O_NORMWISE_F32 = 1e-4
+O_REL_L2_BF16 = 2e-2
+NS_RESIDUAL = 1e-4
+
+
+def f32(x):
+    return float(np.float32(x))
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def gpu_available() -> bool:
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+def device_inputs(x, dtype: str):
+    torch = torch_mod()
+
+    def conv(a):
+        if dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    return conv(x.q), conv(x.k), conv(x.v)
+
+
+def run_gpu(w: Workload, x, *, params=None, debug=True, cached=False):
+    """Run the HIP forward on workload ``w`` with inputs ``x``; numpy results."""
+    torch = torch_mod()
+    import laplacian_nystr_approximation_amd as L
+    params = params if params is not None else L.params_for(w)
+    q, k, v = device_inputs(x, w.dtype)
+    out = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device="cuda")
+    res = {}
+    if cached:
+        L.lapnys_forward(q, k, v, out, params)
+        torch.cuda.synchronize()
+    else:
+        ws = torch.empty(L.lapnys_workspace_size(params), dtype=torch.uint8, device="cuda")
+        if debug:
+            P, m = w.P, w.m
+            dbg = {
+                "landmarks": torch.empty((P, m, w.d), device="cuda"),
+                "C_t": torch.empty((P, m, w.N), device="cuda"),
+                "W": torch.empty((P, m, m), device="cuda"),
+                "X": torch.empty((P, m, m), device="cuda"),
+                "BV": torch.empty((P, m, w.d), device="cuda"),
+                "Y": torch.empty((P, m, w.d), device="cuda"),
+                "mu": torch.empty((P, m), device="cuda"),
+                "sigma": torch.empty((P, m), device="cuda"),
+            }
+            L.lapnys_forward_debug(q, k, v, out, params, ws, dbg)
+            res.update({key: t.cpu().numpy() for key, t in dbg.items()})
+        else:
+            L.lapnys_forward_ws(q, k, v, out, params, ws)
+            torch.cuda.synchronize()
+    res["O"] = out.cpu().numpy().reshape(w.P, w.N, w.d)
+    return res
+
+
+def run_oracle(w: Workload, x, problems=None):
+    """Oracle results for the listed problem indices p = b*H + h (default all)."""
+    pairs = None if problems is None else [divmod(p, w.H) for p in problems]
+    r = oracle.forward(x.qf, x.kf, x.vf, grid_h=w.grid_h, grid_w=w.grid_w, pool=w.pool, lam=f32(w.lam),
+                       eps=f32(w.eps), ns_iters=w.ns_iters, whiten=w.whiten, problems=pairs)
+    if problems is None:
+        r = {k: (v.reshape((w.P,) + v.shape[2:]) if isinstance(v, np.ndarray) else v) for k, v in r.items()}
+    return r
+
+
+def o_errors(o_gpu, o_ref):
+    d = o_gpu.astype(np.float64) - o_ref
+    normwise = np.abs(d).max() / max(np.abs(o_ref).max(), 1e-300)
+    rel_l2 = np.linalg.norm(d) / max(np.linalg.norm(o_ref), 1e-300)
+    return normwise, rel_l2
+
+
+def ns_residual(w_gpu, x_gpu):
+    wd = w_gpu.astype(np.float64)
+    xd = x_gpu.astype(np.float64)
+    return np.linalg.norm(wd @ xd - np.eye(wd.shape[0]))
+
+
+def check_problem(w: Workload, gpu, g, ref, r, *, check_ns=True, report=None):
+    """Compare GPU problem index g against oracle entry r; raise AssertionError on failure."""
+    lm_ref = ref["landmarks"][r].astype(np.float32)
+    assert np.array_equal(gpu["landmarks"][g].view(np.uint32), lm_ref.view(np.uint32)), "landmarks not bit-exact"
+    wg = gpu["W"][g]
+    assert np.array_equal(wg, wg.T), "W not bit-symmetric"
+    diag = np.float32(1.0) + np.float32(w.eps)
+    assert np.all(np.diag(wg) == diag), "W diagonal != 1 + eps in float32"
+    assert np.abs(wg - ref["W"][r]).max() <= 2e-5, "W"
+    res = ns_residual(wg, gpu["X"][g])
+    if report is not None:
+        report.setdefault("ns_residual", []).append(res)
+    if check_ns:
+        assert res <= NS_RESIDUAL, f"NS residual {res:.3e}"
+    mu_ref, sg_ref = ref["mu"][r], ref["sigma"][r]
+    assert np.abs(gpu["mu"][g] - mu_ref).max() <= 1e-5 * np.abs(mu_ref).max() + 1e-7, "mu"
+    assert np.abs(gpu["sigma"][g] - sg_ref).max() <= 1e-4 * np.abs(sg_ref).max() + 1e-7, "sigma"
+    ct_ref = ref["C"][r].T
+    assert np.abs(gpu["C_t"][g] - ct_ref).max() <= 1e-5, "C"
+    bv_ref = ref["BV"][r]
+    assert np.abs(gpu["BV"][g] - bv_ref).max() <= 1e-5 * np.abs(bv_ref).max() * 10, "BV"
+    nw, l2 = o_errors(gpu["O"][g], ref["O"][r])
+    if report is not None:
+        report.setdefault("o_normwise", []).append(nw)
+        report.setdefault("o_rel_l2", []).append(l2)
+    if w.dtype == "f32":
+        assert nw <= O_NORMWISE_F32, f"O normwise {nw:.3e}"
+    else:
+        assert l2 <= O_REL_L2_BF16, f"O rel L2 {l2:.3e}"
+
+
+def workload_inputs(w: Workload, seed=None):
+    return make_inputs(w, seed)

@@ -1,0 +1,129 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/lapnys.h declares, and rejects invalid calls with the documented
+status before touching any device (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import laplacian_nystr_approximation_amd as L
+from laplacian_nystr_approximation_amd import lapnys as B
+from lapnys_inputs import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lapnys.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lapnys_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert _declared() == sorted([
+        "lapnys_forward", "lapnys_forward_debug", "lapnys_forward_profiled", "lapnys_forward_ws",
+        "lapnys_landmark_count", "lapnys_release", "lapnys_status_string", "lapnys_workspace_size"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (lapnys_\w+)", nm))
+    assert exported == set(_declared())
+
+
+def test_struct_layout_matches_header():
+    # 7 int32, 2 float, 2 int32, 1 uint32, no padding
+    assert ctypes.sizeof(B.lapnys_params) == 12 * 4
+    assert ctypes.sizeof(B.lapnys_debug) == 8 * ctypes.sizeof(ctypes.c_void_p)
+
+
+def test_status_strings():
+    for code in [0, -1, -2, -3, -4, -5]:
+        assert L.lapnys_status_string(code) not in ("", "unknown status")
+    assert L.lapnys_status_string(-99) == "unknown status"
+
+
+def _p(**kw):
+    base = dict(B=2, H=3, grid_h=14, grid_w=14, d=64, pool=2, lam=4.0, eps=1e-3, ns_iters=20, dtype="bf16")
+    base.update(kw)
+    return L.make_params(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), B.LAPNYS_ERR_INVALID_ARG),
+    (dict(H=-1), B.LAPNYS_ERR_INVALID_ARG),
+    (dict(pool=0), B.LAPNYS_ERR_INVALID_ARG),
+    (dict(lam=0.0), B.LAPNYS_ERR_INVALID_ARG),
+    (dict(lam=float("inf")), B.LAPNYS_ERR_INVALID_ARG),
+    (dict(lam=float("nan")), B.LAPNYS_ERR_INVALID_ARG),
+    (dict(eps=-1e-3), B.LAPNYS_ERR_INVALID_ARG),
+    (dict(ns_iters=-1), B.LAPNYS_ERR_INVALID_ARG),
+    (dict(N=195), B.LAPNYS_ERR_SHAPE),
+    (dict(pool=3), B.LAPNYS_ERR_SHAPE),
+    (dict(d=48), B.LAPNYS_ERR_UNSUPPORTED),
+    (dict(d=128), B.LAPNYS_ERR_UNSUPPORTED),
+    (dict(dtype=7), B.LAPNYS_ERR_UNSUPPORTED),
+    (dict(grid_h=34, grid_w=32, pool=2), B.LAPNYS_ERR_UNSUPPORTED),  # m = 272 > 256
+    (dict(B=300, H=300), B.LAPNYS_ERR_UNSUPPORTED),
+])
+def test_invalid_params_rejected(kw, code):
+    p = _p(**kw)
+    with pytest.raises(L.LapnysError) as e:
+        L.lapnys_workspace_size(p)
+    assert e.value.code == code
+    assert L.library().lapnys_landmark_count(ctypes.byref(p)) == code
+    # The forward entry points validate before any device work; the buffer
+    # arguments are never dereferenced on an error path.
+    fake = 1 << 20
+    rc = L.library().lapnys_forward_ws(fake, fake, fake, fake * 3, ctypes.byref(p), fake * 5, 1 << 30, None)
+    assert rc == code
+    rc = L.library().lapnys_forward(fake, fake, fake, fake * 3, ctypes.byref(p), None)
+    assert rc == code
+
+
+def test_unknown_flag_bits_rejected():
+    p = _p()
+    p.flags = 6
+    assert L.library().lapnys_landmark_count(ctypes.byref(p)) == B.LAPNYS_ERR_INVALID_ARG
+
+
+def test_buffer_checks_before_launch():
+    p = _p()
+    lib = L.library()
+    need = L.lapnys_workspace_size(p)
+    a = 1 << 24
+    q, k, v, out, ws = a, 2 * a, 3 * a, 4 * a, 8 * a
+    # null and misaligned pointers
+    assert lib.lapnys_forward_ws(None, k, v, out, ctypes.byref(p), ws, need, None) == B.LAPNYS_ERR_INVALID_ARG
+    assert lib.lapnys_forward_ws(q + 4, k, v, out, ctypes.byref(p), ws, need, None) == B.LAPNYS_ERR_INVALID_ARG
+    # out overlapping an input
+    assert lib.lapnys_forward_ws(q, k, v, q + 256, ctypes.byref(p), ws, need, None) == B.LAPNYS_ERR_INVALID_ARG
+    # workspace missing, too small, misaligned
+    assert lib.lapnys_forward_ws(q, k, v, out, ctypes.byref(p), None, need, None) == B.LAPNYS_ERR_WORKSPACE
+    assert lib.lapnys_forward_ws(q, k, v, out, ctypes.byref(p), ws, need - 1, None) == B.LAPNYS_ERR_WORKSPACE
+    assert lib.lapnys_forward_ws(q, k, v, out, ctypes.byref(p), ws + 64, need, None) == B.LAPNYS_ERR_WORKSPACE
+    # debug / profiled argument checks
+    assert lib.lapnys_forward_debug(q, k, v, out, ctypes.byref(p), ws, need, None, None) == B.LAPNYS_ERR_INVALID_ARG
+    assert lib.lapnys_forward_profiled(q, k, v, out, ctypes.byref(p), ws, need, None, None) == \
+        B.LAPNYS_ERR_INVALID_ARG
+
+
+def test_landmark_count_and_workspace():
+    for name, w in WORKLOADS.items():
+        p = L.params_for(w)
+        assert L.lapnys_landmark_count(p) == w.m
+        n1 = L.lapnys_workspace_size(p)
+        assert n1 == L.lapnys_workspace_size(p)
+        assert n1 % 256 == 0
+        # at least the landmark-major C buffer
+        assert n1 >= w.P * w.m * w.N * 4
+    # monotone in the token count at fixed landmarks
+    sizes = [L.lapnys_workspace_size(_p(grid_h=g, grid_w=g, pool=g // 8, dtype="f32")) for g in (16, 32, 64, 128)]
+    assert sizes == sorted(sizes)

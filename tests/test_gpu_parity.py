@@ -1,0 +1,147 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs, stage by stage and end to end.  Run on an MI355X with
+``pytest -m gpu``."""
+
+import sys
+
+import numpy as np
+import pytest
+
+from gpu_harness import (NS_RESIDUAL, O_NORMWISE_F32, check_problem, gpu_available, o_errors, run_gpu,
+                         run_oracle, workload_inputs)
+from lapnys_inputs import WORKLOADS, Workload, bf16_bits_to_f32, f32_to_bf16_bits
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="no GPU device visible")]
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+FULL_ORACLE = ["tiny_f32", "stage1_56x56_f32", "stage1_56x56_bf16", "stage2_28x28_bf16", "stage3_14x14_bf16"]
+
+
+@pytest.mark.parametrize("name", FULL_ORACLE)
+def test_workload_parity(name):
+    """Every problem of the workload against the oracle."""
+    w = WORKLOADS[name]
+    _say(f"[parity] {name} P={w.P} N={w.N} d={w.d} m={w.m} {w.dtype}")
+    x = workload_inputs(w)
+    gpu = run_gpu(w, x)
+    ref = run_oracle(w, x)
+    report = {}
+    for p in range(w.P):
+        check_problem(w, gpu, p, ref, p, report=report)
+    _say(f"[parity] {name}: max O normwise {max(report['o_normwise']):.2e}, "
+         f"max rel L2 {max(report['o_rel_l2']):.2e}, max NS residual {max(report['ns_residual']):.2e}")
+
+
+@pytest.mark.parametrize("name", ["sweep_64x64_bf16", "sweep_128x128_bf16", "long_256x256_bf16"])
+def test_long_sequence_parity(name):
+    """m = 256 workloads: landmarks of every problem bit-exact; the full oracle on
+    problem 0 (and the last problem) at full size."""
+    w = WORKLOADS[name]
+    _say(f"[parity] {name} P={w.P} N={w.N} m={w.m}")
+    x = workload_inputs(w)
+    gpu = run_gpu(w, x)
+    sample = [0, w.P - 1]
+    ref = run_oracle(w, x, problems=sample)
+    report = {}
+    # The residual gate is a property of the iteration count: at 256 x 256 with
+    # 24 steps the float64 iteration itself ends near 1e-3 (W's condition
+    # number is ~1.4e3), so only the other two shapes are held to it.
+    gate = name != "long_256x256_bf16"
+    for r, p in enumerate(sample):
+        check_problem(w, gpu, p, ref, r, check_ns=gate, report=report)
+    res_all = [np.linalg.norm(gpu["W"][p].astype(np.float64) @ gpu["X"][p].astype(np.float64) - np.eye(w.m))
+               for p in range(w.P)]
+    _say(f"[parity] {name}: O normwise {max(report['o_normwise']):.2e}, rel L2 {max(report['o_rel_l2']):.2e}, "
+         f"NS residual max over problems {max(res_all):.2e}")
+    if gate:
+        assert max(res_all) <= NS_RESIDUAL
+
+
+def _edge_cases():
+    base = dict(B=1, H=2, lam=4.0, eps=1e-3, ns_iters=20, seed_index=40)
+    cases = [
+        # ragged token tiles and odd landmark counts
+        Workload("ragged_18x14_p2", grid_h=18, grid_w=14, d=64, pool=2, dtype="f32", **base),
+        Workload("ragged_10x30_p5_d32", grid_h=10, grid_w=30, d=32, pool=5, dtype="bf16", **base),
+        # every key a landmark (pool 1)
+        Workload("pool1_7x9", grid_h=7, grid_w=9, d=32, pool=1, dtype="f32", **base),
+        # a single landmark
+        Workload("single_landmark_6x6", grid_h=6, grid_w=6, d=64, pool=6, dtype="f32", **base),
+        # largest landmark count of the in-LDS Newton-Schulz, and the first of the batched one
+        Workload("m64_16x16_p2", grid_h=16, grid_w=16, d=64, pool=2, dtype="bf16", **base),
+        Workload("m81_18x18_p2", grid_h=18, grid_w=18, d=64, pool=2, dtype="f32", **base),
+        Workload("m100_20x20_p2_d32", grid_h=20, grid_w=20, d=32, pool=2, dtype="f32", **base),
+        Workload("m256_16x16_p1", grid_h=16, grid_w=16, d=64, pool=1, dtype="f32",
+                 **{**base, "ns_iters": 40}),
+        # whitening off, zero and one Newton-Schulz steps
+        Workload("nowhiten_14x14", grid_h=14, grid_w=14, d=64, pool=2, dtype="f32", whiten=False, **base),
+        Workload("ns0_14x14", grid_h=14, grid_w=14, d=32, pool=2, dtype="f32", **{**base, "ns_iters": 0}),
+        Workload("ns1_12x12_m36", grid_h=12, grid_w=12, d=64, pool=2, dtype="bf16", **{**base, "ns_iters": 1}),
+        # a few tokens past a whole number of 256-token tiles; 66 landmarks in
+        # blocks of 32, 32 and 2
+        Workload("tail_22x12_p2_m66", grid_h=22, grid_w=12, d=64, pool=2, dtype="bf16", **base),
+        Workload("tail_18x30_p3_m60", grid_h=18, grid_w=30, d=32, pool=3, dtype="f32", **base),
+    ]
+    return cases
+
+
+@pytest.mark.parametrize("w", _edge_cases(), ids=lambda w: w.name)
+def test_edge_case_parity(w):
+    if w.m > 256:
+        pytest.skip("beyond the supported landmark count")
+    _say(f"[edge] {w.name} N={w.N} m={w.m} d={w.d} {w.dtype} whiten={w.whiten} T={w.ns_iters}")
+    x = workload_inputs(w)
+    gpu = run_gpu(w, x)
+    ref = run_oracle(w, x)
+    converged = w.ns_iters >= 20
+    for p in range(w.P):
+        check_problem(w, gpu, p, ref, p, check_ns=converged)
+        if not converged:
+            # Before convergence the output tracks the oracle's X_T, not W^-1.
+            nw, _ = o_errors(gpu["O"][p], ref["O"][p])
+            assert nw <= O_NORMWISE_F32
+
+
+def test_bitwise_repeatable():
+    w = WORKLOADS["stage1_56x56_bf16"]
+    x = workload_inputs(w)
+    a = run_gpu(w, x, debug=False)["O"]
+    b = run_gpu(w, x, debug=False)["O"]
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_cached_workspace_form_matches():
+    w = WORKLOADS["stage2_28x28_bf16"]
+    x = workload_inputs(w)
+    a = run_gpu(w, x, debug=False)["O"]
+    b = run_gpu(w, x, cached=True)["O"]
+    c = run_gpu(w, x, cached=True)["O"]
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert np.array_equal(a.view(np.uint32), c.view(np.uint32))
+
+
+def test_scale_metamorphic_bitwise():
+    """(Q, K, lambda) -> (2Q, 2K, 2 lambda) leaves every float32 step bit-identical."""
+    w = WORKLOADS["stage1_56x56_f32"].with_(B=4)
+    x = workload_inputs(w)
+    a = run_gpu(w, x, debug=False)["O"]
+    x2 = workload_inputs(w)
+    x2.q[...] = x.q * np.float32(2)
+    x2.k[...] = x.k * np.float32(2)
+    b = run_gpu(w.with_(lam=8.0), x2, debug=False)["O"]
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_linear_in_v():
+    w = WORKLOADS["stage2_28x28_bf16"].with_(B=4)
+    x = workload_inputs(w)
+    a = run_gpu(w, x, debug=False)["O"]
+    x2 = workload_inputs(w)
+    x2.v[...] = f32_to_bf16_bits(2 * bf16_bits_to_f32(x.v))  # doubling is exact
+    b = run_gpu(w, x2, debug=False)["O"]
+    assert np.array_equal((2 * a).view(np.uint32), b.view(np.uint32))

@@ -148,7 +148,9 @@ int lapnys_forward_debug(const void* q, const void* k, const void* v, float* out
 /* lapnys_forward_ws that also records stage_events[2*s] before and
  * stage_events[2*s+1] after stage s (LAPNYS_STAGE_*) on the stream that runs
  * that stage, so hipEventElapsedTime gives per-stage device time.
- * stage_events: 2 * LAPNYS_NUM_STAGES events created by the caller. */
+ * stage_events: array of 2 * LAPNYS_NUM_STAGES events created by the caller;
+ * a NULL entry is skipped (record only the stages of interest: every event
+ * record is a command on the stream and costs a little time). */
 int lapnys_forward_profiled(const void* q, const void* k, const void* v, float* out,
                             const lapnys_params* p, void* ws, size_t ws_bytes,
                             hipEvent_t* stage_events, hipStream_t stream);

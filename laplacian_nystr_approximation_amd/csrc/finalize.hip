@@ -1,14 +1,18 @@
 // Reductions between the kernel-matrix stage and the output stage.
 //
+//  * B V = sum over tile groups of the partial products, in group order.
 //  * Whitening statistics (EN page, section 2.B; KO section 2.2): for every
 //    landmark column j of C, the mean and the population standard deviation
-//    over the N tokens of the problem.  The per-tile (sum, squared-deviation
-//    sum) pairs are merged in float64 in tile order with the exact
-//    decomposition M2 = sum_t [M2_t + n_t (mean_t - mean)^2], so the result
-//    is the two-pass statistic, not a one-pass E[c^2] - E[c]^2.
-//  * B V = sum over tile groups of the partial products, in group order.
-//  * Y = X (B V): the Newton-Schulz inverse applied to B V (m x d).
-// Every reduction runs in a fixed order, so results repeat bit for bit.
+//    over the N tokens of the problem.  The per-tile (sum, squared deviations
+//    about the tile mean) pairs are merged in float64, in tile order, with the
+//    exact decomposition M2 = sum_t [M2_t + n_t (mean_t - mean)^2], so the
+//    result is the two-pass statistic, not a one-pass E[c^2] - E[c]^2.
+//
+// One lane per B V element: the launch is wide (every partial is read once,
+// in parallel across the chip) and each lane keeps up to 16 groups' loads in
+// flight before its ordered adds.  One extra workgroup per problem produces
+// the statistics, one lane per landmark.  Every reduction has a fixed order,
+// so results repeat bit for bit.
 #include <math.h>
 
 #include "lapnys_internal.hpp"
@@ -17,22 +21,35 @@ namespace lapnys {
 
 namespace {
 
-// One lane per (problem, landmark, feature): B V sum; feature-0 lanes also
-// produce the landmark's mean, sigma and 1/sigma.
+constexpr int kChunk = 16;
+
 __global__ __launch_bounds__(256) void reduce_kernel(const float2* __restrict__ stats,
                                                      const float* __restrict__ bvpart, float* __restrict__ bv,
                                                      float* __restrict__ mu, float* __restrict__ sigma,
-                                                     float* __restrict__ rs, int N, int m, int D, int ntiles,
-                                                     int tt, int groups, int whiten) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+                                                     float* __restrict__ rs, int N, int m, int D, int ntiles, int tt,
+                                                     int groups, int whiten) {
   const int p = blockIdx.y;
-  if (e >= m * D) return;
-  const int j = e / D, t = e % D;
-  const float* src = bvpart + (size_t)p * groups * m * D + (size_t)j * D + t;
-  float acc = 0.f;
-  for (int g = 0; g < groups; ++g) acc += src[(size_t)g * m * D];
-  bv[((size_t)p * m + j) * D + t] = acc;
-  if (t != 0) return;
+  const int md = m * D;
+  const int nbv = (md + 255) / 256;
+  if ((int)blockIdx.x < nbv) {
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= md) return;
+    const float* src = bvpart + (size_t)p * groups * md + e;
+    float sum = 0.f;
+    for (int g0 = 0; g0 < groups; g0 += kChunk) {
+      float v[kChunk];
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) v[u] = (g0 + u < groups) ? src[(size_t)(g0 + u) * md] : 0.f;
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u)
+        if (g0 + u < groups) sum += v[u];
+    }
+    bv[(size_t)p * md + e] = sum;
+    return;
+  }
+
+  const int j = threadIdx.x;
+  if (j >= m) return;
   if (!whiten) {
     mu[p * m + j] = 0.f;
     sigma[p * m + j] = 1.f;
@@ -41,14 +58,28 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float2* __restrict__ 
   }
   const float2* st = stats + (size_t)p * ntiles * m + j;
   double total = 0.0;
-  for (int i = 0; i < ntiles; ++i) total += (double)st[(size_t)i * m].x;
+  for (int i0 = 0; i0 < ntiles; i0 += kChunk) {
+    float v[kChunk];
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) v[u] = (i0 + u < ntiles) ? st[(size_t)(i0 + u) * m].x : 0.f;
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u)
+      if (i0 + u < ntiles) total += (double)v[u];
+  }
   const double mean = total / (double)N;
   double m2 = 0.0;
-  for (int i = 0; i < ntiles; ++i) {
-    const float2 sv = st[(size_t)i * m];
-    const int n = min(tt, N - i * tt);
-    const double dm = (double)sv.x / (double)n - mean;
-    m2 += (double)sv.y + (double)n * dm * dm;
+  for (int i0 = 0; i0 < ntiles; i0 += kChunk) {
+    float2 v[kChunk];
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) v[u] = (i0 + u < ntiles) ? st[(size_t)(i0 + u) * m] : make_float2(0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      if (i0 + u < ntiles) {
+        const int n = min(tt, N - (i0 + u) * tt);
+        const double dm = (double)v[u].x / (double)n - mean;
+        m2 += (double)v[u].y + (double)n * dm * dm;
+      }
+    }
   }
   const double sd = sqrt(m2 / (double)N);
   mu[p * m + j] = (float)mean;
@@ -56,29 +87,13 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float2* __restrict__ 
   rs[p * m + j] = sd > 0.0 ? (float)(1.0 / sd) : 0.f;
 }
 
-// Y[p][a][t] = sum_{b < m} X[p][a][b] * BV[p][b][t], X stored with row stride mp.
-__global__ __launch_bounds__(256) void y_kernel(const float* __restrict__ x, const float* __restrict__ bv,
-                                                float* __restrict__ y, int m, int mp, int D) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  const int p = blockIdx.y;
-  if (e >= m * D) return;
-  const int a = e / D, t = e % D;
-  const float* xr = x + ((size_t)p * mp + a) * mp;
-  const float* bc = bv + (size_t)p * m * D + t;
-  float acc = 0.f;
-  for (int b = 0; b < m; ++b) acc = fmaf(xr[b], bc[(size_t)b * D], acc);
-  y[((size_t)p * m + a) * D + t] = acc;
-}
-
 }  // namespace
 
-hipError_t launch_finalize(const Plan& pl, const float* stats, const float* bvpart, const float* x, float* bv,
-                           float* mu, float* sigma, float* rs, float* y, hipStream_t s) {
-  const int n = pl.m * pl.d;
-  const dim3 grid((n + 255) / 256, pl.P);
-  hipLaunchKernelGGL(reduce_kernel, grid, dim3(256), 0, s, reinterpret_cast<const float2*>(stats), bvpart, bv, mu,
-                     sigma, rs, pl.N, pl.m, pl.d, pl.ntiles, pl.tt, pl.groups, pl.whiten ? 1 : 0);
-  hipLaunchKernelGGL(y_kernel, grid, dim3(256), 0, s, x, bv, y, pl.m, pl.mp, pl.d);
+hipError_t launch_reduce(const Plan& pl, const Work& w, hipStream_t s) {
+  const int nbv = (pl.m * pl.d + 255) / 256;
+  hipLaunchKernelGGL(reduce_kernel, dim3(nbv + 1, pl.P), dim3(256), 0, s, reinterpret_cast<const float2*>(w.stats),
+                     w.bvpart, w.bv, w.mu, w.sigma, w.rs, pl.N, pl.m, pl.d, pl.ntiles, pl.tt, pl.groups,
+                     pl.whiten ? 1 : 0);
   return hipGetLastError();
 }
 

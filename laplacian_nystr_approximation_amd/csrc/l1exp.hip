@@ -7,17 +7,18 @@
 //     problem), for the output stage;
 //   * per token tile and landmark: the sum of C and the sum of squared
 //     deviations from the tile mean (whitening statistics, EN section 2.B);
-//   * B V partial products over the tile, on fp32 MFMA.  B itself never
-//     leaves the chip.
+//   * B V partial products over each tile group, on fp32 MFMA.  B itself
+//     never leaves the chip.
+// The partials are reduced by the finalize stage (finalize.hip).
 //
 // Layout of the work: one lane per token.  A workgroup of 256 lanes takes a
-// tile of 256 consecutive tokens of one problem and a block of landmarks whose
-// K~ rows sit in LDS; every landmark value is read by a wave-uniform LDS
-// address (a broadcast), so the inner loop is pure VALU: one subtract and one
-// add with an |.| source modifier per (token, landmark, feature).  This stage
-// is not a dense contraction; it runs on the vector ALUs, not on MFMA.
+// tile of 256 consecutive tokens of one problem and a block of landmarks; every
+// landmark value is wave-uniform and comes from a scalar register, so the
+// inner loop is pure VALU: one subtract and one add with an |.| source
+// modifier per (token, landmark, feature).  This stage is not a dense
+// contraction; it runs on the vector ALUs, not on MFMA.
 //
-// LDS per workgroup: K~ block [lb][D] and a tile buffer [lb][256 + 2] that
+// LDS per workgroup: a tile buffer [lb + 1][256 + 2] (the extra row is zero) that
 // holds C, then B, transposed (landmark-major) so that the statistics pass and
 // the C store are coalesced and the MFMA reads B columns without bank
 // conflicts.
@@ -28,69 +29,86 @@ namespace lapnys {
 namespace {
 
 constexpr int kTT = 256;        // tokens per tile = lanes per workgroup
-constexpr int kTP = kTT + 2;    // tile buffer row stride (floats)
+constexpr int kTP = kTT + 4;    // tile buffer row stride (floats; rows stay 16-byte aligned)
 constexpr int kNW = kTT / 64;   // wavefronts per workgroup
 
+// A token row held as raw 16-byte words: issued early, widened later.
+template <typename T, int D>
+struct RawRow {
+  static constexpr int kWords = D * (int)sizeof(T) / 16;
+  uint4 w[kWords];
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void issue_row(const T* __restrict__ src, bool valid, RawRow<T, D>& r) {
+  const uint4* s4 = reinterpret_cast<const uint4*>(src);
+#pragma unroll
+  for (int c = 0; c < RawRow<T, D>::kWords; ++c) r.w[c] = valid ? s4[c] : make_uint4(0u, 0u, 0u, 0u);
+}
+
 template <int D>
-__device__ __forceinline__ void load_row(const float* __restrict__ src, bool valid, float (&x)[D]) {
-  if (valid) {
-    const float4* s4 = reinterpret_cast<const float4*>(src);
+__device__ __forceinline__ void widen_row(const RawRow<float, D>& r, float (&x)[D]) {
 #pragma unroll
-    for (int c = 0; c < D / 4; ++c) {
-      const float4 u = s4[c];
-      x[4 * c + 0] = u.x;
-      x[4 * c + 1] = u.y;
-      x[4 * c + 2] = u.z;
-      x[4 * c + 3] = u.w;
-    }
-  } else {
-#pragma unroll
-    for (int t = 0; t < D; ++t) x[t] = 0.f;
+  for (int c = 0; c < D / 4; ++c) {
+    x[4 * c + 0] = __uint_as_float(r.w[c].x);
+    x[4 * c + 1] = __uint_as_float(r.w[c].y);
+    x[4 * c + 2] = __uint_as_float(r.w[c].z);
+    x[4 * c + 3] = __uint_as_float(r.w[c].w);
   }
 }
 
 template <int D>
-__device__ __forceinline__ void load_row(const uint16_t* __restrict__ src, bool valid, float (&x)[D]) {
-  if (valid) {
-    const uint4* s4 = reinterpret_cast<const uint4*>(src);
+__device__ __forceinline__ void widen_row(const RawRow<uint16_t, D>& r, float (&x)[D]) {
 #pragma unroll
-    for (int c = 0; c < D / 8; ++c) {
-      const uint4 u = s4[c];
-      const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+  for (int c = 0; c < D / 8; ++c) {
+    const uint32_t w4[4] = {r.w[c].x, r.w[c].y, r.w[c].z, r.w[c].w};
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        x[8 * c + 2 * h + 0] = __uint_as_float(w4[h] << 16);
-        x[8 * c + 2 * h + 1] = __uint_as_float(w4[h] & 0xffff0000u);
-      }
+    for (int h = 0; h < 4; ++h) {
+      x[8 * c + 2 * h + 0] = __uint_as_float(w4[h] << 16);
+      x[8 * c + 2 * h + 1] = __uint_as_float(w4[h] & 0xffff0000u);
     }
-  } else {
-#pragma unroll
-    for (int t = 0; t < D; ++t) x[t] = 0.f;
   }
 }
 
-// tl[j][col] = exp2(scale * sum_t |x[t] - kl[j][t]|) for the lb landmarks of the
-// block (0 for a lane past the last token).  Two partial sums per landmark
-// (even / odd features) and four landmarks at a time give eight independent
-// add chains.  The K~ values are broadcast-read from LDS one 4-feature chunk
-// ahead of their use (double buffer); the compiler barriers keep the
-// compiler from hoisting every load of the unrolled loop, which would cost
-// more registers than the loop has.
+// Half of the V operand of the B V MFMA for one tile, per lane:
+// V[t0 + 64 lk + s][col] for the kTT/8 steps s of half h (s in [32h, 32h+32)).
+// (Step s of lane group lk takes token 64 lk + s of the tile: every token is
+// summed exactly once, and one lane's B values for four consecutive steps are
+// contiguous in LDS.)  Tokens past N read the last token's row (their B column
+// is zero).  Each half is issued well before its MFMAs.
+template <typename T, int D>
+struct VHalf {
+  T w[kTT / 8];
+  __device__ __forceinline__ void issue(const T* __restrict__ vcol, int t0, int lk, int h, int tok_last) {
+#pragma unroll
+    for (int i = 0; i < kTT / 8; ++i) w[i] = vcol[min(t0 + 64 * lk + 32 * h + i, tok_last) * D];
+  }
+  __device__ __forceinline__ float get(int i) const { return widen(w[i]); }
+};
+
+// tl[j][col] = exp2(scale * sum_t |x[t] - kg[j][t]|) for the lb landmarks of the
+// block (0 for a lane past the last token).  kg points at the block's K~ rows
+// in global memory; every address is wave-uniform, so the values arrive by
+// scalar loads into SGPRs and feed the VALU directly (no LDS traffic, no VGPR
+// copies).  Two partial sums per landmark (even / odd features) and four
+// landmarks at a time give eight independent add chains.  The landmark values
+// are loaded one 4-feature chunk ahead of their use (double buffer); the
+// compiler barriers keep the loads and adds in that shape.
 template <int D>
-__device__ __forceinline__ void kernel_row(const float (&x)[D], const float* kl, int lb, float scale,
+__device__ __forceinline__ void kernel_row(const float (&x)[D], const float* __restrict__ kg, int lb, float scale,
                                            float* __restrict__ tl, int col, bool valid) {
   int j = 0;
   for (; j + 4 <= lb; j += 4) {
     float sa[4] = {0.f, 0.f, 0.f, 0.f}, sb[4] = {0.f, 0.f, 0.f, 0.f};
     float4 kv[2][4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) kv[0][u] = *reinterpret_cast<const float4*>(&kl[(j + u) * D]);
+    for (int u = 0; u < 4; ++u) kv[0][u] = *reinterpret_cast<const float4*>(&kg[(j + u) * D]);
 #pragma unroll
     for (int c = 0; c < D / 4; ++c) {
       const int cur = c & 1;
       if (c + 1 < D / 4) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) kv[cur ^ 1][u] = *reinterpret_cast<const float4*>(&kl[(j + u) * D + 4 * (c + 1)]);
+        for (int u = 0; u < 4; ++u) kv[cur ^ 1][u] = *reinterpret_cast<const float4*>(&kg[(j + u) * D + 4 * (c + 1)]);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -111,7 +129,7 @@ __device__ __forceinline__ void kernel_row(const float (&x)[D], const float* kl,
     float sa = 0.f, sb = 0.f;
 #pragma unroll
     for (int t = 0; t < D; t += 4) {
-      const float4 kv = *reinterpret_cast<const float4*>(&kl[j * D + t]);
+      const float4 kv = *reinterpret_cast<const float4*>(&kg[j * D + t]);
       sa += fabsf(x[t + 0] - kv.x);
       sb += fabsf(x[t + 1] - kv.y);
       sa += fabsf(x[t + 2] - kv.z);
@@ -121,42 +139,54 @@ __device__ __forceinline__ void kernel_row(const float (&x)[D], const float* kl,
   }
 }
 
-// Grid: (landmark block, tile group, problem).  Dynamic LDS: lb*D + lb*kTP floats.
-template <typename T, int D>
+// Grid: (landmark block, tile group, problem).  LBB = 16-row blocks per
+// landmark block (lb rounded up to 16, over 16).  Dynamic LDS:
+// (lb + 1) * kTP floats.
+template <typename T, int D, int LBB>
 __global__ __launch_bounds__(kTT) void l1exp_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                     const T* __restrict__ v, const float* __restrict__ kt,
                                                     float* __restrict__ ct, float2* __restrict__ stats,
                                                     float* __restrict__ bvpart, int N, int m, int lbmax, int ntiles,
                                                     int tpg, int groups, float scale) {
-  extern __shared__ float4 lds4[];
-  float* kl = reinterpret_cast<float*>(lds4);  // [lb][D]
-  float* tl = kl + lbmax * D;                   // [lb][kTP]
+  extern __shared__ float tl[];  // [lb + 1][kTP]; row lb stays zero
 
   const int jb = blockIdx.x, g = blockIdx.y, p = blockIdx.z;
   const int j0 = jb * lbmax;
   const int lb = min(lbmax, m - j0);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
-  const float4* ktp4 = reinterpret_cast<const float4*>(kt + ((size_t)p * m + j0) * D);
-  for (int e = tid; e < lb * D / 4; e += kTT) lds4[e] = ktp4[e];
+  const float* kg = kt + ((size_t)p * m + j0) * D;  // this block's K~ rows
+  for (int e = lb * kTP + tid; e < (lb + 1) * kTP; e += kTT) tl[e] = 0.f;
+  const int li = lane & 15, lk = lane >> 4;
 
-  // B V output blocks (16 x 16) of this wavefront: rows are landmarks of the
-  // block (up to 64, four 16-row blocks), columns are features (D/16 blocks).
+  // B V output blocks (16 x 16) of this wavefront: one 16-feature column block
+  // bt0 and BIW of the LBB 16-row landmark blocks, starting at bi0.  When the
+  // row blocks do not split evenly, a wavefront's last block may lie past
+  // LBB: it reads a valid (zero-padded) row block and is not stored, so every
+  // MFMA issues unconditionally.
   constexpr int DB = D / 16;
-  constexpr int BTW = (kNW <= DB) ? DB / kNW : 1;
-  constexpr int BIW = (kNW <= DB) ? 4 : 4 / (kNW / DB);
-  const int bt0 = (kNW <= DB) ? w * BTW : (w % DB);
-  const int bi0 = (kNW <= DB) ? 0 : (w / DB) * BIW;
-  f32x4 acc[BIW][BTW];
+  static_assert(kNW % DB == 0, "wavefronts must cover the feature blocks");
+  constexpr int SPLIT = kNW / DB;
+  constexpr int BIW = (LBB + SPLIT - 1) / SPLIT;
+  const int bt0 = w % DB;
+  const int bi0 = (w / DB) * BIW;
+  f32x4 acc[BIW];
 #pragma unroll
-  for (int a = 0; a < BIW; ++a)
-#pragma unroll
-    for (int b = 0; b < BTW; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int a = 0; a < BIW; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const size_t prob = (size_t)p * N * D;
   const int tile_begin = g * tpg;
   const int tile_end = min(ntiles, tile_begin + tpg);
+  // Lane li of row block bi reads landmark row 16 bi + li, or the zero row lb
+  // past the block's landmarks.
+  const float* arow[BIW];
+#pragma unroll
+  for (int a = 0; a < BIW; ++a) arow[a] = tl + min(16 * min(bi0 + a, LBB - 1) + li, lb) * kTP + 64 * lk;
+  const T* vcol = v + prob + 16 * bt0 + li;
+  const int tok_last = N - 1;
+
   float x[D];
+  RawRow<T, D> raw;
   for (int tile = tile_begin; tile < tile_end; ++tile) {
     const int t0 = tile * kTT;
     const int nvalid = min(kTT, N - t0);
@@ -164,10 +194,19 @@ __global__ __launch_bounds__(kTT) void l1exp_kernel(const T* __restrict__ q, con
     const size_t row = prob + (size_t)(t0 + (valid ? tid : 0)) * D;
 
     // ---- C = k(Q, K~) ----
-    load_row<D>(q + row, valid, x);
-    __syncthreads();  // K~ staged (first tile); tile buffer free (later tiles)
-    kernel_row<D>(x, kl, lb, scale, tl, tid, valid);
+    issue_row<T, D>(q + row, valid, raw);
+    widen_row<D>(raw, x);
+    __syncthreads();  // tile buffer free (previous tile's MFMA reads done)
+    kernel_row<D>(x, kg, lb, scale, tl, tid, valid);
     __syncthreads();
+
+    // The key row and this lane's V operands are issued now and arrive while
+    // the statistics pass runs.
+    issue_row<T, D>(k + row, valid, raw);
+    VHalf<T, D> v0;
+    v0.issue(vcol, t0, lk, 0, tok_last);
+
+    // ---- column statistics of C over the tile, and the C^T store ----
     for (int j = w; j < lb; j += kNW) {
       float vals[kTT / 64];
       float s = 0.f;
@@ -177,7 +216,7 @@ __global__ __launch_bounds__(kTT) void l1exp_kernel(const T* __restrict__ q, con
         vals[c] = tl[j * kTP + col];
         if (col < nvalid) s += vals[c];
       }
-      s = wave_sum(s);
+      s = wave_sum_dpp(s);
       const float mean = s / (float)nvalid;
       float m2 = 0.f;
 #pragma unroll
@@ -188,7 +227,7 @@ __global__ __launch_bounds__(kTT) void l1exp_kernel(const T* __restrict__ q, con
           m2 += dv * dv;
         }
       }
-      m2 = wave_sum(m2);
+      m2 = wave_sum_dpp(m2);
       if (lane == 0) stats[((size_t)p * ntiles + tile) * m + j0 + j] = make_float2(s, m2);
       float* crow = ct + ((size_t)p * m + j0 + j) * N + t0;
 #pragma unroll
@@ -199,79 +238,90 @@ __global__ __launch_bounds__(kTT) void l1exp_kernel(const T* __restrict__ q, con
     }
 
     // ---- B = k(K~, K), kept on chip ----
-    load_row<D>(k + row, valid, x);
+    widen_row<D>(raw, x);
     __syncthreads();  // statistics pass done with the tile buffer
-    kernel_row<D>(x, kl, lb, scale, tl, tid, valid);
+    kernel_row<D>(x, kg, lb, scale, tl, tid, valid);
     __syncthreads();
 
     // ---- B V partial: acc[landmark][feature] += sum over the tile's tokens ----
     // fp32 MFMA 16x16x4: lane l supplies A[l%16][l/16] = B[landmark][token] and
-    // B[l/16][l%16] = V[token][feature]; four tokens per step.
-    const int li = lane & 15, lk = lane >> 4;
-#pragma unroll 8
-    for (int s4 = 0; s4 < kTT / 4; ++s4) {
-      const int tk = 4 * s4 + lk;
-      const int tok = t0 + tk;
-      float bv[BTW];
+    // B[l/16][l%16] = V[token][feature], token = 64 (l/16) + step.  A lane's B
+    // values for four steps are one 16-byte LDS read; the first half of V is
+    // already in registers and the second half lands during the first half's
+    // MFMAs; tile-buffer rows past the block's landmarks are zero.
+    VHalf<T, D> v1;
+    v1.issue(vcol, t0, lk, 1, tok_last);
 #pragma unroll
-      for (int b = 0; b < BTW; ++b)
-        bv[b] = (tok < N) ? widen(v[prob + (size_t)tok * D + 16 * (bt0 + b) + li]) : 0.f;
+    for (int h = 0; h < 2; ++h) {
+      const VHalf<T, D>& vh = h ? v1 : v0;
 #pragma unroll
-      for (int a = 0; a < BIW; ++a) {
-        const int r0 = 16 * (bi0 + a);
-        if (r0 < lb) {
-          const float av = (r0 + li < lb) ? tl[(r0 + li) * kTP + tk] : 0.f;
+      for (int i = 0; i < kTT / 8; i += 4) {
+        float4 av[BIW];
 #pragma unroll
-          for (int b = 0; b < BTW; ++b)
-            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv[b], acc[a][b], 0, 0, 0);
+        for (int a = 0; a < BIW; ++a) av[a] = *reinterpret_cast<const float4*>(arow[a] + 32 * h + i);
+#pragma unroll
+        for (int a = 0; a < BIW; ++a) {
+          acc[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a].x, vh.get(i + 0), acc[a], 0, 0, 0);
+          acc[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a].y, vh.get(i + 1), acc[a], 0, 0, 0);
+          acc[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a].z, vh.get(i + 2), acc[a], 0, 0, 0);
+          acc[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a].w, vh.get(i + 3), acc[a], 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
 
   // Partial B V of this tile group: rows j0 + [0, lb) of bvpart[p][g].
   float* bvp = bvpart + ((size_t)p * groups + g) * m * D;
-  const int li = lane & 15, lk = lane >> 4;
 #pragma unroll
   for (int a = 0; a < BIW; ++a) {
     const int r0 = 16 * (bi0 + a);
-    if (r0 >= lb) continue;
+    if (bi0 + a >= LBB) continue;
 #pragma unroll
-    for (int b = 0; b < BTW; ++b)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rr = r0 + 4 * lk + r;
-        if (rr < lb) bvp[(size_t)(j0 + rr) * D + 16 * (bt0 + b) + li] = acc[a][b][r];
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int rr = r0 + 4 * lk + r;
+      if (rr < lb) bvp[(size_t)(j0 + rr) * D + 16 * bt0 + li] = acc[a][r];
+    }
   }
+
 }
 
-template <typename T, int D>
-hipError_t launch_typed(const Plan& pl, const void* q, const void* k, const void* v, const float* kt, float* ct,
-                        float* stats, float* bvpart, hipStream_t s) {
+template <typename T, int D, int LBB>
+hipError_t launch_lbb(const Plan& pl, const void* q, const void* k, const void* v, const Work& w, hipStream_t s) {
   const int lbmax = pl.lb;
-  const size_t shmem = (size_t)(lbmax * D + lbmax * kTP) * sizeof(float);
-  auto kern = l1exp_kernel<T, D>;
+  const size_t shmem = (size_t)(lbmax + 1) * kTP * sizeof(float);
+  auto kern = l1exp_kernel<T, D, LBB>;
   if (shmem > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(kern, dim3(pl.jblocks, pl.groups, pl.P), dim3(kTT), shmem, s, (const T*)q, (const T*)k,
-                     (const T*)v, kt, ct, reinterpret_cast<float2*>(stats), bvpart, pl.N, pl.m, lbmax, pl.ntiles,
-                     pl.tpg, pl.groups, pl.scale);
+                     (const T*)v, w.kt, w.ct, reinterpret_cast<float2*>(w.stats), w.bvpart, pl.N, pl.m, lbmax,
+                     pl.ntiles, pl.tpg, pl.groups, pl.scale);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_typed(const Plan& pl, const void* q, const void* k, const void* v, const Work& w,
+                        hipStream_t s) {
+  switch ((pl.lb + 15) / 16) {
+    case 1: return launch_lbb<T, D, 1>(pl, q, k, v, w, s);
+    case 2: return launch_lbb<T, D, 2>(pl, q, k, v, w, s);
+    case 3: return launch_lbb<T, D, 3>(pl, q, k, v, w, s);
+    default: return launch_lbb<T, D, 4>(pl, q, k, v, w, s);
+  }
 }
 
 }  // namespace
 
-hipError_t launch_l1exp(const Plan& pl, const void* q, const void* k, const void* v, const float* kt, float* ct,
-                        float* stats, float* bvpart, hipStream_t s) {
+hipError_t launch_l1exp(const Plan& pl, const void* q, const void* k, const void* v, const Work& w,
+                        hipStream_t s) {
   if (pl.dtype == 1) {
-    if (pl.d == 64) return launch_typed<uint16_t, 64>(pl, q, k, v, kt, ct, stats, bvpart, s);
-    return launch_typed<uint16_t, 32>(pl, q, k, v, kt, ct, stats, bvpart, s);
+    if (pl.d == 64) return launch_typed<uint16_t, 64>(pl, q, k, v, w, s);
+    return launch_typed<uint16_t, 32>(pl, q, k, v, w, s);
   }
-  if (pl.d == 64) return launch_typed<float, 64>(pl, q, k, v, kt, ct, stats, bvpart, s);
-  return launch_typed<float, 32>(pl, q, k, v, kt, ct, stats, bvpart, s);
+  if (pl.d == 64) return launch_typed<float, 64>(pl, q, k, v, w, s);
+  return launch_typed<float, 32>(pl, q, k, v, w, s);
 }
 
 }  // namespace lapnys

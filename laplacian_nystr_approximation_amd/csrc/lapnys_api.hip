@@ -2,12 +2,16 @@
 // the per-call plan and workspace layout, the stage sequence, the
 // library-owned workspace of lapnys_forward, and the debug/profiled forms.
 //
-// Stage sequence on the caller's stream (no host synchronisation):
-//   pool      K -> K~                                  (pool.hip)
-//   ns        K~ -> W, X = NS inverse of W             (ns.hip)
-//   kernel    Q, K, V, K~ -> C^T, tile statistics, B V partials (l1exp.hip)
-//   finalize  statistics -> mu, sigma; partials -> B V; Y = X (B V) (finalize.hip)
-//   output    O = whiten(C) Y                          (output.hip)
+// Stage sequence (no host synchronisation):
+//   pool      K -> K~                                           caller's stream
+//   ns        K~ -> W, X = NS inverse of W                      side stream (forked)
+//   kernel    Q, K, V, K~ -> C^T, tile statistics, B V partials caller's stream
+//   finalize  partials -> mu, sigma, B V; for m > 64 also
+//             Y = X (B V) on a tile GEMM (after the join)       caller's stream
+//   output    Y = X (B V) for m <= 64, then O = whiten(C) Y     caller's stream
+// The Newton-Schulz stage depends only on the landmarks, so it runs on a
+// library-owned stream of the device (default priority) concurrently with the
+// kernel-matrix stage and joins before the stages that need X.
 #include <math.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -132,52 +136,87 @@ int check_buffers(const void* q, const void* k, const void* v, const float* out,
   return LAPNYS_OK;
 }
 
-struct Buffers {
-  float *kt, *w, *x, *x2, *pm, *ct, *stats, *bvpart, *bv, *mu, *sigma, *rs, *y;
-  float* x_final;
-};
-
-Buffers carve(const Plan& pl, void* ws) {
+lapnys::Work carve(const Plan& pl, void* ws) {
   char* b = (char*)ws;
-  Buffers B;
-  B.kt = (float*)(b + pl.off_kt);
-  B.w = (float*)(b + pl.off_w);
-  B.x = (float*)(b + pl.off_x);
-  B.x2 = (float*)(b + pl.off_x2);
-  B.pm = (float*)(b + pl.off_pm);
-  B.ct = (float*)(b + pl.off_ct);
-  B.stats = (float*)(b + pl.off_stats);
-  B.bvpart = (float*)(b + pl.off_bvpart);
-  B.bv = (float*)(b + pl.off_bv);
-  B.mu = (float*)(b + pl.off_mu);
-  B.sigma = (float*)(b + pl.off_sigma);
-  B.rs = (float*)(b + pl.off_rs);
-  B.y = (float*)(b + pl.off_y);
-  B.x_final = B.x;
-  return B;
+  lapnys::Work W;
+  W.kt = (float*)(b + pl.off_kt);
+  W.w = (float*)(b + pl.off_w);
+  W.x = (float*)(b + pl.off_x);
+  W.x2 = (float*)(b + pl.off_x2);
+  W.pm = (float*)(b + pl.off_pm);
+  W.ct = (float*)(b + pl.off_ct);
+  W.stats = (float*)(b + pl.off_stats);
+  W.bvpart = (float*)(b + pl.off_bvpart);
+  W.bv = (float*)(b + pl.off_bv);
+  W.mu = (float*)(b + pl.off_mu);
+  W.sigma = (float*)(b + pl.off_sigma);
+  W.rs = (float*)(b + pl.off_rs);
+  W.y = (float*)(b + pl.off_y);
+  W.x_final = W.x;
+  return W;
 }
 
-int run(const Plan& pl, const void* q, const void* k, const void* v, float* out, Buffers& B, hipEvent_t* ev,
+// Per-device side stream and the fork/join events, created on first use.
+struct DeviceCtx {
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_ctx_mu;  // also serialises the fork/join sequence of concurrent callers
+std::vector<DeviceCtx> g_ctx;
+
+int device_ctx(DeviceCtx** out) {
+  int dev = 0;
+  if (!ok(hipGetDevice(&dev), "hipGetDevice") || dev < 0) return LAPNYS_ERR_HIP;
+  if ((int)g_ctx.size() <= dev) g_ctx.resize(dev + 1);
+  DeviceCtx& c = g_ctx[dev];
+  if (!c.side) {
+    if (!ok(hipStreamCreateWithFlags(&c.side, hipStreamNonBlocking), "hipStreamCreateWithFlags")) {
+      c.side = nullptr;
+      return LAPNYS_ERR_HIP;
+    }
+    if (!ok(hipEventCreateWithFlags(&c.fork, hipEventDisableTiming), "hipEventCreateWithFlags") ||
+        !ok(hipEventCreateWithFlags(&c.join, hipEventDisableTiming), "hipEventCreateWithFlags"))
+      return LAPNYS_ERR_HIP;
+  }
+  *out = &c;
+  return LAPNYS_OK;
+}
+
+int run(const Plan& pl, const void* q, const void* k, const void* v, float* out, lapnys::Work& W, hipEvent_t* ev,
         hipStream_t s) {
+  std::lock_guard<std::mutex> lock(g_ctx_mu);
+  DeviceCtx* dc = nullptr;
+  const int st = device_ctx(&dc);
+  if (st != LAPNYS_OK) return st;
+  hipStream_t side = dc->side;
   // An error left by an earlier, unrelated runtime call would otherwise be
   // reported by the first launch check below.
   (void)hipGetLastError();
-  auto mark = [&](int idx) { return !ev || ok(hipEventRecord(ev[idx], s), "hipEventRecord"); };
-  if (!mark(2 * LAPNYS_STAGE_POOL)) return LAPNYS_ERR_HIP;
-  if (!ok(lapnys::launch_pool(pl, k, B.kt, s), "pool launch")) return LAPNYS_ERR_HIP;
-  if (!mark(2 * LAPNYS_STAGE_POOL + 1) || !mark(2 * LAPNYS_STAGE_NS)) return LAPNYS_ERR_HIP;
-  if (!ok(lapnys::launch_ns(pl, B.kt, B.w, B.x, B.x2, B.pm, &B.x_final, s), "Newton-Schulz launch"))
+  auto mark = [&](int idx, hipStream_t on) {
+    return !ev || !ev[idx] || ok(hipEventRecord(ev[idx], on), "hipEventRecord");
+  };
+  if (!mark(2 * LAPNYS_STAGE_POOL, s)) return LAPNYS_ERR_HIP;
+  if (!ok(lapnys::launch_pool(pl, k, W, s), "pool launch")) return LAPNYS_ERR_HIP;
+  if (!mark(2 * LAPNYS_STAGE_POOL + 1, s)) return LAPNYS_ERR_HIP;
+  // fork: Newton-Schulz on the side stream once the landmarks exist
+  if (!ok(hipEventRecord(dc->fork, s), "hipEventRecord") || !ok(hipStreamWaitEvent(side, dc->fork, 0), "hipStreamWaitEvent"))
     return LAPNYS_ERR_HIP;
-  if (!mark(2 * LAPNYS_STAGE_NS + 1) || !mark(2 * LAPNYS_STAGE_KERNEL)) return LAPNYS_ERR_HIP;
-  if (!ok(lapnys::launch_l1exp(pl, q, k, v, B.kt, B.ct, B.stats, B.bvpart, s), "kernel-matrix launch"))
-    return LAPNYS_ERR_HIP;
-  if (!mark(2 * LAPNYS_STAGE_KERNEL + 1) || !mark(2 * LAPNYS_STAGE_FINALIZE)) return LAPNYS_ERR_HIP;
-  if (!ok(lapnys::launch_finalize(pl, B.stats, B.bvpart, B.x_final, B.bv, B.mu, B.sigma, B.rs, B.y, s),
-          "finalize launch"))
-    return LAPNYS_ERR_HIP;
-  if (!mark(2 * LAPNYS_STAGE_FINALIZE + 1) || !mark(2 * LAPNYS_STAGE_OUTPUT)) return LAPNYS_ERR_HIP;
-  if (!ok(lapnys::launch_output(pl, B.ct, B.y, B.mu, B.rs, out, s), "output launch")) return LAPNYS_ERR_HIP;
-  if (!mark(2 * LAPNYS_STAGE_OUTPUT + 1)) return LAPNYS_ERR_HIP;
+  if (!mark(2 * LAPNYS_STAGE_NS, side)) return LAPNYS_ERR_HIP;
+  if (!ok(lapnys::launch_ns(pl, W, side), "Newton-Schulz launch")) return LAPNYS_ERR_HIP;
+  if (!mark(2 * LAPNYS_STAGE_NS + 1, side)) return LAPNYS_ERR_HIP;
+  if (!ok(hipEventRecord(dc->join, side), "hipEventRecord")) return LAPNYS_ERR_HIP;
+  // kernel matrices, statistics and B V on the caller's stream, concurrently
+  if (!mark(2 * LAPNYS_STAGE_KERNEL, s)) return LAPNYS_ERR_HIP;
+  if (!ok(lapnys::launch_l1exp(pl, q, k, v, W, s), "kernel-matrix launch")) return LAPNYS_ERR_HIP;
+  if (!mark(2 * LAPNYS_STAGE_KERNEL + 1, s)) return LAPNYS_ERR_HIP;
+  if (!mark(2 * LAPNYS_STAGE_FINALIZE, s)) return LAPNYS_ERR_HIP;
+  if (!ok(lapnys::launch_reduce(pl, W, s), "reduce launch")) return LAPNYS_ERR_HIP;
+  // join: everything after needs X
+  if (!ok(hipStreamWaitEvent(s, dc->join, 0), "hipStreamWaitEvent")) return LAPNYS_ERR_HIP;
+  if (!pl.fused_ns && !ok(lapnys::launch_y(pl, W, s), "Y launch")) return LAPNYS_ERR_HIP;
+  if (!mark(2 * LAPNYS_STAGE_FINALIZE + 1, s) || !mark(2 * LAPNYS_STAGE_OUTPUT, s)) return LAPNYS_ERR_HIP;
+  if (!ok(lapnys::launch_output(pl, W, out, s), "output launch")) return LAPNYS_ERR_HIP;
+  if (!mark(2 * LAPNYS_STAGE_OUTPUT + 1, s)) return LAPNYS_ERR_HIP;
   return LAPNYS_OK;
 }
 
@@ -188,7 +227,7 @@ int forward_impl(const void* q, const void* k, const void* v, float* out, const 
   if (st != LAPNYS_OK) return st;
   st = check_buffers(q, k, v, out, pl, ws, ws_bytes);
   if (st != LAPNYS_OK) return st;
-  Buffers B = carve(pl, ws);
+  lapnys::Work B = carve(pl, ws);
   st = run(pl, q, k, v, out, B, ev, s);
   if (st != LAPNYS_OK || !dbg) return st;
   const size_t f = sizeof(float);
@@ -197,8 +236,11 @@ int forward_impl(const void* q, const void* k, const void* v, float* out, const 
     return !dst || ok(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s), "debug copy");
   };
   bool good = cp(dbg->landmarks, B.kt, Pm * pl.d * f) && cp(dbg->C_t, B.ct, Pm * pl.N * f) &&
-            cp(dbg->BV, B.bv, Pm * pl.d * f) && cp(dbg->Y, B.y, Pm * pl.d * f) && cp(dbg->mu, B.mu, Pm * f) &&
-            cp(dbg->sigma, B.sigma, Pm * f);
+              cp(dbg->BV, B.bv, Pm * pl.d * f) && cp(dbg->mu, B.mu, Pm * f) && cp(dbg->sigma, B.sigma, Pm * f);
+  // Y for m <= 64 lives only in the output stage's LDS; the debug form forms
+  // it once more with the tile GEMM into the workspace.
+  if (good && dbg->Y && pl.fused_ns) good = ok(lapnys::launch_y(pl, B, s), "Y launch");
+  if (good) good = cp(dbg->Y, B.y, Pm * pl.d * f);
   if (good && dbg->W) good = ok(lapnys::launch_extract_square(B.w, pl.mp, dbg->W, pl.m, pl.P, s), "W extract");
   if (good && dbg->X)
     good = ok(lapnys::launch_extract_square(B.x_final, pl.mp, dbg->X, pl.m, pl.P, s), "X extract");
@@ -240,8 +282,6 @@ int lapnys_forward_ws(const void* q, const void* k, const void* v, float* out, c
 int lapnys_forward_profiled(const void* q, const void* k, const void* v, float* out, const lapnys_params* p,
                             void* ws, size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream) {
   if (!stage_events) return LAPNYS_ERR_INVALID_ARG;
-  for (int i = 0; i < 2 * LAPNYS_NUM_STAGES; ++i)
-    if (!stage_events[i]) return LAPNYS_ERR_INVALID_ARG;
   return forward_impl(q, k, v, out, p, ws, ws_bytes, stage_events, nullptr, stream);
 }
 

@@ -17,12 +17,21 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ float widen(float x) { return x; }
 __device__ __forceinline__ float widen(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// Butterfly sum over the 64 lanes of a wavefront.  The pairing is fixed, so
-// the result is the same on every run.
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
+// Sum over the 64 lanes of a wavefront, returned to every lane.  Within each
+// 16-lane row, DPP row rotations by 8, 4, 2 and 1 leave the row sum in every
+// lane (VALU only, no LDS round trip); the four row sums are then read from
+// lanes 0, 16, 32 and 48 and added in that order.  The order is fixed, so the
+// result repeats bit for bit.
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, false));  // row_ror:8
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xf, 0xf, false));  // row_ror:4
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x122, 0xf, 0xf, false));  // row_ror:2
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x121, 0xf, 0xf, false));  // row_ror:1
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return ((r0 + r1) + r2) + r3;
 }
 
 // Landmark block handled by one workgroup of the fused kernel-matrix stage.
@@ -57,16 +66,20 @@ struct Plan {
       off_mu, off_sigma, off_rs, off_y, total;
 };
 
-// Kernel launchers (each returns the hipError_t of its launch).
-hipError_t launch_pool(const Plan& pl, const void* k, float* kt, hipStream_t s);
-hipError_t launch_ns(const Plan& pl, const float* kt, float* w, float* x, float* x2, float* pm,
-                     float** x_final, hipStream_t s);
-hipError_t launch_l1exp(const Plan& pl, const void* q, const void* k, const void* v, const float* kt,
-                        float* ct, float* stats, float* bvpart, hipStream_t s);
-hipError_t launch_finalize(const Plan& pl, const float* stats, const float* bvpart, const float* x,
-                           float* bv, float* mu, float* sigma, float* rs, float* y, hipStream_t s);
-hipError_t launch_output(const Plan& pl, const float* ct, const float* y, const float* mu, const float* rs,
-                         float* out, hipStream_t s);
+// Device pointers into one call's workspace.
+struct Work {
+  float *kt, *w, *x, *x2, *pm, *ct, *stats, *bvpart, *bv, *mu, *sigma, *rs, *y;
+  float* x_final;      // the Newton-Schulz result (x or x2), set by launch_ns
+};
+
+// Kernel launchers (each returns the hipError_t of its launches).
+hipError_t launch_pool(const Plan& pl, const void* k, const Work& w, hipStream_t s);
+hipError_t launch_ns(const Plan& pl, Work& w, hipStream_t s);
+hipError_t launch_l1exp(const Plan& pl, const void* q, const void* k, const void* v, const Work& w,
+                        hipStream_t s);
+hipError_t launch_reduce(const Plan& pl, const Work& w, hipStream_t s);
+hipError_t launch_y(const Plan& pl, const Work& w, hipStream_t s);  // m > kFusedNsMaxM only
+hipError_t launch_output(const Plan& pl, const Work& w, float* out, hipStream_t s);
 hipError_t launch_extract_square(const float* src, int src_ld, float* dst, int n, int P, hipStream_t s);
 
 }  // namespace lapnys

@@ -16,7 +16,8 @@
 //    (32x32x2) along the reduction; padding rows and columns stay exactly zero.
 //  * 64 < m <= 256: the products are too large for one LDS; W and the iterates
 //    live in the workspace (L2-resident) and each product is one batched launch
-//    of 64 x 64 output tiles, two launches per step.
+//    of 64 x 64 output tiles, two launches per step.  The same tile kernel also
+//    forms Y = X (B V) for these sizes.
 #include "lapnys_internal.hpp"
 
 namespace lapnys {
@@ -92,32 +93,79 @@ __global__ __launch_bounds__(256) void ns_fused_kernel(const float* __restrict__
 
   const int bi = w >> 1, bj = w & 1;
   const int li = lane & 31, lk = lane >> 5;
-  const int kext = (m + 1) & ~1;  // reduction extent: m rounded up to the MFMA depth
+  // Reduction extent: m rounded up to 8 (four MFMA steps of depth 2).  The
+  // padding rows and columns hold exact zeros, so the extra steps add +0.
+  const int nsteps = ((m + 7) & ~7) / 2;
   float* xc = xa;
   float* xn = xb;
+  const int col = 32 * bj + li;
   for (int it = 0; it < iters; ++it) {
-    // P = W X
+    // P = W X.  Operands of the next four steps are read while the current
+    // four MFMAs run.
     f32x16 acc = {0.f};
-    for (int k0 = 0; k0 < kext; k0 += 2) {
-      const float a = wl[(32 * bi + li) * kLD + k0 + lk];
-      const float b = xc[(k0 + lk) * kLD + 32 * bj + li];
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+    {
+      const float* arow = wl + (32 * bi + li) * kLD + lk;
+      const float* bcol = xc + lk * kLD + col;
+      float a[4], b[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a[u] = arow[2 * u];
+        b[u] = bcol[2 * u * kLD];
+      }
+      for (int s0 = 0; s0 < nsteps; s0 += 4) {
+        float an[4], bn[4];
+        const int nx = (s0 + 4 < nsteps) ? s0 + 4 : s0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          an[u] = arow[2 * (nx + u)];
+          bn[u] = bcol[2 * (nx + u) * kLD];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u], b[u], acc, 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          a[u] = an[u];
+          b[u] = bn[u];
+        }
+      }
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      pl[(32 * bi + 8 * (r >> 2) + 4 * lk + (r & 3)) * kLD + 32 * bj + li] = acc[r];
+      pl[(32 * bi + 8 * (r >> 2) + 4 * lk + (r & 3)) * kLD + col] = acc[r];
     __syncthreads();
     // X_next = X (2I - P)
     acc = f32x16{0.f};
-    for (int k0 = 0; k0 < kext; k0 += 2) {
-      const int kk = k0 + lk, col = 32 * bj + li;
-      const float a = xc[(32 * bi + li) * kLD + kk];
-      const float b = (kk == col ? 2.f : 0.f) - pl[kk * kLD + col];
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+    {
+      const float* arow = xc + (32 * bi + li) * kLD + lk;
+      const float* bcol = pl + lk * kLD + col;
+      float a[4], b[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int kk = 2 * u + lk;
+        a[u] = arow[2 * u];
+        b[u] = (kk == col ? 2.f : 0.f) - bcol[2 * u * kLD];
+      }
+      for (int s0 = 0; s0 < nsteps; s0 += 4) {
+        float an[4], bn[4];
+        const int nx = (s0 + 4 < nsteps) ? s0 + 4 : s0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int kk = 2 * (nx + u) + lk;
+          an[u] = arow[2 * (nx + u)];
+          bn[u] = (kk == col ? 2.f : 0.f) - bcol[2 * (nx + u) * kLD];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u], b[u], acc, 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          a[u] = an[u];
+          b[u] = bn[u];
+        }
+      }
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      xn[(32 * bi + 8 * (r >> 2) + 4 * lk + (r & 3)) * kLD + 32 * bj + li] = acc[r];
+      xn[(32 * bi + 8 * (r >> 2) + 4 * lk + (r & 3)) * kLD + col] = acc[r];
     __syncthreads();
     float* t = xc;
     xc = xn;
@@ -198,27 +246,34 @@ __global__ __launch_bounds__(256) void alpha_x0_kernel(const float* __restrict__
   }
 }
 
-// out = A B (mode 0) or out = A (2I - B) (mode 1), 64 x 64 output tile
-// (blockIdx.x, blockIdx.y) of problem blockIdx.z; reduction over [0, kext).
-__global__ __launch_bounds__(256) void ns_gemm_kernel(const float* __restrict__ amat, const float* __restrict__ bmat,
-                                                      float* __restrict__ out, int mp, int kext, int mode) {
+// One 64 x 64 output tile (blockIdx.x, blockIdx.y) of problem blockIdx.z:
+//   C = A B (mode 0)  or  C = A (2I - B) (mode 1),
+// reduction over [0, kext) (a multiple of 32) staged through LDS 32 at a time.
+// B entries outside [0, brows) x [0, bcols) read as zero (before the 2I
+// transform); C is stored for rows < crows and columns < ccols.  Each of the
+// four wavefronts owns a 32 x 32 block and issues fp32 MFMA 32x32x2.
+__global__ __launch_bounds__(256) void gemm64_kernel(const float* __restrict__ A, int lda, long long sa,
+                                                     const float* __restrict__ B, int ldb, long long sb, int brows,
+                                                     int bcols, float* __restrict__ C, int ldc, long long sc,
+                                                     int crows, int ccols, int kext, int mode) {
   __shared__ float as[64 * 33];
   __shared__ float bs[32 * 64];
   const int p = blockIdx.z, r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wr = w >> 1, wc = w & 1, li = lane & 31, lk = lane >> 5;
-  const float* A = amat + (size_t)p * mp * mp;
-  const float* B = bmat + (size_t)p * mp * mp;
+  const float* Ap = A + p * sa;
+  const float* Bp = B + p * sb;
   f32x16 acc = {0.f};
   for (int kc = 0; kc < kext; kc += 32) {
     for (int e = tid; e < 64 * 32; e += 256) {
       const int r = e >> 5, c = e & 31;
-      as[r * 33 + c] = A[(size_t)(r0 + r) * mp + kc + c];
+      as[r * 33 + c] = Ap[(size_t)(r0 + r) * lda + kc + c];
     }
     for (int e = tid; e < 32 * 64; e += 256) {
       const int r = e >> 6, c = e & 63;
-      float bv = B[(size_t)(kc + r) * mp + c0 + c];
-      if (mode) bv = ((kc + r == c0 + c) ? 2.f : 0.f) - bv;
+      const int gr = kc + r, gc = c0 + c;
+      float bv = (gr < brows && gc < bcols) ? Bp[(size_t)gr * ldb + gc] : 0.f;
+      if (mode) bv = (gr == gc ? 2.f : 0.f) - bv;
       bs[r * 64 + c] = bv;
     }
     __syncthreads();
@@ -230,10 +285,13 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(const float* __restrict__ 
     }
     __syncthreads();
   }
-  float* O = out + (size_t)p * mp * mp;
+  float* Cp = C + p * sc;
+  const int cc = c0 + 32 * wc + li;
 #pragma unroll
-  for (int r = 0; r < 16; ++r)
-    O[(size_t)(r0 + 32 * wr + 8 * (r >> 2) + 4 * lk + (r & 3)) * mp + c0 + 32 * wc + li] = acc[r];
+  for (int r = 0; r < 16; ++r) {
+    const int rr = r0 + 32 * wr + 8 * (r >> 2) + 4 * lk + (r & 3);
+    if (rr < crows && cc < ccols) Cp[(size_t)rr * ldc + cc] = acc[r];
+  }
 }
 
 __global__ __launch_bounds__(256) void extract_square_kernel(const float* __restrict__ src, int src_ld,
@@ -248,42 +306,53 @@ __global__ __launch_bounds__(256) void extract_square_kernel(const float* __rest
 
 }  // namespace
 
-hipError_t launch_ns(const Plan& pl, const float* kt, float* w, float* x, float* x2, float* pm, float** x_final,
-                     hipStream_t s) {
+hipError_t launch_ns(const Plan& pl, Work& wk, hipStream_t s) {
   if (pl.fused_ns) {
     if (pl.d == 64)
-      hipLaunchKernelGGL(ns_fused_kernel<64>, dim3(pl.P), dim3(256), 0, s, kt, w, x, pl.m, pl.scale, pl.eps,
+      hipLaunchKernelGGL(ns_fused_kernel<64>, dim3(pl.P), dim3(256), 0, s, wk.kt, wk.w, wk.x, pl.m, pl.scale, pl.eps,
                          pl.ns_iters);
     else
-      hipLaunchKernelGGL(ns_fused_kernel<32>, dim3(pl.P), dim3(256), 0, s, kt, w, x, pl.m, pl.scale, pl.eps,
+      hipLaunchKernelGGL(ns_fused_kernel<32>, dim3(pl.P), dim3(256), 0, s, wk.kt, wk.w, wk.x, pl.m, pl.scale, pl.eps,
                          pl.ns_iters);
-    *x_final = x;
+    wk.x_final = wk.x;
     return hipGetLastError();
   }
   const int mp = pl.mp;
   if (pl.d == 64)
-    hipLaunchKernelGGL(wbuild_big_kernel<64>, dim3(mp / 16, pl.P), dim3(256), 0, s, kt, w, pl.m, mp, pl.scale,
+    hipLaunchKernelGGL(wbuild_big_kernel<64>, dim3(mp / 16, pl.P), dim3(256), 0, s, wk.kt, wk.w, pl.m, mp, pl.scale,
                        pl.eps);
   else
-    hipLaunchKernelGGL(wbuild_big_kernel<32>, dim3(mp / 16, pl.P), dim3(256), 0, s, kt, w, pl.m, mp, pl.scale,
+    hipLaunchKernelGGL(wbuild_big_kernel<32>, dim3(mp / 16, pl.P), dim3(256), 0, s, wk.kt, wk.w, pl.m, mp, pl.scale,
                        pl.eps);
-  hipLaunchKernelGGL(alpha_x0_kernel, dim3(pl.P), dim3(256), 0, s, w, x, mp);
+  hipLaunchKernelGGL(alpha_x0_kernel, dim3(pl.P), dim3(256), 0, s, wk.w, wk.x, mp);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int kext = (pl.m + 31) & ~31;
-  float* xc = x;
-  float* xn = x2;
+  const long long sq = (long long)mp * mp;
+  const dim3 grid(mp / 64, mp / 64, pl.P);
+  float* xc = wk.x;
+  float* xn = wk.x2;
   for (int it = 0; it < pl.ns_iters; ++it) {
-    hipLaunchKernelGGL(ns_gemm_kernel, dim3(mp / 64, mp / 64, pl.P), dim3(256), 0, s, w, xc, pm, mp, kext, 0);
-    hipLaunchKernelGGL(ns_gemm_kernel, dim3(mp / 64, mp / 64, pl.P), dim3(256), 0, s, xc, pm, xn, mp, kext, 1);
+    hipLaunchKernelGGL(gemm64_kernel, grid, dim3(256), 0, s, wk.w, mp, sq, xc, mp, sq, mp, mp, wk.pm, mp, sq, mp, mp,
+                       kext, 0);
+    hipLaunchKernelGGL(gemm64_kernel, grid, dim3(256), 0, s, xc, mp, sq, wk.pm, mp, sq, mp, mp, xn, mp, sq, mp, mp,
+                       kext, 1);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     float* t = xc;
     xc = xn;
     xn = t;
   }
-  *x_final = xc;
+  wk.x_final = xc;
   return hipSuccess;
+}
+
+hipError_t launch_y(const Plan& pl, const Work& wk, hipStream_t s) {
+  const int kext = (pl.m + 31) & ~31;
+  const long long md = (long long)pl.m * pl.d;
+  hipLaunchKernelGGL(gemm64_kernel, dim3((pl.m + 63) / 64, (pl.d + 63) / 64, pl.P), dim3(256), 0, s, wk.x_final,
+                     pl.mp, (long long)pl.mp * pl.mp, wk.bv, pl.d, md, pl.m, pl.d, wk.y, pl.d, md, pl.m, pl.d, kext, 0);
+  return hipGetLastError();
 }
 
 hipError_t launch_extract_square(const float* src, int src_ld, float* dst, int n, int P, hipStream_t s) {

@@ -12,35 +12,66 @@
 
 namespace lapnys {
 
-template <typename T>
-__global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ k, float* __restrict__ kt,
-                                                   int N, int d, int grid_w, int pool, int gw, int m,
-                                                   long long total) {
+// POOL > 0: the window size is a compile-time constant, so every load of the
+// window is issued before the (dependent) float64 adds.  POOL == 0: any window
+// size, loads issued a window row at a time in chunks of 8.
+template <typename T, int POOL>
+__global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ k, float* __restrict__ kt, int N, int d,
+                                                   int grid_w, int pool_rt, int gw, int m, long long total) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
+  const int pool = POOL > 0 ? POOL : pool_rt;
   const int t = (int)(idx % d);
   const long long rest = idx / d;
   const int j = (int)(rest % m);
   const long long p = rest / m;
   const int R = j / gw, Cc = j % gw;
-  const T* kp = k + p * (long long)N * d;
+  const T* base = k + p * (long long)N * d + ((long long)R * pool * grid_w + (long long)Cc * pool) * d + t;
+  const long long row_stride = (long long)grid_w * d;
   double acc = 0.0;
-  for (int r = 0; r < pool; ++r) {
-    const T* row = kp + ((long long)(R * pool + r) * grid_w + (long long)Cc * pool) * d + t;
-    for (int c = 0; c < pool; ++c) acc += (double)widen(row[(long long)c * d]);
+  if constexpr (POOL > 0) {
+    float vals[POOL * POOL];
+#pragma unroll
+    for (int r = 0; r < POOL; ++r)
+#pragma unroll
+      for (int c = 0; c < POOL; ++c) vals[r * POOL + c] = widen(base[r * row_stride + (long long)c * d]);
+#pragma unroll
+    for (int e = 0; e < POOL * POOL; ++e) acc += (double)vals[e];
+  } else {
+    for (int r = 0; r < pool; ++r) {
+      const T* row = base + r * row_stride;
+      for (int c0 = 0; c0 < pool; c0 += 8) {
+        float vals[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) vals[c] = (c0 + c < pool) ? widen(row[(long long)(c0 + c) * d]) : 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          if (c0 + c < pool) acc += (double)vals[c];
+      }
+    }
   }
   kt[idx] = (float)(acc / (double)(pool * pool));
 }
 
-hipError_t launch_pool(const Plan& pl, const void* k, float* kt, hipStream_t s) {
+template <typename T>
+void launch_typed(const Plan& pl, const T* k, float* kt, hipStream_t s) {
   const long long total = (long long)pl.P * pl.m * pl.d;
-  const unsigned blocks = (unsigned)((total + 255) / 256);
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  switch (pl.pool) {
+    case 1: hipLaunchKernelGGL((pool_kernel<T, 1>), grid, block, 0, s, k, kt, pl.N, pl.d, pl.grid_w, 1, pl.gw, pl.m, total); break;
+    case 2: hipLaunchKernelGGL((pool_kernel<T, 2>), grid, block, 0, s, k, kt, pl.N, pl.d, pl.grid_w, 2, pl.gw, pl.m, total); break;
+    case 4: hipLaunchKernelGGL((pool_kernel<T, 4>), grid, block, 0, s, k, kt, pl.N, pl.d, pl.grid_w, 4, pl.gw, pl.m, total); break;
+    case 8: hipLaunchKernelGGL((pool_kernel<T, 8>), grid, block, 0, s, k, kt, pl.N, pl.d, pl.grid_w, 8, pl.gw, pl.m, total); break;
+    case 16: hipLaunchKernelGGL((pool_kernel<T, 16>), grid, block, 0, s, k, kt, pl.N, pl.d, pl.grid_w, 16, pl.gw, pl.m, total); break;
+    default: hipLaunchKernelGGL((pool_kernel<T, 0>), grid, block, 0, s, k, kt, pl.N, pl.d, pl.grid_w, pl.pool, pl.gw, pl.m, total); break;
+  }
+}
+
+hipError_t launch_pool(const Plan& pl, const void* k, const Work& w, hipStream_t s) {
   if (pl.dtype == 1)
-    hipLaunchKernelGGL(pool_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s, (const uint16_t*)k, kt, pl.N,
-                       pl.d, pl.grid_w, pl.pool, pl.gw, pl.m, total);
+    launch_typed<uint16_t>(pl, (const uint16_t*)k, w.kt, s);
   else
-    hipLaunchKernelGGL(pool_kernel<float>, dim3(blocks), dim3(256), 0, s, (const float*)k, kt, pl.N, pl.d,
-                       pl.grid_w, pl.pool, pl.gw, pl.m, total);
+    launch_typed<float>(pl, (const float*)k, w.kt, s);
   return hipGetLastError();
 }
 

@@ -10,10 +10,9 @@
 // exp(0) + eps = 1 + eps exactly as float32 arithmetic gives it.
 //
 // Two schedules:
-//  * m <= 64: one workgroup per problem keeps W, X and W X in LDS (64 x 64,
-//    zero padded) and runs every step in one launch.  Each of the four
-//    wavefronts owns a 32 x 32 block of a product and issues fp32 MFMA
-//    (32x32x2) along the reduction; padding rows and columns stay exactly zero.
+//  * m <= 64: one workgroup per problem keeps W, X and 2I - W X in LDS
+//    (64 x 64, zero padded) and runs every step in one launch on fp32 MFMA;
+//    padding rows and columns stay exactly zero (see ns_fused_kernel).
 //  * 64 < m <= 256: the products are too large for one LDS; W and the iterates
 //    live in the workspace (L2-resident) and each product is one batched launch
 //    of 64 x 64 output tiles, two launches per step.  The same tile kernel also
@@ -24,21 +23,38 @@ namespace lapnys {
 
 namespace {
 
-constexpr int kMP = 64;   // padded size of the in-LDS schedule
-constexpr int kLD = 65;   // LDS row stride: column reads hit 32 distinct banks
+constexpr int kMP = 64;  // padded size of the in-LDS schedule
+constexpr int kLD = 68;  // LDS row stride (floats): rows stay 16-byte aligned
 
+// In-LDS schedule for m <= 64: one workgroup of four wavefronts per problem;
+// wavefront w owns the 32 x 32 output block (w/2, w%2) of every 64 x 64
+// (zero-padded) product and issues fp32 MFMA 32x32x2.
+//
+// Operand layout.  The reduction index k runs over [0, kext), kext = m rounded
+// up to 8 (padding entries are exact zeros, so they add +0).  Lane half h =
+// lane/32 covers k in [h*KH, (h+1)*KH), KH = kext/2, and MFMA step s takes
+// k = h*KH + s, so a lane's operands for four consecutive steps are four
+// consecutive floats of one LDS row: one 16-byte read.  That needs every
+// operand matrix stored with k along its rows:
+//   A operands (rows i, k):   W (kept in registers for all steps), X
+//   B operands (k, columns j) stored transposed:  X^T, R^T with R = 2I - W X
+// Each step writes X_next in both layouts and R^T straight from the MFMA
+// accumulators (R = 2I - P needs no separate pass).
 template <int D>
 __global__ __launch_bounds__(256) void ns_fused_kernel(const float* __restrict__ kt, float* __restrict__ wout,
                                                        float* __restrict__ xout, int m, float scale, float eps,
                                                        int iters) {
   constexpr int KLD = D + 1;
-  __shared__ float kl[kMP * KLD];
-  __shared__ float wl[kMP * kLD];
-  __shared__ float xa[kMP * kLD];
-  __shared__ float xb[kMP * kLD];
-  __shared__ float pl[kMP * kLD];
+  __shared__ float4 wl4[kMP * kLD / 4];       // W, row-major
+  __shared__ float4 xa4[2][kMP * kLD / 4];    // X (ping-pong), row-major
+  __shared__ float4 xt4[2][kMP * kLD / 4];    // X^T (ping-pong)
+  __shared__ float4 rt4[kMP * kLD / 4];       // R^T; also the landmark staging area
   __shared__ float red[128];
   __shared__ float alpha_s;
+  static_assert(kMP * KLD <= kMP * kLD, "landmark staging must fit in the R^T buffer");
+  float* wl = reinterpret_cast<float*>(wl4);
+  float* rt = reinterpret_cast<float*>(rt4);
+  float* kl = rt;
 
   const int p = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const float* ktp = kt + (size_t)p * m * D;
@@ -64,119 +80,117 @@ __global__ __launch_bounds__(256) void ns_fused_kernel(const float* __restrict__
   __syncthreads();
 
   // alpha = ||W||_1 * ||W||_inf (largest absolute column sum times largest row sum).
-  if (tid < kMP) {
-    float r = 0.f;
-    for (int b = 0; b < kMP; ++b) r += fabsf(wl[tid * kLD + b]);
-    red[tid] = r;
-  } else if (tid < 2 * kMP) {
-    const int c = tid - kMP;
-    float s = 0.f;
-    for (int a = 0; a < kMP; ++a) s += fabsf(wl[a * kLD + c]);
-    red[tid] = s;
+  if (tid < 2 * kMP) {
+    const int i = tid & 63;
+    const bool rows = tid < kMP;
+    float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b0 = 0; b0 < kMP; b0 += 8)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc8[u] += fabsf(rows ? wl[i * kLD + b0 + u] : wl[(b0 + u) * kLD + i]);
+    red[tid] = ((acc8[0] + acc8[1]) + (acc8[2] + acc8[3])) + ((acc8[4] + acc8[5]) + (acc8[6] + acc8[7]));
   }
   __syncthreads();
-  if (tid == 0) {
-    float rm = 0.f, cm = 0.f;
-    for (int i = 0; i < kMP; ++i) {
-      rm = fmaxf(rm, red[i]);
-      cm = fmaxf(cm, red[kMP + i]);
+  if (tid < 64) {
+    float rm = red[tid], cm = red[kMP + tid];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      rm = fmaxf(rm, __shfl_xor(rm, off, 64));
+      cm = fmaxf(cm, __shfl_xor(cm, off, 64));
     }
-    alpha_s = cm * rm;
+    if (tid == 0) alpha_s = cm * rm;
   }
   __syncthreads();
-  const float alpha = alpha_s;
-  for (int e = tid; e < kMP * kMP; e += 256) {
-    const int a = e >> 6, b = e & 63;
-    xa[a * kLD + b] = wl[b * kLD + a] / alpha;
+  // X0 = W^T / alpha, in both layouts: X0[a][b] = W[b][a] / alpha, X0^T[a][b] = W[a][b] / alpha.
+  {
+    const float alpha = alpha_s;
+    float* x0 = reinterpret_cast<float*>(xa4[0]);
+    float* x0t = reinterpret_cast<float*>(xt4[0]);
+    for (int e = tid; e < kMP * kMP; e += 256) {
+      const int a = e >> 6, b = e & 63;
+      x0[a * kLD + b] = wl[b * kLD + a] / alpha;
+      x0t[a * kLD + b] = wl[a * kLD + b] / alpha;
+    }
+  }
+
+  const int bi = w >> 1, bj = w & 1;
+  const int li = lane & 31, h = lane >> 5;
+  const int kh = ((m + 7) & ~7) / 2;  // steps per product; a multiple of 4
+  const int row_a = 32 * bi + li;      // A-operand row of this lane
+  const int row_b = 32 * bj + li;      // B-operand (transposed) row of this lane
+  // W's A operands for every step, kept in registers: kh <= 32 values.
+  float wreg[32];
+#pragma unroll
+  for (int s4 = 0; s4 < 32; s4 += 4) {
+    const float4 v = (s4 < kh) ? *reinterpret_cast<const float4*>(&wl[row_a * kLD + h * kh + s4])
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+    wreg[s4 + 0] = v.x;
+    wreg[s4 + 1] = v.y;
+    wreg[s4 + 2] = v.z;
+    wreg[s4 + 3] = v.w;
   }
   __syncthreads();
 
-  const int bi = w >> 1, bj = w & 1;
-  const int li = lane & 31, lk = lane >> 5;
-  // Reduction extent: m rounded up to 8 (four MFMA steps of depth 2).  The
-  // padding rows and columns hold exact zeros, so the extra steps add +0.
-  const int nsteps = ((m + 7) & ~7) / 2;
-  float* xc = xa;
-  float* xn = xb;
-  const int col = 32 * bj + li;
+  int cur = 0;
   for (int it = 0; it < iters; ++it) {
-    // P = W X.  Operands of the next four steps are read while the current
-    // four MFMAs run.
-    f32x16 acc = {0.f};
+    const float* xc = reinterpret_cast<const float*>(xa4[cur]);
+    const float* xtc = reinterpret_cast<const float*>(xt4[cur]);
+    // P = W X;  R^T[j][i] = 2 [i == j] - P[i][j]
     {
-      const float* arow = wl + (32 * bi + li) * kLD + lk;
-      const float* bcol = xc + lk * kLD + col;
-      float a[4], b[4];
+      f32x16 acc = {0.f};
+      const float* bp = xtc + row_b * kLD + h * kh;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        a[u] = arow[2 * u];
-        b[u] = bcol[2 * u * kLD];
+      for (int s4 = 0; s4 < 32; s4 += 4) {
+        if (s4 < kh) {
+          const float4 b = *reinterpret_cast<const float4*>(bp + s4);
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(wreg[s4 + 0], b.x, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(wreg[s4 + 1], b.y, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(wreg[s4 + 2], b.z, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(wreg[s4 + 3], b.w, acc, 0, 0, 0);
+        }
       }
-      for (int s0 = 0; s0 < nsteps; s0 += 4) {
-        float an[4], bn[4];
-        const int nx = (s0 + 4 < nsteps) ? s0 + 4 : s0;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          an[u] = arow[2 * (nx + u)];
-          bn[u] = bcol[2 * (nx + u) * kLD];
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u], b[u], acc, 0, 0, 0);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          a[u] = an[u];
-          b[u] = bn[u];
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int i = 32 * bi + 8 * (r >> 2) + 4 * h + (r & 3), j = 32 * bj + li;
+        rt[j * kLD + i] = (i == j ? 2.f : 0.f) - acc[r];
       }
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      pl[(32 * bi + 8 * (r >> 2) + 4 * lk + (r & 3)) * kLD + col] = acc[r];
     __syncthreads();
-    // X_next = X (2I - P)
-    acc = f32x16{0.f};
+    // X_next = X R, written row-major and transposed
     {
-      const float* arow = xc + (32 * bi + li) * kLD + lk;
-      const float* bcol = pl + lk * kLD + col;
-      float a[4], b[4];
+      f32x16 acc = {0.f};
+      const float* ap = xc + row_a * kLD + h * kh;
+      const float* bp = rt + row_b * kLD + h * kh;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int kk = 2 * u + lk;
-        a[u] = arow[2 * u];
-        b[u] = (kk == col ? 2.f : 0.f) - bcol[2 * u * kLD];
+      for (int s4 = 0; s4 < 32; s4 += 4) {
+        if (s4 < kh) {
+          const float4 a = *reinterpret_cast<const float4*>(ap + s4);
+          const float4 b = *reinterpret_cast<const float4*>(bp + s4);
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b.x, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b.y, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, b.z, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, b.w, acc, 0, 0, 0);
+        }
       }
-      for (int s0 = 0; s0 < nsteps; s0 += 4) {
-        float an[4], bn[4];
-        const int nx = (s0 + 4 < nsteps) ? s0 + 4 : s0;
+      float* xn = reinterpret_cast<float*>(xa4[cur ^ 1]);
+      float* xtn = reinterpret_cast<float*>(xt4[cur ^ 1]);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int kk = 2 * (nx + u) + lk;
-          an[u] = arow[2 * (nx + u)];
-          bn[u] = (kk == col ? 2.f : 0.f) - bcol[2 * (nx + u) * kLD];
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u], b[u], acc, 0, 0, 0);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          a[u] = an[u];
-          b[u] = bn[u];
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int i = 32 * bi + 8 * (r >> 2) + 4 * h + (r & 3), j = 32 * bj + li;
+        xn[i * kLD + j] = acc[r];
+        xtn[j * kLD + i] = acc[r];
       }
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      xn[(32 * bi + 8 * (r >> 2) + 4 * lk + (r & 3)) * kLD + col] = acc[r];
     __syncthreads();
-    float* t = xc;
-    xc = xn;
-    xn = t;
+    cur ^= 1;
   }
 
   float* wp = wout + (size_t)p * kMP * kMP;
   float* xp = xout + (size_t)p * kMP * kMP;
+  const float* xf = reinterpret_cast<const float*>(xa4[cur]);
   for (int e = tid; e < kMP * kMP; e += 256) {
     wp[e] = wl[(e >> 6) * kLD + (e & 63)];
-    xp[e] = xc[(e >> 6) * kLD + (e & 63)];
+    xp[e] = xf[(e >> 6) * kLD + (e & 63)];
   }
 }
 

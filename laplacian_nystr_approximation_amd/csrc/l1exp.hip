@@ -12,11 +12,13 @@
 // The partials are reduced by the finalize stage (finalize.hip).
 //
 // Layout of the work: one lane per token.  A workgroup of 256 lanes takes a
-// tile of 256 consecutive tokens of one problem and a block of landmarks; every
-// landmark value is wave-uniform and comes from a scalar register, so the
-// inner loop is pure VALU: one subtract and one add with an |.| source
-// modifier per (token, landmark, feature).  This stage is not a dense
-// contraction; it runs on the vector ALUs, not on MFMA.
+// tile of 256 consecutive tokens of one problem and a block of landmarks.  A
+// landmark row is spread over the 16 lanes of each DPP row and reaches every
+// lane through a row_newbcast source operand, so the inner loop is pure VALU:
+// one subtract (with the broadcast folded in) and one add with an |.| source
+// modifier per (token, landmark, feature), and one 16-byte load per lane feeds
+// a whole landmark row.  This stage is not a dense contraction; it runs on the
+// vector ALUs, not on MFMA.
 //
 // LDS per workgroup: a tile buffer [lb + 1][256 + 2] (the extra row is zero) that
 // holds C, then B, transposed (landmark-major) so that the statistics pass and
@@ -86,56 +88,100 @@ struct VHalf {
   __device__ __forceinline__ float get(int i) const { return widen(w[i]); }
 };
 
+// A landmark row spread over the 16 lanes of a DPP row: lane li holds
+// features KW li .. KW li + KW - 1 (KW = D / 16).  Every 16-lane row of the
+// wavefront holds the same copy, so a row_newbcast:i source operand hands
+// feature KW i + c of the landmark to all 64 lanes inside the VALU
+// instruction itself: one 16-byte load per lane feeds D subtractions.
+template <int D>
+struct KRow {
+  static constexpr int KW = D / 16;
+  float v[KW];
+  __device__ __forceinline__ void load(const float* __restrict__ row, int li) {
+    if constexpr (KW == 4) {
+      const float4 t = *reinterpret_cast<const float4*>(row + 4 * li);
+      v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+    } else {
+      const float2 t = *reinterpret_cast<const float2*>(row + 2 * li);
+      v[0] = t.x; v[1] = t.y;
+    }
+  }
+};
+
+template <int I>
+__device__ __forceinline__ float row_bcast(float v) {
+  // DPP row_newbcast:I (control 0x150 + I): lane I of each 16-lane row.
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + I, 0xF, 0xF, false));
+}
+
+// Adds |x[t] - k_u[t]| over the features of the U landmark rows kr[u] into
+// sa[u] (even t) and sb[u] (odd t), in increasing t.  The compiler barrier
+// after each 16-lane broadcast step keeps every subtraction next to its add
+// (otherwise all D differences are computed first and held in registers).
+template <int D, int U, int I = 0>
+__device__ __forceinline__ void l1_accumulate(const float (&x)[D], const KRow<D> (&kr)[U], float (&sa)[U],
+                                              float (&sb)[U]) {
+  if constexpr (I < 16) {
+    constexpr int KW = KRow<D>::KW;
+#pragma unroll
+    for (int c = 0; c < KW; ++c) {
+      // All U differences first, then the U adds: consecutive DPP
+      // instructions then write different registers (a DPP result register
+      // read again within two instructions costs a wait state).
+      float dv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) dv[u] = x[KW * I + c] - row_bcast<I>(kr[u].v[c]);
+      if constexpr (U == 4) {
+        asm volatile("" : "+v"(dv[0]), "+v"(dv[1]), "+v"(dv[2]), "+v"(dv[3]));
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if ((KW * I + c) % 2 == 0) sa[u] += fabsf(dv[u]); else sb[u] += fabsf(dv[u]);
+      }
+    }
+    if constexpr (U == 4) {
+      asm volatile("" : "+v"(sa[0]), "+v"(sa[1]), "+v"(sa[2]), "+v"(sa[3]), "+v"(sb[0]), "+v"(sb[1]), "+v"(sb[2]),
+                   "+v"(sb[3]));
+    } else {
+      asm volatile("" : "+v"(sa[0]), "+v"(sb[0]));
+    }
+    l1_accumulate<D, U, I + 1>(x, kr, sa, sb);
+  }
+}
+
 // tl[j][col] = exp2(scale * sum_t |x[t] - kg[j][t]|) for the lb landmarks of the
 // block (0 for a lane past the last token).  kg points at the block's K~ rows
-// in global memory; every address is wave-uniform, so the values arrive by
-// scalar loads into SGPRs and feed the VALU directly (no LDS traffic, no VGPR
-// copies).  Two partial sums per landmark (even / odd features) and four
-// landmarks at a time give eight independent add chains.  The landmark values
-// are loaded one 4-feature chunk ahead of their use (double buffer); the
-// compiler barriers keep the loads and adds in that shape.
+// in global memory (a few KB per problem, served from cache).  Four landmarks
+// at a time, each with two partial sums (even / odd features), give eight
+// independent add chains; the next four landmark rows are loaded while the
+// current four are summed.
 template <int D>
 __device__ __forceinline__ void kernel_row(const float (&x)[D], const float* __restrict__ kg, int lb, float scale,
-                                           float* __restrict__ tl, int col, bool valid) {
-  int j = 0;
-  for (; j + 4 <= lb; j += 4) {
+                                           float* __restrict__ tl, int col, bool valid, int li) {
+  const int lb4 = lb & ~3;
+  KRow<D> kv[4];
+  if (lb4 > 0) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) kv[u].load(kg + u * D, li);
+  }
+  for (int j = 0; j < lb4; j += 4) {
+    KRow<D> kn[4];
+    const int jn = j + 4 < lb4 ? j + 4 : j;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) kn[u].load(kg + (jn + u) * D, li);
     float sa[4] = {0.f, 0.f, 0.f, 0.f}, sb[4] = {0.f, 0.f, 0.f, 0.f};
-    float4 kv[2][4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) kv[0][u] = *reinterpret_cast<const float4*>(&kg[(j + u) * D]);
-#pragma unroll
-    for (int c = 0; c < D / 4; ++c) {
-      const int cur = c & 1;
-      if (c + 1 < D / 4) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) kv[cur ^ 1][u] = *reinterpret_cast<const float4*>(&kg[(j + u) * D + 4 * (c + 1)]);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        sa[u] += fabsf(x[4 * c + 0] - kv[cur][u].x);
-        sb[u] += fabsf(x[4 * c + 1] - kv[cur][u].y);
-        sa[u] += fabsf(x[4 * c + 2] - kv[cur][u].z);
-        sb[u] += fabsf(x[4 * c + 3] - kv[cur][u].w);
-      }
-      // Accumulators are in/out operands: this chunk's adds finish before the
-      // next chunk's loads issue.
-      asm volatile("" : "+v"(sa[0]), "+v"(sa[1]), "+v"(sa[2]), "+v"(sa[3]), "+v"(sb[0]), "+v"(sb[1]),
-                   "+v"(sb[2]), "+v"(sb[3])::"memory");
-    }
+    l1_accumulate<D, 4>(x, kv, sa, sb);
 #pragma unroll
     for (int u = 0; u < 4; ++u) tl[(j + u) * kTP + col] = valid ? exp2f((sa[u] + sb[u]) * scale) : 0.f;
-  }
-  for (; j < lb; ++j) {
-    float sa = 0.f, sb = 0.f;
 #pragma unroll
-    for (int t = 0; t < D; t += 4) {
-      const float4 kv = *reinterpret_cast<const float4*>(&kg[j * D + t]);
-      sa += fabsf(x[t + 0] - kv.x);
-      sb += fabsf(x[t + 1] - kv.y);
-      sa += fabsf(x[t + 2] - kv.z);
-      sb += fabsf(x[t + 3] - kv.w);
-    }
-    tl[j * kTP + col] = valid ? exp2f((sa + sb) * scale) : 0.f;
+    for (int u = 0; u < 4; ++u) kv[u] = kn[u];
+  }
+  for (int j = lb4; j < lb; ++j) {
+    KRow<D> kr[1];
+    kr[0].load(kg + j * D, li);
+    float sa[1] = {0.f}, sb[1] = {0.f};
+    l1_accumulate<D, 1>(x, kr, sa, sb);
+    tl[j * kTP + col] = valid ? exp2f((sa[0] + sb[0]) * scale) : 0.f;
   }
 }
 
@@ -146,7 +192,7 @@ template <typename T, int D, int LBB>
 __global__ __launch_bounds__(kTT) void l1exp_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                     const T* __restrict__ v, const float* __restrict__ kt,
                                                     float* __restrict__ ct, float2* __restrict__ stats,
-                                                    float* __restrict__ bvpart, int N, int m, int lbmax, int ntiles,
+                                                    float* __restrict__ bvpart, int N, int ldc, int m, int lbmax, int ntiles,
                                                     int tpg, int groups, float scale) {
   extern __shared__ float tl[];  // [lb + 1][kTP]; row lb stays zero
 
@@ -197,7 +243,7 @@ __global__ __launch_bounds__(kTT) void l1exp_kernel(const T* __restrict__ q, con
     issue_row<T, D>(q + row, valid, raw);
     widen_row<D>(raw, x);
     __syncthreads();  // tile buffer free (previous tile's MFMA reads done)
-    kernel_row<D>(x, kg, lb, scale, tl, tid, valid);
+    kernel_row<D>(x, kg, lb, scale, tl, tid, valid, li);
     __syncthreads();
 
     // The key row and this lane's V operands are issued now and arrive while
@@ -229,7 +275,7 @@ __global__ __launch_bounds__(kTT) void l1exp_kernel(const T* __restrict__ q, con
       }
       m2 = wave_sum_dpp(m2);
       if (lane == 0) stats[((size_t)p * ntiles + tile) * m + j0 + j] = make_float2(s, m2);
-      float* crow = ct + ((size_t)p * m + j0 + j) * N + t0;
+      float* crow = ct + ((size_t)p * m + j0 + j) * ldc + t0;
 #pragma unroll
       for (int c = 0; c < kTT / 64; ++c) {
         const int col = lane + 64 * c;
@@ -240,7 +286,7 @@ __global__ __launch_bounds__(kTT) void l1exp_kernel(const T* __restrict__ q, con
     // ---- B = k(K~, K), kept on chip ----
     widen_row<D>(raw, x);
     __syncthreads();  // statistics pass done with the tile buffer
-    kernel_row<D>(x, kg, lb, scale, tl, tid, valid);
+    kernel_row<D>(x, kg, lb, scale, tl, tid, valid, li);
     __syncthreads();
 
     // ---- B V partial: acc[landmark][feature] += sum over the tile's tokens ----
@@ -296,7 +342,7 @@ hipError_t launch_lbb(const Plan& pl, const void* q, const void* k, const void* 
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(kern, dim3(pl.jblocks, pl.groups, pl.P), dim3(kTT), shmem, s, (const T*)q, (const T*)k,
-                     (const T*)v, w.kt, w.ct, reinterpret_cast<float2*>(w.stats), w.bvpart, pl.N, pl.m, lbmax,
+                     (const T*)v, w.kt, w.ct, reinterpret_cast<float2*>(w.stats), w.bvpart, pl.N, pl.ldc, pl.m, lbmax,
                      pl.ntiles, pl.tpg, pl.groups, pl.scale);
   return hipGetLastError();
 }

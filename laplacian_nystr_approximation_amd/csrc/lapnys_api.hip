@@ -69,6 +69,7 @@ int make_plan(const lapnys_params* p, Plan* pl) {
   memset(&P, 0, sizeof(P));
   P.P = p->B * p->H;
   P.N = p->N;
+  P.ldc = (p->N + 3) & ~3;
   P.d = p->d;
   P.grid_w = p->grid_w;
   P.pool = p->pool;
@@ -104,7 +105,7 @@ int make_plan(const lapnys_params* p, Plan* pl) {
   P.off_x = take(Pn * P.mp * P.mp * f);
   P.off_x2 = take(P.fused_ns ? 0 : Pn * P.mp * P.mp * f);
   P.off_pm = take(P.fused_ns ? 0 : Pn * P.mp * P.mp * f);
-  P.off_ct = take(Pn * P.m * (size_t)P.N * f);
+  P.off_ct = take(Pn * P.m * (size_t)P.ldc * f);
   P.off_stats = take(Pn * P.ntiles * P.m * 2 * f);
   P.off_bvpart = take(Pn * P.groups * P.m * P.d * f);
   P.off_bv = take(Pn * P.m * P.d * f);
@@ -235,7 +236,11 @@ int forward_impl(const void* q, const void* k, const void* v, float* out, const 
   auto cp = [&](float* dst, const float* src, size_t bytes) {
     return !dst || ok(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s), "debug copy");
   };
-  bool good = cp(dbg->landmarks, B.kt, Pm * pl.d * f) && cp(dbg->C_t, B.ct, Pm * pl.N * f) &&
+  // C^T rows are stored with stride ldc >= N; the debug copy is dense.
+  const bool ct_ok = !dbg->C_t || ok(hipMemcpy2DAsync(dbg->C_t, pl.N * f, B.ct, pl.ldc * f, pl.N * f, Pm,
+                                                      hipMemcpyDeviceToDevice, s),
+                                     "debug copy");
+  bool good = ct_ok && cp(dbg->landmarks, B.kt, Pm * pl.d * f) &&
               cp(dbg->BV, B.bv, Pm * pl.d * f) && cp(dbg->mu, B.mu, Pm * f) && cp(dbg->sigma, B.sigma, Pm * f);
   // Y for m <= 64 lives only in the output stage's LDS; the debug form forms
   // it once more with the tile GEMM into the workspace.

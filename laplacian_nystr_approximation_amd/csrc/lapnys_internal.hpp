@@ -46,6 +46,7 @@ constexpr int kMaxM = 256;
 struct Plan {
   int P;            // B * H problems
   int N, d, m;      // tokens, head dimension, landmarks
+  int ldc;          // row stride of the stored C^T (N rounded up to 4)
   int gw;           // pooled grid width (grid_w / pool)
   int grid_w, pool;
   int dtype;        // lapnys_dtype

@@ -145,12 +145,13 @@ int lapnys_forward_debug(const void* q, const void* k, const void* v, float* out
                          const lapnys_params* p, void* ws, size_t ws_bytes,
                          const lapnys_debug* dbg, hipStream_t stream);
 
-/* lapnys_forward_ws that also records stage_events[2*s] before and
- * stage_events[2*s+1] after stage s (LAPNYS_STAGE_*) on the stream that runs
- * that stage, so hipEventElapsedTime gives per-stage device time.
- * stage_events: array of 2 * LAPNYS_NUM_STAGES events created by the caller;
- * a NULL entry is skipped (record only the stages of interest: every event
- * record is a command on the stream and costs a little time). */
+/* lapnys_forward_ws that also times its stages: stage_events[2*s] receives
+ * the start time of the first kernel of stage s (LAPNYS_STAGE_*) and
+ * stage_events[2*s+1] the end time of its last kernel, taken from the
+ * kernels' own dispatch timestamps (hipExtLaunchKernel's start/stop events),
+ * so hipEventElapsedTime gives the stage's device time and no event command
+ * is inserted between kernels.  stage_events: array of 2 * LAPNYS_NUM_STAGES
+ * events created by the caller; a NULL entry is not recorded. */
 int lapnys_forward_profiled(const void* q, const void* k, const void* v, float* out,
                             const lapnys_params* p, void* ws, size_t ws_bytes,
                             hipEvent_t* stage_events, hipStream_t stream);

@@ -89,9 +89,10 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float2* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_reduce(const Plan& pl, const Work& w, hipStream_t s) {
+hipError_t launch_reduce(const Plan& pl, const Work& w, hipStream_t s, Span t) {
   const int nbv = (pl.m * pl.d + 255) / 256;
-  hipLaunchKernelGGL(reduce_kernel, dim3(nbv + 1, pl.P), dim3(256), 0, s, reinterpret_cast<const float2*>(w.stats),
+  hipExtLaunchKernelGGL(reduce_kernel, dim3(nbv + 1, pl.P), dim3(256), 0, s, t.start, t.stop, 0,
+                        reinterpret_cast<const float2*>(w.stats),
                      w.bvpart, w.bv, w.mu, w.sigma, w.rs, pl.N, pl.m, pl.d, pl.ntiles, pl.tt, pl.groups,
                      pl.whiten ? 1 : 0);
   return hipGetLastError();

@@ -333,7 +333,8 @@ __global__ __launch_bounds__(kTT) void l1exp_kernel(const T* __restrict__ q, con
 }
 
 template <typename T, int D, int LBB>
-hipError_t launch_lbb(const Plan& pl, const void* q, const void* k, const void* v, const Work& w, hipStream_t s) {
+hipError_t launch_lbb(const Plan& pl, const void* q, const void* k, const void* v, const Work& w, hipStream_t s,
+                      Span t) {
   const int lbmax = pl.lb;
   const size_t shmem = (size_t)(lbmax + 1) * kTP * sizeof(float);
   auto kern = l1exp_kernel<T, D, LBB>;
@@ -341,7 +342,8 @@ hipError_t launch_lbb(const Plan& pl, const void* q, const void* k, const void* 
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kern, dim3(pl.jblocks, pl.groups, pl.P), dim3(kTT), shmem, s, (const T*)q, (const T*)k,
+  hipExtLaunchKernelGGL(kern, dim3(pl.jblocks, pl.groups, pl.P), dim3(kTT), shmem, s, t.start, t.stop, 0, (const T*)q,
+                        (const T*)k,
                      (const T*)v, w.kt, w.ct, reinterpret_cast<float2*>(w.stats), w.bvpart, pl.N, pl.ldc, pl.m, lbmax,
                      pl.ntiles, pl.tpg, pl.groups, pl.scale);
   return hipGetLastError();
@@ -349,25 +351,25 @@ hipError_t launch_lbb(const Plan& pl, const void* q, const void* k, const void* 
 
 template <typename T, int D>
 hipError_t launch_typed(const Plan& pl, const void* q, const void* k, const void* v, const Work& w,
-                        hipStream_t s) {
+                        hipStream_t s, Span t) {
   switch ((pl.lb + 15) / 16) {
-    case 1: return launch_lbb<T, D, 1>(pl, q, k, v, w, s);
-    case 2: return launch_lbb<T, D, 2>(pl, q, k, v, w, s);
-    case 3: return launch_lbb<T, D, 3>(pl, q, k, v, w, s);
-    default: return launch_lbb<T, D, 4>(pl, q, k, v, w, s);
+    case 1: return launch_lbb<T, D, 1>(pl, q, k, v, w, s, t);
+    case 2: return launch_lbb<T, D, 2>(pl, q, k, v, w, s, t);
+    case 3: return launch_lbb<T, D, 3>(pl, q, k, v, w, s, t);
+    default: return launch_lbb<T, D, 4>(pl, q, k, v, w, s, t);
   }
 }
 
 }  // namespace
 
 hipError_t launch_l1exp(const Plan& pl, const void* q, const void* k, const void* v, const Work& w,
-                        hipStream_t s) {
+                        hipStream_t s, Span t) {
   if (pl.dtype == 1) {
-    if (pl.d == 64) return launch_typed<uint16_t, 64>(pl, q, k, v, w, s);
-    return launch_typed<uint16_t, 32>(pl, q, k, v, w, s);
+    if (pl.d == 64) return launch_typed<uint16_t, 64>(pl, q, k, v, w, s, t);
+    return launch_typed<uint16_t, 32>(pl, q, k, v, w, s, t);
   }
-  if (pl.d == 64) return launch_typed<float, 64>(pl, q, k, v, w, s);
-  return launch_typed<float, 32>(pl, q, k, v, w, s);
+  if (pl.d == 64) return launch_typed<float, 64>(pl, q, k, v, w, s, t);
+  return launch_typed<float, 32>(pl, q, k, v, w, s, t);
 }
 
 }  // namespace lapnys

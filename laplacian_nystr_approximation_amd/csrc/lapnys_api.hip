@@ -175,8 +175,11 @@ int device_ctx(DeviceCtx** out) {
       c.side = nullptr;
       return LAPNYS_ERR_HIP;
     }
-    if (!ok(hipEventCreateWithFlags(&c.fork, hipEventDisableTiming), "hipEventCreateWithFlags") ||
-        !ok(hipEventCreateWithFlags(&c.join, hipEventDisableTiming), "hipEventCreateWithFlags"))
+    // The fork/join events order work between two streams of one device: a
+    // device-scope release is all they need (no host-visible write-back).
+    const unsigned flags = hipEventDisableTiming | hipEventReleaseToDevice;
+    if (!ok(hipEventCreateWithFlags(&c.fork, flags), "hipEventCreateWithFlags") ||
+        !ok(hipEventCreateWithFlags(&c.join, flags), "hipEventCreateWithFlags"))
       return LAPNYS_ERR_HIP;
   }
   *out = &c;
@@ -193,31 +196,30 @@ int run(const Plan& pl, const void* q, const void* k, const void* v, float* out,
   // An error left by an earlier, unrelated runtime call would otherwise be
   // reported by the first launch check below.
   (void)hipGetLastError();
-  auto mark = [&](int idx, hipStream_t on) {
-    return !ev || !ev[idx] || ok(hipEventRecord(ev[idx], on), "hipEventRecord");
+  auto span = [&](int stage) {
+    lapnys::Span t;
+    if (ev) {
+      t.start = ev[2 * stage];
+      t.stop = ev[2 * stage + 1];
+    }
+    return t;
   };
-  if (!mark(2 * LAPNYS_STAGE_POOL, s)) return LAPNYS_ERR_HIP;
-  if (!ok(lapnys::launch_pool(pl, k, W, s), "pool launch")) return LAPNYS_ERR_HIP;
-  if (!mark(2 * LAPNYS_STAGE_POOL + 1, s)) return LAPNYS_ERR_HIP;
+  const lapnys::Span fin = span(LAPNYS_STAGE_FINALIZE);
+  if (!ok(lapnys::launch_pool(pl, k, W, s, span(LAPNYS_STAGE_POOL)), "pool launch")) return LAPNYS_ERR_HIP;
   // fork: Newton-Schulz on the side stream once the landmarks exist
   if (!ok(hipEventRecord(dc->fork, s), "hipEventRecord") || !ok(hipStreamWaitEvent(side, dc->fork, 0), "hipStreamWaitEvent"))
     return LAPNYS_ERR_HIP;
-  if (!mark(2 * LAPNYS_STAGE_NS, side)) return LAPNYS_ERR_HIP;
-  if (!ok(lapnys::launch_ns(pl, W, side), "Newton-Schulz launch")) return LAPNYS_ERR_HIP;
-  if (!mark(2 * LAPNYS_STAGE_NS + 1, side)) return LAPNYS_ERR_HIP;
+  if (!ok(lapnys::launch_ns(pl, W, side, span(LAPNYS_STAGE_NS)), "Newton-Schulz launch")) return LAPNYS_ERR_HIP;
   if (!ok(hipEventRecord(dc->join, side), "hipEventRecord")) return LAPNYS_ERR_HIP;
   // kernel matrices, statistics and B V on the caller's stream, concurrently
-  if (!mark(2 * LAPNYS_STAGE_KERNEL, s)) return LAPNYS_ERR_HIP;
-  if (!ok(lapnys::launch_l1exp(pl, q, k, v, W, s), "kernel-matrix launch")) return LAPNYS_ERR_HIP;
-  if (!mark(2 * LAPNYS_STAGE_KERNEL + 1, s)) return LAPNYS_ERR_HIP;
-  if (!mark(2 * LAPNYS_STAGE_FINALIZE, s)) return LAPNYS_ERR_HIP;
-  if (!ok(lapnys::launch_reduce(pl, W, s), "reduce launch")) return LAPNYS_ERR_HIP;
+  if (!ok(lapnys::launch_l1exp(pl, q, k, v, W, s, span(LAPNYS_STAGE_KERNEL)), "kernel-matrix launch"))
+    return LAPNYS_ERR_HIP;
+  if (!ok(lapnys::launch_reduce(pl, W, s, {fin.start, pl.fused_ns ? fin.stop : nullptr}), "reduce launch"))
+    return LAPNYS_ERR_HIP;
   // join: everything after needs X
   if (!ok(hipStreamWaitEvent(s, dc->join, 0), "hipStreamWaitEvent")) return LAPNYS_ERR_HIP;
-  if (!pl.fused_ns && !ok(lapnys::launch_y(pl, W, s), "Y launch")) return LAPNYS_ERR_HIP;
-  if (!mark(2 * LAPNYS_STAGE_FINALIZE + 1, s) || !mark(2 * LAPNYS_STAGE_OUTPUT, s)) return LAPNYS_ERR_HIP;
-  if (!ok(lapnys::launch_output(pl, W, out, s), "output launch")) return LAPNYS_ERR_HIP;
-  if (!mark(2 * LAPNYS_STAGE_OUTPUT + 1, s)) return LAPNYS_ERR_HIP;
+  if (!pl.fused_ns && !ok(lapnys::launch_y(pl, W, s, {nullptr, fin.stop}), "Y launch")) return LAPNYS_ERR_HIP;
+  if (!ok(lapnys::launch_output(pl, W, out, s, span(LAPNYS_STAGE_OUTPUT)), "output launch")) return LAPNYS_ERR_HIP;
   return LAPNYS_OK;
 }
 

@@ -3,6 +3,7 @@
 // launchers.  Nothing here is part of the public C ABI (include/lapnys.h).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -73,14 +74,23 @@ struct Work {
   float* x_final;      // the Newton-Schulz result (x or x2), set by launch_ns
 };
 
+// Optional timing events of one stage: the start time of its first kernel and
+// the end time of its last kernel, taken from the kernels' own dispatch
+// timestamps (hipExtLaunchKernel), so no event command sits between kernels.
+// Null members are not recorded.
+struct Span {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
 // Kernel launchers (each returns the hipError_t of its launches).
-hipError_t launch_pool(const Plan& pl, const void* k, const Work& w, hipStream_t s);
-hipError_t launch_ns(const Plan& pl, Work& w, hipStream_t s);
+hipError_t launch_pool(const Plan& pl, const void* k, const Work& w, hipStream_t s, Span t = {});
+hipError_t launch_ns(const Plan& pl, Work& w, hipStream_t s, Span t = {});
 hipError_t launch_l1exp(const Plan& pl, const void* q, const void* k, const void* v, const Work& w,
-                        hipStream_t s);
-hipError_t launch_reduce(const Plan& pl, const Work& w, hipStream_t s);
-hipError_t launch_y(const Plan& pl, const Work& w, hipStream_t s);  // m > kFusedNsMaxM only
-hipError_t launch_output(const Plan& pl, const Work& w, float* out, hipStream_t s);
+                        hipStream_t s, Span t = {});
+hipError_t launch_reduce(const Plan& pl, const Work& w, hipStream_t s, Span t = {});
+hipError_t launch_y(const Plan& pl, const Work& w, hipStream_t s, Span t = {});  // m > kFusedNsMaxM only
+hipError_t launch_output(const Plan& pl, const Work& w, float* out, hipStream_t s, Span t = {});
 hipError_t launch_extract_square(const float* src, int src_ld, float* dst, int n, int P, hipStream_t s);
 
 }  // namespace lapnys

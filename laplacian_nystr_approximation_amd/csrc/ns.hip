@@ -320,25 +320,26 @@ __global__ __launch_bounds__(256) void extract_square_kernel(const float* __rest
 
 }  // namespace
 
-hipError_t launch_ns(const Plan& pl, Work& wk, hipStream_t s) {
+hipError_t launch_ns(const Plan& pl, Work& wk, hipStream_t s, Span t) {
   if (pl.fused_ns) {
     if (pl.d == 64)
-      hipLaunchKernelGGL(ns_fused_kernel<64>, dim3(pl.P), dim3(256), 0, s, wk.kt, wk.w, wk.x, pl.m, pl.scale, pl.eps,
-                         pl.ns_iters);
+      hipExtLaunchKernelGGL(ns_fused_kernel<64>, dim3(pl.P), dim3(256), 0, s, t.start, t.stop, 0, wk.kt, wk.w, wk.x,
+                            pl.m, pl.scale, pl.eps, pl.ns_iters);
     else
-      hipLaunchKernelGGL(ns_fused_kernel<32>, dim3(pl.P), dim3(256), 0, s, wk.kt, wk.w, wk.x, pl.m, pl.scale, pl.eps,
-                         pl.ns_iters);
+      hipExtLaunchKernelGGL(ns_fused_kernel<32>, dim3(pl.P), dim3(256), 0, s, t.start, t.stop, 0, wk.kt, wk.w, wk.x,
+                            pl.m, pl.scale, pl.eps, pl.ns_iters);
     wk.x_final = wk.x;
     return hipGetLastError();
   }
   const int mp = pl.mp;
   if (pl.d == 64)
-    hipLaunchKernelGGL(wbuild_big_kernel<64>, dim3(mp / 16, pl.P), dim3(256), 0, s, wk.kt, wk.w, pl.m, mp, pl.scale,
-                       pl.eps);
+    hipExtLaunchKernelGGL(wbuild_big_kernel<64>, dim3(mp / 16, pl.P), dim3(256), 0, s, t.start, nullptr, 0, wk.kt,
+                          wk.w, pl.m, mp, pl.scale, pl.eps);
   else
-    hipLaunchKernelGGL(wbuild_big_kernel<32>, dim3(mp / 16, pl.P), dim3(256), 0, s, wk.kt, wk.w, pl.m, mp, pl.scale,
-                       pl.eps);
-  hipLaunchKernelGGL(alpha_x0_kernel, dim3(pl.P), dim3(256), 0, s, wk.w, wk.x, mp);
+    hipExtLaunchKernelGGL(wbuild_big_kernel<32>, dim3(mp / 16, pl.P), dim3(256), 0, s, t.start, nullptr, 0, wk.kt,
+                          wk.w, pl.m, mp, pl.scale, pl.eps);
+  hipExtLaunchKernelGGL(alpha_x0_kernel, dim3(pl.P), dim3(256), 0, s, nullptr, pl.ns_iters == 0 ? t.stop : nullptr, 0,
+                        wk.w, wk.x, mp);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int kext = (pl.m + 31) & ~31;
@@ -349,8 +350,8 @@ hipError_t launch_ns(const Plan& pl, Work& wk, hipStream_t s) {
   for (int it = 0; it < pl.ns_iters; ++it) {
     hipLaunchKernelGGL(gemm64_kernel, grid, dim3(256), 0, s, wk.w, mp, sq, xc, mp, sq, mp, mp, wk.pm, mp, sq, mp, mp,
                        kext, 0);
-    hipLaunchKernelGGL(gemm64_kernel, grid, dim3(256), 0, s, xc, mp, sq, wk.pm, mp, sq, mp, mp, xn, mp, sq, mp, mp,
-                       kext, 1);
+    hipExtLaunchKernelGGL(gemm64_kernel, grid, dim3(256), 0, s, nullptr, it + 1 == pl.ns_iters ? t.stop : nullptr, 0,
+                          xc, mp, sq, wk.pm, mp, sq, mp, mp, xn, mp, sq, mp, mp, kext, 1);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     float* t = xc;
@@ -361,10 +362,11 @@ hipError_t launch_ns(const Plan& pl, Work& wk, hipStream_t s) {
   return hipSuccess;
 }
 
-hipError_t launch_y(const Plan& pl, const Work& wk, hipStream_t s) {
+hipError_t launch_y(const Plan& pl, const Work& wk, hipStream_t s, Span t) {
   const int kext = (pl.m + 31) & ~31;
   const long long md = (long long)pl.m * pl.d;
-  hipLaunchKernelGGL(gemm64_kernel, dim3((pl.m + 63) / 64, (pl.d + 63) / 64, pl.P), dim3(256), 0, s, wk.x_final,
+  hipExtLaunchKernelGGL(gemm64_kernel, dim3((pl.m + 63) / 64, (pl.d + 63) / 64, pl.P), dim3(256), 0, s, t.start,
+                        t.stop, 0, wk.x_final,
                      pl.mp, (long long)pl.mp * pl.mp, wk.bv, pl.d, md, pl.m, pl.d, wk.y, pl.d, md, pl.m, pl.d, kext, 0);
   return hipGetLastError();
 }

@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256) void output_kernel(const float* __restrict__ c
 }
 
 template <int D, bool FUSED_Y>
-hipError_t launch_typed(const Plan& pl, const Work& wk, float* out, hipStream_t s) {
+hipError_t launch_typed(const Plan& pl, const Work& wk, float* out, hipStream_t s, Span t) {
   const int m4 = (pl.m + 3) & ~3;
   // yl, then the (mu, 1/sigma) pairs (64 of them in the fused form, so that
   // the prologue's X and B V buffers start at a fixed offset).
@@ -207,20 +207,21 @@ hipError_t launch_typed(const Plan& pl, const Work& wk, float* out, hipStream_t 
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kern, dim3((pl.N + 255) / 256, pl.P), dim3(256), shmem, s, wk.ct, pl.ldc, wk.x_final, pl.mp,
+  hipExtLaunchKernelGGL(kern, dim3((pl.N + 255) / 256, pl.P), dim3(256), shmem, s, t.start, t.stop, 0, wk.ct, pl.ldc,
+                        wk.x_final, pl.mp,
                      wk.bv, wk.y, wk.mu, wk.rs, out, pl.N, pl.m);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_output(const Plan& pl, const Work& wk, float* out, hipStream_t s) {
+hipError_t launch_output(const Plan& pl, const Work& wk, float* out, hipStream_t s, Span t) {
   if (pl.fused_ns) {
-    if (pl.d == 64) return launch_typed<64, true>(pl, wk, out, s);
-    return launch_typed<32, true>(pl, wk, out, s);
+    if (pl.d == 64) return launch_typed<64, true>(pl, wk, out, s, t);
+    return launch_typed<32, true>(pl, wk, out, s, t);
   }
-  if (pl.d == 64) return launch_typed<64, false>(pl, wk, out, s);
-  return launch_typed<32, false>(pl, wk, out, s);
+  if (pl.d == 64) return launch_typed<64, false>(pl, wk, out, s, t);
+  return launch_typed<32, false>(pl, wk, out, s, t);
 }
 
 }  // namespace lapnys

@@ -54,24 +54,24 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ k, floa
 }
 
 template <typename T>
-void launch_typed(const Plan& pl, const T* k, float* kt, hipStream_t s) {
+void launch_typed(const Plan& pl, const T* k, float* kt, hipStream_t s, Span t) {
   const long long total = (long long)pl.P * pl.m * pl.d;
   const dim3 grid((unsigned)((total + 255) / 256)), block(256);
   switch (pl.pool) {
-    case 1: hipLaunchKernelGGL((pool_kernel<T, 1>), grid, block, 0, s, k, kt, pl.N, pl.d, pl.grid_w, 1, pl.gw, pl.m, total); break;
-    case 2: hipLaunchKernelGGL((pool_kernel<T, 2>), grid, block, 0, s, k, kt, pl.N, pl.d, pl.grid_w, 2, pl.gw, pl.m, total); break;
-    case 4: hipLaunchKernelGGL((pool_kernel<T, 4>), grid, block, 0, s, k, kt, pl.N, pl.d, pl.grid_w, 4, pl.gw, pl.m, total); break;
-    case 8: hipLaunchKernelGGL((pool_kernel<T, 8>), grid, block, 0, s, k, kt, pl.N, pl.d, pl.grid_w, 8, pl.gw, pl.m, total); break;
-    case 16: hipLaunchKernelGGL((pool_kernel<T, 16>), grid, block, 0, s, k, kt, pl.N, pl.d, pl.grid_w, 16, pl.gw, pl.m, total); break;
-    default: hipLaunchKernelGGL((pool_kernel<T, 0>), grid, block, 0, s, k, kt, pl.N, pl.d, pl.grid_w, pl.pool, pl.gw, pl.m, total); break;
+    case 1: hipExtLaunchKernelGGL((pool_kernel<T, 1>), grid, block, 0, s, t.start, t.stop, 0, k, kt, pl.N, pl.d, pl.grid_w, 1, pl.gw, pl.m, total); break;
+    case 2: hipExtLaunchKernelGGL((pool_kernel<T, 2>), grid, block, 0, s, t.start, t.stop, 0, k, kt, pl.N, pl.d, pl.grid_w, 2, pl.gw, pl.m, total); break;
+    case 4: hipExtLaunchKernelGGL((pool_kernel<T, 4>), grid, block, 0, s, t.start, t.stop, 0, k, kt, pl.N, pl.d, pl.grid_w, 4, pl.gw, pl.m, total); break;
+    case 8: hipExtLaunchKernelGGL((pool_kernel<T, 8>), grid, block, 0, s, t.start, t.stop, 0, k, kt, pl.N, pl.d, pl.grid_w, 8, pl.gw, pl.m, total); break;
+    case 16: hipExtLaunchKernelGGL((pool_kernel<T, 16>), grid, block, 0, s, t.start, t.stop, 0, k, kt, pl.N, pl.d, pl.grid_w, 16, pl.gw, pl.m, total); break;
+    default: hipExtLaunchKernelGGL((pool_kernel<T, 0>), grid, block, 0, s, t.start, t.stop, 0, k, kt, pl.N, pl.d, pl.grid_w, pl.pool, pl.gw, pl.m, total); break;
   }
 }
 
-hipError_t launch_pool(const Plan& pl, const void* k, const Work& w, hipStream_t s) {
+hipError_t launch_pool(const Plan& pl, const void* k, const Work& w, hipStream_t s, Span t) {
   if (pl.dtype == 1)
-    launch_typed<uint16_t>(pl, (const uint16_t*)k, w.kt, s);
+    launch_typed<uint16_t>(pl, (const uint16_t*)k, w.kt, s, t);
   else
-    launch_typed<float>(pl, (const float*)k, w.kt, s);
+    launch_typed<float>(pl, (const float*)k, w.kt, s, t);
   return hipGetLastError();
 }
 

@@ -197,17 +197,22 @@ def lapnys_release() -> None:
 class HipEvents:
     """Raw hipEvent_t handles from the HIP runtime (timing events for the profiled form)."""
 
-    def __init__(self, n: int):
+    # hipEventDisableSystemFence: a timing-only event, recorded without the
+    # system-scope cache write-back that would otherwise stretch the work
+    # around it.
+    TIMING_ONLY = 0x20000000
+
+    def __init__(self, n: int, flags: int = TIMING_ONLY):
         self._hip = ctypes.CDLL("libamdhip64.so")
-        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                   ctypes.c_void_p]
         self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.handles = []
         for _ in range(n):
             h = ctypes.c_void_p()
-            if self._hip.hipEventCreate(ctypes.byref(h)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            if self._hip.hipEventCreateWithFlags(ctypes.byref(h), flags) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
             self.handles.append(h.value)
 
     def elapsed_ms(self, a: int, b: int) -> float:

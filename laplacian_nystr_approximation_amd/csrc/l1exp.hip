@@ -88,106 +88,72 @@ struct VHalf {
   __device__ __forceinline__ float get(int i) const { return widen(w[i]); }
 };
 
-// A landmark row spread over the 16 lanes of a DPP row: lane li holds
-// features KW li .. KW li + KW - 1 (KW = D / 16).  Every 16-lane row of the
-// wavefront holds the same copy, so a row_newbcast:i source operand hands
-// feature KW i + c of the landmark to all 64 lanes inside the VALU
-// instruction itself: one 16-byte load per lane feeds D subtractions.
+// Where each of the four landmarks of a group reads its features from:
+// kLds = broadcast reads of the block's landmark rows staged in LDS (every
+// lane reads the same 16 bytes); kSgpr = scalar loads of the rows in global
+// memory (wave-uniform addresses), feeding the subtract as an SGPR operand.
+// Both leave the VALU free to dual-issue from two wavefronts (a DPP-broadcast
+// operand does not).  Scalar loads are as fast when the scalar cache holds
+// the rows, but workgroups of different problems sharing a CU evict each
+// other's rows, so every landmark reads from LDS.
+constexpr int kLds = 0, kSgpr = 1;
+constexpr int kSrc[4] = {kLds, kLds, kLds, kLds};
+
+// tl[j][col] = exp2(scale * sum_t |x[t] - k_j[t]|) for the lb landmarks of the
+// block (0 for a lane past the last token).  kl: the block's landmark rows in
+// LDS; kg: the same rows in global memory.  Four landmarks at a time, each
+// with two partial sums (even / odd features), give eight independent add
+// chains; the operands of the next 4-feature chunk are loaded while the
+// current chunk is summed, and the compiler barriers keep that shape.
 template <int D>
-struct KRow {
-  static constexpr int KW = D / 16;
-  float v[KW];
-  __device__ __forceinline__ void load(const float* __restrict__ row, int li) {
-    if constexpr (KW == 4) {
-      const float4 t = *reinterpret_cast<const float4*>(row + 4 * li);
-      v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
-    } else {
-      const float2 t = *reinterpret_cast<const float2*>(row + 2 * li);
-      v[0] = t.x; v[1] = t.y;
-    }
-  }
-};
-
-template <int I>
-__device__ __forceinline__ float row_bcast(float v) {
-  // DPP row_newbcast:I (control 0x150 + I): lane I of each 16-lane row.
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + I, 0xF, 0xF, false));
-}
-
-// Adds |x[t] - k_u[t]| over the features of the U landmark rows kr[u] into
-// sa[u] (even t) and sb[u] (odd t), in increasing t.  The compiler barrier
-// after each 16-lane broadcast step keeps every subtraction next to its add
-// (otherwise all D differences are computed first and held in registers).
-template <int D, int U, int I = 0>
-__device__ __forceinline__ void l1_accumulate(const float (&x)[D], const KRow<D> (&kr)[U], float (&sa)[U],
-                                              float (&sb)[U]) {
-  if constexpr (I < 16) {
-    constexpr int KW = KRow<D>::KW;
-#pragma unroll
-    for (int c = 0; c < KW; ++c) {
-      // All U differences first, then the U adds: consecutive DPP
-      // instructions then write different registers (a DPP result register
-      // read again within two instructions costs a wait state).
-      float dv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) dv[u] = x[KW * I + c] - row_bcast<I>(kr[u].v[c]);
-      if constexpr (U == 4) {
-        asm volatile("" : "+v"(dv[0]), "+v"(dv[1]), "+v"(dv[2]), "+v"(dv[3]));
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if ((KW * I + c) % 2 == 0) sa[u] += fabsf(dv[u]); else sb[u] += fabsf(dv[u]);
-      }
-    }
-    if constexpr (U == 4) {
-      asm volatile("" : "+v"(sa[0]), "+v"(sa[1]), "+v"(sa[2]), "+v"(sa[3]), "+v"(sb[0]), "+v"(sb[1]), "+v"(sb[2]),
-                   "+v"(sb[3]));
-    } else {
-      asm volatile("" : "+v"(sa[0]), "+v"(sb[0]));
-    }
-    l1_accumulate<D, U, I + 1>(x, kr, sa, sb);
-  }
-}
-
-// tl[j][col] = exp2(scale * sum_t |x[t] - kg[j][t]|) for the lb landmarks of the
-// block (0 for a lane past the last token).  kg points at the block's K~ rows
-// in global memory (a few KB per problem, served from cache).  Four landmarks
-// at a time, each with two partial sums (even / odd features), give eight
-// independent add chains; the next four landmark rows are loaded while the
-// current four are summed.
-template <int D>
-__device__ __forceinline__ void kernel_row(const float (&x)[D], const float* __restrict__ kg, int lb, float scale,
-                                           float* __restrict__ tl, int col, bool valid, int li) {
-  const int lb4 = lb & ~3;
-  KRow<D> kv[4];
-  if (lb4 > 0) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) kv[u].load(kg + u * D, li);
-  }
-  for (int j = 0; j < lb4; j += 4) {
-    KRow<D> kn[4];
-    const int jn = j + 4 < lb4 ? j + 4 : j;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) kn[u].load(kg + (jn + u) * D, li);
+__device__ __forceinline__ void kernel_row(const float (&x)[D], const float* __restrict__ kl,
+                                           const float* __restrict__ kg, int lb, float scale, float* __restrict__ tl,
+                                           int col, bool valid) {
+  int j = 0;
+  for (; j + 4 <= lb; j += 4) {
     float sa[4] = {0.f, 0.f, 0.f, 0.f}, sb[4] = {0.f, 0.f, 0.f, 0.f};
-    l1_accumulate<D, 4>(x, kv, sa, sb);
+    float4 kv[2][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      kv[0][u] = *reinterpret_cast<const float4*>((kSrc[u] == kLds ? kl : kg) + (j + u) * D);
+#pragma unroll
+    for (int c = 0; c < D / 4; ++c) {
+      const int cur = c & 1;
+      if (c + 1 < D / 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          kv[cur ^ 1][u] = *reinterpret_cast<const float4*>((kSrc[u] == kLds ? kl : kg) + (j + u) * D + 4 * (c + 1));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        sa[u] += fabsf(x[4 * c + 0] - kv[cur][u].x);
+        sb[u] += fabsf(x[4 * c + 1] - kv[cur][u].y);
+        sa[u] += fabsf(x[4 * c + 2] - kv[cur][u].z);
+        sb[u] += fabsf(x[4 * c + 3] - kv[cur][u].w);
+      }
+      asm volatile("" : "+v"(sa[0]), "+v"(sa[1]), "+v"(sa[2]), "+v"(sa[3]), "+v"(sb[0]), "+v"(sb[1]),
+                   "+v"(sb[2]), "+v"(sb[3])::"memory");
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) tl[(j + u) * kTP + col] = valid ? exp2f((sa[u] + sb[u]) * scale) : 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) kv[u] = kn[u];
   }
-  for (int j = lb4; j < lb; ++j) {
-    KRow<D> kr[1];
-    kr[0].load(kg + j * D, li);
-    float sa[1] = {0.f}, sb[1] = {0.f};
-    l1_accumulate<D, 1>(x, kr, sa, sb);
-    tl[j * kTP + col] = valid ? exp2f((sa[0] + sb[0]) * scale) : 0.f;
+  for (; j < lb; ++j) {
+    float sa = 0.f, sb = 0.f;
+#pragma unroll
+    for (int t = 0; t < D; t += 4) {
+      const float4 kv = *reinterpret_cast<const float4*>(kl + j * D + t);
+      sa += fabsf(x[t + 0] - kv.x);
+      sb += fabsf(x[t + 1] - kv.y);
+      sa += fabsf(x[t + 2] - kv.z);
+      sb += fabsf(x[t + 3] - kv.w);
+    }
+    tl[j * kTP + col] = valid ? exp2f((sa + sb) * scale) : 0.f;
   }
 }
 
 // Grid: (landmark block, tile group, problem).  LBB = 16-row blocks per
-// landmark block (lb rounded up to 16, over 16).  Dynamic LDS:
-// (lb + 1) * kTP floats.
+// landmark block (lb rounded up to 16, over 16).  Dynamic LDS: the tile
+// buffer, then the block's landmark rows: (lbmax + 1) * kTP + lbmax * D floats.
 template <typename T, int D, int LBB>
 __global__ __launch_bounds__(kTT) void l1exp_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                     const T* __restrict__ v, const float* __restrict__ kt,
@@ -195,6 +161,7 @@ __global__ __launch_bounds__(kTT) void l1exp_kernel(const T* __restrict__ q, con
                                                     float* __restrict__ bvpart, int N, int ldc, int m, int lbmax, int ntiles,
                                                     int tpg, int groups, float scale) {
   extern __shared__ float tl[];  // [lb + 1][kTP]; row lb stays zero
+  float* kl = tl + (lbmax + 1) * kTP;  // [lb][D]: this block's landmark rows
 
   const int jb = blockIdx.x, g = blockIdx.y, p = blockIdx.z;
   const int j0 = jb * lbmax;
@@ -203,6 +170,7 @@ __global__ __launch_bounds__(kTT) void l1exp_kernel(const T* __restrict__ q, con
 
   const float* kg = kt + ((size_t)p * m + j0) * D;  // this block's K~ rows
   for (int e = lb * kTP + tid; e < (lb + 1) * kTP; e += kTT) tl[e] = 0.f;
+  for (int e = tid; e < lb * D; e += kTT) kl[e] = kg[e];
   const int li = lane & 15, lk = lane >> 4;
 
   // B V output blocks (16 x 16) of this wavefront: one 16-feature column block
@@ -243,7 +211,7 @@ __global__ __launch_bounds__(kTT) void l1exp_kernel(const T* __restrict__ q, con
     issue_row<T, D>(q + row, valid, raw);
     widen_row<D>(raw, x);
     __syncthreads();  // tile buffer free (previous tile's MFMA reads done)
-    kernel_row<D>(x, kg, lb, scale, tl, tid, valid, li);
+    kernel_row<D>(x, kl, kg, lb, scale, tl, tid, valid);
     __syncthreads();
 
     // The key row and this lane's V operands are issued now and arrive while
@@ -286,7 +254,7 @@ __global__ __launch_bounds__(kTT) void l1exp_kernel(const T* __restrict__ q, con
     // ---- B = k(K~, K), kept on chip ----
     widen_row<D>(raw, x);
     __syncthreads();  // statistics pass done with the tile buffer
-    kernel_row<D>(x, kg, lb, scale, tl, tid, valid, li);
+    kernel_row<D>(x, kl, kg, lb, scale, tl, tid, valid);
     __syncthreads();
 
     // ---- B V partial: acc[landmark][feature] += sum over the tile's tokens ----
@@ -336,7 +304,7 @@ template <typename T, int D, int LBB>
 hipError_t launch_lbb(const Plan& pl, const void* q, const void* k, const void* v, const Work& w, hipStream_t s,
                       Span t) {
   const int lbmax = pl.lb;
-  const size_t shmem = (size_t)(lbmax + 1) * kTP * sizeof(float);
+  const size_t shmem = ((size_t)(lbmax + 1) * kTP + (size_t)lbmax * D) * sizeof(float);
   auto kern = l1exp_kernel<T, D, LBB>;
   if (shmem > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);

@@ -57,30 +57,51 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float2* __restrict__ 
     return;
   }
   const float2* st = stats + (size_t)p * ntiles * m + j;
-  double total = 0.0;
-  for (int i0 = 0; i0 < ntiles; i0 += kChunk) {
-    float v[kChunk];
-#pragma unroll
-    for (int u = 0; u < kChunk; ++u) v[u] = (i0 + u < ntiles) ? st[(size_t)(i0 + u) * m].x : 0.f;
-#pragma unroll
-    for (int u = 0; u < kChunk; ++u)
-      if (i0 + u < ntiles) total += (double)v[u];
-  }
-  const double mean = total / (double)N;
-  double m2 = 0.0;
-  for (int i0 = 0; i0 < ntiles; i0 += kChunk) {
+  // Each chunk of (sum, M2) pairs is loaded once when the tiles fit in one
+  // chunk (the common case): the mean needs every tile's sum first, and the
+  // deviation pass reuses the same registers.
+  double total = 0.0, m2 = 0.0;
+  if (ntiles <= kChunk) {
     float2 v[kChunk];
 #pragma unroll
-    for (int u = 0; u < kChunk; ++u) v[u] = (i0 + u < ntiles) ? st[(size_t)(i0 + u) * m] : make_float2(0.f, 0.f);
+    for (int u = 0; u < kChunk; ++u) v[u] = (u < ntiles) ? st[(size_t)u * m] : make_float2(0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u)
+      if (u < ntiles) total += (double)v[u].x;
+    const double mean = total / (double)N;
 #pragma unroll
     for (int u = 0; u < kChunk; ++u) {
-      if (i0 + u < ntiles) {
-        const int n = min(tt, N - (i0 + u) * tt);
+      if (u < ntiles) {
+        const int n = min(tt, N - u * tt);
         const double dm = (double)v[u].x / (double)n - mean;
         m2 += (double)v[u].y + (double)n * dm * dm;
       }
     }
+  } else {
+    for (int i0 = 0; i0 < ntiles; i0 += kChunk) {
+      float v[kChunk];
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) v[u] = (i0 + u < ntiles) ? st[(size_t)(i0 + u) * m].x : 0.f;
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u)
+        if (i0 + u < ntiles) total += (double)v[u];
+    }
+    const double mean = total / (double)N;
+    for (int i0 = 0; i0 < ntiles; i0 += kChunk) {
+      float2 v[kChunk];
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) v[u] = (i0 + u < ntiles) ? st[(size_t)(i0 + u) * m] : make_float2(0.f, 0.f);
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) {
+        if (i0 + u < ntiles) {
+          const int n = min(tt, N - (i0 + u) * tt);
+          const double dm = (double)v[u].x / (double)n - mean;
+          m2 += (double)v[u].y + (double)n * dm * dm;
+        }
+      }
+    }
   }
+  const double mean = total / (double)N;
   const double sd = sqrt(m2 / (double)N);
   mu[p * m + j] = (float)mean;
   sigma[p * m + j] = (float)sd;

@@ -3,15 +3,16 @@
 // library-owned workspace of lapnys_forward, and the debug/profiled forms.
 //
 // Stage sequence (no host synchronisation):
-//   pool      K -> K~                                           caller's stream
-//   ns        K~ -> W, X = NS inverse of W                      side stream (forked)
+//   pool      K -> K~                                           side stream (forked)
+//   ns        K~ -> W, X = NS inverse of W                      side stream
 //   kernel    Q, K, V, K~ -> C^T, tile statistics, B V partials caller's stream
 //   finalize  partials -> mu, sigma, B V; for m > 64 also
 //             Y = X (B V) on a tile GEMM (after the join)       caller's stream
 //   output    Y = X (B V) for m <= 64, then O = whiten(C) Y     caller's stream
 // The Newton-Schulz stage depends only on the landmarks, so it runs on a
 // library-owned stream of the device (default priority) concurrently with the
-// kernel-matrix stage and joins before the stages that need X.
+// kernel-matrix stage, which waits for the pool stage across streams, and
+// joins before the stages that need X.
 #include <math.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -160,7 +161,7 @@ lapnys::Work carve(const Plan& pl, void* ws) {
 // Per-device side stream and the fork/join events, created on first use.
 struct DeviceCtx {
   hipStream_t side = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t fork = nullptr, pooled = nullptr, join = nullptr;
 };
 std::mutex g_ctx_mu;  // also serialises the fork/join sequence of concurrent callers
 std::vector<DeviceCtx> g_ctx;
@@ -179,7 +180,8 @@ int device_ctx(DeviceCtx** out) {
     // device-scope release is all they need (no host-visible write-back).
     const unsigned flags = hipEventDisableTiming | hipEventReleaseToDevice;
     if (!ok(hipEventCreateWithFlags(&c.fork, flags), "hipEventCreateWithFlags") ||
-        !ok(hipEventCreateWithFlags(&c.join, flags), "hipEventCreateWithFlags"))
+        !ok(hipEventCreateWithFlags(&c.join, flags), "hipEventCreateWithFlags") ||
+        !ok(hipEventCreateWithFlags(&c.pooled, flags), "hipEventCreateWithFlags"))
       return LAPNYS_ERR_HIP;
   }
   *out = &c;
@@ -205,12 +207,18 @@ int run(const Plan& pl, const void* q, const void* k, const void* v, float* out,
     return t;
   };
   const lapnys::Span fin = span(LAPNYS_STAGE_FINALIZE);
-  if (!ok(lapnys::launch_pool(pl, k, W, s, span(LAPNYS_STAGE_POOL)), "pool launch")) return LAPNYS_ERR_HIP;
-  // fork: Newton-Schulz on the side stream once the landmarks exist
+  // fork: everything before this call on the caller's stream precedes the side stream's work
   if (!ok(hipEventRecord(dc->fork, s), "hipEventRecord") || !ok(hipStreamWaitEvent(side, dc->fork, 0), "hipStreamWaitEvent"))
     return LAPNYS_ERR_HIP;
+  // The pool stage runs on the side stream right before the solver, and the
+  // caller's stream waits for it across streams: the solver's workgroups are
+  // then dispatched before the kernel-matrix stage's and always find room on
+  // the CUs (started after, they can wait for CUs until that stage drains).
+  if (!ok(lapnys::launch_pool(pl, k, W, side, span(LAPNYS_STAGE_POOL)), "pool launch")) return LAPNYS_ERR_HIP;
+  if (!ok(hipEventRecord(dc->pooled, side), "hipEventRecord")) return LAPNYS_ERR_HIP;
   if (!ok(lapnys::launch_ns(pl, W, side, span(LAPNYS_STAGE_NS)), "Newton-Schulz launch")) return LAPNYS_ERR_HIP;
   if (!ok(hipEventRecord(dc->join, side), "hipEventRecord")) return LAPNYS_ERR_HIP;
+  if (!ok(hipStreamWaitEvent(s, dc->pooled, 0), "hipStreamWaitEvent")) return LAPNYS_ERR_HIP;
   // kernel matrices, statistics and B V on the caller's stream, concurrently
   if (!ok(lapnys::launch_l1exp(pl, q, k, v, W, s, span(LAPNYS_STAGE_KERNEL)), "kernel-matrix launch"))
     return LAPNYS_ERR_HIP;

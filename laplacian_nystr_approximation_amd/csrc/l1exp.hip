@@ -25,6 +25,7 @@
 // the C store are coalesced and the MFMA reads B columns without bank
 // conflicts.
 #include "lapnys_internal.hpp"
+#include "ns_small.hpp"
 
 namespace lapnys {
 
@@ -151,19 +152,20 @@ __device__ __forceinline__ void kernel_row(const float (&x)[D], const float* __r
   }
 }
 
-// Grid: (landmark block, tile group, problem).  LBB = 16-row blocks per
-// landmark block (lb rounded up to 16, over 16).  Dynamic LDS: the tile
-// buffer, then the block's landmark rows: (lbmax + 1) * kTP + lbmax * D floats.
+// One workgroup's share of the stage: landmark block jb (lb <= lbmax
+// landmarks from j0 = jb * lbmax), tile group g, problem p.  LBB = 16-row
+// blocks per landmark block (lbmax rounded up to 16, over 16).  tl: the
+// workgroup's LDS, (lbmax + 1) * kTP + lbmax * D floats.
 template <typename T, int D, int LBB>
-__global__ __launch_bounds__(kTT) void l1exp_kernel(const T* __restrict__ q, const T* __restrict__ k,
-                                                    const T* __restrict__ v, const float* __restrict__ kt,
-                                                    float* __restrict__ ct, float2* __restrict__ stats,
-                                                    float* __restrict__ bvpart, int N, int ldc, int m, int lbmax, int ntiles,
-                                                    int tpg, int groups, float scale) {
-  extern __shared__ float tl[];  // [lb + 1][kTP]; row lb stays zero
-  float* kl = tl + (lbmax + 1) * kTP;  // [lb][D]: this block's landmark rows
+__device__ __forceinline__ void l1exp_body(const T* __restrict__ q, const T* __restrict__ k,
+                                           const T* __restrict__ v, const float* __restrict__ kt,
+                                           float* __restrict__ ct, float2* __restrict__ stats,
+                                           float* __restrict__ bvpart, int N, int ldc, int m, int lbmax, int ntiles,
+                                           int tpg, int groups, float scale, int jb, int g, int p,
+                                           float* __restrict__ tl) {
+  // tl: [lb + 1][kTP], row lb stays zero; then kl: [lb][D], this block's landmark rows
+  float* kl = tl + (lbmax + 1) * kTP;
 
-  const int jb = blockIdx.x, g = blockIdx.y, p = blockIdx.z;
   const int j0 = jb * lbmax;
   const int lb = min(lbmax, m - j0);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -300,37 +302,109 @@ __global__ __launch_bounds__(kTT) void l1exp_kernel(const T* __restrict__ q, con
 
 }
 
-template <typename T, int D, int LBB>
-hipError_t launch_lbb(const Plan& pl, const void* q, const void* k, const void* v, const Work& w, hipStream_t s,
-                      Span t) {
+// The stage's launch.  For m <= 64 (KS > 0) the first nns workgroups each run
+// one problem's Newton-Schulz schedule (ns_small.hpp) and the rest the
+// kernel-matrix work, so the two share the machine without a second stream or
+// any cross-stream wait: workgroups start in index order, the solver's first,
+// and the workgroups [gap, gap + nns) that would share a CU with them exit at
+// once.  Grid: nns + jblocks * groups * P workgroups (plus nns empty ones),
+// the kernel-matrix ones numbered landmark block fastest, then tile group,
+// then problem.
+// Dynamic LDS: the larger of the two parts' needs, 16-byte aligned.  The
+// register budget of the union of both parts is held to three wavefronts per
+// SIMD (the L1 loop needs at least two to dual-issue).
+template <typename T, int D, int LBB, int KS>
+__global__ __launch_bounds__(kTT) void l1exp_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ kt,
+    float* __restrict__ ct, float2* __restrict__ stats, float* __restrict__ bvpart, float* __restrict__ wout,
+    float* __restrict__ xout, int N, int ldc, int m, int lbmax, int ntiles, int tpg, int groups, int jblocks,
+    float scale, float eps, int iters, int nns, int gap) {
+  extern __shared__ __align__(16) float lds[];
+  int b = blockIdx.x;
+  if constexpr (KS > 0) {
+    if (b < nns) {
+      ns_detail::ns_small<D, KS>(kt, wout, xout, m, scale, eps, iters, b, lds);
+      return;
+    }
+    // Workgroups [gap, gap + nns) do nothing (see launch_kernel).
+    if (b >= gap && b < gap + nns) return;
+    b -= b >= gap ? 2 * nns : nns;
+  }
+  const int jb = b % jblocks, g = (b / jblocks) % groups, p = b / (jblocks * groups);
+  l1exp_body<T, D, LBB>(q, k, v, kt, ct, stats, bvpart, N, ldc, m, lbmax, ntiles, tpg, groups, scale, jb, g, p, lds);
+}
+
+// CUs of the current device (queried once per device; 0 if unknown).
+int cu_count() {
+  static int cached[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <typename T, int D, int LBB, int KS>
+hipError_t launch_kernel(const Plan& pl, const void* q, const void* k, const void* v, Work& w, hipStream_t s,
+                         Span t) {
   const int lbmax = pl.lb;
-  const size_t shmem = ((size_t)(lbmax + 1) * kTP + (size_t)lbmax * D) * sizeof(float);
-  auto kern = l1exp_kernel<T, D, LBB>;
+  size_t floats = (size_t)(lbmax + 1) * kTP + (size_t)lbmax * D;
+  if (KS > 0 && floats < (size_t)ns_detail::kNsLdsFloats) floats = ns_detail::kNsLdsFloats;
+  const size_t shmem = floats * sizeof(float);
+  auto kern = l1exp_kernel<T, D, LBB, KS>;
   if (shmem > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
   }
-  hipExtLaunchKernelGGL(kern, dim3(pl.jblocks, pl.groups, pl.P), dim3(kTT), shmem, s, t.start, t.stop, 0, (const T*)q,
-                        (const T*)k,
-                     (const T*)v, w.kt, w.ct, reinterpret_cast<float2*>(w.stats), w.bvpart, pl.N, pl.ldc, pl.m, lbmax,
-                     pl.ntiles, pl.tpg, pl.groups, pl.scale);
+  // Workgroups are placed on the CUs in index order, one per CU per round, so
+  // workgroup i and workgroup i + (CU count) share a CU.  The second-round
+  // workgroups that would land beside the solver workgroups (ids cus .. cus +
+  // nns - 1) exit at once: a kernel-matrix workgroup there would only get the
+  // issue slots the solver leaves, and finish last.  (If the placement differs,
+  // only the balance changes.)
+  const int nns = KS > 0 ? pl.P : 0;
+  long long grid = (long long)nns + (long long)pl.jblocks * pl.groups * pl.P;
+  int gap = 0x7fffffff;
+  if (nns > 0) {
+    const int cus = cu_count();
+    if (cus > 0 && nns <= cus && grid > cus) {
+      gap = cus;
+      grid += nns;
+    }
+  }
+  hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kTT), shmem, s, t.start, t.stop, 0, (const T*)q,
+                        (const T*)k, (const T*)v, w.kt, w.ct, reinterpret_cast<float2*>(w.stats), w.bvpart, w.w,
+                        w.x, pl.N, pl.ldc, pl.m, lbmax, pl.ntiles, pl.tpg, pl.groups, pl.jblocks, pl.scale, pl.eps,
+                        pl.ns_iters, nns, gap);
+  if (KS > 0) w.x_final = w.x;
   return hipGetLastError();
 }
 
-template <typename T, int D>
-hipError_t launch_typed(const Plan& pl, const void* q, const void* k, const void* v, const Work& w,
-                        hipStream_t s, Span t) {
-  switch ((pl.lb + 15) / 16) {
-    case 1: return launch_lbb<T, D, 1>(pl, q, k, v, w, s, t);
-    case 2: return launch_lbb<T, D, 2>(pl, q, k, v, w, s, t);
-    case 3: return launch_lbb<T, D, 3>(pl, q, k, v, w, s, t);
-    default: return launch_lbb<T, D, 4>(pl, q, k, v, w, s, t);
+// m <= 64: the Newton-Schulz step count KS = ceil(m / 4) and the landmark
+// row blocks LBB = ceil(m / 16) are compile-time constants.
+template <typename T, int D, int KS = 1>
+hipError_t launch_fused(const Plan& pl, const void* q, const void* k, const void* v, Work& w, hipStream_t s,
+                        Span t) {
+  if constexpr (KS < 16) {
+    if ((pl.m + 3) / 4 > KS) return launch_fused<T, D, KS + 1>(pl, q, k, v, w, s, t);
   }
+  return launch_kernel<T, D, (KS + 3) / 4, KS>(pl, q, k, v, w, s, t);
+}
+
+template <typename T, int D>
+hipError_t launch_typed(const Plan& pl, const void* q, const void* k, const void* v, Work& w, hipStream_t s,
+                        Span t) {
+  if (pl.fused_ns) return launch_fused<T, D>(pl, q, k, v, w, s, t);
+  // m > 64: landmark blocks of 32 (two row blocks); the solver runs on its own.
+  return launch_kernel<T, D, 2, 0>(pl, q, k, v, w, s, t);
 }
 
 }  // namespace
 
-hipError_t launch_l1exp(const Plan& pl, const void* q, const void* k, const void* v, const Work& w,
+hipError_t launch_l1exp(const Plan& pl, const void* q, const void* k, const void* v, Work& w,
                         hipStream_t s, Span t) {
   if (pl.dtype == 1) {
     if (pl.d == 64) return launch_typed<uint16_t, 64>(pl, q, k, v, w, s, t);

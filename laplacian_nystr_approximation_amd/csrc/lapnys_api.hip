@@ -2,17 +2,16 @@
 // the per-call plan and workspace layout, the stage sequence, the
 // library-owned workspace of lapnys_forward, and the debug/profiled forms.
 //
-// Stage sequence (no host synchronisation):
-//   pool      K -> K~                                           side stream (forked)
-//   ns        K~ -> W, X = NS inverse of W                      side stream
-//   kernel    Q, K, V, K~ -> C^T, tile statistics, B V partials caller's stream
-//   finalize  partials -> mu, sigma, B V; for m > 64 also
-//             Y = X (B V) on a tile GEMM (after the join)       caller's stream
-//   output    Y = X (B V) for m <= 64, then O = whiten(C) Y     caller's stream
-// The Newton-Schulz stage depends only on the landmarks, so it runs on a
-// library-owned stream of the device (default priority) concurrently with the
-// kernel-matrix stage, which waits for the pool stage across streams, and
-// joins before the stages that need X.
+// Stage sequence (no host synchronisation), all on the caller's stream:
+//   pool      K -> K~
+//   kernel    Q, K, V, K~ -> C^T, tile statistics, B V partials; for m <= 64
+//             the same launch also runs the Newton-Schulz solver (K~ -> W, X)
+//   finalize  partials -> mu, sigma, B V
+//   output    Y = X (B V), then O = whiten(C) Y
+// For 64 < m <= 256 the solver is a sequence of launches on a library-owned
+// stream of the device (default priority), forked after the pool stage and
+// joined before Y = X (B V), which is then its own launch in the finalize
+// stage.
 #include <math.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -190,11 +189,6 @@ int device_ctx(DeviceCtx** out) {
 
 int run(const Plan& pl, const void* q, const void* k, const void* v, float* out, lapnys::Work& W, hipEvent_t* ev,
         hipStream_t s) {
-  std::lock_guard<std::mutex> lock(g_ctx_mu);
-  DeviceCtx* dc = nullptr;
-  const int st = device_ctx(&dc);
-  if (st != LAPNYS_OK) return st;
-  hipStream_t side = dc->side;
   // An error left by an earlier, unrelated runtime call would otherwise be
   // reported by the first launch check below.
   (void)hipGetLastError();
@@ -206,27 +200,43 @@ int run(const Plan& pl, const void* q, const void* k, const void* v, float* out,
     }
     return t;
   };
+  auto mark = [&](int idx) { return !ev || !ev[idx] || ok(hipEventRecord(ev[idx], s), "hipEventRecord"); };
   const lapnys::Span fin = span(LAPNYS_STAGE_FINALIZE);
+
+  if (pl.fused_ns) {
+    // m <= 64: one stream; the solver runs inside the kernel-matrix launch,
+    // and its stage events bracket that launch.
+    if (!ok(lapnys::launch_pool(pl, k, W, s, span(LAPNYS_STAGE_POOL)), "pool launch")) return LAPNYS_ERR_HIP;
+    if (!mark(2 * LAPNYS_STAGE_NS)) return LAPNYS_ERR_HIP;
+    if (!ok(lapnys::launch_l1exp(pl, q, k, v, W, s, span(LAPNYS_STAGE_KERNEL)), "kernel-matrix launch"))
+      return LAPNYS_ERR_HIP;
+    if (!mark(2 * LAPNYS_STAGE_NS + 1)) return LAPNYS_ERR_HIP;
+    if (!ok(lapnys::launch_reduce(pl, W, s, fin), "reduce launch")) return LAPNYS_ERR_HIP;
+    if (!ok(lapnys::launch_output(pl, W, out, s, span(LAPNYS_STAGE_OUTPUT)), "output launch")) return LAPNYS_ERR_HIP;
+    return LAPNYS_OK;
+  }
+
+  // m > 64: the solver's launches run on a library-owned stream beside the
+  // kernel-matrix stage.  The pool stage runs on that stream ahead of them and
+  // the caller's stream waits for it, so the solver is dispatched first.
+  std::lock_guard<std::mutex> lock(g_ctx_mu);
+  DeviceCtx* dc = nullptr;
+  const int st = device_ctx(&dc);
+  if (st != LAPNYS_OK) return st;
+  hipStream_t side = dc->side;
   // fork: everything before this call on the caller's stream precedes the side stream's work
   if (!ok(hipEventRecord(dc->fork, s), "hipEventRecord") || !ok(hipStreamWaitEvent(side, dc->fork, 0), "hipStreamWaitEvent"))
     return LAPNYS_ERR_HIP;
-  // The pool stage runs on the side stream right before the solver, and the
-  // caller's stream waits for it across streams: the solver's workgroups are
-  // then dispatched before the kernel-matrix stage's and always find room on
-  // the CUs (started after, they can wait for CUs until that stage drains).
   if (!ok(lapnys::launch_pool(pl, k, W, side, span(LAPNYS_STAGE_POOL)), "pool launch")) return LAPNYS_ERR_HIP;
   if (!ok(hipEventRecord(dc->pooled, side), "hipEventRecord")) return LAPNYS_ERR_HIP;
   if (!ok(lapnys::launch_ns(pl, W, side, span(LAPNYS_STAGE_NS)), "Newton-Schulz launch")) return LAPNYS_ERR_HIP;
   if (!ok(hipEventRecord(dc->join, side), "hipEventRecord")) return LAPNYS_ERR_HIP;
   if (!ok(hipStreamWaitEvent(s, dc->pooled, 0), "hipStreamWaitEvent")) return LAPNYS_ERR_HIP;
-  // kernel matrices, statistics and B V on the caller's stream, concurrently
   if (!ok(lapnys::launch_l1exp(pl, q, k, v, W, s, span(LAPNYS_STAGE_KERNEL)), "kernel-matrix launch"))
     return LAPNYS_ERR_HIP;
-  if (!ok(lapnys::launch_reduce(pl, W, s, {fin.start, pl.fused_ns ? fin.stop : nullptr}), "reduce launch"))
-    return LAPNYS_ERR_HIP;
-  // join: everything after needs X
+  if (!ok(lapnys::launch_reduce(pl, W, s, {fin.start, nullptr}), "reduce launch")) return LAPNYS_ERR_HIP;
   if (!ok(hipStreamWaitEvent(s, dc->join, 0), "hipStreamWaitEvent")) return LAPNYS_ERR_HIP;
-  if (!pl.fused_ns && !ok(lapnys::launch_y(pl, W, s, {nullptr, fin.stop}), "Y launch")) return LAPNYS_ERR_HIP;
+  if (!ok(lapnys::launch_y(pl, W, s, {nullptr, fin.stop}), "Y launch")) return LAPNYS_ERR_HIP;
   if (!ok(lapnys::launch_output(pl, W, out, s, span(LAPNYS_STAGE_OUTPUT)), "output launch")) return LAPNYS_ERR_HIP;
   return LAPNYS_OK;
 }

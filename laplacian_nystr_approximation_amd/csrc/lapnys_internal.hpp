@@ -41,6 +41,8 @@ constexpr int kLandmarkBlock = 64;
 constexpr int kFusedNsMaxM = 64;
 // Largest supported landmark count.
 constexpr int kMaxM = 256;
+// Devices per process with cached per-device launch data.
+constexpr int kMaxDevices = 64;
 
 // Per-call plan: sizes, tiling and the workspace layout (byte offsets, each
 // 256-byte aligned).  Computed on the host from the validated parameters.
@@ -85,8 +87,11 @@ struct Span {
 
 // Kernel launchers (each returns the hipError_t of its launches).
 hipError_t launch_pool(const Plan& pl, const void* k, const Work& w, hipStream_t s, Span t = {});
+// The solver for 64 < m <= 256 (separate launches).
 hipError_t launch_ns(const Plan& pl, Work& w, hipStream_t s, Span t = {});
-hipError_t launch_l1exp(const Plan& pl, const void* q, const void* k, const void* v, const Work& w,
+// The kernel-matrix stage; for m <= 64 the same launch also runs the
+// Newton-Schulz solver (and sets w.x_final).
+hipError_t launch_l1exp(const Plan& pl, const void* q, const void* k, const void* v, Work& w,
                         hipStream_t s, Span t = {});
 hipError_t launch_reduce(const Plan& pl, const Work& w, hipStream_t s, Span t = {});
 hipError_t launch_y(const Plan& pl, const Work& w, hipStream_t s, Span t = {});  // m > kFusedNsMaxM only

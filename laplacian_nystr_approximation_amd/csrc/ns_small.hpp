@@ -1,0 +1,260 @@
+// Newton-Schulz inverse of the landmark Gram matrix for m <= 64, one
+// workgroup per problem with every operand in LDS (EN page, section 2.C.2;
+// DE section 2; ZH section 2.2; KO section 2.3; JA section 2.3):
+//
+//   W  = k(K~, K~) + eps I,   k(x, y) = exp(-||x - y||_1 / lambda)
+//   X0 = W^T / (||W||_1 ||W||_inf)
+//   X <- X (2I - W X), a fixed number of times, matrix products only.
+//
+// W is built so that it is bit-symmetric: entry (a, b) and entry (b, a) sum
+// the same |differences| in the same feature order, and the diagonal is
+// exp(0) + eps = 1 + eps exactly as float32 arithmetic gives it.  These
+// workgroups run inside the kernel-matrix stage's launch (l1exp.hip).
+#pragma once
+
+#include "lapnys_internal.hpp"
+
+namespace lapnys {
+namespace ns_detail {
+
+constexpr int kMP = 64;  // padded size of the in-LDS schedule
+constexpr int kLD = 68;  // LDS row stride (floats): conflict-free column reads
+// LDS of one problem's schedule (floats): X twice, (W X)^T, 128 partial sums, alpha.
+constexpr int kNsLdsFloats = 3 * kMP * kLD + 132;
+
+// In-LDS schedule for m <= 64: one workgroup of four wavefronts per problem,
+// 52 KB of LDS (so it can share a CU with the kernel-matrix stage).
+//
+// Each step is evaluated as X_next = 2X - X (W X), which equals X (2I - W X).
+// Symmetry: W is bit-symmetric and X0 = W^T / alpha = W / alpha; for a
+// symmetric X the product X W X is symmetric whatever rounding X carries, so
+// Q = W X is formed in full (wavefront w: the four 16 x 16 blocks of block row
+// w) and stored transposed, while S = X Q is formed only on its 10 upper
+// 16 x 16 blocks (spread over the wavefronts as 3, 3, 2, 2) and stored with
+// its mirror image.  X thus stays exactly symmetric in one row-major copy,
+// and a column of X is read as a row.  (Mirroring a product that is not
+// symmetric in exact arithmetic, such as W X, would not be a faithful step:
+// the iteration then drifts away once it has converged.)
+//
+// The reduction runs over k in [0, 4 KS), KS = ceil(m / 4), on fp32 MFMA
+// 16x16x4.  Padding rows and columns of W and X are exact zeros and stay so.
+__device__ __constant__ int8_t kBlkI[4][3] = {{0, 0, 0}, {0, 1, 1}, {1, 2, -1}, {2, 3, -1}};
+__device__ __constant__ int8_t kBlkJ[4][3] = {{0, 1, 2}, {3, 1, 2}, {3, 2, -1}, {3, 3, -1}};
+
+// Problem p's W and X, for one workgroup of 256 lanes.  lds: kNsLdsFloats
+// floats, 16-byte aligned.
+template <int D, int KS>
+__device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __restrict__ wout,
+                                         float* __restrict__ xout, int m, float scale, float eps, int iters, int p,
+                                         float* __restrict__ lds) {
+  constexpr int KLD = D + 4;  // landmark staging stride: 16-byte rows for broadcast reads
+  static_assert(kMP * KLD <= kMP * kLD, "landmark staging must fit in an X buffer");
+  float4(*xs4)[kMP * kLD / 4] = reinterpret_cast<float4(*)[kMP * kLD / 4]>(lds);  // X (ping-pong), symmetric
+  float* ql = lds + 2 * kMP * kLD;  // (W X)^T; W during set-up
+  float* wl = ql;
+  float* red = ql + kMP * kLD;      // [128] partial sums, then alpha
+  float& alpha_s = red[128];
+  float* kl = reinterpret_cast<float*>(xs4[1]);  // landmark staging
+
+  // Beside the kernel-matrix workgroups on the same CUs, the solver's chain
+  // of dependent products is the longer one: its wavefronts take issue
+  // priority.
+  __builtin_amdgcn_s_setprio(3);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const float* ktp = kt + (size_t)p * m * D;
+  for (int e = tid; e < m * D; e += 256) kl[(e / D) * KLD + (e % D)] = ktp[e];
+  __syncthreads();
+
+  // W = k(K~, K~) + eps I, zero padded.  Lane b holds landmark b in
+  // registers; wavefront w forms rows [16 w, 16 w + 16) four at a time with
+  // the row landmark broadcast from LDS.  Entry (a, b) sums |K~_a - K~_b| over
+  // even and odd features in increasing order, the same sums as entry (b, a),
+  // so W is bit-symmetric.
+  {
+    const int b = lane;
+    float xb[D];
+#pragma unroll
+    for (int t = 0; t < D; ++t) xb[t] = kl[min(b, m - 1) * KLD + t];
+    for (int a0 = 16 * w; a0 < 16 * w + 16; a0 += 4) {
+      if (a0 < m) {
+        float s0[4] = {0.f, 0.f, 0.f, 0.f}, s1[4] = {0.f, 0.f, 0.f, 0.f};
+        const float* ka[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ka[u] = kl + min(a0 + u, m - 1) * KLD;
+#pragma unroll
+        for (int t = 0; t < D; t += 4) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float4 r = *reinterpret_cast<const float4*>(ka[u] + t);
+            s0[u] += fabsf(r.x - xb[t]);
+            s1[u] += fabsf(r.y - xb[t + 1]);
+            s0[u] += fabsf(r.z - xb[t + 2]);
+            s1[u] += fabsf(r.w - xb[t + 3]);
+          }
+          // The sums are in/out operands here: each 4-feature chunk's row
+          // values are read just before use (bounded registers).
+          asm volatile("" : "+v"(s0[0]), "+v"(s0[1]), "+v"(s0[2]), "+v"(s0[3]), "+v"(s1[0]), "+v"(s1[1]),
+                       "+v"(s1[2]), "+v"(s1[3])::"memory");
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int a = a0 + u;
+          float val = 0.f;
+          if (a < m && b < m) {
+            val = exp2f((s0[u] + s1[u]) * scale);
+            if (a == b) val += eps;
+          }
+          wl[a * kLD + b] = val;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) wl[(a0 + u) * kLD + b] = 0.f;
+      }
+    }
+  }
+  __syncthreads();
+
+  // alpha = ||W||_1 * ||W||_inf (largest absolute column sum times largest row
+  // sum); W goes out to the workspace, the second X buffer is cleared.
+  float* wp = wout + (size_t)p * kMP * kMP;
+  for (int e = tid; e < kMP * kMP; e += 256) {
+    wp[e] = wl[(e >> 6) * kLD + (e & 63)];
+    kl[(e >> 6) * kLD + (e & 63)] = 0.f;
+  }
+  if (tid < 2 * kMP) {
+    const int i = tid & 63;
+    const bool rows = tid < kMP;
+    float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b0 = 0; b0 < kMP; b0 += 8)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc8[u] += fabsf(rows ? wl[i * kLD + b0 + u] : wl[(b0 + u) * kLD + i]);
+    red[tid] = ((acc8[0] + acc8[1]) + (acc8[2] + acc8[3])) + ((acc8[4] + acc8[5]) + (acc8[6] + acc8[7]));
+  }
+  __syncthreads();
+  if (tid < 64) {
+    float rm = red[tid], cm = red[kMP + tid];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      rm = fmaxf(rm, __shfl_xor(rm, off, 64));
+      cm = fmaxf(cm, __shfl_xor(cm, off, 64));
+    }
+    if (tid == 0) alpha_s = cm * rm;
+  }
+  __syncthreads();
+
+  // W's A operands for every step of Q = W X, block row w:
+  // A[li][lk] of step s = W[16 w + li][4 s + lk].  Then this wavefront's
+  // upper blocks of S = X Q.
+  // KS = ceil(m / 4) steps per product (a template parameter, so the step
+  // loops unroll without branches).  Wavefronts with two upper blocks run a
+  // third, unstored copy of their last block: every wavefront issues the
+  // same MFMA sequence and none branches inside it.
+  const int li = lane & 15, lk = lane >> 4;
+  float wreg[KS];
+#pragma unroll
+  for (int st = 0; st < KS; ++st) wreg[st] = wl[(16 * w + li) * kLD + 4 * st + lk];
+  int bI[3], bJ[3];
+#pragma unroll
+  for (int b = 0; b < 3; ++b) {
+    bI[b] = kBlkI[w][b];
+    bJ[b] = kBlkJ[w][b];
+  }
+  const int nb = bI[2] < 0 ? 2 : 3;
+  if (nb == 2) {
+    bI[2] = bI[1];
+    bJ[2] = bJ[1];
+  }
+  // X0 = W^T / alpha = W / alpha (W is symmetric).
+  {
+    const float alpha = alpha_s;
+    float* x0 = reinterpret_cast<float*>(xs4[0]);
+    for (int e = tid; e < kMP * kMP; e += 256) {
+      const int a = e >> 6, b = e & 63;
+      x0[a * kLD + b] = wl[b * kLD + a] / alpha;
+    }
+  }
+  __syncthreads();
+
+  int cur = 0;
+  for (int it = 0; it < iters; ++it) {
+    const float* xc = reinterpret_cast<const float*>(xs4[cur]);
+    // Q = W X, block row w, stored transposed: ql[j][i] = Q[i][j].
+    {
+      f32x4 acc[4];
+#pragma unroll
+      for (int bj = 0; bj < 4; ++bj) acc[bj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < KS; ++st) {
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) {
+          const float xb = xc[(16 * bj + li) * kLD + 4 * st + lk];  // X[4 st + lk][16 bj + li]
+          acc[bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(wreg[st], xb, acc[bj], 0, 0, 0);
+        }
+      }
+      // acc[bj][r] = Q[16 w + 4 lk + r][16 bj + li]: four consecutive entries of
+      // row 16 bj + li of Q^T.
+#pragma unroll
+      for (int bj = 0; bj < 4; ++bj)
+        *reinterpret_cast<float4*>(&ql[(16 * bj + li) * kLD + 16 * w + 4 * lk]) =
+            make_float4(acc[bj][0], acc[bj][1], acc[bj][2], acc[bj][3]);
+    }
+    __syncthreads();
+    // S = X Q on the upper blocks; X_next = 2 X - S stored with its mirror.
+    {
+      float xij[3][4];  // X entries of this lane's outputs, read ahead of the products
+#pragma unroll
+      for (int b = 0; b < 3; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) xij[b][r] = xc[(16 * bI[b] + 4 * lk + r) * kLD + 16 * bJ[b] + li];
+      f32x4 acc[3];
+#pragma unroll
+      for (int b = 0; b < 3; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < KS; ++st) {
+#pragma unroll
+        for (int b = 0; b < 3; ++b) {
+          const float xa = xc[(16 * bI[b] + li) * kLD + 4 * st + lk];  // X[16 bi + li][4 st + lk]
+          const float qb = ql[(16 * bJ[b] + li) * kLD + 4 * st + lk];  // Q[4 st + lk][16 bj + li]
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa, qb, acc[b], 0, 0, 0);
+        }
+      }
+      float* xn = reinterpret_cast<float*>(xs4[cur ^ 1]);
+#pragma unroll
+      for (int b = 0; b < 3; ++b) {
+        if (b < nb) {
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = 2.f * xij[b][r] - acc[b][r];
+          const int i0 = 16 * bI[b] + 4 * lk, j = 16 * bJ[b] + li;
+          if (bI[b] != bJ[b]) {
+            // off the diagonal every entry is upper: the mirror image is four
+            // consecutive entries of row j
+#pragma unroll
+            for (int r = 0; r < 4; ++r) xn[(i0 + r) * kLD + j] = v[r];
+            *reinterpret_cast<float4*>(&xn[j * kLD + i0]) = make_float4(v[0], v[1], v[2], v[3]);
+          } else {
+            // diagonal block: only the upper-triangle entries, with their mirrors
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              if (i0 + r <= j) {
+                xn[(i0 + r) * kLD + j] = v[r];
+                xn[j * kLD + i0 + r] = v[r];
+              }
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+    cur ^= 1;
+  }
+
+  float* xp = xout + (size_t)p * kMP * kMP;
+  const float* xf = reinterpret_cast<const float*>(xs4[cur]);
+  for (int e = tid; e < kMP * kMP; e += 256) xp[e] = xf[(e >> 6) * kLD + (e & 63)];
+}
+
+
+}  // namespace ns_detail
+}  // namespace lapnys

@@ -223,33 +223,49 @@ __device__ __forceinline__ void l1exp_body(const T* __restrict__ q, const T* __r
     v0.issue(vcol, t0, lk, 0, tok_last);
 
     // ---- column statistics of C over the tile, and the C^T store ----
-    for (int j = w; j < lb; j += kNW) {
-      float vals[kTT / 64];
-      float s = 0.f;
+    // Wavefront w takes landmarks w, w + 4, ..., four of them at a time so
+    // that their wavefront reductions overlap.
+    for (int jq = w; jq < lb; jq += 4 * kNW) {
+      float vals[4][kTT / 64];
+      float s[4], m2[4];
 #pragma unroll
-      for (int c = 0; c < kTT / 64; ++c) {
-        const int col = lane + 64 * c;
-        vals[c] = tl[j * kTP + col];
-        if (col < nvalid) s += vals[c];
-      }
-      s = wave_sum_dpp(s);
-      const float mean = s / (float)nvalid;
-      float m2 = 0.f;
+      for (int u = 0; u < 4; ++u) {
+        const int jj = min(jq + kNW * u, lb - 1);  // rows past lb: read, not stored
+        s[u] = 0.f;
 #pragma unroll
-      for (int c = 0; c < kTT / 64; ++c) {
-        const int col = lane + 64 * c;
-        if (col < nvalid) {
-          const float dv = vals[c] - mean;
-          m2 += dv * dv;
+        for (int c = 0; c < kTT / 64; ++c) {
+          const int col = lane + 64 * c;
+          vals[u][c] = tl[jj * kTP + col];
+          if (col < nvalid) s[u] += vals[u][c];
         }
       }
-      m2 = wave_sum_dpp(m2);
-      if (lane == 0) stats[((size_t)p * ntiles + tile) * m + j0 + j] = make_float2(s, m2);
-      float* crow = ct + ((size_t)p * m + j0 + j) * ldc + t0;
+      wave_sum_dpp_n<4>(s);
 #pragma unroll
-      for (int c = 0; c < kTT / 64; ++c) {
-        const int col = lane + 64 * c;
-        if (col < nvalid) crow[col] = vals[c];
+      for (int u = 0; u < 4; ++u) {
+        const float mean = s[u] / (float)nvalid;
+        m2[u] = 0.f;
+#pragma unroll
+        for (int c = 0; c < kTT / 64; ++c) {
+          const int col = lane + 64 * c;
+          if (col < nvalid) {
+            const float dv = vals[u][c] - mean;
+            m2[u] += dv * dv;
+          }
+        }
+      }
+      wave_sum_dpp_n<4>(m2);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = jq + kNW * u;
+        if (j < lb) {
+          if (lane == 0) stats[((size_t)p * ntiles + tile) * m + j0 + j] = make_float2(s[u], m2[u]);
+          float* crow = ct + ((size_t)p * m + j0 + j) * ldc + t0;
+#pragma unroll
+          for (int c = 0; c < kTT / 64; ++c) {
+            const int col = lane + 64 * c;
+            if (col < nvalid) crow[col] = vals[u][c];
+          }
+        }
       }
     }
 

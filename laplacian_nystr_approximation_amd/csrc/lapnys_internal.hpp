@@ -35,6 +35,29 @@ __device__ __forceinline__ float wave_sum_dpp(float x) {
   return ((r0 + r1) + r2) + r3;
 }
 
+// wave_sum_dpp on U independent values at once, the steps interleaved so the
+// DPP and lane-read latencies of one overlap the others'.  Each result is
+// bit-identical to wave_sum_dpp of that value.
+template <int U>
+__device__ __forceinline__ void wave_sum_dpp_n(float (&x)[U]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) x[u] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x[u]), 0x128, 0xf, 0xf, false));
+#pragma unroll
+  for (int u = 0; u < U; ++u) x[u] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x[u]), 0x124, 0xf, 0xf, false));
+#pragma unroll
+  for (int u = 0; u < U; ++u) x[u] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x[u]), 0x122, 0xf, 0xf, false));
+#pragma unroll
+  for (int u = 0; u < U; ++u) x[u] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x[u]), 0x121, 0xf, 0xf, false));
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[u]), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[u]), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[u]), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[u]), 48));
+    x[u] = ((r0 + r1) + r2) + r3;
+  }
+}
+
 // Landmark block handled by one workgroup of the fused kernel-matrix stage.
 constexpr int kLandmarkBlock = 64;
 // Largest landmark count the fused single-workgroup Newton-Schulz handles.

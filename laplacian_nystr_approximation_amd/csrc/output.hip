@@ -2,32 +2,40 @@
 // whitening of EN page section 2.B) and Y = X (B V), i.e. O = Z W^-1 (B V).
 //
 // One workgroup per 256-token tile, four wavefronts of 64 tokens each.  The
-// stage streams C once and writes O once; its arithmetic (2 N m d flops per
-// problem) is small, so the design goal is to keep every C load in flight
-// early and every store full-width.
+// stage streams C once and writes O once.
 //
 //  * Each lane loads C^T[landmark][4 consecutive tokens] as one 16-byte load;
 //    16 lanes cover a 256-byte run of one landmark row.  All of a wavefront's
 //    C loads (up to 64 landmarks) are issued before anything else, so their
 //    latency overlaps the Y prologue.  For m > 64 the loads of the next 64
-//    landmarks are issued group by group as the current ones are consumed.
+//    landmarks are issued slot by slot as the current ones are consumed.
 //  * Prologue (m <= 64): the workgroup forms Y = X (B V) itself on fp32 MFMA
-//    (a 64 x 64 x 64 product, zero padded) into LDS; for larger m, Y comes
-//    from a batched tile GEMM and is copied into LDS.
-//  * Main loop: a wavefront's 64 x D output is (4 x D/16) blocks of fp32
-//    MFMA 16x16x4 reducing over four landmarks per step.  Lane (li, lk)
-//    feeds A[li][lk] = Z[token tb + 4 li + a][landmark] for token block a,
-//    and B[lk][li] = Y[landmark][D/16 li + b] for feature block b, so that a
-//    lane ends up holding D/16 consecutive features of each of its tokens and
-//    writes them with one 16-byte (D = 64) or 8-byte (D = 32) store.
+//    (a 64 x 64 x 64 product, zero padded); for larger m, Y comes from a
+//    batched tile GEMM.  Either way Y is stored in LDS transposed, as bf16
+//    high and low parts (y = hi + lo to about 16 bits).
+//  * Main loop: Z Y on bf16 MFMA 16x16x32 with three products per step,
+//    Zhi Yhi + Zhi Ylo + Zlo Yhi: the dropped Zlo Ylo term and the rounding
+//    of the low parts are about 2^-16 of each product, so the stage keeps
+//    near-fp32 accuracy at a fifth of the fp32 MFMA cycles.  Lane (li, lk)
+//    holds 8 landmarks (32 h + 8 lk + e, e < 8) of its 4 tokens tb + 4 li + a
+//    and feeds them as the A operand of token block a; the B operand of
+//    feature block b is Y[same 8 landmarks][D/16 li + b], one 16-byte LDS read.
+//    A lane thus ends up holding D/16 consecutive features of each of its
+//    tokens and writes them with one 16-byte (D = 64) or 8-byte (D = 32) store.
 #include "lapnys_internal.hpp"
 
 namespace lapnys {
 
 namespace {
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kXLD = 65;   // LDS row stride of X in the prologue
-constexpr int kGroups = 16;  // landmark groups of four held in registers (64 landmarks)
+constexpr int kSlots = 16; // C loads of four tokens each held per lane (64 landmarks)
 
 // All-ones when ok, else zero, opaque to the optimiser: masking a loaded
 // value with it (instead of a select) keeps the load unconditional, so it
@@ -39,6 +47,25 @@ __device__ __forceinline__ uint32_t lane_mask(bool ok) {
 }
 
 __device__ __forceinline__ float masked(float v, uint32_t mk) { return __uint_as_float(__float_as_uint(v) & mk); }
+
+// Splits two floats into bf16 high parts (round to nearest even) and bf16
+// low parts (the rounded remainders), each pair packed in one dword.
+__device__ __forceinline__ void split2(float z0, float z1, uint32_t& hi, uint32_t& lo) {
+  const bf16x2 h = __builtin_convertvector((f32x2){z0, z1}, bf16x2);
+  const f32x2 hf = __builtin_convertvector(h, f32x2);
+  const bf16x2 l = __builtin_convertvector((f32x2){z0 - hf.x, z1 - hf.y}, bf16x2);
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
+// Y^T in LDS: element (feature f, landmark l) of a [D][rl] bf16 array (rl a
+// multiple of 64).  The 8-landmark chunks of a row are XOR-swizzled by the
+// reading lane's index t = f / (D/16), so the 16 lanes that read one chunk
+// column for 16 different features spread over distinct banks.
+__device__ __forceinline__ int yt_index(int f, int l, int t, int rl) {
+  const int c = l >> 3;
+  return f * rl + 8 * ((c & ~7) | ((c ^ t) & 7)) + (l & 7);
+}
 
 template <int D>
 struct OutVec;
@@ -58,11 +85,11 @@ __global__ __launch_bounds__(256) void output_kernel(const float* __restrict__ c
                                                      const float* __restrict__ mu, const float* __restrict__ rs,
                                                      float* __restrict__ out, int N, int m) {
   constexpr int DB = D / 16;
-  extern __shared__ float lds[];
-  const int m4 = (m + 3) & ~3;
-  const int ym = FUSED_Y ? 64 : m4;  // rows of Y in LDS; rows >= m are zero
-  float* yl = lds;                   // [ym][D]
-  float2* mrs = reinterpret_cast<float2*>(yl + ym * D);  // [m4]: (mu, 1/sigma), zero past m
+  extern __shared__ __align__(16) float lds[];
+  const int rl = FUSED_Y ? 64 : (m + 63) & ~63;  // landmarks per Y^T row; rows past m are zero
+  __bf16* yth = reinterpret_cast<__bf16*>(lds);  // [D][rl] high parts
+  __bf16* ytl = yth + D * rl;                    // [D][rl] low parts
+  float2* mrs = reinterpret_cast<float2*>(ytl + D * rl);  // [rl]: (mu, 1/sigma), zero past m
   const int tile = blockIdx.x, p = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int li = lane & 15, lk = lane >> 4;
@@ -70,13 +97,15 @@ __global__ __launch_bounds__(256) void output_kernel(const float* __restrict__ c
   const int tok4 = tb + 4 * li;        // first of this lane's four tokens
   const bool tok_ok = tok4 < N;
 
-  // C loads: landmark rows past m and tokens past N are read from a clamped,
-  // in-bounds address and masked to zero where they are used, so the loads
-  // are unconditional and all issue before the first wait.
-  float4 cr[kGroups];
+  // C loads: slot s holds landmark c0 + 32 (s / 8) + 8 lk + s % 8.  Landmark
+  // rows past m and tokens past N are read from a clamped, in-bounds address
+  // and masked to zero where they are used, so the loads are unconditional
+  // and all issue before the first wait.
+  float4 cr[kSlots];
   const float* cpc = ct + (size_t)p * m * ldc + min(tok4, ldc - 4);
-  auto load_group = [&](int c0, int g) {
-    cr[g] = *reinterpret_cast<const float4*>(cpc + (size_t)min(c0 + 4 * g + lk, m - 1) * ldc);
+  auto load_slot = [&](int c0, int s) {
+    const int j = c0 + 32 * (s >> 3) + 8 * lk + (s & 7);
+    cr[s] = *reinterpret_cast<const float4*>(cpc + (size_t)min(j, m - 1) * ldc);
   };
 
   if constexpr (FUSED_Y) {
@@ -94,7 +123,7 @@ __global__ __launch_bounds__(256) void output_kernel(const float* __restrict__ c
     const int jt = tid & 63;
     const float mu_t = mu[p * m + min(jt, m - 1)], rs_t = rs[p * m + min(jt, m - 1)];
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g) load_group(0, g);
+    for (int s = 0; s < kSlots; ++s) load_slot(0, s);
     __builtin_amdgcn_sched_barrier(0);
 
     // Y = X (B V), 64 x D, on fp32 MFMA 32x32x2; X and B V zero padded to 64 rows.
@@ -126,16 +155,37 @@ __global__ __launch_bounds__(256) void output_kernel(const float* __restrict__ c
         const float b = bvl[(k0 + yk) * D + 32 * bj + yi];
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
       }
+      // acc[r] = Y[32 bi + 8 (r / 4) + 4 yk + r % 4][32 bj + yi]: four
+      // consecutive landmarks of one feature, stored as one 8-byte run each.
+      const int f = 32 * bj + yi;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) yl[(32 * bi + 8 * (r >> 2) + 4 * yk + (r & 3)) * D + 32 * bj + yi] = acc[r];
+      for (int q = 0; q < 4; ++q) {
+        bf16x4 hi, lo;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = acc[4 * q + r];
+          hi[r] = (__bf16)v;
+          lo[r] = (__bf16)(v - (float)hi[r]);
+        }
+        const int at = yt_index(f, 32 * bi + 8 * q + 4 * yk, f / DB, rl);
+        *reinterpret_cast<bf16x4*>(yth + at) = hi;
+        *reinterpret_cast<bf16x4*>(ytl + at) = lo;
+      }
     }
   } else {
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g) load_group(0, g);
-    for (int e = tid; e < m4; e += 256)
+    for (int s = 0; s < kSlots; ++s) load_slot(0, s);
+    for (int e = tid; e < rl; e += 256)
       mrs[e] = (e < m) ? make_float2(mu[p * m + e], rs[p * m + e]) : make_float2(0.f, 0.f);
     const float* yp = y + (size_t)p * m * D;
-    for (int e = tid; e < m4 * D; e += 256) yl[e] = (e < m * D) ? yp[e] : 0.f;
+    for (int e = tid; e < rl * D; e += 256) {
+      const int l = e / D, f = e % D;
+      const float v = l < m ? yp[e] : 0.f;
+      const __bf16 hi = (__bf16)v;
+      const int at = yt_index(f, l, f / DB, rl);
+      yth[at] = hi;
+      ytl[at] = (__bf16)(v - (float)hi);
+    }
   }
   __syncthreads();
 
@@ -145,31 +195,56 @@ __global__ __launch_bounds__(256) void output_kernel(const float* __restrict__ c
 #pragma unroll
     for (int b = 0; b < DB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int c0 = 0; c0 < m4; c0 += 4 * kGroups) {
+  // One pass over 64 landmarks when Y is formed here (m <= 64).
+  const int mc = FUSED_Y ? 64 : m;
+  for (int c0 = 0; c0 < mc; c0 += 64) {
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g) {
-      if (c0 + 4 * g < m4) {
-        const int j = c0 + 4 * g + lk;
-        const float2 s = mrs[j];
-        float yb[DB];
-        if constexpr (DB == 4) {
-          const float4 t = *reinterpret_cast<const float4*>(yl + j * D + 4 * li);
-          yb[0] = t.x; yb[1] = t.y; yb[2] = t.z; yb[3] = t.w;
-        } else {
-          const float2 t = *reinterpret_cast<const float2*>(yl + j * D + 2 * li);
-          yb[0] = t.x; yb[1] = t.y;
+    for (int h = 0; h < 2; ++h) {
+      if (c0 + 32 * h < m) {  // else the half is past m (uniform)
+        // A operands: z of landmarks c0 + 32 h + 8 lk + e for token block a,
+        // split into bf16 high and low parts, two landmarks per dword.
+        u32x4 ah[4], al[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          float z[2][4];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int s = 8 * h + e + u;
+            const int j = c0 + 32 * h + 8 * lk + e + u;
+            const float2 st = mrs[j];
+            // Landmarks past m have mu = 1/sigma = 0 and a zero C value: z = 0.
+            const uint32_t mk = lane_mask(tok_ok && j < m);
+            z[u][0] = (masked(cr[s].x, mk) - st.x) * st.y;
+            z[u][1] = (masked(cr[s].y, mk) - st.x) * st.y;
+            z[u][2] = (masked(cr[s].z, mk) - st.x) * st.y;
+            z[u][3] = (masked(cr[s].w, mk) - st.x) * st.y;
+            if constexpr (!FUSED_Y) {
+              if (c0 + 64 < m) load_slot(c0 + 64, s);
+            }
+          }
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            uint32_t hw, lw;
+            split2(z[0][a], z[1][a], hw, lw);
+            ah[a][e / 2] = hw;
+            al[a][e / 2] = lw;
+          }
         }
-        const uint32_t mk = lane_mask(tok_ok && j < m);
-        const float c4[4] = {masked(cr[g].x, mk), masked(cr[g].y, mk), masked(cr[g].z, mk), masked(cr[g].w, mk)};
+        const int chunk = 4 * h + lk + (c0 >> 3);
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          // Landmarks past m have mu = 1/sigma = 0 and a zero C value: z = 0.
-          const float za = (c4[a] - s.x) * s.y;
+        for (int b = 0; b < DB; ++b) {
+          const int at = (DB * li + b) * rl + 8 * ((chunk & ~7) | ((chunk ^ li) & 7));
+          const bf16x8 bh = *reinterpret_cast<const bf16x8*>(yth + at);
+          const bf16x8 bl = *reinterpret_cast<const bf16x8*>(ytl + at);
 #pragma unroll
-          for (int b = 0; b < DB; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(za, yb[b], acc[a][b], 0, 0, 0);
-        }
-        if constexpr (!FUSED_Y) {
-          if (c0 + 4 * kGroups + 4 * g < m4) load_group(c0 + 4 * kGroups, g);
+          for (int a = 0; a < 4; ++a)
+            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, al[a]), bh, acc[a][b], 0, 0, 0);
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ah[a]), bl, acc[a][b], 0, 0, 0);
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ah[a]), bh, acc[a][b], 0, 0, 0);
         }
       }
     }
@@ -197,11 +272,10 @@ __global__ __launch_bounds__(256) void output_kernel(const float* __restrict__ c
 
 template <int D, bool FUSED_Y>
 hipError_t launch_typed(const Plan& pl, const Work& wk, float* out, hipStream_t s, Span t) {
-  const int m4 = (pl.m + 3) & ~3;
-  // yl, then the (mu, 1/sigma) pairs (64 of them in the fused form, so that
-  // the prologue's X and B V buffers start at a fixed offset).
-  const size_t floats = FUSED_Y ? (size_t)64 * D + 2 * 64 + 64 * kXLD + 64 * D : (size_t)m4 * D + 2 * m4;
-  const size_t shmem = floats * sizeof(float);
+  // Y^T high and low parts (bf16, rl landmarks per row), the (mu, 1/sigma)
+  // pairs, and in the fused form the prologue's X and B V buffers.
+  const size_t rl = FUSED_Y ? 64 : (size_t)(pl.m + 63) & ~(size_t)63;
+  const size_t shmem = 2 * D * rl * 2 + rl * 8 + (FUSED_Y ? (size_t)(64 * kXLD + 64 * D) * sizeof(float) : 0);
   auto kern = output_kernel<D, FUSED_Y>;
   if (shmem > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);

@@ -19,8 +19,8 @@ namespace ns_detail {
 
 constexpr int kMP = 64;  // padded size of the in-LDS schedule
 constexpr int kLD = 68;  // LDS row stride (floats): conflict-free column reads
-// LDS of one problem's schedule (floats): X twice, (W X)^T, 128 partial sums, alpha.
-constexpr int kNsLdsFloats = 3 * kMP * kLD + 132;
+// LDS of one problem's schedule (floats): X twice, (W X)^T, 256 partial sums, alpha.
+constexpr int kNsLdsFloats = 3 * kMP * kLD + 260;
 
 // In-LDS schedule for m <= 64: one workgroup of four wavefronts per problem,
 // 52 KB of LDS (so it can share a CU with the kernel-matrix stage).
@@ -52,8 +52,8 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
   float4(*xs4)[kMP * kLD / 4] = reinterpret_cast<float4(*)[kMP * kLD / 4]>(lds);  // X (ping-pong), symmetric
   float* ql = lds + 2 * kMP * kLD;  // (W X)^T; W during set-up
   float* wl = ql;
-  float* red = ql + kMP * kLD;      // [128] partial sums, then alpha
-  float& alpha_s = red[128];
+  float* red = ql + kMP * kLD;      // [256] partial column sums, then alpha
+  float& alpha_s = red[256];
   float* kl = reinterpret_cast<float*>(xs4[1]);  // landmark staging
 
   // Beside the kernel-matrix workgroups on the same CUs, the solver's chain
@@ -61,8 +61,23 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
   // priority.
   __builtin_amdgcn_s_setprio(3);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const float* ktp = kt + (size_t)p * m * D;
-  for (int e = tid; e < m * D; e += 256) kl[(e / D) * KLD + (e % D)] = ktp[e];
+  // Landmark rows into LDS: every load of the (at most 64 x D) block is
+  // issued before the first store, so the staging costs one memory latency.
+  {
+    constexpr int kV = kMP * D / 4 / 256;  // float4 per lane
+    const float4* ktp4 = reinterpret_cast<const float4*>(kt + (size_t)p * m * D);
+    float4 kv[kV];
+#pragma unroll
+    for (int i = 0; i < kV; ++i) {
+      const int e4 = tid + 256 * i;
+      kv[i] = (4 * e4 < m * D) ? ktp4[e4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < kV; ++i) {
+      const int e = 4 * (tid + 256 * i);
+      *reinterpret_cast<float4*>(&kl[(e / D) * KLD + (e % D)]) = kv[i];
+    }
+  }
   __syncthreads();
 
   // W = k(K~, K~) + eps I, zero padded.  Lane b holds landmark b in
@@ -72,6 +87,7 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
   // so W is bit-symmetric.
   {
     const int b = lane;
+    float csum = 0.f;  // |W[a][b]| over this wavefront's rows a, in increasing a
     float xb[D];
 #pragma unroll
     for (int t = 0; t < D; ++t) xb[t] = kl[min(b, m - 1) * KLD + t];
@@ -105,41 +121,32 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
             if (a == b) val += eps;
           }
           wl[a * kLD + b] = val;
+          csum += val;  // entries are positive
         }
       } else {
 #pragma unroll
         for (int u = 0; u < 4; ++u) wl[(a0 + u) * kLD + b] = 0.f;
       }
     }
+    red[w * kMP + b] = csum;
   }
   __syncthreads();
 
-  // alpha = ||W||_1 * ||W||_inf (largest absolute column sum times largest row
-  // sum); W goes out to the workspace, the second X buffer is cleared.
+  // alpha = ||W||_1 ||W||_inf.  W is symmetric, so its largest absolute
+  // column sum (the 1-norm) is also its largest row sum (the inf-norm):
+  // alpha = (max_b sum_a |W[a][b]|)^2, the column sums merged from the four
+  // wavefronts' partial sums in wavefront order.  W goes out to the
+  // workspace, the second X buffer is cleared.
   float* wp = wout + (size_t)p * kMP * kMP;
   for (int e = tid; e < kMP * kMP; e += 256) {
     wp[e] = wl[(e >> 6) * kLD + (e & 63)];
     kl[(e >> 6) * kLD + (e & 63)] = 0.f;
   }
-  if (tid < 2 * kMP) {
-    const int i = tid & 63;
-    const bool rows = tid < kMP;
-    float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int b0 = 0; b0 < kMP; b0 += 8)
-#pragma unroll
-      for (int u = 0; u < 8; ++u) acc8[u] += fabsf(rows ? wl[i * kLD + b0 + u] : wl[(b0 + u) * kLD + i]);
-    red[tid] = ((acc8[0] + acc8[1]) + (acc8[2] + acc8[3])) + ((acc8[4] + acc8[5]) + (acc8[6] + acc8[7]));
-  }
-  __syncthreads();
   if (tid < 64) {
-    float rm = red[tid], cm = red[kMP + tid];
+    float cm = ((red[tid] + red[kMP + tid]) + red[2 * kMP + tid]) + red[3 * kMP + tid];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      rm = fmaxf(rm, __shfl_xor(rm, off, 64));
-      cm = fmaxf(cm, __shfl_xor(cm, off, 64));
-    }
-    if (tid == 0) alpha_s = cm * rm;
+    for (int off = 32; off >= 1; off >>= 1) cm = fmaxf(cm, __shfl_xor(cm, off, 64));
+    if (tid == 0) alpha_s = cm * cm;
   }
   __syncthreads();
 

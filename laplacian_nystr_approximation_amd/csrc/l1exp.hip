@@ -7,8 +7,9 @@
 //     problem), for the output stage;
 //   * per token tile and landmark: the sum of C and the sum of squared
 //     deviations from the tile mean (whitening statistics, EN section 2.B);
-//   * B V partial products over each tile group, on fp32 MFMA.  B itself
-//     never leaves the chip.
+//   * B V partial products over each tile group, on bf16 MFMA with B split
+//     into bf16 high and low parts (and V too for float32 inputs; bf16 V is
+//     exact).  B itself never leaves the chip.
 // The partials are reduced by the finalize stage (finalize.hip).
 //
 // Layout of the work: one lane per token.  A workgroup of 256 lanes takes a
@@ -20,10 +21,11 @@
 // a whole landmark row.  This stage is not a dense contraction; it runs on the
 // vector ALUs, not on MFMA.
 //
-// LDS per workgroup: a tile buffer [lb + 1][256 + 2] (the extra row is zero) that
-// holds C, then B, transposed (landmark-major) so that the statistics pass and
-// the C store are coalesced and the MFMA reads B columns without bank
-// conflicts.
+// LDS per workgroup: a tile buffer that holds C as float32 [lb][256 + 4], then
+// B as bf16 high and low parts [lb + 1][264] each (the extra row is zero),
+// both landmark-major, so that the statistics pass and the C store are
+// coalesced and the MFMA reads eight tokens of a landmark row as one 16-byte
+// access without bank conflicts.
 #include "lapnys_internal.hpp"
 #include "ns_small.hpp"
 
@@ -32,8 +34,12 @@ namespace lapnys {
 namespace {
 
 constexpr int kTT = 256;        // tokens per tile = lanes per workgroup
-constexpr int kTP = kTT + 4;    // tile buffer row stride (floats; rows stay 16-byte aligned)
+constexpr int kTP = kTT + 4;    // C tile row stride (floats; rows stay 16-byte aligned)
+constexpr int kRB = kTT + 8;    // B tile row stride (bf16; 528-byte rows: 16-byte aligned, and
+                                // 16 consecutive rows start in distinct 4-bank groups)
+constexpr int kTileRow = kRB;   // tile buffer floats per landmark row: max(kTP, 2 kRB / 2)
 constexpr int kNW = kTT / 64;   // wavefronts per workgroup
+static_assert(kTileRow >= kTP, "the C tile must fit in the tile buffer");
 
 // A token row held as raw 16-byte words: issued early, widened later.
 template <typename T, int D>
@@ -73,20 +79,36 @@ __device__ __forceinline__ void widen_row(const RawRow<uint16_t, D>& r, float (&
   }
 }
 
-// Half of the V operand of the B V MFMA for one tile, per lane:
-// V[t0 + 64 lk + s][col] for the kTT/8 steps s of half h (s in [32h, 32h+32)).
-// (Step s of lane group lk takes token 64 lk + s of the tile: every token is
-// summed exactly once, and one lane's B values for four consecutive steps are
-// contiguous in LDS.)  Tokens past N read the last token's row (their B column
-// is zero).  Each half is issued well before its MFMAs.
+// Half of the V operand of the B V MFMA for one tile, per lane: for the four
+// 32-token steps s = 4 h + sp of half h, V[t0 + 32 s + 8 lk + e][col], e < 8
+// (step s covers tokens t0 + 32 s + [0, 32), lane group lk eight of them).
+// Tokens past N read the last token's row (their B column is zero).  Each
+// half is issued well before its MFMAs.
 template <typename T, int D>
 struct VHalf {
   T w[kTT / 8];
   __device__ __forceinline__ void issue(const T* __restrict__ vcol, int t0, int lk, int h, int tok_last) {
 #pragma unroll
-    for (int i = 0; i < kTT / 8; ++i) w[i] = vcol[min(t0 + 64 * lk + 32 * h + i, tok_last) * D];
+    for (int sp = 0; sp < 4; ++sp)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        w[8 * sp + e] = vcol[min(t0 + 128 * h + 32 * sp + 8 * lk + e, tok_last) * D];
   }
-  __device__ __forceinline__ float get(int i) const { return widen(w[i]); }
+  // The eight values of step sp as a bf16 MFMA operand: bf16 inputs as they
+  // are (lo unused), float32 inputs split into high and low parts.
+  __device__ __forceinline__ void operand(int sp, u32x4& hi, u32x4& lo) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (sizeof(T) == 2) {
+        hi[i] = (uint32_t)w[8 * sp + 2 * i] | ((uint32_t)w[8 * sp + 2 * i + 1] << 16);
+      } else {
+        uint32_t h, l;
+        split2(widen(w[8 * sp + 2 * i]), widen(w[8 * sp + 2 * i + 1]), h, l);
+        hi[i] = h;
+        lo[i] = l;
+      }
+    }
+  }
 };
 
 // Where each of the four landmarks of a group reads its features from:
@@ -100,16 +122,29 @@ struct VHalf {
 constexpr int kLds = 0, kSgpr = 1;
 constexpr int kSrc[4] = {kLds, kLds, kLds, kLds};
 
-// tl[j][col] = exp2(scale * sum_t |x[t] - k_j[t]|) for the lb landmarks of the
-// block (0 for a lane past the last token).  kl: the block's landmark rows in
-// LDS; kg: the same rows in global memory.  Four landmarks at a time, each
+// Row j of the tile = exp2(scale * sum_t |x[t] - k_j[t]|) for the lb landmarks
+// of the block (0 for a lane past the last token): float32 rows of stride kTP
+// at tl, or (SPLIT) bf16 high parts at tl and low parts rows * kRB further,
+// rows of stride kRB, followed by a zero row lb.  kl: the block's landmark
+// rows in LDS; kg: the same rows in global memory.  Four landmarks at a time, each
 // with two partial sums (even / odd features), give eight independent add
 // chains; the operands of the next 4-feature chunk are loaded while the
 // current chunk is summed, and the compiler barriers keep that shape.
-template <int D>
+template <int D, bool SPLIT>
 __device__ __forceinline__ void kernel_row(const float (&x)[D], const float* __restrict__ kl,
                                            const float* __restrict__ kg, int lb, float scale, float* __restrict__ tl,
-                                           int col, bool valid) {
+                                           int rows, int col, bool valid) {
+  auto put = [&](int j, float sum) {
+    const float val = valid ? exp2f(sum * scale) : 0.f;
+    if constexpr (SPLIT) {
+      __bf16* th = reinterpret_cast<__bf16*>(tl);
+      const __bf16 hi = (__bf16)val;
+      th[j * kRB + col] = hi;
+      th[(rows + j) * kRB + col] = (__bf16)(val - (float)hi);
+    } else {
+      tl[j * kTP + col] = val;
+    }
+  };
   int j = 0;
   for (; j + 4 <= lb; j += 4) {
     float sa[4] = {0.f, 0.f, 0.f, 0.f}, sb[4] = {0.f, 0.f, 0.f, 0.f};
@@ -136,7 +171,7 @@ __device__ __forceinline__ void kernel_row(const float (&x)[D], const float* __r
                    "+v"(sb[2]), "+v"(sb[3])::"memory");
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) tl[(j + u) * kTP + col] = valid ? exp2f((sa[u] + sb[u]) * scale) : 0.f;
+    for (int u = 0; u < 4; ++u) put(j + u, sa[u] + sb[u]);
   }
   for (; j < lb; ++j) {
     float sa = 0.f, sb = 0.f;
@@ -148,14 +183,19 @@ __device__ __forceinline__ void kernel_row(const float (&x)[D], const float* __r
       sa += fabsf(x[t + 2] - kv.z);
       sb += fabsf(x[t + 3] - kv.w);
     }
-    tl[j * kTP + col] = valid ? exp2f((sa + sb) * scale) : 0.f;
+    put(j, sa + sb);
+  }
+  if constexpr (SPLIT) {
+    __bf16* th = reinterpret_cast<__bf16*>(tl);
+    th[lb * kRB + col] = (__bf16)0.f;
+    th[(rows + lb) * kRB + col] = (__bf16)0.f;
   }
 }
 
 // One workgroup's share of the stage: landmark block jb (lb <= lbmax
 // landmarks from j0 = jb * lbmax), tile group g, problem p.  LBB = 16-row
 // blocks per landmark block (lbmax rounded up to 16, over 16).  tl: the
-// workgroup's LDS, (lbmax + 1) * kTP + lbmax * D floats.
+// workgroup's LDS, (lbmax + 1) * kTileRow + lbmax * D floats.
 template <typename T, int D, int LBB>
 __device__ __forceinline__ void l1exp_body(const T* __restrict__ q, const T* __restrict__ k,
                                            const T* __restrict__ v, const float* __restrict__ kt,
@@ -163,15 +203,17 @@ __device__ __forceinline__ void l1exp_body(const T* __restrict__ q, const T* __r
                                            float* __restrict__ bvpart, int N, int ldc, int m, int lbmax, int ntiles,
                                            int tpg, int groups, float scale, int jb, int g, int p,
                                            float* __restrict__ tl) {
-  // tl: [lb + 1][kTP], row lb stays zero; then kl: [lb][D], this block's landmark rows
-  float* kl = tl + (lbmax + 1) * kTP;
+  // tl: the tile buffer, (lbmax + 1) * kTileRow floats; then kl: [lb][D],
+  // this block's landmark rows
+  float* kl = tl + (lbmax + 1) * kTileRow;
+  const __bf16* bh = reinterpret_cast<const __bf16*>(tl);  // B tile high parts, [lbmax + 1][kRB]
+  const __bf16* bl = bh + (lbmax + 1) * kRB;               // low parts
 
   const int j0 = jb * lbmax;
   const int lb = min(lbmax, m - j0);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
   const float* kg = kt + ((size_t)p * m + j0) * D;  // this block's K~ rows
-  for (int e = lb * kTP + tid; e < (lb + 1) * kTP; e += kTT) tl[e] = 0.f;
   for (int e = tid; e < lb * D; e += kTT) kl[e] = kg[e];
   const int li = lane & 15, lk = lane >> 4;
 
@@ -193,11 +235,12 @@ __device__ __forceinline__ void l1exp_body(const T* __restrict__ q, const T* __r
   const size_t prob = (size_t)p * N * D;
   const int tile_begin = g * tpg;
   const int tile_end = min(ntiles, tile_begin + tpg);
-  // Lane li of row block bi reads landmark row 16 bi + li, or the zero row lb
-  // past the block's landmarks.
-  const float* arow[BIW];
+  // Lane li of row block bi reads landmark row 16 bi + li of the B tile, or
+  // the zero row lb past the block's landmarks; lane group lk reads tokens
+  // 8 lk + [0, 8) of each 32-token step.
+  int aoff[BIW];
 #pragma unroll
-  for (int a = 0; a < BIW; ++a) arow[a] = tl + min(16 * min(bi0 + a, LBB - 1) + li, lb) * kTP + 64 * lk;
+  for (int a = 0; a < BIW; ++a) aoff[a] = min(16 * min(bi0 + a, LBB - 1) + li, lb) * kRB + 8 * lk;
   const T* vcol = v + prob + 16 * bt0 + li;
   const int tok_last = N - 1;
 
@@ -213,7 +256,7 @@ __device__ __forceinline__ void l1exp_body(const T* __restrict__ q, const T* __r
     issue_row<T, D>(q + row, valid, raw);
     widen_row<D>(raw, x);
     __syncthreads();  // tile buffer free (previous tile's MFMA reads done)
-    kernel_row<D>(x, kl, kg, lb, scale, tl, tid, valid);
+    kernel_row<D, false>(x, kl, kg, lb, scale, tl, lbmax + 1, tid, valid);
     __syncthreads();
 
     // The key row and this lane's V operands are issued now and arrive while
@@ -272,32 +315,43 @@ __device__ __forceinline__ void l1exp_body(const T* __restrict__ q, const T* __r
     // ---- B = k(K~, K), kept on chip ----
     widen_row<D>(raw, x);
     __syncthreads();  // statistics pass done with the tile buffer
-    kernel_row<D>(x, kl, kg, lb, scale, tl, tid, valid);
+    kernel_row<D, true>(x, kl, kg, lb, scale, tl, lbmax + 1, tid, valid);
     __syncthreads();
 
     // ---- B V partial: acc[landmark][feature] += sum over the tile's tokens ----
-    // fp32 MFMA 16x16x4: lane l supplies A[l%16][l/16] = B[landmark][token] and
-    // B[l/16][l%16] = V[token][feature], token = 64 (l/16) + step.  A lane's B
-    // values for four steps are one 16-byte LDS read; the first half of V is
-    // already in registers and the second half lands during the first half's
-    // MFMAs; tile-buffer rows past the block's landmarks are zero.
+    // bf16 MFMA 16x16x32, one 32-token step at a time: lane (li, lk) supplies
+    // A[li][8 lk + e] = B[landmark][token 32 s + 8 lk + e] (one 16-byte LDS
+    // read of the high parts, one of the low parts) and B[8 lk + e][li] =
+    // V[same token][feature].  Per step and row block: Blo V + Bhi V for bf16
+    // V, plus Bhi Vlo for float32 V.  The first half of V is already in
+    // registers and the second half lands during the first half's MFMAs; tile
+    // rows past the block's landmarks are zero.
     VHalf<T, D> v1;
     v1.issue(vcol, t0, lk, 1, tok_last);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const VHalf<T, D>& vh = h ? v1 : v0;
 #pragma unroll
-      for (int i = 0; i < kTT / 8; i += 4) {
-        float4 av[BIW];
-#pragma unroll
-        for (int a = 0; a < BIW; ++a) av[a] = *reinterpret_cast<const float4*>(arow[a] + 32 * h + i);
+      for (int sp = 0; sp < 4; ++sp) {
+        const int s32 = 32 * (4 * h + sp);
+        u32x4 vhi, vlo;
+        vh.operand(sp, vhi, vlo);
+        bf16x8 ah[BIW], al[BIW];
 #pragma unroll
         for (int a = 0; a < BIW; ++a) {
-          acc[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a].x, vh.get(i + 0), acc[a], 0, 0, 0);
-          acc[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a].y, vh.get(i + 1), acc[a], 0, 0, 0);
-          acc[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a].z, vh.get(i + 2), acc[a], 0, 0, 0);
-          acc[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a].w, vh.get(i + 3), acc[a], 0, 0, 0);
+          ah[a] = *reinterpret_cast<const bf16x8*>(bh + aoff[a] + s32);
+          al[a] = *reinterpret_cast<const bf16x8*>(bl + aoff[a] + s32);
         }
+        const bf16x8 vb = __builtin_bit_cast(bf16x8, vhi);
+#pragma unroll
+        for (int a = 0; a < BIW; ++a) acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[a], vb, acc[a], 0, 0, 0);
+        if constexpr (sizeof(T) == 4) {
+          const bf16x8 vl = __builtin_bit_cast(bf16x8, vlo);
+#pragma unroll
+          for (int a = 0; a < BIW; ++a) acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[a], vl, acc[a], 0, 0, 0);
+        }
+#pragma unroll
+        for (int a = 0; a < BIW; ++a) acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[a], vb, acc[a], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -367,7 +421,7 @@ template <typename T, int D, int LBB, int KS>
 hipError_t launch_kernel(const Plan& pl, const void* q, const void* k, const void* v, Work& w, hipStream_t s,
                          Span t) {
   const int lbmax = pl.lb;
-  size_t floats = (size_t)(lbmax + 1) * kTP + (size_t)lbmax * D;
+  size_t floats = (size_t)(lbmax + 1) * kTileRow + (size_t)lbmax * D;
   if (KS > 0 && floats < (size_t)ns_detail::kNsLdsFloats) floats = ns_detail::kNsLdsFloats;
   const size_t shmem = floats * sizeof(float);
   auto kern = l1exp_kernel<T, D, LBB, KS>;

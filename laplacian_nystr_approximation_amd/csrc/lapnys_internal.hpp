@@ -10,8 +10,25 @@
 
 namespace lapnys {
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Splits two floats into bf16 high parts (round to nearest even) and bf16
+// low parts (the rounded remainders), each pair packed in one dword: with
+// both operands of a product split this way, hi*hi + hi*lo + lo*hi on bf16
+// MFMA keeps all but about 2^-16 of the product.
+__device__ __forceinline__ void split2(float z0, float z1, uint32_t& hi, uint32_t& lo) {
+  const bf16x2 h = __builtin_convertvector((f32x2){z0, z1}, bf16x2);
+  const f32x2 hf = __builtin_convertvector(h, f32x2);
+  const bf16x2 l = __builtin_convertvector((f32x2){z0 - hf.x, z1 - hf.y}, bf16x2);
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, l);
+}
 
 // Input element widening: float32 passes through, bfloat16 (stored as its
 // 16-bit pattern) widens exactly by placing it in the high half of a float32.

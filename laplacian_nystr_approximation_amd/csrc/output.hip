@@ -28,12 +28,6 @@ namespace lapnys {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 constexpr int kXLD = 65;   // LDS row stride of X in the prologue
 constexpr int kSlots = 16; // C loads of four tokens each held per lane (64 landmarks)
 
@@ -47,16 +41,6 @@ __device__ __forceinline__ uint32_t lane_mask(bool ok) {
 }
 
 __device__ __forceinline__ float masked(float v, uint32_t mk) { return __uint_as_float(__float_as_uint(v) & mk); }
-
-// Splits two floats into bf16 high parts (round to nearest even) and bf16
-// low parts (the rounded remainders), each pair packed in one dword.
-__device__ __forceinline__ void split2(float z0, float z1, uint32_t& hi, uint32_t& lo) {
-  const bf16x2 h = __builtin_convertvector((f32x2){z0, z1}, bf16x2);
-  const f32x2 hf = __builtin_convertvector(h, f32x2);
-  const bf16x2 l = __builtin_convertvector((f32x2){z0 - hf.x, z1 - hf.y}, bf16x2);
-  hi = __builtin_bit_cast(uint32_t, h);
-  lo = __builtin_bit_cast(uint32_t, l);
-}
 
 // Y^T in LDS: element (feature f, landmark l) of a [D][rl] bf16 array (rl a
 // multiple of 64).  The 8-landmark chunks of a row are XOR-swizzled by the

@@ -266,35 +266,34 @@ __device__ __forceinline__ void l1exp_body(const T* __restrict__ q, const T* __r
     v0.issue(vcol, t0, lk, 0, tok_last);
 
     // ---- column statistics of C over the tile, and the C^T store ----
-    // Wavefront w takes landmarks w, w + 4, ..., four of them at a time so
-    // that their wavefront reductions overlap.
+    // Lane l takes tokens 4 l + [0, 4) of the tile: one 16-byte LDS read and
+    // one 16-byte store of the C^T row per landmark.  Wavefront w takes
+    // landmarks w, w + 4, ..., four of them at a time so that their
+    // wavefront reductions overlap.  Tokens past N hold C = 0 (kernel_row),
+    // so the sums need no mask; the squared deviations do.  The C^T row
+    // stride is N rounded up to 4, so a lane's 16-byte store past N stays in
+    // the row's padding.
+    const bool full = nvalid == kTT;
+    const float inv_n = 1.f / (float)nvalid;  // 1/256 exactly for a full tile
     for (int jq = w; jq < lb; jq += 4 * kNW) {
-      float vals[4][kTT / 64];
+      float4 vals[4];
       float s[4], m2[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int jj = min(jq + kNW * u, lb - 1);  // rows past lb: read, not stored
-        s[u] = 0.f;
-#pragma unroll
-        for (int c = 0; c < kTT / 64; ++c) {
-          const int col = lane + 64 * c;
-          vals[u][c] = tl[jj * kTP + col];
-          if (col < nvalid) s[u] += vals[u][c];
-        }
+        vals[u] = *reinterpret_cast<const float4*>(tl + jj * kTP + 4 * lane);
+        s[u] = (vals[u].x + vals[u].y) + (vals[u].z + vals[u].w);
       }
       wave_sum_dpp_n<4>(s);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const float mean = s[u] / (float)nvalid;
-        m2[u] = 0.f;
+        const float mean = s[u] * inv_n;
+        float d[4] = {vals[u].x - mean, vals[u].y - mean, vals[u].z - mean, vals[u].w - mean};
+        if (!full) {
 #pragma unroll
-        for (int c = 0; c < kTT / 64; ++c) {
-          const int col = lane + 64 * c;
-          if (col < nvalid) {
-            const float dv = vals[u][c] - mean;
-            m2[u] += dv * dv;
-          }
+          for (int i = 0; i < 4; ++i) d[i] = (4 * lane + i < nvalid) ? d[i] : 0.f;
         }
+        m2[u] = (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
       }
       wave_sum_dpp_n<4>(m2);
 #pragma unroll
@@ -303,11 +302,7 @@ __device__ __forceinline__ void l1exp_body(const T* __restrict__ q, const T* __r
         if (j < lb) {
           if (lane == 0) stats[((size_t)p * ntiles + tile) * m + j0 + j] = make_float2(s[u], m2[u]);
           float* crow = ct + ((size_t)p * m + j0 + j) * ldc + t0;
-#pragma unroll
-          for (int c = 0; c < kTT / 64; ++c) {
-            const int col = lane + 64 * c;
-            if (col < nvalid) crow[col] = vals[u][c];
-          }
+          if (4 * lane < nvalid) *reinterpret_cast<float4*>(crow + 4 * lane) = vals[u];
         }
       }
     }

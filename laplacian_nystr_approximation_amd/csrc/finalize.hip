@@ -10,7 +10,10 @@
 //
 // One lane per B V element: the launch is wide (every partial is read once,
 // in parallel across the chip) and each lane keeps up to 16 groups' loads in
-// flight before its ordered adds.  One extra workgroup per problem produces
+// flight before its ordered adds.  Loads past the last group or tile read a
+// clamped, valid address and are dropped where they are used: a load under a
+// condition would become a branch with its own wait, one memory round trip
+// per load.  One extra workgroup per problem produces
 // the statistics, one lane per landmark.  Every reduction has a fixed order,
 // so results repeat bit for bit.
 #include <math.h>
@@ -39,7 +42,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float2* __restrict__ 
     for (int g0 = 0; g0 < groups; g0 += kChunk) {
       float v[kChunk];
 #pragma unroll
-      for (int u = 0; u < kChunk; ++u) v[u] = (g0 + u < groups) ? src[(size_t)(g0 + u) * md] : 0.f;
+      for (int u = 0; u < kChunk; ++u) v[u] = src[(size_t)min(g0 + u, groups - 1) * md];
 #pragma unroll
       for (int u = 0; u < kChunk; ++u)
         if (g0 + u < groups) sum += v[u];
@@ -64,7 +67,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float2* __restrict__ 
   if (ntiles <= kChunk) {
     float2 v[kChunk];
 #pragma unroll
-    for (int u = 0; u < kChunk; ++u) v[u] = (u < ntiles) ? st[(size_t)u * m] : make_float2(0.f, 0.f);
+    for (int u = 0; u < kChunk; ++u) v[u] = st[(size_t)min(u, ntiles - 1) * m];
 #pragma unroll
     for (int u = 0; u < kChunk; ++u)
       if (u < ntiles) total += (double)v[u].x;
@@ -81,7 +84,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float2* __restrict__ 
     for (int i0 = 0; i0 < ntiles; i0 += kChunk) {
       float v[kChunk];
 #pragma unroll
-      for (int u = 0; u < kChunk; ++u) v[u] = (i0 + u < ntiles) ? st[(size_t)(i0 + u) * m].x : 0.f;
+      for (int u = 0; u < kChunk; ++u) v[u] = st[(size_t)min(i0 + u, ntiles - 1) * m].x;
 #pragma unroll
       for (int u = 0; u < kChunk; ++u)
         if (i0 + u < ntiles) total += (double)v[u];
@@ -90,7 +93,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float2* __restrict__ 
     for (int i0 = 0; i0 < ntiles; i0 += kChunk) {
       float2 v[kChunk];
 #pragma unroll
-      for (int u = 0; u < kChunk; ++u) v[u] = (i0 + u < ntiles) ? st[(size_t)(i0 + u) * m] : make_float2(0.f, 0.f);
+      for (int u = 0; u < kChunk; ++u) v[u] = st[(size_t)min(i0 + u, ntiles - 1) * m];
 #pragma unroll
       for (int u = 0; u < kChunk; ++u) {
         if (i0 + u < ntiles) {

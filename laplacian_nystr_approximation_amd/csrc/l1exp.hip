@@ -214,7 +214,19 @@ __device__ __forceinline__ void l1exp_body(const T* __restrict__ q, const T* __r
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
   const float* kg = kt + ((size_t)p * m + j0) * D;  // this block's K~ rows
-  for (int e = tid; e < lb * D; e += kTT) kl[e] = kg[e];
+  {
+    // The block's landmark rows into LDS, every load issued before the first
+    // store (lb <= 64 rows, at most four 16-byte loads per lane).
+    constexpr int kV = 64 * D / 4 / kTT;
+    const int n4 = lb * D / 4;
+    const float4* kg4 = reinterpret_cast<const float4*>(kg);
+    float4 kv[kV];
+#pragma unroll
+    for (int i = 0; i < kV; ++i) kv[i] = kg4[min(tid + kTT * i, n4 - 1)];
+#pragma unroll
+    for (int i = 0; i < kV; ++i)
+      if (tid + kTT * i < n4) reinterpret_cast<float4*>(kl)[tid + kTT * i] = kv[i];
+  }
   const int li = lane & 15, lk = lane >> 4;
 
   // B V output blocks (16 x 16) of this wavefront: one 16-feature column block

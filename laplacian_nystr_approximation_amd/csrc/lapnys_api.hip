@@ -113,6 +113,7 @@ int make_plan(const lapnys_params* p, Plan* pl) {
   P.off_sigma = take(Pn * P.m * f);
   P.off_rs = take(Pn * P.m * f);
   P.off_y = take(Pn * P.m * P.d * f);
+  P.off_yt = take(P.fused_ns ? Pn * 2 * P.d * 64 * sizeof(uint16_t) : 0);
   P.total = off;
   return LAPNYS_OK;
 }
@@ -153,6 +154,7 @@ lapnys::Work carve(const Plan& pl, void* ws) {
   W.sigma = (float*)(b + pl.off_sigma);
   W.rs = (float*)(b + pl.off_rs);
   W.y = (float*)(b + pl.off_y);
+  W.yt = (__bf16*)(b + pl.off_yt);
   W.x_final = W.x;
   return W;
 }

@@ -95,14 +95,25 @@ struct Plan {
   int groups;       // tile groups per problem
   // workspace offsets in bytes
   size_t off_kt, off_w, off_x, off_x2, off_pm, off_ct, off_stats, off_bvpart, off_bv,
-      off_mu, off_sigma, off_rs, off_y, total;
+      off_mu, off_sigma, off_rs, off_y, off_yt, total;
 };
 
 // Device pointers into one call's workspace.
 struct Work {
   float *kt, *w, *x, *x2, *pm, *ct, *stats, *bvpart, *bv, *mu, *sigma, *rs, *y;
+  __bf16* yt;          // m <= 64: Y^T as bf16 high and low parts, [P][2][d][64] (yt_index layout)
   float* x_final;      // the Newton-Schulz result (x or x2), set by launch_ns
 };
+
+// Position of Y^T element (feature f, landmark l) in a [D][rl] bf16 array (rl
+// a multiple of 64), the layout the output stage reads its B operands from.
+// The 8-landmark chunks of a row are XOR-swizzled by t = f / (D / 16), the
+// index of the lane that reads feature f, so the 16 lanes that read one
+// chunk column for 16 different features spread over distinct banks.
+__device__ __forceinline__ int yt_index(int f, int l, int t, int rl) {
+  const int c = l >> 3;
+  return f * rl + 8 * ((c & ~7) | ((c ^ t) & 7)) + (l & 7);
+}
 
 // Optional timing events of one stage: the start time of its first kernel and
 // the end time of its last kernel, taken from the kernels' own dispatch
@@ -121,6 +132,8 @@ hipError_t launch_ns(const Plan& pl, Work& w, hipStream_t s, Span t = {});
 // Newton-Schulz solver (and sets w.x_final).
 hipError_t launch_l1exp(const Plan& pl, const void* q, const void* k, const void* v, Work& w,
                         hipStream_t s, Span t = {});
+// Reductions after the kernel-matrix stage: B V, the whitening statistics,
+// and for m <= 64 also Y = X (B V) into w.yt.
 hipError_t launch_reduce(const Plan& pl, const Work& w, hipStream_t s, Span t = {});
 hipError_t launch_y(const Plan& pl, const Work& w, hipStream_t s, Span t = {});  // m > kFusedNsMaxM only
 hipError_t launch_output(const Plan& pl, const Work& w, float* out, hipStream_t s, Span t = {});

@@ -9,10 +9,11 @@
 //    C loads (up to 64 landmarks) are issued before anything else, so their
 //    latency overlaps the Y prologue.  For m > 64 the loads of the next 64
 //    landmarks are issued slot by slot as the current ones are consumed.
-//  * Prologue (m <= 64): the workgroup forms Y = X (B V) itself on fp32 MFMA
-//    (a 64 x 64 x 64 product, zero padded); for larger m, Y comes from a
-//    batched tile GEMM.  Either way Y is stored in LDS transposed, as bf16
-//    high and low parts (y = hi + lo to about 16 bits).
+//  * Prologue: Y = X (B V) is stored in LDS transposed, as bf16 high and low
+//    parts (y = hi + lo to about 16 bits).  For m <= 64 the finalize stage
+//    has already formed it in this layout (once per problem) and the
+//    workgroup copies 16 KB; for larger m it comes from a batched tile GEMM
+//    in float32 and is split here.
 //  * Main loop: Z Y on bf16 MFMA 16x16x32 with three products per step,
 //    Zhi Yhi + Zhi Ylo + Zlo Yhi: the dropped Zlo Ylo term and the rounding
 //    of the low parts are about 2^-16 of each product, so the stage keeps
@@ -28,7 +29,6 @@ namespace lapnys {
 
 namespace {
 
-constexpr int kXLD = 65;   // LDS row stride of X in the prologue
 constexpr int kSlots = 16; // C loads of four tokens each held per lane (64 landmarks)
 
 // All-ones when ok, else zero, opaque to the optimiser: masking a loaded
@@ -41,15 +41,6 @@ __device__ __forceinline__ uint32_t lane_mask(bool ok) {
 }
 
 __device__ __forceinline__ float masked(float v, uint32_t mk) { return __uint_as_float(__float_as_uint(v) & mk); }
-
-// Y^T in LDS: element (feature f, landmark l) of a [D][rl] bf16 array (rl a
-// multiple of 64).  The 8-landmark chunks of a row are XOR-swizzled by the
-// reading lane's index t = f / (D/16), so the 16 lanes that read one chunk
-// column for 16 different features spread over distinct banks.
-__device__ __forceinline__ int yt_index(int f, int l, int t, int rl) {
-  const int c = l >> 3;
-  return f * rl + 8 * ((c & ~7) | ((c ^ t) & 7)) + (l & 7);
-}
 
 template <int D>
 struct OutVec;
@@ -64,8 +55,7 @@ struct OutVec<32> {
 
 template <int D, bool FUSED_Y>
 __global__ __launch_bounds__(256) void output_kernel(const float* __restrict__ ct, int ldc,
-                                                     const float* __restrict__ x, int mp,
-                                                     const float* __restrict__ bv, const float* __restrict__ y,
+                                                     const __bf16* __restrict__ yt, const float* __restrict__ y,
                                                      const float* __restrict__ mu, const float* __restrict__ rs,
                                                      float* __restrict__ out, int N, int m) {
   constexpr int DB = D / 16;
@@ -93,68 +83,27 @@ __global__ __launch_bounds__(256) void output_kernel(const float* __restrict__ c
   };
 
   if constexpr (FUSED_Y) {
-    // Prologue operands are loaded into registers ahead of the C loads, and
+    // Y^T high and low parts come from the finalize stage in this LDS layout
+    // (2 D 64 bf16): they are loaded into registers ahead of the C loads, and
     // nothing consumes a loaded value before the scheduling barrier, so the
-    // wait for the prologue operands leaves the C loads in flight.
-    constexpr int kXPer = 64 * 64 / 256, kBPer = 64 * D / 256;
-    const float* xp = x + (size_t)p * mp * mp;
-    const float* bp = bv + (size_t)p * m * D;
-    float xr[kXPer], br[kBPer];
+    // wait for them leaves the C loads in flight.
+    constexpr int kYv = 2 * D * 64 * 2 / 16 / 256;  // 16-byte loads per lane
+    const float4* ysrc = reinterpret_cast<const float4*>(yt + (size_t)p * 2 * D * 64);
+    float4 yv[kYv];
 #pragma unroll
-    for (int i = 0; i < kXPer; ++i) xr[i] = xp[(size_t)(i * 4 + (tid >> 6)) * mp + (tid & 63)];  // row, col < 64 <= mp
-#pragma unroll
-    for (int i = 0; i < kBPer; ++i) br[i] = bp[min(tid + 256 * i, m * D - 1)];
+    for (int i = 0; i < kYv; ++i) yv[i] = ysrc[tid + 256 * i];
     const int jt = tid & 63;
     const float mu_t = mu[p * m + min(jt, m - 1)], rs_t = rs[p * m + min(jt, m - 1)];
 #pragma unroll
     for (int s = 0; s < kSlots; ++s) load_slot(0, s);
     __builtin_amdgcn_sched_barrier(0);
-
-    // Y = X (B V), 64 x D, on fp32 MFMA 32x32x2; X and B V zero padded to 64 rows.
-    float* xl = reinterpret_cast<float*>(mrs + 64);  // [64][kXLD]
-    float* bvl = xl + 64 * kXLD;                    // [64][D]
 #pragma unroll
-    for (int i = 0; i < kXPer; ++i) {
-      const int r = i * 4 + (tid >> 6), c = tid & 63;
-      xl[r * kXLD + c] = masked(xr[i], lane_mask(r < m && c < m));
-    }
-#pragma unroll
-    for (int i = 0; i < kBPer; ++i) bvl[tid + 256 * i] = masked(br[i], lane_mask(tid + 256 * i < m * D));
+    for (int i = 0; i < kYv; ++i) reinterpret_cast<float4*>(yth)[tid + 256 * i] = yv[i];
     {
       // Every wavefront stores the same 64 pairs (an unconditional store keeps
       // the two loads from being moved behind the C loads' wait).
       const uint32_t mk = lane_mask(jt < m);
       mrs[jt] = make_float2(masked(mu_t, mk), masked(rs_t, mk));
-    }
-    __syncthreads();
-    const int yi = lane & 31, yk = lane >> 5;
-    const int bi = w >> 1, bj = w & 1;
-    if (32 * bj < D) {
-      f32x16 acc = {0.f};
-      // Full 64-deep product over the zero-padded operands, unrolled so that
-      // the LDS reads run ahead of the MFMA chain.
-#pragma unroll
-      for (int k0 = 0; k0 < 64; k0 += 2) {
-        const float a = xl[(32 * bi + yi) * kXLD + k0 + yk];
-        const float b = bvl[(k0 + yk) * D + 32 * bj + yi];
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
-      }
-      // acc[r] = Y[32 bi + 8 (r / 4) + 4 yk + r % 4][32 bj + yi]: four
-      // consecutive landmarks of one feature, stored as one 8-byte run each.
-      const int f = 32 * bj + yi;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        bf16x4 hi, lo;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float v = acc[4 * q + r];
-          hi[r] = (__bf16)v;
-          lo[r] = (__bf16)(v - (float)hi[r]);
-        }
-        const int at = yt_index(f, 32 * bi + 8 * q + 4 * yk, f / DB, rl);
-        *reinterpret_cast<bf16x4*>(yth + at) = hi;
-        *reinterpret_cast<bf16x4*>(ytl + at) = lo;
-      }
     }
   } else {
 #pragma unroll
@@ -256,18 +205,17 @@ __global__ __launch_bounds__(256) void output_kernel(const float* __restrict__ c
 
 template <int D, bool FUSED_Y>
 hipError_t launch_typed(const Plan& pl, const Work& wk, float* out, hipStream_t s, Span t) {
-  // Y^T high and low parts (bf16, rl landmarks per row), the (mu, 1/sigma)
-  // pairs, and in the fused form the prologue's X and B V buffers.
+  // Y^T high and low parts (bf16, rl landmarks per row), then the
+  // (mu, 1/sigma) pairs.
   const size_t rl = FUSED_Y ? 64 : (size_t)(pl.m + 63) & ~(size_t)63;
-  const size_t shmem = 2 * D * rl * 2 + rl * 8 + (FUSED_Y ? (size_t)(64 * kXLD + 64 * D) * sizeof(float) : 0);
+  const size_t shmem = 2 * D * rl * 2 + rl * 8;
   auto kern = output_kernel<D, FUSED_Y>;
   if (shmem > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
   }
   hipExtLaunchKernelGGL(kern, dim3((pl.N + 255) / 256, pl.P), dim3(256), shmem, s, t.start, t.stop, 0, wk.ct, pl.ldc,
-                        wk.x_final, pl.mp,
-                     wk.bv, wk.y, wk.mu, wk.rs, out, pl.N, pl.m);
+                        wk.yt, wk.y, wk.mu, wk.rs, out, pl.N, pl.m);
   return hipGetLastError();
 }
 

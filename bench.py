@@ -109,6 +109,34 @@ def cpu_baseline(w, x, budget_s: float):
                       f"float64 numpy, one thread, {el:.1f} s"}
 
 
+def stage_hbm_bytes(w):
+    """Algorithmic HBM bytes per forward of the stages bounded by memory (all
+    problems): what each must read and write at least, from the sizes alone."""
+    s_in = 2 if w.dtype == "bf16" else 4
+    P, N, d, m = w.P, w.N, w.d, w.m
+    ntiles = -(-N // 256)
+    jblocks = 1 if m <= 64 else -(-m // 32)
+    tpg = max(1, ntiles * jblocks * P // 4096)
+    groups = -(-ntiles // tpg)
+    mp = 64 if m <= 64 else -(-m // 64) * 64
+    pool = P * (N * d * s_in + m * d * 4)
+    # partials in; B V, statistics out; X in and Y (split, or float32 for m > 64) out
+    y_out = 2 * d * 64 * 2 if m <= 64 else m * d * 4
+    finalize = P * (groups * m * d * 4 + ntiles * m * 8 + mp * mp * 4 + m * d * 4 + 3 * m * 4 + y_out)
+    output = P * (m * N * 4 + N * d * 4 + y_out + 2 * m * 4)
+    return {"pool": pool, "finalize": finalize, "output": output}
+
+
+def stage_rooflines(w, stage_ms):
+    out = {}
+    for name, nbytes in stage_hbm_bytes(w).items():
+        t = stage_ms[name] * 1e-3
+        gbs = nbytes / t / 1e9
+        out[name] = {"bound": "hbm", "achieved": gbs, "peak": HBM_BYTES_S / 1e9, "unit": "GB/s",
+                     "frac": gbs * 1e9 / HBM_BYTES_S, "bytes": nbytes, "ms": stage_ms[name]}
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -231,6 +259,7 @@ def main(argv=None):
                      "kernel_ms_samples": f"HIP events on every {EVERY}th timed step ({len(sampled)} of {K})"},
         "cpu_baseline": cpu,
         "stage_ms": stage_ms,
+        "stage_roofline": stage_rooflines(w, stage_ms),
         "ms_per_step_without_events": plain_ms,
     }
     print(json.dumps(line), flush=True)

@@ -22,7 +22,8 @@
 //    and feeds them as the A operand of token block a; the B operand of
 //    feature block b is Y[same 8 landmarks][D/16 li + b], one 16-byte LDS read.
 //    A lane thus ends up holding D/16 consecutive features of each of its
-//    tokens and writes them with one 16-byte (D = 64) or 8-byte (D = 32) store.
+//    tokens and writes them with one 16-byte (D = 64) or 8-byte (D = 32)
+//    streaming store.
 #include "lapnys_internal.hpp"
 
 namespace lapnys {
@@ -41,17 +42,6 @@ __device__ __forceinline__ uint32_t lane_mask(bool ok) {
 }
 
 __device__ __forceinline__ float masked(float v, uint32_t mk) { return __uint_as_float(__float_as_uint(v) & mk); }
-
-template <int D>
-struct OutVec;
-template <>
-struct OutVec<64> {
-  using type = float4;
-};
-template <>
-struct OutVec<32> {
-  using type = float2;
-};
 
 template <int D, bool FUSED_Y>
 __global__ __launch_bounds__(256) void output_kernel(const float* __restrict__ ct, int ldc,
@@ -183,8 +173,10 @@ __global__ __launch_bounds__(256) void output_kernel(const float* __restrict__ c
     }
   }
 
-  // acc[a][b][r] = O[token tb + 4 (4 lk + r) + a][feature DB li + b]
-  using V = typename OutVec<D>::type;
+  // acc[a][b][r] = O[token tb + 4 (4 lk + r) + a][feature DB li + b].  O is
+  // written with streaming (nontemporal) stores: it is not read again here,
+  // and the writes drain to memory while the kernel runs instead of being
+  // written back from L2 when it ends.
   float* op = out + (size_t)p * N * D + DB * li;
 #pragma unroll
   for (int r = 0; r < 4; ++r)
@@ -192,13 +184,13 @@ __global__ __launch_bounds__(256) void output_kernel(const float* __restrict__ c
     for (int a = 0; a < 4; ++a) {
       const int tok = tb + 16 * lk + 4 * r + a;
       if (tok < N) {
-        V o;
         if constexpr (DB == 4) {
-          o = make_float4(acc[a][0][r], acc[a][1][r], acc[a][2][r], acc[a][3][r]);
+          const f32x4 o = {acc[a][0][r], acc[a][1][r], acc[a][2][r], acc[a][3][r]};
+          __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(op + (size_t)tok * D));
         } else {
-          o = make_float2(acc[a][0][r], acc[a][1][r]);
+          const f32x2 o = {acc[a][0][r], acc[a][1][r]};
+          __builtin_nontemporal_store(o, reinterpret_cast<f32x2*>(op + (size_t)tok * D));
         }
-        *reinterpret_cast<V*>(op + (size_t)tok * D) = o;
       }
     }
 }

@@ -137,6 +137,68 @@ def stage_rooflines(w, stage_ms):
     return out
 
 
+SWEEP = ("sweep_64x64_bf16", "sweep_128x128_bf16", "long_256x256_bf16", HEADLINE)
+
+
+def sweep_main(args):
+    """Time against N at m = 256 (and the headline workload), warm and cold.
+
+    Per workload: the median, 10th and 90th percentile of single-call device
+    times (events around one forward on the stream); warm = back to back, cold
+    = a 512 MiB buffer written between calls so the last-level cache holds
+    none of the inputs; and the peak device memory of inputs, workspace and
+    output (the _ws form allocates nothing itself).  One JSON line each."""
+    import torch
+    import laplacian_nystr_approximation_amd.lapnys as L
+    from lapnys_inputs import make_inputs
+
+    dev = torch.device("cuda:0")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    for name in SWEEP:
+        w = WORKLOADS[name]
+        x = make_inputs(w)
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats(dev)
+        base = torch.cuda.memory_allocated(dev)
+
+        def up(a):
+            a = np.ascontiguousarray(a)
+            return torch.from_numpy(a.view(np.int16) if w.dtype == "bf16" else a).to(dev)
+
+        q, k, v = up(x.q), up(x.k), up(x.v)
+        del x
+        params = L.params_for(w)
+        out = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
+        ws = torch.empty(L.lapnys_workspace_size(params), dtype=torch.uint8, device=dev)
+        stream = torch.cuda.current_stream()
+        reps = 50 if w.N <= 16384 else 20
+        times = {}
+        for mode in ("warm", "cold"):
+            for _ in range(5):
+                L.lapnys_forward_ws(q, k, v, out, params, ws, stream)
+            ts = []
+            for _ in range(reps):
+                if mode == "cold":
+                    flush.fill_(1)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                L.lapnys_forward_ws(q, k, v, out, params, ws, stream)
+                e1.record(stream)
+                e1.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            times[mode] = {"median_ms": float(np.median(ts)), "p10_ms": float(np.percentile(ts, 10)),
+                           "p90_ms": float(np.percentile(ts, 90))}
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated(dev) - base
+        print(json.dumps({"workload": name, "N": w.N, "m": w.m, "P": w.P, "d": w.d, "ns_iters": w.ns_iters,
+                          "tokens_per_s_warm": w.P * w.N / (times["warm"]["median_ms"] * 1e-3),
+                          "warm": times["warm"], "cold": times["cold"], "peak_device_bytes": int(peak),
+                          "workspace_bytes": int(ws.numel())}), flush=True)
+        del q, k, v, out, ws
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,10 +206,15 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0: skip)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the bench line: warm and cold single-call times and peak memory over the "
+                         "length sweep at m = 256 and the headline workload")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="after the measurements, run a plain float32 copy kernel of this many MiB three times "
                          "(the known-size reference for HBM traffic counters)")
     args = ap.parse_args(argv)
+    if args.sweep:
+        return sweep_main(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this forward has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)

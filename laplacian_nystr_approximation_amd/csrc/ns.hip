@@ -25,19 +25,26 @@ namespace {
 // ---- 64 < m <= 256 -------------------------------------------------------
 
 // W rows [16*blockIdx.x, +16) of problem blockIdx.y; thread b owns column b.
+// Loads read clamped, in-bounds addresses (rows past m are masked where
+// used), so every load of the block issues before the first wait.
 template <int D>
 __global__ __launch_bounds__(256) void wbuild_big_kernel(const float* __restrict__ kt, float* __restrict__ w, int m,
                                                          int mp, float scale, float eps) {
   __shared__ float kl[16 * D];
   const int p = blockIdx.y, a0 = blockIdx.x * 16, b = threadIdx.x;
   const float* ktp = kt + (size_t)p * m * D;
-  for (int e = threadIdx.x; e < 16 * D; e += 256) {
-    const int a = a0 + e / D;
-    kl[e] = (a < m) ? ktp[(size_t)a * D + e % D] : 0.f;
+  constexpr int kPer = 16 * D / 256;
+  float kv[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = threadIdx.x + 256 * i;
+    kv[i] = ktp[(size_t)min(a0 + e / D, m - 1) * D + e % D];
   }
   float xb[D];
 #pragma unroll
-  for (int t = 0; t < D; ++t) xb[t] = (b < m) ? ktp[(size_t)b * D + t] : 0.f;
+  for (int t = 0; t < D; ++t) xb[t] = ktp[(size_t)min(b, m - 1) * D + t];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) kl[threadIdx.x + 256 * i] = kv[i];
   __syncthreads();
   if (b >= mp) return;
   for (int r = 0; r < 16; ++r) {
@@ -57,74 +64,107 @@ __global__ __launch_bounds__(256) void wbuild_big_kernel(const float* __restrict
   }
 }
 
-// alpha and X0 = W^T / alpha for problem blockIdx.x.
+// alpha and X0 = W^T / alpha for problem blockIdx.x.  W is bit-symmetric
+// (entry (a, b) sums the same |differences| in the same order as (b, a)), so
+// its 1-norm and inf-norm are the same largest column sum and W^T = W: alpha
+// = (max column sum)^2 and X0 = W / alpha, read row-major.  Column sums: one
+// lane per column, 16 rows' loads in flight at a time.
 __global__ __launch_bounds__(256) void alpha_x0_kernel(const float* __restrict__ w, float* __restrict__ x, int mp) {
-  __shared__ float red[512];
-  __shared__ float alpha_s;
+  __shared__ float red[4];
   const int p = blockIdx.x, tid = threadIdx.x;
   const float* wp = w + (size_t)p * mp * mp;
-  float rs = 0.f, cs = 0.f;
+  float cs = 0.f;
   if (tid < mp) {
-    for (int b = 0; b < mp; ++b) rs += fabsf(wp[(size_t)tid * mp + b]);
-    for (int a = 0; a < mp; ++a) cs += fabsf(wp[(size_t)a * mp + tid]);
-  }
-  red[tid] = rs;
-  red[256 + tid] = cs;
-  __syncthreads();
-  if (tid == 0) {
-    float rm = 0.f, cm = 0.f;
-    for (int i = 0; i < 256; ++i) {
-      rm = fmaxf(rm, red[i]);
-      cm = fmaxf(cm, red[256 + i]);
+    for (int a0 = 0; a0 < mp; a0 += 16) {  // mp is a multiple of 64
+      float v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = wp[(size_t)(a0 + u) * mp + tid];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) cs += fabsf(v[u]);
     }
-    alpha_s = cm * rm;
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) cs = fmaxf(cs, __shfl_xor(cs, off, 64));
+  if ((tid & 63) == 0) red[tid >> 6] = cs;
   __syncthreads();
-  const float alpha = alpha_s;
+  const float cm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float alpha = cm * cm;
   float* xp = x + (size_t)p * mp * mp;
-  for (int e = tid; e < mp * mp; e += 256) {
-    const int a = e / mp, b = e % mp;
-    xp[e] = wp[(size_t)b * mp + a] / alpha;
-  }
+  for (int e = tid; e < mp * mp; e += 256) xp[e] = wp[e] / alpha;
 }
 
 // One 64 x 64 output tile (blockIdx.x, blockIdx.y) of problem blockIdx.z:
 //   C = A B (mode 0)  or  C = A (2I - B) (mode 1),
-// reduction over [0, kext) (a multiple of 32) staged through LDS 32 at a time.
-// B entries outside [0, brows) x [0, bcols) read as zero (before the 2I
-// transform); C is stored for rows < crows and columns < ccols.  Each of the
-// four wavefronts owns a 32 x 32 block and issues fp32 MFMA 32x32x2.
+// reduction over [0, kext) (a multiple of 32), 32 at a time.  A stage's A
+// (64 x 32) and B (32 x 64) values are loaded into registers, two 16-byte
+// loads of each per lane, one stage ahead, and stored to the LDS buffer not
+// being read, so the loads overlap the products of the stage before.  B
+// entries outside [0, brows) x [0, bcols) read a clamped, in-bounds address
+// and are zeroed (before the 2I transform); C is stored for rows < crows and
+// columns < ccols.  Each of the four wavefronts owns a 32 x 32 block and
+// issues fp32 MFMA 32x32x2.  A's rows r0 + [0, 64) and columns [0, kext)
+// must be in range (lda and the row count are multiples of 64, kext <= lda).
 __global__ __launch_bounds__(256) void gemm64_kernel(const float* __restrict__ A, int lda, long long sa,
                                                      const float* __restrict__ B, int ldb, long long sb, int brows,
                                                      int bcols, float* __restrict__ C, int ldc, long long sc,
                                                      int crows, int ccols, int kext, int mode) {
-  __shared__ float as[64 * 33];
-  __shared__ float bs[32 * 64];
+  __shared__ float as[2][64 * 33];
+  __shared__ __align__(16) float bs[2][32 * 64];
   const int p = blockIdx.z, r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wr = w >> 1, wc = w & 1, li = lane & 31, lk = lane >> 5;
   const float* Ap = A + p * sa;
   const float* Bp = B + p * sb;
+  float4 ra[2], rb[2];
+  auto load = [&](int kc) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e4 = tid + 256 * i;
+      const int r = e4 >> 3, c4 = 4 * (e4 & 7);  // A: 64 rows of 8 float4
+      ra[i] = *reinterpret_cast<const float4*>(Ap + (size_t)(r0 + r) * lda + kc + c4);
+      const int br = e4 >> 4, bc4 = 4 * (e4 & 15);  // B: 32 rows of 16 float4
+      const int gr = kc + br, gc = c0 + bc4;
+      rb[i] = *reinterpret_cast<const float4*>(Bp + (size_t)min(gr, brows - 1) * ldb + min(gc, bcols - 4));
+    }
+  };
+  auto store = [&](int kc, int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e4 = tid + 256 * i;
+      const int r = e4 >> 3, c4 = 4 * (e4 & 7);
+      float* ad = &as[buf][r * 33 + c4];
+      ad[0] = ra[i].x;
+      ad[1] = ra[i].y;
+      ad[2] = ra[i].z;
+      ad[3] = ra[i].w;
+      const int br = e4 >> 4, bc4 = 4 * (e4 & 15);
+      const int gr = kc + br, gc = c0 + bc4;
+      float bv[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (!(gr < brows && gc + u < bcols)) bv[u] = 0.f;
+        if (mode) bv[u] = (gr == gc + u ? 2.f : 0.f) - bv[u];
+      }
+      *reinterpret_cast<float4*>(&bs[buf][br * 64 + bc4]) = make_float4(bv[0], bv[1], bv[2], bv[3]);
+    }
+  };
   f32x16 acc = {0.f};
+  load(0);
+  store(0, 0);
+  __syncthreads();
   for (int kc = 0; kc < kext; kc += 32) {
-    for (int e = tid; e < 64 * 32; e += 256) {
-      const int r = e >> 5, c = e & 31;
-      as[r * 33 + c] = Ap[(size_t)(r0 + r) * lda + kc + c];
-    }
-    for (int e = tid; e < 32 * 64; e += 256) {
-      const int r = e >> 6, c = e & 63;
-      const int gr = kc + r, gc = c0 + c;
-      float bv = (gr < brows && gc < bcols) ? Bp[(size_t)gr * ldb + gc] : 0.f;
-      if (mode) bv = (gr == gc ? 2.f : 0.f) - bv;
-      bs[r * 64 + c] = bv;
-    }
-    __syncthreads();
+    const int cur = (kc >> 5) & 1;
+    const bool more = kc + 32 < kext;
+    if (more) load(kc + 32);  // lands during this stage's products
 #pragma unroll
     for (int k0 = 0; k0 < 32; k0 += 2) {
-      const float a = as[(32 * wr + li) * 33 + k0 + lk];
-      const float b = bs[(k0 + lk) * 64 + 32 * wc + li];
+      const float a = as[cur][(32 * wr + li) * 33 + k0 + lk];
+      const float b = bs[cur][(k0 + lk) * 64 + 32 * wc + li];
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
     }
+    // The other buffer was last read in the stage before, behind the barrier
+    // that ended it.
+    if (more) store(kc + 32, cur ^ 1);
     __syncthreads();
   }
   float* Cp = C + p * sc;

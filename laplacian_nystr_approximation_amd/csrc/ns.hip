@@ -24,12 +24,15 @@ namespace {
 
 // ---- 64 < m <= 256 -------------------------------------------------------
 
-// W rows [16*blockIdx.x, +16) of problem blockIdx.y; thread b owns column b.
-// Loads read clamped, in-bounds addresses (rows past m are masked where
-// used), so every load of the block issues before the first wait.
+// W rows [16*blockIdx.x, +16) of problem blockIdx.y; thread b owns column b
+// and also writes the sum of its 16 entries (all positive) to
+// part[p][blockIdx.x][b], the block's share of the column sums.  Loads read
+// clamped, in-bounds addresses (rows past m are masked where used), so every
+// load of the block issues before the first wait.
 template <int D>
-__global__ __launch_bounds__(256) void wbuild_big_kernel(const float* __restrict__ kt, float* __restrict__ w, int m,
-                                                         int mp, float scale, float eps) {
+__global__ __launch_bounds__(256) void wbuild_big_kernel(const float* __restrict__ kt, float* __restrict__ w,
+                                                         float* __restrict__ part, int m, int mp, float scale,
+                                                         float eps) {
   __shared__ float kl[16 * D];
   const int p = blockIdx.y, a0 = blockIdx.x * 16, b = threadIdx.x;
   const float* ktp = kt + (size_t)p * m * D;
@@ -47,6 +50,7 @@ __global__ __launch_bounds__(256) void wbuild_big_kernel(const float* __restrict
   for (int i = 0; i < kPer; ++i) kl[threadIdx.x + 256 * i] = kv[i];
   __syncthreads();
   if (b >= mp) return;
+  float csum = 0.f;
   for (int r = 0; r < 16; ++r) {
     const int a = a0 + r;
     float val = 0.f;
@@ -61,27 +65,34 @@ __global__ __launch_bounds__(256) void wbuild_big_kernel(const float* __restrict
       if (a == b) val += eps;
     }
     w[((size_t)p * mp + a) * mp + b] = val;
+    csum += val;
   }
+  part[((size_t)p * (mp / 16) + blockIdx.x) * mp + b] = csum;
 }
 
-// alpha and X0 = W^T / alpha for problem blockIdx.x.  W is bit-symmetric
+// alpha and rows [blockIdx.y mp / 16, +mp / 16) of X0 = W^T / alpha for
+// problem blockIdx.x (every workgroup of a problem forms the same alpha from
+// the same partials, in the same order).  W is bit-symmetric
 // (entry (a, b) sums the same |differences| in the same order as (b, a)), so
 // its 1-norm and inf-norm are the same largest column sum and W^T = W: alpha
 // = (max column sum)^2 and X0 = W / alpha, read row-major.  Column sums: one
-// lane per column, 16 rows' loads in flight at a time.
-__global__ __launch_bounds__(256) void alpha_x0_kernel(const float* __restrict__ w, float* __restrict__ x, int mp) {
+// lane per column adds the W build's mp / 16 (<= 16) partial sums in block
+// order, all loaded at once.
+__global__ __launch_bounds__(256) void alpha_x0_kernel(const float* __restrict__ w, const float* __restrict__ part,
+                                                       float* __restrict__ x, int mp) {
   __shared__ float red[4];
   const int p = blockIdx.x, tid = threadIdx.x;
   const float* wp = w + (size_t)p * mp * mp;
+  const int nblk = mp / 16;  // also the rows of this workgroup's X0 slab
   float cs = 0.f;
   if (tid < mp) {
-    for (int a0 = 0; a0 < mp; a0 += 16) {  // mp is a multiple of 64
-      float v[16];
+    const float* pp = part + (size_t)p * nblk * mp + tid;
+    float v[16];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = wp[(size_t)(a0 + u) * mp + tid];
+    for (int u = 0; u < 16; ++u) v[u] = pp[(size_t)min(u, nblk - 1) * mp];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) cs += fabsf(v[u]);
-    }
+    for (int u = 0; u < 16; ++u)
+      if (u < nblk) cs += v[u];
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) cs = fmaxf(cs, __shfl_xor(cs, off, 64));
@@ -89,8 +100,18 @@ __global__ __launch_bounds__(256) void alpha_x0_kernel(const float* __restrict__
   __syncthreads();
   const float cm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float alpha = cm * cm;
-  float* xp = x + (size_t)p * mp * mp;
-  for (int e = tid; e < mp * mp; e += 256) xp[e] = wp[e] / alpha;
+  // The slab: nblk rows of mp = 16 nblk^2 entries, nblk^2 / 16 per lane.
+  const size_t slab = (size_t)blockIdx.y * nblk * mp;
+  float* xp = x + (size_t)p * mp * mp + slab;
+  const float* ws = wp + slab;
+  for (int e0 = tid; e0 < nblk * mp; e0 += 256 * 16) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = ws[min(e0 + 256 * u, nblk * mp - 1)];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (e0 + 256 * u < nblk * mp) xp[e0 + 256 * u] = v[u] / alpha;
+  }
 }
 
 // One 64 x 64 output tile (blockIdx.x, blockIdx.y) of problem blockIdx.z:
@@ -194,12 +215,14 @@ hipError_t launch_ns(const Plan& pl, Work& wk, hipStream_t s, Span t) {
   const int mp = pl.mp;
   if (pl.d == 64)
     hipExtLaunchKernelGGL(wbuild_big_kernel<64>, dim3(mp / 16, pl.P), dim3(256), 0, s, t.start, nullptr, 0, wk.kt,
-                          wk.w, pl.m, mp, pl.scale, pl.eps);
+                          wk.w, wk.pm, pl.m, mp, pl.scale, pl.eps);
   else
     hipExtLaunchKernelGGL(wbuild_big_kernel<32>, dim3(mp / 16, pl.P), dim3(256), 0, s, t.start, nullptr, 0, wk.kt,
-                          wk.w, pl.m, mp, pl.scale, pl.eps);
-  hipExtLaunchKernelGGL(alpha_x0_kernel, dim3(pl.P), dim3(256), 0, s, nullptr, pl.ns_iters == 0 ? t.stop : nullptr, 0,
-                        wk.w, wk.x, mp);
+                          wk.w, wk.pm, pl.m, mp, pl.scale, pl.eps);
+  // The column-sum partials go to the product buffer, which the steps only
+  // write after alpha_x0 has read them.
+  hipExtLaunchKernelGGL(alpha_x0_kernel, dim3(pl.P, 16), dim3(256), 0, s, nullptr, pl.ns_iters == 0 ? t.stop : nullptr,
+                        0, wk.w, wk.pm, wk.x, mp);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int kext = (pl.m + 31) & ~31;

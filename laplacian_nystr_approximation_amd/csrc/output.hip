@@ -44,7 +44,7 @@ __device__ __forceinline__ uint32_t lane_mask(bool ok) {
 __device__ __forceinline__ float masked(float v, uint32_t mk) { return __uint_as_float(__float_as_uint(v) & mk); }
 
 template <int D, bool FUSED_Y>
-__global__ __launch_bounds__(256) void output_kernel(const float* __restrict__ ct, int ldc,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void output_kernel(const float* __restrict__ ct, int ldc,
                                                      const __bf16* __restrict__ yt, const float* __restrict__ y,
                                                      const float* __restrict__ mu, const float* __restrict__ rs,
                                                      float* __restrict__ out, int N, int m) {

@@ -6,5 +6,6 @@ from .lapnys_oracle import (  # noqa: F401
     laplacian_kernel,
     newton_schulz_inverse,
     pool_landmarks,
+    refine_inverse,
     whiten_columns,
 )

@@ -95,6 +95,21 @@ def newton_schulz_inverse(w, iters):
     return x
 
 
+def refine_inverse(w, x):
+    """One residual-correction step applied to an approximate inverse X of W.
+
+    An extension beyond the pages' fixed-count iteration (EN section 2.C.2
+    fixes the step count and uses matrix products only): R = I - W X, then
+    X' = X + X R.  Algebraically I - W X' = R - W X R = R - (I - R) R = R^2,
+    so one step squares the residual.  The oracle forms it in float64 like
+    everything else.
+    """
+    w = np.asarray(w, dtype=np.float64)
+    x = np.asarray(x, dtype=np.float64)
+    r = np.eye(w.shape[0]) - w @ x
+    return x + x @ r
+
+
 def whiten_columns(c):
     """Diagonal whitening of the query-side similarity vectors.
 
@@ -117,7 +132,7 @@ def whiten_columns(c):
     return z, mu, sigma
 
 
-def attention_problem(q, k, v, *, grid_h, grid_w, pool, lam, eps, ns_iters, whiten=True):
+def attention_problem(q, k, v, *, grid_h, grid_w, pool, lam, eps, ns_iters, whiten=True, refine=False):
     """Forward of one (batch, head) problem; returns every intermediate.
 
     Steps, in the method's order:
@@ -125,6 +140,7 @@ def attention_problem(q, k, v, *, grid_h, grid_w, pool, lam, eps, ns_iters, whit
       C = k(Q, K~)  [N x m],  B = k(K~, K)  [m x N]      (EN 2.A, 2.C.1)
       W = k(K~, K~) + eps I  [m x m]                     (EN 2.C.2)
       X = Newton-Schulz inverse of W                    (EN 2.C.2)
+          (refine: one residual correction afterwards, refine_inverse)
       Z = whitened C (or C itself when whitening is off) (EN 2.B)
       O = Z (X (B V)), evaluated right to left so the cost is linear in N.
     Reading taken for the Nystrom form: the ZH page (section 2.2) writes the
@@ -142,6 +158,8 @@ def attention_problem(q, k, v, *, grid_h, grid_w, pool, lam, eps, ns_iters, whit
     b = laplacian_kernel(kt, k, lam)
     w = laplacian_kernel(kt, kt, lam) + eps * np.eye(m)
     x = newton_schulz_inverse(w, ns_iters)
+    if refine:
+        x = refine_inverse(w, x)
     if whiten:
         z, mu, sigma = whiten_columns(c)
     else:
@@ -153,7 +171,7 @@ def attention_problem(q, k, v, *, grid_h, grid_w, pool, lam, eps, ns_iters, whit
             "mu": mu, "sigma": sigma, "BV": bv, "Y": y, "O": o}
 
 
-def forward(q, k, v, *, grid_h, grid_w, pool, lam, eps, ns_iters, whiten=True, problems=None):
+def forward(q, k, v, *, grid_h, grid_w, pool, lam, eps, ns_iters, whiten=True, problems=None, refine=False):
     """Forward over [B, H, N, d] inputs; every (b, h) problem is independent.
 
     ``problems`` optionally lists the (b, h) pairs to compute (a sample of a large
@@ -165,7 +183,7 @@ def forward(q, k, v, *, grid_h, grid_w, pool, lam, eps, ns_iters, whiten=True, p
     bsz, heads = q.shape[0], q.shape[1]
     pairs = list(problems) if problems is not None else [(b, h) for b in range(bsz) for h in range(heads)]
     outs = [attention_problem(q[b, h], k[b, h], v[b, h], grid_h=grid_h, grid_w=grid_w, pool=pool,
-                              lam=lam, eps=eps, ns_iters=ns_iters, whiten=whiten)
+                              lam=lam, eps=eps, ns_iters=ns_iters, whiten=whiten, refine=refine)
             for (b, h) in pairs]
     res = {key: np.stack([o[key] for o in outs]) for key in outs[0]}
     if problems is None:

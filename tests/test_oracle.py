@@ -243,10 +243,28 @@ def pin_forward_layout(orc):
     assert np.array_equal(samp["O"][0], one["O"])
 
 
+def pin_refine_squares_residual(orc):
+    # One correction step X' = X + X R, R = I - W X, leaves I - W X' = R^2
+    # exactly in exact arithmetic; in float64 to rounding.  The start is a
+    # short Newton-Schulz run, so R is far from zero.
+    rng = _rng(12)
+    lm = _heavy(rng, (30, 6))
+    w = orc.laplacian_kernel(lm, lm, 4.0) + 1e-3 * np.eye(30)
+    x = orc.newton_schulz_inverse(w, 17)
+    r = np.eye(30) - w @ x
+    assert 1e-3 < np.abs(r).max() < 0.5
+    x2 = orc.refine_inverse(w, x)
+    r2 = np.eye(30) - w @ x2
+    assert np.abs(r2 - r @ r).max() <= 1e-12
+    # and it moves X towards the inverse by the same factor
+    inv = np.linalg.inv(w)
+    assert np.abs(x2 - inv).max() <= 1.01 * np.abs(r @ r).max() * np.abs(inv).sum(axis=1).max() + 1e-12
+
+
 PINS = [pin_kernel_hand, pin_kernel_invariants, pin_pool_ramp, pin_pool_special_cases,
         pin_pool_fixed_order, pin_ns_closed_form, pin_ns_lu, pin_ns_residual_squares,
         pin_whiten_moments, pin_nystrom_pool1, pin_single_landmark, pin_metamorphic,
-        pin_forward_layout]
+        pin_forward_layout, pin_refine_squares_residual]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -352,8 +370,20 @@ def _whiten_rows(c):
     return (c - mu) / sigma, mu[:, 0], sigma[:, 0]
 
 
+def _refine_plus_residual(w, x):
+    w = np.asarray(w, float)
+    x = np.asarray(x, float)
+    return x + x @ (np.eye(len(w)) + w @ x)
+
+
+def _refine_minus(w, x):
+    w = np.asarray(w, float)
+    x = np.asarray(x, float)
+    return x - x @ (np.eye(len(w)) - w @ x)
+
+
 def _attention_variant(variant):
-    def f(q, k, v, *, grid_h, grid_w, pool, lam, eps, ns_iters, whiten=True):
+    def f(q, k, v, *, grid_h, grid_w, pool, lam, eps, ns_iters, whiten=True, refine=False):
         kt = O.pool_landmarks(k, grid_h, grid_w, pool)
         m = kt.shape[0]
         c = O.laplacian_kernel(q, kt, lam)
@@ -362,6 +392,8 @@ def _attention_variant(variant):
         x = O.newton_schulz_inverse(w, ns_iters)
         if variant == "skip_inverse":
             x = np.eye(m)
+        if refine:
+            x = O.refine_inverse(w, x)
         if whiten:
             z, mu, sigma = O.whiten_columns(c)
         else:
@@ -391,6 +423,8 @@ MUTANTS = {
     "key_factor_from_queries": ("attention_problem", _attention_variant("b_from_q")),
     "no_diagonal_shift": ("attention_problem", _attention_variant("no_eps")),
     "inverse_skipped": ("attention_problem", _attention_variant("skip_inverse")),
+    "refine_residual_sign": ("refine_inverse", _refine_plus_residual),
+    "refine_correction_sign": ("refine_inverse", _refine_minus),
 }
 
 

@@ -137,7 +137,10 @@ def stage_rooflines(w, stage_ms):
     return out
 
 
-SWEEP = ("sweep_64x64_bf16", "sweep_128x128_bf16", "long_256x256_bf16", HEADLINE)
+# (workload, LAPNYS_NS_REFINE): the refined lines price the float64-residual
+# correction of the Newton-Schulz result.
+SWEEP = (("sweep_64x64_bf16", False), ("sweep_128x128_bf16", False), ("long_256x256_bf16", False),
+         ("long_256x256_bf16", True), (HEADLINE, False), (HEADLINE, True))
 
 
 def sweep_main(args):
@@ -147,15 +150,19 @@ def sweep_main(args):
     times (events around one forward on the stream); warm = back to back, cold
     = a 512 MiB buffer written between calls so the last-level cache holds
     none of the inputs; and the peak device memory of inputs, workspace and
-    output (the _ws form allocates nothing itself).  One JSON line each."""
+    output (the _ws form allocates nothing itself); and the median device time
+    of the solver stage (its own kernels' dispatch timestamps, warm).  One JSON
+    line each."""
+    import dataclasses
+
     import torch
     import laplacian_nystr_approximation_amd.lapnys as L
     from lapnys_inputs import make_inputs
 
     dev = torch.device("cuda:0")
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    for name in SWEEP:
-        w = WORKLOADS[name]
+    for name, refine in SWEEP:
+        w = dataclasses.replace(WORKLOADS[name], refine=refine)
         x = make_inputs(w)
         torch.cuda.synchronize()
         torch.cuda.reset_peak_memory_stats(dev)
@@ -188,9 +195,18 @@ def sweep_main(args):
                 ts.append(e0.elapsed_time(e1))
             times[mode] = {"median_ms": float(np.median(ts)), "p10_ms": float(np.percentile(ts, 10)),
                            "p90_ms": float(np.percentile(ts, 90))}
+        ns = 2 * L.LAPNYS_STAGE_NS
+        evs = L.HipEvents(2 * reps)
+        for i in range(reps):
+            slots = [None] * (2 * L.LAPNYS_NUM_STAGES)
+            slots[ns], slots[ns + 1] = evs.handles[2 * i], evs.handles[2 * i + 1]
+            L.lapnys_forward_profiled(q, k, v, out, params, ws, slots, stream)
         torch.cuda.synchronize()
+        ns_ms = float(np.median([evs.elapsed_ms(2 * i, 2 * i + 1) for i in range(reps)]))
+        evs.close()
         peak = torch.cuda.max_memory_allocated(dev) - base
-        print(json.dumps({"workload": name, "N": w.N, "m": w.m, "P": w.P, "d": w.d, "ns_iters": w.ns_iters,
+        print(json.dumps({"workload": name, "refine": refine, "N": w.N, "m": w.m, "P": w.P, "d": w.d,
+                          "ns_iters": w.ns_iters, "ns_stage_ms": ns_ms,
                           "tokens_per_s_warm": w.P * w.N / (times["warm"]["median_ms"] * 1e-3),
                           "warm": times["warm"], "cold": times["cold"], "peak_device_bytes": int(peak),
                           "workspace_bytes": int(ws.numel())}), flush=True)

@@ -51,8 +51,20 @@ extern "C" {
 /* Storage type of q, k and v. */
 typedef enum { LAPNYS_F32 = 0, LAPNYS_BF16 = 1 } lapnys_dtype;
 
-/* flags: apply the diagonal whitening to C (EN 2.B).  Without it Z = C. */
-enum { LAPNYS_WHITEN = 1u };
+/* flags.
+ * LAPNYS_WHITEN: apply the diagonal whitening to C (EN 2.B).  Without it
+ *   Z = C.
+ * LAPNYS_NS_REFINE: after the ns_iters Newton-Schulz steps (EN 2.C.2), one
+ *   correction X <- X + X R with the residual R = I - W X accumulated in
+ *   float64 from the float32 W and X.  This is an extension beyond the pages'
+ *   fixed-count iteration, not part of the method: exactly, the step leaves
+ *   the residual R^2 (it is the Newton-Schulz update X (2I - W X) with W X
+ *   formed more accurately), so a large, poorly conditioned W whose float32
+ *   iterate stops short of the wanted residual (for example 256 landmarks of
+ *   a 256 x 256 grid, condition number near 1.4e3) reaches the float32
+ *   representation floor of its inverse.  Off, the result is the pages'
+ *   fixed-count X. */
+enum { LAPNYS_WHITEN = 1u, LAPNYS_NS_REFINE = 2u };
 
 /* Status codes. */
 enum {
@@ -82,7 +94,7 @@ typedef struct {
   float eps;             /* >= 0 */
   int32_t ns_iters;      /* Newton-Schulz steps, >= 0 */
   int32_t dtype;         /* lapnys_dtype */
-  uint32_t flags;        /* LAPNYS_WHITEN or 0 */
+  uint32_t flags;        /* LAPNYS_WHITEN | LAPNYS_NS_REFINE, or 0 */
 } lapnys_params;
 
 /* Optional device buffers for the intermediates of one call (debug form).
@@ -105,7 +117,8 @@ typedef struct {
 /* Stage indices for lapnys_forward_profiled. */
 enum {
   LAPNYS_STAGE_POOL = 0,     /* landmark average pooling */
-  LAPNYS_STAGE_NS = 1,       /* W build, scaling, Newton-Schulz */
+  LAPNYS_STAGE_NS = 1,       /* W build, scaling, Newton-Schulz (and the
+                                correction of LAPNYS_NS_REFINE) */
   LAPNYS_STAGE_KERNEL = 2,   /* fused L1 + exp: C, column statistics, B V */
   LAPNYS_STAGE_FINALIZE = 3, /* statistics and B V reductions, Y = X (B V) */
   LAPNYS_STAGE_OUTPUT = 4,   /* O = whiten(C) Y */

@@ -51,7 +51,7 @@ int validate(const lapnys_params* p) {
   if (!(isfinite(p->lambda) && p->lambda > 0.f)) return LAPNYS_ERR_INVALID_ARG;
   if (!(isfinite(p->eps) && p->eps >= 0.f)) return LAPNYS_ERR_INVALID_ARG;
   if (p->ns_iters < 0) return LAPNYS_ERR_INVALID_ARG;
-  if (p->flags & ~(uint32_t)LAPNYS_WHITEN) return LAPNYS_ERR_INVALID_ARG;
+  if (p->flags & ~(uint32_t)(LAPNYS_WHITEN | LAPNYS_NS_REFINE)) return LAPNYS_ERR_INVALID_ARG;
   if (p->dtype != LAPNYS_F32 && p->dtype != LAPNYS_BF16) return LAPNYS_ERR_UNSUPPORTED;
   if ((int64_t)p->grid_h * p->grid_w != (int64_t)p->N) return LAPNYS_ERR_SHAPE;
   if (p->grid_h % p->pool || p->grid_w % p->pool) return LAPNYS_ERR_SHAPE;
@@ -78,6 +78,7 @@ int make_plan(const lapnys_params* p, Plan* pl) {
   P.dtype = p->dtype;
   P.whiten = (p->flags & LAPNYS_WHITEN) != 0;
   P.ns_iters = p->ns_iters;
+  P.refine = (p->flags & LAPNYS_NS_REFINE) != 0;
   // exp(-s / lambda) = exp2(s * scale)
   P.scale = (float)(-1.4426950408889634074 / (double)p->lambda);
   P.eps = p->eps;
@@ -103,8 +104,11 @@ int make_plan(const lapnys_params* p, Plan* pl) {
   P.off_kt = take(Pn * P.m * P.d * f);
   P.off_w = take(Pn * P.mp * P.mp * f);
   P.off_x = take(Pn * P.mp * P.mp * f);
-  P.off_x2 = take(P.fused_ns ? 0 : Pn * P.mp * P.mp * f);
-  P.off_pm = take(P.fused_ns ? 0 : Pn * P.mp * P.mp * f);
+  // The second iterate and the product buffer serve the tiled solver's
+  // steps, and the correction of LAPNYS_NS_REFINE at any size.
+  const bool tiled = !P.fused_ns || P.refine;
+  P.off_x2 = take(tiled ? Pn * P.mp * P.mp * f : 0);
+  P.off_pm = take(tiled ? Pn * P.mp * P.mp * f : 0);
   P.off_ct = take(Pn * P.m * (size_t)P.ldc * f);
   P.off_stats = take(Pn * P.ntiles * P.m * 2 * f);
   P.off_bvpart = take(Pn * P.groups * P.m * P.d * f);
@@ -212,6 +216,7 @@ int run(const Plan& pl, const void* q, const void* k, const void* v, float* out,
     if (!mark(2 * LAPNYS_STAGE_NS)) return LAPNYS_ERR_HIP;
     if (!ok(lapnys::launch_l1exp(pl, q, k, v, W, s, span(LAPNYS_STAGE_KERNEL)), "kernel-matrix launch"))
       return LAPNYS_ERR_HIP;
+    if (pl.refine && !ok(lapnys::launch_refine(pl, W, s), "refinement launch")) return LAPNYS_ERR_HIP;
     if (!mark(2 * LAPNYS_STAGE_NS + 1)) return LAPNYS_ERR_HIP;
     if (!ok(lapnys::launch_reduce(pl, W, s, fin), "reduce launch")) return LAPNYS_ERR_HIP;
     if (!ok(lapnys::launch_output(pl, W, out, s, span(LAPNYS_STAGE_OUTPUT)), "output launch")) return LAPNYS_ERR_HIP;

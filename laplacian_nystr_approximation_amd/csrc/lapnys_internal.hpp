@@ -83,6 +83,7 @@ struct Plan {
   int dtype;        // lapnys_dtype
   bool whiten;
   int ns_iters;
+  bool refine;      // one float64-residual correction after the steps
   float scale;      // -log2(e) / lambda, so k = exp2(scale * L1)
   float eps;
   int mp;           // padded Newton-Schulz size (64, or m rounded up to 64)
@@ -128,6 +129,10 @@ struct Span {
 hipError_t launch_pool(const Plan& pl, const void* k, const Work& w, hipStream_t s, Span t = {});
 // The solver for 64 < m <= 256 (separate launches).
 hipError_t launch_ns(const Plan& pl, Work& w, hipStream_t s, Span t = {});
+// The correction X <- X + X (I - W X) of w.x_final (residual in float64),
+// into the other iterate buffer; updates w.x_final.  Any m; the stop event,
+// if given, is recorded by its last kernel.
+hipError_t launch_refine(const Plan& pl, Work& w, hipStream_t s, hipEvent_t stop = nullptr);
 // The kernel-matrix stage; for m <= 64 the same launch also runs the
 // Newton-Schulz solver (and sets w.x_final).
 hipError_t launch_l1exp(const Plan& pl, const void* q, const void* k, const void* v, Work& w,

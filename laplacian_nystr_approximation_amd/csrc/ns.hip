@@ -16,6 +16,12 @@
 //    the iterates live in the workspace (L2-resident) and each product is one
 //    batched launch of 64 x 64 output tiles, two launches per step.  The same
 //    tile kernel also forms Y = X (B V) for these sizes.
+//
+// Optional correction (LAPNYS_NS_REFINE, beyond the pages' fixed-count
+// iteration), for either schedule: R = I - W X with float64 accumulation, then
+// X <- X + X R on the tile kernel.  Exactly, the new residual is R^2; the
+// float64 residual lets it reach the float32 representation floor of W^-1
+// where the float32 products of the steps themselves stall above it.
 #include "lapnys_internal.hpp"
 
 namespace lapnys {
@@ -115,7 +121,7 @@ __global__ __launch_bounds__(256) void alpha_x0_kernel(const float* __restrict__
 }
 
 // One 64 x 64 output tile (blockIdx.x, blockIdx.y) of problem blockIdx.z:
-//   C = A B (mode 0)  or  C = A (2I - B) (mode 1),
+//   C = A B (mode 0),  C = A (2I - B) (mode 1)  or  C = A + A B (mode 2),
 // reduction over [0, kext) (a multiple of 32), 32 at a time.  A stage's A
 // (64 x 32) and B (32 x 64) values are loaded into registers, two 16-byte
 // loads of each per lane, one stage ahead, and stored to the LDS buffer not
@@ -164,7 +170,7 @@ __global__ __launch_bounds__(256) void gemm64_kernel(const float* __restrict__ A
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         if (!(gr < brows && gc + u < bcols)) bv[u] = 0.f;
-        if (mode) bv[u] = (gr == gc + u ? 2.f : 0.f) - bv[u];
+        if (mode == 1) bv[u] = (gr == gc + u ? 2.f : 0.f) - bv[u];
       }
       *reinterpret_cast<float4*>(&bs[buf][br * 64 + bc4]) = make_float4(bv[0], bv[1], bv[2], bv[3]);
     }
@@ -193,7 +199,60 @@ __global__ __launch_bounds__(256) void gemm64_kernel(const float* __restrict__ A
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int rr = r0 + 32 * wr + 8 * (r >> 2) + 4 * lk + (r & 3);
-    if (rr < crows && cc < ccols) Cp[(size_t)rr * ldc + cc] = acc[r];
+    if (rr < crows && cc < ccols) Cp[(size_t)rr * ldc + cc] = mode == 2 ? Ap[(size_t)rr * lda + cc] + acc[r] : acc[r];
+  }
+}
+
+// The residual R = I - W X of one 32 x 32 tile (blockIdx.x, blockIdx.y) of
+// problem blockIdx.z, accumulated in float64: every product of two float32
+// values is exact in float64, and the sums of at most 256 of them carry
+// about 2^-45 relative error, so R keeps its leading digits even where
+// W X agrees with I to float32 precision (there a float32 sum would return
+// mostly rounding noise).  The identity is restricted to [0, m); W's rows and
+// X's columns past m are zero, so R is zero outside the m x m block.  The
+// reduction runs over [0, kext), 32 at a time, in ascending order.  Each
+// stage's operands are widened to float64 once, as they are staged in LDS (W
+// transposed); lane (ty, tx) owns rows 2 ty + [0, 2) and columns 2 tx + [0, 2)
+// and reads both operand pairs as 16-byte loads.  Small tiles give the launch
+// 16 (mp / 64)^2 workgroups per problem, enough to cover the chip at m = 256.
+__global__ __launch_bounds__(256) void residual_kernel(const float* __restrict__ W, const float* __restrict__ X,
+                                                       float* __restrict__ R, int m, int mp, int kext) {
+  constexpr int kS = 34;
+  __shared__ __align__(16) double at[32 * kS];  // at[k][row] = W[r0 + row][kc + k]
+  __shared__ __align__(16) double bt[32 * kS];  // bt[k][col] = X[kc + k][c0 + col]
+  const int p = blockIdx.z, r0 = blockIdx.x * 32, c0 = blockIdx.y * 32;
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int sr = tid >> 3, s4 = 4 * (tid & 7);  // staging: row (or k) and 4 consecutive columns
+  const size_t sq = (size_t)mp * mp;
+  const float* Wp = W + p * sq;
+  const float* Xp = X + p * sq;
+  double acc[2][2] = {{0.0, 0.0}, {0.0, 0.0}};
+  for (int kc = 0; kc < kext; kc += 32) {
+    const f32x4 wa = *reinterpret_cast<const f32x4*>(Wp + (size_t)(r0 + sr) * mp + kc + s4);
+    const f32x4 xb = *reinterpret_cast<const f32x4*>(Xp + (size_t)(kc + sr) * mp + c0 + s4);
+    __syncthreads();  // the stage before has finished reading
+#pragma unroll
+    for (int u = 0; u < 4; ++u) at[(s4 + u) * kS + sr] = (double)wa[u];
+    *reinterpret_cast<double2*>(&bt[sr * kS + s4]) = make_double2(xb[0], xb[1]);
+    *reinterpret_cast<double2*>(&bt[sr * kS + s4 + 2]) = make_double2(xb[2], xb[3]);
+    __syncthreads();
+#pragma unroll 8
+    for (int k = 0; k < 32; ++k) {
+      const double2 a = *reinterpret_cast<const double2*>(&at[k * kS + 2 * ty]);
+      const double2 b = *reinterpret_cast<const double2*>(&bt[k * kS + 2 * tx]);
+      acc[0][0] = fma(a.x, b.x, acc[0][0]);
+      acc[0][1] = fma(a.x, b.y, acc[0][1]);
+      acc[1][0] = fma(a.y, b.x, acc[1][0]);
+      acc[1][1] = fma(a.y, b.y, acc[1][1]);
+    }
+  }
+  float* Rp = R + p * sq;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = r0 + 2 * ty + i, col = c0 + 2 * tx;
+    const double d0 = row == col && row < m ? 1.0 : 0.0;
+    const double d1 = row == col + 1 && row < m ? 1.0 : 0.0;
+    *reinterpret_cast<f32x2*>(Rp + (size_t)row * mp + col) = (f32x2){(float)(d0 - acc[i][0]), (float)(d1 - acc[i][1])};
   }
 }
 
@@ -221,8 +280,8 @@ hipError_t launch_ns(const Plan& pl, Work& wk, hipStream_t s, Span t) {
                           wk.w, wk.pm, pl.m, mp, pl.scale, pl.eps);
   // The column-sum partials go to the product buffer, which the steps only
   // write after alpha_x0 has read them.
-  hipExtLaunchKernelGGL(alpha_x0_kernel, dim3(pl.P, 16), dim3(256), 0, s, nullptr, pl.ns_iters == 0 ? t.stop : nullptr,
-                        0, wk.w, wk.pm, wk.x, mp);
+  hipExtLaunchKernelGGL(alpha_x0_kernel, dim3(pl.P, 16), dim3(256), 0, s, nullptr,
+                        pl.ns_iters == 0 && !pl.refine ? t.stop : nullptr, 0, wk.w, wk.pm, wk.x, mp);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int kext = (pl.m + 31) & ~31;
@@ -233,7 +292,8 @@ hipError_t launch_ns(const Plan& pl, Work& wk, hipStream_t s, Span t) {
   for (int it = 0; it < pl.ns_iters; ++it) {
     hipLaunchKernelGGL(gemm64_kernel, grid, dim3(256), 0, s, wk.w, mp, sq, xc, mp, sq, mp, mp, wk.pm, mp, sq, mp, mp,
                        kext, 0);
-    hipExtLaunchKernelGGL(gemm64_kernel, grid, dim3(256), 0, s, nullptr, it + 1 == pl.ns_iters ? t.stop : nullptr, 0,
+    hipExtLaunchKernelGGL(gemm64_kernel, grid, dim3(256), 0, s, nullptr,
+                          it + 1 == pl.ns_iters && !pl.refine ? t.stop : nullptr, 0,
                           xc, mp, sq, wk.pm, mp, sq, mp, mp, xn, mp, sq, mp, mp, kext, 1);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -242,6 +302,22 @@ hipError_t launch_ns(const Plan& pl, Work& wk, hipStream_t s, Span t) {
     xn = t;
   }
   wk.x_final = xc;
+  return pl.refine ? launch_refine(pl, wk, s, t.stop) : hipSuccess;
+}
+
+hipError_t launch_refine(const Plan& pl, Work& wk, hipStream_t s, hipEvent_t stop) {
+  const int mp = pl.mp;
+  const int kext = (pl.m + 31) & ~31;
+  const long long sq = (long long)mp * mp;
+  const dim3 grid(mp / 64, mp / 64, pl.P);
+  float* xc = wk.x_final;
+  float* xn = xc == wk.x ? wk.x2 : wk.x;
+  hipLaunchKernelGGL(residual_kernel, dim3(mp / 32, mp / 32, pl.P), dim3(256), 0, s, wk.w, xc, wk.pm, pl.m, mp, kext);
+  hipExtLaunchKernelGGL(gemm64_kernel, grid, dim3(256), 0, s, nullptr, stop, 0, xc, mp, sq, wk.pm, mp, sq, mp, mp,
+                        xn, mp, sq, mp, mp, kext, 2);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  wk.x_final = xn;
   return hipSuccess;
 }
 

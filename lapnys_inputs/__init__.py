@@ -40,6 +40,7 @@ class Workload:
     dtype: str = "f32"  # storage type of Q, K, V: "f32" or "bf16"
     whiten: bool = True
     seed_index: int = 0
+    refine: bool = False  # one float64-residual correction after the Newton-Schulz steps
 
     @property
     def N(self) -> int:

@@ -94,6 +94,18 @@ def test_unknown_flag_bits_rejected():
     assert L.library().lapnys_landmark_count(ctypes.byref(p)) == B.LAPNYS_ERR_INVALID_ARG
 
 
+def test_refine_flag_accepted_and_sized():
+    """LAPNYS_NS_REFINE is a known flag; with m <= 64 it adds the second
+    iterate and the residual buffer (two P x 64 x 64 float32 arrays)."""
+    plain, refined = _p(), _p(refine=True)
+    assert refined.flags == B.LAPNYS_WHITEN | B.LAPNYS_NS_REFINE
+    assert L.library().lapnys_landmark_count(ctypes.byref(refined)) == 49
+    grow = L.lapnys_workspace_size(refined) - L.lapnys_workspace_size(plain)
+    assert 2 * 6 * 64 * 64 * 4 <= grow <= 2 * 6 * 64 * 64 * 4 + 512
+    big = dict(grid_h=32, grid_w=32)  # m = 256: the tiled solver has both buffers already
+    assert L.lapnys_workspace_size(_p(refine=True, **big)) == L.lapnys_workspace_size(_p(**big))
+
+
 def test_buffer_checks_before_launch():
     p = _p()
     lib = L.library()

@@ -2,6 +2,7 @@
 same seeded inputs, stage by stage and end to end.  Run on an MI355X with
 ``pytest -m gpu``."""
 
+import dataclasses
 import sys
 
 import numpy as np
@@ -57,6 +58,42 @@ def test_long_sequence_parity(name):
     res_all = [np.linalg.norm(gpu["W"][p].astype(np.float64) @ gpu["X"][p].astype(np.float64) - np.eye(w.m))
                for p in range(w.P)]
     _say(f"[parity] {name}: O normwise {max(report['o_normwise']):.2e}, rel L2 {max(report['o_rel_l2']):.2e}, "
+         f"NS residual max over problems {max(res_all):.2e}")
+    if gate:
+        assert max(res_all) <= NS_RESIDUAL
+
+
+def _refine_cases():
+    long = WORKLOADS["long_256x256_bf16"]
+    return [
+        # m = 256, 24 steps: the plain float32 iteration ends near 1e-3
+        dataclasses.replace(long, name="long_256x256_f32_refine", dtype="f32", refine=True),
+        dataclasses.replace(WORKLOADS["stage1_56x56_f32"], name="stage1_56x56_f32_refine", refine=True),
+        Workload("m100_20x20_p2_d32_refine", B=1, H=2, grid_h=20, grid_w=20, d=32, pool=2, dtype="f32",
+                 seed_index=41, refine=True),
+        # one step, then the correction: far from converged, so only parity
+        Workload("ns1_12x12_m36_refine", B=1, H=2, grid_h=12, grid_w=12, d=64, pool=2, dtype="f32", ns_iters=1,
+                 seed_index=42, refine=True),
+    ]
+
+
+@pytest.mark.parametrize("w", _refine_cases(), ids=lambda w: w.name)
+def test_refined_solver(w):
+    """LAPNYS_NS_REFINE against the oracle's X + X (I - W X): the output to the
+    float32 bar, and every problem's residual, from the GPU's own W and X,
+    within the 1e-4 gate once the steps have converged that far."""
+    _say(f"[refine] {w.name} P={w.P} N={w.N} m={w.m} T={w.ns_iters}")
+    x = workload_inputs(w)
+    gpu = run_gpu(w, x)
+    sample = list(range(w.P)) if w.N * w.P <= 20000 else [0, w.P - 1]
+    ref = run_oracle(w, x, problems=sample)
+    gate = w.ns_iters >= 20
+    report = {}
+    for r, p in enumerate(sample):
+        check_problem(w, gpu, p, ref, r, check_ns=gate, report=report)
+    res_all = [np.linalg.norm(gpu["W"][p].astype(np.float64) @ gpu["X"][p].astype(np.float64) - np.eye(w.m))
+               for p in range(w.P)]
+    _say(f"[refine] {w.name}: O normwise {max(report['o_normwise']):.2e}, "
          f"NS residual max over problems {max(res_all):.2e}")
     if gate:
         assert max(res_all) <= NS_RESIDUAL

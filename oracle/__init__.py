@@ -3,6 +3,7 @@
 from .lapnys_oracle import (  # noqa: F401
     attention_problem,
     forward,
+    gaussian_kernel,
     laplacian_kernel,
     newton_schulz_inverse,
     pool_landmarks,

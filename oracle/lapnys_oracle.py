@@ -53,6 +53,26 @@ def laplacian_kernel(x, y, lam):
     return out
 
 
+def gaussian_kernel(x, y, lam):
+    """Gaussian kernel matrix: out[i, j] = exp(-sum_t (x[i, t] - y[j, t])^2 / lam).
+
+    The kernel the Laplacian one replaces: similarity decaying with the squared
+    L2 distance (EN page, section 1, first flaw, and section 2.A, which swaps
+    that distance for the L1 one inside the same exponential).  Reading taken:
+    the same scale lam divides the squared distance, with no factor 2 and no
+    1/d, so that the two kernels differ only in the distance.  The squared
+    differences are summed directly, not through |x|^2 + |y|^2 - 2 x.y.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    out = np.empty((x.shape[0], y.shape[0]), dtype=np.float64)
+    rows = max(1, _BLOCK_BYTES // max(1, 8 * y.shape[0] * y.shape[1]))
+    for s in range(0, x.shape[0], rows):
+        diff = x[s:s + rows, None, :] - y[None, :, :]
+        out[s:s + rows] = np.exp(-(diff * diff).sum(axis=2) / lam)
+    return out
+
+
 def pool_landmarks(k, grid_h, grid_w, pool):
     """Landmark keys: the average of K over each non-overlapping pool x pool window.
 
@@ -132,7 +152,8 @@ def whiten_columns(c):
     return z, mu, sigma
 
 
-def attention_problem(q, k, v, *, grid_h, grid_w, pool, lam, eps, ns_iters, whiten=True, refine=False):
+def attention_problem(q, k, v, *, grid_h, grid_w, pool, lam, eps, ns_iters, whiten=True, refine=False,
+                      kernel="laplacian"):
     """Forward of one (batch, head) problem; returns every intermediate.
 
     Steps, in the method's order:
@@ -147,16 +168,20 @@ def attention_problem(q, k, v, *, grid_h, grid_w, pool, lam, eps, ns_iters, whit
     low-rank factorisation C W^+ C^T; for attention between queries and keys the
     key-side factor is B = k(K~, K), and W^+ = W^-1 because W + eps I is
     positive definite.  No row normalisation of the output is applied: the pages
-    mention none.
+    mention none.  ``kernel="gaussian"`` runs the same steps with gaussian_kernel
+    in place of laplacian_kernel for C, B and W (the pages' baseline kernel).
     """
+    if kernel not in ("laplacian", "gaussian"):
+        raise ValueError(f"unknown kernel {kernel!r}")
+    kfun = gaussian_kernel if kernel == "gaussian" else laplacian_kernel
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     kt = pool_landmarks(k, grid_h, grid_w, pool)
     m = kt.shape[0]
-    c = laplacian_kernel(q, kt, lam)
-    b = laplacian_kernel(kt, k, lam)
-    w = laplacian_kernel(kt, kt, lam) + eps * np.eye(m)
+    c = kfun(q, kt, lam)
+    b = kfun(kt, k, lam)
+    w = kfun(kt, kt, lam) + eps * np.eye(m)
     x = newton_schulz_inverse(w, ns_iters)
     if refine:
         x = refine_inverse(w, x)
@@ -171,7 +196,8 @@ def attention_problem(q, k, v, *, grid_h, grid_w, pool, lam, eps, ns_iters, whit
             "mu": mu, "sigma": sigma, "BV": bv, "Y": y, "O": o}
 
 
-def forward(q, k, v, *, grid_h, grid_w, pool, lam, eps, ns_iters, whiten=True, problems=None, refine=False):
+def forward(q, k, v, *, grid_h, grid_w, pool, lam, eps, ns_iters, whiten=True, problems=None, refine=False,
+            kernel="laplacian"):
     """Forward over [B, H, N, d] inputs; every (b, h) problem is independent.
 
     ``problems`` optionally lists the (b, h) pairs to compute (a sample of a large
@@ -183,7 +209,7 @@ def forward(q, k, v, *, grid_h, grid_w, pool, lam, eps, ns_iters, whiten=True, p
     bsz, heads = q.shape[0], q.shape[1]
     pairs = list(problems) if problems is not None else [(b, h) for b in range(bsz) for h in range(heads)]
     outs = [attention_problem(q[b, h], k[b, h], v[b, h], grid_h=grid_h, grid_w=grid_w, pool=pool,
-                              lam=lam, eps=eps, ns_iters=ns_iters, whiten=whiten, refine=refine)
+                              lam=lam, eps=eps, ns_iters=ns_iters, whiten=whiten, refine=refine, kernel=kernel)
             for (b, h) in pairs]
     res = {key: np.stack([o[key] for o in outs]) for key in outs[0]}
     if problems is None:

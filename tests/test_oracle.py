@@ -17,6 +17,7 @@ import pytest
 import oracle.lapnys_oracle as O
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "laplacian_kernel_hand.txt")
+GOLDEN_GAUSS = os.path.join(os.path.dirname(__file__), "golden", "gaussian_kernel_hand.txt")
 
 
 def _rng(seed=0):
@@ -27,9 +28,9 @@ def _heavy(rng, shape):
     return rng.standard_t(3.0, size=shape) * 0.25
 
 
-def _golden_rows():
+def _golden_rows(path=GOLDEN):
     rows = []
-    with open(GOLDEN) as f:
+    with open(path) as f:
         for line in f:
             line = line.strip()
             if not line or line.startswith("#"):
@@ -62,6 +63,54 @@ def pin_kernel_invariants(orc):
     assert np.linalg.eigvalsh(kxx).min() > 0
     y = _heavy(rng, (4, 6))
     assert np.array_equal(orc.laplacian_kernel(x, y, 4.0), orc.laplacian_kernel(y, x, 4.0).T)
+
+
+def pin_gaussian_hand(orc):
+    for x, y, lam, dist2 in _golden_rows(GOLDEN_GAUSS):
+        got = orc.gaussian_kernel(x[None, :], y[None, :], lam)[0, 0]
+        want = math.exp(-dist2 / lam)
+        assert abs(got - want) <= 1e-15 * want, (x, y, lam, got, want)
+
+
+def pin_gaussian_library_and_invariants(orc):
+    from scipy.spatial.distance import cdist
+    rng = _rng(12)
+    x, y = _heavy(rng, (11, 7)), _heavy(rng, (5, 7))
+    lam = 4.0
+    got = orc.gaussian_kernel(x, y, lam)
+    want = np.exp(-cdist(x, y, "sqeuclidean") / lam)
+    assert np.abs(got - want).max() <= 1e-14
+    # A product of one-dimensional Gaussians, one per feature.
+    prod = np.ones((11, 5))
+    for t in range(7):
+        prod *= np.exp(-((x[:, t, None] - y[None, :, t]) ** 2) / lam)
+    assert np.abs(got - prod).max() <= 1e-14
+    kxx = orc.gaussian_kernel(x, x, lam)
+    assert np.all(np.diag(kxx) == 1.0)
+    assert np.array_equal(kxx, kxx.T)
+    assert np.linalg.eigvalsh(kxx).min() > 0  # positive definite on distinct points
+    # Against the Laplacian kernel on the same points: where every per-feature
+    # difference is below 1 in magnitude, the squared distance is the smaller.
+    small = x[:3] * 0.1
+    assert np.all(orc.gaussian_kernel(small, small[::-1], lam) >= orc.laplacian_kernel(small, small[::-1], lam))
+
+
+def pin_gaussian_nystrom_pool1(orc):
+    # The pool = 1 identity holds for any kernel: with G = k(K, K) and an exact
+    # inverse, C (G + eps I)^-1 G = C - eps C (G + eps I)^-1, here for the
+    # Gaussian kernel through the whole forward, against brute force.
+    rng = _rng(13)
+    gh, gw, d, lam = 3, 4, 3, 4.0
+    q, k, v = (_heavy(rng, (gh * gw, d)) for _ in range(3))
+    g_qk = np.exp(-np.array([[sum((a - b) ** 2 for a, b in zip(qi, kj)) for kj in k] for qi in q]) / lam)
+    g_kk = np.exp(-np.array([[sum((a - b) ** 2 for a, b in zip(ki, kj)) for kj in k] for ki in k]) / lam)
+    for eps in [1e-1, 1e-2]:
+        res = orc.attention_problem(q, k, v, grid_h=gh, grid_w=gw, pool=1, lam=lam, eps=eps,
+                                    ns_iters=120, whiten=False, kernel="gaussian")
+        a = g_kk + eps * np.eye(gh * gw)
+        want = (g_qk - eps * g_qk @ np.linalg.solve(a, np.eye(gh * gw))) @ v
+        assert np.abs(res["O"] - want).max() <= 1e-9 * np.abs(want).max(), eps
+        assert np.abs(res["W"] - a).max() <= 1e-15
 
 
 def pin_pool_ramp(orc):
@@ -264,7 +313,8 @@ def pin_refine_squares_residual(orc):
 PINS = [pin_kernel_hand, pin_kernel_invariants, pin_pool_ramp, pin_pool_special_cases,
         pin_pool_fixed_order, pin_ns_closed_form, pin_ns_lu, pin_ns_residual_squares,
         pin_whiten_moments, pin_nystrom_pool1, pin_single_landmark, pin_metamorphic,
-        pin_forward_layout, pin_refine_squares_residual]
+        pin_forward_layout, pin_refine_squares_residual, pin_gaussian_hand,
+        pin_gaussian_library_and_invariants, pin_gaussian_nystrom_pool1]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -382,13 +432,31 @@ def _refine_minus(w, x):
     return x - x @ (np.eye(len(w)) - w @ x)
 
 
+def _g_unsquared(x, y, lam):
+    x, y = np.asarray(x, float), np.asarray(y, float)
+    return np.exp(-np.sqrt(((x[:, None, :] - y[None, :, :]) ** 2).sum(axis=2)) / lam)
+
+
+def _g_half_scale(x, y, lam):
+    x, y = np.asarray(x, float), np.asarray(y, float)
+    return np.exp(-((x[:, None, :] - y[None, :, :]) ** 2).sum(axis=2) / (2 * lam))
+
+
+def _g_expansion_sign(x, y, lam):
+    x, y = np.asarray(x, float), np.asarray(y, float)
+    d2 = (x * x).sum(1)[:, None] + (y * y).sum(1)[None, :] + 2 * x @ y.T
+    return np.exp(-d2 / lam)
+
+
 def _attention_variant(variant):
-    def f(q, k, v, *, grid_h, grid_w, pool, lam, eps, ns_iters, whiten=True, refine=False):
+    def f(q, k, v, *, grid_h, grid_w, pool, lam, eps, ns_iters, whiten=True, refine=False, kernel="laplacian"):
         kt = O.pool_landmarks(k, grid_h, grid_w, pool)
         m = kt.shape[0]
-        c = O.laplacian_kernel(q, kt, lam)
-        b = O.laplacian_kernel(kt, q if variant == "b_from_q" else k, lam)
-        w = O.laplacian_kernel(kt, kt, lam) + (0.0 if variant == "no_eps" else eps) * np.eye(m)
+        kf = O.gaussian_kernel if kernel == "gaussian" else O.laplacian_kernel
+        c = kf(q, kt, lam)
+        b = kf(kt, q if variant == "b_from_q" else k, lam)
+        wk = O.laplacian_kernel if variant == "gaussian_w_laplacian" else kf
+        w = wk(kt, kt, lam) + (0.0 if variant == "no_eps" else eps) * np.eye(m)
         x = O.newton_schulz_inverse(w, ns_iters)
         if variant == "skip_inverse":
             x = np.eye(m)
@@ -425,6 +493,10 @@ MUTANTS = {
     "inverse_skipped": ("attention_problem", _attention_variant("skip_inverse")),
     "refine_residual_sign": ("refine_inverse", _refine_plus_residual),
     "refine_correction_sign": ("refine_inverse", _refine_minus),
+    "gaussian_unsquared_distance": ("gaussian_kernel", _g_unsquared),
+    "gaussian_half_scale": ("gaussian_kernel", _g_half_scale),
+    "gaussian_expansion_sign": ("gaussian_kernel", _g_expansion_sign),
+    "gaussian_w_from_laplacian": ("attention_problem", _attention_variant("gaussian_w_laplacian")),
 }
 
 

@@ -43,6 +43,13 @@ KERNEL_SOURCES = ("l1exp.hip", "ns_small.hpp", "lapnys_internal.hpp", "lapnys_ap
 CUS, CLOCK_HZ = 256, 2.4e9
 VALU_F32_LANE_OPS = CUS * 128 * CLOCK_HZ
 HBM_BYTES_S = 8.0e12
+MFMA_F32_FLOPS = 157.3e12
+
+
+def gauss_stage_flops(w) -> float:
+    """Algorithmic fp32 MFMA flops of one launch of the Gaussian kernel-matrix
+    stage: the dot products of C (N x m) and B (m x N), d multiply-adds each."""
+    return 2.0 * (2.0 * w.N * w.m * w.d) * w.P
 
 
 def kernel_stage_ops(w) -> float:
@@ -97,7 +104,7 @@ def cpu_baseline(w, x, budget_s: float):
         b, h = divmod(p, w.H)
         oracle.attention_problem(x.qf[b, h], x.kf[b, h], x.vf[b, h], grid_h=w.grid_h, grid_w=w.grid_w,
                                  pool=w.pool, lam=float(np.float32(w.lam)), eps=float(np.float32(w.eps)),
-                                 ns_iters=w.ns_iters, whiten=w.whiten)
+                                 ns_iters=w.ns_iters, whiten=w.whiten, refine=w.refine, kernel=w.kernel)
         done += 1
         if time.perf_counter() - t0 > budget_s:
             break
@@ -221,6 +228,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
+    ap.add_argument("--kernel", default="laplacian", choices=("laplacian", "gaussian"),
+                    help="gaussian: the Gaussian-kernel variant of the same forward (LAPNYS_GAUSSIAN)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0: skip)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the bench line: warm and cold single-call times and peak memory over the "
@@ -236,6 +245,9 @@ def main(argv=None):
               file=sys.stderr)
         return 2
     w = WORKLOADS[args.workload]
+    if args.kernel != "laplacian":
+        import dataclasses
+        w = dataclasses.replace(w, kernel=args.kernel)
     x = make_inputs(w)
 
     # The CPU leg runs before the GPU is touched.
@@ -317,9 +329,22 @@ def main(argv=None):
         del src, dst
 
     tokens = w.P * w.N
-    achieved = kernel_stage_ops(w) / (kernel_ms * 1e-3) / 1e12
-    peak = VALU_F32_LANE_OPS / 1e12
-    metric = HEADLINE_METRIC if w.name == HEADLINE else f"attention tokens/s ({w.name})"
+    gauss = w.kernel == "gaussian"
+    if gauss:
+        roof = {"kernel": "gauss_kernel (squared L2 on fp32 MFMA + exp, C store, column statistics, B V)",
+                "bound": "mfma", "unit": "TFLOP/s", "peak": MFMA_F32_FLOPS / 1e12,
+                "achieved": gauss_stage_flops(w) / (kernel_ms * 1e-3) / 1e12, "traffic": None}
+    else:
+        roof = {"kernel": "l1exp_kernel (fused L1 + exp, C store, column statistics, B V)",
+                "bound": "alu", "unit": "TOP/s", "peak": VALU_F32_LANE_OPS / 1e12,
+                "achieved": kernel_stage_ops(w) / (kernel_ms * 1e-3) / 1e12, "traffic": measured_traffic(w.name)}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["kernel_ms"] = kernel_ms
+    roof["kernel_ms_samples"] = f"HIP events on every {EVERY}th timed step ({len(sampled)} of {K})"
+    if w.name == HEADLINE and not gauss:
+        metric = HEADLINE_METRIC
+    else:
+        metric = f"attention tokens/s ({w.name}{', Gaussian kernel' if gauss else ''})"
     line = {
         "metric": metric,
         "value": tokens / (ms_step * 1e-3),
@@ -335,11 +360,8 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "grid": [w.grid_h, w.grid_w], "N": w.N, "d": w.d,
                    "pool": w.pool, "m": w.m, "input_dtype": w.dtype, "lambda": w.lam, "eps": w.eps,
-                   "ns_iters": w.ns_iters, "whiten": w.whiten},
-        "roofline": {"kernel": "l1exp_kernel (fused L1 + exp, C store, column statistics, B V)",
-                     "bound": "alu", "achieved": achieved, "peak": peak, "unit": "TOP/s",
-                     "frac": achieved / peak, "traffic": measured_traffic(w.name), "kernel_ms": kernel_ms,
-                     "kernel_ms_samples": f"HIP events on every {EVERY}th timed step ({len(sampled)} of {K})"},
+                   "ns_iters": w.ns_iters, "whiten": w.whiten, "kernel": w.kernel},
+        "roofline": roof,
         "cpu_baseline": cpu,
         "stage_ms": stage_ms,
         "stage_roofline": stage_rooflines(w, stage_ms),

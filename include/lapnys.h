@@ -63,8 +63,15 @@ typedef enum { LAPNYS_F32 = 0, LAPNYS_BF16 = 1 } lapnys_dtype;
  *   iterate stops short of the wanted residual (for example 256 landmarks of
  *   a 256 x 256 grid, condition number near 1.4e3) reaches the float32
  *   representation floor of its inverse.  Off, the result is the pages'
- *   fixed-count X. */
-enum { LAPNYS_WHITEN = 1u, LAPNYS_NS_REFINE = 2u };
+ *   fixed-count X.
+ * LAPNYS_GAUSSIAN: the Gaussian kernel k(x, y) = exp(-||x - y||_2^2 / lambda)
+ *   in place of the Laplacian one, for C, B and W alike: the kernel the
+ *   pages' method replaces (EN section 1 and 2.A), read with the same scale
+ *   lambda.  Every other step is unchanged.  The squared distances of C and
+ *   B are formed as ||x||^2 + ||y||^2 - 2 x.y (the dot products on fp32
+ *   MFMA) and clamped at 0; W's are summed directly.  The solver then runs
+ *   as launches of its own, beside the kernel-matrix stage, at every m. */
+enum { LAPNYS_WHITEN = 1u, LAPNYS_NS_REFINE = 2u, LAPNYS_GAUSSIAN = 4u };
 
 /* Status codes. */
 enum {
@@ -94,7 +101,7 @@ typedef struct {
   float eps;             /* >= 0 */
   int32_t ns_iters;      /* Newton-Schulz steps, >= 0 */
   int32_t dtype;         /* lapnys_dtype */
-  uint32_t flags;        /* LAPNYS_WHITEN | LAPNYS_NS_REFINE, or 0 */
+  uint32_t flags;        /* LAPNYS_WHITEN | LAPNYS_NS_REFINE | LAPNYS_GAUSSIAN, or 0 */
 } lapnys_params;
 
 /* Optional device buffers for the intermediates of one call (debug form).
@@ -119,7 +126,7 @@ enum {
   LAPNYS_STAGE_POOL = 0,     /* landmark average pooling */
   LAPNYS_STAGE_NS = 1,       /* W build, scaling, Newton-Schulz (and the
                                 correction of LAPNYS_NS_REFINE) */
-  LAPNYS_STAGE_KERNEL = 2,   /* fused L1 + exp: C, column statistics, B V */
+  LAPNYS_STAGE_KERNEL = 2,   /* fused distance + exp: C, column statistics, B V */
   LAPNYS_STAGE_FINALIZE = 3, /* statistics and B V reductions, Y = X (B V) */
   LAPNYS_STAGE_OUTPUT = 4,   /* O = whiten(C) Y */
   LAPNYS_NUM_STAGES = 5

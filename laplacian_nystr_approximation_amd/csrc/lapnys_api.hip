@@ -51,7 +51,7 @@ int validate(const lapnys_params* p) {
   if (!(isfinite(p->lambda) && p->lambda > 0.f)) return LAPNYS_ERR_INVALID_ARG;
   if (!(isfinite(p->eps) && p->eps >= 0.f)) return LAPNYS_ERR_INVALID_ARG;
   if (p->ns_iters < 0) return LAPNYS_ERR_INVALID_ARG;
-  if (p->flags & ~(uint32_t)(LAPNYS_WHITEN | LAPNYS_NS_REFINE)) return LAPNYS_ERR_INVALID_ARG;
+  if (p->flags & ~(uint32_t)(LAPNYS_WHITEN | LAPNYS_NS_REFINE | LAPNYS_GAUSSIAN)) return LAPNYS_ERR_INVALID_ARG;
   if (p->dtype != LAPNYS_F32 && p->dtype != LAPNYS_BF16) return LAPNYS_ERR_UNSUPPORTED;
   if ((int64_t)p->grid_h * p->grid_w != (int64_t)p->N) return LAPNYS_ERR_SHAPE;
   if (p->grid_h % p->pool || p->grid_w % p->pool) return LAPNYS_ERR_SHAPE;
@@ -79,9 +79,13 @@ int make_plan(const lapnys_params* p, Plan* pl) {
   P.whiten = (p->flags & LAPNYS_WHITEN) != 0;
   P.ns_iters = p->ns_iters;
   P.refine = (p->flags & LAPNYS_NS_REFINE) != 0;
+  P.gaussian = (p->flags & LAPNYS_GAUSSIAN) != 0;
   // exp(-s / lambda) = exp2(s * scale)
   P.scale = (float)(-1.4426950408889634074 / (double)p->lambda);
   P.eps = p->eps;
+  // m <= 64: one workgroup per problem runs the steps (inside the
+  // kernel-matrix launch for the Laplacian form, a launch of its own beside
+  // it for the Gaussian form).
   P.fused_ns = P.m <= lapnys::kFusedNsMaxM;
   P.mp = P.fused_ns ? 64 : ((P.m + 63) / 64) * 64;
   P.tt = 256;
@@ -105,8 +109,9 @@ int make_plan(const lapnys_params* p, Plan* pl) {
   P.off_w = take(Pn * P.mp * P.mp * f);
   P.off_x = take(Pn * P.mp * P.mp * f);
   // The second iterate and the product buffer serve the tiled solver's
-  // steps, and the correction of LAPNYS_NS_REFINE at any size.
-  const bool tiled = !P.fused_ns || P.refine;
+  // steps and its column-sum partials, and the correction of LAPNYS_NS_REFINE
+  // at any size.
+  const bool tiled = !P.fused_ns || P.refine || P.gaussian;
   P.off_x2 = take(tiled ? Pn * P.mp * P.mp * f : 0);
   P.off_pm = take(tiled ? Pn * P.mp * P.mp * f : 0);
   P.off_ct = take(Pn * P.m * (size_t)P.ldc * f);
@@ -209,7 +214,7 @@ int run(const Plan& pl, const void* q, const void* k, const void* v, float* out,
   auto mark = [&](int idx) { return !ev || !ev[idx] || ok(hipEventRecord(ev[idx], s), "hipEventRecord"); };
   const lapnys::Span fin = span(LAPNYS_STAGE_FINALIZE);
 
-  if (pl.fused_ns) {
+  if (pl.fused_ns && !pl.gaussian) {
     // m <= 64: one stream; the solver runs inside the kernel-matrix launch,
     // and its stage events bracket that launch.
     if (!ok(lapnys::launch_pool(pl, k, W, s, span(LAPNYS_STAGE_POOL)), "pool launch")) return LAPNYS_ERR_HIP;
@@ -223,9 +228,10 @@ int run(const Plan& pl, const void* q, const void* k, const void* v, float* out,
     return LAPNYS_OK;
   }
 
-  // m > 64: the solver's launches run on a library-owned stream beside the
-  // kernel-matrix stage.  The pool stage runs on that stream ahead of them and
-  // the caller's stream waits for it, so the solver is dispatched first.
+  // m > 64, and the Gaussian form at every m: the solver's launches run on a
+  // library-owned stream beside the kernel-matrix stage.  The pool stage runs
+  // on that stream ahead of them and the caller's stream waits for it, so the
+  // solver is dispatched first.
   std::lock_guard<std::mutex> lock(g_ctx_mu);
   DeviceCtx* dc = nullptr;
   const int st = device_ctx(&dc);
@@ -239,11 +245,20 @@ int run(const Plan& pl, const void* q, const void* k, const void* v, float* out,
   if (!ok(lapnys::launch_ns(pl, W, side, span(LAPNYS_STAGE_NS)), "Newton-Schulz launch")) return LAPNYS_ERR_HIP;
   if (!ok(hipEventRecord(dc->join, side), "hipEventRecord")) return LAPNYS_ERR_HIP;
   if (!ok(hipStreamWaitEvent(s, dc->pooled, 0), "hipStreamWaitEvent")) return LAPNYS_ERR_HIP;
-  if (!ok(lapnys::launch_l1exp(pl, q, k, v, W, s, span(LAPNYS_STAGE_KERNEL)), "kernel-matrix launch"))
+  const lapnys::Span ks = span(LAPNYS_STAGE_KERNEL);
+  if (!ok(pl.gaussian ? lapnys::launch_gauss(pl, q, k, v, W, s, ks) : lapnys::launch_l1exp(pl, q, k, v, W, s, ks),
+          "kernel-matrix launch"))
     return LAPNYS_ERR_HIP;
-  if (!ok(lapnys::launch_reduce(pl, W, s, {fin.start, nullptr}), "reduce launch")) return LAPNYS_ERR_HIP;
-  if (!ok(hipStreamWaitEvent(s, dc->join, 0), "hipStreamWaitEvent")) return LAPNYS_ERR_HIP;
-  if (!ok(lapnys::launch_y(pl, W, s, {nullptr, fin.stop}), "Y launch")) return LAPNYS_ERR_HIP;
+  if (pl.fused_ns) {
+    // m <= 64 (Gaussian form): the reductions also form Y = X (B V), so they
+    // wait for the solver.
+    if (!ok(hipStreamWaitEvent(s, dc->join, 0), "hipStreamWaitEvent")) return LAPNYS_ERR_HIP;
+    if (!ok(lapnys::launch_reduce(pl, W, s, fin), "reduce launch")) return LAPNYS_ERR_HIP;
+  } else {
+    if (!ok(lapnys::launch_reduce(pl, W, s, {fin.start, nullptr}), "reduce launch")) return LAPNYS_ERR_HIP;
+    if (!ok(hipStreamWaitEvent(s, dc->join, 0), "hipStreamWaitEvent")) return LAPNYS_ERR_HIP;
+    if (!ok(lapnys::launch_y(pl, W, s, {nullptr, fin.stop}), "Y launch")) return LAPNYS_ERR_HIP;
+  }
   if (!ok(lapnys::launch_output(pl, W, out, s, span(LAPNYS_STAGE_OUTPUT)), "output launch")) return LAPNYS_ERR_HIP;
   return LAPNYS_OK;
 }

@@ -84,6 +84,7 @@ struct Plan {
   bool whiten;
   int ns_iters;
   bool refine;      // one float64-residual correction after the steps
+  bool gaussian;    // Gaussian kernel exp(-||x - y||_2^2 / lambda) instead of the Laplacian
   float scale;      // -log2(e) / lambda, so k = exp2(scale * L1)
   float eps;
   int mp;           // padded Newton-Schulz size (64, or m rounded up to 64)
@@ -127,7 +128,8 @@ struct Span {
 
 // Kernel launchers (each returns the hipError_t of its launches).
 hipError_t launch_pool(const Plan& pl, const void* k, const Work& w, hipStream_t s, Span t = {});
-// The solver for 64 < m <= 256 (separate launches).
+// The solver as launches of its own: 64 < m <= 256, and the Gaussian form at
+// every m (sets w.x_final).
 hipError_t launch_ns(const Plan& pl, Work& w, hipStream_t s, Span t = {});
 // The correction X <- X + X (I - W X) of w.x_final (residual in float64),
 // into the other iterate buffer; updates w.x_final.  Any m; the stop event,
@@ -137,6 +139,10 @@ hipError_t launch_refine(const Plan& pl, Work& w, hipStream_t s, hipEvent_t stop
 // Newton-Schulz solver (and sets w.x_final).
 hipError_t launch_l1exp(const Plan& pl, const void* q, const void* k, const void* v, Work& w,
                         hipStream_t s, Span t = {});
+// The Gaussian-kernel form of the kernel-matrix stage (pl.gaussian; the
+// solver then runs as launch_ns at every m).
+hipError_t launch_gauss(const Plan& pl, const void* q, const void* k, const void* v, Work& w, hipStream_t s,
+                        Span t = {});
 // Reductions after the kernel-matrix stage: B V, the whitening statistics,
 // and for m <= 64 also Y = X (B V) into w.yt.
 hipError_t launch_reduce(const Plan& pl, const Work& w, hipStream_t s, Span t = {});

@@ -30,12 +30,14 @@ namespace {
 
 // ---- 64 < m <= 256 -------------------------------------------------------
 
-// W rows [16*blockIdx.x, +16) of problem blockIdx.y; thread b owns column b
+// W rows [16*blockIdx.x, +16) of problem blockIdx.y (the Laplacian kernel,
+// or with GAUSS the Gaussian one, exp(-sum_t (x_t - y_t)^2 / lambda), its
+// squared differences summed directly); thread b owns column b
 // and also writes the sum of its 16 entries (all positive) to
 // part[p][blockIdx.x][b], the block's share of the column sums.  Loads read
 // clamped, in-bounds addresses (rows past m are masked where used), so every
 // load of the block issues before the first wait.
-template <int D>
+template <int D, bool GAUSS>
 __global__ __launch_bounds__(256) void wbuild_big_kernel(const float* __restrict__ kt, float* __restrict__ w,
                                                          float* __restrict__ part, int m, int mp, float scale,
                                                          float eps) {
@@ -64,8 +66,14 @@ __global__ __launch_bounds__(256) void wbuild_big_kernel(const float* __restrict
       float s0 = 0.f, s1 = 0.f;
 #pragma unroll
       for (int t = 0; t < D; t += 2) {
-        s0 += fabsf(kl[r * D + t] - xb[t]);
-        s1 += fabsf(kl[r * D + t + 1] - xb[t + 1]);
+        const float e0 = kl[r * D + t] - xb[t], e1 = kl[r * D + t + 1] - xb[t + 1];
+        if constexpr (GAUSS) {
+          s0 = fmaf(e0, e0, s0);
+          s1 = fmaf(e1, e1, s1);
+        } else {
+          s0 += fabsf(e0);
+          s1 += fabsf(e1);
+        }
       }
       val = exp2f((s0 + s1) * scale);
       if (a == b) val += eps;
@@ -256,6 +264,81 @@ __global__ __launch_bounds__(256) void residual_kernel(const float* __restrict__
   }
 }
 
+// m <= 64, Gaussian form: the steps X <- X (2I - W X) of one problem per
+// workgroup with W and the iterates in LDS (64 x 64, zero padded), from the W
+// and X0 of wbuild_big_kernel and alpha_x0_kernel, in the tiled steps' form:
+// T = 2I - W X in full, then X T, float32 products on fp32 MFMA 16x16x4
+// over k in [0, kext).  (The in-LDS schedule of the Laplacian form keeps X
+// exactly symmetric by mirroring one triangle of X (W X); for an iterate that
+// is still far from converged after the fixed step count, as a Gaussian W
+// often leaves it, the mirrored rounding errors cost about 6x in the output's
+// agreement with the float64 iteration, so this form keeps every entry.)
+// Wavefront w forms block row w of each product.  X is updated in place: the
+// second product of wavefront w reads only block row w of X (and all of T),
+// and writes that block row after its reads.  The final X overwrites X0.
+__global__ __launch_bounds__(256) void ns_plain_kernel(const float* __restrict__ w, float* __restrict__ x, int kext,
+                                                       int iters) {
+  constexpr int kS = 68;  // row stride: the A-operand column reads hit distinct banks
+  __shared__ __align__(16) float ws[64 * kS];
+  __shared__ __align__(16) float xs[64 * kS];
+  __shared__ __align__(16) float ts[64 * kS];
+  const int p = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int li = lane & 15, lk = lane >> 4;
+  const f32x4* w4 = reinterpret_cast<const f32x4*>(w + (size_t)p * 64 * 64);
+  f32x4* x4 = reinterpret_cast<f32x4*>(x + (size_t)p * 64 * 64);
+  f32x4 wv4[4], xv4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    wv4[i] = w4[tid + 256 * i];
+    xv4[i] = x4[tid + 256 * i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e4 = tid + 256 * i;
+    *reinterpret_cast<f32x4*>(&ws[(e4 >> 4) * kS + 4 * (e4 & 15)]) = wv4[i];
+    *reinterpret_cast<f32x4*>(&xs[(e4 >> 4) * kS + 4 * (e4 & 15)]) = xv4[i];
+  }
+  __syncthreads();
+  for (int it = 0; it < iters; ++it) {
+    f32x4 acc[4];
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) acc[bj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < kext; k0 += 4) {
+      const float a = ws[(16 * wv + li) * kS + k0 + lk];
+#pragma unroll
+      for (int bj = 0; bj < 4; ++bj)
+        acc[bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, xs[(k0 + lk) * kS + 16 * bj + li], acc[bj], 0, 0, 0);
+    }
+    // acc[bj][r] = (W X)[16 w + 4 lk + r][16 bj + li]
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * wv + 4 * lk + r, j = 16 * bj + li;
+        ts[i * kS + j] = (i == j ? 2.f : 0.f) - acc[bj][r];
+      }
+    __syncthreads();  // T complete; every wavefront is done reading X for W X
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) acc[bj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < kext; k0 += 4) {
+      const float a = xs[(16 * wv + li) * kS + k0 + lk];
+#pragma unroll
+      for (int bj = 0; bj < 4; ++bj)
+        acc[bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, ts[(k0 + lk) * kS + 16 * bj + li], acc[bj], 0, 0, 0);
+    }
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) xs[(16 * wv + 4 * lk + r) * kS + 16 * bj + li] = acc[bj][r];
+    __syncthreads();  // X_next complete; T free for the next step
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e4 = tid + 256 * i;
+    x4[e4] = *reinterpret_cast<const f32x4*>(&xs[(e4 >> 4) * kS + 4 * (e4 & 15)]);
+  }
+}
+
 __global__ __launch_bounds__(256) void extract_square_kernel(const float* __restrict__ src, int src_ld,
                                                              float* __restrict__ dst, int n, long long total) {
   const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -269,22 +352,30 @@ __global__ __launch_bounds__(256) void extract_square_kernel(const float* __rest
 }  // namespace
 
 hipError_t launch_ns(const Plan& pl, Work& wk, hipStream_t s, Span t) {
-  // m <= 64 runs inside the kernel-matrix launch (launch_l1exp).
-  if (pl.fused_ns) return hipErrorInvalidValue;
+  // m <= 64: the Laplacian form runs inside the kernel-matrix launch
+  // (launch_l1exp); the Gaussian form builds W and X0 here as for larger m and
+  // then runs its steps in one workgroup per problem.
+  if (pl.fused_ns && !pl.gaussian) return hipErrorInvalidValue;
   const int mp = pl.mp;
-  if (pl.d == 64)
-    hipExtLaunchKernelGGL(wbuild_big_kernel<64>, dim3(mp / 16, pl.P), dim3(256), 0, s, t.start, nullptr, 0, wk.kt,
-                          wk.w, wk.pm, pl.m, mp, pl.scale, pl.eps);
-  else
-    hipExtLaunchKernelGGL(wbuild_big_kernel<32>, dim3(mp / 16, pl.P), dim3(256), 0, s, t.start, nullptr, 0, wk.kt,
-                          wk.w, wk.pm, pl.m, mp, pl.scale, pl.eps);
+  auto wbuild = pl.d == 64 ? (pl.gaussian ? wbuild_big_kernel<64, true> : wbuild_big_kernel<64, false>)
+                           : (pl.gaussian ? wbuild_big_kernel<32, true> : wbuild_big_kernel<32, false>);
+  hipExtLaunchKernelGGL(wbuild, dim3(mp / 16, pl.P), dim3(256), 0, s, t.start, nullptr, 0, wk.kt, wk.w, wk.pm, pl.m,
+                        mp, pl.scale, pl.eps);
   // The column-sum partials go to the product buffer, which the steps only
   // write after alpha_x0 has read them.
   hipExtLaunchKernelGGL(alpha_x0_kernel, dim3(pl.P, 16), dim3(256), 0, s, nullptr,
-                        pl.ns_iters == 0 && !pl.refine ? t.stop : nullptr, 0, wk.w, wk.pm, wk.x, mp);
+                        pl.ns_iters == 0 && !pl.refine && !pl.fused_ns ? t.stop : nullptr, 0, wk.w, wk.pm, wk.x, mp);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int kext = (pl.m + 31) & ~31;
+  if (pl.fused_ns) {
+    hipExtLaunchKernelGGL(ns_plain_kernel, dim3(pl.P), dim3(256), 0, s, nullptr, pl.refine ? nullptr : t.stop, 0,
+                          wk.w, wk.x, kext, pl.ns_iters);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    wk.x_final = wk.x;
+    return pl.refine ? launch_refine(pl, wk, s, t.stop) : hipSuccess;
+  }
   const long long sq = (long long)mp * mp;
   const dim3 grid(mp / 64, mp / 64, pl.P);
   float* xc = wk.x;

@@ -41,6 +41,7 @@ class Workload:
     whiten: bool = True
     seed_index: int = 0
     refine: bool = False  # one float64-residual correction after the Newton-Schulz steps
+    kernel: str = "laplacian"  # or "gaussian"
 
     @property
     def N(self) -> int:

@@ -93,7 +93,8 @@ def run_oracle(w: Workload, x, problems=None):
     """Oracle results for the listed problem indices p = b*H + h (default all)."""
     pairs = None if problems is None else [divmod(p, w.H) for p in problems]
     r = oracle.forward(x.qf, x.kf, x.vf, grid_h=w.grid_h, grid_w=w.grid_w, pool=w.pool, lam=f32(w.lam),
-                       eps=f32(w.eps), ns_iters=w.ns_iters, whiten=w.whiten, refine=w.refine, problems=pairs)
+                       eps=f32(w.eps), ns_iters=w.ns_iters, whiten=w.whiten, refine=w.refine,
+                       kernel=w.kernel, problems=pairs)
     if problems is None:
         r = {k: (v.reshape((w.P,) + v.shape[2:]) if isinstance(v, np.ndarray) else v) for k, v in r.items()}
     return r

@@ -90,7 +90,7 @@ def test_invalid_params_rejected(kw, code):
 
 def test_unknown_flag_bits_rejected():
     p = _p()
-    p.flags = 6
+    p.flags = 8
     assert L.library().lapnys_landmark_count(ctypes.byref(p)) == B.LAPNYS_ERR_INVALID_ARG
 
 
@@ -104,6 +104,21 @@ def test_refine_flag_accepted_and_sized():
     assert 2 * 6 * 64 * 64 * 4 <= grow <= 2 * 6 * 64 * 64 * 4 + 512
     big = dict(grid_h=32, grid_w=32)  # m = 256: the tiled solver has both buffers already
     assert L.lapnys_workspace_size(_p(refine=True, **big)) == L.lapnys_workspace_size(_p(**big))
+
+
+def test_gaussian_flag_accepted():
+    """LAPNYS_GAUSSIAN is a known flag.  At m <= 64 its solver builds W and X0
+    as the tiled one does, so it adds that solver's two P x 64 x 64 buffers;
+    above 64 the workspace is the Laplacian form's."""
+    g = _p(kernel="gaussian")
+    assert g.flags == B.LAPNYS_WHITEN | B.LAPNYS_GAUSSIAN
+    assert L.library().lapnys_landmark_count(ctypes.byref(g)) == 49
+    grow = L.lapnys_workspace_size(g) - L.lapnys_workspace_size(_p())
+    assert 2 * 6 * 64 * 64 * 4 <= grow <= 2 * 6 * 64 * 64 * 4 + 512
+    big = dict(grid_h=32, grid_w=32)
+    assert L.lapnys_workspace_size(_p(kernel="gaussian", **big)) == L.lapnys_workspace_size(_p(**big))
+    with pytest.raises(ValueError):
+        _p(kernel="cosine")
 
 
 def test_buffer_checks_before_launch():

@@ -99,6 +99,43 @@ def test_refined_solver(w):
         assert max(res_all) <= NS_RESIDUAL
 
 
+def _gaussian_cases():
+    base = dict(B=1, H=2, lam=4.0, eps=1e-3, ns_iters=20, seed_index=50, kernel="gaussian")
+    g = lambda name: dataclasses.replace(WORKLOADS[name], name=name + "_gauss", kernel="gaussian")
+    return [
+        g("tiny_f32"), g("stage1_56x56_f32"), g("stage1_56x56_bf16"), g("stage3_14x14_bf16"),
+        Workload("gauss_ragged_18x14_p2", grid_h=18, grid_w=14, d=64, pool=2, dtype="f32", **base),
+        Workload("gauss_ragged_10x30_p5_d32", grid_h=10, grid_w=30, d=32, pool=5, dtype="bf16", **base),
+        Workload("gauss_m81_18x18_p2", grid_h=18, grid_w=18, d=64, pool=2, dtype="f32", **base),
+        Workload("gauss_tail_22x12_p2_m66", grid_h=22, grid_w=12, d=64, pool=2, dtype="bf16", **base),
+        Workload("gauss_m100_20x20_p2_d32", grid_h=20, grid_w=20, d=32, pool=2, dtype="f32", **base),
+        Workload("gauss_single_landmark_6x6", grid_h=6, grid_w=6, d=64, pool=6, dtype="f32", **base),
+        g("long_256x256_bf16"),
+    ]
+
+
+@pytest.mark.parametrize("w", _gaussian_cases(), ids=lambda w: w.name)
+def test_gaussian_parity(w):
+    """LAPNYS_GAUSSIAN against the oracle's Gaussian-kernel forward.  The
+    residual gate applies where the float64 iteration itself reaches 1e-5 in
+    the given steps (a Gaussian W on pooled landmarks can be far worse
+    conditioned than the Laplacian one)."""
+    _say(f"[gauss] {w.name} P={w.P} N={w.N} m={w.m} d={w.d} {w.dtype} T={w.ns_iters}")
+    x = workload_inputs(w)
+    gpu = run_gpu(w, x)
+    sample = list(range(w.P)) if w.N * w.P <= 120000 else [0, w.P - 1]
+    ref = run_oracle(w, x, problems=sample)
+    report = {}
+    for r, p in enumerate(sample):
+        own = np.linalg.norm(ref["W"][r] @ ref["X"][r] - np.eye(w.m))
+        check_problem(w, gpu, p, ref, r, check_ns=own <= 1e-5, report=report)
+        if own > 1e-5 and w.dtype == "f32":
+            nw, _ = o_errors(gpu["O"][p], ref["O"][r])
+            assert nw <= O_NORMWISE_F32
+    _say(f"[gauss] {w.name}: O normwise {max(report['o_normwise']):.2e}, rel L2 {max(report['o_rel_l2']):.2e}, "
+         f"NS residual {max(report['ns_residual']):.2e}")
+
+
 def _edge_cases():
     base = dict(B=1, H=2, lam=4.0, eps=1e-3, ns_iters=20, seed_index=40)
     cases = [

@@ -222,6 +222,37 @@ def sweep_main(args):
     return 0
 
 
+def kernel_value_comparison(w, q, k, v, dev):
+    """Both kernels' C = k(Q, K~) on the same inputs, from the GPU's own
+    intermediates (the debug form): quantiles of all entries, the share below
+    1e-6, and per query the largest landmark's share of the row sum (how far
+    one landmark dominates), averaged over queries.  The pages' argument
+    against the Gaussian kernel on heavy-tailed distances is that it
+    suppresses moderate interactions and lets outliers dominate."""
+    import dataclasses
+
+    import torch
+    import laplacian_nystr_approximation_amd as L
+
+    out = {}
+    for kern in ("laplacian", "gaussian"):
+        wk = dataclasses.replace(w, kernel=kern)
+        params = L.params_for(wk)
+        ws = torch.empty(L.lapnys_workspace_size(params), dtype=torch.uint8, device=dev)
+        o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
+        ct = torch.empty((w.P, w.m, w.N), dtype=torch.float32, device=dev)
+        L.lapnys_forward_debug(q, k, v, o, params, ws, {"C_t": ct})
+        c = ct.double()
+        qs = torch.quantile(c.flatten()[:: -(-c.numel() // (1 << 23))],
+                            torch.tensor([0.01, 0.1, 0.5, 0.9, 0.99], dtype=torch.float64, device=dev))
+        top_share = (c.max(dim=1).values / c.sum(dim=1).clamp_min(1e-300)).mean()
+        out[kern] = {"quantiles_1_10_50_90_99": [float(t) for t in qs.cpu()],
+                     "share_below_1e-6": float((c < 1e-6).double().mean()),
+                     "mean_top_landmark_share": float(top_share)}
+        del ws, o, ct, c
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -367,6 +398,8 @@ def main(argv=None):
         "stage_roofline": stage_rooflines(w, stage_ms),
         "ms_per_step_without_events": plain_ms,
     }
+    if gauss:
+        line["kernel_values"] = kernel_value_comparison(w, q, k, v, dev)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -109,9 +109,8 @@ int make_plan(const lapnys_params* p, Plan* pl) {
   P.off_w = take(Pn * P.mp * P.mp * f);
   P.off_x = take(Pn * P.mp * P.mp * f);
   // The second iterate and the product buffer serve the tiled solver's
-  // steps and its column-sum partials, and the correction of LAPNYS_NS_REFINE
-  // at any size.
-  const bool tiled = !P.fused_ns || P.refine || P.gaussian;
+  // steps, and the correction of LAPNYS_NS_REFINE at any size.
+  const bool tiled = !P.fused_ns || P.refine;
   P.off_x2 = take(tiled ? Pn * P.mp * P.mp * f : 0);
   P.off_pm = take(tiled ? Pn * P.mp * P.mp * f : 0);
   P.off_ct = take(Pn * P.m * (size_t)P.ldc * f);

@@ -264,80 +264,177 @@ __global__ __launch_bounds__(256) void residual_kernel(const float* __restrict__
   }
 }
 
-// m <= 64, Gaussian form: the steps X <- X (2I - W X) of one problem per
-// workgroup with W and the iterates in LDS (64 x 64, zero padded), from the W
-// and X0 of wbuild_big_kernel and alpha_x0_kernel, in the tiled steps' form:
-// T = 2I - W X in full, then X T, float32 products on fp32 MFMA 16x16x4
-// over k in [0, kext).  (The in-LDS schedule of the Laplacian form keeps X
+// m <= 64, Gaussian form: W, alpha, X0 and the steps X <- X (2I - W X) of
+// one problem per workgroup, with W and the iterates in LDS (64 x 64, zero
+// padded).  W's entries are formed as in wbuild_big_kernel (squared
+// differences over even and odd features, in increasing order, so W is
+// bit-symmetric, and the diagonal is 1 + eps) and written out; alpha = (max
+// column sum)^2 and X0 = W / alpha as in alpha_x0_kernel.  The steps take the
+// tiled steps' form: T = 2I - W X in full, then X T, float32 products on fp32
+// MFMA 16x16x4 over k in [0, kext).  (The in-LDS schedule of the Laplacian form keeps X
 // exactly symmetric by mirroring one triangle of X (W X); for an iterate that
 // is still far from converged after the fixed step count, as a Gaussian W
 // often leaves it, the mirrored rounding errors cost about 6x in the output's
 // agreement with the float64 iteration, so this form keeps every entry.)
-// Wavefront w forms block row w of each product.  X is updated in place: the
-// second product of wavefront w reads only block row w of X (and all of T),
-// and writes that block row after its reads.  The final X overwrites X0.
-__global__ __launch_bounds__(256) void ns_plain_kernel(const float* __restrict__ w, float* __restrict__ x, int kext,
+//
+// Eight wavefronts: wavefront v forms block row v / 2 and column blocks
+// 2 (v % 2) + [0, 2) of each product.  The reduction index is permuted so
+// that lane group lk takes k in [S lk, S lk + S), S = kext / 4: every operand
+// is then read as 16-byte LDS loads, four steps at a time, from row-major
+// copies of W (symmetric), X, X^T and T^T.  X is double-buffered (two
+// wavefronts share a block row); X^T and T^T are rewritten only after every
+// wavefront has passed the barrier behind their last reads.
+template <int D>
+__global__ __launch_bounds__(512) void ns_plain_kernel(const float* __restrict__ kt, float* __restrict__ w,
+                                                       float* __restrict__ x, int m, float scale, float eps, int kext,
                                                        int iters) {
-  constexpr int kS = 68;  // row stride: the A-operand column reads hit distinct banks
-  __shared__ __align__(16) float ws[64 * kS];
-  __shared__ __align__(16) float xs[64 * kS];
-  __shared__ __align__(16) float ts[64 * kS];
+  constexpr int kS = 68;  // row stride (floats): 16-byte rows, quarter-waves on distinct banks
+  constexpr int kN = 64 * kS;
+  extern __shared__ __align__(16) float lds[];
+  float* ws = lds;            // W
+  float* xr = ws + kN;        // X, two buffers
+  float* xt = xr + 2 * kN;    // X^T
+  float* tt = xt + kN;        // T^T
   const int p = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int li = lane & 15, lk = lane >> 4;
-  const f32x4* w4 = reinterpret_cast<const f32x4*>(w + (size_t)p * 64 * 64);
+  const int br = wv >> 1, bc0 = 2 * (wv & 1);
+  const int S = kext / 4;
+  f32x4* w4 = reinterpret_cast<f32x4*>(w + (size_t)p * 64 * 64);
   f32x4* x4 = reinterpret_cast<f32x4*>(x + (size_t)p * 64 * 64);
-  f32x4 wv4[4], xv4[4];
+  {
+    // Landmark rows (zero past m) into the T^T buffer, every load issued
+    // before the first store.
+    constexpr int kQ = D / 4;
+    constexpr int kV = 64 * kQ / 512;
+    const f32x4* k4 = reinterpret_cast<const f32x4*>(kt + (size_t)p * m * D);
+    f32x4 kv[kV];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    wv4[i] = w4[tid + 256 * i];
-    xv4[i] = x4[tid + 256 * i];
-  }
+    for (int i = 0; i < kV; ++i) {
+      const int e = tid + 512 * i;
+      kv[i] = k4[min(e / kQ, m - 1) * kQ + e % kQ];
+    }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e4 = tid + 256 * i;
-    *reinterpret_cast<f32x4*>(&ws[(e4 >> 4) * kS + 4 * (e4 & 15)]) = wv4[i];
-    *reinterpret_cast<f32x4*>(&xs[(e4 >> 4) * kS + 4 * (e4 & 15)]) = xv4[i];
+    for (int i = 0; i < kV; ++i) {
+      const int e = tid + 512 * i;
+      *reinterpret_cast<f32x4*>(&tt[(e / kQ) * kS + 4 * (e % kQ)]) = e / kQ < m ? kv[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
   }
   __syncthreads();
-  for (int it = 0; it < iters; ++it) {
-    f32x4 acc[4];
+  {
+    // W: lane b = tid % 64 forms column b for rows a = 8 g + [0, 8), g = tid / 64.
+    const int b = tid & 63, g = tid >> 6;
+    float kb[D];
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj) acc[bj] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < kext; k0 += 4) {
-      const float a = ws[(16 * wv + li) * kS + k0 + lk];
+    for (int t = 0; t < D; ++t) kb[t] = tt[b * kS + t];
+    float csum = 0.f;
+    for (int a = 8 * g; a < 8 * g + 8; ++a) {
+      float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-      for (int bj = 0; bj < 4; ++bj)
-        acc[bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, xs[(k0 + lk) * kS + 16 * bj + li], acc[bj], 0, 0, 0);
-    }
-    // acc[bj][r] = (W X)[16 w + 4 lk + r][16 bj + li]
-#pragma unroll
-    for (int bj = 0; bj < 4; ++bj)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * wv + 4 * lk + r, j = 16 * bj + li;
-        ts[i * kS + j] = (i == j ? 2.f : 0.f) - acc[bj][r];
+      for (int t = 0; t < D; t += 2) {
+        const float e0 = tt[a * kS + t] - kb[t], e1 = tt[a * kS + t + 1] - kb[t + 1];
+        s0 = fmaf(e0, e0, s0);
+        s1 = fmaf(e1, e1, s1);
       }
-    __syncthreads();  // T complete; every wavefront is done reading X for W X
+      float val = 0.f;
+      if (a < m && b < m) {
+        val = exp2f((s0 + s1) * scale);
+        if (a == b) val += eps;
+      }
+      ws[a * kS + b] = val;
+      csum += val;
+    }
+    xr[kN + g * 64 + b] = csum;  // partial column sums in the second X buffer
+  }
+  __syncthreads();
+  if (tid < 64) {
+    float cs = 0.f;
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj) acc[bj] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < kext; k0 += 4) {
-      const float a = xs[(16 * wv + li) * kS + k0 + lk];
+    for (int g = 0; g < 8; ++g) cs += xr[kN + g * 64 + tid];
 #pragma unroll
-      for (int bj = 0; bj < 4; ++bj)
-        acc[bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, ts[(k0 + lk) * kS + 16 * bj + li], acc[bj], 0, 0, 0);
+    for (int off = 32; off >= 1; off >>= 1) cs = fmaxf(cs, __shfl_xor(cs, off, 64));
+    if (tid == 0) xr[kN + 512] = cs * cs;
+  }
+  __syncthreads();
+  const float alpha = xr[kN + 512];
+  // X0 = W^T / alpha = W / alpha; W goes out to the workspace.
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e4 = tid + 512 * i, row = e4 >> 4, c4 = 4 * (e4 & 15);
+    const f32x4 wrow = *reinterpret_cast<const f32x4*>(&ws[row * kS + c4]);
+    w4[e4] = wrow;
+    f32x4 x0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x0[u] = wrow[u] / alpha;
+    *reinterpret_cast<f32x4*>(&xr[row * kS + c4]) = x0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) xt[(c4 + u) * kS + row] = x0[u];
+  }
+  __syncthreads();
+  const int arow = (16 * br + li) * kS + S * lk;  // A operand: row 16 br + li, this lane group's k
+  int brow[2];                                    // B operand: transposed row 16 bj + li
+#pragma unroll
+  for (int j = 0; j < 2; ++j) brow[j] = (16 * (bc0 + j) + li) * kS + S * lk;
+  int cur = 0;
+  for (int it = 0; it < iters; ++it) {
+    const float* xc = xr + cur * kN;
+    float* xn = xr + (cur ^ 1) * kN;
+    f32x4 acc[2];
+    // T = 2I - W X, stored transposed
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < S; c += 4) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(&ws[arow + c]);
+      f32x4 b[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = *reinterpret_cast<const f32x4*>(&xt[brow[j] + c]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[j][e], acc[j], 0, 0, 0);
+    }
+    // acc[j][r] = (W X)[16 br + 4 lk + r][16 (bc0 + j) + li]
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = 16 * (bc0 + j) + li, row0 = 16 * br + 4 * lk;
+      f32x4 t;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) t[r] = (row0 + r == col ? 2.f : 0.f) - acc[j][r];
+      *reinterpret_cast<f32x4*>(&tt[col * kS + row0]) = t;
+    }
+    __syncthreads();  // T complete; every wavefront is done reading X^T
+    // X_next = X T
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < S; c += 4) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(&xc[arow + c]);
+      f32x4 b[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = *reinterpret_cast<const f32x4*>(&tt[brow[j] + c]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[j][e], acc[j], 0, 0, 0);
     }
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj)
+    for (int j = 0; j < 2; ++j) {
+      const int col = 16 * (bc0 + j) + li, row0 = 16 * br + 4 * lk;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) xs[(16 * wv + 4 * lk + r) * kS + 16 * bj + li] = acc[bj][r];
-    __syncthreads();  // X_next complete; T free for the next step
+      for (int r = 0; r < 4; ++r) xn[(row0 + r) * kS + col] = acc[j][r];
+      *reinterpret_cast<f32x4*>(&xt[col * kS + row0]) = acc[j];
+    }
+    __syncthreads();  // X_next and its transpose complete; T^T free
+    cur ^= 1;
   }
+  const float* xf = xr + cur * kN;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e4 = tid + 256 * i;
-    x4[e4] = *reinterpret_cast<const f32x4*>(&xs[(e4 >> 4) * kS + 4 * (e4 & 15)]);
+  for (int i = 0; i < 2; ++i) {
+    const int e4 = tid + 512 * i;
+    x4[e4] = *reinterpret_cast<const f32x4*>(&xf[(e4 >> 4) * kS + 4 * (e4 & 15)]);
   }
 }
+
+// LDS of ns_plain_kernel: W, X twice, X^T and T^T, 64 rows of 68 floats each.
+constexpr size_t kPlainLds = 5 * 64 * 68 * sizeof(float);
 
 __global__ __launch_bounds__(256) void extract_square_kernel(const float* __restrict__ src, int src_ld,
                                                              float* __restrict__ dst, int n, long long total) {
@@ -352,10 +449,23 @@ __global__ __launch_bounds__(256) void extract_square_kernel(const float* __rest
 }  // namespace
 
 hipError_t launch_ns(const Plan& pl, Work& wk, hipStream_t s, Span t) {
-  // m <= 64: the Laplacian form runs inside the kernel-matrix launch
-  // (launch_l1exp); the Gaussian form builds W and X0 here as for larger m and
-  // then runs its steps in one workgroup per problem.
-  if (pl.fused_ns && !pl.gaussian) return hipErrorInvalidValue;
+  const int kext = (pl.m + 31) & ~31;
+  if (pl.fused_ns) {
+    // m <= 64: the Laplacian form runs inside the kernel-matrix launch
+    // (launch_l1exp); the Gaussian form runs one workgroup per problem here.
+    // kext (m rounded up to 32) is a multiple of 16, as the operand reads need.
+    if (!pl.gaussian) return hipErrorInvalidValue;
+    auto kern = pl.d == 64 ? ns_plain_kernel<64> : ns_plain_kernel<32>;
+    hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)kPlainLds);
+    if (err != hipSuccess) return err;
+    hipExtLaunchKernelGGL(kern, dim3(pl.P), dim3(512), kPlainLds, s, t.start, pl.refine ? nullptr : t.stop, 0, wk.kt,
+                          wk.w, wk.x, pl.m, pl.scale, pl.eps, kext, pl.ns_iters);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    wk.x_final = wk.x;
+    return pl.refine ? launch_refine(pl, wk, s, t.stop) : hipSuccess;
+  }
   const int mp = pl.mp;
   auto wbuild = pl.d == 64 ? (pl.gaussian ? wbuild_big_kernel<64, true> : wbuild_big_kernel<64, false>)
                            : (pl.gaussian ? wbuild_big_kernel<32, true> : wbuild_big_kernel<32, false>);
@@ -364,18 +474,9 @@ hipError_t launch_ns(const Plan& pl, Work& wk, hipStream_t s, Span t) {
   // The column-sum partials go to the product buffer, which the steps only
   // write after alpha_x0 has read them.
   hipExtLaunchKernelGGL(alpha_x0_kernel, dim3(pl.P, 16), dim3(256), 0, s, nullptr,
-                        pl.ns_iters == 0 && !pl.refine && !pl.fused_ns ? t.stop : nullptr, 0, wk.w, wk.pm, wk.x, mp);
+                        pl.ns_iters == 0 && !pl.refine ? t.stop : nullptr, 0, wk.w, wk.pm, wk.x, mp);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int kext = (pl.m + 31) & ~31;
-  if (pl.fused_ns) {
-    hipExtLaunchKernelGGL(ns_plain_kernel, dim3(pl.P), dim3(256), 0, s, nullptr, pl.refine ? nullptr : t.stop, 0,
-                          wk.w, wk.x, kext, pl.ns_iters);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    wk.x_final = wk.x;
-    return pl.refine ? launch_refine(pl, wk, s, t.stop) : hipSuccess;
-  }
   const long long sq = (long long)mp * mp;
   const dim3 grid(mp / 64, mp / 64, pl.P);
   float* xc = wk.x;

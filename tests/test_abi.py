@@ -107,14 +107,12 @@ def test_refine_flag_accepted_and_sized():
 
 
 def test_gaussian_flag_accepted():
-    """LAPNYS_GAUSSIAN is a known flag.  At m <= 64 its solver builds W and X0
-    as the tiled one does, so it adds that solver's two P x 64 x 64 buffers;
-    above 64 the workspace is the Laplacian form's."""
+    """LAPNYS_GAUSSIAN is a known flag and needs no other workspace: the
+    intermediates are the same as the Laplacian form's."""
     g = _p(kernel="gaussian")
     assert g.flags == B.LAPNYS_WHITEN | B.LAPNYS_GAUSSIAN
     assert L.library().lapnys_landmark_count(ctypes.byref(g)) == 49
-    grow = L.lapnys_workspace_size(g) - L.lapnys_workspace_size(_p())
-    assert 2 * 6 * 64 * 64 * 4 <= grow <= 2 * 6 * 64 * 64 * 4 + 512
+    assert L.lapnys_workspace_size(g) == L.lapnys_workspace_size(_p())
     big = dict(grid_h=32, grid_w=32)
     assert L.lapnys_workspace_size(_p(kernel="gaussian", **big)) == L.lapnys_workspace_size(_p(**big))
     with pytest.raises(ValueError):

@@ -2,6 +2,7 @@
 
 from .lapnys_oracle import (  # noqa: F401
     attention_problem,
+    conjugate_gradient,
     forward,
     gaussian_kernel,
     laplacian_kernel,

@@ -130,6 +130,39 @@ def refine_inverse(w, x):
     return x + x @ r
 
 
+def conjugate_gradient(w, rhs, iters):
+    """Solve W Y = rhs column by column with a fixed number of conjugate-gradient steps.
+
+    The pages compare Newton-Schulz against a conjugate-gradient solver in
+    their ablation (EN page, section 4, solver robustness; DE section 4,
+    ablations; ZH, KO and JA section 4) without spelling it out.  Reading
+    taken: CG computes the product the inverse is needed for, Y = W^-1 (B V),
+    directly: one independent CG run per column of the right-hand side, from
+    Y0 = 0, no preconditioner, exactly ``iters`` steps (as the Newton-Schulz
+    count is fixed).  Step: a = r.r / p.(W p); y += a p; r -= a W p;
+    b = r'.r' / r.r; p = r' + b p.  A column whose residual is exactly zero
+    stops changing (a = b = 0 instead of 0/0).
+    """
+    w = np.asarray(w, dtype=np.float64)
+    rhs = np.asarray(rhs, dtype=np.float64)
+    y = np.zeros_like(rhs)
+    r = rhs.copy()
+    p = r.copy()
+    rr = (r * r).sum(axis=0)
+    for _ in range(iters):
+        q = w @ p
+        pq = (p * q).sum(axis=0)
+        live = rr > 0
+        a = np.where(live, rr / np.where(live, pq, 1.0), 0.0)
+        y = y + a * p
+        r = r - a * q
+        rr_new = (r * r).sum(axis=0)
+        b = np.where(live, rr_new / np.where(live, rr, 1.0), 0.0)
+        p = r + b * p
+        rr = rr_new
+    return y
+
+
 def whiten_columns(c):
     """Diagonal whitening of the query-side similarity vectors.
 
@@ -153,7 +186,7 @@ def whiten_columns(c):
 
 
 def attention_problem(q, k, v, *, grid_h, grid_w, pool, lam, eps, ns_iters, whiten=True, refine=False,
-                      kernel="laplacian"):
+                      kernel="laplacian", solver="ns"):
     """Forward of one (batch, head) problem; returns every intermediate.
 
     Steps, in the method's order:
@@ -170,7 +203,11 @@ def attention_problem(q, k, v, *, grid_h, grid_w, pool, lam, eps, ns_iters, whit
     positive definite.  No row normalisation of the output is applied: the pages
     mention none.  ``kernel="gaussian"`` runs the same steps with gaussian_kernel
     in place of laplacian_kernel for C, B and W (the pages' baseline kernel).
+    ``solver="cg"`` replaces X (B V) by conjugate_gradient(W, B V, ns_iters)
+    (the pages' solver ablation); X is then not formed and is returned as None.
     """
+    if solver not in ("ns", "cg"):
+        raise ValueError(f"unknown solver {solver!r}")
     if kernel not in ("laplacian", "gaussian"):
         raise ValueError(f"unknown kernel {kernel!r}")
     kfun = gaussian_kernel if kernel == "gaussian" else laplacian_kernel
@@ -182,22 +219,26 @@ def attention_problem(q, k, v, *, grid_h, grid_w, pool, lam, eps, ns_iters, whit
     c = kfun(q, kt, lam)
     b = kfun(kt, k, lam)
     w = kfun(kt, kt, lam) + eps * np.eye(m)
-    x = newton_schulz_inverse(w, ns_iters)
-    if refine:
-        x = refine_inverse(w, x)
     if whiten:
         z, mu, sigma = whiten_columns(c)
     else:
         z, mu, sigma = c, np.zeros(m), np.ones(m)
     bv = b @ v
-    y = x @ bv
+    if solver == "cg":
+        x = None
+        y = conjugate_gradient(w, bv, ns_iters)
+    else:
+        x = newton_schulz_inverse(w, ns_iters)
+        if refine:
+            x = refine_inverse(w, x)
+        y = x @ bv
     o = z @ y
     return {"landmarks": kt, "C": c, "B": b, "W": w, "X": x, "Z": z,
             "mu": mu, "sigma": sigma, "BV": bv, "Y": y, "O": o}
 
 
 def forward(q, k, v, *, grid_h, grid_w, pool, lam, eps, ns_iters, whiten=True, problems=None, refine=False,
-            kernel="laplacian"):
+            kernel="laplacian", solver="ns"):
     """Forward over [B, H, N, d] inputs; every (b, h) problem is independent.
 
     ``problems`` optionally lists the (b, h) pairs to compute (a sample of a large
@@ -209,9 +250,10 @@ def forward(q, k, v, *, grid_h, grid_w, pool, lam, eps, ns_iters, whiten=True, p
     bsz, heads = q.shape[0], q.shape[1]
     pairs = list(problems) if problems is not None else [(b, h) for b in range(bsz) for h in range(heads)]
     outs = [attention_problem(q[b, h], k[b, h], v[b, h], grid_h=grid_h, grid_w=grid_w, pool=pool,
-                              lam=lam, eps=eps, ns_iters=ns_iters, whiten=whiten, refine=refine, kernel=kernel)
+                              lam=lam, eps=eps, ns_iters=ns_iters, whiten=whiten, refine=refine, kernel=kernel,
+                              solver=solver)
             for (b, h) in pairs]
-    res = {key: np.stack([o[key] for o in outs]) for key in outs[0]}
+    res = {key: np.stack([o[key] for o in outs]) for key in outs[0] if outs[0][key] is not None}
     if problems is None:
         res = {key: val.reshape((bsz, heads) + val.shape[1:]) for key, val in res.items()}
     res["problems"] = pairs

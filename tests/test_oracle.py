@@ -113,6 +113,62 @@ def pin_gaussian_nystrom_pool1(orc):
         assert np.abs(res["W"] - a).max() <= 1e-15
 
 
+def _spd(rng, m, eigs):
+    qm, _ = np.linalg.qr(rng.standard_normal((m, m)))
+    return (qm * np.asarray(eigs, float)) @ qm.T
+
+
+def pin_cg_finite_termination(orc):
+    # In exact arithmetic CG solves an m x m SPD system in at most m steps, and
+    # in as many steps as W has distinct eigenvalues.
+    rng = _rng(20)
+    w = _spd(rng, 6, [0.5, 1.0, 2.0, 3.0, 5.0, 8.0])
+    b = rng.standard_normal((6, 3))
+    want = np.linalg.solve(w, b)
+    got = orc.conjugate_gradient(w, b, 6)
+    assert np.abs(got - want).max() <= 1e-10 * np.abs(want).max()
+    w3 = _spd(rng, 8, [1.0, 1.0, 1.0, 4.0, 4.0, 9.0, 9.0, 9.0])
+    b3 = rng.standard_normal((8, 2))
+    got3 = orc.conjugate_gradient(w3, b3, 3)
+    assert np.abs(w3 @ got3 - b3).max() <= 1e-10 * np.abs(b3).max()
+    got2 = orc.conjugate_gradient(w3, b3, 2)
+    assert np.abs(w3 @ got2 - b3).max() > 1e-4  # not yet
+
+
+def pin_cg_first_step_and_monotone(orc):
+    # Step one is a steepest-descent step, y1 = (b.b / b.Wb) b; the W-norm of the
+    # error never grows; a zero right-hand side stays zero.
+    rng = _rng(21)
+    w = _spd(rng, 7, np.geomspace(0.1, 10.0, 7))
+    b = rng.standard_normal((7, 2))
+    b[:, 1] = 0.0
+    y1 = orc.conjugate_gradient(w, b, 1)
+    col = b[:, 0]
+    assert np.allclose(y1[:, 0], (col @ col) / (col @ w @ col) * col, rtol=1e-13, atol=0)
+    assert np.all(y1[:, 1] == 0.0)
+    ystar = np.linalg.solve(w, b[:, :1])
+    errs = []
+    for t in range(0, 8):
+        e = orc.conjugate_gradient(w, b, t)[:, :1] - ystar
+        errs.append(float(np.sqrt((e.T @ w @ e)[0, 0])))
+    assert all(errs[i + 1] <= errs[i] * (1 + 1e-12) for i in range(len(errs) - 1)), errs
+    assert errs[3] < 0.9 * errs[0]
+
+
+def pin_cg_in_forward(orc):
+    # solver="cg" feeds Y = CG(W, B V) to the output product: with enough steps it
+    # reaches the same output as an exact solve.
+    rng = _rng(22)
+    gh, gw, d = 6, 6, 4
+    q, k, v = (_heavy(rng, (gh * gw, d)) for _ in range(3))
+    res = orc.attention_problem(q, k, v, grid_h=gh, grid_w=gw, pool=2, lam=4.0, eps=1e-2, ns_iters=40,
+                                solver="cg")
+    want = res["Z"] @ np.linalg.solve(res["W"], res["BV"])
+    assert np.abs(res["O"] - want).max() <= 1e-9 * np.abs(want).max()
+    assert res["X"] is None
+    assert np.abs(res["Y"] - orc.conjugate_gradient(res["W"], res["BV"], 40)).max() == 0.0
+
+
 def pin_pool_ramp(orc):
     # K[n, t] = n + 1000 t on a row-major grid: the window mean has a closed form.
     for gh, gw, p in [(6, 10, 2), (9, 6, 3), (4, 8, 4), (5, 5, 1)]:
@@ -314,7 +370,8 @@ PINS = [pin_kernel_hand, pin_kernel_invariants, pin_pool_ramp, pin_pool_special_
         pin_pool_fixed_order, pin_ns_closed_form, pin_ns_lu, pin_ns_residual_squares,
         pin_whiten_moments, pin_nystrom_pool1, pin_single_landmark, pin_metamorphic,
         pin_forward_layout, pin_refine_squares_residual, pin_gaussian_hand,
-        pin_gaussian_library_and_invariants, pin_gaussian_nystrom_pool1]
+        pin_gaussian_library_and_invariants, pin_gaussian_nystrom_pool1, pin_cg_finite_termination,
+        pin_cg_first_step_and_monotone, pin_cg_in_forward]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -448,8 +505,31 @@ def _g_expansion_sign(x, y, lam):
     return np.exp(-d2 / lam)
 
 
+def _cg_variant(variant):
+    def f(w, rhs, iters):
+        w = np.asarray(w, float)
+        y = np.zeros_like(rhs, dtype=float)
+        r = np.array(rhs, dtype=float)
+        p = r.copy()
+        rr = (r * r).sum(0)
+        for _ in range(iters):
+            q = w @ p
+            den = (p * p).sum(0) if variant == "alpha_pp" else (p * q).sum(0)
+            a = np.where(rr > 0, rr / np.where(rr > 0, den, 1.0), 0.0)
+            y = y + a * p
+            r = r + a * q if variant == "residual_sign" else r - a * q
+            rn = (r * r).sum(0)
+            bta = np.where(rr > 0, (rr / np.where(rn > 0, rn, 1.0)) if variant == "beta_inverted"
+                           else rn / np.where(rr > 0, rr, 1.0), 0.0)
+            p = r if variant == "steepest_descent" else r + bta * p
+            rr = rn
+        return y
+    return f
+
+
 def _attention_variant(variant):
-    def f(q, k, v, *, grid_h, grid_w, pool, lam, eps, ns_iters, whiten=True, refine=False, kernel="laplacian"):
+    def f(q, k, v, *, grid_h, grid_w, pool, lam, eps, ns_iters, whiten=True, refine=False, kernel="laplacian",
+          solver="ns"):
         kt = O.pool_landmarks(k, grid_h, grid_w, pool)
         m = kt.shape[0]
         kf = O.gaussian_kernel if kernel == "gaussian" else O.laplacian_kernel
@@ -467,7 +547,13 @@ def _attention_variant(variant):
         else:
             z, mu, sigma = c, np.zeros(m), np.ones(m)
         bv = b @ v
-        y = x @ bv
+        if solver == "cg":
+            x = None
+            y = O.conjugate_gradient(w, bv, ns_iters)
+            if variant == "skip_inverse":
+                y = bv
+        else:
+            y = x @ bv
         o = z @ y
         return {"landmarks": kt, "C": c, "B": b, "W": w, "X": x, "Z": z,
                 "mu": mu, "sigma": sigma, "BV": bv, "Y": y, "O": o}
@@ -497,6 +583,10 @@ MUTANTS = {
     "gaussian_half_scale": ("gaussian_kernel", _g_half_scale),
     "gaussian_expansion_sign": ("gaussian_kernel", _g_expansion_sign),
     "gaussian_w_from_laplacian": ("attention_problem", _attention_variant("gaussian_w_laplacian")),
+    "cg_alpha_over_pp": ("conjugate_gradient", _cg_variant("alpha_pp")),
+    "cg_residual_sign": ("conjugate_gradient", _cg_variant("residual_sign")),
+    "cg_beta_inverted": ("conjugate_gradient", _cg_variant("beta_inverted")),
+    "cg_steepest_descent": ("conjugate_gradient", _cg_variant("steepest_descent")),
 }
 
 

@@ -70,16 +70,23 @@ typedef enum { LAPNYS_F32 = 0, LAPNYS_BF16 = 1 } lapnys_dtype;
  *   lambda.  Every other step is unchanged.  The squared distances of C and
  *   B are formed as ||x||^2 + ||y||^2 - 2 x.y (the dot products on fp32
  *   MFMA) and clamped at 0; W's are summed directly.  The solver then runs
- *   as launches of its own, beside the kernel-matrix stage, at every m. */
-enum { LAPNYS_WHITEN = 1u, LAPNYS_NS_REFINE = 2u, LAPNYS_GAUSSIAN = 4u };
+ *   as launches of its own, beside the kernel-matrix stage, at every m.
+ * LAPNYS_SOLVER_CG: the conjugate-gradient solver of the pages' solver
+ *   ablation (EN section 4) in place of Newton-Schulz: Y = W^-1 (B V) is
+ *   computed directly by ns_iters CG steps per column of B V, from Y0 = 0,
+ *   without a preconditioner, in float32 (a column whose residual is exactly
+ *   zero, or so small that p.(W p) underflows to zero, stops changing).  X is not formed: the debug form leaves its X
+ *   buffer untouched.  Not combinable with LAPNYS_NS_REFINE. */
+enum { LAPNYS_WHITEN = 1u, LAPNYS_NS_REFINE = 2u, LAPNYS_GAUSSIAN = 4u, LAPNYS_SOLVER_CG = 8u };
 
 /* Status codes. */
 enum {
   LAPNYS_OK = 0,
   LAPNYS_ERR_INVALID_ARG = -1, /* null/misaligned pointer, non-positive size,
                                   lambda <= 0, eps < 0, ns_iters < 0, unknown
-                                  flag bits, non-finite lambda/eps, or out
-                                  overlapping an input */
+                                  flag bits, LAPNYS_SOLVER_CG together with
+                                  LAPNYS_NS_REFINE, non-finite lambda/eps, or
+                                  out overlapping an input */
   LAPNYS_ERR_SHAPE = -2,       /* N != grid_h * grid_w, or pool does not divide
                                   grid_h and grid_w */
   LAPNYS_ERR_UNSUPPORTED = -3, /* d not in {32, 64}, m > 256, unknown dtype, or
@@ -101,7 +108,8 @@ typedef struct {
   float eps;             /* >= 0 */
   int32_t ns_iters;      /* Newton-Schulz steps, >= 0 */
   int32_t dtype;         /* lapnys_dtype */
-  uint32_t flags;        /* LAPNYS_WHITEN | LAPNYS_NS_REFINE | LAPNYS_GAUSSIAN, or 0 */
+  uint32_t flags;        /* LAPNYS_WHITEN | LAPNYS_NS_REFINE | LAPNYS_GAUSSIAN |
+                            LAPNYS_SOLVER_CG, or 0 */
 } lapnys_params;
 
 /* Optional device buffers for the intermediates of one call (debug form).
@@ -125,9 +133,11 @@ typedef struct {
 enum {
   LAPNYS_STAGE_POOL = 0,     /* landmark average pooling */
   LAPNYS_STAGE_NS = 1,       /* W build, scaling, Newton-Schulz (and the
-                                correction of LAPNYS_NS_REFINE) */
+                                correction of LAPNYS_NS_REFINE); with
+                                LAPNYS_SOLVER_CG the W build only */
   LAPNYS_STAGE_KERNEL = 2,   /* fused distance + exp: C, column statistics, B V */
-  LAPNYS_STAGE_FINALIZE = 3, /* statistics and B V reductions, Y = X (B V) */
+  LAPNYS_STAGE_FINALIZE = 3, /* statistics and B V reductions, Y = X (B V)
+                                (the CG solve with LAPNYS_SOLVER_CG) */
   LAPNYS_STAGE_OUTPUT = 4,   /* O = whiten(C) Y */
   LAPNYS_NUM_STAGES = 5
 };

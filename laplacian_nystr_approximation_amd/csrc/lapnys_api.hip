@@ -51,7 +51,9 @@ int validate(const lapnys_params* p) {
   if (!(isfinite(p->lambda) && p->lambda > 0.f)) return LAPNYS_ERR_INVALID_ARG;
   if (!(isfinite(p->eps) && p->eps >= 0.f)) return LAPNYS_ERR_INVALID_ARG;
   if (p->ns_iters < 0) return LAPNYS_ERR_INVALID_ARG;
-  if (p->flags & ~(uint32_t)(LAPNYS_WHITEN | LAPNYS_NS_REFINE | LAPNYS_GAUSSIAN)) return LAPNYS_ERR_INVALID_ARG;
+  if (p->flags & ~(uint32_t)(LAPNYS_WHITEN | LAPNYS_NS_REFINE | LAPNYS_GAUSSIAN | LAPNYS_SOLVER_CG))
+    return LAPNYS_ERR_INVALID_ARG;
+  if ((p->flags & LAPNYS_SOLVER_CG) && (p->flags & LAPNYS_NS_REFINE)) return LAPNYS_ERR_INVALID_ARG;
   if (p->dtype != LAPNYS_F32 && p->dtype != LAPNYS_BF16) return LAPNYS_ERR_UNSUPPORTED;
   if ((int64_t)p->grid_h * p->grid_w != (int64_t)p->N) return LAPNYS_ERR_SHAPE;
   if (p->grid_h % p->pool || p->grid_w % p->pool) return LAPNYS_ERR_SHAPE;
@@ -80,17 +82,20 @@ int make_plan(const lapnys_params* p, Plan* pl) {
   P.ns_iters = p->ns_iters;
   P.refine = (p->flags & LAPNYS_NS_REFINE) != 0;
   P.gaussian = (p->flags & LAPNYS_GAUSSIAN) != 0;
+  P.cg = (p->flags & LAPNYS_SOLVER_CG) != 0;
   // exp(-s / lambda) = exp2(s * scale)
   P.scale = (float)(-1.4426950408889634074 / (double)p->lambda);
   P.eps = p->eps;
   // m <= 64: one workgroup per problem runs the steps (inside the
   // kernel-matrix launch for the Laplacian form, a launch of its own beside
   // it for the Gaussian form).
-  P.fused_ns = P.m <= lapnys::kFusedNsMaxM;
+  P.fused_ns = P.m <= lapnys::kFusedNsMaxM && !P.cg;
   P.mp = P.fused_ns ? 64 : ((P.m + 63) / 64) * 64;
   P.tt = 256;
   P.ntiles = (P.N + P.tt - 1) / P.tt;
-  P.lb = P.m <= lapnys::kLandmarkBlock ? P.m : 32;
+  // Landmark blocks: all m <= 64 landmarks in one block beside the in-LDS
+  // solver, else blocks of 32.
+  P.lb = P.fused_ns ? P.m : (P.m < 32 ? P.m : 32);
   P.jblocks = (P.m + P.lb - 1) / P.lb;
   // Tiles per workgroup: enough workgroups to fill the chip several times,
   // few enough that the B V partials stay small.
@@ -253,6 +258,11 @@ int run(const Plan& pl, const void* q, const void* k, const void* v, float* out,
     // wait for the solver.
     if (!ok(hipStreamWaitEvent(s, dc->join, 0), "hipStreamWaitEvent")) return LAPNYS_ERR_HIP;
     if (!ok(lapnys::launch_reduce(pl, W, s, fin), "reduce launch")) return LAPNYS_ERR_HIP;
+  } else if (pl.cg) {
+    // CG: Y = W^-1 (B V) once B V and W are both there.
+    if (!ok(lapnys::launch_reduce(pl, W, s, {fin.start, nullptr}), "reduce launch")) return LAPNYS_ERR_HIP;
+    if (!ok(hipStreamWaitEvent(s, dc->join, 0), "hipStreamWaitEvent")) return LAPNYS_ERR_HIP;
+    if (!ok(lapnys::launch_cg(pl, W, s, fin.stop), "CG launch")) return LAPNYS_ERR_HIP;
   } else {
     if (!ok(lapnys::launch_reduce(pl, W, s, {fin.start, nullptr}), "reduce launch")) return LAPNYS_ERR_HIP;
     if (!ok(hipStreamWaitEvent(s, dc->join, 0), "hipStreamWaitEvent")) return LAPNYS_ERR_HIP;
@@ -288,7 +298,7 @@ int forward_impl(const void* q, const void* k, const void* v, float* out, const 
   if (good && dbg->Y && pl.fused_ns) good = ok(lapnys::launch_y(pl, B, s), "Y launch");
   if (good) good = cp(dbg->Y, B.y, Pm * pl.d * f);
   if (good && dbg->W) good = ok(lapnys::launch_extract_square(B.w, pl.mp, dbg->W, pl.m, pl.P, s), "W extract");
-  if (good && dbg->X)
+  if (good && dbg->X && !pl.cg)
     good = ok(lapnys::launch_extract_square(B.x_final, pl.mp, dbg->X, pl.m, pl.P, s), "X extract");
   if (!good || !ok(hipStreamSynchronize(s), "hipStreamSynchronize")) return LAPNYS_ERR_HIP;
   return LAPNYS_OK;

@@ -85,6 +85,7 @@ struct Plan {
   int ns_iters;
   bool refine;      // one float64-residual correction after the steps
   bool gaussian;    // Gaussian kernel exp(-||x - y||_2^2 / lambda) instead of the Laplacian
+  bool cg;          // conjugate gradient for Y = W^-1 (B V) instead of Newton-Schulz
   float scale;      // -log2(e) / lambda, so k = exp2(scale * L1)
   float eps;
   int mp;           // padded Newton-Schulz size (64, or m rounded up to 64)
@@ -147,6 +148,8 @@ hipError_t launch_gauss(const Plan& pl, const void* q, const void* k, const void
 // and for m <= 64 also Y = X (B V) into w.yt.
 hipError_t launch_reduce(const Plan& pl, const Work& w, hipStream_t s, Span t = {});
 hipError_t launch_y(const Plan& pl, const Work& w, hipStream_t s, Span t = {});  // m > kFusedNsMaxM only
+// pl.cg: Y = W^-1 (B V) by pl.ns_iters CG steps per column, into w.y.
+hipError_t launch_cg(const Plan& pl, const Work& w, hipStream_t s, hipEvent_t stop = nullptr);
 hipError_t launch_output(const Plan& pl, const Work& w, float* out, hipStream_t s, Span t = {});
 hipError_t launch_extract_square(const float* src, int src_ld, float* dst, int n, int P, hipStream_t s);
 

@@ -469,8 +469,9 @@ hipError_t launch_ns(const Plan& pl, Work& wk, hipStream_t s, Span t) {
   const int mp = pl.mp;
   auto wbuild = pl.d == 64 ? (pl.gaussian ? wbuild_big_kernel<64, true> : wbuild_big_kernel<64, false>)
                            : (pl.gaussian ? wbuild_big_kernel<32, true> : wbuild_big_kernel<32, false>);
-  hipExtLaunchKernelGGL(wbuild, dim3(mp / 16, pl.P), dim3(256), 0, s, t.start, nullptr, 0, wk.kt, wk.w, wk.pm, pl.m,
-                        mp, pl.scale, pl.eps);
+  hipExtLaunchKernelGGL(wbuild, dim3(mp / 16, pl.P), dim3(256), 0, s, t.start, pl.cg ? t.stop : nullptr, 0, wk.kt,
+                        wk.w, wk.pm, pl.m, mp, pl.scale, pl.eps);
+  if (pl.cg) return hipGetLastError();  // the CG solve (cg.hip) needs W only
   // The column-sum partials go to the product buffer, which the steps only
   // write after alpha_x0 has read them.
   hipExtLaunchKernelGGL(alpha_x0_kernel, dim3(pl.P, 16), dim3(256), 0, s, nullptr,

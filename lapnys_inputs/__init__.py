@@ -42,6 +42,7 @@ class Workload:
     seed_index: int = 0
     refine: bool = False  # one float64-residual correction after the Newton-Schulz steps
     kernel: str = "laplacian"  # or "gaussian"
+    solver: str = "ns"  # or "cg" (conjugate gradient for W^-1 (B V))
 
     @property
     def N(self) -> int:

@@ -90,7 +90,7 @@ def test_invalid_params_rejected(kw, code):
 
 def test_unknown_flag_bits_rejected():
     p = _p()
-    p.flags = 8
+    p.flags = 16
     assert L.library().lapnys_landmark_count(ctypes.byref(p)) == B.LAPNYS_ERR_INVALID_ARG
 
 
@@ -117,6 +117,19 @@ def test_gaussian_flag_accepted():
     assert L.lapnys_workspace_size(_p(kernel="gaussian", **big)) == L.lapnys_workspace_size(_p(**big))
     with pytest.raises(ValueError):
         _p(kernel="cosine")
+
+
+def test_cg_flag():
+    """LAPNYS_SOLVER_CG is a known flag, refused together with LAPNYS_NS_REFINE;
+    at m <= 64 it uses the separate-launch layout (no in-LDS solver)."""
+    cg = _p(solver="cg")
+    assert cg.flags == B.LAPNYS_WHITEN | B.LAPNYS_SOLVER_CG
+    assert L.library().lapnys_landmark_count(ctypes.byref(cg)) == 49
+    both = _p(solver="cg", refine=True)
+    assert L.library().lapnys_landmark_count(ctypes.byref(both)) == B.LAPNYS_ERR_INVALID_ARG
+    assert L.lapnys_workspace_size(cg) > 0
+    with pytest.raises(ValueError):
+        _p(solver="gmres")
 
 
 def test_buffer_checks_before_launch():

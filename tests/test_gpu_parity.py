@@ -136,6 +136,47 @@ def test_gaussian_parity(w):
          f"NS residual {max(report['ns_residual']):.2e}")
 
 
+def _cg_cases():
+    base = dict(B=1, H=2, lam=4.0, eps=1e-3, ns_iters=20, seed_index=60, solver="cg")
+    c = lambda name, **kw: dataclasses.replace(WORKLOADS[name], name=name + "_cg", solver="cg", **kw)
+    return [
+        c("tiny_f32"), c("stage1_56x56_f32"), c("stage1_56x56_bf16"), c("stage3_14x14_bf16"),
+        c("stage3_14x14_bf16", kernel="gaussian"), c("stage1_56x56_f32", kernel="gaussian"),
+        Workload("cg_ragged_18x14_p2", grid_h=18, grid_w=14, d=64, pool=2, dtype="f32", **base),
+        Workload("cg_ragged_10x30_p5_d32", grid_h=10, grid_w=30, d=32, pool=5, dtype="bf16", **base),
+        Workload("cg_m81_18x18_p2", grid_h=18, grid_w=18, d=64, pool=2, dtype="f32", **base),
+        Workload("cg_m100_20x20_p2_d32", grid_h=20, grid_w=20, d=32, pool=2, dtype="f32", **base),
+        Workload("cg_m256_16x16_p1", grid_h=16, grid_w=16, d=64, pool=1, dtype="f32", **{**base, "ns_iters": 40}),
+        Workload("cg_single_landmark_6x6", grid_h=6, grid_w=6, d=64, pool=6, dtype="f32", **base),
+        Workload("cg_ns0_14x14", grid_h=14, grid_w=14, d=32, pool=2, dtype="f32", **{**base, "ns_iters": 0}),
+        c("long_256x256_bf16"),
+    ]
+
+
+@pytest.mark.parametrize("w", _cg_cases(), ids=lambda w: w.name)
+def test_cg_parity(w):
+    """LAPNYS_SOLVER_CG against the oracle's conjugate-gradient forward (same
+    step count): every stage to the usual bar; the output to the float32 or
+    bf16-input bar where the float64 CG has converged (relative residual
+    <= 1e-4), since the converged solve is unique.  Before convergence a
+    float32 CG loses the orthogonality of its directions and follows another
+    path than the float64 one (the solver's sensitivity the pages' ablation
+    reports, measured by bench.py --solver-study); there the output is checked
+    finite and reported."""
+    _say(f"[cg] {w.name} P={w.P} N={w.N} m={w.m} d={w.d} {w.dtype} {w.kernel} T={w.ns_iters}")
+    x = workload_inputs(w)
+    gpu = run_gpu(w, x)
+    sample = list(range(w.P)) if w.N * w.P <= 120000 else [0, w.P - 1]
+    ref = run_oracle(w, x, problems=sample)
+    report = {}
+    own = []
+    for r, p in enumerate(sample):
+        own.append(np.linalg.norm(ref["W"][r] @ ref["Y"][r] - ref["BV"][r]) / np.linalg.norm(ref["BV"][r]))
+        check_problem(w, gpu, p, ref, r, check_ns=False, check_o=own[-1] <= 1e-4, report=report)
+    _say(f"[cg] {w.name}: O normwise {max(report['o_normwise']):.2e}, rel L2 {max(report['o_rel_l2']):.2e}, "
+         f"CG relative residual {max(report['cg_residual']):.2e} (float64 CG: {max(own):.2e})")
+
+
 def _edge_cases():
     base = dict(B=1, H=2, lam=4.0, eps=1e-3, ns_iters=20, seed_index=40)
     cases = [

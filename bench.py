@@ -104,7 +104,8 @@ def cpu_baseline(w, x, budget_s: float):
         b, h = divmod(p, w.H)
         oracle.attention_problem(x.qf[b, h], x.kf[b, h], x.vf[b, h], grid_h=w.grid_h, grid_w=w.grid_w,
                                  pool=w.pool, lam=float(np.float32(w.lam)), eps=float(np.float32(w.eps)),
-                                 ns_iters=w.ns_iters, whiten=w.whiten, refine=w.refine, kernel=w.kernel)
+                                 ns_iters=w.ns_iters, whiten=w.whiten, refine=w.refine, kernel=w.kernel,
+                                 solver=w.solver)
         done += 1
         if time.perf_counter() - t0 > budget_s:
             break
@@ -253,6 +254,78 @@ def kernel_value_comparison(w, q, k, v, dev):
     return out
 
 
+def near_duplicate_keys(k, w, delta, rng):
+    """K with every odd pooled window of each landmark row replaced by its left
+    neighbour's tokens plus delta-scaled noise, so that pairs of landmarks
+    nearly coincide and W is close to singular (float32 inputs)."""
+    k = k.copy()
+    p, gw = w.pool, w.grid_w // w.pool
+    g = k.reshape(w.B, w.H, w.grid_h, w.grid_w, w.d)
+    for j in range(1, gw, 2):
+        src = g[:, :, :, (j - 1) * p:j * p, :]
+        g[:, :, :, j * p:(j + 1) * p, :] = src + delta * rng.standard_normal(src.shape).astype(np.float32)
+    return g.reshape(k.shape)
+
+
+def solver_study_main(args):
+    """Residual against iterations, Newton-Schulz against CG, on W made
+    ill-conditioned by a small eps or by near-duplicate landmarks (the pages'
+    solver ablation, reproduced on synthetic inputs).  Per condition and step
+    count T, for each solver, on the GPU (float32, the library's own W, X, Y
+    and B V from the debug form) and in float64 on the same W and B V (the
+    oracle's solvers): the relative residual of the solve, ||W Y - B V|| /
+    ||B V||, the quantity the output depends on.  One JSON line each."""
+    import dataclasses
+
+    import torch
+    import laplacian_nystr_approximation_amd as L
+    import oracle
+    from lapnys_inputs import make_inputs
+
+    dev = torch.device("cuda:0")
+    base = dataclasses.replace(WORKLOADS["stage1_56x56_f32"], B=4, name="study_56x56_f32")
+    x = make_inputs(base)
+    rng = np.random.Generator(np.random.PCG64(7))
+    conditions = [("eps=1e-1", 1e-1, None), ("eps=1e-3", 1e-3, None),
+                  ("eps=1e-3, near-duplicate landmarks (delta=1e-2)", 1e-3, 1e-2),
+                  ("eps=1e-5, near-duplicate landmarks (delta=1e-3)", 1e-5, 1e-3),
+                  ("eps=1e-6, near-duplicate landmarks (delta=1e-4)", 1e-6, 1e-4)]
+    steps = (4, 8, 12, 16, 20, 24, 32, 48)
+    P, m = base.P, base.m
+    for label, eps, delta in conditions:
+        k32 = x.k if delta is None else near_duplicate_keys(x.k, base, delta, rng)
+        q, k, v = (torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev) for a in (x.q, k32, x.v))
+        kappa = None
+        for solver in ("ns", "cg"):
+            for T in steps:
+                w = dataclasses.replace(base, eps=eps, ns_iters=T, solver=solver)
+                params = L.params_for(w)
+                ws = torch.empty(L.lapnys_workspace_size(params), dtype=torch.uint8, device=dev)
+                out = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
+                dbg = {"W": torch.empty((P, m, m), device=dev), "X": torch.zeros((P, m, m), device=dev),
+                       "Y": torch.empty((P, m, w.d), device=dev), "BV": torch.empty((P, m, w.d), device=dev)}
+                L.lapnys_forward_debug(q, k, v, out, params, ws, dbg)
+                W_, Y_, BV_ = (dbg[key].cpu().double().numpy() for key in ("W", "Y", "BV"))
+                gpu_res, f64_res = [], []
+                for p_ in range(P):
+                    nb = np.linalg.norm(BV_[p_])
+                    gpu_res.append(float(np.linalg.norm(W_[p_] @ Y_[p_] - BV_[p_]) / nb))
+                    if solver == "ns":
+                        y64 = oracle.newton_schulz_inverse(W_[p_], T) @ BV_[p_]
+                    else:
+                        y64 = oracle.conjugate_gradient(W_[p_], BV_[p_], T)
+                    f64_res.append(float(np.linalg.norm(W_[p_] @ y64 - BV_[p_]) / nb))
+                if kappa is None:
+                    ev = [np.linalg.eigvalsh(W_[p_]) for p_ in range(P)]
+                    kappa = [float(e[-1] / e[0]) for e in ev]
+                print(json.dumps({"condition": label, "solver": solver, "steps": T,
+                                  "gpu_rel_residual_max": max(gpu_res), "f64_rel_residual_max": max(f64_res),
+                                  "kappa_W": [min(kappa), max(kappa)], "finite": bool(np.isfinite(Y_).all())}),
+                      flush=True)
+                del ws, out, dbg
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -261,6 +334,11 @@ def main(argv=None):
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--kernel", default="laplacian", choices=("laplacian", "gaussian"),
                     help="gaussian: the Gaussian-kernel variant of the same forward (LAPNYS_GAUSSIAN)")
+    ap.add_argument("--solver", default="ns", choices=("ns", "cg"),
+                    help="cg: the conjugate-gradient solver variant (LAPNYS_SOLVER_CG)")
+    ap.add_argument("--solver-study", action="store_true",
+                    help="instead of the bench line: solve residual against steps, Newton-Schulz and CG, on "
+                         "ill-conditioned W (small eps, near-duplicate landmarks), GPU and float64")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0: skip)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the bench line: warm and cold single-call times and peak memory over the "
@@ -271,14 +349,16 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.sweep:
         return sweep_main(args)
+    if args.solver_study:
+        return solver_study_main(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this forward has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         return 2
     w = WORKLOADS[args.workload]
-    if args.kernel != "laplacian":
+    if args.kernel != "laplacian" or args.solver != "ns":
         import dataclasses
-        w = dataclasses.replace(w, kernel=args.kernel)
+        w = dataclasses.replace(w, kernel=args.kernel, solver=args.solver)
     x = make_inputs(w)
 
     # The CPU leg runs before the GPU is touched.
@@ -372,10 +452,11 @@ def main(argv=None):
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["kernel_ms"] = kernel_ms
     roof["kernel_ms_samples"] = f"HIP events on every {EVERY}th timed step ({len(sampled)} of {K})"
-    if w.name == HEADLINE and not gauss:
+    if w.name == HEADLINE and not gauss and w.solver == "ns":
         metric = HEADLINE_METRIC
     else:
-        metric = f"attention tokens/s ({w.name}{', Gaussian kernel' if gauss else ''})"
+        variant = (", Gaussian kernel" if gauss else "") + (", CG solver" if w.solver == "cg" else "")
+        metric = f"attention tokens/s ({w.name}{variant})"
     line = {
         "metric": metric,
         "value": tokens / (ms_step * 1e-3),
@@ -391,7 +472,7 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "grid": [w.grid_h, w.grid_w], "N": w.N, "d": w.d,
                    "pool": w.pool, "m": w.m, "input_dtype": w.dtype, "lambda": w.lam, "eps": w.eps,
-                   "ns_iters": w.ns_iters, "whiten": w.whiten, "kernel": w.kernel},
+                   "ns_iters": w.ns_iters, "whiten": w.whiten, "kernel": w.kernel, "solver": w.solver},
         "roofline": roof,
         "cpu_baseline": cpu,
         "stage_ms": stage_ms,

@@ -176,19 +176,43 @@ def lapnys_workspace_size(params: lapnys_params) -> int:
     return n.value
 
 
+def _sizes_ok(params: lapnys_params, q, k, v, out, dbg=None) -> None:
+    """Tensor arguments (raw pointers pass unchecked) must hold at least the
+    elements the call reads or writes, with the element size of the declared
+    storage type: the library cannot see tensor sizes."""
+    P, N, d = params.B * params.H, params.N, params.d
+    m = (params.grid_h // max(params.pool, 1)) * (params.grid_w // max(params.pool, 1))
+    in_size = 2 if params.dtype == LAPNYS_BF16 else 4
+    need = {"q": (q, in_size, P * N * d), "k": (k, in_size, P * N * d), "v": (v, in_size, P * N * d),
+            "out": (out, 4, P * N * d)}
+    per = {"landmarks": P * m * d, "C_t": P * m * N, "W": P * m * m, "X": P * m * m, "BV": P * m * d,
+           "Y": P * m * d, "mu": P * m, "sigma": P * m}
+    for name, t in (dbg or {}).items():
+        need[name] = (t, 4, per[name])
+    for name, (t, size, count) in need.items():
+        if t is None or isinstance(t, int):
+            continue
+        if t.element_size() != size or t.numel() < count:
+            raise ValueError(f"{name}: expected at least {count} elements of {size} bytes, "
+                             f"got {t.numel()} of {t.element_size()}")
+
+
 def lapnys_forward_ws(q, k, v, out, params: lapnys_params, ws, stream=None) -> None:
+    _sizes_ok(params, q, k, v, out)
     wp, wn = _ws(ws)
     _check(_lib.lapnys_forward_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.byref(params), wp, wn,
                                   _stream(stream)), "lapnys_forward_ws")
 
 
 def lapnys_forward(q, k, v, out, params: lapnys_params, stream=None) -> None:
+    _sizes_ok(params, q, k, v, out)
     _check(_lib.lapnys_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.byref(params), _stream(stream)),
            "lapnys_forward")
 
 
 def lapnys_forward_debug(q, k, v, out, params: lapnys_params, ws, dbg: Dict[str, object], stream=None) -> None:
     """``dbg`` maps lapnys_debug field names to device tensors (missing = not written)."""
+    _sizes_ok(params, q, k, v, out, dbg)
     d = lapnys_debug(*[_ptr(dbg.get(name)) for name in DEBUG_FIELDS])
     wp, wn = _ws(ws)
     _check(_lib.lapnys_forward_debug(_ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.byref(params), wp, wn,
@@ -197,6 +221,7 @@ def lapnys_forward_debug(q, k, v, out, params: lapnys_params, ws, dbg: Dict[str,
 
 def lapnys_forward_profiled(q, k, v, out, params: lapnys_params, ws, events: Sequence[int], stream=None) -> None:
     """``events``: 2 * LAPNYS_NUM_STAGES raw hipEvent_t handles (see HipEvents)."""
+    _sizes_ok(params, q, k, v, out)
     arr = (ctypes.c_void_p * len(events))(*events)
     wp, wn = _ws(ws)
     _check(_lib.lapnys_forward_profiled(_ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.byref(params), wp, wn,

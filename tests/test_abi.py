@@ -119,6 +119,24 @@ def test_gaussian_flag_accepted():
         _p(kernel="cosine")
 
 
+def test_binding_checks_tensor_sizes():
+    """The binding refuses tensors whose element size or count does not match
+    the params (the library sees only pointers), before any device call."""
+    import torch
+    p = _p(B=1, H=1, dtype="f32")
+    n = 196 * 64
+    good = torch.zeros(n, dtype=torch.float32)
+    with pytest.raises(ValueError, match="q: expected"):
+        L.lapnys_forward_ws(torch.zeros(n, dtype=torch.float64), good, good, good, p, 0)
+    with pytest.raises(ValueError, match="out: expected"):
+        L.lapnys_forward_ws(good, good, good, torch.zeros(n - 1), p, 0)
+    with pytest.raises(ValueError, match="W: expected"):
+        L.lapnys_forward_debug(good, good, good, good, p, 0, {"W": torch.zeros(10)})
+    pb = _p(B=1, H=1, dtype="bf16")
+    with pytest.raises(ValueError, match="k: expected"):
+        L.lapnys_forward(torch.zeros(n, dtype=torch.int16), good, good, good, pb)
+
+
 def test_cg_flag():
     """LAPNYS_SOLVER_CG is a known flag, refused together with LAPNYS_NS_REFINE;
     at m <= 64 it uses the separate-launch layout (no in-LDS solver)."""

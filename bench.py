@@ -270,8 +270,9 @@ def near_duplicate_keys(k, w, delta, rng):
 def solver_study_main(args):
     """Residual against iterations, Newton-Schulz against CG, on W made
     ill-conditioned by a small eps or by near-duplicate landmarks (the pages'
-    solver ablation, reproduced on synthetic inputs).  Per condition and step
-    count T, for each solver, on the GPU (float32, the library's own W, X, Y
+    solver ablation, reproduced on synthetic inputs).  Solvers: "ns" (the
+    default m <= 64 schedule), "ns_plain" (LAPNYS_NS_PLAIN) and "cg".  Per
+    condition and step count T, for each solver, on the GPU (float32, the library's own W, X, Y
     and B V from the debug form) and in float64 on the same W and B V (the
     oracle's solvers): the relative residual of the solve, ||W Y - B V|| /
     ||B V||, the quantity the output depends on.  One JSON line each."""
@@ -296,9 +297,10 @@ def solver_study_main(args):
         k32 = x.k if delta is None else near_duplicate_keys(x.k, base, delta, rng)
         q, k, v = (torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev) for a in (x.q, k32, x.v))
         kappa = None
-        for solver in ("ns", "cg"):
+        for solver in ("ns", "ns_plain", "cg"):
             for T in steps:
-                w = dataclasses.replace(base, eps=eps, ns_iters=T, solver=solver)
+                w = dataclasses.replace(base, eps=eps, ns_iters=T, solver="cg" if solver == "cg" else "ns",
+                                        ns_plain=solver == "ns_plain")
                 params = L.params_for(w)
                 ws = torch.empty(L.lapnys_workspace_size(params), dtype=torch.uint8, device=dev)
                 out = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
@@ -310,7 +312,7 @@ def solver_study_main(args):
                 for p_ in range(P):
                     nb = np.linalg.norm(BV_[p_])
                     gpu_res.append(float(np.linalg.norm(W_[p_] @ Y_[p_] - BV_[p_]) / nb))
-                    if solver == "ns":
+                    if solver != "cg":
                         y64 = oracle.newton_schulz_inverse(W_[p_], T) @ BV_[p_]
                     else:
                         y64 = oracle.conjugate_gradient(W_[p_], BV_[p_], T)

@@ -76,8 +76,18 @@ typedef enum { LAPNYS_F32 = 0, LAPNYS_BF16 = 1 } lapnys_dtype;
  *   computed directly by ns_iters CG steps per column of B V, from Y0 = 0,
  *   without a preconditioner, in float32 (a column whose residual is exactly
  *   zero, or so small that p.(W p) underflows to zero, stops changing).  X is not formed: the debug form leaves its X
- *   buffer untouched.  Not combinable with LAPNYS_NS_REFINE. */
-enum { LAPNYS_WHITEN = 1u, LAPNYS_NS_REFINE = 2u, LAPNYS_GAUSSIAN = 4u, LAPNYS_SOLVER_CG = 8u };
+ *   buffer untouched.  Not combinable with LAPNYS_NS_REFINE.
+ * LAPNYS_NS_PLAIN: m <= 64 only (larger m always runs so): the Newton-Schulz
+ *   steps in the plain form, X <- X (2I - W X) with every entry formed on
+ *   float32 products, as a launch of its own beside the kernel-matrix stage.
+ *   The default schedule for m <= 64 runs inside the kernel-matrix launch,
+ *   takes most steps on bf16-split products and keeps X exactly symmetric by
+ *   storing one triangle of X (W X) with its mirror; it reaches the float32
+ *   floor for cond(W) up to ~1e3, but a near-singular W (cond ~1e4 and more,
+ *   e.g. near-duplicate landmarks with a tiny eps) makes it stall or diverge
+ *   where the plain form converges.  Slower; same results otherwise. */
+enum { LAPNYS_WHITEN = 1u, LAPNYS_NS_REFINE = 2u, LAPNYS_GAUSSIAN = 4u, LAPNYS_SOLVER_CG = 8u,
+       LAPNYS_NS_PLAIN = 16u };
 
 /* Status codes. */
 enum {
@@ -109,7 +119,7 @@ typedef struct {
   int32_t ns_iters;      /* Newton-Schulz steps, >= 0 */
   int32_t dtype;         /* lapnys_dtype */
   uint32_t flags;        /* LAPNYS_WHITEN | LAPNYS_NS_REFINE | LAPNYS_GAUSSIAN |
-                            LAPNYS_SOLVER_CG, or 0 */
+                            LAPNYS_SOLVER_CG | LAPNYS_NS_PLAIN, or 0 */
 } lapnys_params;
 
 /* Optional device buffers for the intermediates of one call (debug form).

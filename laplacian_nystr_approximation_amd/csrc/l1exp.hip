@@ -296,8 +296,8 @@ hipError_t launch_fused(const Plan& pl, const void* q, const void* k, const void
 template <typename T, int D>
 hipError_t launch_typed(const Plan& pl, const void* q, const void* k, const void* v, Work& w, hipStream_t s,
                         Span t) {
-  if (pl.fused_ns) return launch_fused<T, D>(pl, q, k, v, w, s, t);
-  // m > 64: landmark blocks of 32 (two row blocks); the solver runs on its own.
+  if (pl.ns_in_launch) return launch_fused<T, D>(pl, q, k, v, w, s, t);
+  // Landmark blocks of (at most) 32, two row blocks; the solver runs on its own.
   return launch_kernel<T, D, 2, 0>(pl, q, k, v, w, s, t);
 }
 

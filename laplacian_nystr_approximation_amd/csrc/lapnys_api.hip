@@ -51,7 +51,8 @@ int validate(const lapnys_params* p) {
   if (!(isfinite(p->lambda) && p->lambda > 0.f)) return LAPNYS_ERR_INVALID_ARG;
   if (!(isfinite(p->eps) && p->eps >= 0.f)) return LAPNYS_ERR_INVALID_ARG;
   if (p->ns_iters < 0) return LAPNYS_ERR_INVALID_ARG;
-  if (p->flags & ~(uint32_t)(LAPNYS_WHITEN | LAPNYS_NS_REFINE | LAPNYS_GAUSSIAN | LAPNYS_SOLVER_CG))
+  if (p->flags &
+      ~(uint32_t)(LAPNYS_WHITEN | LAPNYS_NS_REFINE | LAPNYS_GAUSSIAN | LAPNYS_SOLVER_CG | LAPNYS_NS_PLAIN))
     return LAPNYS_ERR_INVALID_ARG;
   if ((p->flags & LAPNYS_SOLVER_CG) && (p->flags & LAPNYS_NS_REFINE)) return LAPNYS_ERR_INVALID_ARG;
   if (p->dtype != LAPNYS_F32 && p->dtype != LAPNYS_BF16) return LAPNYS_ERR_UNSUPPORTED;
@@ -90,12 +91,15 @@ int make_plan(const lapnys_params* p, Plan* pl) {
   // kernel-matrix launch for the Laplacian form, a launch of its own beside
   // it for the Gaussian form).
   P.fused_ns = P.m <= lapnys::kFusedNsMaxM && !P.cg;
+  // The in-launch schedule is the Laplacian default; the Gaussian form and
+  // LAPNYS_NS_PLAIN run the plain steps as a launch of their own.
+  P.ns_in_launch = P.fused_ns && !P.gaussian && !(p->flags & LAPNYS_NS_PLAIN);
   P.mp = P.fused_ns ? 64 : ((P.m + 63) / 64) * 64;
   P.tt = 256;
   P.ntiles = (P.N + P.tt - 1) / P.tt;
   // Landmark blocks: all m <= 64 landmarks in one block beside the in-LDS
   // solver, else blocks of 32.
-  P.lb = P.fused_ns ? P.m : (P.m < 32 ? P.m : 32);
+  P.lb = P.ns_in_launch || (P.fused_ns && P.gaussian) ? P.m : (P.m < 32 ? P.m : 32);
   P.jblocks = (P.m + P.lb - 1) / P.lb;
   // Tiles per workgroup: enough workgroups to fill the chip several times,
   // few enough that the B V partials stay small.
@@ -218,7 +222,7 @@ int run(const Plan& pl, const void* q, const void* k, const void* v, float* out,
   auto mark = [&](int idx) { return !ev || !ev[idx] || ok(hipEventRecord(ev[idx], s), "hipEventRecord"); };
   const lapnys::Span fin = span(LAPNYS_STAGE_FINALIZE);
 
-  if (pl.fused_ns && !pl.gaussian) {
+  if (pl.ns_in_launch) {
     // m <= 64: one stream; the solver runs inside the kernel-matrix launch,
     // and its stage events bracket that launch.
     if (!ok(lapnys::launch_pool(pl, k, W, s, span(LAPNYS_STAGE_POOL)), "pool launch")) return LAPNYS_ERR_HIP;
@@ -232,8 +236,8 @@ int run(const Plan& pl, const void* q, const void* k, const void* v, float* out,
     return LAPNYS_OK;
   }
 
-  // m > 64, and the Gaussian form at every m: the solver's launches run on a
-  // library-owned stream beside the kernel-matrix stage.  The pool stage runs
+  // Otherwise (m > 64, the Gaussian form, the plain steps, CG): the solver's
+  // launches run on a library-owned stream beside the kernel-matrix stage.  The pool stage runs
   // on that stream ahead of them and the caller's stream waits for it, so the
   // solver is dispatched first.
   std::lock_guard<std::mutex> lock(g_ctx_mu);
@@ -254,8 +258,8 @@ int run(const Plan& pl, const void* q, const void* k, const void* v, float* out,
           "kernel-matrix launch"))
     return LAPNYS_ERR_HIP;
   if (pl.fused_ns) {
-    // m <= 64 (Gaussian form): the reductions also form Y = X (B V), so they
-    // wait for the solver.
+    // m <= 64 (a solver launch of its own): the reductions also form
+    // Y = X (B V), so they wait for the solver.
     if (!ok(hipStreamWaitEvent(s, dc->join, 0), "hipStreamWaitEvent")) return LAPNYS_ERR_HIP;
     if (!ok(lapnys::launch_reduce(pl, W, s, fin), "reduce launch")) return LAPNYS_ERR_HIP;
   } else if (pl.cg) {

@@ -89,7 +89,8 @@ struct Plan {
   float scale;      // -log2(e) / lambda, so k = exp2(scale * L1)
   float eps;
   int mp;           // padded Newton-Schulz size (64, or m rounded up to 64)
-  bool fused_ns;    // m <= kFusedNsMaxM: one workgroup per problem
+  bool fused_ns;    // m <= kFusedNsMaxM: one workgroup per problem (64 x 64 padded X)
+  bool ns_in_launch;  // ... inside the kernel-matrix launch (the Laplacian default)
   int tt;           // tokens per tile of the kernel-matrix stage (256 or 128)
   int ntiles;       // token tiles per problem
   int lb;           // landmarks per block of the kernel-matrix stage

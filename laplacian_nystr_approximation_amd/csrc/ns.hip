@@ -264,18 +264,20 @@ __global__ __launch_bounds__(256) void residual_kernel(const float* __restrict__
   }
 }
 
-// m <= 64, Gaussian form: W, alpha, X0 and the steps X <- X (2I - W X) of
-// one problem per workgroup, with W and the iterates in LDS (64 x 64, zero
-// padded).  W's entries are formed as in wbuild_big_kernel (squared
-// differences over even and odd features, in increasing order, so W is
-// bit-symmetric, and the diagonal is 1 + eps) and written out; alpha = (max
+// m <= 64, Gaussian form or the plain steps (LAPNYS_NS_PLAIN): W, alpha, X0
+// and the steps X <- X (2I - W X) of one problem per workgroup, with W and
+// the iterates in LDS (64 x 64, zero padded).  W's entries are formed as in
+// wbuild_big_kernel (squared or absolute differences over even and odd
+// features, in increasing order, so W is bit-symmetric, and the diagonal is
+// 1 + eps) and written out; alpha = (max
 // column sum)^2 and X0 = W / alpha as in alpha_x0_kernel.  The steps take the
 // tiled steps' form: T = 2I - W X in full, then X T, float32 products on fp32
 // MFMA 16x16x4 over k in [0, kext).  (The in-LDS schedule of the Laplacian form keeps X
 // exactly symmetric by mirroring one triangle of X (W X); for an iterate that
 // is still far from converged after the fixed step count, as a Gaussian W
 // often leaves it, the mirrored rounding errors cost about 6x in the output's
-// agreement with the float64 iteration, so this form keeps every entry.)
+// agreement with the float64 iteration, and for a near-singular W they stall
+// or diverge the iteration, so this form keeps every entry.)
 //
 // Eight wavefronts: wavefront v forms block row v / 2 and column blocks
 // 2 (v % 2) + [0, 2) of each product.  The reduction index is permuted so
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(256) void residual_kernel(const float* __restrict__
 // copies of W (symmetric), X, X^T and T^T.  X is double-buffered (two
 // wavefronts share a block row); X^T and T^T are rewritten only after every
 // wavefront has passed the barrier behind their last reads.
-template <int D>
+template <int D, bool GAUSS>
 __global__ __launch_bounds__(512) void ns_plain_kernel(const float* __restrict__ kt, float* __restrict__ w,
                                                        float* __restrict__ x, int m, float scale, float eps, int kext,
                                                        int iters) {
@@ -332,8 +334,13 @@ __global__ __launch_bounds__(512) void ns_plain_kernel(const float* __restrict__
 #pragma unroll
       for (int t = 0; t < D; t += 2) {
         const float e0 = tt[a * kS + t] - kb[t], e1 = tt[a * kS + t + 1] - kb[t + 1];
-        s0 = fmaf(e0, e0, s0);
-        s1 = fmaf(e1, e1, s1);
+        if constexpr (GAUSS) {
+          s0 = fmaf(e0, e0, s0);
+          s1 = fmaf(e1, e1, s1);
+        } else {
+          s0 += fabsf(e0);
+          s1 += fabsf(e1);
+        }
       }
       float val = 0.f;
       if (a < m && b < m) {
@@ -451,11 +458,13 @@ __global__ __launch_bounds__(256) void extract_square_kernel(const float* __rest
 hipError_t launch_ns(const Plan& pl, Work& wk, hipStream_t s, Span t) {
   const int kext = (pl.m + 31) & ~31;
   if (pl.fused_ns) {
-    // m <= 64: the Laplacian form runs inside the kernel-matrix launch
-    // (launch_l1exp); the Gaussian form runs one workgroup per problem here.
-    // kext (m rounded up to 32) is a multiple of 16, as the operand reads need.
-    if (!pl.gaussian) return hipErrorInvalidValue;
-    auto kern = pl.d == 64 ? ns_plain_kernel<64> : ns_plain_kernel<32>;
+    // m <= 64: the default Laplacian schedule runs inside the kernel-matrix
+    // launch (launch_l1exp); the plain steps run one workgroup per problem
+    // here.  kext (m rounded up to 32) is a multiple of 16, as the operand
+    // reads need.
+    if (pl.ns_in_launch) return hipErrorInvalidValue;
+    auto kern = pl.d == 64 ? (pl.gaussian ? ns_plain_kernel<64, true> : ns_plain_kernel<64, false>)
+                           : (pl.gaussian ? ns_plain_kernel<32, true> : ns_plain_kernel<32, false>);
     hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                          (int)kPlainLds);
     if (err != hipSuccess) return err;

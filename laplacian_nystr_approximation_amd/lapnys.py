@@ -22,6 +22,7 @@ LAPNYS_WHITEN = 1
 LAPNYS_NS_REFINE = 2
 LAPNYS_GAUSSIAN = 4
 LAPNYS_SOLVER_CG = 8
+LAPNYS_NS_PLAIN = 16
 
 LAPNYS_OK = 0
 LAPNYS_ERR_INVALID_ARG = -1
@@ -106,11 +107,14 @@ def library():
 
 
 def make_params(*, B, H, grid_h, grid_w, d, pool, lam=4.0, eps=1e-3, ns_iters=20, dtype="f32",
-                whiten=True, refine=False, kernel="laplacian", solver="ns", N=None) -> lapnys_params:
+                whiten=True, refine=False, kernel="laplacian", solver="ns", ns_plain=False,
+                N=None) -> lapnys_params:
     """Build a lapnys_params; ``dtype`` is "f32"/"bf16" or the enum value;
     ``refine`` sets LAPNYS_NS_REFINE (one float64-residual correction of the
     Newton-Schulz result); ``kernel`` is "laplacian" or "gaussian"
-    (LAPNYS_GAUSSIAN); ``solver`` is "ns" or "cg" (LAPNYS_SOLVER_CG)."""
+    (LAPNYS_GAUSSIAN); ``solver`` is "ns" or "cg" (LAPNYS_SOLVER_CG);
+    ``ns_plain`` sets LAPNYS_NS_PLAIN (the plain float32 Newton-Schulz steps
+    for m <= 64)."""
     if kernel not in ("laplacian", "gaussian"):
         raise ValueError(f"unknown kernel {kernel!r}")
     if solver not in ("ns", "cg"):
@@ -119,14 +123,15 @@ def make_params(*, B, H, grid_h, grid_w, d, pool, lam=4.0, eps=1e-3, ns_iters=20
     return lapnys_params(B, H, grid_h * grid_w if N is None else N, d, grid_h, grid_w, pool,
                          lam, eps, ns_iters, dt,
                          (LAPNYS_WHITEN if whiten else 0) | (LAPNYS_NS_REFINE if refine else 0)
-                         | (LAPNYS_GAUSSIAN if kernel == "gaussian" else 0) | (LAPNYS_SOLVER_CG if solver == "cg" else 0))
+                         | (LAPNYS_GAUSSIAN if kernel == "gaussian" else 0) | (LAPNYS_SOLVER_CG if solver == "cg" else 0)
+                         | (LAPNYS_NS_PLAIN if ns_plain else 0))
 
 
 def params_for(w) -> lapnys_params:
     """lapnys_params for a ``lapnys_inputs.Workload``."""
     return make_params(B=w.B, H=w.H, grid_h=w.grid_h, grid_w=w.grid_w, d=w.d, pool=w.pool, lam=w.lam,
                        eps=w.eps, ns_iters=w.ns_iters, dtype=w.dtype, whiten=w.whiten,
-                       refine=w.refine, kernel=w.kernel, solver=w.solver)
+                       refine=w.refine, kernel=w.kernel, solver=w.solver, ns_plain=w.ns_plain)
 
 
 def _ptr(x) -> Optional[int]:

@@ -43,6 +43,7 @@ class Workload:
     refine: bool = False  # one float64-residual correction after the Newton-Schulz steps
     kernel: str = "laplacian"  # or "gaussian"
     solver: str = "ns"  # or "cg" (conjugate gradient for W^-1 (B V))
+    ns_plain: bool = False  # m <= 64: the plain float32 Newton-Schulz steps, a launch of their own
 
     @property
     def N(self) -> int:

@@ -90,7 +90,7 @@ def test_invalid_params_rejected(kw, code):
 
 def test_unknown_flag_bits_rejected():
     p = _p()
-    p.flags = 16
+    p.flags = 32
     assert L.library().lapnys_landmark_count(ctypes.byref(p)) == B.LAPNYS_ERR_INVALID_ARG
 
 
@@ -135,6 +135,14 @@ def test_binding_checks_tensor_sizes():
     pb = _p(B=1, H=1, dtype="bf16")
     with pytest.raises(ValueError, match="k: expected"):
         L.lapnys_forward(torch.zeros(n, dtype=torch.int16), good, good, good, pb)
+
+
+def test_plain_ns_flag():
+    """LAPNYS_NS_PLAIN is a known flag; at m <= 64 it needs no other workspace."""
+    pl = _p(ns_plain=True)
+    assert pl.flags == B.LAPNYS_WHITEN | B.LAPNYS_NS_PLAIN
+    assert L.library().lapnys_landmark_count(ctypes.byref(pl)) == 49
+    assert L.lapnys_workspace_size(pl) == L.lapnys_workspace_size(_p())
 
 
 def test_cg_flag():

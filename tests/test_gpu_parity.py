@@ -177,6 +177,32 @@ def test_cg_parity(w):
          f"CG relative residual {max(report['cg_residual']):.2e} (float64 CG: {max(own):.2e})")
 
 
+def _plain_cases():
+    base = dict(B=1, H=2, lam=4.0, eps=1e-3, ns_iters=20, seed_index=70, ns_plain=True)
+    c = lambda name: dataclasses.replace(WORKLOADS[name], name=name + "_plain", ns_plain=True)
+    return [
+        c("tiny_f32"), c("stage1_56x56_f32"), c("stage1_56x56_bf16"), c("stage3_14x14_bf16"),
+        Workload("plain_ragged_18x14_p2", grid_h=18, grid_w=14, d=64, pool=2, dtype="f32", **base),
+        Workload("plain_ragged_10x30_p5_d32", grid_h=10, grid_w=30, d=32, pool=5, dtype="bf16", **base),
+        Workload("plain_single_landmark_6x6", grid_h=6, grid_w=6, d=64, pool=6, dtype="f32", **base),
+        Workload("plain_refine_14x14", grid_h=14, grid_w=14, d=64, pool=2, dtype="f32", refine=True, **base),
+    ]
+
+
+@pytest.mark.parametrize("w", _plain_cases(), ids=lambda w: w.name)
+def test_plain_ns_parity(w):
+    """LAPNYS_NS_PLAIN (m <= 64: the plain float32 steps as a launch of their
+    own) against the oracle, every stage and the residual gate."""
+    _say(f"[plain] {w.name} P={w.P} N={w.N} m={w.m} d={w.d} {w.dtype} T={w.ns_iters}")
+    x = workload_inputs(w)
+    gpu = run_gpu(w, x)
+    ref = run_oracle(w, x)
+    report = {}
+    for p in range(w.P):
+        check_problem(w, gpu, p, ref, p, report=report)
+    _say(f"[plain] {w.name}: O normwise {max(report['o_normwise']):.2e}, NS residual {max(report['ns_residual']):.2e}")
+
+
 def _edge_cases():
     base = dict(B=1, H=2, lam=4.0, eps=1e-3, ns_iters=20, seed_index=40)
     cases = [

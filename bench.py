@@ -33,7 +33,7 @@ EVERY = 4  # timed steps per kernel-duration sample
 # and WRITE_SIZE passes, scaled by a copy kernel of known size).  Reported only
 # while the kernel's sources hash to the value recorded with the counters.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "l1exp_kernel_stage1_56x56_bf16_hbm_traffic.md")
-KERNEL_SOURCES = ("l1exp.hip", "ns_small.hpp", "lapnys_internal.hpp", "lapnys_api.hip")
+KERNEL_SOURCES = ("l1exp.hip", "kmat_tile.hpp", "ns_small.hpp", "lapnys_internal.hpp", "lapnys_api.hip")
 
 # MI355X figures: 256 CUs at 2.4 GHz; published fp32 vector peak 157.3 TFLOP/s,
 # i.e. 78.6e12 fp32 lane-instructions/s counting an FMA as two flops:

@@ -328,6 +328,44 @@ def solver_study_main(args):
     return 0
 
 
+def backward_main(args):
+    """The backward pass (lapnys_backward_ws: the forward, then the gradients of
+    sum(dO * O) with respect to Q, K, V) on the bench workload: warm-up, then
+    K timed calls; one JSON line with tokens/s of forward + backward."""
+    import torch
+    import laplacian_nystr_approximation_amd as L
+    from lapnys_inputs import make_grad_out, make_inputs
+
+    w = WORKLOADS[args.workload]
+    x = make_inputs(w)
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if w.dtype == "bf16" else a).to(dev)
+
+    q, k, v = up(x.q), up(x.k), up(x.v)
+    dout = torch.from_numpy(make_grad_out(w)).to(dev)
+    dq, dk, dv = (torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev) for _ in range(3))
+    params = L.params_for(w)
+    ws = torch.empty(L.lapnys_backward_workspace_size(params), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        L.lapnys_backward_ws(q, k, v, dout, dq, dk, dv, params, ws, stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        L.lapnys_backward_ws(q, k, v, dout, dq, dk, dv, params, ws, stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    print(json.dumps({"metric": f"attention forward+backward tokens/s ({w.name})",
+                      "value": w.P * w.N / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+                      "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "dtype": "f32",
+                      "data": "synthetic", "config": {"workload": w.name, "N": w.N, "m": w.m, "d": w.d, "P": w.P,
+                                                       "input_dtype": w.dtype}}), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -338,6 +376,8 @@ def main(argv=None):
                     help="gaussian: the Gaussian-kernel variant of the same forward (LAPNYS_GAUSSIAN)")
     ap.add_argument("--solver", default="ns", choices=("ns", "cg"),
                     help="cg: the conjugate-gradient solver variant (LAPNYS_SOLVER_CG)")
+    ap.add_argument("--backward", action="store_true",
+                    help="instead of the bench line: forward + backward (lapnys_backward_ws) on the workload")
     ap.add_argument("--solver-study", action="store_true",
                     help="instead of the bench line: solve residual against steps, Newton-Schulz and CG, on "
                          "ill-conditioned W (small eps, near-duplicate landmarks), GPU and float64")
@@ -353,6 +393,8 @@ def main(argv=None):
         return sweep_main(args)
     if args.solver_study:
         return solver_study_main(args)
+    if args.backward:
+        return backward_main(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this forward has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)

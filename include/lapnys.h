@@ -196,6 +196,21 @@ int lapnys_forward_profiled(const void* q, const void* k, const void* v, float* 
                             const lapnys_params* p, void* ws, size_t ws_bytes,
                             hipEvent_t* stage_events, hipStream_t stream);
 
+/* Backward pass (EN section 3: the kernels serve forward and backward): the
+ * gradients of sum(dout * O) with respect to q, k and v, where O is the
+ * forward's output for the same inputs and params.  The call runs the forward
+ * itself (into the workspace; dq holds O until it is overwritten) and then the
+ * backward kernels.  The inverse enters as X = W^-1 (dW = -X^T dX X^T, with X
+ * the Newton-Schulz result).  Supported: m <= 64, the Laplacian kernel, the
+ * Newton-Schulz solver (with or without LAPNYS_NS_REFINE / LAPNYS_NS_PLAIN);
+ * otherwise LAPNYS_ERR_UNSUPPORTED.  dout: device float32 [B,H,N,d]; dq, dk,
+ * dv: device float32 [B,H,N,d] outputs; all 16-byte aligned, the outputs
+ * overlapping neither each other, the inputs nor ws.  ws: at least
+ * lapnys_backward_workspace_size bytes, 256-byte aligned. */
+int lapnys_backward_workspace_size(const lapnys_params* p, size_t* bytes);
+int lapnys_backward_ws(const void* q, const void* k, const void* v, const float* dout, float* dq, float* dk,
+                       float* dv, const lapnys_params* p, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Frees the library-owned workspaces of lapnys_forward (all devices).
  * Synchronises each device that had one. */
 void lapnys_release(void);

@@ -1,4 +1,4 @@
-"""MI355X-native forward pass of LaplacianFormer's Laplacian-kernel Nystrom attention.
+"""MI355X-native forward (and backward) pass of LaplacianFormer's Laplacian-kernel Nystrom attention.
 
 The computation lives in the HIP library ``liblapnys.so`` (C ABI in
 ``include/lapnys.h``); ``laplacian_nystr_approximation_amd.lapnys`` is its
@@ -13,7 +13,7 @@ _BINDING_NAMES = {
     "HipEvents", "LapnysError", "lapnys_debug", "lapnys_params", "lapnys_forward", "lapnys_forward_ws",
     "lapnys_forward_debug", "lapnys_forward_profiled", "lapnys_landmark_count", "lapnys_workspace_size",
     "lapnys_release", "lapnys_status_string", "make_params", "params_for", "library", "LIB_PATH",
-    "DEBUG_FIELDS", "STAGE_NAMES", "LAPNYS_NUM_STAGES",
+    "DEBUG_FIELDS", "STAGE_NAMES", "LAPNYS_NUM_STAGES", "lapnys_backward_ws", "lapnys_backward_workspace_size",
 }
 
 

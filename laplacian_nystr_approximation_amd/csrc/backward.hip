@@ -1,0 +1,356 @@
+// Backward pass of the Laplacian-kernel Nystrom attention (the pages' kernels
+// serve the forward and the backward pass: EN page, section 3; the L1 kernel's
+// gradient stays away from zero near coincident points: EN section 2.A).  The
+// gradients of sum(dO * O) with respect to Q, K and V, for m <= 64, after a
+// forward call has filled the workspace.  X stands for W^-1 in the derivative
+// (the implicit reading: dW = -X^T dX X^T), which the converged Newton-Schulz
+// iterate approximates.  Per problem, with Z = (C - mu) / sigma, Y = X (B V),
+// O = Z Y, g = dO:
+//
+//   dY = Z^T g = (C^T g - mu (1^T g)) / sigma
+//   dC_ij = (g_i . Y_j - a_j - Z_ij b_j) / sigma_j,
+//       a_j = (1^T g) . Y_j / N,  b_j = Y_j . dY_j / N   (the whitening backward)
+//   G = dC (.) C;  dQ_i = -(1/lambda) sum_j G_ij sign(q_i - K~_j)
+//   dBV = X^T dY;  dX = dY BV^T;  dW = -X^T dX X^T
+//   H_jn = (dBV_j . v_n) B_jn;  dV_n = sum_j B_jn dBV_j
+//   dK_n = (1/lambda) sum_j H_jn sign(K~_j - k_n) + dK~_{j(n)} / pool^2
+//   dK~_j = (1/lambda) [sum_i G_ij sign(q_i - K~_j) - sum_n H_jn sign(K~_j - k_n)
+//                       - sum_b (dW_jb + dW_bj) W'_jb sign(K~_j - K~_b)]
+//
+// (W' = W without eps.)  With whitening off, mu = 0, 1/sigma = 1 and a = b = 0.
+// Every kernel is a plain loop in float32 with a fixed order; the token-side
+// kernels take one lane per token, the landmark-side ones one lane per
+// (landmark, feature).
+#include "lapnys_internal.hpp"
+
+namespace lapnys {
+
+namespace {
+
+constexpr int kBT = 256;  // tokens per tile of the token-side kernels
+
+__device__ __forceinline__ float sgn(float x) { return x > 0.f ? 1.f : (x < 0.f ? -1.f : 0.f); }
+
+template <typename T, int D>
+__device__ __forceinline__ void load_row(const T* __restrict__ src, float (&x)[D]) {
+#pragma unroll
+  for (int t = 0; t < D; ++t) x[t] = widen(src[t]);
+}
+
+// Partial C^T g and 1^T g over one tile of tokens: part[p][tile][j][f],
+// spart[p][tile][f].  Thread (jg, f): feature f, landmarks jg, jg + G, ...
+template <int D>
+__global__ __launch_bounds__(256) void bwd_ctg_kernel(const float* __restrict__ ct, int ldc,
+                                                      const float* __restrict__ dout, float* __restrict__ part,
+                                                      float* __restrict__ spart, int N, int m, int ntiles) {
+  __shared__ float cs[64 * kBT];  // C^T rows of the tile, [j][i]
+  constexpr int G = 256 / D;
+  const int tile = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
+  const int t0 = tile * kBT, nv = min(kBT, N - t0);
+  for (int e = tid; e < m * kBT; e += 256) {
+    const int j = e / kBT, i = e % kBT;
+    cs[e] = i < nv ? ct[((size_t)p * m + j) * ldc + t0 + i] : 0.f;
+  }
+  __syncthreads();
+  const int f = tid % D, jg = tid / D;
+  const float* g = dout + ((size_t)p * N + t0) * D + f;
+  float acc[64 / G];
+#pragma unroll
+  for (int u = 0; u < 64 / G; ++u) acc[u] = 0.f;
+  float s = 0.f;
+  for (int i = 0; i < nv; ++i) {
+    const float gv = g[(size_t)i * D];
+    s += gv;
+#pragma unroll
+    for (int u = 0; u < 64 / G; ++u) {
+      const int j = jg + G * u;
+      if (j < m) acc[u] = fmaf(cs[j * kBT + i], gv, acc[u]);
+    }
+  }
+  float* pp = part + (((size_t)p * ntiles + tile) * m) * D;
+#pragma unroll
+  for (int u = 0; u < 64 / G; ++u) {
+    const int j = jg + G * u;
+    if (j < m) pp[(size_t)j * D + f] = acc[u];
+  }
+  if (jg == 0) spart[((size_t)p * ntiles + tile) * D + f] = s;
+}
+
+// LDS of bwd_small_kernel: X and the m x m scratch (stride 65), B V, dY and Y
+// (64 x D each), 1^T g (D).
+template <int D>
+constexpr size_t bwd_small_lds() {
+  return (size_t)(2 * 64 * 65 + 3 * 64 * D + D) * sizeof(float);
+}
+
+// Per problem (one workgroup): reduce the partials, then Y, dY, a, b, dBV and
+// dW = -X^T (dY BV^T) X^T, all m <= 64 in LDS.  x: the Newton-Schulz result,
+// row stride mp.  Outputs: y, dbv [P][m][D]; ab [P][2][m]; dw [P][m][m].
+template <int D>
+__global__ __launch_bounds__(256) void bwd_small_kernel(const float* __restrict__ part,
+                                                        const float* __restrict__ spart,
+                                                        const float* __restrict__ x, int mp,
+                                                        const float* __restrict__ bv, const float* __restrict__ mu,
+                                                        const float* __restrict__ rs, float* __restrict__ y,
+                                                        float* __restrict__ dbv, float* __restrict__ ab,
+                                                        float* __restrict__ dw, int N, int m, int ntiles,
+                                                        int whiten) {
+  extern __shared__ __align__(16) float lds[];
+  float* xs = lds;
+  float* tmp = xs + 64 * 65;
+  float* bvs = tmp + 64 * 65;
+  float* dys = bvs + 64 * D;
+  float* ys = dys + 64 * D;
+  float* ss = ys + 64 * D;
+  const int p = blockIdx.x, tid = threadIdx.x;
+  for (int e = tid; e < m * m; e += 256) xs[(e / m) * 65 + e % m] = x[(size_t)p * mp * mp + (e / m) * mp + e % m];
+  for (int e = tid; e < m * D; e += 256) bvs[e] = bv[(size_t)p * m * D + e];
+  for (int f = tid; f < D; f += 256) {
+    float s = 0.f;
+    for (int t = 0; t < ntiles; ++t) s += spart[((size_t)p * ntiles + t) * D + f];
+    ss[f] = s;
+  }
+  __syncthreads();
+  for (int e = tid; e < m * D; e += 256) {
+    const int j = e / D, f = e % D;
+    float c = 0.f;
+    for (int t = 0; t < ntiles; ++t) c += part[(((size_t)p * ntiles + t) * m) * D + e];
+    dys[e] = (c - mu[p * m + j] * ss[f]) * rs[p * m + j];
+    float yv = 0.f;
+    for (int kk = 0; kk < m; ++kk) yv = fmaf(xs[j * 65 + kk], bvs[kk * D + f], yv);
+    ys[e] = yv;
+    y[(size_t)p * m * D + e] = yv;
+  }
+  __syncthreads();
+  for (int j = tid; j < m; j += 256) {
+    float a = 0.f, b = 0.f;
+    for (int f = 0; f < D; ++f) {
+      a = fmaf(ss[f], ys[j * D + f], a);
+      b = fmaf(ys[j * D + f], dys[j * D + f], b);
+    }
+    ab[(size_t)p * 2 * m + j] = whiten ? a / (float)N : 0.f;
+    ab[(size_t)p * 2 * m + m + j] = whiten ? b / (float)N : 0.f;
+  }
+  // dBV = X^T dY
+  for (int e = tid; e < m * D; e += 256) {
+    const int kk = e / D, f = e % D;
+    float s = 0.f;
+    for (int j = 0; j < m; ++j) s = fmaf(xs[j * 65 + kk], dys[j * D + f], s);
+    dbv[(size_t)p * m * D + e] = s;
+  }
+  // tmp = dX = dY BV^T (m x m)
+  for (int e = tid; e < m * m; e += 256) {
+    const int j = e / m, kk = e % m;
+    float s = 0.f;
+    for (int f = 0; f < D; ++f) s = fmaf(dys[j * D + f], bvs[kk * D + f], s);
+    tmp[j * 65 + kk] = s;
+  }
+  __syncthreads();
+  // dW = -X^T dX X^T: R = X^T dX (each lane keeps its at most 16 entries in
+  // registers until every lane has read dX), then -R X^T.
+  float rv[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int e = tid + 256 * u;
+    float s = 0.f;
+    if (e < m * m) {
+      const int a = e / m, c = e % m;
+      for (int j = 0; j < m; ++j) s = fmaf(xs[j * 65 + a], tmp[j * 65 + c], s);
+    }
+    rv[u] = s;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int e = tid + 256 * u;
+    if (e < m * m) tmp[(e / m) * 65 + e % m] = rv[u];
+  }
+  __syncthreads();
+  for (int e = tid; e < m * m; e += 256) {
+    const int a = e / m, b = e % m;
+    float s = 0.f;
+    for (int c = 0; c < m; ++c) s = fmaf(tmp[a * 65 + c], xs[b * 65 + c], s);
+    dw[(size_t)p * m * m + e] = -s;
+  }
+}
+
+// Query side: one lane per token i of the tile.  G^T[p][j][i] is stored for
+// the landmark-side reduction; dq is written.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_q_kernel(const T* __restrict__ q, const float* __restrict__ dout,
+                                                    const float* __restrict__ kt, const float* __restrict__ ct,
+                                                    int ldc, const float* __restrict__ y,
+                                                    const float* __restrict__ mu, const float* __restrict__ rs,
+                                                    const float* __restrict__ ab, float* __restrict__ gt,
+                                                    float* __restrict__ dq, int N, int m, float inv_lam) {
+  __shared__ float kls[64 * D], yls[64 * D];
+  const int tile = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
+  for (int e = tid; e < m * D; e += 256) {
+    kls[e] = kt[(size_t)p * m * D + e];
+    yls[e] = y[(size_t)p * m * D + e];
+  }
+  __syncthreads();
+  const int i = tile * kBT + tid;
+  if (i >= N) return;
+  float qv[D], gv[D], dqv[D];
+  load_row<T, D>(q + ((size_t)p * N + i) * D, qv);
+  load_row<float, D>(dout + ((size_t)p * N + i) * D, gv);
+#pragma unroll
+  for (int t = 0; t < D; ++t) dqv[t] = 0.f;
+  for (int j = 0; j < m; ++j) {
+    float g = 0.f;
+#pragma unroll
+    for (int f = 0; f < D; ++f) g = fmaf(gv[f], yls[j * D + f], g);
+    const float c = ct[((size_t)p * m + j) * ldc + i];
+    const float r = rs[p * m + j];
+    const float z = (c - mu[p * m + j]) * r;
+    const float dc = (g - ab[(size_t)p * 2 * m + j] - z * ab[(size_t)p * 2 * m + m + j]) * r;
+    const float gg = dc * c;
+    gt[((size_t)p * m + j) * N + i] = gg;
+    const float w = -gg * inv_lam;
+#pragma unroll
+    for (int t = 0; t < D; ++t) dqv[t] = fmaf(w, sgn(qv[t] - kls[j * D + t]), dqv[t]);
+  }
+  float* dqp = dq + ((size_t)p * N + i) * D;
+#pragma unroll
+  for (int t = 0; t < D; ++t) dqp[t] = dqv[t];
+}
+
+// Key side: one lane per token n.  B recomputed; with DV false, H^T[p][j][n]
+// is stored and the B part of dk written; with DV true, dv is written (two
+// passes keep each lane's registers to two feature rows).
+template <typename T, int D, bool DV>
+__global__ __launch_bounds__(256) void bwd_k_kernel(const T* __restrict__ k, const T* __restrict__ v,
+                                                    const float* __restrict__ kt, const float* __restrict__ dbv,
+                                                    float* __restrict__ ht, float* __restrict__ dk,
+                                                    float* __restrict__ dv, int N, int m, float scale,
+                                                    float inv_lam) {
+  __shared__ float kls[64 * D], dls[64 * D];
+  const int tile = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
+  for (int e = tid; e < m * D; e += 256) {
+    kls[e] = kt[(size_t)p * m * D + e];
+    dls[e] = dbv[(size_t)p * m * D + e];
+  }
+  __syncthreads();
+  const int n = tile * kBT + tid;
+  if (n >= N) return;
+  float kv[D], acc[D];
+  load_row<T, D>(k + ((size_t)p * N + n) * D, kv);
+#pragma unroll
+  for (int t = 0; t < D; ++t) acc[t] = 0.f;
+  const T* vrow = v + ((size_t)p * N + n) * D;
+  for (int j = 0; j < m; ++j) {
+    float l1 = 0.f;
+#pragma unroll
+    for (int t = 0; t < D; ++t) l1 += fabsf(kls[j * D + t] - kv[t]);
+    const float b = exp2f(l1 * scale);
+    if constexpr (DV) {
+#pragma unroll
+      for (int t = 0; t < D; ++t) acc[t] = fmaf(b, dls[j * D + t], acc[t]);
+    } else {
+      float hd = 0.f;
+#pragma unroll
+      for (int t = 0; t < D; ++t) hd = fmaf(dls[j * D + t], widen(vrow[t]), hd);
+      const float h = hd * b;
+      ht[((size_t)p * m + j) * N + n] = h;
+      const float w = h * inv_lam;
+#pragma unroll
+      for (int t = 0; t < D; ++t) acc[t] = fmaf(w, sgn(kls[j * D + t] - kv[t]), acc[t]);
+    }
+  }
+  float* out = (DV ? dv : dk) + ((size_t)p * N + n) * D;
+#pragma unroll
+  for (int t = 0; t < D; ++t) out[t] = acc[t];
+}
+
+// Landmark side: one lane per (problem, landmark j, feature t).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_kt_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                     const float* __restrict__ kt, const float* __restrict__ gt,
+                                                     const float* __restrict__ ht, const float* __restrict__ w,
+                                                     int mp, const float* __restrict__ dw,
+                                                     float* __restrict__ dkt, int N, int m, float eps,
+                                                     float inv_lam, long long total) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int t = (int)(idx % D);
+  const long long rest = idx / D;
+  const int j = (int)(rest % m);
+  const int p = (int)(rest / m);
+  const float kj = kt[((size_t)p * m + j) * D + t];
+  const float* gr = gt + ((size_t)p * m + j) * N;
+  const float* hr = ht + ((size_t)p * m + j) * N;
+  const T* qc = q + (size_t)p * N * D + t;
+  const T* kc = k + (size_t)p * N * D + t;
+  float a = 0.f, b = 0.f;
+  for (int i = 0; i < N; ++i) {
+    a = fmaf(gr[i], sgn(widen(qc[(size_t)i * D]) - kj), a);
+    b = fmaf(hr[i], sgn(kj - widen(kc[(size_t)i * D])), b);
+  }
+  float c = 0.f;
+  for (int bb = 0; bb < m; ++bb) {
+    float wv = w[(size_t)p * mp * mp + (size_t)j * mp + bb];
+    if (bb == j) wv -= eps;
+    const float dws = dw[((size_t)p * m + j) * m + bb] + dw[((size_t)p * m + bb) * m + j];
+    c = fmaf(dws * wv, sgn(kj - kt[((size_t)p * m + bb) * D + t]), c);
+  }
+  dkt[((size_t)p * m + j) * D + t] = (a - b - c) * inv_lam;
+}
+
+// dk[p][n][t] += dK~[p][j(n)][t] / pool^2 (the pooling adjoint).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pool_kernel(const float* __restrict__ dkt, float* __restrict__ dk, int N,
+                                                       int m, int grid_w, int pool, int gw, long long total) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int t = (int)(idx % D);
+  const long long rest = idx / D;
+  const int n = (int)(rest % N);
+  const int p = (int)(rest / N);
+  const int r = n / grid_w, c = n % grid_w;
+  const int j = (r / pool) * gw + c / pool;
+  dk[idx] += dkt[((size_t)p * m + j) * D + t] / (float)(pool * pool);
+}
+
+template <typename T, int D>
+hipError_t launch_typed(const Plan& pl, const BwdWork& b, const Work& w, const void* q, const void* k,
+                        const void* v, const float* dout, float* dq, float* dk, float* dv, hipStream_t s) {
+  const int nt = (pl.N + kBT - 1) / kBT;
+  const float inv_lam = -pl.scale / 1.4426950408889634f;  // 1 / lambda from scale = -log2(e) / lambda
+  hipLaunchKernelGGL(bwd_ctg_kernel<D>, dim3(nt, pl.P), dim3(256), 0, s, w.ct, pl.ldc, dout, b.part, b.spart, pl.N,
+                     pl.m, nt);
+  constexpr size_t small_lds = bwd_small_lds<D>();
+  hipError_t e = hipFuncSetAttribute((const void*)bwd_small_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)small_lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_small_kernel<D>, dim3(pl.P), dim3(256), small_lds, s, b.part, b.spart, w.x_final, pl.mp,
+                     w.bv, w.mu, w.rs, b.y, b.dbv, b.ab, b.dw, pl.N, pl.m, nt, pl.whiten ? 1 : 0);
+  hipLaunchKernelGGL((bwd_q_kernel<T, D>), dim3(nt, pl.P), dim3(256), 0, s, (const T*)q, dout, w.kt, w.ct, pl.ldc,
+                     b.y, w.mu, w.rs, b.ab, b.gt, dq, pl.N, pl.m, inv_lam);
+  hipLaunchKernelGGL((bwd_k_kernel<T, D, false>), dim3(nt, pl.P), dim3(256), 0, s, (const T*)k, (const T*)v, w.kt,
+                     b.dbv, b.ht, dk, dv, pl.N, pl.m, pl.scale, inv_lam);
+  hipLaunchKernelGGL((bwd_k_kernel<T, D, true>), dim3(nt, pl.P), dim3(256), 0, s, (const T*)k, (const T*)v, w.kt,
+                     b.dbv, b.ht, dk, dv, pl.N, pl.m, pl.scale, inv_lam);
+  const long long lt = (long long)pl.P * pl.m * D;
+  hipLaunchKernelGGL((bwd_kt_kernel<T, D>), dim3((unsigned)((lt + 255) / 256)), dim3(256), 0, s, (const T*)q,
+                     (const T*)k, w.kt, b.gt, b.ht, w.w, pl.mp, b.dw, b.dkt, pl.N, pl.m, pl.eps, inv_lam, lt);
+  const long long tt = (long long)pl.P * pl.N * D;
+  hipLaunchKernelGGL(bwd_pool_kernel<D>, dim3((unsigned)((tt + 255) / 256)), dim3(256), 0, s, b.dkt, dk, pl.N, pl.m,
+                     pl.grid_w, pl.pool, pl.gw, tt);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward(const Plan& pl, const BwdWork& b, const Work& w, const void* q, const void* k,
+                           const void* v, const float* dout, float* dq, float* dk, float* dv, hipStream_t s) {
+  if (pl.m > 64) return hipErrorInvalidValue;
+  if (pl.dtype == 1) {
+    return pl.d == 64 ? launch_typed<uint16_t, 64>(pl, b, w, q, k, v, dout, dq, dk, dv, s)
+                      : launch_typed<uint16_t, 32>(pl, b, w, q, k, v, dout, dq, dk, dv, s);
+  }
+  return pl.d == 64 ? launch_typed<float, 64>(pl, b, w, q, k, v, dout, dq, dk, dv, s)
+                    : launch_typed<float, 32>(pl, b, w, q, k, v, dout, dq, dk, dv, s);
+}
+
+}  // namespace lapnys

@@ -308,6 +308,59 @@ int forward_impl(const void* q, const void* k, const void* v, float* out, const 
   return LAPNYS_OK;
 }
 
+// Backward buffers after the forward's workspace (each 256-byte aligned).
+int backward_plan(const lapnys_params* p, Plan* pl, size_t off[9], size_t* total) {
+  const int st = make_plan(p, pl);
+  if (st != LAPNYS_OK) return st;
+  if (pl->m > lapnys::kFusedNsMaxM || pl->cg || pl->gaussian) return LAPNYS_ERR_UNSUPPORTED;
+  const size_t f = sizeof(float), Pn = (size_t)pl->P, m = (size_t)pl->m, d = (size_t)pl->d, N = (size_t)pl->N;
+  const size_t nt = (N + 255) / 256;
+  const size_t sizes[9] = {Pn * nt * m * d * f, Pn * nt * d * f, Pn * m * d * f, Pn * m * d * f, Pn * 2 * m * f,
+                           Pn * m * m * f,      Pn * m * N * f,  Pn * m * N * f, Pn * m * d * f};
+  size_t o = pl->total;
+  for (int i = 0; i < 9; ++i) {
+    off[i] = o;
+    o = align256(o + sizes[i]);
+  }
+  *total = o;
+  return LAPNYS_OK;
+}
+
+int backward_impl(const void* q, const void* k, const void* v, const float* dout, float* dq, float* dk, float* dv,
+                  const lapnys_params* p, void* ws, size_t ws_bytes, hipStream_t s) {
+  Plan pl;
+  size_t off[9], total = 0;
+  int st = backward_plan(p, &pl, off, &total);
+  if (st != LAPNYS_OK) return st;
+  if (!dout || !dk || !dv || (((uintptr_t)dout | (uintptr_t)dk | (uintptr_t)dv) & 15)) return LAPNYS_ERR_INVALID_ARG;
+  // dq doubles as the forward's output buffer: the same checks apply to it.
+  st = check_buffers(q, k, v, dq, pl, ws, ws_bytes);
+  if (st != LAPNYS_OK) return st;
+  if (ws_bytes < total) return LAPNYS_ERR_WORKSPACE;
+  const size_t elems = (size_t)pl.P * pl.N * pl.d;
+  const size_t in_bytes = elems * (pl.dtype == LAPNYS_BF16 ? 2 : 4), out_bytes = elems * 4;
+  const void* ins[4] = {q, k, v, dout};
+  const size_t in_sz[4] = {in_bytes, in_bytes, in_bytes, out_bytes};
+  const float* outs[3] = {dq, dk, dv};
+  for (int o = 0; o < 3; ++o) {
+    for (int i = 0; i < 4; ++i)
+      if (overlaps(outs[o], out_bytes, ins[i], in_sz[i])) return LAPNYS_ERR_INVALID_ARG;
+    for (int o2 = o + 1; o2 < 3; ++o2)
+      if (overlaps(outs[o], out_bytes, outs[o2], out_bytes)) return LAPNYS_ERR_INVALID_ARG;
+    if (overlaps(outs[o], out_bytes, ws, total)) return LAPNYS_ERR_INVALID_ARG;
+  }
+  if (overlaps(dout, out_bytes, ws, total)) return LAPNYS_ERR_INVALID_ARG;
+  lapnys::Work W = carve(pl, ws);
+  st = run(pl, q, k, v, dq, W, nullptr, s);
+  if (st != LAPNYS_OK) return st;
+  char* b = (char*)ws;
+  lapnys::BwdWork B;
+  float** slots[9] = {&B.part, &B.spart, &B.y, &B.dbv, &B.ab, &B.dw, &B.gt, &B.ht, &B.dkt};
+  for (int i = 0; i < 9; ++i) *slots[i] = (float*)(b + off[i]);
+  if (!ok(lapnys::launch_backward(pl, B, W, q, k, v, dout, dq, dk, dv, s), "backward launch")) return LAPNYS_ERR_HIP;
+  return LAPNYS_OK;
+}
+
 struct Cached {
   void* ptr = nullptr;
   size_t bytes = 0;
@@ -390,6 +443,21 @@ void lapnys_release(void) {
     g_cache[dev] = Cached();
   }
   if (have_cur) hipSetDevice(cur);
+}
+
+int lapnys_backward_workspace_size(const lapnys_params* p, size_t* bytes) {
+  if (!bytes) return LAPNYS_ERR_INVALID_ARG;
+  Plan pl;
+  size_t off[9], total = 0;
+  const int st = backward_plan(p, &pl, off, &total);
+  if (st != LAPNYS_OK) return st;
+  *bytes = total;
+  return LAPNYS_OK;
+}
+
+int lapnys_backward_ws(const void* q, const void* k, const void* v, const float* dout, float* dq, float* dk,
+                       float* dv, const lapnys_params* p, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return backward_impl(q, k, v, dout, dq, dk, dv, p, ws, ws_bytes, stream);
 }
 
 const char* lapnys_status_string(int status) {

@@ -109,6 +109,14 @@ struct Work {
   float* x_final;      // the Newton-Schulz result (x or x2), set by launch_ns
 };
 
+// Backward-pass buffers, after the forward's workspace (float32):
+//   part [P][tiles][m][d], spart [P][tiles][d]   partial C^T dO and 1^T dO
+//   y, dbv [P][m][d]; ab [P][2][m]; dw [P][m][m]; dkt [P][m][d]
+//   gt, ht [P][m][N]                              G^T and H^T
+struct BwdWork {
+  float *part, *spart, *y, *dbv, *ab, *dw, *gt, *ht, *dkt;
+};
+
 // Position of Y^T element (feature f, landmark l) in a [D][rl] bf16 array (rl
 // a multiple of 64), the layout the output stage reads its B operands from.
 // The 8-landmark chunks of a row are XOR-swizzled by t = f / (D / 16), the
@@ -152,6 +160,10 @@ hipError_t launch_y(const Plan& pl, const Work& w, hipStream_t s, Span t = {}); 
 // pl.cg: Y = W^-1 (B V) by pl.ns_iters CG steps per column, into w.y.
 hipError_t launch_cg(const Plan& pl, const Work& w, hipStream_t s, hipEvent_t stop = nullptr);
 hipError_t launch_output(const Plan& pl, const Work& w, float* out, hipStream_t s, Span t = {});
+// The gradients of sum(dout * O) into dq, dk, dv (float32 [B,H,N,d]) after a
+// forward call on the same workspace (m <= 64, Laplacian kernel, Newton-Schulz).
+hipError_t launch_backward(const Plan& pl, const BwdWork& b, const Work& w, const void* q, const void* k,
+                           const void* v, const float* dout, float* dq, float* dk, float* dv, hipStream_t s);
 hipError_t launch_extract_square(const float* src, int src_ld, float* dst, int n, int P, hipStream_t s);
 
 }  // namespace lapnys

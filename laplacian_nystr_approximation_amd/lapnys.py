@@ -91,6 +91,10 @@ def _load():
     lib.lapnys_forward_profiled.argtypes = [vp, vp, vp, vp, P, vp, ctypes.c_size_t,
                                             ctypes.POINTER(ctypes.c_void_p), vp]
     lib.lapnys_forward_profiled.restype = ctypes.c_int
+    lib.lapnys_backward_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.lapnys_backward_workspace_size.restype = ctypes.c_int
+    lib.lapnys_backward_ws.argtypes = [vp, vp, vp, vp, vp, vp, vp, P, vp, ctypes.c_size_t, vp]
+    lib.lapnys_backward_ws.restype = ctypes.c_int
     lib.lapnys_release.argtypes = []
     lib.lapnys_release.restype = None
     lib.lapnys_status_string.argtypes = [ctypes.c_int]
@@ -231,6 +235,24 @@ def lapnys_forward_profiled(q, k, v, out, params: lapnys_params, ws, events: Seq
     wp, wn = _ws(ws)
     _check(_lib.lapnys_forward_profiled(_ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.byref(params), wp, wn,
                                         arr, _stream(stream)), "lapnys_forward_profiled")
+
+
+def lapnys_backward_workspace_size(params: lapnys_params) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.lapnys_backward_workspace_size(ctypes.byref(params), ctypes.byref(n)),
+           "lapnys_backward_workspace_size")
+    return n.value
+
+
+def lapnys_backward_ws(q, k, v, dout, dq, dk, dv, params: lapnys_params, ws, stream=None) -> None:
+    """Gradients of sum(dout * O) into dq, dk, dv (see include/lapnys.h)."""
+    _sizes_ok(params, q, k, v, dout)
+    _sizes_ok(params, q, k, v, dq)
+    _sizes_ok(params, q, k, v, dk)
+    _sizes_ok(params, q, k, v, dv)
+    wp, wn = _ws(ws)
+    _check(_lib.lapnys_backward_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                   ctypes.byref(params), wp, wn, _stream(stream)), "lapnys_backward_ws")
 
 
 def lapnys_release() -> None:

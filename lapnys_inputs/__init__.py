@@ -138,6 +138,12 @@ def _draw(rng: np.random.Generator, shape, dtype: str):
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
+def make_grad_out(w: Workload, seed: int = 99) -> np.ndarray:
+    """A float32 output gradient dO of shape [B, H, N, d] (standard normal, PCG64(seed))."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.standard_normal((w.B, w.H, w.N, w.d)).astype(np.float32)
+
+
 def make_inputs(w: Workload, seed: int | None = None) -> Inputs:
     """Draw Q, K, V for workload ``w`` from PCG64(seed) (default: the workload's seed)."""
     rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))

@@ -25,6 +25,7 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted([
+        "lapnys_backward_workspace_size", "lapnys_backward_ws",
         "lapnys_forward", "lapnys_forward_debug", "lapnys_forward_profiled", "lapnys_forward_ws",
         "lapnys_landmark_count", "lapnys_release", "lapnys_status_string", "lapnys_workspace_size"])
 
@@ -143,6 +144,17 @@ def test_plain_ns_flag():
     assert pl.flags == B.LAPNYS_WHITEN | B.LAPNYS_NS_PLAIN
     assert L.library().lapnys_landmark_count(ctypes.byref(pl)) == 49
     assert L.lapnys_workspace_size(pl) == L.lapnys_workspace_size(_p())
+
+
+def test_backward_workspace_and_support():
+    """The backward workspace extends the forward's; m > 64, the Gaussian form
+    and CG are refused as unsupported before any device call."""
+    p = _p()
+    assert L.lapnys_backward_workspace_size(p) > L.lapnys_workspace_size(p)
+    for bad in (_p(grid_h=32, grid_w=32), _p(kernel="gaussian"), _p(solver="cg")):
+        n = ctypes.c_size_t(0)
+        assert L.library().lapnys_backward_workspace_size(ctypes.byref(bad), ctypes.byref(n)) == \
+            B.LAPNYS_ERR_UNSUPPORTED
 
 
 def test_cg_flag():

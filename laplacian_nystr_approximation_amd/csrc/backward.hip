@@ -39,32 +39,40 @@ __device__ __forceinline__ void load_row(const T* __restrict__ src, float (&x)[D
 
 // Partial C^T g and 1^T g over one tile of tokens: part[p][tile][j][f],
 // spart[p][tile][f].  Thread (jg, f): feature f, landmarks jg, jg + G, ...
+// The tile's tokens pass through LDS in chunks of 64: the C^T entries of all
+// landmarks and the rows of g, loaded coalesced, then summed in token order.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_ctg_kernel(const float* __restrict__ ct, int ldc,
                                                       const float* __restrict__ dout, float* __restrict__ part,
                                                       float* __restrict__ spart, int N, int m, int ntiles) {
-  __shared__ float cs[64 * kBT];  // C^T rows of the tile, [j][i]
+  constexpr int kC = 64;
+  __shared__ float cs[64 * kC];  // [j][i]
+  __shared__ float gs[kC * D];   // [i][f]
   constexpr int G = 256 / D;
   const int tile = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
   const int t0 = tile * kBT, nv = min(kBT, N - t0);
-  for (int e = tid; e < m * kBT; e += 256) {
-    const int j = e / kBT, i = e % kBT;
-    cs[e] = i < nv ? ct[((size_t)p * m + j) * ldc + t0 + i] : 0.f;
-  }
-  __syncthreads();
   const int f = tid % D, jg = tid / D;
-  const float* g = dout + ((size_t)p * N + t0) * D + f;
   float acc[64 / G];
 #pragma unroll
   for (int u = 0; u < 64 / G; ++u) acc[u] = 0.f;
   float s = 0.f;
-  for (int i = 0; i < nv; ++i) {
-    const float gv = g[(size_t)i * D];
-    s += gv;
+  for (int c0 = 0; c0 < nv; c0 += kC) {
+    const int nc = min(kC, nv - c0);
+    __syncthreads();  // the previous chunk's reads are done
+    for (int e = tid; e < 64 * kC; e += 256) {
+      const int j = e / kC, i = e % kC;
+      cs[e] = (j < m && i < nc) ? ct[((size_t)p * m + min(j, m - 1)) * ldc + t0 + c0 + i] : 0.f;
+    }
+    for (int e = tid; e < kC * D; e += 256) {
+      const int i = e / D;
+      gs[e] = i < nc ? dout[((size_t)p * N + t0 + c0 + i) * D + e % D] : 0.f;
+    }
+    __syncthreads();
+    for (int i = 0; i < nc; ++i) {
+      const float gv = gs[i * D + f];
+      s += gv;
 #pragma unroll
-    for (int u = 0; u < 64 / G; ++u) {
-      const int j = jg + G * u;
-      if (j < m) acc[u] = fmaf(cs[j * kBT + i], gv, acc[u]);
+      for (int u = 0; u < 64 / G; ++u) acc[u] = fmaf(cs[(jg + G * u) * kC + i], gv, acc[u]);
     }
   }
   float* pp = part + (((size_t)p * ntiles + tile) * m) * D;
@@ -114,9 +122,11 @@ __global__ __launch_bounds__(256) void bwd_small_kernel(const float* __restrict_
   for (int e = tid; e < m * D; e += 256) {
     const int j = e / D, f = e % D;
     float c = 0.f;
+#pragma unroll 4
     for (int t = 0; t < ntiles; ++t) c += part[(((size_t)p * ntiles + t) * m) * D + e];
     dys[e] = (c - mu[p * m + j] * ss[f]) * rs[p * m + j];
     float yv = 0.f;
+#pragma unroll 8
     for (int kk = 0; kk < m; ++kk) yv = fmaf(xs[j * 65 + kk], bvs[kk * D + f], yv);
     ys[e] = yv;
     y[(size_t)p * m * D + e] = yv;
@@ -135,6 +145,7 @@ __global__ __launch_bounds__(256) void bwd_small_kernel(const float* __restrict_
   for (int e = tid; e < m * D; e += 256) {
     const int kk = e / D, f = e % D;
     float s = 0.f;
+#pragma unroll 8
     for (int j = 0; j < m; ++j) s = fmaf(xs[j * 65 + kk], dys[j * D + f], s);
     dbv[(size_t)p * m * D + e] = s;
   }
@@ -142,6 +153,7 @@ __global__ __launch_bounds__(256) void bwd_small_kernel(const float* __restrict_
   for (int e = tid; e < m * m; e += 256) {
     const int j = e / m, kk = e % m;
     float s = 0.f;
+#pragma unroll 8
     for (int f = 0; f < D; ++f) s = fmaf(dys[j * D + f], bvs[kk * D + f], s);
     tmp[j * 65 + kk] = s;
   }
@@ -155,6 +167,7 @@ __global__ __launch_bounds__(256) void bwd_small_kernel(const float* __restrict_
     float s = 0.f;
     if (e < m * m) {
       const int a = e / m, c = e % m;
+#pragma unroll 8
       for (int j = 0; j < m; ++j) s = fmaf(xs[j * 65 + a], tmp[j * 65 + c], s);
     }
     rv[u] = s;
@@ -169,6 +182,7 @@ __global__ __launch_bounds__(256) void bwd_small_kernel(const float* __restrict_
   for (int e = tid; e < m * m; e += 256) {
     const int a = e / m, b = e % m;
     float s = 0.f;
+#pragma unroll 8
     for (int c = 0; c < m; ++c) s = fmaf(tmp[a * 65 + c], xs[b * 65 + c], s);
     dw[(size_t)p * m * m + e] = -s;
   }
@@ -263,30 +277,74 @@ __global__ __launch_bounds__(256) void bwd_k_kernel(const T* __restrict__ k, con
   for (int t = 0; t < D; ++t) out[t] = acc[t];
 }
 
-// Landmark side: one lane per (problem, landmark j, feature t).
+// Landmark side: one lane per (landmark j, feature t); workgroup (jb, p) takes
+// landmarks jb LG + [0, LG), LG = 256 / D.  The tokens are streamed through LDS
+// in chunks of kKC: the chunk's rows of Q (then K) and its G^T (then H^T)
+// entries for the workgroup's landmarks, loaded coalesced by all lanes, then
+// summed per lane in token order.
+constexpr int kKC = 128;
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_kt_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                      const float* __restrict__ kt, const float* __restrict__ gt,
                                                      const float* __restrict__ ht, const float* __restrict__ w,
                                                      int mp, const float* __restrict__ dw,
                                                      float* __restrict__ dkt, int N, int m, float eps,
-                                                     float inv_lam, long long total) {
-  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= total) return;
-  const int t = (int)(idx % D);
-  const long long rest = idx / D;
-  const int j = (int)(rest % m);
-  const int p = (int)(rest / m);
-  const float kj = kt[((size_t)p * m + j) * D + t];
-  const float* gr = gt + ((size_t)p * m + j) * N;
-  const float* hr = ht + ((size_t)p * m + j) * N;
-  const T* qc = q + (size_t)p * N * D + t;
-  const T* kc = k + (size_t)p * N * D + t;
-  float a = 0.f, b = 0.f;
-  for (int i = 0; i < N; ++i) {
-    a = fmaf(gr[i], sgn(widen(qc[(size_t)i * D]) - kj), a);
-    b = fmaf(hr[i], sgn(kj - widen(kc[(size_t)i * D])), b);
+                                                     float inv_lam) {
+  constexpr int LG = 256 / D;
+  __shared__ float xs[kKC * D];
+  __shared__ float gs[LG * kKC];
+  const int p = blockIdx.y, tid = threadIdx.x;
+  const int jl = tid / D, t = tid % D;
+  const int j0 = blockIdx.x * LG, j = j0 + jl;
+  const bool valid = j < m;
+  const int jc = min(j, m - 1);
+  const float kj = kt[((size_t)p * m + jc) * D + t];
+  // Per lane, the chunk's loads: kX row values and kG weights, issued one
+  // chunk ahead so that they land while the current chunk is summed.  Tokens
+  // past N read the last token and carry weight 0.
+  constexpr int kX = kKC * D / 256, kG = LG * kKC / 256;
+  float sums[2] = {0.f, 0.f};
+#pragma unroll
+  for (int side = 0; side < 2; ++side) {
+    const T* rows = (side == 0 ? q : k) + (size_t)p * N * D;
+    const float* wt = (side == 0 ? gt : ht) + (size_t)p * m * N;
+    float xr[kX], gr[kG];
+    auto fetch = [&](int c0) {
+#pragma unroll
+      for (int u = 0; u < kX; ++u) {
+        const int e = tid + 256 * u, i = e / D;
+        xr[u] = widen(rows[(size_t)min(c0 + i, N - 1) * D + e % D]);
+      }
+#pragma unroll
+      for (int u = 0; u < kG; ++u) {
+        const int e = tid + 256 * u, l = e / kKC, i = e % kKC;
+        const float g = wt[(size_t)min(j0 + l, m - 1) * N + min(c0 + i, N - 1)];
+        gr[u] = c0 + i < N ? g : 0.f;
+      }
+    };
+    float acc = 0.f;
+    fetch(0);
+    for (int c0 = 0; c0 < N; c0 += kKC) {
+      __syncthreads();  // the previous chunk's reads are done
+#pragma unroll
+      for (int u = 0; u < kX; ++u) xs[tid + 256 * u] = xr[u];
+#pragma unroll
+      for (int u = 0; u < kG; ++u) gs[tid + 256 * u] = gr[u];
+      __syncthreads();
+      if (c0 + kKC < N) fetch(c0 + kKC);
+      const float* gl = gs + jl * kKC;
+      if (side == 0) {
+#pragma unroll 16
+        for (int i = 0; i < kKC; ++i) acc = fmaf(gl[i], sgn(xs[i * D + t] - kj), acc);
+      } else {
+#pragma unroll 16
+        for (int i = 0; i < kKC; ++i) acc = fmaf(gl[i], sgn(kj - xs[i * D + t]), acc);
+      }
+    }
+    sums[side] = acc;
   }
+  if (!valid) return;
   float c = 0.f;
   for (int bb = 0; bb < m; ++bb) {
     float wv = w[(size_t)p * mp * mp + (size_t)j * mp + bb];
@@ -294,7 +352,7 @@ __global__ __launch_bounds__(256) void bwd_kt_kernel(const T* __restrict__ q, co
     const float dws = dw[((size_t)p * m + j) * m + bb] + dw[((size_t)p * m + bb) * m + j];
     c = fmaf(dws * wv, sgn(kj - kt[((size_t)p * m + bb) * D + t]), c);
   }
-  dkt[((size_t)p * m + j) * D + t] = (a - b - c) * inv_lam;
+  dkt[((size_t)p * m + j) * D + t] = (sums[0] - sums[1] - c) * inv_lam;
 }
 
 // dk[p][n][t] += dK~[p][j(n)][t] / pool^2 (the pooling adjoint).
@@ -331,9 +389,9 @@ hipError_t launch_typed(const Plan& pl, const BwdWork& b, const Work& w, const v
                      b.dbv, b.ht, dk, dv, pl.N, pl.m, pl.scale, inv_lam);
   hipLaunchKernelGGL((bwd_k_kernel<T, D, true>), dim3(nt, pl.P), dim3(256), 0, s, (const T*)k, (const T*)v, w.kt,
                      b.dbv, b.ht, dk, dv, pl.N, pl.m, pl.scale, inv_lam);
-  const long long lt = (long long)pl.P * pl.m * D;
-  hipLaunchKernelGGL((bwd_kt_kernel<T, D>), dim3((unsigned)((lt + 255) / 256)), dim3(256), 0, s, (const T*)q,
-                     (const T*)k, w.kt, b.gt, b.ht, w.w, pl.mp, b.dw, b.dkt, pl.N, pl.m, pl.eps, inv_lam, lt);
+  constexpr int LG = 256 / D;
+  hipLaunchKernelGGL((bwd_kt_kernel<T, D>), dim3((pl.m + LG - 1) / LG, pl.P), dim3(256), 0, s, (const T*)q,
+                     (const T*)k, w.kt, b.gt, b.ht, w.w, pl.mp, b.dw, b.dkt, pl.N, pl.m, pl.eps, inv_lam);
   const long long tt = (long long)pl.P * pl.N * D;
   hipLaunchKernelGGL(bwd_pool_kernel<D>, dim3((unsigned)((tt + 255) / 256)), dim3(256), 0, s, b.dkt, dk, pl.N, pl.m,
                      pl.grid_w, pl.pool, pl.gw, tt);

@@ -188,29 +188,22 @@ __global__ __launch_bounds__(256) void bwd_small_kernel(const float* __restrict_
   }
 }
 
-// Query side: one lane per token i of the tile.  G^T[p][j][i] is stored for
-// the landmark-side reduction; dq is written.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_q_kernel(const T* __restrict__ q, const float* __restrict__ dout,
-                                                    const float* __restrict__ kt, const float* __restrict__ ct,
+// Query side, first pass: one lane per token i of the tile.  G_ij =
+// dC_ij C_ij for every landmark, stored as G^T[p][j][i].
+template <int D>
+__global__ __launch_bounds__(256) void bwd_g_kernel(const float* __restrict__ dout, const float* __restrict__ ct,
                                                     int ldc, const float* __restrict__ y,
                                                     const float* __restrict__ mu, const float* __restrict__ rs,
-                                                    const float* __restrict__ ab, float* __restrict__ gt,
-                                                    float* __restrict__ dq, int N, int m, float inv_lam) {
-  __shared__ float kls[64 * D], yls[64 * D];
+                                                    const float* __restrict__ ab, float* __restrict__ gt, int N,
+                                                    int m) {
+  __shared__ float yls[64 * D];
   const int tile = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
-  for (int e = tid; e < m * D; e += 256) {
-    kls[e] = kt[(size_t)p * m * D + e];
-    yls[e] = y[(size_t)p * m * D + e];
-  }
+  for (int e = tid; e < m * D; e += 256) yls[e] = y[(size_t)p * m * D + e];
   __syncthreads();
   const int i = tile * kBT + tid;
   if (i >= N) return;
-  float qv[D], gv[D], dqv[D];
-  load_row<T, D>(q + ((size_t)p * N + i) * D, qv);
+  float gv[D];
   load_row<float, D>(dout + ((size_t)p * N + i) * D, gv);
-#pragma unroll
-  for (int t = 0; t < D; ++t) dqv[t] = 0.f;
   for (int j = 0; j < m; ++j) {
     float g = 0.f;
 #pragma unroll
@@ -219,26 +212,17 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(const T* __restrict__ q, con
     const float r = rs[p * m + j];
     const float z = (c - mu[p * m + j]) * r;
     const float dc = (g - ab[(size_t)p * 2 * m + j] - z * ab[(size_t)p * 2 * m + m + j]) * r;
-    const float gg = dc * c;
-    gt[((size_t)p * m + j) * N + i] = gg;
-    const float w = -gg * inv_lam;
-#pragma unroll
-    for (int t = 0; t < D; ++t) dqv[t] = fmaf(w, sgn(qv[t] - kls[j * D + t]), dqv[t]);
+    gt[((size_t)p * m + j) * N + i] = dc * c;
   }
-  float* dqp = dq + ((size_t)p * N + i) * D;
-#pragma unroll
-  for (int t = 0; t < D; ++t) dqp[t] = dqv[t];
 }
 
-// Key side: one lane per token n.  B recomputed; with DV false, H^T[p][j][n]
-// is stored and the B part of dk written; with DV true, dv is written (two
-// passes keep each lane's registers to two feature rows).
-template <typename T, int D, bool DV>
-__global__ __launch_bounds__(256) void bwd_k_kernel(const T* __restrict__ k, const T* __restrict__ v,
-                                                    const float* __restrict__ kt, const float* __restrict__ dbv,
-                                                    float* __restrict__ ht, float* __restrict__ dk,
-                                                    float* __restrict__ dv, int N, int m, float scale,
-                                                    float inv_lam) {
+// Key side, first pass: one lane per token n.  B recomputed from K~ and k_n;
+// H_jn = (dBV_j . v_n) B_jn stored as H^T[p][j][n]; dv_n = sum_j B_jn dBV_j.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_hv_kernel(const T* __restrict__ k, const T* __restrict__ v,
+                                                     const float* __restrict__ kt, const float* __restrict__ dbv,
+                                                     float* __restrict__ ht, float* __restrict__ dv, int N, int m,
+                                                     float scale) {
   __shared__ float kls[64 * D], dls[64 * D];
   const int tile = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
   for (int e = tid; e < m * D; e += 256) {
@@ -248,33 +232,55 @@ __global__ __launch_bounds__(256) void bwd_k_kernel(const T* __restrict__ k, con
   __syncthreads();
   const int n = tile * kBT + tid;
   if (n >= N) return;
-  float kv[D], acc[D];
+  float kv[D], vv[D], acc[D];
   load_row<T, D>(k + ((size_t)p * N + n) * D, kv);
+  load_row<T, D>(v + ((size_t)p * N + n) * D, vv);
 #pragma unroll
   for (int t = 0; t < D; ++t) acc[t] = 0.f;
-  const T* vrow = v + ((size_t)p * N + n) * D;
   for (int j = 0; j < m; ++j) {
-    float l1 = 0.f;
+    float l1 = 0.f, hd = 0.f;
 #pragma unroll
-    for (int t = 0; t < D; ++t) l1 += fabsf(kls[j * D + t] - kv[t]);
-    const float b = exp2f(l1 * scale);
-    if constexpr (DV) {
-#pragma unroll
-      for (int t = 0; t < D; ++t) acc[t] = fmaf(b, dls[j * D + t], acc[t]);
-    } else {
-      float hd = 0.f;
-#pragma unroll
-      for (int t = 0; t < D; ++t) hd = fmaf(dls[j * D + t], widen(vrow[t]), hd);
-      const float h = hd * b;
-      ht[((size_t)p * m + j) * N + n] = h;
-      const float w = h * inv_lam;
-#pragma unroll
-      for (int t = 0; t < D; ++t) acc[t] = fmaf(w, sgn(kls[j * D + t] - kv[t]), acc[t]);
+    for (int t = 0; t < D; ++t) {
+      l1 += fabsf(kls[j * D + t] - kv[t]);
+      hd = fmaf(dls[j * D + t], vv[t], hd);
     }
-  }
-  float* out = (DV ? dv : dk) + ((size_t)p * N + n) * D;
+    const float b = exp2f(l1 * scale);
+    ht[((size_t)p * m + j) * N + n] = hd * b;
 #pragma unroll
-  for (int t = 0; t < D; ++t) out[t] = acc[t];
+    for (int t = 0; t < D; ++t) acc[t] = fmaf(b, dls[j * D + t], acc[t]);
+  }
+  float* dvp = dv + ((size_t)p * N + n) * D;
+#pragma unroll
+  for (int t = 0; t < D; ++t) dvp[t] = acc[t];
+}
+
+// Token-side sign sums, one lane per token n: out_n = -(1/lambda) sum_j
+// w[j][n] sign(x_n - K~_j), per feature.  With x = Q and w = G^T this is dQ;
+// with x = K and w = H^T it is the B part of dK (sign(K~_j - k_n) =
+// -sign(k_n - K~_j)).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_sign_kernel(const T* __restrict__ x, const float* __restrict__ kt,
+                                                       const float* __restrict__ wt, float* __restrict__ out, int N,
+                                                       int m, float inv_lam) {
+  __shared__ float kls[64 * D];
+  const int tile = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
+  for (int e = tid; e < m * D; e += 256) kls[e] = kt[(size_t)p * m * D + e];
+  __syncthreads();
+  const int n = tile * kBT + tid;
+  if (n >= N) return;
+  float xv[D], acc[D];
+  load_row<T, D>(x + ((size_t)p * N + n) * D, xv);
+#pragma unroll
+  for (int t = 0; t < D; ++t) acc[t] = 0.f;
+  const float* wc = wt + (size_t)p * m * N + n;
+  for (int j = 0; j < m; ++j) {
+    const float wj = wc[(size_t)j * N];
+#pragma unroll
+    for (int t = 0; t < D; ++t) acc[t] = fmaf(wj, sgn(xv[t] - kls[j * D + t]), acc[t]);
+  }
+  float* op = out + ((size_t)p * N + n) * D;
+#pragma unroll
+  for (int t = 0; t < D; ++t) op[t] = -inv_lam * acc[t];
 }
 
 // Landmark side: one lane per (landmark j, feature t); workgroup (jb, p) takes
@@ -383,12 +389,14 @@ hipError_t launch_typed(const Plan& pl, const BwdWork& b, const Work& w, const v
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_small_kernel<D>, dim3(pl.P), dim3(256), small_lds, s, b.part, b.spart, w.x_final, pl.mp,
                      w.bv, w.mu, w.rs, b.y, b.dbv, b.ab, b.dw, pl.N, pl.m, nt, pl.whiten ? 1 : 0);
-  hipLaunchKernelGGL((bwd_q_kernel<T, D>), dim3(nt, pl.P), dim3(256), 0, s, (const T*)q, dout, w.kt, w.ct, pl.ldc,
-                     b.y, w.mu, w.rs, b.ab, b.gt, dq, pl.N, pl.m, inv_lam);
-  hipLaunchKernelGGL((bwd_k_kernel<T, D, false>), dim3(nt, pl.P), dim3(256), 0, s, (const T*)k, (const T*)v, w.kt,
-                     b.dbv, b.ht, dk, dv, pl.N, pl.m, pl.scale, inv_lam);
-  hipLaunchKernelGGL((bwd_k_kernel<T, D, true>), dim3(nt, pl.P), dim3(256), 0, s, (const T*)k, (const T*)v, w.kt,
-                     b.dbv, b.ht, dk, dv, pl.N, pl.m, pl.scale, inv_lam);
+  hipLaunchKernelGGL(bwd_g_kernel<D>, dim3(nt, pl.P), dim3(256), 0, s, dout, w.ct, pl.ldc, b.y, w.mu, w.rs, b.ab,
+                     b.gt, pl.N, pl.m);
+  hipLaunchKernelGGL((bwd_sign_kernel<T, D>), dim3(nt, pl.P), dim3(256), 0, s, (const T*)q, w.kt, b.gt, dq, pl.N,
+                     pl.m, inv_lam);
+  hipLaunchKernelGGL((bwd_hv_kernel<T, D>), dim3(nt, pl.P), dim3(256), 0, s, (const T*)k, (const T*)v, w.kt, b.dbv,
+                     b.ht, dv, pl.N, pl.m, pl.scale);
+  hipLaunchKernelGGL((bwd_sign_kernel<T, D>), dim3(nt, pl.P), dim3(256), 0, s, (const T*)k, w.kt, b.ht, dk, pl.N,
+                     pl.m, inv_lam);
   constexpr int LG = 256 / D;
   hipLaunchKernelGGL((bwd_kt_kernel<T, D>), dim3((pl.m + LG - 1) / LG, pl.P), dim3(256), 0, s, (const T*)q,
                      (const T*)k, w.kt, b.gt, b.ht, w.w, pl.mp, b.dw, b.dkt, pl.N, pl.m, pl.eps, inv_lam);

@@ -18,9 +18,9 @@
 //                       - sum_b (dW_jb + dW_bj) W'_jb sign(K~_j - K~_b)]
 //
 // (W' = W without eps.)  With whitening off, mu = 0, 1/sigma = 1 and a = b = 0.
-// Every kernel is a plain loop in float32 with a fixed order; the token-side
-// kernels take one lane per token, the landmark-side ones one lane per
-// (landmark, feature).
+// Every kernel is a loop in float32 with a fixed order; the token-side
+// kernels take one lane per token, the landmark-side one one lane per
+// (landmark, feature) with the tokens streamed through LDS.
 #include "lapnys_internal.hpp"
 
 namespace lapnys {
@@ -257,11 +257,13 @@ __global__ __launch_bounds__(256) void bwd_hv_kernel(const T* __restrict__ k, co
 // Token-side sign sums, one lane per token n: out_n = -(1/lambda) sum_j
 // w[j][n] sign(x_n - K~_j), per feature.  With x = Q and w = G^T this is dQ;
 // with x = K and w = H^T it is the B part of dK (sign(K~_j - k_n) =
-// -sign(k_n - K~_j)).
+// -sign(k_n - K~_j)), to which the pooling adjoint then adds dK~_{j(n)} /
+// pool^2 when dkt is given (grid_w, pool, gw locate token n's window).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_sign_kernel(const T* __restrict__ x, const float* __restrict__ kt,
                                                        const float* __restrict__ wt, float* __restrict__ out, int N,
-                                                       int m, float inv_lam) {
+                                                       int m, float inv_lam, const float* __restrict__ dkt,
+                                                       int grid_w, int pool, int gw) {
   __shared__ float kls[64 * D];
   const int tile = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
   for (int e = tid; e < m * D; e += 256) kls[e] = kt[(size_t)p * m * D + e];
@@ -279,8 +281,16 @@ __global__ __launch_bounds__(256) void bwd_sign_kernel(const T* __restrict__ x, 
     for (int t = 0; t < D; ++t) acc[t] = fmaf(wj, sgn(xv[t] - kls[j * D + t]), acc[t]);
   }
   float* op = out + ((size_t)p * N + n) * D;
+  if (dkt) {
+    const int jn = (n / grid_w / pool) * gw + (n % grid_w) / pool;
+    const float* dr = dkt + ((size_t)p * m + jn) * D;
+    const float inv_area = 1.f / (float)(pool * pool);
 #pragma unroll
-  for (int t = 0; t < D; ++t) op[t] = -inv_lam * acc[t];
+    for (int t = 0; t < D; ++t) op[t] = fmaf(dr[t], inv_area, -inv_lam * acc[t]);
+  } else {
+#pragma unroll
+    for (int t = 0; t < D; ++t) op[t] = -inv_lam * acc[t];
+  }
 }
 
 // Landmark side: one lane per (landmark j, feature t); workgroup (jb, p) takes
@@ -361,21 +371,6 @@ __global__ __launch_bounds__(256) void bwd_kt_kernel(const T* __restrict__ q, co
   dkt[((size_t)p * m + j) * D + t] = (sums[0] - sums[1] - c) * inv_lam;
 }
 
-// dk[p][n][t] += dK~[p][j(n)][t] / pool^2 (the pooling adjoint).
-template <int D>
-__global__ __launch_bounds__(256) void bwd_pool_kernel(const float* __restrict__ dkt, float* __restrict__ dk, int N,
-                                                       int m, int grid_w, int pool, int gw, long long total) {
-  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= total) return;
-  const int t = (int)(idx % D);
-  const long long rest = idx / D;
-  const int n = (int)(rest % N);
-  const int p = (int)(rest / N);
-  const int r = n / grid_w, c = n % grid_w;
-  const int j = (r / pool) * gw + c / pool;
-  dk[idx] += dkt[((size_t)p * m + j) * D + t] / (float)(pool * pool);
-}
-
 template <typename T, int D>
 hipError_t launch_typed(const Plan& pl, const BwdWork& b, const Work& w, const void* q, const void* k,
                         const void* v, const float* dout, float* dq, float* dk, float* dv, hipStream_t s) {
@@ -392,17 +387,15 @@ hipError_t launch_typed(const Plan& pl, const BwdWork& b, const Work& w, const v
   hipLaunchKernelGGL(bwd_g_kernel<D>, dim3(nt, pl.P), dim3(256), 0, s, dout, w.ct, pl.ldc, b.y, w.mu, w.rs, b.ab,
                      b.gt, pl.N, pl.m);
   hipLaunchKernelGGL((bwd_sign_kernel<T, D>), dim3(nt, pl.P), dim3(256), 0, s, (const T*)q, w.kt, b.gt, dq, pl.N,
-                     pl.m, inv_lam);
+                     pl.m, inv_lam, nullptr, pl.grid_w, pl.pool, pl.gw);
   hipLaunchKernelGGL((bwd_hv_kernel<T, D>), dim3(nt, pl.P), dim3(256), 0, s, (const T*)k, (const T*)v, w.kt, b.dbv,
                      b.ht, dv, pl.N, pl.m, pl.scale);
-  hipLaunchKernelGGL((bwd_sign_kernel<T, D>), dim3(nt, pl.P), dim3(256), 0, s, (const T*)k, w.kt, b.ht, dk, pl.N,
-                     pl.m, inv_lam);
   constexpr int LG = 256 / D;
   hipLaunchKernelGGL((bwd_kt_kernel<T, D>), dim3((pl.m + LG - 1) / LG, pl.P), dim3(256), 0, s, (const T*)q,
                      (const T*)k, w.kt, b.gt, b.ht, w.w, pl.mp, b.dw, b.dkt, pl.N, pl.m, pl.eps, inv_lam);
-  const long long tt = (long long)pl.P * pl.N * D;
-  hipLaunchKernelGGL(bwd_pool_kernel<D>, dim3((unsigned)((tt + 255) / 256)), dim3(256), 0, s, b.dkt, dk, pl.N, pl.m,
-                     pl.grid_w, pl.pool, pl.gw, tt);
+  // dK: the B part, plus the pooling adjoint of dK~.
+  hipLaunchKernelGGL((bwd_sign_kernel<T, D>), dim3(nt, pl.P), dim3(256), 0, s, (const T*)k, w.kt, b.ht, dk, pl.N,
+                     pl.m, inv_lam, b.dkt, pl.grid_w, pl.pool, pl.gw);
   return hipGetLastError();
 }
 

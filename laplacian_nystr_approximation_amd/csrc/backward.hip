@@ -31,6 +31,17 @@ constexpr int kBT = 256;  // tokens per tile of the token-side kernels
 
 __device__ __forceinline__ float sgn(float x) { return x > 0.f ? 1.f : (x < 0.f ? -1.f : 0.f); }
 
+// sign(x - y) in two instructions for the hot loops: with ys = y * 2^64
+// (exact), fma(x, 2^64, -ys) is (x - y) * 2^64 rounded once, so it is zero
+// exactly when x == y and has the sign of x - y; the median with -1 and 1 then
+// gives -1, 0 or 1 whenever |x - y| >= 2^-64 (smaller nonzero gaps, between
+// values below ~2^-40, would give a fraction).  Inputs must stay below 2^63 in
+// magnitude.
+constexpr float kSgnScale = 1.8446744073709552e19f;  // 2^64
+__device__ __forceinline__ float sgn_diff(float x, float ys) {
+  return __builtin_amdgcn_fmed3f(fmaf(x, kSgnScale, -ys), -1.f, 1.f);
+}
+
 template <typename T, int D>
 __device__ __forceinline__ void load_row(const T* __restrict__ src, float (&x)[D]) {
 #pragma unroll
@@ -264,9 +275,9 @@ __global__ __launch_bounds__(256) void bwd_sign_kernel(const T* __restrict__ x, 
                                                        const float* __restrict__ wt, float* __restrict__ out, int N,
                                                        int m, float inv_lam, const float* __restrict__ dkt,
                                                        int grid_w, int pool, int gw) {
-  __shared__ float kls[64 * D];
+  __shared__ float kls[64 * D];  // K~ * 2^64
   const int tile = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
-  for (int e = tid; e < m * D; e += 256) kls[e] = kt[(size_t)p * m * D + e];
+  for (int e = tid; e < m * D; e += 256) kls[e] = kt[(size_t)p * m * D + e] * kSgnScale;
   __syncthreads();
   const int n = tile * kBT + tid;
   if (n >= N) return;
@@ -278,7 +289,7 @@ __global__ __launch_bounds__(256) void bwd_sign_kernel(const T* __restrict__ x, 
   for (int j = 0; j < m; ++j) {
     const float wj = wc[(size_t)j * N];
 #pragma unroll
-    for (int t = 0; t < D; ++t) acc[t] = fmaf(wj, sgn(xv[t] - kls[j * D + t]), acc[t]);
+    for (int t = 0; t < D; ++t) acc[t] = fmaf(wj, sgn_diff(xv[t], kls[j * D + t]), acc[t]);
   }
   float* op = out + ((size_t)p * N + n) * D;
   if (dkt) {
@@ -316,6 +327,7 @@ __global__ __launch_bounds__(256) void bwd_kt_kernel(const T* __restrict__ q, co
   const bool valid = j < m;
   const int jc = min(j, m - 1);
   const float kj = kt[((size_t)p * m + jc) * D + t];
+  const float kjs = kj * kSgnScale;
   // Per lane, the chunk's loads: kX row values and kG weights, issued one
   // chunk ahead so that they land while the current chunk is summed.  Tokens
   // past N read the last token and carry weight 0.
@@ -350,13 +362,9 @@ __global__ __launch_bounds__(256) void bwd_kt_kernel(const T* __restrict__ q, co
       __syncthreads();
       if (c0 + kKC < N) fetch(c0 + kKC);
       const float* gl = gs + jl * kKC;
-      if (side == 0) {
+      // Both sides sum w_i sign(x_i - K~_jt); the B side enters negated below.
 #pragma unroll 16
-        for (int i = 0; i < kKC; ++i) acc = fmaf(gl[i], sgn(xs[i * D + t] - kj), acc);
-      } else {
-#pragma unroll 16
-        for (int i = 0; i < kKC; ++i) acc = fmaf(gl[i], sgn(kj - xs[i * D + t]), acc);
-      }
+      for (int i = 0; i < kKC; ++i) acc = fmaf(gl[i], sgn_diff(xs[i * D + t], kjs), acc);
     }
     sums[side] = acc;
   }
@@ -368,7 +376,8 @@ __global__ __launch_bounds__(256) void bwd_kt_kernel(const T* __restrict__ q, co
     const float dws = dw[((size_t)p * m + j) * m + bb] + dw[((size_t)p * m + bb) * m + j];
     c = fmaf(dws * wv, sgn(kj - kt[((size_t)p * m + bb) * D + t]), c);
   }
-  dkt[((size_t)p * m + j) * D + t] = (sums[0] - sums[1] - c) * inv_lam;
+  // sum_n H_jn sign(K~_j - k_n) = -sums[1]
+  dkt[((size_t)p * m + j) * D + t] = (sums[0] + sums[1] - c) * inv_lam;
 }
 
 template <typename T, int D>

@@ -95,16 +95,43 @@ __global__ __launch_bounds__(256) void bwd_ctg_kernel(const float* __restrict__ 
   if (jg == 0) spart[((size_t)p * ntiles + tile) * D + f] = s;
 }
 
-// LDS of bwd_small_kernel: X and the m x m scratch (stride 65), B V, dY and Y
-// (64 x D each), 1^T g (D).
+// LDS of bwd_small_kernel: five 64-row matrices of row stride 65 (X, the m x m
+// scratch dX, R, and B V, dY, Y of D columns), and 1^T g (D).
 template <int D>
 constexpr size_t bwd_small_lds() {
-  return (size_t)(2 * 64 * 65 + 3 * 64 * D + D) * sizeof(float);
+  return (size_t)(6 * 64 * 65 + D) * sizeof(float);
+}
+
+// out[i][j] = sum_{k < K} A(i, k) B(k, j) for i < 64, j < NC, on fp32 MFMA
+// 16x16x4: wavefront w forms rows [16 w, 16 w + 16).  A(i, k) = a[i][k] or,
+// with TA, a[k][i]; B(k, j) = b[k][j] or, with TB, b[j][k]; all row stride 65.
+template <int NC, bool TA, bool TB>
+__device__ __forceinline__ void mm64(const float* __restrict__ a, const float* __restrict__ b,
+                                     float* __restrict__ out, int K, float sign) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, li = lane & 15, lk = lane >> 4;
+  f32x4 acc[NC / 16];
+#pragma unroll
+  for (int bj = 0; bj < NC / 16; ++bj) acc[bj] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < K; k0 += 4) {
+    const int i = 16 * w + li, k = k0 + lk;
+    const float av = TA ? a[k * 65 + i] : a[i * 65 + k];
+#pragma unroll
+    for (int bj = 0; bj < NC / 16; ++bj) {
+      const int j = 16 * bj + li;
+      const float bv = TB ? b[j * 65 + k] : b[k * 65 + j];
+      acc[bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[bj], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int bj = 0; bj < NC / 16; ++bj)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) out[(16 * w + 4 * lk + r) * 65 + 16 * bj + li] = sign * acc[bj][r];
 }
 
 // Per problem (one workgroup): reduce the partials, then Y, dY, a, b, dBV and
-// dW = -X^T (dY BV^T) X^T, all m <= 64 in LDS.  x: the Newton-Schulz result,
-// row stride mp.  Outputs: y, dbv [P][m][D]; ab [P][2][m]; dw [P][m][m].
+// dW = -X^T (dY BV^T) X^T, every matrix zero padded to 64 rows in LDS and the
+// products on fp32 MFMA.  x: the Newton-Schulz result, row stride mp.
+// Outputs: y, dbv [P][m][D]; ab [P][2][m]; dw [P][m][m].
 template <int D>
 __global__ __launch_bounds__(256) void bwd_small_kernel(const float* __restrict__ part,
                                                         const float* __restrict__ spart,
@@ -115,88 +142,61 @@ __global__ __launch_bounds__(256) void bwd_small_kernel(const float* __restrict_
                                                         float* __restrict__ dw, int N, int m, int ntiles,
                                                         int whiten) {
   extern __shared__ __align__(16) float lds[];
+  constexpr int kS = 64 * 65;
   float* xs = lds;
-  float* tmp = xs + 64 * 65;
-  float* bvs = tmp + 64 * 65;
-  float* dys = bvs + 64 * D;
-  float* ys = dys + 64 * D;
-  float* ss = ys + 64 * D;
+  float* dxs = xs + kS;
+  float* rsm = dxs + kS;
+  float* bvs = rsm + kS;
+  float* dys = bvs + kS;
+  float* ys = dys + kS;
+  float* ss = ys + kS;
   const int p = blockIdx.x, tid = threadIdx.x;
-  for (int e = tid; e < m * m; e += 256) xs[(e / m) * 65 + e % m] = x[(size_t)p * mp * mp + (e / m) * mp + e % m];
-  for (int e = tid; e < m * D; e += 256) bvs[e] = bv[(size_t)p * m * D + e];
+  for (int e = tid; e < 64 * 64; e += 256) {
+    const int r = e >> 6, c = e & 63;
+    xs[r * 65 + c] = (r < m && c < m) ? x[(size_t)p * mp * mp + (size_t)r * mp + c] : 0.f;
+  }
+  for (int e = tid; e < 64 * D; e += 256) {
+    const int r = e / D, c = e % D;
+    bvs[r * 65 + c] = r < m ? bv[(size_t)p * m * D + e] : 0.f;
+  }
   for (int f = tid; f < D; f += 256) {
     float s = 0.f;
     for (int t = 0; t < ntiles; ++t) s += spart[((size_t)p * ntiles + t) * D + f];
     ss[f] = s;
   }
   __syncthreads();
-  for (int e = tid; e < m * D; e += 256) {
+  for (int e = tid; e < 64 * D; e += 256) {
     const int j = e / D, f = e % D;
     float c = 0.f;
+    if (j < m) {
 #pragma unroll 4
-    for (int t = 0; t < ntiles; ++t) c += part[(((size_t)p * ntiles + t) * m) * D + e];
-    dys[e] = (c - mu[p * m + j] * ss[f]) * rs[p * m + j];
-    float yv = 0.f;
-#pragma unroll 8
-    for (int kk = 0; kk < m; ++kk) yv = fmaf(xs[j * 65 + kk], bvs[kk * D + f], yv);
-    ys[e] = yv;
-    y[(size_t)p * m * D + e] = yv;
+      for (int t = 0; t < ntiles; ++t) c += part[(((size_t)p * ntiles + t) * m) * D + e];
+      c = (c - mu[p * m + j] * ss[f]) * rs[p * m + j];
+    }
+    dys[j * 65 + f] = c;
   }
+  mm64<D, false, false>(xs, bvs, ys, 64, 1.f);  // Y = X BV
   __syncthreads();
+  for (int e = tid; e < m * D; e += 256) y[(size_t)p * m * D + e] = ys[(e / D) * 65 + e % D];
   for (int j = tid; j < m; j += 256) {
     float a = 0.f, b = 0.f;
     for (int f = 0; f < D; ++f) {
-      a = fmaf(ss[f], ys[j * D + f], a);
-      b = fmaf(ys[j * D + f], dys[j * D + f], b);
+      a = fmaf(ss[f], ys[j * 65 + f], a);
+      b = fmaf(ys[j * 65 + f], dys[j * 65 + f], b);
     }
     ab[(size_t)p * 2 * m + j] = whiten ? a / (float)N : 0.f;
     ab[(size_t)p * 2 * m + m + j] = whiten ? b / (float)N : 0.f;
   }
-  // dBV = X^T dY
-  for (int e = tid; e < m * D; e += 256) {
-    const int kk = e / D, f = e % D;
-    float s = 0.f;
-#pragma unroll 8
-    for (int j = 0; j < m; ++j) s = fmaf(xs[j * 65 + kk], dys[j * D + f], s);
-    dbv[(size_t)p * m * D + e] = s;
-  }
-  // tmp = dX = dY BV^T (m x m)
-  for (int e = tid; e < m * m; e += 256) {
-    const int j = e / m, kk = e % m;
-    float s = 0.f;
-#pragma unroll 8
-    for (int f = 0; f < D; ++f) s = fmaf(dys[j * D + f], bvs[kk * D + f], s);
-    tmp[j * 65 + kk] = s;
-  }
   __syncthreads();
-  // dW = -X^T dX X^T: R = X^T dX (each lane keeps its at most 16 entries in
-  // registers until every lane has read dX), then -R X^T.
-  float rv[16];
-#pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int e = tid + 256 * u;
-    float s = 0.f;
-    if (e < m * m) {
-      const int a = e / m, c = e % m;
-#pragma unroll 8
-      for (int j = 0; j < m; ++j) s = fmaf(xs[j * 65 + a], tmp[j * 65 + c], s);
-    }
-    rv[u] = s;
-  }
+  mm64<D, true, false>(xs, dys, ys, 64, 1.f);    // dBV = X^T dY (into the Y buffer)
+  mm64<64, false, true>(dys, bvs, dxs, D, 1.f);  // dX = dY BV^T
   __syncthreads();
-#pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int e = tid + 256 * u;
-    if (e < m * m) tmp[(e / m) * 65 + e % m] = rv[u];
-  }
+  for (int e = tid; e < m * D; e += 256) dbv[(size_t)p * m * D + e] = ys[(e / D) * 65 + e % D];
+  mm64<64, true, false>(xs, dxs, rsm, 64, 1.f);  // R = X^T dX
   __syncthreads();
-  for (int e = tid; e < m * m; e += 256) {
-    const int a = e / m, b = e % m;
-    float s = 0.f;
-#pragma unroll 8
-    for (int c = 0; c < m; ++c) s = fmaf(tmp[a * 65 + c], xs[b * 65 + c], s);
-    dw[(size_t)p * m * m + e] = -s;
-  }
+  mm64<64, false, true>(rsm, xs, dxs, 64, -1.f);  // dW = -R X^T (into the dX buffer)
+  __syncthreads();
+  for (int e = tid; e < m * m; e += 256) dw[(size_t)p * m * m + e] = dxs[(e / m) * 65 + e % m];
 }
 
 // Query side, first pass: one lane per token i of the tile.  G_ij =

@@ -49,50 +49,59 @@ __device__ __forceinline__ void load_row(const T* __restrict__ src, float (&x)[D
 }
 
 // Partial C^T g and 1^T g over one tile of tokens: part[p][tile][j][f],
-// spart[p][tile][f].  Thread (jg, f): feature f, landmarks jg, jg + G, ...
-// The tile's tokens pass through LDS in chunks of 64: the C^T entries of all
-// landmarks and the rows of g, loaded coalesced, then summed in token order.
+// spart[p][tile][f].  The tile's tokens pass through LDS in chunks of 64 (the
+// C^T entries of all landmarks, zero past m, and the rows of g); C^T g runs on
+// fp32 MFMA 16x16x4, wavefront w forming landmark rows [16 w, 16 w + 16), and
+// lanes tid < D add up 1^T g in token order.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_ctg_kernel(const float* __restrict__ ct, int ldc,
                                                       const float* __restrict__ dout, float* __restrict__ part,
                                                       float* __restrict__ spart, int N, int m, int ntiles) {
   constexpr int kC = 64;
-  __shared__ float cs[64 * kC];  // [j][i]
-  __shared__ float gs[kC * D];   // [i][f]
-  constexpr int G = 256 / D;
+  constexpr int kCS = kC + 1, kGS = D + 1;
+  __shared__ float cs[64 * kCS];  // [j][i]
+  __shared__ float gs[kC * kGS];  // [i][f]
   const int tile = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, li = lane & 15, lk = lane >> 4;
   const int t0 = tile * kBT, nv = min(kBT, N - t0);
-  const int f = tid % D, jg = tid / D;
-  float acc[64 / G];
+  f32x4 acc[D / 16];
 #pragma unroll
-  for (int u = 0; u < 64 / G; ++u) acc[u] = 0.f;
+  for (int bj = 0; bj < D / 16; ++bj) acc[bj] = f32x4{0.f, 0.f, 0.f, 0.f};
   float s = 0.f;
   for (int c0 = 0; c0 < nv; c0 += kC) {
     const int nc = min(kC, nv - c0);
     __syncthreads();  // the previous chunk's reads are done
     for (int e = tid; e < 64 * kC; e += 256) {
       const int j = e / kC, i = e % kC;
-      cs[e] = (j < m && i < nc) ? ct[((size_t)p * m + min(j, m - 1)) * ldc + t0 + c0 + i] : 0.f;
+      const float c = ct[((size_t)p * m + min(j, m - 1)) * ldc + t0 + c0 + min(i, nc - 1)];
+      cs[j * kCS + i] = (j < m && i < nc) ? c : 0.f;
     }
     for (int e = tid; e < kC * D; e += 256) {
-      const int i = e / D;
-      gs[e] = i < nc ? dout[((size_t)p * N + t0 + c0 + i) * D + e % D] : 0.f;
+      const int i = e / D, f = e % D;
+      const float g = dout[((size_t)p * N + t0 + c0 + min(i, nc - 1)) * D + f];
+      gs[i * kGS + f] = i < nc ? g : 0.f;
     }
     __syncthreads();
-    for (int i = 0; i < nc; ++i) {
-      const float gv = gs[i * D + f];
-      s += gv;
+#pragma unroll 4
+    for (int k0 = 0; k0 < kC; k0 += 4) {
+      const float a = cs[(16 * w + li) * kCS + k0 + lk];
 #pragma unroll
-      for (int u = 0; u < 64 / G; ++u) acc[u] = fmaf(cs[(jg + G * u) * kC + i], gv, acc[u]);
+      for (int bj = 0; bj < D / 16; ++bj)
+        acc[bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, gs[(k0 + lk) * kGS + 16 * bj + li], acc[bj], 0, 0, 0);
     }
+    if (tid < D)
+      for (int i = 0; i < nc; ++i) s += gs[i * kGS + tid];
   }
+  // acc[bj][r] = (C^T g)[16 w + 4 lk + r][16 bj + li]
   float* pp = part + (((size_t)p * ntiles + tile) * m) * D;
 #pragma unroll
-  for (int u = 0; u < 64 / G; ++u) {
-    const int j = jg + G * u;
-    if (j < m) pp[(size_t)j * D + f] = acc[u];
-  }
-  if (jg == 0) spart[((size_t)p * ntiles + tile) * D + f] = s;
+  for (int bj = 0; bj < D / 16; ++bj)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = 16 * w + 4 * lk + r;
+      if (j < m) pp[(size_t)j * D + 16 * bj + li] = acc[bj][r];
+    }
+  if (tid < D) spart[((size_t)p * ntiles + tile) * D + tid] = s;
 }
 
 // LDS of bwd_small_kernel: five 64-row matrices of row stride 65 (X, the m x m

@@ -201,9 +201,10 @@ int lapnys_forward_profiled(const void* q, const void* k, const void* v, float* 
  * forward's output for the same inputs and params.  The call runs the forward
  * itself (into the workspace; dq holds O until it is overwritten) and then the
  * backward kernels.  The inverse enters as X = W^-1 (dW = -X^T dX X^T, with X
- * the Newton-Schulz result).  Supported: m <= 64, the Laplacian kernel, the
- * Newton-Schulz solver (with or without LAPNYS_NS_REFINE / LAPNYS_NS_PLAIN);
- * otherwise LAPNYS_ERR_UNSUPPORTED.  dout: device float32 [B,H,N,d]; dq, dk,
+ * the Newton-Schulz result).  Supported: the Laplacian kernel with the
+ * Newton-Schulz solver (with or without LAPNYS_NS_REFINE / LAPNYS_NS_PLAIN),
+ * every m the forward supports; with LAPNYS_GAUSSIAN or LAPNYS_SOLVER_CG,
+ * LAPNYS_ERR_UNSUPPORTED.  dout: device float32 [B,H,N,d]; dq, dk,
  * dv: device float32 [B,H,N,d] outputs; all 16-byte aligned, the outputs
  * overlapping neither each other, the inputs nor ws.  ws: at least
  * lapnys_backward_workspace_size bytes, 256-byte aligned. */

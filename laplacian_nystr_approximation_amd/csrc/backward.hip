@@ -1,8 +1,8 @@
 // Backward pass of the Laplacian-kernel Nystrom attention (the pages' kernels
 // serve the forward and the backward pass: EN page, section 3; the L1 kernel's
 // gradient stays away from zero near coincident points: EN section 2.A).  The
-// gradients of sum(dO * O) with respect to Q, K and V, for m <= 64, after a
-// forward call has filled the workspace.  X stands for W^-1 in the derivative
+// gradients of sum(dO * O) with respect to Q, K and V after a forward call has
+// filled the workspace.  X stands for W^-1 in the derivative
 // (the implicit reading: dW = -X^T dX X^T), which the converged Newton-Schulz
 // iterate approximates.  Per problem, with Z = (C - mu) / sigma, Y = X (B V),
 // O = Z Y, g = dO:
@@ -49,10 +49,11 @@ __device__ __forceinline__ void load_row(const T* __restrict__ src, float (&x)[D
 }
 
 // Partial C^T g and 1^T g over one tile of tokens: part[p][tile][j][f],
-// spart[p][tile][f].  The tile's tokens pass through LDS in chunks of 64 (the
-// C^T entries of all landmarks, zero past m, and the rows of g); C^T g runs on
-// fp32 MFMA 16x16x4, wavefront w forming landmark rows [16 w, 16 w + 16), and
-// lanes tid < D add up 1^T g in token order.
+// spart[p][tile][f].  Workgroup (tile, p, jb) takes landmarks [64 jb, 64 jb +
+// 64).  The tile's tokens pass through LDS in chunks of 64 (the C^T entries of
+// those landmarks, zero past m, and the rows of g); C^T g runs on fp32 MFMA
+// 16x16x4, wavefront w forming landmark rows 64 jb + [16 w, 16 w + 16), and
+// lanes tid < D of block 0 add up 1^T g in token order.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_ctg_kernel(const float* __restrict__ ct, int ldc,
                                                       const float* __restrict__ dout, float* __restrict__ part,
@@ -61,9 +62,10 @@ __global__ __launch_bounds__(256) void bwd_ctg_kernel(const float* __restrict__ 
   constexpr int kCS = kC + 1, kGS = D + 1;
   __shared__ float cs[64 * kCS];  // [j][i]
   __shared__ float gs[kC * kGS];  // [i][f]
-  const int tile = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
+  const int tile = blockIdx.x, p = blockIdx.y, j0 = 64 * blockIdx.z, tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, li = lane & 15, lk = lane >> 4;
   const int t0 = tile * kBT, nv = min(kBT, N - t0);
+  const bool sums = blockIdx.z == 0;
   f32x4 acc[D / 16];
 #pragma unroll
   for (int bj = 0; bj < D / 16; ++bj) acc[bj] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -72,9 +74,9 @@ __global__ __launch_bounds__(256) void bwd_ctg_kernel(const float* __restrict__ 
     const int nc = min(kC, nv - c0);
     __syncthreads();  // the previous chunk's reads are done
     for (int e = tid; e < 64 * kC; e += 256) {
-      const int j = e / kC, i = e % kC;
+      const int j = j0 + e / kC, i = e % kC;
       const float c = ct[((size_t)p * m + min(j, m - 1)) * ldc + t0 + c0 + min(i, nc - 1)];
-      cs[j * kCS + i] = (j < m && i < nc) ? c : 0.f;
+      cs[(e / kC) * kCS + i] = (j < m && i < nc) ? c : 0.f;
     }
     for (int e = tid; e < kC * D; e += 256) {
       const int i = e / D, f = e % D;
@@ -89,7 +91,7 @@ __global__ __launch_bounds__(256) void bwd_ctg_kernel(const float* __restrict__ 
       for (int bj = 0; bj < D / 16; ++bj)
         acc[bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, gs[(k0 + lk) * kGS + 16 * bj + li], acc[bj], 0, 0, 0);
     }
-    if (tid < D)
+    if (sums && tid < D)
       for (int i = 0; i < nc; ++i) s += gs[i * kGS + tid];
   }
   // acc[bj][r] = (C^T g)[16 w + 4 lk + r][16 bj + li]
@@ -98,10 +100,10 @@ __global__ __launch_bounds__(256) void bwd_ctg_kernel(const float* __restrict__ 
   for (int bj = 0; bj < D / 16; ++bj)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int j = 16 * w + 4 * lk + r;
+      const int j = j0 + 16 * w + 4 * lk + r;
       if (j < m) pp[(size_t)j * D + 16 * bj + li] = acc[bj][r];
     }
-  if (tid < D) spart[((size_t)p * ntiles + tile) * D + tid] = s;
+  if (sums && tid < D) spart[((size_t)p * ntiles + tile) * D + tid] = s;
 }
 
 // LDS of bwd_small_kernel: five 64-row matrices of row stride 65 (X, the m x m
@@ -137,10 +139,10 @@ __device__ __forceinline__ void mm64(const float* __restrict__ a, const float* _
     for (int r = 0; r < 4; ++r) out[(16 * w + 4 * lk + r) * 65 + 16 * bj + li] = sign * acc[bj][r];
 }
 
-// Per problem (one workgroup): reduce the partials, then Y, dY, a, b, dBV and
-// dW = -X^T (dY BV^T) X^T, every matrix zero padded to 64 rows in LDS and the
-// products on fp32 MFMA.  x: the Newton-Schulz result, row stride mp.
-// Outputs: y, dbv [P][m][D]; ab [P][2][m]; dw [P][m][m].
+// m <= 64, per problem (one workgroup): reduce the partials, then Y, dY, a, b,
+// dBV and R X^T = X^T (dY BV^T) X^T = -dW, every matrix zero padded to 64 rows
+// in LDS and the products on fp32 MFMA.  x: the Newton-Schulz result, row
+// stride mp (= 64).  Outputs: y, dbv [P][m][D]; ab [P][2][m]; dw [P][mp][mp].
 template <int D>
 __global__ __launch_bounds__(256) void bwd_small_kernel(const float* __restrict__ part,
                                                         const float* __restrict__ spart,
@@ -203,9 +205,59 @@ __global__ __launch_bounds__(256) void bwd_small_kernel(const float* __restrict_
   for (int e = tid; e < m * D; e += 256) dbv[(size_t)p * m * D + e] = ys[(e / D) * 65 + e % D];
   mm64<64, true, false>(xs, dxs, rsm, 64, 1.f);  // R = X^T dX
   __syncthreads();
-  mm64<64, false, true>(rsm, xs, dxs, 64, -1.f);  // dW = -R X^T (into the dX buffer)
+  mm64<64, false, true>(rsm, xs, dxs, 64, 1.f);  // R X^T = -dW (into the dX buffer)
   __syncthreads();
-  for (int e = tid; e < m * m; e += 256) dw[(size_t)p * m * m + e] = dxs[(e / m) * 65 + e % m];
+  for (int e = tid; e < m * m; e += 256) dw[((size_t)p * mp + e / m) * mp + e % m] = dxs[(e / m) * 65 + e % m];
+}
+
+// m > 64: dY = (C^T g - mu (1^T g)) / sigma from the partials into dy
+// [P][mp][D] (zero rows past m), and 1^T g into s [P][D].
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dy_kernel(const float* __restrict__ part, const float* __restrict__ spart,
+                                                     const float* __restrict__ mu, const float* __restrict__ rs,
+                                                     float* __restrict__ dy, float* __restrict__ sg, int m, int mp,
+                                                     int ntiles) {
+  const int p = blockIdx.y, e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= mp * D) return;
+  const int j = e / D, f = e % D;
+  float sv = 0.f;
+  for (int t = 0; t < ntiles; ++t) sv += spart[((size_t)p * ntiles + t) * D + f];
+  if (j == 0) sg[(size_t)p * D + f] = sv;
+  float c = 0.f;
+  if (j < m) {
+    for (int t = 0; t < ntiles; ++t) c += part[(((size_t)p * ntiles + t) * m + j) * D + f];
+    c = (c - mu[p * m + j] * sv) * rs[p * m + j];
+  }
+  dy[(size_t)p * mp * D + e] = c;
+}
+
+// m > 64: a_j = (1^T g) . Y_j / N and b_j = Y_j . dY_j / N (0 with whitening off).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_ab_kernel(const float* __restrict__ y, const float* __restrict__ dy,
+                                                     const float* __restrict__ sg, float* __restrict__ ab, int N,
+                                                     int m, int mp, int whiten) {
+  const int p = blockIdx.y, j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= m) return;
+  float a = 0.f, b = 0.f;
+  for (int f = 0; f < D; ++f) {
+    const float yv = y[((size_t)p * m + j) * D + f];
+    a = fmaf(sg[(size_t)p * D + f], yv, a);
+    b = fmaf(yv, dy[((size_t)p * mp + j) * D + f], b);
+  }
+  ab[(size_t)p * 2 * m + j] = whiten ? a / (float)N : 0.f;
+  ab[(size_t)p * 2 * m + m + j] = whiten ? b / (float)N : 0.f;
+}
+
+// dst[c][r] = src[r][c] for r < rows, c < cols; zero for r in [rows, rp) (per
+// problem; src row stride lds, dst row stride rp).
+__global__ __launch_bounds__(256) void bwd_transpose_kernel(const float* __restrict__ src, int lds_, long long ss,
+                                                            float* __restrict__ dst, long long sd, int rows, int cols,
+                                                            int rp) {
+  const int p = blockIdx.y;
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (long long)cols * rp) return;
+  const int c = (int)(e / rp), r = (int)(e % rp);
+  dst[p * sd + e] = r < rows ? src[p * ss + (long long)r * lds_ + c] : 0.f;
 }
 
 // Query side, first pass: one lane per token i of the tile.  G_ij =
@@ -216,7 +268,7 @@ __global__ __launch_bounds__(256) void bwd_g_kernel(const float* __restrict__ do
                                                     const float* __restrict__ mu, const float* __restrict__ rs,
                                                     const float* __restrict__ ab, float* __restrict__ gt, int N,
                                                     int m) {
-  __shared__ float yls[64 * D];
+  extern __shared__ __align__(16) float yls[];  // [m][D]
   const int tile = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
   for (int e = tid; e < m * D; e += 256) yls[e] = y[(size_t)p * m * D + e];
   __syncthreads();
@@ -243,7 +295,8 @@ __global__ __launch_bounds__(256) void bwd_hv_kernel(const T* __restrict__ k, co
                                                      const float* __restrict__ kt, const float* __restrict__ dbv,
                                                      float* __restrict__ ht, float* __restrict__ dv, int N, int m,
                                                      float scale) {
-  __shared__ float kls[64 * D], dls[64 * D];
+  extern __shared__ __align__(16) float kls[];  // [m][D] K~, then [m][D] dBV
+  float* dls = kls + m * D;
   const int tile = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
   for (int e = tid; e < m * D; e += 256) {
     kls[e] = kt[(size_t)p * m * D + e];
@@ -284,7 +337,7 @@ __global__ __launch_bounds__(256) void bwd_sign_kernel(const T* __restrict__ x, 
                                                        const float* __restrict__ wt, float* __restrict__ out, int N,
                                                        int m, float inv_lam, const float* __restrict__ dkt,
                                                        int grid_w, int pool, int gw) {
-  __shared__ float kls[64 * D];  // K~ * 2^64
+  extern __shared__ __align__(16) float kls[];  // [m][D] K~ * 2^64
   const int tile = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
   for (int e = tid; e < m * D; e += 256) kls[e] = kt[(size_t)p * m * D + e] * kSgnScale;
   __syncthreads();
@@ -382,11 +435,11 @@ __global__ __launch_bounds__(256) void bwd_kt_kernel(const T* __restrict__ q, co
   for (int bb = 0; bb < m; ++bb) {
     float wv = w[(size_t)p * mp * mp + (size_t)j * mp + bb];
     if (bb == j) wv -= eps;
-    const float dws = dw[((size_t)p * m + j) * m + bb] + dw[((size_t)p * m + bb) * m + j];
+    const float dws = dw[((size_t)p * mp + j) * mp + bb] + dw[((size_t)p * mp + bb) * mp + j];
     c = fmaf(dws * wv, sgn(kj - kt[((size_t)p * m + bb) * D + t]), c);
   }
-  // sum_n H_jn sign(K~_j - k_n) = -sums[1]
-  dkt[((size_t)p * m + j) * D + t] = (sums[0] + sums[1] - c) * inv_lam;
+  // sum_n H_jn sign(K~_j - k_n) = -sums[1]; dw holds -dW, so -c is +c here.
+  dkt[((size_t)p * m + j) * D + t] = (sums[0] + sums[1] + c) * inv_lam;
 }
 
 template <typename T, int D>
@@ -394,26 +447,56 @@ hipError_t launch_typed(const Plan& pl, const BwdWork& b, const Work& w, const v
                         const void* v, const float* dout, float* dq, float* dk, float* dv, hipStream_t s) {
   const int nt = (pl.N + kBT - 1) / kBT;
   const float inv_lam = -pl.scale / 1.4426950408889634f;  // 1 / lambda from scale = -log2(e) / lambda
-  hipLaunchKernelGGL(bwd_ctg_kernel<D>, dim3(nt, pl.P), dim3(256), 0, s, w.ct, pl.ldc, dout, b.part, b.spart, pl.N,
-                     pl.m, nt);
-  constexpr size_t small_lds = bwd_small_lds<D>();
-  hipError_t e = hipFuncSetAttribute((const void*)bwd_small_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)small_lds);
+  const int mp = pl.mp, m = pl.m;
+  hipLaunchKernelGGL(bwd_ctg_kernel<D>, dim3(nt, pl.P, (m + 63) / 64), dim3(256), 0, s, w.ct, pl.ldc, dout, b.part,
+                     b.spart, pl.N, m, nt);
+  hipError_t e;
+  if (m <= 64) {
+    constexpr size_t small_lds = bwd_small_lds<D>();
+    e = hipFuncSetAttribute((const void*)bwd_small_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)small_lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_small_kernel<D>, dim3(pl.P), dim3(256), small_lds, s, b.part, b.spart, w.x_final, mp,
+                       w.bv, w.mu, w.rs, b.y, b.dbv, b.ab, b.dw, pl.N, m, nt, pl.whiten ? 1 : 0);
+  } else {
+    // The same quantities with the products on the tile GEMM, in the workspace.
+    const long long sq = (long long)mp * mp, md = (long long)m * D, mpd = (long long)mp * D;
+    const int kext = (m + 31) & ~31;
+    hipLaunchKernelGGL(bwd_dy_kernel<D>, dim3((mp * D + 255) / 256, pl.P), dim3(256), 0, s, b.part, b.spart, w.mu,
+                       w.rs, b.dy, b.s, m, mp, nt);
+    e = launch_gemm(w.x_final, mp, sq, w.bv, D, md, m, D, b.y, D, md, m, D, kext, pl.P, s);  // Y = X BV
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_ab_kernel<D>, dim3((m + 255) / 256, pl.P), dim3(256), 0, s, b.y, b.dy, b.s, b.ab, pl.N, m,
+                       mp, pl.whiten ? 1 : 0);
+    hipLaunchKernelGGL(bwd_transpose_kernel, dim3((unsigned)((sq + 255) / 256), pl.P), dim3(256), 0, s, w.x_final,
+                       mp, sq, b.xt, sq, mp, mp, mp);  // X^T
+    hipLaunchKernelGGL(bwd_transpose_kernel, dim3((unsigned)((D * mp + 255) / 256), pl.P), dim3(256), 0, s, w.bv, D,
+                       md, b.bvt, (long long)D * mp, m, D, mp);  // BV^T, zero past m
+    e = launch_gemm(b.xt, mp, sq, b.dy, D, mpd, mp, D, b.dbv, D, md, m, D, kext, pl.P, s);  // dBV = X^T dY
+    if (e != hipSuccess) return e;
+    e = launch_gemm(b.dy, D, mpd, b.bvt, mp, (long long)D * mp, D, mp, b.dx, mp, sq, mp, mp, D, pl.P, s);  // dX
+    if (e != hipSuccess) return e;
+    e = launch_gemm(b.xt, mp, sq, b.dx, mp, sq, mp, mp, b.r, mp, sq, mp, mp, kext, pl.P, s);  // R = X^T dX
+    if (e != hipSuccess) return e;
+    e = launch_gemm(b.r, mp, sq, b.xt, mp, sq, mp, mp, b.dw, mp, sq, mp, mp, kext, pl.P, s);  // R X^T = -dW
+    if (e != hipSuccess) return e;
+  }
+  const size_t row_lds = (size_t)m * D * sizeof(float);  // <= 64 KB
+  hipLaunchKernelGGL(bwd_g_kernel<D>, dim3(nt, pl.P), dim3(256), row_lds, s, dout, w.ct, pl.ldc, b.y, w.mu, w.rs,
+                     b.ab, b.gt, pl.N, m);
+  hipLaunchKernelGGL((bwd_sign_kernel<T, D>), dim3(nt, pl.P), dim3(256), row_lds, s, (const T*)q, w.kt, b.gt, dq,
+                     pl.N, m, inv_lam, nullptr, pl.grid_w, pl.pool, pl.gw);
+  e = hipFuncSetAttribute((const void*)bwd_hv_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)(2 * row_lds));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_small_kernel<D>, dim3(pl.P), dim3(256), small_lds, s, b.part, b.spart, w.x_final, pl.mp,
-                     w.bv, w.mu, w.rs, b.y, b.dbv, b.ab, b.dw, pl.N, pl.m, nt, pl.whiten ? 1 : 0);
-  hipLaunchKernelGGL(bwd_g_kernel<D>, dim3(nt, pl.P), dim3(256), 0, s, dout, w.ct, pl.ldc, b.y, w.mu, w.rs, b.ab,
-                     b.gt, pl.N, pl.m);
-  hipLaunchKernelGGL((bwd_sign_kernel<T, D>), dim3(nt, pl.P), dim3(256), 0, s, (const T*)q, w.kt, b.gt, dq, pl.N,
-                     pl.m, inv_lam, nullptr, pl.grid_w, pl.pool, pl.gw);
-  hipLaunchKernelGGL((bwd_hv_kernel<T, D>), dim3(nt, pl.P), dim3(256), 0, s, (const T*)k, (const T*)v, w.kt, b.dbv,
-                     b.ht, dv, pl.N, pl.m, pl.scale);
+  hipLaunchKernelGGL((bwd_hv_kernel<T, D>), dim3(nt, pl.P), dim3(256), 2 * row_lds, s, (const T*)k, (const T*)v, w.kt,
+                     b.dbv, b.ht, dv, pl.N, m, pl.scale);
   constexpr int LG = 256 / D;
   hipLaunchKernelGGL((bwd_kt_kernel<T, D>), dim3((pl.m + LG - 1) / LG, pl.P), dim3(256), 0, s, (const T*)q,
                      (const T*)k, w.kt, b.gt, b.ht, w.w, pl.mp, b.dw, b.dkt, pl.N, pl.m, pl.eps, inv_lam);
   // dK: the B part, plus the pooling adjoint of dK~.
-  hipLaunchKernelGGL((bwd_sign_kernel<T, D>), dim3(nt, pl.P), dim3(256), 0, s, (const T*)k, w.kt, b.ht, dk, pl.N,
-                     pl.m, inv_lam, b.dkt, pl.grid_w, pl.pool, pl.gw);
+  hipLaunchKernelGGL((bwd_sign_kernel<T, D>), dim3(nt, pl.P), dim3(256), row_lds, s, (const T*)k, w.kt, b.ht, dk,
+                     pl.N, m, inv_lam, b.dkt, pl.grid_w, pl.pool, pl.gw);
   return hipGetLastError();
 }
 
@@ -421,7 +504,6 @@ hipError_t launch_typed(const Plan& pl, const BwdWork& b, const Work& w, const v
 
 hipError_t launch_backward(const Plan& pl, const BwdWork& b, const Work& w, const void* q, const void* k,
                            const void* v, const float* dout, float* dq, float* dk, float* dv, hipStream_t s) {
-  if (pl.m > 64) return hipErrorInvalidValue;
   if (pl.dtype == 1) {
     return pl.d == 64 ? launch_typed<uint16_t, 64>(pl, b, w, q, k, v, dout, dq, dk, dv, s)
                       : launch_typed<uint16_t, 32>(pl, b, w, q, k, v, dout, dq, dk, dv, s);

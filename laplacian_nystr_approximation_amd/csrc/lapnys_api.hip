@@ -309,16 +309,22 @@ int forward_impl(const void* q, const void* k, const void* v, float* out, const 
 }
 
 // Backward buffers after the forward's workspace (each 256-byte aligned).
-int backward_plan(const lapnys_params* p, Plan* pl, size_t off[9], size_t* total) {
+constexpr int kBwdBuffers = 15;
+
+int backward_plan(const lapnys_params* p, Plan* pl, size_t off[kBwdBuffers], size_t* total) {
   const int st = make_plan(p, pl);
   if (st != LAPNYS_OK) return st;
-  if (pl->m > lapnys::kFusedNsMaxM || pl->cg || pl->gaussian) return LAPNYS_ERR_UNSUPPORTED;
+  if (pl->cg || pl->gaussian) return LAPNYS_ERR_UNSUPPORTED;
   const size_t f = sizeof(float), Pn = (size_t)pl->P, m = (size_t)pl->m, d = (size_t)pl->d, N = (size_t)pl->N;
-  const size_t nt = (N + 255) / 256;
-  const size_t sizes[9] = {Pn * nt * m * d * f, Pn * nt * d * f, Pn * m * d * f, Pn * m * d * f, Pn * 2 * m * f,
-                           Pn * m * m * f,      Pn * m * N * f,  Pn * m * N * f, Pn * m * d * f};
+  const size_t mp = (size_t)pl->mp, nt = (N + 255) / 256;
+  const bool big = pl->m > lapnys::kFusedNsMaxM;
+  const size_t sizes[kBwdBuffers] = {
+      Pn * nt * m * d * f, Pn * nt * d * f, Pn * m * d * f, Pn * m * d * f, Pn * 2 * m * f, Pn * mp * mp * f,
+      Pn * m * N * f,      Pn * m * N * f,  Pn * m * d * f,
+      big ? Pn * mp * d * f : 0, big ? Pn * d * mp * f : 0, big ? Pn * d * f : 0, big ? Pn * mp * mp * f : 0,
+      big ? Pn * mp * mp * f : 0, big ? Pn * mp * mp * f : 0};
   size_t o = pl->total;
-  for (int i = 0; i < 9; ++i) {
+  for (int i = 0; i < kBwdBuffers; ++i) {
     off[i] = o;
     o = align256(o + sizes[i]);
   }
@@ -329,7 +335,7 @@ int backward_plan(const lapnys_params* p, Plan* pl, size_t off[9], size_t* total
 int backward_impl(const void* q, const void* k, const void* v, const float* dout, float* dq, float* dk, float* dv,
                   const lapnys_params* p, void* ws, size_t ws_bytes, hipStream_t s) {
   Plan pl;
-  size_t off[9], total = 0;
+  size_t off[kBwdBuffers], total = 0;
   int st = backward_plan(p, &pl, off, &total);
   if (st != LAPNYS_OK) return st;
   if (!dout || !dk || !dv || (((uintptr_t)dout | (uintptr_t)dk | (uintptr_t)dv) & 15)) return LAPNYS_ERR_INVALID_ARG;
@@ -355,8 +361,9 @@ int backward_impl(const void* q, const void* k, const void* v, const float* dout
   if (st != LAPNYS_OK) return st;
   char* b = (char*)ws;
   lapnys::BwdWork B;
-  float** slots[9] = {&B.part, &B.spart, &B.y, &B.dbv, &B.ab, &B.dw, &B.gt, &B.ht, &B.dkt};
-  for (int i = 0; i < 9; ++i) *slots[i] = (float*)(b + off[i]);
+  float** slots[kBwdBuffers] = {&B.part, &B.spart, &B.y,  &B.dbv, &B.ab, &B.dw, &B.gt, &B.ht,
+                                &B.dkt,  &B.dy,    &B.bvt, &B.s,   &B.xt, &B.dx, &B.r};
+  for (int i = 0; i < kBwdBuffers; ++i) *slots[i] = (float*)(b + off[i]);
   if (!ok(lapnys::launch_backward(pl, B, W, q, k, v, dout, dq, dk, dv, s), "backward launch")) return LAPNYS_ERR_HIP;
   return LAPNYS_OK;
 }
@@ -448,7 +455,7 @@ void lapnys_release(void) {
 int lapnys_backward_workspace_size(const lapnys_params* p, size_t* bytes) {
   if (!bytes) return LAPNYS_ERR_INVALID_ARG;
   Plan pl;
-  size_t off[9], total = 0;
+  size_t off[kBwdBuffers], total = 0;
   const int st = backward_plan(p, &pl, off, &total);
   if (st != LAPNYS_OK) return st;
   *bytes = total;

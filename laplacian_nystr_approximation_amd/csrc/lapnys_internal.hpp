@@ -109,12 +109,17 @@ struct Work {
   float* x_final;      // the Newton-Schulz result (x or x2), set by launch_ns
 };
 
-// Backward-pass buffers, after the forward's workspace (float32):
+// Backward-pass buffers, after the forward's workspace (float32; mp = m
+// rounded up to 64):
 //   part [P][tiles][m][d], spart [P][tiles][d]   partial C^T dO and 1^T dO
-//   y, dbv [P][m][d]; ab [P][2][m]; dw [P][m][m]; dkt [P][m][d]
+//   y, dbv [P][m][d]; ab [P][2][m]; dkt [P][m][d]
+//   dw [P][mp][mp]   R X^T with R = X^T dX, i.e. -dW
 //   gt, ht [P][m][N]                              G^T and H^T
+//   m > 64 only: dy [P][mp][d] (zero rows past m), bvt [P][d][mp], s [P][d],
+//   xt, dx, r [P][mp][mp]
 struct BwdWork {
   float *part, *spart, *y, *dbv, *ab, *dw, *gt, *ht, *dkt;
+  float *dy, *bvt, *s, *xt, *dx, *r;
 };
 
 // Position of Y^T element (feature f, landmark l) in a [D][rl] bf16 array (rl
@@ -161,9 +166,14 @@ hipError_t launch_y(const Plan& pl, const Work& w, hipStream_t s, Span t = {}); 
 hipError_t launch_cg(const Plan& pl, const Work& w, hipStream_t s, hipEvent_t stop = nullptr);
 hipError_t launch_output(const Plan& pl, const Work& w, float* out, hipStream_t s, Span t = {});
 // The gradients of sum(dout * O) into dq, dk, dv (float32 [B,H,N,d]) after a
-// forward call on the same workspace (m <= 64, Laplacian kernel, Newton-Schulz).
+// forward call on the same workspace (Laplacian kernel, Newton-Schulz).
 hipError_t launch_backward(const Plan& pl, const BwdWork& b, const Work& w, const void* q, const void* k,
                            const void* v, const float* dout, float* dq, float* dk, float* dv, hipStream_t s);
+// Batched C = A B on the tile GEMM (ns.hip): A rows [0, 64 ceil(crows / 64))
+// and columns [0, kext) in range, B read where in [0, brows) x [0, bcols).
+hipError_t launch_gemm(const float* A, int lda, long long sa, const float* B, int ldb, long long sb, int brows,
+                       int bcols, float* C, int ldc, long long sc, int crows, int ccols, int kext, int P,
+                       hipStream_t s);
 hipError_t launch_extract_square(const float* src, int src_ld, float* dst, int n, int P, hipStream_t s);
 
 }  // namespace lapnys

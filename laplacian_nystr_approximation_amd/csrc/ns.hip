@@ -532,6 +532,14 @@ hipError_t launch_y(const Plan& pl, const Work& wk, hipStream_t s, Span t) {
   return hipGetLastError();
 }
 
+hipError_t launch_gemm(const float* A, int lda, long long sa, const float* B, int ldb, long long sb, int brows,
+                       int bcols, float* C, int ldc, long long sc, int crows, int ccols, int kext, int P,
+                       hipStream_t s) {
+  hipLaunchKernelGGL(gemm64_kernel, dim3((crows + 63) / 64, (ccols + 63) / 64, P), dim3(256), 0, s, A, lda, sa, B,
+                     ldb, sb, brows, bcols, C, ldc, sc, crows, ccols, kext, 0);
+  return hipGetLastError();
+}
+
 hipError_t launch_extract_square(const float* src, int src_ld, float* dst, int n, int P, hipStream_t s) {
   const long long total = (long long)P * n * n;
   if (total == 0) return hipSuccess;

@@ -147,11 +147,11 @@ def test_plain_ns_flag():
 
 
 def test_backward_workspace_and_support():
-    """The backward workspace extends the forward's; m > 64, the Gaussian form
-    and CG are refused as unsupported before any device call."""
-    p = _p()
-    assert L.lapnys_backward_workspace_size(p) > L.lapnys_workspace_size(p)
-    for bad in (_p(grid_h=32, grid_w=32), _p(kernel="gaussian"), _p(solver="cg")):
+    """The backward workspace extends the forward's (at m = 49 and m = 256);
+    the Gaussian form and CG are refused as unsupported before any device call."""
+    for p in (_p(), _p(grid_h=32, grid_w=32)):
+        assert L.lapnys_backward_workspace_size(p) > L.lapnys_workspace_size(p)
+    for bad in (_p(kernel="gaussian"), _p(solver="cg")):
         n = ctypes.c_size_t(0)
         assert L.library().lapnys_backward_workspace_size(ctypes.byref(bad), ctypes.byref(n)) == \
             B.LAPNYS_ERR_UNSUPPORTED

@@ -30,6 +30,12 @@ def _cases():
         (WORKLOADS["stage3_14x14_bf16"], [0, 7, 319]),
         (WORKLOADS["stage1_56x56_f32"], [0, 31]),
         (dataclasses.replace(WORKLOADS["tiny_f32"], name="tiny_f32_plain", ns_plain=True), None),
+        # the tiled solver's sizes: m = 81, 100 and 256
+        (Workload("bwd_m81_18x18_p2", grid_h=18, grid_w=18, d=64, pool=2, dtype="f32", **base), None),
+        (Workload("bwd_m100_20x20_p2_d32", grid_h=20, grid_w=20, d=32, pool=2, dtype="f32", **base), None),
+        (Workload("bwd_m256_16x16_p1", grid_h=16, grid_w=16, d=64, pool=1, dtype="f32",
+                  **{**base, "ns_iters": 40}), None),
+        (WORKLOADS["sweep_64x64_bf16"], [0]),
     ]
 
 

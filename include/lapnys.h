@@ -204,7 +204,8 @@ int lapnys_forward_profiled(const void* q, const void* k, const void* v, float* 
  * the Newton-Schulz result).  Supported: the Laplacian kernel with the
  * Newton-Schulz solver (with or without LAPNYS_NS_REFINE / LAPNYS_NS_PLAIN),
  * every m the forward supports; with LAPNYS_GAUSSIAN or LAPNYS_SOLVER_CG,
- * LAPNYS_ERR_UNSUPPORTED.  dout: device float32 [B,H,N,d]; dq, dk,
+ * LAPNYS_ERR_UNSUPPORTED.  The sign of q - K~ and K~ - k is taken exactly (0
+ * on ties) for inputs below 2^63 in magnitude.  dout: device float32 [B,H,N,d]; dq, dk,
  * dv: device float32 [B,H,N,d] outputs; all 16-byte aligned, the outputs
  * overlapping neither each other, the inputs nor ws.  ws: at least
  * lapnys_backward_workspace_size bytes, 256-byte aligned. */

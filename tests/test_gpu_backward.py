@@ -36,6 +36,10 @@ def _cases():
         (Workload("bwd_m256_16x16_p1", grid_h=16, grid_w=16, d=64, pool=1, dtype="f32",
                   **{**base, "ns_iters": 40}), None),
         (WORKLOADS["sweep_64x64_bf16"], [0]),
+        # bf16 with d = 32, the refined inverse, whitening off at m > 64
+        (Workload("bwd_ragged_10x30_p5_d32", grid_h=10, grid_w=30, d=32, pool=5, dtype="bf16", **base), None),
+        (dataclasses.replace(WORKLOADS["tiny_f32"], name="tiny_f32_refine", refine=True), None),
+        (Workload("bwd_nowhiten_m81", grid_h=18, grid_w=18, d=64, pool=2, dtype="f32", whiten=False, **base), None),
     ]
 
 

@@ -70,20 +70,39 @@ __global__ __launch_bounds__(256) void bwd_ctg_kernel(const float* __restrict__ 
 #pragma unroll
   for (int bj = 0; bj < D / 16; ++bj) acc[bj] = f32x4{0.f, 0.f, 0.f, 0.f};
   float s = 0.f;
+  // Per lane, one chunk's loads (kCE entries of C^T, kGE of g), issued a chunk
+  // ahead so that they land while the current chunk's products run.
+  constexpr int kCE = 64 * kC / 256, kGE = kC * D / 256;
+  float cr[kCE], gr[kGE];
+  auto fetch = [&](int c0) {
+    const int nc = min(kC, nv - c0);
+#pragma unroll
+    for (int u = 0; u < kCE; ++u) {
+      const int e = tid + 256 * u, j = j0 + e / kC, i = e % kC;
+      cr[u] = ct[((size_t)p * m + min(j, m - 1)) * ldc + t0 + c0 + min(i, nc - 1)];
+    }
+#pragma unroll
+    for (int u = 0; u < kGE; ++u) {
+      const int e = tid + 256 * u, i = e / D, f = e % D;
+      gr[u] = dout[((size_t)p * N + t0 + c0 + min(i, nc - 1)) * D + f];
+    }
+  };
+  fetch(0);
   for (int c0 = 0; c0 < nv; c0 += kC) {
     const int nc = min(kC, nv - c0);
     __syncthreads();  // the previous chunk's reads are done
-    for (int e = tid; e < 64 * kC; e += 256) {
-      const int j = j0 + e / kC, i = e % kC;
-      const float c = ct[((size_t)p * m + min(j, m - 1)) * ldc + t0 + c0 + min(i, nc - 1)];
-      cs[(e / kC) * kCS + i] = (j < m && i < nc) ? c : 0.f;
+#pragma unroll
+    for (int u = 0; u < kCE; ++u) {
+      const int e = tid + 256 * u, j = j0 + e / kC, i = e % kC;
+      cs[(e / kC) * kCS + i] = (j < m && i < nc) ? cr[u] : 0.f;
     }
-    for (int e = tid; e < kC * D; e += 256) {
-      const int i = e / D, f = e % D;
-      const float g = dout[((size_t)p * N + t0 + c0 + min(i, nc - 1)) * D + f];
-      gs[i * kGS + f] = i < nc ? g : 0.f;
+#pragma unroll
+    for (int u = 0; u < kGE; ++u) {
+      const int e = tid + 256 * u, i = e / D, f = e % D;
+      gs[i * kGS + f] = i < nc ? gr[u] : 0.f;
     }
     __syncthreads();
+    if (c0 + kC < nv) fetch(c0 + kC);
 #pragma unroll 4
     for (int k0 = 0; k0 < kC; k0 += 4) {
       const float a = cs[(16 * w + li) * kCS + k0 + lk];
@@ -260,71 +279,191 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(const float* __restr
   dst[p * sd + e] = r < rows ? src[p * ss + (long long)r * lds_ + c] : 0.f;
 }
 
-// Query side, first pass: one lane per token i of the tile.  G_ij =
-// dC_ij C_ij for every landmark, stored as G^T[p][j][i].
+// Query side, first pass: G_ij = dC_ij C_ij, stored as G^T[p][j][i], with
+// dC_ij = (g_ij - a_j - z_ij b_j) r_j, z_ij = (C_ij - mu_j) r_j and g = dO Y^T.
+// Workgroup (tile, p) takes kGT tokens; per block of 64 landmarks, g^T for the
+// tile runs on fp32 MFMA 16x16x4 from Y and the tile's rows of dO in LDS
+// (wavefront w: landmarks 16 w + [0, 16)), and the lanes finish G^T from C^T
+// in their own accumulator positions.
+constexpr int kGT = 64;  // tokens per tile
+
 template <int D>
 __global__ __launch_bounds__(256) void bwd_g_kernel(const float* __restrict__ dout, const float* __restrict__ ct,
                                                     int ldc, const float* __restrict__ y,
                                                     const float* __restrict__ mu, const float* __restrict__ rs,
                                                     const float* __restrict__ ab, float* __restrict__ gt, int N,
                                                     int m) {
-  extern __shared__ __align__(16) float yls[];  // [m][D]
+  constexpr int kS = D + 1;
+  __shared__ float ys[64 * kS];   // [j][f] the block's Y rows
+  __shared__ float gs[kGT * kS];  // [i][f] the tile's dO rows
   const int tile = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
-  for (int e = tid; e < m * D; e += 256) yls[e] = y[(size_t)p * m * D + e];
-  __syncthreads();
-  const int i = tile * kBT + tid;
-  if (i >= N) return;
-  float gv[D];
-  load_row<float, D>(dout + ((size_t)p * N + i) * D, gv);
-  for (int j = 0; j < m; ++j) {
-    float g = 0.f;
+  const int lane = tid & 63, w = tid >> 6, li = lane & 15, lk = lane >> 4;
+  const int n0 = tile * kGT, nv = min(kGT, N - n0);
+  constexpr int kE = 64 * D / 256;
+  float gr[kE], yr[kE];
 #pragma unroll
-    for (int f = 0; f < D; ++f) g = fmaf(gv[f], yls[j * D + f], g);
-    const float c = ct[((size_t)p * m + j) * ldc + i];
-    const float r = rs[p * m + j];
-    const float z = (c - mu[p * m + j]) * r;
-    const float dc = (g - ab[(size_t)p * 2 * m + j] - z * ab[(size_t)p * 2 * m + m + j]) * r;
-    gt[((size_t)p * m + j) * N + i] = dc * c;
+  for (int u = 0; u < kE; ++u) {
+    const int e = tid + 256 * u, i = e / D, f = e % D;
+    gr[u] = dout[((size_t)p * N + n0 + min(i, nv - 1)) * D + f];
+  }
+  for (int j0 = 0; j0 < m; j0 += 64) {
+    const int jv = min(64, m - j0);
+#pragma unroll
+    for (int u = 0; u < kE; ++u) {
+      const int e = tid + 256 * u, jj = e / D, f = e % D;
+      yr[u] = y[((size_t)p * m + j0 + min(jj, jv - 1)) * D + f];
+    }
+    __syncthreads();  // the previous block's reads are done
+#pragma unroll
+    for (int u = 0; u < kE; ++u) {
+      const int e = tid + 256 * u, r = e / D, f = e % D;
+      ys[r * kS + f] = r < jv ? yr[u] : 0.f;
+      if (j0 == 0) gs[r * kS + f] = r < nv ? gr[u] : 0.f;
+    }
+    __syncthreads();
+    if (16 * w >= jv) continue;
+    f32x4 acc[kGT / 16];
+#pragma unroll
+    for (int bj = 0; bj < kGT / 16; ++bj) acc[bj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int k0 = 0; k0 < D; k0 += 4) {
+      const float av = ys[(16 * w + li) * kS + k0 + lk];
+#pragma unroll
+      for (int bj = 0; bj < kGT / 16; ++bj)
+        acc[bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, gs[(16 * bj + li) * kS + k0 + lk], acc[bj], 0, 0, 0);
+    }
+    // acc[bj][r] = g[token n0 + 16 bj + li][landmark j0 + 16 w + 4 lk + r]
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = j0 + 16 * w + 4 * lk + r;
+      if (j >= m) continue;
+      const float rj = rs[p * m + j], mj = mu[p * m + j];
+      const float aj = ab[(size_t)p * 2 * m + j], bj2 = ab[(size_t)p * 2 * m + m + j];
+#pragma unroll
+      for (int bj = 0; bj < kGT / 16; ++bj) {
+        const int i = 16 * bj + li;
+        if (i < nv) {
+          const float c = ct[((size_t)p * m + j) * ldc + n0 + i];
+          const float z = (c - mj) * rj;
+          const float dc = (acc[bj][r] - aj - z * bj2) * rj;
+          gt[((size_t)p * m + j) * N + n0 + i] = dc * c;
+        }
+      }
+    }
   }
 }
 
-// Key side, first pass: one lane per token n.  B recomputed from K~ and k_n;
-// H_jn = (dBV_j . v_n) B_jn stored as H^T[p][j][n]; dv_n = sum_j B_jn dBV_j.
+// Key side, first pass, on fp32 MFMA 16x16x4.  The forward left B in the
+// H^T buffer ([P][m][N]); workgroup (tile, p) takes kHT tokens and, per block
+// of 64 landmarks, stages that block's B, dBV and the tile's V in LDS, forms
+// dBV V^T (wavefront w: landmarks 16 w + [0, 16)) and overwrites B with
+// H = (dBV V^T) (.) B in place, and accumulates dV = B^T dBV over the blocks
+// (wavefront w: tokens 16 w + [0, 16)).  The dV reduction runs over the
+// block's landmarks rounded up to 4 (rows past m are zero).
+constexpr int kHT = 64;  // tokens per tile
+
+template <int D>
+constexpr size_t bwd_hv_lds() {
+  return (size_t)(64 * (D + 1) + kHT * (D + 1) + 64 * (kHT + 4)) * sizeof(float);
+}
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_hv_kernel(const T* __restrict__ k, const T* __restrict__ v,
-                                                     const float* __restrict__ kt, const float* __restrict__ dbv,
-                                                     float* __restrict__ ht, float* __restrict__ dv, int N, int m,
-                                                     float scale) {
-  extern __shared__ __align__(16) float kls[];  // [m][D] K~, then [m][D] dBV
-  float* dls = kls + m * D;
+__global__ __launch_bounds__(256, 3) void bwd_hv_kernel(const T* __restrict__ v, const float* __restrict__ dbv,
+                                                     float* __restrict__ ht, float* __restrict__ dv, int N, int m) {
+  constexpr int kVS = D + 1, kBS = kHT + 4;
+  extern __shared__ __align__(16) float lds[];
+  float* dbl = lds;             // [64][D+1]  the block's dBV rows
+  float* vs = dbl + 64 * kVS;   // [kHT][D+1] the tile's V rows
+  float* bs = vs + kHT * kVS;   // [64][kHT+4] B of the block and tile
   const int tile = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
-  for (int e = tid; e < m * D; e += 256) {
-    kls[e] = kt[(size_t)p * m * D + e];
-    dls[e] = dbv[(size_t)p * m * D + e];
-  }
-  __syncthreads();
-  const int n = tile * kBT + tid;
-  if (n >= N) return;
-  float kv[D], vv[D], acc[D];
-  load_row<T, D>(k + ((size_t)p * N + n) * D, kv);
-  load_row<T, D>(v + ((size_t)p * N + n) * D, vv);
+  const int lane = tid & 63, w = tid >> 6, li = lane & 15, lk = lane >> 4;
+  const int n0 = tile * kHT, nv = min(kHT, N - n0);
+  const size_t prob = (size_t)p * N * D;
+  // Staging: every global load of a phase is issued before its LDS stores.
+  constexpr int kVE = kHT * D / 256, kDE = 64 * D / 256, kBE = 64 * kHT / 256;
+  float vr[kVE], dr[kDE], br[kBE];
+  auto load_block = [&](int j0, int jv) {
 #pragma unroll
-  for (int t = 0; t < D; ++t) acc[t] = 0.f;
-  for (int j = 0; j < m; ++j) {
-    float l1 = 0.f, hd = 0.f;
-#pragma unroll
-    for (int t = 0; t < D; ++t) {
-      l1 += fabsf(kls[j * D + t] - kv[t]);
-      hd = fmaf(dls[j * D + t], vv[t], hd);
+    for (int i = 0; i < kDE; ++i) {
+      const int e = tid + 256 * i, jj = e / D, f = e % D;
+      dr[i] = dbv[((size_t)p * m + j0 + min(jj, jv - 1)) * D + f];
     }
-    const float b = exp2f(l1 * scale);
-    ht[((size_t)p * m + j) * N + n] = hd * b;
 #pragma unroll
-    for (int t = 0; t < D; ++t) acc[t] = fmaf(b, dls[j * D + t], acc[t]);
+    for (int i = 0; i < kBE; ++i) {
+      const int e = tid + 256 * i, jj = e / kHT, n = e % kHT;
+      br[i] = ht[((size_t)p * m + j0 + min(jj, jv - 1)) * N + n0 + min(n, nv - 1)];
+    }
+  };
+  auto store_block = [&](int jv) {
+#pragma unroll
+    for (int i = 0; i < kDE; ++i) {
+      const int e = tid + 256 * i, jj = e / D, f = e % D;
+      dbl[jj * kVS + f] = jj < jv ? dr[i] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < kBE; ++i) {
+      const int e = tid + 256 * i, jj = e / kHT, n = e % kHT;
+      bs[jj * kBS + n] = (jj < jv && n < nv) ? br[i] : 0.f;
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < kVE; ++i) {
+    const int e = tid + 256 * i, n = e / D, f = e % D;
+    vr[i] = widen(v[prob + (size_t)(n0 + min(n, nv - 1)) * D + f]);
   }
-  float* dvp = dv + ((size_t)p * N + n) * D;
+  load_block(0, min(64, m));
 #pragma unroll
-  for (int t = 0; t < D; ++t) dvp[t] = acc[t];
+  for (int i = 0; i < kVE; ++i) {
+    const int e = tid + 256 * i, n = e / D, f = e % D;
+    vs[n * kVS + f] = n < nv ? vr[i] : 0.f;
+  }
+  f32x4 adv[D / 16];
+#pragma unroll
+  for (int bj = 0; bj < D / 16; ++bj) adv[bj] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < m; j0 += 64) {
+    const int jv = min(64, m - j0);
+    if (j0 > 0) {
+      load_block(j0, jv);
+      __syncthreads();  // the previous block's reads are done
+    }
+    store_block(jv);
+    __syncthreads();
+    // H = (dBV V^T) (.) B: landmarks 16 w + [0, 16) of the block, every token.
+    if (16 * w < jv) {
+      f32x4 acc[kHT / 16];
+#pragma unroll
+      for (int bj = 0; bj < kHT / 16; ++bj) acc[bj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int k0 = 0; k0 < D; k0 += 4) {
+        const float a = dbl[(16 * w + li) * kVS + k0 + lk];
+#pragma unroll
+        for (int bj = 0; bj < kHT / 16; ++bj)
+          acc[bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, vs[(16 * bj + li) * kVS + k0 + lk], acc[bj], 0, 0, 0);
+      }
+#pragma unroll
+      for (int bj = 0; bj < kHT / 16; ++bj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int jj = 16 * w + 4 * lk + r, n = 16 * bj + li;
+          if (jj < jv && n < nv) ht[((size_t)p * m + j0 + jj) * N + n0 + n] = acc[bj][r] * bs[jj * kBS + n];
+        }
+    }
+    // dV += B^T dBV: tokens 16 w + [0, 16).
+    const int kend = (jv + 3) & ~3;
+    for (int k0 = 0; k0 < kend; k0 += 4) {
+      const float bt = bs[(k0 + lk) * kBS + 16 * w + li];
+#pragma unroll
+      for (int bj = 0; bj < D / 16; ++bj)
+        adv[bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(bt, dbl[(k0 + lk) * kVS + 16 * bj + li], adv[bj], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int bj = 0; bj < D / 16; ++bj)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int n = 16 * w + 4 * lk + r;
+      if (n < nv) dv[prob + (size_t)(n0 + n) * D + 16 * bj + li] = adv[bj][r];
+    }
 }
 
 // Token-side sign sums, one lane per token n: out_n = -(1/lambda) sum_j
@@ -482,15 +621,14 @@ hipError_t launch_typed(const Plan& pl, const BwdWork& b, const Work& w, const v
     if (e != hipSuccess) return e;
   }
   const size_t row_lds = (size_t)m * D * sizeof(float);  // <= 64 KB
-  hipLaunchKernelGGL(bwd_g_kernel<D>, dim3(nt, pl.P), dim3(256), row_lds, s, dout, w.ct, pl.ldc, b.y, w.mu, w.rs,
-                     b.ab, b.gt, pl.N, m);
+  hipLaunchKernelGGL(bwd_g_kernel<D>, dim3((pl.N + kGT - 1) / kGT, pl.P), dim3(256), 0, s, dout, w.ct, pl.ldc, b.y,
+                     w.mu, w.rs, b.ab, b.gt, pl.N, m);
   hipLaunchKernelGGL((bwd_sign_kernel<T, D>), dim3(nt, pl.P), dim3(256), row_lds, s, (const T*)q, w.kt, b.gt, dq,
                      pl.N, m, inv_lam, nullptr, pl.grid_w, pl.pool, pl.gw);
-  e = hipFuncSetAttribute((const void*)bwd_hv_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)(2 * row_lds));
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_hv_kernel<T, D>), dim3(nt, pl.P), dim3(256), 2 * row_lds, s, (const T*)k, (const T*)v, w.kt,
-                     b.dbv, b.ht, dv, pl.N, m, pl.scale);
+  constexpr size_t hv_lds = bwd_hv_lds<D>();
+  static_assert(hv_lds <= 65536, "the key-side first pass fits in static-size LDS");
+  hipLaunchKernelGGL((bwd_hv_kernel<T, D>), dim3((pl.N + kHT - 1) / kHT, pl.P), dim3(256), hv_lds, s, (const T*)v,
+                     b.dbv, b.ht, dv, pl.N, m);
   constexpr int LG = 256 / D;
   hipLaunchKernelGGL((bwd_kt_kernel<T, D>), dim3((pl.m + LG - 1) / LG, pl.P), dim3(256), 0, s, (const T*)q,
                      (const T*)k, w.kt, b.gt, b.ht, w.w, pl.mp, b.dw, b.dkt, pl.N, pl.m, pl.eps, inv_lam);

@@ -58,7 +58,8 @@ constexpr int kSrc[4] = {kLds, kLds, kLds, kLds};
 template <int D, bool SPLIT>
 __device__ __forceinline__ void kernel_row(const float (&x)[D], const float* __restrict__ kl,
                                            const float* __restrict__ kg, int lb, float scale, float* __restrict__ tl,
-                                           int rows, int col, bool valid) {
+                                           int rows, int col, bool valid, float* __restrict__ bout = nullptr,
+                                           int ldb = 0) {
   auto put = [&](int j, float sum) {
     const float val = valid ? exp2f(sum * scale) : 0.f;
     if constexpr (SPLIT) {
@@ -66,6 +67,7 @@ __device__ __forceinline__ void kernel_row(const float (&x)[D], const float* __r
       const __bf16 hi = (__bf16)val;
       th[j * kRB + col] = hi;
       th[(rows + j) * kRB + col] = (__bf16)(val - (float)hi);
+      if (bout != nullptr && valid) bout[(size_t)j * ldb] = val;
     } else {
       tl[j * kTP + col] = val;
     }
@@ -125,9 +127,9 @@ template <typename T, int D, int LBB>
 __device__ __forceinline__ void l1exp_body(const T* __restrict__ q, const T* __restrict__ k,
                                            const T* __restrict__ v, const float* __restrict__ kt,
                                            float* __restrict__ ct, float2* __restrict__ stats,
-                                           float* __restrict__ bvpart, int N, int ldc, int m, int lbmax, int ntiles,
-                                           int tpg, int groups, float scale, int jb, int g, int p,
-                                           float* __restrict__ tl) {
+                                           float* __restrict__ bvpart, float* __restrict__ bt, int N, int ldc,
+                                           int m, int lbmax, int ntiles, int tpg, int groups, float scale, int jb,
+                                           int g, int p, float* __restrict__ tl) {
   // tl: the tile buffer, (lbmax + 1) * kTileRow floats; then kl: [lb][D],
   // this block's landmark rows
   float* kl = tl + (lbmax + 1) * kTileRow;
@@ -188,7 +190,8 @@ __device__ __forceinline__ void l1exp_body(const T* __restrict__ q, const T* __r
     // ---- B = k(K~, K), kept on chip ----
     widen_row<D>(raw, x);
     __syncthreads();  // statistics pass done with the tile buffer
-    kernel_row<D, true>(x, kl, kg, lb, scale, tl, lbmax + 1, tid, valid);
+    kernel_row<D, true>(x, kl, kg, lb, scale, tl, lbmax + 1, tid, valid,
+                        bt != nullptr ? bt + ((size_t)p * m + j0) * N + t0 + tid : nullptr, N);
     __syncthreads();
 
     // ---- B V partial: acc[landmark][feature] += sum over the tile's tokens ----
@@ -215,8 +218,8 @@ __device__ __forceinline__ void l1exp_body(const T* __restrict__ q, const T* __r
 template <typename T, int D, int LBB, int KS>
 __global__ __launch_bounds__(kTT) void l1exp_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ kt,
-    float* __restrict__ ct, float2* __restrict__ stats, float* __restrict__ bvpart, float* __restrict__ wout,
-    float* __restrict__ xout, int N, int ldc, int m, int lbmax, int ntiles, int tpg, int groups, int jblocks,
+    float* __restrict__ ct, float2* __restrict__ stats, float* __restrict__ bvpart, float* __restrict__ bt,
+    float* __restrict__ wout, float* __restrict__ xout, int N, int ldc, int m, int lbmax, int ntiles, int tpg, int groups, int jblocks,
     float scale, float eps, int iters, int nns, int gap) {
   extern __shared__ __align__(16) float lds[];
   int b = blockIdx.x;
@@ -230,7 +233,8 @@ __global__ __launch_bounds__(kTT) void l1exp_kernel(
     b -= b >= gap ? 2 * nns : nns;
   }
   const int jb = b % jblocks, g = (b / jblocks) % groups, p = b / (jblocks * groups);
-  l1exp_body<T, D, LBB>(q, k, v, kt, ct, stats, bvpart, N, ldc, m, lbmax, ntiles, tpg, groups, scale, jb, g, p, lds);
+  l1exp_body<T, D, LBB>(q, k, v, kt, ct, stats, bvpart, bt, N, ldc, m, lbmax, ntiles, tpg, groups, scale, jb, g, p,
+                        lds);
 }
 
 // CUs of the current device (queried once per device; 0 if unknown).
@@ -275,7 +279,7 @@ hipError_t launch_kernel(const Plan& pl, const void* q, const void* k, const voi
     }
   }
   hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kTT), shmem, s, t.start, t.stop, 0, (const T*)q,
-                        (const T*)k, (const T*)v, w.kt, w.ct, reinterpret_cast<float2*>(w.stats), w.bvpart, w.w,
+                        (const T*)k, (const T*)v, w.kt, w.ct, reinterpret_cast<float2*>(w.stats), w.bvpart, w.bt, w.w,
                         w.x, pl.N, pl.ldc, pl.m, lbmax, pl.ntiles, pl.tpg, pl.groups, pl.jblocks, pl.scale, pl.eps,
                         pl.ns_iters, nns, gap);
   if (KS > 0) w.x_final = w.x;

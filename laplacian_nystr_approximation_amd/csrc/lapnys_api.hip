@@ -356,14 +356,17 @@ int backward_impl(const void* q, const void* k, const void* v, const float* dout
     if (overlaps(outs[o], out_bytes, ws, total)) return LAPNYS_ERR_INVALID_ARG;
   }
   if (overlaps(dout, out_bytes, ws, total)) return LAPNYS_ERR_INVALID_ARG;
-  lapnys::Work W = carve(pl, ws);
-  st = run(pl, q, k, v, dq, W, nullptr, s);
-  if (st != LAPNYS_OK) return st;
   char* b = (char*)ws;
   lapnys::BwdWork B;
   float** slots[kBwdBuffers] = {&B.part, &B.spart, &B.y,  &B.dbv, &B.ab, &B.dw, &B.gt, &B.ht,
                                 &B.dkt,  &B.dy,    &B.bvt, &B.s,   &B.xt, &B.dx, &B.r};
   for (int i = 0; i < kBwdBuffers; ++i) *slots[i] = (float*)(b + off[i]);
+  // The forward leaves B in the H^T buffer, which the backward turns into H
+  // in place.
+  lapnys::Work W = carve(pl, ws);
+  W.bt = B.ht;
+  st = run(pl, q, k, v, dq, W, nullptr, s);
+  if (st != LAPNYS_OK) return st;
   if (!ok(lapnys::launch_backward(pl, B, W, q, k, v, dout, dq, dk, dv, s), "backward launch")) return LAPNYS_ERR_HIP;
   return LAPNYS_OK;
 }

@@ -107,6 +107,7 @@ struct Work {
   float *kt, *w, *x, *x2, *pm, *ct, *stats, *bvpart, *bv, *mu, *sigma, *rs, *y;
   __bf16* yt;          // m <= 64: Y^T as bf16 high and low parts, [P][2][d][64] (yt_index layout)
   float* x_final;      // the Newton-Schulz result (x or x2), set by launch_ns
+  float* bt = nullptr; // if set (Laplacian form only): the kernel-matrix stage also stores B as [P][m][N]
 };
 
 // Backward-pass buffers, after the forward's workspace (float32; mp = m

@@ -466,74 +466,94 @@ __global__ __launch_bounds__(256, 3) void bwd_hv_kernel(const T* __restrict__ v,
     }
 }
 
-// Token-side sign sums, one lane per token n: out_n = -(1/lambda) sum_j
-// w[j][n] sign(x_n - K~_j), per feature.  With x = Q and w = G^T this is dQ;
-// with x = K and w = H^T it is the B part of dK (sign(K~_j - k_n) =
-// -sign(k_n - K~_j)), to which the pooling adjoint then adds dK~_{j(n)} /
-// pool^2 when dkt is given (grid_w, pool, gw locate token n's window).
+// Token-side sign sums: out_n = -(1/lambda) sum_j w[j][n] sign(x_n - K~_j),
+// per feature.  With x = Q and w = G^T this is dQ; with x = K and w = H^T it
+// is the B part of dK (sign(K~_j - k_n) = -sign(k_n - K~_j)), to which the
+// pooling adjoint then adds dK~_{j(n)} / pool^2 when dkt is given (grid_w,
+// pool, gw locate token n's window).  Workgroup (tile, p) takes kST tokens
+// with D / 16 wavefronts: wavefront fb holds features 16 fb + [0, 16) of
+// every token of the tile, one lane per token, so each lane keeps 16 inputs
+// and 16 sums in registers; the weights of the next group of landmarks are
+// loaded while the current group is summed.
+constexpr int kST = 64;  // tokens per tile
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_sign_kernel(const T* __restrict__ x, const float* __restrict__ kt,
-                                                       const float* __restrict__ wt, float* __restrict__ out, int N,
-                                                       int m, float inv_lam, const float* __restrict__ dkt,
-                                                       int grid_w, int pool, int gw) {
+__global__ __launch_bounds__(4 * D) void bwd_sign_kernel(const T* __restrict__ x, const float* __restrict__ kt,
+                                                         const float* __restrict__ wt, float* __restrict__ out,
+                                                         int N, int m, float inv_lam, const float* __restrict__ dkt,
+                                                         int grid_w, int pool, int gw) {
   extern __shared__ __align__(16) float kls[];  // [m][D] K~ * 2^64
   const int tile = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
-  for (int e = tid; e < m * D; e += 256) kls[e] = kt[(size_t)p * m * D + e] * kSgnScale;
+  const int lane = tid & 63, f0 = 16 * (tid >> 6);
+  for (int e = tid; e < m * D; e += 4 * D) kls[e] = kt[(size_t)p * m * D + e] * kSgnScale;
   __syncthreads();
-  const int n = tile * kBT + tid;
+  const int n = tile * kST + lane;
   if (n >= N) return;
-  float xv[D], acc[D];
-  load_row<T, D>(x + ((size_t)p * N + n) * D, xv);
+  float xv[16], acc[16];
+  load_row<T, 16>(x + ((size_t)p * N + n) * D + f0, xv);
 #pragma unroll
-  for (int t = 0; t < D; ++t) acc[t] = 0.f;
+  for (int t = 0; t < 16; ++t) acc[t] = 0.f;
   const float* wc = wt + (size_t)p * m * N + n;
-  for (int j = 0; j < m; ++j) {
-    const float wj = wc[(size_t)j * N];
+  constexpr int kJU = 8;  // landmarks per group; the next group's weights load during this one
+  float wcur[kJU], wnext[kJU];
+  auto fetch_w = [&](int j0, float (&dst)[kJU]) {
 #pragma unroll
-    for (int t = 0; t < D; ++t) acc[t] = fmaf(wj, sgn_diff(xv[t], kls[j * D + t]), acc[t]);
+    for (int u = 0; u < kJU; ++u) dst[u] = wc[(size_t)min(j0 + u, m - 1) * N];
+  };
+  fetch_w(0, wcur);
+  for (int j0 = 0; j0 < m; j0 += kJU) {
+    if (j0 + kJU < m) fetch_w(j0 + kJU, wnext);
+#pragma unroll
+    for (int u = 0; u < kJU; ++u) {
+      if (j0 + u < m) {
+        const float* kr = kls + (j0 + u) * D + f0;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) acc[t] = fmaf(wcur[u], sgn_diff(xv[t], kr[t]), acc[t]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kJU; ++u) wcur[u] = wnext[u];
   }
-  float* op = out + ((size_t)p * N + n) * D;
+  float* op = out + ((size_t)p * N + n) * D + f0;
   if (dkt) {
     const int jn = (n / grid_w / pool) * gw + (n % grid_w) / pool;
-    const float* dr = dkt + ((size_t)p * m + jn) * D;
+    const float* dr = dkt + ((size_t)p * m + jn) * D + f0;
     const float inv_area = 1.f / (float)(pool * pool);
 #pragma unroll
-    for (int t = 0; t < D; ++t) op[t] = fmaf(dr[t], inv_area, -inv_lam * acc[t]);
+    for (int t = 0; t < 16; ++t) op[t] = fmaf(dr[t], inv_area, -inv_lam * acc[t]);
   } else {
 #pragma unroll
-    for (int t = 0; t < D; ++t) op[t] = -inv_lam * acc[t];
+    for (int t = 0; t < 16; ++t) op[t] = -inv_lam * acc[t];
   }
 }
 
-// Landmark side: one lane per (landmark j, feature t); workgroup (jb, p) takes
-// landmarks jb LG + [0, LG), LG = 256 / D.  The tokens are streamed through LDS
-// in chunks of kKC: the chunk's rows of Q (then K) and its G^T (then H^T)
-// entries for the workgroup's landmarks, loaded coalesced by all lanes, then
-// summed per lane in token order.
-constexpr int kKC = 128;
+// Landmark side: one lane per (landmark j, feature t); workgroup (jb, p, sl)
+// takes landmarks jb LG + [0, LG), LG = 256 / D, and the tokens of slice sl
+// (kKC-token chunks, slice_chunks of them).  The chunks are streamed through
+// LDS: the chunk's rows of Q (then K) and its G^T (then H^T) entries for the
+// workgroup's landmarks, loaded coalesced by all lanes one chunk ahead, then
+// summed per lane in token order on two chains (even and odd tokens).  The
+// slice's sum of both sides goes to kpart[sl][p][j][t]; bwd_kt_combine_kernel
+// adds the slices in order and the W term.
+constexpr int kKC = 64;
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_kt_kernel(const T* __restrict__ q, const T* __restrict__ k,
+__global__ __launch_bounds__(256, 3) void bwd_kt_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                      const float* __restrict__ kt, const float* __restrict__ gt,
-                                                     const float* __restrict__ ht, const float* __restrict__ w,
-                                                     int mp, const float* __restrict__ dw,
-                                                     float* __restrict__ dkt, int N, int m, float eps,
-                                                     float inv_lam) {
+                                                     const float* __restrict__ ht, float* __restrict__ kpart, int N,
+                                                     int m, int slice_chunks) {
   constexpr int LG = 256 / D;
   __shared__ float xs[kKC * D];
   __shared__ float gs[LG * kKC];
-  const int p = blockIdx.y, tid = threadIdx.x;
+  const int p = blockIdx.y, sl = blockIdx.z, tid = threadIdx.x;
   const int jl = tid / D, t = tid % D;
   const int j0 = blockIdx.x * LG, j = j0 + jl;
-  const bool valid = j < m;
-  const int jc = min(j, m - 1);
-  const float kj = kt[((size_t)p * m + jc) * D + t];
-  const float kjs = kj * kSgnScale;
-  // Per lane, the chunk's loads: kX row values and kG weights, issued one
-  // chunk ahead so that they land while the current chunk is summed.  Tokens
-  // past N read the last token and carry weight 0.
+  const float kjs = kt[((size_t)p * m + min(j, m - 1)) * D + t] * kSgnScale;
+  const int n_begin = sl * slice_chunks * kKC, n_end = min(N, n_begin + slice_chunks * kKC);
+  // Per lane, the chunk's loads: kX row values and kG weights.  Tokens past
+  // the slice read a valid row and carry weight 0.
   constexpr int kX = kKC * D / 256, kG = LG * kKC / 256;
-  float sums[2] = {0.f, 0.f};
+  float total = 0.f;
 #pragma unroll
   for (int side = 0; side < 2; ++side) {
     const T* rows = (side == 0 ? q : k) + (size_t)p * N * D;
@@ -549,36 +569,69 @@ __global__ __launch_bounds__(256) void bwd_kt_kernel(const T* __restrict__ q, co
       for (int u = 0; u < kG; ++u) {
         const int e = tid + 256 * u, l = e / kKC, i = e % kKC;
         const float g = wt[(size_t)min(j0 + l, m - 1) * N + min(c0 + i, N - 1)];
-        gr[u] = c0 + i < N ? g : 0.f;
+        gr[u] = c0 + i < n_end ? g : 0.f;
       }
     };
-    float acc = 0.f;
-    fetch(0);
-    for (int c0 = 0; c0 < N; c0 += kKC) {
+    float a0 = 0.f, a1 = 0.f;
+    fetch(n_begin);
+    for (int c0 = n_begin; c0 < n_end; c0 += kKC) {
       __syncthreads();  // the previous chunk's reads are done
 #pragma unroll
       for (int u = 0; u < kX; ++u) xs[tid + 256 * u] = xr[u];
 #pragma unroll
       for (int u = 0; u < kG; ++u) gs[tid + 256 * u] = gr[u];
       __syncthreads();
-      if (c0 + kKC < N) fetch(c0 + kKC);
+      if (c0 + kKC < n_end) fetch(c0 + kKC);
       const float* gl = gs + jl * kKC;
-      // Both sides sum w_i sign(x_i - K~_jt); the B side enters negated below.
-#pragma unroll 16
-      for (int i = 0; i < kKC; ++i) acc = fmaf(gl[i], sgn_diff(xs[i * D + t], kjs), acc);
+      // Both sides sum w_i sign(x_i - K~_jt); the B side's sign is flipped in
+      // the combine.
+#pragma unroll 8
+      for (int i = 0; i < kKC; i += 2) {
+        a0 = fmaf(gl[i], sgn_diff(xs[i * D + t], kjs), a0);
+        a1 = fmaf(gl[i + 1], sgn_diff(xs[(i + 1) * D + t], kjs), a1);
+      }
     }
-    sums[side] = acc;
+    total += a0 + a1;
   }
-  if (!valid) return;
+  if (j < m) kpart[(((size_t)sl * gridDim.y + p) * m + j) * D + t] = total;
+}
+
+// dK~_jt = (1/lambda) (sum over slices of kpart + c_jt), one lane per (j, t);
+// workgroup (jb, p) takes landmarks jb LG + [0, LG), LG = 256 / D:
+// c_jt = sum_b a_jb sign(K~_jt - K~_bt), a_jb = (dw_jb + dw_bj)(W_jb - eps [j = b]).
+// dw holds -dW, so the W term of the gradient, -(1/lambda) sum_b (dW_jb +
+// dW_bj)(W_jb - eps [j = b]) sign(K~_jt - K~_bt), is +c_jt / lambda.  The
+// coefficients a_jb go to LDS first.  sum_n H_jn sign(K~_j - k_n) is minus
+// the K side of kpart.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_kt_combine_kernel(const float* __restrict__ kpart, int slices,
+                                                             const float* __restrict__ kt,
+                                                             const float* __restrict__ w, int mp,
+                                                             const float* __restrict__ dw, float* __restrict__ dkt,
+                                                             int m, float eps, float inv_lam) {
+  constexpr int LG = 256 / D;
+  __shared__ float coef[LG * kMaxM];
+  const int p = blockIdx.y, tid = threadIdx.x, jl = tid / D, t = tid % D;
+  const int j0 = blockIdx.x * LG, j = j0 + jl;
+  const float* wp = w + (size_t)p * mp * mp;
+  const float* dwp = dw + (size_t)p * mp * mp;
+  for (int e = tid; e < LG * m; e += 256) {
+    const int l = e / m, bb = e % m, jj = min(j0 + l, m - 1);
+    const float wv = wp[(size_t)jj * mp + bb] - (bb == jj ? eps : 0.f);
+    coef[l * kMaxM + bb] = (dwp[(size_t)jj * mp + bb] + dwp[(size_t)bb * mp + jj]) * wv;
+  }
+  __syncthreads();
+  if (j >= m) return;
+  const size_t slice_stride = (size_t)gridDim.y * m * D;
+  float s = 0.f;
+  for (int sl = 0; sl < slices; ++sl) s += kpart[sl * slice_stride + ((size_t)p * m + j) * D + t];
+  const float* ktp = kt + (size_t)p * m * D + t;
+  const float kj = ktp[(size_t)j * D];
+  const float* cl = coef + jl * kMaxM;
   float c = 0.f;
-  for (int bb = 0; bb < m; ++bb) {
-    float wv = w[(size_t)p * mp * mp + (size_t)j * mp + bb];
-    if (bb == j) wv -= eps;
-    const float dws = dw[((size_t)p * mp + j) * mp + bb] + dw[((size_t)p * mp + bb) * mp + j];
-    c = fmaf(dws * wv, sgn(kj - kt[((size_t)p * m + bb) * D + t]), c);
-  }
-  // sum_n H_jn sign(K~_j - k_n) = -sums[1]; dw holds -dW, so -c is +c here.
-  dkt[((size_t)p * m + j) * D + t] = (sums[0] + sums[1] + c) * inv_lam;
+#pragma unroll 8
+  for (int bb = 0; bb < m; ++bb) c = fmaf(cl[bb], sgn(kj - ktp[(size_t)bb * D]), c);
+  dkt[((size_t)p * m + j) * D + t] = (s + c) * inv_lam;
 }
 
 template <typename T, int D>
@@ -621,19 +674,28 @@ hipError_t launch_typed(const Plan& pl, const BwdWork& b, const Work& w, const v
     if (e != hipSuccess) return e;
   }
   const size_t row_lds = (size_t)m * D * sizeof(float);  // <= 64 KB
+  const int nst = (pl.N + kST - 1) / kST;
   hipLaunchKernelGGL(bwd_g_kernel<D>, dim3((pl.N + kGT - 1) / kGT, pl.P), dim3(256), 0, s, dout, w.ct, pl.ldc, b.y,
                      w.mu, w.rs, b.ab, b.gt, pl.N, m);
-  hipLaunchKernelGGL((bwd_sign_kernel<T, D>), dim3(nt, pl.P), dim3(256), row_lds, s, (const T*)q, w.kt, b.gt, dq,
+  hipLaunchKernelGGL((bwd_sign_kernel<T, D>), dim3(nst, pl.P), dim3(4 * D), row_lds, s, (const T*)q, w.kt, b.gt, dq,
                      pl.N, m, inv_lam, nullptr, pl.grid_w, pl.pool, pl.gw);
   constexpr size_t hv_lds = bwd_hv_lds<D>();
   static_assert(hv_lds <= 65536, "the key-side first pass fits in static-size LDS");
   hipLaunchKernelGGL((bwd_hv_kernel<T, D>), dim3((pl.N + kHT - 1) / kHT, pl.P), dim3(256), hv_lds, s, (const T*)v,
                      b.dbv, b.ht, dv, pl.N, m);
-  constexpr int LG = 256 / D;
-  hipLaunchKernelGGL((bwd_kt_kernel<T, D>), dim3((pl.m + LG - 1) / LG, pl.P), dim3(256), 0, s, (const T*)q,
-                     (const T*)k, w.kt, b.gt, b.ht, w.w, pl.mp, b.dw, b.dkt, pl.N, pl.m, pl.eps, inv_lam);
+  // Landmark side in token slices of kSliceChunks chunks; the partials reuse
+  // the C^T g partial buffer ([P][tiles][m][d], tiles >= slices), which is
+  // free once dY is formed.
+  constexpr int LG = 256 / D, kSliceChunks = 10;
+  const int chunks = (pl.N + kKC - 1) / kKC;
+  const int slices = (chunks + kSliceChunks - 1) / kSliceChunks;
+  if (slices > nt) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((bwd_kt_kernel<T, D>), dim3((m + LG - 1) / LG, pl.P, slices), dim3(256), 0, s, (const T*)q,
+                     (const T*)k, w.kt, b.gt, b.ht, b.part, pl.N, m, kSliceChunks);
+  hipLaunchKernelGGL(bwd_kt_combine_kernel<D>, dim3((m + LG - 1) / LG, pl.P), dim3(256), 0, s, b.part, slices,
+                     w.kt, w.w, pl.mp, b.dw, b.dkt, m, pl.eps, inv_lam);
   // dK: the B part, plus the pooling adjoint of dK~.
-  hipLaunchKernelGGL((bwd_sign_kernel<T, D>), dim3(nt, pl.P), dim3(256), row_lds, s, (const T*)k, w.kt, b.ht, dk,
+  hipLaunchKernelGGL((bwd_sign_kernel<T, D>), dim3(nst, pl.P), dim3(4 * D), row_lds, s, (const T*)k, w.kt, b.ht, dk,
                      pl.N, m, inv_lam, b.dkt, pl.grid_w, pl.pool, pl.gw);
   return hipGetLastError();
 }

@@ -527,33 +527,40 @@ __global__ __launch_bounds__(4 * D) void bwd_sign_kernel(const T* __restrict__ x
   }
 }
 
-// Landmark side: one lane per (landmark j, feature t); workgroup (jb, p, sl)
-// takes landmarks jb LG + [0, LG), LG = 256 / D, and the tokens of slice sl
-// (kKC-token chunks, slice_chunks of them).  The chunks are streamed through
-// LDS: the chunk's rows of Q (then K) and its G^T (then H^T) entries for the
-// workgroup's landmarks, loaded coalesced by all lanes one chunk ahead, then
-// summed per lane in token order on two chains (even and odd tokens).  The
-// slice's sum of both sides goes to kpart[sl][p][j][t]; bwd_kt_combine_kernel
-// adds the slices in order and the W term.
+// Landmark side: lane (jl, t) takes feature t of landmarks jb LW + jl + LG u,
+// u < kJPL (LG = 256 / D, LW = kJPL LG landmarks per workgroup), so that each
+// token value read from LDS serves kJPL landmarks; workgroup (jb, p, sl) takes
+// the tokens of slice sl (kKC-token chunks, slice_chunks of them).  The chunks
+// are streamed through LDS: the chunk's rows of Q (then K) and its G^T (then
+// H^T) entries for the workgroup's landmarks, loaded coalesced by all lanes one
+// chunk ahead, then summed per lane in token order on two chains per landmark
+// (even and odd tokens).  The slice's sum of both sides goes to
+// kpart[sl][p][j][t]; bwd_kt_combine_kernel adds the slices in order and the W
+// term.
 constexpr int kKC = 64;
+constexpr int kJPL = 4;
 
 template <typename T, int D>
 __global__ __launch_bounds__(256, 3) void bwd_kt_kernel(const T* __restrict__ q, const T* __restrict__ k,
-                                                     const float* __restrict__ kt, const float* __restrict__ gt,
-                                                     const float* __restrict__ ht, float* __restrict__ kpart, int N,
-                                                     int m, int slice_chunks) {
-  constexpr int LG = 256 / D;
+                                                        const float* __restrict__ kt, const float* __restrict__ gt,
+                                                        const float* __restrict__ ht, float* __restrict__ kpart,
+                                                        int N, int m, int slice_chunks) {
+  constexpr int LG = 256 / D, LW = kJPL * LG;
   __shared__ float xs[kKC * D];
-  __shared__ float gs[LG * kKC];
+  __shared__ __align__(16) float gs[LW * kKC];
   const int p = blockIdx.y, sl = blockIdx.z, tid = threadIdx.x;
   const int jl = tid / D, t = tid % D;
-  const int j0 = blockIdx.x * LG, j = j0 + jl;
-  const float kjs = kt[((size_t)p * m + min(j, m - 1)) * D + t] * kSgnScale;
+  const int j0 = blockIdx.x * LW;
+  float kjs[kJPL];
+#pragma unroll
+  for (int u = 0; u < kJPL; ++u) kjs[u] = kt[((size_t)p * m + min(j0 + jl + LG * u, m - 1)) * D + t] * kSgnScale;
   const int n_begin = sl * slice_chunks * kKC, n_end = min(N, n_begin + slice_chunks * kKC);
   // Per lane, the chunk's loads: kX row values and kG weights.  Tokens past
   // the slice read a valid row and carry weight 0.
-  constexpr int kX = kKC * D / 256, kG = LG * kKC / 256;
-  float total = 0.f;
+  constexpr int kX = kKC * D / 256, kG = LW * kKC / 256;
+  float total[kJPL];
+#pragma unroll
+  for (int u = 0; u < kJPL; ++u) total[u] = 0.f;
 #pragma unroll
   for (int side = 0; side < 2; ++side) {
     const T* rows = (side == 0 ? q : k) + (size_t)p * N * D;
@@ -572,7 +579,9 @@ __global__ __launch_bounds__(256, 3) void bwd_kt_kernel(const T* __restrict__ q,
         gr[u] = c0 + i < n_end ? g : 0.f;
       }
     };
-    float a0 = 0.f, a1 = 0.f;
+    float a0[kJPL], a1[kJPL];
+#pragma unroll
+    for (int u = 0; u < kJPL; ++u) a0[u] = a1[u] = 0.f;
     fetch(n_begin);
     for (int c0 = n_begin; c0 < n_end; c0 += kKC) {
       __syncthreads();  // the previous chunk's reads are done
@@ -582,18 +591,27 @@ __global__ __launch_bounds__(256, 3) void bwd_kt_kernel(const T* __restrict__ q,
       for (int u = 0; u < kG; ++u) gs[tid + 256 * u] = gr[u];
       __syncthreads();
       if (c0 + kKC < n_end) fetch(c0 + kKC);
-      const float* gl = gs + jl * kKC;
       // Both sides sum w_i sign(x_i - K~_jt); the B side's sign is flipped in
       // the combine.
-#pragma unroll 8
+#pragma unroll 4
       for (int i = 0; i < kKC; i += 2) {
-        a0 = fmaf(gl[i], sgn_diff(xs[i * D + t], kjs), a0);
-        a1 = fmaf(gl[i + 1], sgn_diff(xs[(i + 1) * D + t], kjs), a1);
+        const float x0 = xs[i * D + t], x1 = xs[(i + 1) * D + t];
+#pragma unroll
+        for (int u = 0; u < kJPL; ++u) {
+          const float* gl = gs + (jl + LG * u) * kKC;
+          a0[u] = fmaf(gl[i], sgn_diff(x0, kjs[u]), a0[u]);
+          a1[u] = fmaf(gl[i + 1], sgn_diff(x1, kjs[u]), a1[u]);
+        }
       }
     }
-    total += a0 + a1;
+#pragma unroll
+    for (int u = 0; u < kJPL; ++u) total[u] += a0[u] + a1[u];
   }
-  if (j < m) kpart[(((size_t)sl * gridDim.y + p) * m + j) * D + t] = total;
+#pragma unroll
+  for (int u = 0; u < kJPL; ++u) {
+    const int j = j0 + jl + LG * u;
+    if (j < m) kpart[(((size_t)sl * gridDim.y + p) * m + j) * D + t] = total[u];
+  }
 }
 
 // dK~_jt = (1/lambda) (sum over slices of kpart + c_jt), one lane per (j, t);
@@ -686,12 +704,12 @@ hipError_t launch_typed(const Plan& pl, const BwdWork& b, const Work& w, const v
   // Landmark side in token slices of kSliceChunks chunks; the partials reuse
   // the C^T g partial buffer ([P][tiles][m][d], tiles >= slices), which is
   // free once dY is formed.
-  constexpr int LG = 256 / D, kSliceChunks = 10;
+  constexpr int LG = 256 / D, kSliceChunks = 4;
   const int chunks = (pl.N + kKC - 1) / kKC;
   const int slices = (chunks + kSliceChunks - 1) / kSliceChunks;
   if (slices > nt) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((bwd_kt_kernel<T, D>), dim3((m + LG - 1) / LG, pl.P, slices), dim3(256), 0, s, (const T*)q,
-                     (const T*)k, w.kt, b.gt, b.ht, b.part, pl.N, m, kSliceChunks);
+  hipLaunchKernelGGL((bwd_kt_kernel<T, D>), dim3((m + kJPL * LG - 1) / (kJPL * LG), pl.P, slices), dim3(256), 0, s,
+                     (const T*)q, (const T*)k, w.kt, b.gt, b.ht, b.part, pl.N, m, kSliceChunks);
   hipLaunchKernelGGL(bwd_kt_combine_kernel<D>, dim3((m + LG - 1) / LG, pl.P), dim3(256), 0, s, b.part, slices,
                      w.kt, w.w, pl.mp, b.dw, b.dkt, m, pl.eps, inv_lam);
   // dK: the B part, plus the pooling adjoint of dK~.

@@ -158,19 +158,17 @@ __device__ __forceinline__ void mm64(const float* __restrict__ a, const float* _
     for (int r = 0; r < 4; ++r) out[(16 * w + 4 * lk + r) * 65 + 16 * bj + li] = sign * acc[bj][r];
 }
 
-// m <= 64, per problem (one workgroup): reduce the partials, then Y, dY, a, b,
-// dBV and R X^T = X^T (dY BV^T) X^T = -dW, every matrix zero padded to 64 rows
-// in LDS and the products on fp32 MFMA.  x: the Newton-Schulz result, row
-// stride mp (= 64).  Outputs: y, dbv [P][m][D]; ab [P][2][m]; dw [P][mp][mp].
+// m <= 64, per problem (one workgroup), from dY and 1^T g (bwd_dy_kernel):
+// Y, a, b, dBV and R X^T = X^T (dY BV^T) X^T = -dW, every matrix zero padded
+// to 64 rows in LDS and the products on fp32 MFMA.  x: the Newton-Schulz
+// result, row stride mp (= 64); dyg: dY [P][mp][D], zero rows past m.
+// Outputs: y, dbv [P][m][D]; ab [P][2][m]; dw [P][mp][mp].
 template <int D>
-__global__ __launch_bounds__(256) void bwd_small_kernel(const float* __restrict__ part,
-                                                        const float* __restrict__ spart,
+__global__ __launch_bounds__(256) void bwd_small_kernel(const float* __restrict__ dyg, const float* __restrict__ sg,
                                                         const float* __restrict__ x, int mp,
-                                                        const float* __restrict__ bv, const float* __restrict__ mu,
-                                                        const float* __restrict__ rs, float* __restrict__ y,
+                                                        const float* __restrict__ bv, float* __restrict__ y,
                                                         float* __restrict__ dbv, float* __restrict__ ab,
-                                                        float* __restrict__ dw, int N, int m, int ntiles,
-                                                        int whiten) {
+                                                        float* __restrict__ dw, int N, int m, int whiten) {
   extern __shared__ __align__(16) float lds[];
   constexpr int kS = 64 * 65;
   float* xs = lds;
@@ -181,41 +179,57 @@ __global__ __launch_bounds__(256) void bwd_small_kernel(const float* __restrict_
   float* ys = dys + kS;
   float* ss = ys + kS;
   const int p = blockIdx.x, tid = threadIdx.x;
-  for (int e = tid; e < 64 * 64; e += 256) {
-    const int r = e >> 6, c = e & 63;
-    xs[r * 65 + c] = (r < m && c < m) ? x[(size_t)p * mp * mp + (size_t)r * mp + c] : 0.f;
-  }
-  for (int e = tid; e < 64 * D; e += 256) {
-    const int r = e / D, c = e % D;
-    bvs[r * 65 + c] = r < m ? bv[(size_t)p * m * D + e] : 0.f;
-  }
-  for (int f = tid; f < D; f += 256) {
-    float s = 0.f;
-    for (int t = 0; t < ntiles; ++t) s += spart[((size_t)p * ntiles + t) * D + f];
-    ss[f] = s;
+  {
+    // Every load is issued before the first LDS store.
+    constexpr int kXE = 64 * 64 / 256, kBE = 64 * D / 256;
+    float xr[kXE], br[kBE], dr[kBE];
+#pragma unroll
+    for (int u = 0; u < kXE; ++u) {
+      const int e = tid + 256 * u, r = e >> 6, c = e & 63;
+      xr[u] = x[(size_t)p * mp * mp + (size_t)min(r, m - 1) * mp + min(c, m - 1)];
+    }
+#pragma unroll
+    for (int u = 0; u < kBE; ++u) {
+      const int e = tid + 256 * u, r = e / D, c = e % D;
+      br[u] = bv[((size_t)p * m + min(r, m - 1)) * D + c];
+      dr[u] = dyg[((size_t)p * mp + r) * D + c];
+    }
+    const float sv = sg[(size_t)p * D + tid % D];
+#pragma unroll
+    for (int u = 0; u < kXE; ++u) {
+      const int e = tid + 256 * u, r = e >> 6, c = e & 63;
+      xs[r * 65 + c] = (r < m && c < m) ? xr[u] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kBE; ++u) {
+      const int e = tid + 256 * u, r = e / D, c = e % D;
+      bvs[r * 65 + c] = r < m ? br[u] : 0.f;
+      dys[r * 65 + c] = dr[u];
+    }
+    if (tid < D) ss[tid] = sv;
   }
   __syncthreads();
-  for (int e = tid; e < 64 * D; e += 256) {
-    const int j = e / D, f = e % D;
-    float c = 0.f;
-    if (j < m) {
-#pragma unroll 4
-      for (int t = 0; t < ntiles; ++t) c += part[(((size_t)p * ntiles + t) * m) * D + e];
-      c = (c - mu[p * m + j] * ss[f]) * rs[p * m + j];
-    }
-    dys[j * 65 + f] = c;
-  }
   mm64<D, false, false>(xs, bvs, ys, 64, 1.f);  // Y = X BV
   __syncthreads();
   for (int e = tid; e < m * D; e += 256) y[(size_t)p * m * D + e] = ys[(e / D) * 65 + e % D];
-  for (int j = tid; j < m; j += 256) {
+  {
+    // a_j = (1^T g) . Y_j / N, b_j = Y_j . dY_j / N: four lanes per landmark,
+    // D / 4 features each, then merged ((0 + 1) + (2 + 3)).
+    const int j = tid >> 2, q4 = tid & 3;
     float a = 0.f, b = 0.f;
-    for (int f = 0; f < D; ++f) {
+#pragma unroll
+    for (int f = q4 * (D / 4); f < (q4 + 1) * (D / 4); ++f) {
       a = fmaf(ss[f], ys[j * 65 + f], a);
       b = fmaf(ys[j * 65 + f], dys[j * 65 + f], b);
     }
-    ab[(size_t)p * 2 * m + j] = whiten ? a / (float)N : 0.f;
-    ab[(size_t)p * 2 * m + m + j] = whiten ? b / (float)N : 0.f;
+    a += __shfl_xor(a, 1, 64);
+    b += __shfl_xor(b, 1, 64);
+    a += __shfl_xor(a, 2, 64);
+    b += __shfl_xor(b, 2, 64);
+    if (q4 == 0 && j < m) {
+      ab[(size_t)p * 2 * m + j] = whiten ? a / (float)N : 0.f;
+      ab[(size_t)p * 2 * m + m + j] = whiten ? b / (float)N : 0.f;
+    }
   }
   __syncthreads();
   mm64<D, true, false>(xs, dys, ys, 64, 1.f);    // dBV = X^T dY (into the Y buffer)
@@ -229,7 +243,7 @@ __global__ __launch_bounds__(256) void bwd_small_kernel(const float* __restrict_
   for (int e = tid; e < m * m; e += 256) dw[((size_t)p * mp + e / m) * mp + e % m] = dxs[(e / m) * 65 + e % m];
 }
 
-// m > 64: dY = (C^T g - mu (1^T g)) / sigma from the partials into dy
+// dY = (C^T g - mu (1^T g)) / sigma from the partials into dy
 // [P][mp][D] (zero rows past m), and 1^T g into s [P][D].
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dy_kernel(const float* __restrict__ part, const float* __restrict__ spart,
@@ -240,10 +254,12 @@ __global__ __launch_bounds__(256) void bwd_dy_kernel(const float* __restrict__ p
   if (e >= mp * D) return;
   const int j = e / D, f = e % D;
   float sv = 0.f;
+#pragma unroll 8
   for (int t = 0; t < ntiles; ++t) sv += spart[((size_t)p * ntiles + t) * D + f];
   if (j == 0) sg[(size_t)p * D + f] = sv;
   float c = 0.f;
   if (j < m) {
+#pragma unroll 8
     for (int t = 0; t < ntiles; ++t) c += part[(((size_t)p * ntiles + t) * m + j) * D + f];
     c = (c - mu[p * m + j] * sv) * rs[p * m + j];
   }
@@ -666,8 +682,10 @@ hipError_t launch_typed(const Plan& pl, const BwdWork& b, const Work& w, const v
     e = hipFuncSetAttribute((const void*)bwd_small_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)small_lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_small_kernel<D>, dim3(pl.P), dim3(256), small_lds, s, b.part, b.spart, w.x_final, mp,
-                       w.bv, w.mu, w.rs, b.y, b.dbv, b.ab, b.dw, pl.N, m, nt, pl.whiten ? 1 : 0);
+    hipLaunchKernelGGL(bwd_dy_kernel<D>, dim3((mp * D + 255) / 256, pl.P), dim3(256), 0, s, b.part, b.spart, w.mu,
+                       w.rs, b.dy, b.s, m, mp, nt);
+    hipLaunchKernelGGL(bwd_small_kernel<D>, dim3(pl.P), dim3(256), small_lds, s, b.dy, b.s, w.x_final, mp, w.bv,
+                       b.y, b.dbv, b.ab, b.dw, pl.N, m, pl.whiten ? 1 : 0);
   } else {
     // The same quantities with the products on the tile GEMM, in the workspace.
     const long long sq = (long long)mp * mp, md = (long long)m * D, mpd = (long long)mp * D;

@@ -321,7 +321,7 @@ int backward_plan(const lapnys_params* p, Plan* pl, size_t off[kBwdBuffers], siz
   const size_t sizes[kBwdBuffers] = {
       Pn * nt * m * d * f, Pn * nt * d * f, Pn * m * d * f, Pn * m * d * f, Pn * 2 * m * f, Pn * mp * mp * f,
       Pn * m * N * f,      Pn * m * N * f,  Pn * m * d * f,
-      big ? Pn * mp * d * f : 0, big ? Pn * d * mp * f : 0, big ? Pn * d * f : 0, big ? Pn * mp * mp * f : 0,
+      Pn * mp * d * f,           big ? Pn * d * mp * f : 0, Pn * d * f,           big ? Pn * mp * mp * f : 0,
       big ? Pn * mp * mp * f : 0, big ? Pn * mp * mp * f : 0};
   size_t o = pl->total;
   for (int i = 0; i < kBwdBuffers; ++i) {

@@ -116,8 +116,8 @@ struct Work {
 //   y, dbv [P][m][d]; ab [P][2][m]; dkt [P][m][d]
 //   dw [P][mp][mp]   R X^T with R = X^T dX, i.e. -dW
 //   gt, ht [P][m][N]                              G^T and H^T
-//   m > 64 only: dy [P][mp][d] (zero rows past m), bvt [P][d][mp], s [P][d],
-//   xt, dx, r [P][mp][mp]
+//   dy [P][mp][d] (zero rows past m), s [P][d]
+//   m > 64 only: bvt [P][d][mp], xt, dx, r [P][mp][mp]
 struct BwdWork {
   float *part, *spart, *y, *dbv, *ab, *dw, *gt, *ht, *dkt;
   float *dy, *bvt, *s, *xt, *dx, *r;

@@ -501,7 +501,20 @@ __global__ __launch_bounds__(4 * D) void bwd_sign_kernel(const T* __restrict__ x
   extern __shared__ __align__(16) float kls[];  // [m][D] K~ * 2^64
   const int tile = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, f0 = 16 * (tid >> 6);
-  for (int e = tid; e < m * D; e += 4 * D) kls[e] = kt[(size_t)p * m * D + e] * kSgnScale;
+  {
+    // K~ into LDS in batches of kB loads per lane, each batch's loads issued
+    // before its stores.
+    constexpr int kB = 16;
+    const float* kp = kt + (size_t)p * m * D;
+    for (int base = 0; base < m * D; base += kB * 4 * D) {
+      float r[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) r[u] = kp[min(base + tid + 4 * D * u, m * D - 1)];
+#pragma unroll
+      for (int u = 0; u < kB; ++u)
+        if (base + tid + 4 * D * u < m * D) kls[base + tid + 4 * D * u] = r[u] * kSgnScale;
+    }
+  }
   __syncthreads();
   const int n = tile * kST + lane;
   if (n >= N) return;

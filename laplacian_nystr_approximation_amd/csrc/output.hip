@@ -100,14 +100,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void o
     for (int s = 0; s < kSlots; ++s) load_slot(0, s);
     for (int e = tid; e < rl; e += 256)
       mrs[e] = (e < m) ? make_float2(mu[p * m + e], rs[p * m + e]) : make_float2(0.f, 0.f);
+    // Y^T into LDS in batches of kB loads per lane, each batch's loads
+    // issued before its stores.
     const float* yp = y + (size_t)p * m * D;
-    for (int e = tid; e < rl * D; e += 256) {
-      const int l = e / D, f = e % D;
-      const float v = l < m ? yp[e] : 0.f;
-      const __bf16 hi = (__bf16)v;
-      const int at = yt_index(f, l, f / DB, rl);
-      yth[at] = hi;
-      ytl[at] = (__bf16)(v - (float)hi);
+    constexpr int kB = 16;
+    for (int base = 0; base < rl * D; base += kB * 256) {
+      float r[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) r[u] = yp[min(base + tid + 256 * u, m * D - 1)];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int e = base + tid + 256 * u;
+        if (e < rl * D) {
+          const int l = e / D, f = e % D;
+          const float v = l < m ? r[u] : 0.f;
+          const __bf16 hi = (__bf16)v;
+          const int at = yt_index(f, l, f / DB, rl);
+          yth[at] = hi;
+          ytl[at] = (__bf16)(v - (float)hi);
+        }
+      }
     }
   }
   __syncthreads();

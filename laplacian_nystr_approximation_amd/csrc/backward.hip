@@ -18,9 +18,12 @@
 //                       - sum_b (dW_jb + dW_bj) W'_jb sign(K~_j - K~_b)]
 //
 // (W' = W without eps.)  With whitening off, mu = 0, 1/sigma = 1 and a = b = 0.
-// Every kernel is a loop in float32 with a fixed order; the token-side
-// kernels take one lane per token, the landmark-side one one lane per
-// (landmark, feature) with the tokens streamed through LDS.
+// Every kernel works in float32 with a fixed summation order, so results
+// repeat bit for bit.  B comes from the forward (stored into the H^T buffer);
+// the products over d or over 64-row blocks (C^T g, g Y^T, dBV V^T, B^T dBV
+// and the m x m ones) run on fp32 MFMA; the sign sums run on the vector ALUs,
+// the token-side ones one lane per token and 16 features, the landmark-side
+// one one lane per (feature, 4 landmarks) with the tokens streamed through LDS.
 #include "lapnys_internal.hpp"
 
 namespace lapnys {

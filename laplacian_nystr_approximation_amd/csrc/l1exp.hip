@@ -301,7 +301,10 @@ template <typename T, int D>
 hipError_t launch_typed(const Plan& pl, const void* q, const void* k, const void* v, Work& w, hipStream_t s,
                         Span t) {
   if (pl.ns_in_launch) return launch_fused<T, D>(pl, q, k, v, w, s, t);
-  // Landmark blocks of (at most) 32, two row blocks; the solver runs on its own.
+  // The solver runs on its own: one block of m <= 64 landmarks (up to four
+  // 16-row blocks), or landmark blocks of at most 32 (two row blocks).
+  if (pl.lb > 48) return launch_kernel<T, D, 4, 0>(pl, q, k, v, w, s, t);
+  if (pl.lb > 32) return launch_kernel<T, D, 3, 0>(pl, q, k, v, w, s, t);
   return launch_kernel<T, D, 2, 0>(pl, q, k, v, w, s, t);
 }
 

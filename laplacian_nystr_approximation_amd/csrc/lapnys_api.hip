@@ -97,9 +97,11 @@ int make_plan(const lapnys_params* p, Plan* pl) {
   P.mp = P.fused_ns ? 64 : ((P.m + 63) / 64) * 64;
   P.tt = 256;
   P.ntiles = (P.N + P.tt - 1) / P.tt;
-  // Landmark blocks: all m <= 64 landmarks in one block beside the in-LDS
-  // solver, else blocks of 32.
-  P.lb = P.ns_in_launch || (P.fused_ns && P.gaussian) ? P.m : (P.m < 32 ? P.m : 32);
+  // Landmark blocks: all m <= 64 landmarks in one block (every solver of the
+  // Laplacian form; the Gaussian form beside its Newton-Schulz solver), else
+  // blocks of 32.
+  const bool one_block = P.m <= lapnys::kFusedNsMaxM && (!P.gaussian || P.fused_ns);
+  P.lb = one_block ? P.m : (P.m < 32 ? P.m : 32);
   P.jblocks = (P.m + P.lb - 1) / P.lb;
   // Tiles per workgroup: enough workgroups to fill the chip several times,
   // few enough that the B V partials stay small.

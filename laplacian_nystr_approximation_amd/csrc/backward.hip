@@ -625,7 +625,7 @@ __global__ __launch_bounds__(256, 3) void bwd_kt_kernel(const T* __restrict__ q,
       if (c0 + kKC < n_end) fetch(c0 + kKC);
       // Both sides sum w_i sign(x_i - K~_jt); the B side's sign is flipped in
       // the combine.
-#pragma unroll 4
+#pragma unroll 8
       for (int i = 0; i < kKC; i += 2) {
         const float x0 = xs[i * D + t], x1 = xs[(i + 1) * D + t];
 #pragma unroll

@@ -497,12 +497,19 @@ __global__ __launch_bounds__(256, 3) void bwd_hv_kernel(const T* __restrict__ v,
 constexpr int kST = 64;  // tokens per tile
 
 template <typename T, int D>
-__global__ __launch_bounds__(4 * D) void bwd_sign_kernel(const T* __restrict__ x, const float* __restrict__ kt,
-                                                         const float* __restrict__ wt, float* __restrict__ out,
-                                                         int N, int m, float inv_lam, const float* __restrict__ dkt,
-                                                         int grid_w, int pool, int gw) {
+__global__ __launch_bounds__(4 * D) void bwd_sign_kernel(const T* __restrict__ x0, const float* __restrict__ wt0,
+                                                         float* __restrict__ out0, const T* __restrict__ x1,
+                                                         const float* __restrict__ wt1, float* __restrict__ out1,
+                                                         const float* __restrict__ dkt1, const float* __restrict__ kt,
+                                                         int N, int m, float inv_lam, int grid_w, int pool, int gw) {
   extern __shared__ __align__(16) float kls[];  // [m][D] K~ * 2^64
   const int tile = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
+  // blockIdx.z picks the side: 0 = (x0, wt0, out0), 1 = (x1, wt1, out1, dkt1).
+  const bool second = blockIdx.z != 0;
+  const T* __restrict__ x = second ? x1 : x0;
+  const float* __restrict__ wt = second ? wt1 : wt0;
+  float* __restrict__ out = second ? out1 : out0;
+  const float* __restrict__ dkt = second ? dkt1 : nullptr;
   const int lane = tid & 63, f0 = 16 * (tid >> 6);
   {
     // K~ into LDS in batches of kB loads per lane, each batch's loads issued
@@ -729,8 +736,6 @@ hipError_t launch_typed(const Plan& pl, const BwdWork& b, const Work& w, const v
   const int nst = (pl.N + kST - 1) / kST;
   hipLaunchKernelGGL(bwd_g_kernel<D>, dim3((pl.N + kGT - 1) / kGT, pl.P), dim3(256), 0, s, dout, w.ct, pl.ldc, b.y,
                      w.mu, w.rs, b.ab, b.gt, pl.N, m);
-  hipLaunchKernelGGL((bwd_sign_kernel<T, D>), dim3(nst, pl.P), dim3(4 * D), row_lds, s, (const T*)q, w.kt, b.gt, dq,
-                     pl.N, m, inv_lam, nullptr, pl.grid_w, pl.pool, pl.gw);
   constexpr size_t hv_lds = bwd_hv_lds<D>();
   static_assert(hv_lds <= 65536, "the key-side first pass fits in static-size LDS");
   hipLaunchKernelGGL((bwd_hv_kernel<T, D>), dim3((pl.N + kHT - 1) / kHT, pl.P), dim3(256), hv_lds, s, (const T*)v,
@@ -746,9 +751,9 @@ hipError_t launch_typed(const Plan& pl, const BwdWork& b, const Work& w, const v
                      (const T*)q, (const T*)k, w.kt, b.gt, b.ht, b.part, pl.N, m, kSliceChunks);
   hipLaunchKernelGGL(bwd_kt_combine_kernel<D>, dim3((m + LG - 1) / LG, pl.P), dim3(256), 0, s, b.part, slices,
                      w.kt, w.w, pl.mp, b.dw, b.dkt, m, pl.eps, inv_lam);
-  // dK: the B part, plus the pooling adjoint of dK~.
-  hipLaunchKernelGGL((bwd_sign_kernel<T, D>), dim3(nst, pl.P), dim3(4 * D), row_lds, s, (const T*)k, w.kt, b.ht, dk,
-                     pl.N, m, inv_lam, b.dkt, pl.grid_w, pl.pool, pl.gw);
+  // dQ, and dK: the B part plus the pooling adjoint of dK~, in one launch.
+  hipLaunchKernelGGL((bwd_sign_kernel<T, D>), dim3(nst, pl.P, 2), dim3(4 * D), row_lds, s, (const T*)q, b.gt, dq,
+                     (const T*)k, b.ht, dk, b.dkt, w.kt, pl.N, m, inv_lam, pl.grid_w, pl.pool, pl.gw);
   return hipGetLastError();
 }
 

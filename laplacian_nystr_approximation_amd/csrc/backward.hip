@@ -302,19 +302,18 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(const float* __restr
 // dC_ij = (g_ij - a_j - z_ij b_j) r_j, z_ij = (C_ij - mu_j) r_j and g = dO Y^T.
 // Workgroup (tile, p) takes kGT tokens; per block of 64 landmarks, g^T for the
 // tile runs on fp32 MFMA 16x16x4 from Y and the tile's rows of dO in LDS
-// (wavefront w: landmarks 16 w + [0, 16)), and the lanes finish G^T from C^T
-// in their own accumulator positions.
+// (2 x 64 rows of D + 1 floats at lds; wavefront w: landmarks 16 w + [0, 16)),
+// and the lanes finish G^T from C^T in their own accumulator positions.
 constexpr int kGT = 64;  // tokens per tile
 
 template <int D>
-__global__ __launch_bounds__(256) void bwd_g_kernel(const float* __restrict__ dout, const float* __restrict__ ct,
-                                                    int ldc, const float* __restrict__ y,
-                                                    const float* __restrict__ mu, const float* __restrict__ rs,
-                                                    const float* __restrict__ ab, float* __restrict__ gt, int N,
-                                                    int m) {
+__device__ __forceinline__ void bwd_g_body(float* __restrict__ lds, const float* __restrict__ dout,
+                                           const float* __restrict__ ct, int ldc, const float* __restrict__ y,
+                                           const float* __restrict__ mu, const float* __restrict__ rs,
+                                           const float* __restrict__ ab, float* __restrict__ gt, int N, int m) {
   constexpr int kS = D + 1;
-  __shared__ float ys[64 * kS];   // [j][f] the block's Y rows
-  __shared__ float gs[kGT * kS];  // [i][f] the tile's dO rows
+  float* ys = lds;            // [64][D+1] the block's Y rows
+  float* gs = ys + 64 * kS;   // [kGT][D+1] the tile's dO rows
   const int tile = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, li = lane & 15, lk = lane >> 4;
   const int n0 = tile * kGT, nv = min(kGT, N - n0);
@@ -373,7 +372,8 @@ __global__ __launch_bounds__(256) void bwd_g_kernel(const float* __restrict__ do
 }
 
 // Key side, first pass, on fp32 MFMA 16x16x4.  The forward left B in the
-// H^T buffer ([P][m][N]); workgroup (tile, p) takes kHT tokens and, per block
+// H^T buffer ([P][m][N]); workgroup (tile, p) takes kHT tokens (LDS at lds,
+// bwd_hv_lds bytes) and, per block
 // of 64 landmarks, stages that block's B, dBV and the tile's V in LDS, forms
 // dBV V^T (wavefront w: landmarks 16 w + [0, 16)) and overwrites B with
 // H = (dBV V^T) (.) B in place, and accumulates dV = B^T dBV over the blocks
@@ -387,10 +387,10 @@ constexpr size_t bwd_hv_lds() {
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(256, 3) void bwd_hv_kernel(const T* __restrict__ v, const float* __restrict__ dbv,
-                                                     float* __restrict__ ht, float* __restrict__ dv, int N, int m) {
+__device__ __forceinline__ void bwd_hv_body(float* __restrict__ lds, const T* __restrict__ v,
+                                            const float* __restrict__ dbv, float* __restrict__ ht,
+                                            float* __restrict__ dv, int N, int m) {
   constexpr int kVS = D + 1, kBS = kHT + 4;
-  extern __shared__ __align__(16) float lds[];
   float* dbl = lds;             // [64][D+1]  the block's dBV rows
   float* vs = dbl + 64 * kVS;   // [kHT][D+1] the tile's V rows
   float* bs = vs + kHT * kVS;   // [64][kHT+4] B of the block and tile
@@ -483,6 +483,31 @@ __global__ __launch_bounds__(256, 3) void bwd_hv_kernel(const T* __restrict__ v,
       const int n = 16 * w + 4 * lk + r;
       if (n < nv) dv[prob + (size_t)(n0 + n) * D + 16 * bj + li] = adv[bj][r];
     }
+}
+
+// The two first passes in one launch: blockIdx.z = 0 runs the query side
+// (bwd_g_body), 1 the key side (bwd_hv_body), on the same 64-token tiles; one
+// dynamic LDS buffer serves either.
+static_assert(kGT == kHT, "both first passes take the same token tiles");
+
+template <int D>
+constexpr size_t bwd_first_lds() {
+  return bwd_hv_lds<D>() > 2 * 64 * (D + 1) * sizeof(float) ? bwd_hv_lds<D>() : 2 * 64 * (D + 1) * sizeof(float);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256, 3) void bwd_first_kernel(const float* __restrict__ dout,
+                                                           const float* __restrict__ ct, int ldc,
+                                                           const float* __restrict__ y, const float* __restrict__ mu,
+                                                           const float* __restrict__ rs, const float* __restrict__ ab,
+                                                           float* __restrict__ gt, const T* __restrict__ v,
+                                                           const float* __restrict__ dbv, float* __restrict__ ht,
+                                                           float* __restrict__ dv, int N, int m) {
+  extern __shared__ __align__(16) float lds[];
+  if (blockIdx.z == 0)
+    bwd_g_body<D>(lds, dout, ct, ldc, y, mu, rs, ab, gt, N, m);
+  else
+    bwd_hv_body<T, D>(lds, v, dbv, ht, dv, N, m);
 }
 
 // Token-side sign sums: out_n = -(1/lambda) sum_j w[j][n] sign(x_n - K~_j),
@@ -734,12 +759,11 @@ hipError_t launch_typed(const Plan& pl, const BwdWork& b, const Work& w, const v
   }
   const size_t row_lds = (size_t)m * D * sizeof(float);  // <= 64 KB
   const int nst = (pl.N + kST - 1) / kST;
-  hipLaunchKernelGGL(bwd_g_kernel<D>, dim3((pl.N + kGT - 1) / kGT, pl.P), dim3(256), 0, s, dout, w.ct, pl.ldc, b.y,
-                     w.mu, w.rs, b.ab, b.gt, pl.N, m);
-  constexpr size_t hv_lds = bwd_hv_lds<D>();
-  static_assert(hv_lds <= 65536, "the key-side first pass fits in static-size LDS");
-  hipLaunchKernelGGL((bwd_hv_kernel<T, D>), dim3((pl.N + kHT - 1) / kHT, pl.P), dim3(256), hv_lds, s, (const T*)v,
-                     b.dbv, b.ht, dv, pl.N, m);
+  // G (query side) and H, dV (key side) in one launch.
+  constexpr size_t first_lds = bwd_first_lds<D>();
+  static_assert(first_lds <= 65536, "the first passes fit in static-size LDS");
+  hipLaunchKernelGGL((bwd_first_kernel<T, D>), dim3((pl.N + kHT - 1) / kHT, pl.P, 2), dim3(256), first_lds, s, dout,
+                     w.ct, pl.ldc, b.y, w.mu, w.rs, b.ab, b.gt, (const T*)v, b.dbv, b.ht, dv, pl.N, m);
   // Landmark side in token slices of kSliceChunks chunks; the partials reuse
   // the C^T g partial buffer ([P][tiles][m][d], tiles >= slices), which is
   // free once dY is formed.

@@ -199,8 +199,8 @@ int lapnys_forward_profiled(const void* q, const void* k, const void* v, float* 
 /* Backward pass (EN section 3: the kernels serve forward and backward): the
  * gradients of sum(dout * O) with respect to q, k and v, where O is the
  * forward's output for the same inputs and params.  The call runs the forward
- * itself (into the workspace; dq holds O until it is overwritten) and then the
- * backward kernels.  The inverse enters as X = W^-1 (dW = -X^T dX X^T, with X
+ * itself into the workspace (all but its output stage: O is not needed)
+ * and then the backward kernels.  The inverse enters as X = W^-1 (dW = -X^T dX X^T, with X
  * the Newton-Schulz result).  Supported: the Laplacian kernel with the
  * Newton-Schulz solver (with or without LAPNYS_NS_REFINE / LAPNYS_NS_PLAIN),
  * every m the forward supports; with LAPNYS_GAUSSIAN or LAPNYS_SOLVER_CG,

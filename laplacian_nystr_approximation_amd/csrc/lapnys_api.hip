@@ -234,7 +234,8 @@ int run(const Plan& pl, const void* q, const void* k, const void* v, float* out,
     if (pl.refine && !ok(lapnys::launch_refine(pl, W, s), "refinement launch")) return LAPNYS_ERR_HIP;
     if (!mark(2 * LAPNYS_STAGE_NS + 1)) return LAPNYS_ERR_HIP;
     if (!ok(lapnys::launch_reduce(pl, W, s, fin), "reduce launch")) return LAPNYS_ERR_HIP;
-    if (!ok(lapnys::launch_output(pl, W, out, s, span(LAPNYS_STAGE_OUTPUT)), "output launch")) return LAPNYS_ERR_HIP;
+    if (out && !ok(lapnys::launch_output(pl, W, out, s, span(LAPNYS_STAGE_OUTPUT)), "output launch"))
+      return LAPNYS_ERR_HIP;
     return LAPNYS_OK;
   }
 
@@ -274,7 +275,8 @@ int run(const Plan& pl, const void* q, const void* k, const void* v, float* out,
     if (!ok(hipStreamWaitEvent(s, dc->join, 0), "hipStreamWaitEvent")) return LAPNYS_ERR_HIP;
     if (!ok(lapnys::launch_y(pl, W, s, {nullptr, fin.stop}), "Y launch")) return LAPNYS_ERR_HIP;
   }
-  if (!ok(lapnys::launch_output(pl, W, out, s, span(LAPNYS_STAGE_OUTPUT)), "output launch")) return LAPNYS_ERR_HIP;
+  if (out && !ok(lapnys::launch_output(pl, W, out, s, span(LAPNYS_STAGE_OUTPUT)), "output launch"))
+    return LAPNYS_ERR_HIP;
   return LAPNYS_OK;
 }
 
@@ -341,7 +343,7 @@ int backward_impl(const void* q, const void* k, const void* v, const float* dout
   int st = backward_plan(p, &pl, off, &total);
   if (st != LAPNYS_OK) return st;
   if (!dout || !dk || !dv || (((uintptr_t)dout | (uintptr_t)dk | (uintptr_t)dv) & 15)) return LAPNYS_ERR_INVALID_ARG;
-  // dq doubles as the forward's output buffer: the same checks apply to it.
+  // dq is checked as an output buffer of the forward's shape would be.
   st = check_buffers(q, k, v, dq, pl, ws, ws_bytes);
   if (st != LAPNYS_OK) return st;
   if (ws_bytes < total) return LAPNYS_ERR_WORKSPACE;
@@ -367,7 +369,9 @@ int backward_impl(const void* q, const void* k, const void* v, const float* dout
   // in place.
   lapnys::Work W = carve(pl, ws);
   W.bt = B.ht;
-  st = run(pl, q, k, v, dq, W, nullptr, s);
+  // The backward reads C, B, W, X, B V and the column statistics from the
+  // workspace but not O, so the forward skips its output stage (out = null).
+  st = run(pl, q, k, v, nullptr, W, nullptr, s);
   if (st != LAPNYS_OK) return st;
   if (!ok(lapnys::launch_backward(pl, B, W, q, k, v, dout, dq, dk, dv, s), "backward launch")) return LAPNYS_ERR_HIP;
   return LAPNYS_OK;

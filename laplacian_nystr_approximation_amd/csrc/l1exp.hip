@@ -44,7 +44,8 @@ using namespace kmat;
 // operand does not).  Scalar loads are as fast when the scalar cache holds
 // the rows, but workgroups of different problems sharing a CU evict each
 // other's rows, so every landmark reads from LDS.
-constexpr int kLds = 0, kSgpr = 1;
+constexpr int kLds = 0;
+[[maybe_unused]] constexpr int kSgpr = 1;
 constexpr int kSrc[4] = {kLds, kLds, kLds, kLds};
 
 // Row j of the tile = exp2(scale * sum_t |x[t] - k_j[t]|) for the lb landmarks

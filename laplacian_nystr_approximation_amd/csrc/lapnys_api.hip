@@ -433,7 +433,7 @@ int lapnys_forward(const void* q, const void* k, const void* v, float* out, cons
   if (c.bytes < pl.total) {
     if (c.ptr) {
       if (hipDeviceSynchronize() != hipSuccess) return LAPNYS_ERR_HIP;
-      hipFree(c.ptr);
+      (void)hipFree(c.ptr);
       c.ptr = nullptr;
       c.bytes = 0;
     }
@@ -452,13 +452,15 @@ void lapnys_release(void) {
   const bool have_cur = hipGetDevice(&cur) == hipSuccess;
   for (size_t dev = 0; dev < g_cache.size(); ++dev) {
     if (!g_cache[dev].ptr) continue;
+    // Release is best effort: a failed synchronise or free leaves nothing to
+    // report to (the function returns no status), and the slot is dropped.
     if (hipSetDevice((int)dev) == hipSuccess) {
-      hipDeviceSynchronize();
-      hipFree(g_cache[dev].ptr);
+      (void)hipDeviceSynchronize();
+      (void)hipFree(g_cache[dev].ptr);
     }
     g_cache[dev] = Cached();
   }
-  if (have_cur) hipSetDevice(cur);
+  if (have_cur) (void)hipSetDevice(cur);
 }
 
 int lapnys_backward_workspace_size(const lapnys_params* p, size_t* bytes) {

@@ -148,6 +148,8 @@ def _cg_cases():
         Workload("cg_m100_20x20_p2_d32", grid_h=20, grid_w=20, d=32, pool=2, dtype="f32", **base),
         Workload("cg_m256_16x16_p1", grid_h=16, grid_w=16, d=64, pool=1, dtype="f32", **{**base, "ns_iters": 40}),
         Workload("cg_single_landmark_6x6", grid_h=6, grid_w=6, d=64, pool=6, dtype="f32", **base),
+        # m = 36: three 16-row landmark blocks in the kernel-matrix stage
+        Workload("cg_m36_12x12_p2", grid_h=12, grid_w=12, d=64, pool=2, dtype="f32", **base),
         Workload("cg_ns0_14x14", grid_h=14, grid_w=14, d=32, pool=2, dtype="f32", **{**base, "ns_iters": 0}),
         c("long_256x256_bf16"),
     ]
@@ -185,6 +187,8 @@ def _plain_cases():
         Workload("plain_ragged_18x14_p2", grid_h=18, grid_w=14, d=64, pool=2, dtype="f32", **base),
         Workload("plain_ragged_10x30_p5_d32", grid_h=10, grid_w=30, d=32, pool=5, dtype="bf16", **base),
         Workload("plain_single_landmark_6x6", grid_h=6, grid_w=6, d=64, pool=6, dtype="f32", **base),
+        # m = 40: three 16-row landmark blocks in the kernel-matrix stage
+        Workload("plain_m40_16x10_p2_d32", grid_h=16, grid_w=10, d=32, pool=2, dtype="bf16", **base),
         Workload("plain_refine_14x14", grid_h=14, grid_w=14, d=64, pool=2, dtype="f32", refine=True, **base),
     ]
 

@@ -254,19 +254,6 @@ def kernel_value_comparison(w, q, k, v, dev):
     return out
 
 
-def near_duplicate_keys(k, w, delta, rng):
-    """K with every odd pooled window of each landmark row replaced by its left
-    neighbour's tokens plus delta-scaled noise, so that pairs of landmarks
-    nearly coincide and W is close to singular (float32 inputs)."""
-    k = k.copy()
-    p, gw = w.pool, w.grid_w // w.pool
-    g = k.reshape(w.B, w.H, w.grid_h, w.grid_w, w.d)
-    for j in range(1, gw, 2):
-        src = g[:, :, :, (j - 1) * p:j * p, :]
-        g[:, :, :, j * p:(j + 1) * p, :] = src + delta * rng.standard_normal(src.shape).astype(np.float32)
-    return g.reshape(k.shape)
-
-
 def solver_study_main(args):
     """Residual against iterations, Newton-Schulz against CG, on W made
     ill-conditioned by a small eps or by near-duplicate landmarks (the pages'
@@ -285,8 +272,6 @@ def solver_study_main(args):
 
     dev = torch.device("cuda:0")
     base = dataclasses.replace(WORKLOADS["stage1_56x56_f32"], B=4, name="study_56x56_f32")
-    x = make_inputs(base)
-    rng = np.random.Generator(np.random.PCG64(7))
     conditions = [("eps=1e-1", 1e-1, None), ("eps=1e-3", 1e-3, None),
                   ("eps=1e-3, near-duplicate landmarks (delta=1e-2)", 1e-3, 1e-2),
                   ("eps=1e-5, near-duplicate landmarks (delta=1e-3)", 1e-5, 1e-3),
@@ -294,8 +279,10 @@ def solver_study_main(args):
     steps = (4, 8, 12, 16, 20, 24, 32, 48)
     P, m = base.P, base.m
     for label, eps, delta in conditions:
-        k32 = x.k if delta is None else near_duplicate_keys(x.k, base, delta, rng)
-        q, k, v = (torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev) for a in (x.q, k32, x.v))
+        # Near-duplicate landmarks: every odd pooled window column of K copies
+        # its left neighbour plus delta-scaled noise (lapnys_inputs).
+        x = make_inputs(base if delta is None else base.with_(near_dup=delta))
+        q, k, v = (torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev) for a in (x.q, x.k, x.v))
         kappa = None
         for solver in ("ns", "ns_plain", "cg"):
             for T in steps:

@@ -22,10 +22,22 @@
  *
  * Layouts: q, k, v and out are dense, C-order [B, H, N, d] arrays; problem
  * (b, h) is the contiguous block starting at element (b * H + h) * N * d.
- * q, k and v are float32 or bfloat16 (dtype); out is always float32.  All
- * arithmetic after the input load is float32 (landmark pooling sums in
- * float64 and rounds once), so results do not depend on the input storage
- * type beyond the input values themselves.
+ * q, k and v are float32 or bfloat16 (dtype); out is always float32.
+ *
+ * Precision.  Every value is held in float32 after the input load (bf16
+ * inputs widen exactly).  Landmark pooling sums in float64 and rounds once.
+ * The L1 distances, exponentials, W and the whitening statistics are float32
+ * vector arithmetic (the statistics are merged in float64).  The products
+ * B V and Z Y, and the Newton-Schulz steps for m <= 64 except the last ones,
+ * run on bf16 MFMA with every float32 operand split into a bf16 high part and
+ * a bf16 low part and three of the four partial products (hi*hi, hi*lo,
+ * lo*hi) accumulated in float32: each product keeps all but about 2^-16 of
+ * its value.  The last Newton-Schulz steps (at least two, and every step once
+ * ||W||_1 max|X| exceeds 64), Y = X (B V), the m > 64 solver and the CG
+ * solver use float32 products (fp32 MFMA).  Measured against the float64
+ * oracle the output stays within 1e-4 of max|O| (normwise) for float32 and
+ * bf16 inputs alike.  Results do not depend on the input storage type beyond
+ * the input values themselves.
  *
  * Ownership and threading: every pointer argument belongs to the caller.  The
  * library keeps no pointer after a call returns.  Device pointers must point
@@ -78,14 +90,13 @@ typedef enum { LAPNYS_F32 = 0, LAPNYS_BF16 = 1 } lapnys_dtype;
  *   zero, or so small that p.(W p) underflows to zero, stops changing).  X is not formed: the debug form leaves its X
  *   buffer untouched.  Not combinable with LAPNYS_NS_REFINE.
  * LAPNYS_NS_PLAIN: m <= 64 only (larger m always runs so): the Newton-Schulz
- *   steps in the plain form, X <- X (2I - W X) with every entry formed on
- *   float32 products, as a launch of its own beside the kernel-matrix stage.
- *   The default schedule for m <= 64 runs inside the kernel-matrix launch,
- *   takes most steps on bf16-split products and keeps X exactly symmetric by
- *   storing one triangle of X (W X) with its mirror; it reaches the float32
- *   floor for cond(W) up to ~1e3, but a near-singular W (cond ~1e4 and more,
- *   e.g. near-duplicate landmarks with a tiny eps) makes it stall or diverge
- *   where the plain form converges.  Slower; same results otherwise. */
+ *   steps X <- X (2I - W X) with every product in float32, as a launch of
+ *   its own beside the kernel-matrix stage.  The default schedule for
+ *   m <= 64 runs inside the kernel-matrix launch, forms every entry of
+ *   2X - X (W X) and takes the early steps on bf16-split products while
+ *   ||W||_1 max|X| <= 64; it reaches the same float32 floor as the plain
+ *   steps at every condition number (near-singular W included).  Kept as the
+ *   reference schedule of the solver study; slower. */
 enum { LAPNYS_WHITEN = 1u, LAPNYS_NS_REFINE = 2u, LAPNYS_GAUSSIAN = 4u, LAPNYS_SOLVER_CG = 8u,
        LAPNYS_NS_PLAIN = 16u };
 

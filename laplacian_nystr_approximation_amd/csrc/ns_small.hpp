@@ -11,15 +11,29 @@
 // exp(0) + eps = 1 + eps exactly as float32 arithmetic gives it.  These
 // workgroups run inside the kernel-matrix stage's launch (l1exp.hip).
 //
+// Form of a step: X_next = 2X - X (W X), every entry formed.  With Q = W X
+// rounded to Q + dQ, the step's own error is X dQ, whose residual W X dQ is
+// about dQ once W X is near I.  Copying one triangle of the product onto the
+// other (to keep X exactly symmetric) would put dQ^T X there instead, whose
+// residual W dQ^T X is larger by up to cond(W): that drives the iteration
+// away from the inverse for cond(W) of about 1e4 and more.  So X is not
+// assumed symmetric: it is kept both row-major and transposed.
+//
 // Precision of the steps: the iteration corrects its own errors (from
 // X = W^-1 (I + E) one exact step gives W^-1 (I - E^2)), so only the last
-// steps decide the accuracy of the result.  All but the last kFp32Steps steps
-// take their products on bf16 MFMA with both operands split into high and
-// low parts (hi*hi + hi*lo + lo*hi, about 2^-16 of each product); the last
-// kFp32Steps steps are float32 products on fp32 MFMA, which square the
-// error left by the split steps and end at the float32 floor.  X itself is
-// kept in float32 throughout: each lane holds the entries it produces in
-// registers, and only the MFMA operands in LDS are split.
+// steps decide the accuracy of the result.  Steps take their products on
+// bf16 MFMA with both operands split into high and low parts (hi*hi + hi*lo
+// + lo*hi: each entry of W X is off by about 2^-16 of sum_k |W_ik| |X_kj|,
+// at most 2^-16 rho with rho = ||W||_1 max|X|), while rho stays at most
+// kSplitGuard and until kFp32Steps steps remain; every later step takes
+// float32 products on fp32 MFMA, which square the error the split steps
+// left and end at the float32 floor.  In exact arithmetic rho after k steps
+// is at most 2^(k/2) (the iterate's eigenvalues are at most sqrt(2^k / alpha)
+// and ||W||_1 = sqrt(alpha)), so the guard cannot act before step 12, and
+// for a well-conditioned W (rho stays below 11 on the pooled heavy-tailed
+// landmarks) it never acts.  X itself is float32 throughout: each lane holds
+// the entries it produces in registers, and only the MFMA operands in LDS
+// are split.
 #pragma once
 
 #include "lapnys_internal.hpp"
@@ -32,36 +46,49 @@ constexpr int kLD = 68;  // float32 LDS row stride (floats): conflict-free colum
 constexpr int kLB = 72;  // bf16 LDS row stride (144-byte rows: 16-byte aligned, and
                          // 16 consecutive rows start in distinct 4-bank groups)
 constexpr int kXB = kMP * kLB;  // bf16 elements of one 64 x 64 high or low array
-constexpr int kFp32Steps = 2;   // final steps on float32 products
-// LDS of one problem's schedule (floats).  Split steps: X (high, low) twice
-// and (W X)^T (high, low), 6 kXB bf16 = 3 kXB floats.  Float32 steps (the
-// same bytes): X twice and (W X)^T, 3 kMP kLD floats.  Then 256 partial sums
-// and alpha.
+constexpr int kFp32Steps = 2;   // final steps on float32 products, at least
+constexpr float kSplitGuard = 64.f;  // largest rho = ||W||_1 max|X| for a split step
+// LDS of one problem's schedule (floats).  Split steps: X, X^T and (W X)^T,
+// each as high and low parts, 6 kXB bf16 = 3 kXB floats.  Float32 steps (the
+// same bytes): X, X^T and (W X)^T, 3 kMP kLD floats.  Then 256 partial sums,
+// alpha and ||W||_1.
 constexpr int kNsRegion = 3 * kXB;
 static_assert(3 * kMP * kLD <= kNsRegion, "the float32 layout must fit in the split layout's bytes");
 constexpr int kNsLdsFloats = kNsRegion + 260;
 
+// Largest value over the 64 lanes of a wavefront of a non-negative x,
+// returned to every lane: DPP row rotations leave each 16-lane row's
+// largest value in every lane of the row, then row_bcast:15 and row_bcast:31
+// carry rows 0 and 2 into rows 1 and 3 and rows 0 + 1 into row 3 (rows the
+// mask leaves out read 0, which does not change a maximum of non-negative
+// values), and lane 63 is read.
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x122, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x121, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xa, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xc, 0xf, false)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
 // In-LDS schedule for m <= 64: one workgroup of four wavefronts per problem,
 // 57 KB of LDS (so it can share a CU with the kernel-matrix stage).
 //
-// Each step is evaluated as X_next = 2X - X (W X), which equals X (2I - W X).
-// Symmetry: W is bit-symmetric and X0 = W^T / alpha = W / alpha; for a
-// symmetric X the product X W X is symmetric whatever rounding X carries, so
-// Q = W X is formed in full (wavefront w: the four 16 x 16 blocks of block row
-// w) and stored transposed, while S = X Q is formed only on its 10 upper
-// 16 x 16 blocks (spread over the wavefronts as 3, 3, 2, 2) and stored with
-// its mirror image.  X thus stays exactly symmetric in one row-major copy,
-// and a column of X is read as a row.  (Mirroring a product that is not
-// symmetric in exact arithmetic, such as W X, would not be a faithful step:
-// the iteration then drifts away once it has converged.)
+// Wavefront w owns block row w (rows [16 w, 16 w + 16)) of Q = W X, of
+// S = X Q and of X: each lane holds the 16 entries X[16 w + 4 lk + r]
+// [16 bj + li] (bj, r in [0, 4)) in registers.  A step forms Q's block row
+// (W's rows from registers, X's columns read as rows of X^T), stores it
+// transposed, and after a barrier forms S's block row (X's rows, Q's columns
+// read as rows of Q^T), then writes X_next = 2X - S into both X (row-major)
+// and X^T.  Only wavefront w reads X's block row w, and X^T is read only in
+// the first half of a step, so both are updated in place.
 //
 // The float32 steps reduce over k in [0, 4 KS), KS = ceil(m / 4), on fp32
 // MFMA 16x16x4; the split steps over k in [0, 32 KB), KB = ceil(m / 32), on
 // bf16 MFMA 16x16x32.  Padding rows and columns of W and X are exact zeros
 // and stay so, and every step writes all 64 x 64 entries of X_next.
-__device__ __constant__ int8_t kBlkI[4][3] = {{0, 0, 0}, {0, 1, 1}, {1, 2, -1}, {2, 3, -1}};
-__device__ __constant__ int8_t kBlkJ[4][3] = {{0, 1, 2}, {3, 1, 2}, {3, 2, -1}, {3, 3, -1}};
-
+//
 // Problem p's W and X, for one workgroup of 256 lanes.  lds: kNsLdsFloats
 // floats, 16-byte aligned.
 template <int D, int KS>
@@ -69,21 +96,23 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
                                          float* __restrict__ xout, int m, float scale, float eps, int iters, int p,
                                          float* __restrict__ lds) {
   constexpr int KLD = D + 4;  // landmark staging stride: 16-byte rows for broadcast reads
-  static_assert(kMP * KLD <= kMP * kLD, "landmark staging must fit in an X buffer");
-  // Float32 layout: X (ping-pong, symmetric), then (W X)^T.
-  float4(*xs4)[kMP * kLD / 4] = reinterpret_cast<float4(*)[kMP * kLD / 4]>(lds);
-  float* ql = lds + 2 * kMP * kLD;
-  // Split layout (same bytes): X high/low parts ping-pong, then (W X)^T high/low.
-  __bf16* xb16 = reinterpret_cast<__bf16*>(lds);
-  __bf16* qb16 = xb16 + 4 * kXB;
-  // Set-up: W in the float32 (W X)^T buffer, the landmarks in the second
-  // float32 X buffer.  X0 goes to the first split X buffer (2 kXB bf16 =
-  // kXB floats), which ends before W starts; the landmarks are dead by then.
-  float* wl = ql;
-  float* kl = reinterpret_cast<float*>(xs4[1]);
-  static_assert(kXB <= 2 * kMP * kLD, "X0 must not overlap W");
-  float* red = lds + kNsRegion;  // [256] partial column sums, then alpha
+  static_assert(kMP * KLD <= kMP * kLD, "landmark staging must fit in one float32 buffer");
+  // Float32 layout: X, X^T, (W X)^T.
+  float* xf = lds;
+  float* xtf = lds + kMP * kLD;
+  float* qf = lds + 2 * kMP * kLD;
+  // Split layout (same bytes): X, X^T, (W X)^T, each high parts then low parts.
+  __bf16* xb = reinterpret_cast<__bf16*>(lds);
+  __bf16* xtb = xb + 2 * kXB;
+  __bf16* qb = xb + 4 * kXB;
+  // Set-up: W in the float32 (W X)^T buffer, the landmarks in the float32
+  // X^T buffer.  Both are dead once every lane holds its operands in
+  // registers (a barrier before X0 is stored).
+  float* wl = qf;
+  float* kl = xtf;
+  float* red = lds + kNsRegion;  // [256] partial column sums, then alpha and ||W||_1
   float& alpha_s = red[256];
+  float& norm1_s = red[257];
 
   // Beside the kernel-matrix workgroups on the same CUs, the solver's chain
   // of dependent products is the longer one: its wavefronts take issue
@@ -117,9 +146,9 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
   {
     const int b = lane;
     float csum = 0.f;  // |W[a][b]| over this wavefront's rows a, in increasing a
-    float xb[D];
+    float xb_[D];
 #pragma unroll
-    for (int t = 0; t < D; ++t) xb[t] = kl[min(b, m - 1) * KLD + t];
+    for (int t = 0; t < D; ++t) xb_[t] = kl[min(b, m - 1) * KLD + t];
     for (int a0 = 16 * w; a0 < 16 * w + 16; a0 += 4) {
       if (a0 < m) {
         float s0[4] = {0.f, 0.f, 0.f, 0.f}, s1[4] = {0.f, 0.f, 0.f, 0.f};
@@ -131,10 +160,10 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const float4 r = *reinterpret_cast<const float4*>(ka[u] + t);
-            s0[u] += fabsf(r.x - xb[t]);
-            s1[u] += fabsf(r.y - xb[t + 1]);
-            s0[u] += fabsf(r.z - xb[t + 2]);
-            s1[u] += fabsf(r.w - xb[t + 3]);
+            s0[u] += fabsf(r.x - xb_[t]);
+            s1[u] += fabsf(r.y - xb_[t + 1]);
+            s0[u] += fabsf(r.z - xb_[t + 2]);
+            s1[u] += fabsf(r.w - xb_[t + 3]);
           }
           // The sums are in/out operands here: each 4-feature chunk's row
           // values are read just before use (bounded registers).
@@ -172,25 +201,14 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
     float cm = ((red[tid] + red[kMP + tid]) + red[2 * kMP + tid]) + red[3 * kMP + tid];
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) cm = fmaxf(cm, __shfl_xor(cm, off, 64));
-    if (tid == 0) alpha_s = cm * cm;
+    if (tid == 0) {
+      alpha_s = cm * cm;
+      norm1_s = cm;
+    }
   }
   __syncthreads();
 
   const int li = lane & 15, lk = lane >> 4;
-  // This wavefront's upper blocks of S = X Q.  Wavefronts with two upper
-  // blocks run a third, unstored copy of their last block: every wavefront
-  // issues the same MFMA sequence and none branches inside it.
-  int bI[3], bJ[3];
-#pragma unroll
-  for (int b = 0; b < 3; ++b) {
-    bI[b] = kBlkI[w][b];
-    bJ[b] = kBlkJ[w][b];
-  }
-  const int nb = bI[2] < 0 ? 2 : 3;
-  if (nb == 2) {
-    bI[2] = bI[1];
-    bJ[2] = bJ[1];
-  }
   // W's A operands for every step of Q = W X, block row w.  fp32 MFMA
   // 16x16x4: A[li][lk] of step s = W[16 w + li][4 s + lk], KS = ceil(m / 4)
   // steps (a template parameter, so the step loops unroll without branches).
@@ -212,42 +230,62 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
       wlo[kb][i] = l;
     }
 
-  // X0 = W^T / alpha.  xij[b][r] = X[16 bI + 4 lk + r][16 bJ + li], the
-  // entries this lane produces (the upper-triangle ones of its blocks are
-  // the ones it stores); the split steps keep them in these registers.
+  // X0 = W^T / alpha.  xr[bj][r] = X[16 w + 4 lk + r][16 bj + li], the
+  // entries this lane produces in every step.
   const int n16 = iters > kFp32Steps ? iters - kFp32Steps : 0;
-  const float alpha = alpha_s;
-  float xij[3][4];
+  const float alpha = alpha_s, norm1 = norm1_s;
+  float xr[4][4];
 #pragma unroll
-  for (int b = 0; b < 3; ++b)
+  for (int bj = 0; bj < 4; ++bj)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) xij[b][r] = wl[(16 * bJ[b] + li) * kLD + 16 * bI[b] + 4 * lk + r] / alpha;
-  if (n16 > 0) {
-    // Every entry of X0, as high and low parts.
-    for (int e = tid; e < kMP * kMP / 2; e += 256) {
-      const int a = e >> 5, c = 2 * (e & 31);
-      uint32_t h, l;
-      split2(wl[c * kLD + a] / alpha, wl[(c + 1) * kLD + a] / alpha, h, l);
-      *reinterpret_cast<uint32_t*>(xb16 + a * kLB + c) = h;
-      *reinterpret_cast<uint32_t*>(xb16 + kXB + a * kLB + c) = l;
+    for (int r = 0; r < 4; ++r) xr[bj][r] = wl[(16 * bj + li) * kLD + 16 * w + 4 * lk + r] / alpha;
+  __syncthreads();  // every lane has read W and the landmarks: their buffers are free
+
+  const int i0 = 16 * w + 4 * lk;  // first row of this lane's entries
+  // This lane's entries of X into the split layout: row-major X (four
+  // 16-bit stores per part) and X^T (four consecutive entries of row
+  // 16 bj + li, one 8-byte store per part).
+  auto store_split = [&]() {
+    uint16_t* xh16 = reinterpret_cast<uint16_t*>(xb);
+    uint16_t* xl16 = xh16 + kXB;
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+      uint32_t h0, l0, h1, l1;
+      split2(xr[bj][0], xr[bj][1], h0, l0);
+      split2(xr[bj][2], xr[bj][3], h1, l1);
+      const int j = 16 * bj + li;
+      const uint32_t hw[4] = {h0 & 0xffffu, h0 >> 16, h1 & 0xffffu, h1 >> 16};
+      const uint32_t lw[4] = {l0 & 0xffffu, l0 >> 16, l1 & 0xffffu, l1 >> 16};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        xh16[(i0 + r) * kLB + j] = (uint16_t)hw[r];
+        xl16[(i0 + r) * kLB + j] = (uint16_t)lw[r];
+      }
+      *reinterpret_cast<uint2*>(xtb + j * kLB + i0) = make_uint2(h0, h1);
+      *reinterpret_cast<uint2*>(xtb + kXB + j * kLB + i0) = make_uint2(l0, l1);
     }
-  } else {
-    float* x0 = reinterpret_cast<float*>(xs4[0]);
-    for (int e = tid; e < kMP * kMP; e += 256) {
-      const int a = e >> 6, b = e & 63;
-      x0[a * kLD + b] = wl[b * kLD + a] / alpha;
+  };
+  // The same entries into the float32 layout.
+  auto store_f32 = [&]() {
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+      const int j = 16 * bj + li;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) xf[(i0 + r) * kLD + j] = xr[bj][r];
+      *reinterpret_cast<float4*>(&xtf[j * kLD + i0]) = make_float4(xr[bj][0], xr[bj][1], xr[bj][2], xr[bj][3]);
     }
-  }
+  };
+  if (n16 > 0)
+    store_split();
+  else
+    store_f32();
   __syncthreads();
 
-  // ---- split steps: X (hi, lo) in buffer cur -> buffer cur ^ 1 ----
-  int cur = 0;
-  for (int it = 0; it < n16; ++it) {
-    const __bf16* xh = xb16 + cur * 2 * kXB;
-    const __bf16* xlo = xh + kXB;
+  // ---- split steps ----
+  int it = 0;
+  while (it < n16) {
     // Q = W X, block row w, stored transposed: Q^T[j][i] = Q[i][j].  The B
-    // operand X[32 kb + 8 lk + e][16 bj + li] is read as row 16 bj + li (X is
-    // symmetric).
+    // operand X[32 kb + 8 lk + e][16 bj + li] is row 16 bj + li of X^T.
     {
       f32x4 acc[4];
 #pragma unroll
@@ -257,8 +295,8 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
 #pragma unroll
         for (int bj = 0; bj < 4; ++bj) {
           const int o = (16 * bj + li) * kLB + 32 * kb + 8 * lk;
-          const bf16x8 bh = *reinterpret_cast<const bf16x8*>(xh + o);
-          const bf16x8 bl = *reinterpret_cast<const bf16x8*>(xlo + o);
+          const bf16x8 bh = *reinterpret_cast<const bf16x8*>(xtb + o);
+          const bf16x8 bl = *reinterpret_cast<const bf16x8*>(xtb + kXB + o);
           acc[bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wlo[kb]), bh, acc[bj], 0, 0, 0);
           acc[bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wh[kb]), bl, acc[bj], 0, 0, 0);
           acc[bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wh[kb]), bh, acc[bj], 0, 0, 0);
@@ -271,101 +309,67 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
         uint32_t h0, l0, h1, l1;
         split2(acc[bj][0], acc[bj][1], h0, l0);
         split2(acc[bj][2], acc[bj][3], h1, l1);
-        const int o = (16 * bj + li) * kLB + 16 * w + 4 * lk;
-        *reinterpret_cast<uint2*>(qb16 + o) = make_uint2(h0, h1);
-        *reinterpret_cast<uint2*>(qb16 + kXB + o) = make_uint2(l0, l1);
+        const int o = (16 * bj + li) * kLB + i0;
+        *reinterpret_cast<uint2*>(qb + o) = make_uint2(h0, h1);
+        *reinterpret_cast<uint2*>(qb + kXB + o) = make_uint2(l0, l1);
       }
     }
     __syncthreads();
-    // S = X Q on the upper blocks; X_next = 2 X - S, stored with its mirror.
+    // S = X Q, block row w; X_next = 2 X - S.
     {
-      f32x4 acc[3];
+      f32x4 acc[4];
 #pragma unroll
-      for (int b = 0; b < 3; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int bj = 0; bj < 4; ++bj) acc[bj] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
+        const int oa = (16 * w + li) * kLB + 32 * kb + 8 * lk;  // X[16 w + li][32 kb + 8 lk + e]
+        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(xb + oa);
+        const bf16x8 al = *reinterpret_cast<const bf16x8*>(xb + kXB + oa);
 #pragma unroll
-        for (int b = 0; b < 3; ++b) {
-          const int oa = (16 * bI[b] + li) * kLB + 32 * kb + 8 * lk;  // X[16 bI + li][32 kb + 8 lk + e]
-          const int ob = (16 * bJ[b] + li) * kLB + 32 * kb + 8 * lk;  // Q[32 kb + 8 lk + e][16 bJ + li]
-          const bf16x8 ah = *reinterpret_cast<const bf16x8*>(xh + oa);
-          const bf16x8 al = *reinterpret_cast<const bf16x8*>(xlo + oa);
-          const bf16x8 qh = *reinterpret_cast<const bf16x8*>(qb16 + ob);
-          const bf16x8 ql2 = *reinterpret_cast<const bf16x8*>(qb16 + kXB + ob);
-          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, qh, acc[b], 0, 0, 0);
-          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, ql2, acc[b], 0, 0, 0);
-          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, qh, acc[b], 0, 0, 0);
+        for (int bj = 0; bj < 4; ++bj) {
+          const int ob = (16 * bj + li) * kLB + 32 * kb + 8 * lk;  // Q[32 kb + 8 lk + e][16 bj + li]
+          const bf16x8 qh = *reinterpret_cast<const bf16x8*>(qb + ob);
+          const bf16x8 ql = *reinterpret_cast<const bf16x8*>(qb + kXB + ob);
+          acc[bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, qh, acc[bj], 0, 0, 0);
+          acc[bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, ql, acc[bj], 0, 0, 0);
+          acc[bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, qh, acc[bj], 0, 0, 0);
         }
       }
-      __bf16* nh = xb16 + (cur ^ 1) * 2 * kXB;
-      __bf16* nl = nh + kXB;
+      float amax = 0.f;
 #pragma unroll
-      for (int b = 0; b < 3; ++b) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) xij[b][r] = 2.f * xij[b][r] - acc[b][r];
-        if (b < nb) {
-          uint32_t h0, l0, h1, l1;
-          split2(xij[b][0], xij[b][1], h0, l0);
-          split2(xij[b][2], xij[b][3], h1, l1);
-          const uint32_t hw[4] = {h0 & 0xffffu, h0 >> 16, h1 & 0xffffu, h1 >> 16};
-          const uint32_t lw[4] = {l0 & 0xffffu, l0 >> 16, l1 & 0xffffu, l1 >> 16};
-          const int i0 = 16 * bI[b] + 4 * lk, j = 16 * bJ[b] + li;
-          uint16_t* nh16 = reinterpret_cast<uint16_t*>(nh);
-          uint16_t* nl16 = reinterpret_cast<uint16_t*>(nl);
-          if (bI[b] != bJ[b]) {
-            // off the diagonal every entry is upper: the mirror image is four
-            // consecutive entries of row j
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              nh16[(i0 + r) * kLB + j] = (uint16_t)hw[r];
-              nl16[(i0 + r) * kLB + j] = (uint16_t)lw[r];
-            }
-            *reinterpret_cast<uint2*>(nh + j * kLB + i0) = make_uint2(h0, h1);
-            *reinterpret_cast<uint2*>(nl + j * kLB + i0) = make_uint2(l0, l1);
-          } else {
-            // diagonal block: only the upper-triangle entries, with their mirrors
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              if (i0 + r <= j) {
-                nh16[(i0 + r) * kLB + j] = (uint16_t)hw[r];
-                nl16[(i0 + r) * kLB + j] = (uint16_t)lw[r];
-                nh16[j * kLB + i0 + r] = (uint16_t)hw[r];
-                nl16[j * kLB + i0 + r] = (uint16_t)lw[r];
-              }
-            }
-          }
-        }
-      }
-    }
-    __syncthreads();
-    cur ^= 1;
-  }
-  if (n16 > 0) {
-    // Into the float32 layout for the last steps: the stored (upper) entries
-    // and their mirrors, from the registers.  The split buffers are dead
-    // (every wavefront passed the last step's barrier).
-    float* x0 = reinterpret_cast<float*>(xs4[0]);
-#pragma unroll
-    for (int b = 0; b < 3; ++b) {
-      if (b < nb) {
-        const int i0 = 16 * bI[b] + 4 * lk, j = 16 * bJ[b] + li;
+      for (int bj = 0; bj < 4; ++bj)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          if (bI[b] != bJ[b] || i0 + r <= j) {
-            x0[(i0 + r) * kLD + j] = xij[b][r];
-            x0[j * kLD + i0 + r] = xij[b][r];
-          }
+          xr[bj][r] = 2.f * xr[bj][r] - acc[bj][r];
+          amax = fmaxf(amax, fabsf(xr[bj][r]));
         }
-      }
+      // X's block row w is read by this wavefront only, and its reads above
+      // feed the products these stores depend on; X^T is not read in this
+      // half of the step.
+      store_split();
+      amax = wave_max_nonneg(amax);
+      if (lane == 0) red[w] = amax;
     }
     __syncthreads();
-    cur = 0;
+    ++it;
+    // The guard: the same four values in every wavefront, so the decision
+    // is uniform across the workgroup.  red[0..3] is next written after the
+    // next step's first barrier, which every wavefront passes after this read.
+    const float4 mx = *reinterpret_cast<const float4*>(red);
+    if (norm1 * fmaxf(fmaxf(mx.x, mx.y), fmaxf(mx.z, mx.w)) > kSplitGuard) break;
+  }
+  if (n16 > 0) {
+    // Into the float32 layout for the remaining steps (at least kFp32Steps),
+    // from the registers.  The split buffers are dead: every wavefront passed
+    // the last split step's barrier.
+    store_f32();
+    __syncthreads();
   }
 
   // ---- float32 steps ----
-  for (int it = n16; it < iters; ++it) {
-    const float* xc = reinterpret_cast<const float*>(xs4[cur]);
-    // Q = W X, block row w, stored transposed: ql[j][i] = Q[i][j].
+  for (; it < iters; ++it) {
+    // Q = W X, block row w, stored transposed: qf[j][i] = Q[i][j].  B operand
+    // X[4 st + lk][16 bj + li] = X^T[16 bj + li][4 st + lk].
     {
       f32x4 acc[4];
 #pragma unroll
@@ -374,73 +378,43 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
       for (int st = 0; st < KS; ++st) {
 #pragma unroll
         for (int bj = 0; bj < 4; ++bj) {
-          const float xb = xc[(16 * bj + li) * kLD + 4 * st + lk];  // X[4 st + lk][16 bj + li]
-          acc[bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(wreg[st], xb, acc[bj], 0, 0, 0);
+          const float xv = xtf[(16 * bj + li) * kLD + 4 * st + lk];
+          acc[bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(wreg[st], xv, acc[bj], 0, 0, 0);
         }
       }
-      // acc[bj][r] = Q[16 w + 4 lk + r][16 bj + li]: four consecutive entries of
-      // row 16 bj + li of Q^T.
 #pragma unroll
       for (int bj = 0; bj < 4; ++bj)
-        *reinterpret_cast<float4*>(&ql[(16 * bj + li) * kLD + 16 * w + 4 * lk]) =
+        *reinterpret_cast<float4*>(&qf[(16 * bj + li) * kLD + i0]) =
             make_float4(acc[bj][0], acc[bj][1], acc[bj][2], acc[bj][3]);
     }
     __syncthreads();
-    // S = X Q on the upper blocks; X_next = 2 X - S stored with its mirror.
+    // S = X Q, block row w; X_next = 2 X - S into X and X^T.
     {
-      float xo[3][4];  // X entries of this lane's outputs, read ahead of the products
+      f32x4 acc[4];
 #pragma unroll
-      for (int b = 0; b < 3; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) xo[b][r] = xc[(16 * bI[b] + 4 * lk + r) * kLD + 16 * bJ[b] + li];
-      f32x4 acc[3];
-#pragma unroll
-      for (int b = 0; b < 3; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int bj = 0; bj < 4; ++bj) acc[bj] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < KS; ++st) {
+        const float xa = xf[(16 * w + li) * kLD + 4 * st + lk];  // X[16 w + li][4 st + lk]
 #pragma unroll
-        for (int b = 0; b < 3; ++b) {
-          const float xa = xc[(16 * bI[b] + li) * kLD + 4 * st + lk];  // X[16 bi + li][4 st + lk]
-          const float qb = ql[(16 * bJ[b] + li) * kLD + 4 * st + lk];  // Q[4 st + lk][16 bj + li]
-          acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa, qb, acc[b], 0, 0, 0);
+        for (int bj = 0; bj < 4; ++bj) {
+          const float qv = qf[(16 * bj + li) * kLD + 4 * st + lk];  // Q[4 st + lk][16 bj + li]
+          acc[bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa, qv, acc[bj], 0, 0, 0);
         }
       }
-      float* xn = reinterpret_cast<float*>(xs4[cur ^ 1]);
 #pragma unroll
-      for (int b = 0; b < 3; ++b) {
-        if (b < nb) {
-          float v[4];
+      for (int bj = 0; bj < 4; ++bj)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = 2.f * xo[b][r] - acc[b][r];
-          const int i0 = 16 * bI[b] + 4 * lk, j = 16 * bJ[b] + li;
-          if (bI[b] != bJ[b]) {
-            // off the diagonal every entry is upper: the mirror image is four
-            // consecutive entries of row j
-#pragma unroll
-            for (int r = 0; r < 4; ++r) xn[(i0 + r) * kLD + j] = v[r];
-            *reinterpret_cast<float4*>(&xn[j * kLD + i0]) = make_float4(v[0], v[1], v[2], v[3]);
-          } else {
-            // diagonal block: only the upper-triangle entries, with their mirrors
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              if (i0 + r <= j) {
-                xn[(i0 + r) * kLD + j] = v[r];
-                xn[j * kLD + i0 + r] = v[r];
-              }
-            }
-          }
-        }
-      }
+        for (int r = 0; r < 4; ++r) xr[bj][r] = 2.f * xr[bj][r] - acc[bj][r];
+      store_f32();
     }
     __syncthreads();
-    cur ^= 1;
   }
 
+  // X (row-major, float32 layout) to the workspace.
   float* xp = xout + (size_t)p * kMP * kMP;
-  const float* xf = reinterpret_cast<const float*>(xs4[cur]);
   for (int e = tid; e < kMP * kMP; e += 256) xp[e] = xf[(e >> 6) * kLD + (e & 63)];
 }
-
 
 }  // namespace ns_detail
 }  // namespace lapnys

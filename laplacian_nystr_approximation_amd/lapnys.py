@@ -139,10 +139,18 @@ def params_for(w) -> lapnys_params:
 
 
 def _ptr(x) -> Optional[int]:
+    """Device pointer of a tensor argument.  Host tensors and tensors of
+    another device are refused here, before any call: the kernels would read
+    their addresses as device memory."""
     if x is None:
         return None
     if isinstance(x, int):
         return x
+    if not x.is_cuda:
+        raise ValueError("tensor arguments must be device tensors (got a tensor on the host)")
+    import torch
+    if x.device.index != torch.cuda.current_device():
+        raise ValueError(f"tensor on {x.device}, but the current device is cuda:{torch.cuda.current_device()}")
     if not x.is_contiguous():
         raise ValueError("tensor arguments must be contiguous")
     return x.data_ptr()
@@ -158,10 +166,14 @@ def _stream(stream) -> Optional[int]:
 
 
 def _ws(ws):
+    """(pointer, bytes) of a workspace: a device tensor, a raw (pointer, bytes)
+    pair, or None (null)."""
     if ws is None:
         return None, 0
     if isinstance(ws, tuple):
         return ws
+    if isinstance(ws, int):
+        raise ValueError("a raw workspace is passed as (pointer, bytes)")
     return _ptr(ws), ws.numel() * ws.element_size()
 
 

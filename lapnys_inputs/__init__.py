@@ -44,6 +44,11 @@ class Workload:
     kernel: str = "laplacian"  # or "gaussian"
     solver: str = "ns"  # or "cg" (conjugate gradient for W^-1 (B V))
     ns_plain: bool = False  # m <= 64: the plain float32 Newton-Schulz steps, a launch of their own
+    # > 0: every odd pooled window of each landmark row of K is replaced by its
+    # left neighbour's tokens plus near_dup-scaled normal noise (see
+    # make_inputs), so pairs of landmarks nearly coincide and W is close to
+    # singular.
+    near_dup: float = 0.0
 
     @property
     def N(self) -> int:
@@ -144,10 +149,44 @@ def make_grad_out(w: Workload, seed: int = 99) -> np.ndarray:
     return rng.standard_normal((w.B, w.H, w.N, w.d)).astype(np.float32)
 
 
+def near_duplicate_keys(k32: np.ndarray, w: Workload, delta: float, rng: np.random.Generator) -> np.ndarray:
+    """K (float32, [B, H, N, d]) with every odd pooled window column of the
+    token grid replaced by the window to its left plus delta * N(0, 1) noise
+    (float32): the landmarks of windows 2c and 2c + 1 then differ by about
+    delta, which makes the landmark kernel matrix nearly singular.  A
+    structural recipe for ill-conditioned inputs; it computes nothing of the
+    attention method."""
+    k = np.array(k32, dtype=np.float32, copy=True)
+    p, gw = w.pool, w.grid_w // w.pool
+    g = k.reshape(w.B, w.H, w.grid_h, w.grid_w, w.d)
+    for j in range(1, gw, 2):
+        src = g[:, :, :, (j - 1) * p:j * p, :]
+        g[:, :, :, j * p:(j + 1) * p, :] = src + np.float32(delta) * rng.standard_normal(src.shape).astype(np.float32)
+    return g.reshape(k.shape)
+
+
 def make_inputs(w: Workload, seed: int | None = None) -> Inputs:
-    """Draw Q, K, V for workload ``w`` from PCG64(seed) (default: the workload's seed)."""
-    rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
+    """Draw Q, K, V for workload ``w`` from PCG64(seed) (default: the workload's seed).
+
+    With ``w.near_dup > 0`` the float32 K is then made near-duplicate
+    (``near_duplicate_keys``, noise from PCG64(seed + 1000)) before any
+    rounding to bf16."""
+    s = w.seed if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(s))
     shape = (w.B, w.H, w.N, w.d)
+    if w.near_dup > 0:
+        x64 = [rng.standard_t(3.0, size=shape) * 0.25 for _ in range(3)]
+        x32 = [a.astype(np.float32) for a in x64]
+        x32[1] = near_duplicate_keys(x32[1], w, w.near_dup, np.random.Generator(np.random.PCG64(s + 1000)))
+        out = []
+        for a in x32:
+            if w.dtype == "f32":
+                out.append((a, a.astype(np.float64)))
+            else:
+                bits = f32_to_bf16_bits(a)
+                out.append((bits, bf16_bits_to_f32(bits).astype(np.float64)))
+        (q, qf), (k, kf), (v, vf) = out
+        return Inputs(q, k, v, qf, kf, vf)
     q, qf = _draw(rng, shape, w.dtype)
     k, kf = _draw(rng, shape, w.dtype)
     v, vf = _draw(rng, shape, w.dtype)

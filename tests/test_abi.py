@@ -203,3 +203,22 @@ def test_landmark_count_and_workspace():
     # monotone in the token count at fixed landmarks
     sizes = [L.lapnys_workspace_size(_p(grid_h=g, grid_w=g, pool=g // 8, dtype="f32")) for g in (16, 32, 64, 128)]
     assert sizes == sorted(sizes)
+
+
+def test_binding_refuses_host_tensors():
+    """Tensors on the host are refused by the binding before any call into the
+    library: their addresses are not device memory."""
+    import torch
+    p = _p(B=1, H=1, dtype="f32")
+    t = torch.zeros(196 * 64, dtype=torch.float32)
+    with pytest.raises(ValueError, match="device tensors"):
+        L.lapnys_forward_ws(t, t, t, t, p, None)
+    with pytest.raises(ValueError, match="device tensors"):
+        L.lapnys_forward(t, t, t, t, p)
+    with pytest.raises(ValueError, match="device tensors"):
+        L.lapnys_forward_debug(t, t, t, t, p, None, {})
+    with pytest.raises(ValueError, match="device tensors"):
+        L.lapnys_backward_ws(t, t, t, t, t, t, t, p, None)
+    # the workspace too
+    with pytest.raises(ValueError, match="device tensors"):
+        L.lapnys_forward_ws(1 << 24, 2 << 24, 3 << 24, 4 << 24, p, torch.zeros(1024, dtype=torch.uint8))

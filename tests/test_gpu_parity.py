@@ -8,8 +8,9 @@ import sys
 import numpy as np
 import pytest
 
-from gpu_harness import (NS_RESIDUAL, O_NORMWISE_F32, check_problem, gpu_available, o_errors, run_gpu,
-                         run_oracle, workload_inputs)
+from gpu_harness import (NS_RESIDUAL, O_NORMWISE_F32, U32, check_problem, gpu_available, ns_residual, o_errors,
+                         run_gpu, run_oracle, workload_inputs)
+import oracle
 from lapnys_inputs import WORKLOADS, Workload, bf16_bits_to_f32, f32_to_bf16_bits
 
 pytestmark = [pytest.mark.gpu,
@@ -35,17 +36,24 @@ def test_workload_parity(name):
     for p in range(w.P):
         check_problem(w, gpu, p, ref, p, report=report)
     _say(f"[parity] {name}: max O normwise {max(report['o_normwise']):.2e}, "
-         f"max rel L2 {max(report['o_rel_l2']):.2e}, max NS residual {max(report['ns_residual']):.2e}")
+         f"max rel L2 {max(report['o_rel_l2']):.2e}, max NS residual {max(report['ns_residual']):.2e}, "
+         f"max X rel {max(report['x_rel']):.2e} (gate use {max(report['x_gate_use']):.2f}), "
+         f"Y gate use {max(report['y_gate_use']):.2f}")
 
 
 @pytest.mark.parametrize("name", ["sweep_64x64_bf16", "sweep_128x128_bf16", "long_256x256_bf16"])
 def test_long_sequence_parity(name):
-    """m = 256 workloads: landmarks of every problem bit-exact; the full oracle on
-    problem 0 (and the last problem) at full size."""
+    """m = 256 workloads: the landmarks of every problem bit-exact (the oracle's
+    pooling of each problem); the full oracle on problem 0 and the last problem
+    at full size."""
     w = WORKLOADS[name]
     _say(f"[parity] {name} P={w.P} N={w.N} m={w.m}")
     x = workload_inputs(w)
     gpu = run_gpu(w, x)
+    for p in range(w.P):
+        b, h = divmod(p, w.H)
+        lm = oracle.pool_landmarks(x.kf[b, h], w.grid_h, w.grid_w, w.pool).astype(np.float32)
+        assert np.array_equal(gpu["landmarks"][p].view(np.uint32), lm.view(np.uint32)), f"landmarks of problem {p}"
     sample = [0, w.P - 1]
     ref = run_oracle(w, x, problems=sample)
     report = {}
@@ -61,6 +69,53 @@ def test_long_sequence_parity(name):
          f"NS residual max over problems {max(res_all):.2e}")
     if gate:
         assert max(res_all) <= NS_RESIDUAL
+
+
+def _ill_conditioned_cases():
+    """Near-duplicate landmarks (every odd pooled window column copies its left
+    neighbour plus noise of the given scale) with a small eps: W's condition
+    number is about 1.5e3, 1.5e4 and 1.5e5.  The step counts are ones at which
+    the float64 iteration has converged."""
+    base = WORKLOADS["stage1_56x56_f32"].with_(B=4, seed_index=80)
+    return [
+        base.with_(name="neardup_1e-2_eps1e-3_T32", near_dup=1e-2, eps=1e-3, ns_iters=32),
+        base.with_(name="neardup_1e-3_eps1e-5_T32", near_dup=1e-3, eps=1e-5, ns_iters=32),
+        base.with_(name="neardup_1e-3_eps1e-5_T48", near_dup=1e-3, eps=1e-5, ns_iters=48),
+        base.with_(name="neardup_1e-4_eps1e-6_T48", near_dup=1e-4, eps=1e-6, ns_iters=48),
+        base.with_(name="neardup_1e-3_eps1e-5_T32_bf16", near_dup=1e-3, eps=1e-5, ns_iters=32, dtype="bf16"),
+    ]
+
+
+@pytest.mark.parametrize("w", _ill_conditioned_cases(), ids=lambda w: w.name)
+def test_ill_conditioned_default_schedule(w):
+    """The default m <= 64 schedule on a nearly singular W against the oracle
+    and against LAPNYS_NS_PLAIN on the same inputs.  Every stage up to B V to
+    the usual bar; X and Y entry by entry (gates that grow with W's condition
+    number); the residual ||W X - I||_F within twice the plain float32
+    schedule's (plus 1e-6) and within the float32 floor 8 u cond(W); O within
+    max(1e-4, u cond(W)) normwise of the oracle, the float32 error scale of a
+    solve with W."""
+    _say(f"[ill] {w.name} P={w.P} N={w.N} m={w.m} eps={w.eps} T={w.ns_iters} {w.dtype}")
+    x = workload_inputs(w)
+    gpu = run_gpu(w, x)
+    plain = run_gpu(w.with_(ns_plain=True), x)
+    ref = run_oracle(w, x)
+    report = {}
+    for p in range(w.P):
+        own = np.linalg.norm(ref["W"][p] @ ref["X"][p] - np.eye(w.m))
+        assert own <= 1e-6, f"float64 iteration not converged ({own:.2e}): not a case for this test"
+        check_problem(w, gpu, p, ref, p, check_ns=False, check_o=False, report=report)
+        assert np.all(np.isfinite(gpu["X"][p])) and np.all(np.isfinite(gpu["O"][p]))
+        kappa = np.linalg.cond(gpu["W"][p].astype(np.float64))
+        res, res_plain = ns_residual(gpu["W"][p], gpu["X"][p]), ns_residual(plain["W"][p], plain["X"][p])
+        nw, _ = o_errors(gpu["O"][p], ref["O"][p])
+        _say(f"[ill] {w.name} p{p}: cond(W) {kappa:.2e} residual default {res:.2e} plain {res_plain:.2e} "
+             f"O normwise {nw:.2e}")
+        assert res <= 2.0 * res_plain + 1e-6, "default schedule worse than the plain float32 steps"
+        assert res <= 8.0 * U32 * kappa, "residual above the float32 floor"
+        assert nw <= max(O_NORMWISE_F32, U32 * kappa), f"O normwise {nw:.3e}"
+    _say(f"[ill] {w.name}: max X rel {max(report['x_rel']):.2e} (gate use {max(report['x_gate_use']):.2f}), "
+         f"Y gate use {max(report['y_gate_use']):.2f}")
 
 
 def _refine_cases():

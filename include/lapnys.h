@@ -114,7 +114,9 @@ enum {
                                   sizes beyond 32-bit element counts */
   LAPNYS_ERR_WORKSPACE = -4,   /* workspace null, smaller than
                                   lapnys_workspace_size, or not 256-B aligned */
-  LAPNYS_ERR_HIP = -5          /* a HIP runtime call or kernel launch failed */
+  LAPNYS_ERR_HIP = -5,         /* a HIP runtime call or kernel launch failed */
+  LAPNYS_ERR_SCRATCH = -6      /* lapnys_forward_noalloc: the workspace the
+                                  problem needs exceeds LAPNYS_SCRATCH_MAX_BYTES */
 };
 
 /* Problem description.  lambda is the kernel scale (the pages find 4 best,
@@ -223,6 +225,27 @@ int lapnys_forward_profiled(const void* q, const void* k, const void* v, float* 
 int lapnys_backward_workspace_size(const lapnys_params* p, size_t* bytes);
 int lapnys_backward_ws(const void* q, const void* k, const void* v, const float* dout, float* dq, float* dk,
                        float* dv, const lapnys_params* p, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * lapnys_forward_ws with the library's static device scratch array as the
+ * workspace.  Allocates nothing and calls no allocating routine; the first
+ * call on a device resolves the array's device address (hipGetSymbolAddress)
+ * and keeps it.  Each device holds one array of LAPNYS_SCRATCH_MAX_BYTES
+ * (64 MiB) from then until the process ends; it covers every problem whose
+ * lapnys_workspace_size is at most that (for example 32 problems of 3136
+ * tokens, or 320 problems of 196 tokens, at 49 landmarks), larger ones return
+ * LAPNYS_ERR_SCRATCH before anything is enqueued.  Only the single-stream
+ * sequence is offered: m <= 64 with the Laplacian kernel and the default
+ * Newton-Schulz schedule (LAPNYS_WHITEN and LAPNYS_NS_REFINE allowed); other
+ * flags or m > 64 return LAPNYS_ERR_UNSUPPORTED.  Every call on a device
+ * shares that device's array and its contents on entry do not matter (the
+ * previous call's values are overwritten): calls that overlap in time on one
+ * device race, so order them on one stream.  Other arguments as for
+ * lapnys_forward_ws. */
+#define LAPNYS_SCRATCH_MAX_BYTES ((size_t)64 << 20)
+int lapnys_forward_noalloc(const void* q, const void* k, const void* v, float* out,
+                           const lapnys_params* p, hipStream_t stream);
 
 /* Frees the library-owned workspaces of lapnys_forward (all devices).
  * Synchronises each device that had one. */

@@ -14,6 +14,7 @@ _BINDING_NAMES = {
     "lapnys_forward_debug", "lapnys_forward_profiled", "lapnys_landmark_count", "lapnys_workspace_size",
     "lapnys_release", "lapnys_status_string", "make_params", "params_for", "library", "LIB_PATH",
     "DEBUG_FIELDS", "STAGE_NAMES", "LAPNYS_NUM_STAGES", "lapnys_backward_ws", "lapnys_backward_workspace_size",
+    "lapnys_forward_noalloc",
 }
 
 

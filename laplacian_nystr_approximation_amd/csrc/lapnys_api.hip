@@ -384,6 +384,30 @@ struct Cached {
 std::mutex g_cache_mu;
 std::vector<Cached> g_cache;
 
+// Workspace of lapnys_forward_noalloc: a static device array of
+// LAPNYS_SCRATCH_MAX_BYTES, one copy per device (each device holds its copy
+// from the library's first use on it until the process ends).  In host code
+// `scratch` names a host-side stand-in, not a device address: its device
+// address on each device comes from hipGetSymbolAddress, taken once per
+// device with that device current, and only that address is used.
+static __device__ __align__(256) unsigned char scratch[LAPNYS_SCRATCH_MAX_BYTES];
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch;  // per device: the device address of `scratch`
+
+int scratch_address(void** out) {
+  int dev = 0;
+  if (!ok(hipGetDevice(&dev), "hipGetDevice") || dev < 0) return LAPNYS_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((int)g_scratch.size() <= dev) g_scratch.resize(dev + 1, nullptr);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (!ok(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress") || !ptr) return LAPNYS_ERR_HIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return LAPNYS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -446,6 +470,21 @@ int lapnys_forward(const void* q, const void* k, const void* v, float* out, cons
   return forward_impl(q, k, v, out, p, c.ptr, c.bytes, nullptr, nullptr, stream);
 }
 
+int lapnys_forward_noalloc(const void* q, const void* k, const void* v, float* out, const lapnys_params* p,
+                           hipStream_t stream) {
+  Plan pl;
+  int st = make_plan(p, &pl);
+  if (st != LAPNYS_OK) return st;
+  // Only the single-stream sequence: the other forms fork a library-owned
+  // stream, created on first use.
+  if (!pl.ns_in_launch) return LAPNYS_ERR_UNSUPPORTED;
+  if (pl.total > LAPNYS_SCRATCH_MAX_BYTES) return LAPNYS_ERR_SCRATCH;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != LAPNYS_OK) return st;
+  return forward_impl(q, k, v, out, p, ws, LAPNYS_SCRATCH_MAX_BYTES, nullptr, nullptr, stream);
+}
+
 void lapnys_release(void) {
   std::lock_guard<std::mutex> lock(g_cache_mu);
   int cur = 0;
@@ -486,6 +525,8 @@ const char* lapnys_status_string(int status) {
     case LAPNYS_ERR_UNSUPPORTED: return "unsupported: d must be 32 or 64, m <= 256, dtype f32 or bf16";
     case LAPNYS_ERR_WORKSPACE: return "workspace null, too small or not 256-byte aligned";
     case LAPNYS_ERR_HIP: return "HIP runtime error";
+    case LAPNYS_ERR_SCRATCH:
+      return "the problem's workspace exceeds the static scratch of lapnys_forward_noalloc (LAPNYS_SCRATCH_MAX_BYTES)";
     default: return "unknown status";
   }
 }

@@ -30,6 +30,8 @@ LAPNYS_ERR_SHAPE = -2
 LAPNYS_ERR_UNSUPPORTED = -3
 LAPNYS_ERR_WORKSPACE = -4
 LAPNYS_ERR_HIP = -5
+LAPNYS_ERR_SCRATCH = -6
+LAPNYS_SCRATCH_MAX_BYTES = 64 << 20
 
 LAPNYS_STAGE_POOL = 0
 LAPNYS_STAGE_NS = 1
@@ -95,6 +97,8 @@ def _load():
     lib.lapnys_backward_workspace_size.restype = ctypes.c_int
     lib.lapnys_backward_ws.argtypes = [vp, vp, vp, vp, vp, vp, vp, P, vp, ctypes.c_size_t, vp]
     lib.lapnys_backward_ws.restype = ctypes.c_int
+    lib.lapnys_forward_noalloc.argtypes = [vp, vp, vp, vp, P, vp]
+    lib.lapnys_forward_noalloc.restype = ctypes.c_int
     lib.lapnys_release.argtypes = []
     lib.lapnys_release.restype = None
     lib.lapnys_status_string.argtypes = [ctypes.c_int]
@@ -229,6 +233,13 @@ def lapnys_forward(q, k, v, out, params: lapnys_params, stream=None) -> None:
     _sizes_ok(params, q, k, v, out)
     _check(_lib.lapnys_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.byref(params), _stream(stream)),
            "lapnys_forward")
+
+
+def lapnys_forward_noalloc(q, k, v, out, params: lapnys_params, stream=None) -> None:
+    """The forward on the library's static device scratch (no workspace argument)."""
+    _sizes_ok(params, q, k, v, out)
+    _check(_lib.lapnys_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.byref(params), _stream(stream)),
+           "lapnys_forward_noalloc")
 
 
 def lapnys_forward_debug(q, k, v, out, params: lapnys_params, ws, dbg: Dict[str, object], stream=None) -> None:

@@ -26,7 +26,8 @@ def _declared():
 def test_header_declares_the_entry_points():
     assert _declared() == sorted([
         "lapnys_backward_workspace_size", "lapnys_backward_ws",
-        "lapnys_forward", "lapnys_forward_debug", "lapnys_forward_profiled", "lapnys_forward_ws",
+        "lapnys_forward", "lapnys_forward_debug", "lapnys_forward_noalloc", "lapnys_forward_profiled",
+        "lapnys_forward_ws",
         "lapnys_landmark_count", "lapnys_release", "lapnys_status_string", "lapnys_workspace_size"])
 
 
@@ -46,7 +47,7 @@ def test_struct_layout_matches_header():
 
 
 def test_status_strings():
-    for code in [0, -1, -2, -3, -4, -5]:
+    for code in [0, -1, -2, -3, -4, -5, -6]:
         assert L.lapnys_status_string(code) not in ("", "unknown status")
     assert L.lapnys_status_string(-99) == "unknown status"
 
@@ -222,3 +223,18 @@ def test_binding_refuses_host_tensors():
     # the workspace too
     with pytest.raises(ValueError, match="device tensors"):
         L.lapnys_forward_ws(1 << 24, 2 << 24, 3 << 24, 4 << 24, p, torch.zeros(1024, dtype=torch.uint8))
+
+
+def test_noalloc_checks_before_any_device_call():
+    """lapnys_forward_noalloc refuses, before touching a device, a problem
+    whose workspace exceeds the static scratch (LAPNYS_ERR_SCRATCH) and the
+    forms that need a second stream (LAPNYS_ERR_UNSUPPORTED)."""
+    lib = L.library()
+    a = 1 << 24
+    big = L.params_for(WORKLOADS["stage1_56x56_bf16"].with_(B=128))
+    assert L.lapnys_workspace_size(big) > B.LAPNYS_SCRATCH_MAX_BYTES
+    assert lib.lapnys_forward_noalloc(a, 2 * a, 3 * a, 4 * a, ctypes.byref(big), None) == B.LAPNYS_ERR_SCRATCH
+    for kw in ({"ns_plain": True}, {"solver": "cg"}, {"kernel": "gaussian"}, {"grid_h": 18, "grid_w": 18}):
+        p = L.params_for(WORKLOADS["tiny_f32"].with_(**kw))
+        assert lib.lapnys_forward_noalloc(a, 2 * a, 3 * a, 4 * a, ctypes.byref(p), None) == B.LAPNYS_ERR_UNSUPPORTED
+    assert L.lapnys_status_string(B.LAPNYS_ERR_SCRATCH).startswith("the problem's workspace exceeds")

@@ -89,32 +89,105 @@ def measured_traffic(workload: str):
     return float(rec["bytes_per_launch"])
 
 
-def cpu_baseline(w, x, budget_s: float):
-    """The oracle, single-threaded, over as many (batch, head) problems as fit in
-    the budget; scaled to tokens/s."""
-    import oracle
+_CPU_JOB = {}  # the workload and its inputs, inherited by forked oracle workers
+
+
+def _cpu_worker_init():
     try:
         from threadpoolctl import threadpool_limits
-        limit = threadpool_limits(1)
+        threadpool_limits(1)
     except Exception:  # pragma: no cover
-        limit = None
-    done = 0
-    t0 = time.perf_counter()
-    for p in range(w.P):
-        b, h = divmod(p, w.H)
-        oracle.attention_problem(x.qf[b, h], x.kf[b, h], x.vf[b, h], grid_h=w.grid_h, grid_w=w.grid_w,
-                                 pool=w.pool, lam=float(np.float32(w.lam)), eps=float(np.float32(w.eps)),
-                                 ns_iters=w.ns_iters, whiten=w.whiten, refine=w.refine, kernel=w.kernel,
-                                 solver=w.solver)
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    el = time.perf_counter() - t0
-    if limit is not None:
-        limit.restore_original_limits()
-    return {"value": done * w.N / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {w.P} (batch, head) problems of the same workload (N={w.N} tokens each), "
-                      f"float64 numpy, one thread, {el:.1f} s"}
+        pass
+
+
+def _cpu_problem(p):
+    import oracle
+    w, x = _CPU_JOB["w"], _CPU_JOB["x"]
+    b, h = divmod(p, w.H)
+    oracle.attention_problem(x.qf[b, h], x.kf[b, h], x.vf[b, h], grid_h=w.grid_h, grid_w=w.grid_w, pool=w.pool,
+                             lam=float(np.float32(w.lam)), eps=float(np.float32(w.eps)), ns_iters=w.ns_iters,
+                             whiten=w.whiten, refine=w.refine, kernel=w.kernel, solver=w.solver)
+    return p
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, x, budget_s: float):
+    """The oracle as it stands over the workload's (batch, head) problems on a
+    process pool of one single-threaded worker per available host core (at
+    most 16, the host share of one GPU), in whole rounds over all problems
+    until about budget_s seconds of CPU work are done; scaled to tokens/s.
+    Runs before the GPU is touched (the workers are forked)."""
+    import multiprocessing as mp
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    _CPU_JOB.update(w=w, x=x)
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores, initializer=_cpu_worker_init) as pool:
+        rounds = 0
+        t0 = time.perf_counter()
+        while True:
+            pool.map(_cpu_problem, range(w.P), chunksize=1)
+            rounds += 1
+            el = time.perf_counter() - t0
+            if el * min(cores, w.P) >= budget_s or rounds >= 1000:
+                break
+    _CPU_JOB.clear()
+    return {"value": rounds * w.P * w.N / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"{rounds} round(s) over all {w.P} (batch, head) problems of the same workload "
+                      f"(N={w.N} tokens each), float64 numpy, {cores} worker processes of one thread each "
+                      f"(one problem per task), {el:.2f} s wall"}
+
+
+def wall_clock_hz() -> float:
+    """Rate of the device wall clock (hipDeviceAttributeWallClockRate, kHz)."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    v = ctypes.c_int(0)
+    dev = ctypes.c_int(0)
+    if hip.hipGetDevice(ctypes.byref(dev)) != 0 or hip.hipDeviceGetAttribute(ctypes.byref(v), 10017, dev) != 0:
+        raise RuntimeError("hipDeviceGetAttribute(hipDeviceAttributeWallClockRate) failed")
+    return v.value * 1e3
+
+
+def solver_timing(w, L, q, k, v, out, params, ws, dev):
+    """The in-launch Newton-Schulz solver's own time, from its workgroups'
+    wall-clock stamps (debug form, one warm call), beside the span of the
+    kernel-matrix workgroups of the same launch.  MFMA fraction per occupied
+    CU: the method's 4 m^3 T flops per problem (float32 products) over the
+    solver workgroup's time, against one CU's share of the fp32 MFMA peak."""
+    import torch
+    nsc = torch.zeros((w.P, 3), dtype=torch.int64, device=dev)
+    kc = torch.zeros(2, dtype=torch.int64, device=dev)
+    L.lapnys_forward_debug(q, k, v, out, params, ws, {"ns_clock": nsc, "kernel_clock": kc})
+    hz = wall_clock_hz()
+    c = nsc.cpu().numpy().astype(np.float64)
+    kcl = kc.cpu().numpy().astype(np.float64)
+    us = 1e6 / hz
+    per = (c[:, 2] - c[:, 0]) * us
+    steps = (c[:, 2] - c[:, 1]) * us
+    flops = 4.0 * w.m ** 3 * w.ns_iters
+    cu_peak = MFMA_F32_FLOPS / CUS
+    return {"source": "solver workgroups' wall-clock stamps (lapnys_forward_debug ns_clock / kernel_clock)",
+            "solver_span_us": float((c[:, 2].max() - c[:, 0].min()) * us),
+            "per_problem_us_mean": float(per.mean()), "per_problem_us_max": float(per.max()),
+            "setup_us_mean": float(((c[:, 1] - c[:, 0]) * us).mean()), "steps_us_mean": float(steps.mean()),
+            "kernel_matrix_span_us": float((kcl[1] - kcl[0]) * us),
+            "solver_end_after_kernel_matrix_start_us": float((c[:, 2].max() - kcl[0]) * us),
+            "mfma_flops_per_problem": flops,
+            "mfma_frac_per_occupied_cu": float(flops / (per.mean() * 1e-6) / cu_peak),
+            "mfma_frac_per_occupied_cu_steps_only": float(flops / (steps.mean() * 1e-6) / cu_peak),
+            "chip_wide_mfma_frac": float(flops * w.P / ((c[:, 2].max() - c[:, 0].min()) * us * 1e-6)
+                                         / MFMA_F32_FLOPS)}
 
 
 def stage_hbm_bytes(w):
@@ -315,6 +388,33 @@ def solver_study_main(args):
     return 0
 
 
+def valu_probe_main(args):
+    """VALU issue rate of the L1 loop's instruction pair (v_sub_f32, then
+    v_add_f32 with an |.| source) with register operands, at 1, 2, 3, 4 and 8
+    wavefronts per SIMD (laplacian_nystr_approximation_amd/probe/valu_probe.hip).
+    One JSON line per occupancy: kernel time (events) and lane-operations per
+    CU per clock at the 2.4 GHz peak clock; a counter pass (SQ_INSTS_VALU,
+    GRBM_GUI_ACTIVE) gives the same per the clock actually run."""
+    import ctypes
+
+    import torch  # noqa: F401  (loads the HIP runtime the probe links against)
+    lib = ctypes.CDLL(os.path.join(ROOT, "laplacian_nystr_approximation_amd", "libvaluprobe.so"))
+    lib.valu_probe_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_float),
+                                   ctypes.POINTER(ctypes.c_double)]
+    lib.valu_probe_run.restype = ctypes.c_int
+    for waves in (1, 2, 3, 4, 8):
+        ms, ops = ctypes.c_float(), ctypes.c_double()
+        rc = lib.valu_probe_run(waves, args.probe_iters, 4, ctypes.byref(ms), ctypes.byref(ops))
+        if rc != 0:
+            print(json.dumps({"waves_per_simd": waves, "hip_error": rc}), flush=True)
+            return 1
+        per_clk = ops.value / (ms.value * 1e-3) / (CUS * CLOCK_HZ)
+        print(json.dumps({"probe": "valu_sub_add_abs", "waves_per_simd": waves, "kernel_ms": ms.value,
+                          "lane_ops": ops.value, "lane_ops_per_s": ops.value / (ms.value * 1e-3),
+                          "lane_ops_per_cu_per_clock_at_2.4GHz": per_clk}), flush=True)
+    return 0
+
+
 def backward_main(args):
     """The backward pass (lapnys_backward_ws: the forward, then the gradients of
     sum(dO * O) with respect to Q, K, V) on the bench workload: warm-up, then
@@ -368,6 +468,9 @@ def main(argv=None):
     ap.add_argument("--solver-study", action="store_true",
                     help="instead of the bench line: solve residual against steps, Newton-Schulz and CG, on "
                          "ill-conditioned W (small eps, near-duplicate landmarks), GPU and float64")
+    ap.add_argument("--valu-probe", action="store_true",
+                    help="instead of the bench line: the VALU issue-rate probe of the L1 instruction pair")
+    ap.add_argument("--probe-iters", type=int, default=4000)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0: skip)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the bench line: warm and cold single-call times and peak memory over the "
@@ -382,6 +485,8 @@ def main(argv=None):
         return solver_study_main(args)
     if args.backward:
         return backward_main(args)
+    if args.valu_probe:
+        return valu_probe_main(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this forward has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -453,6 +558,14 @@ def main(argv=None):
                 for s, name in enumerate(STAGE_NAMES)}
     evs.close()
 
+    solver = None
+    in_launch = (w.kernel == "laplacian" and w.solver == "ns" and w.m <= 64 and not w.ns_plain)
+    if in_launch:
+        # The solver runs inside the kernel-matrix launch: its own stamps, not
+        # events around the launch, give its time.
+        solver = solver_timing(w, L, q, k, v, out, params, ws, dev)
+        stage_ms.pop("ns", None)
+
     # Same work without any stage events.
     torch.cuda.synchronize()
     t2 = time.perf_counter()
@@ -507,6 +620,7 @@ def main(argv=None):
         "roofline": roof,
         "cpu_baseline": cpu,
         "stage_ms": stage_ms,
+        "solver": solver,
         "stage_roofline": stage_rooflines(w, stage_ms),
         "ms_per_step_without_events": plain_ms,
     }

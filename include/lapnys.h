@@ -140,7 +140,13 @@ typedef struct {
  * all float32, C order:
  *   landmarks [B*H, m, d]   C_t [B*H, m, N] (C transposed: landmark-major)
  *   W, X      [B*H, m, m]   BV, Y [B*H, m, d]   mu, sigma [B*H, m]
- * With whitening off, mu = 0 and sigma = 1. */
+ * With whitening off, mu = 0 and sigma = 1.
+ * Timing stamps (device wall clock, hipDeviceAttributeWallClockRate kHz):
+ *   ns_clock [B*H, 3]: start, first Newton-Schulz step and end of each
+ *     problem's solver workgroup, written only by the default m <= 64
+ *     schedule (the solver runs inside the kernel-matrix launch);
+ *   kernel_clock [2]: earliest start and latest end over the workgroups of
+ *     the Laplacian kernel-matrix stage (the solver's excluded). */
 typedef struct {
   float* landmarks;
   float* C_t;
@@ -150,6 +156,8 @@ typedef struct {
   float* Y;
   float* mu;
   float* sigma;
+  unsigned long long* ns_clock;
+  unsigned long long* kernel_clock;
 } lapnys_debug;
 
 /* Stage indices for lapnys_forward_profiled. */

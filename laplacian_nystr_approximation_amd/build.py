@@ -20,6 +20,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblapnys.so")
+# Measurement tooling built beside the library: the VALU issue-rate probe
+# (bench.py --valu-probe); not part of liblapnys.
+PROBE_SRC = os.path.join(PKG, "probe", "valu_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libvaluprobe.so")
 ARCH = "gfx950"
 
 # Packed fp32 instructions are disabled for every device compile.
@@ -86,6 +90,12 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-L", stub_dir, "-Wl,--no-as-needed",
           f"-Wl,-rpath,{rocm_lib}", "-Wl,--enable-new-dtags", "-o", tmp] + objs, verbose)
     os.replace(tmp, LIB)
+    pobj = os.path.join(BUILD_DIR, "valu_probe.o")
+    _run([hipcc] + flags + ["-c", PROBE_SRC, "-o", pobj], verbose)
+    ptmp = PROBE_LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-L", stub_dir, "-Wl,--no-as-needed",
+          f"-Wl,-rpath,{rocm_lib}", "-Wl,--enable-new-dtags", "-o", ptmp, pobj], verbose)
+    os.replace(ptmp, PROBE_LIB)
     return LIB
 
 

@@ -130,7 +130,8 @@ __device__ __forceinline__ void l1exp_body(const T* __restrict__ q, const T* __r
                                            float* __restrict__ ct, float2* __restrict__ stats,
                                            float* __restrict__ bvpart, float* __restrict__ bt, int N, int ldc,
                                            int m, int lbmax, int ntiles, int tpg, int groups, float scale, int jb,
-                                           int g, int p, float* __restrict__ tl) {
+                                           int g, int p, float* __restrict__ tl, unsigned long long* __restrict__ kclk) {
+  if (kclk != nullptr && threadIdx.x == 0) atomicMin(kclk, (unsigned long long)wall_clock64());
   // tl: the tile buffer, (lbmax + 1) * kTileRow floats; then kl: [lb][D],
   // this block's landmark rows
   float* kl = tl + (lbmax + 1) * kTileRow;
@@ -203,6 +204,7 @@ __device__ __forceinline__ void l1exp_body(const T* __restrict__ q, const T* __r
 
   // Partial B V of this tile group: rows j0 + [0, lb) of bvpart[p][g].
   bv.store(bvpart + ((size_t)p * groups + g) * m * D, j0, lb);
+  if (kclk != nullptr && threadIdx.x == 0) atomicMax(kclk + 1, (unsigned long long)wall_clock64());
 }
 
 // The stage's launch.  For m <= 64 (KS > 0) the first nns workgroups each run
@@ -221,12 +223,13 @@ __global__ __launch_bounds__(kTT) void l1exp_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ kt,
     float* __restrict__ ct, float2* __restrict__ stats, float* __restrict__ bvpart, float* __restrict__ bt,
     float* __restrict__ wout, float* __restrict__ xout, int N, int ldc, int m, int lbmax, int ntiles, int tpg, int groups, int jblocks,
-    float scale, float eps, int iters, int nns, int gap) {
+    float scale, float eps, int iters, int nns, int gap, unsigned long long* __restrict__ nsclk,
+    unsigned long long* __restrict__ kclk) {
   extern __shared__ __align__(16) float lds[];
   int b = blockIdx.x;
   if constexpr (KS > 0) {
     if (b < nns) {
-      ns_detail::ns_small<D, KS>(kt, wout, xout, m, scale, eps, iters, b, lds);
+      ns_detail::ns_small<D, KS>(kt, wout, xout, m, scale, eps, iters, b, lds, nsclk);
       return;
     }
     // Workgroups [gap, gap + nns) do nothing (see launch_kernel).
@@ -235,7 +238,7 @@ __global__ __launch_bounds__(kTT) void l1exp_kernel(
   }
   const int jb = b % jblocks, g = (b / jblocks) % groups, p = b / (jblocks * groups);
   l1exp_body<T, D, LBB>(q, k, v, kt, ct, stats, bvpart, bt, N, ldc, m, lbmax, ntiles, tpg, groups, scale, jb, g, p,
-                        lds);
+                        lds, kclk);
 }
 
 // CUs of the current device (queried once per device; 0 if unknown).
@@ -282,7 +285,7 @@ hipError_t launch_kernel(const Plan& pl, const void* q, const void* k, const voi
   hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kTT), shmem, s, t.start, t.stop, 0, (const T*)q,
                         (const T*)k, (const T*)v, w.kt, w.ct, reinterpret_cast<float2*>(w.stats), w.bvpart, w.bt, w.w,
                         w.x, pl.N, pl.ldc, pl.m, lbmax, pl.ntiles, pl.tpg, pl.groups, pl.jblocks, pl.scale, pl.eps,
-                        pl.ns_iters, nns, gap);
+                        pl.ns_iters, nns, gap, w.nsclk, w.kclk);
   if (KS > 0) w.x_final = w.x;
   return hipGetLastError();
 }

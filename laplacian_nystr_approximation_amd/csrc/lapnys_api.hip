@@ -288,6 +288,14 @@ int forward_impl(const void* q, const void* k, const void* v, float* out, const 
   st = check_buffers(q, k, v, out, pl, ws, ws_bytes);
   if (st != LAPNYS_OK) return st;
   lapnys::Work B = carve(pl, ws);
+  if (dbg && dbg->kernel_clock) {
+    // earliest start (atomic minimum from all ones) and latest end (atomic maximum from zero)
+    if (!ok(hipMemsetAsync(dbg->kernel_clock, 0xff, sizeof(unsigned long long), s), "hipMemsetAsync") ||
+        !ok(hipMemsetAsync(dbg->kernel_clock + 1, 0, sizeof(unsigned long long), s), "hipMemsetAsync"))
+      return LAPNYS_ERR_HIP;
+    B.kclk = dbg->kernel_clock;
+  }
+  if (dbg && dbg->ns_clock && pl.ns_in_launch) B.nsclk = dbg->ns_clock;
   st = run(pl, q, k, v, out, B, ev, s);
   if (st != LAPNYS_OK || !dbg) return st;
   const size_t f = sizeof(float);

@@ -108,6 +108,12 @@ struct Work {
   __bf16* yt;          // m <= 64: Y^T as bf16 high and low parts, [P][2][d][64] (yt_index layout)
   float* x_final;      // the Newton-Schulz result (x or x2), set by launch_ns
   float* bt = nullptr; // if set (Laplacian form only): the kernel-matrix stage also stores B as [P][m][N]
+  // If set (debug form): device wall-clock stamps.  nsclk [P][3]: start, first
+  // step and end of each problem's in-launch solver workgroup; kclk [2]: the
+  // earliest start and latest end over the Laplacian kernel-matrix workgroups
+  // (kclk[0] must hold the largest value and kclk[1] zero on entry).
+  unsigned long long* nsclk = nullptr;
+  unsigned long long* kclk = nullptr;
 };
 
 // Backward-pass buffers, after the forward's workspace (float32; mp = m

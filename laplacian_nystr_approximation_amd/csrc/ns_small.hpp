@@ -94,7 +94,9 @@ __device__ __forceinline__ float wave_max_nonneg(float x) {
 template <int D, int KS>
 __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __restrict__ wout,
                                          float* __restrict__ xout, int m, float scale, float eps, int iters, int p,
-                                         float* __restrict__ lds) {
+                                         float* __restrict__ lds, unsigned long long* __restrict__ clk) {
+  // Debug stamps (clk non-null): start, first step, end, device wall clock.
+  const unsigned long long t_start = clk ? (unsigned long long)wall_clock64() : 0ull;
   constexpr int KLD = D + 4;  // landmark staging stride: 16-byte rows for broadcast reads
   static_assert(kMP * KLD <= kMP * kLD, "landmark staging must fit in one float32 buffer");
   // Float32 layout: X, X^T, (W X)^T.
@@ -280,6 +282,7 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
   else
     store_f32();
   __syncthreads();
+  const unsigned long long t_steps = clk ? (unsigned long long)wall_clock64() : 0ull;
 
   // ---- split steps ----
   int it = 0;
@@ -414,6 +417,11 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
   // X (row-major, float32 layout) to the workspace.
   float* xp = xout + (size_t)p * kMP * kMP;
   for (int e = tid; e < kMP * kMP; e += 256) xp[e] = xf[(e >> 6) * kLD + (e & 63)];
+  if (clk != nullptr && tid == 0) {
+    clk[3 * p + 0] = t_start;
+    clk[3 * p + 1] = t_steps;
+    clk[3 * p + 2] = (unsigned long long)wall_clock64();
+  }
 }
 
 }  // namespace ns_detail

@@ -55,7 +55,7 @@ class lapnys_params(ctypes.Structure):
 
 class lapnys_debug(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in
-                ["landmarks", "C_t", "W", "X", "BV", "Y", "mu", "sigma"]]
+                ["landmarks", "C_t", "W", "X", "BV", "Y", "mu", "sigma", "ns_clock", "kernel_clock"]]
 
 
 DEBUG_FIELDS = [f[0] for f in lapnys_debug._fields_]
@@ -211,9 +211,9 @@ def _sizes_ok(params: lapnys_params, q, k, v, out, dbg=None) -> None:
     need = {"q": (q, in_size, P * N * d), "k": (k, in_size, P * N * d), "v": (v, in_size, P * N * d),
             "out": (out, 4, P * N * d)}
     per = {"landmarks": P * m * d, "C_t": P * m * N, "W": P * m * m, "X": P * m * m, "BV": P * m * d,
-           "Y": P * m * d, "mu": P * m, "sigma": P * m}
+           "Y": P * m * d, "mu": P * m, "sigma": P * m, "ns_clock": P * 3, "kernel_clock": 2}
     for name, t in (dbg or {}).items():
-        need[name] = (t, 4, per[name])
+        need[name] = (t, 8 if name.endswith("_clock") else 4, per[name])
     for name, (t, size, count) in need.items():
         if t is None or isinstance(t, int):
             continue

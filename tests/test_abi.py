@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 def test_struct_layout_matches_header():
     # 7 int32, 2 float, 2 int32, 1 uint32, no padding
     assert ctypes.sizeof(B.lapnys_params) == 12 * 4
-    assert ctypes.sizeof(B.lapnys_debug) == 8 * ctypes.sizeof(ctypes.c_void_p)
+    assert ctypes.sizeof(B.lapnys_debug) == 10 * ctypes.sizeof(ctypes.c_void_p)
 
 
 def test_status_strings():

@@ -48,13 +48,20 @@ constexpr int kLB = 72;  // bf16 LDS row stride (144-byte rows: 16-byte aligned,
 constexpr int kXB = kMP * kLB;  // bf16 elements of one 64 x 64 high or low array
 constexpr int kFp32Steps = 2;   // final steps on float32 products, at least
 constexpr float kSplitGuard = 64.f;  // largest rho = ||W||_1 max|X| for a split step
-// LDS of one problem's schedule (floats).  Split steps: X, X^T and (W X)^T,
-// each as high and low parts, 6 kXB bf16 = 3 kXB floats.  Float32 steps (the
-// same bytes): X, X^T and (W X)^T, 3 kMP kLD floats.  Then 256 partial sums,
-// alpha and ||W||_1.
+// First step after which the guard is evaluated: in exact arithmetic rho is
+// at most 2^(k/2) after k steps, at most 64 up to step 12.
+constexpr int kGuardFrom = 11;
+// LDS of one problem's schedule (floats).  Split steps: X twice (the current
+// iterate and the next) and one per-wavefront slab that holds X^T and then
+// (W X)^T, each as high and low parts, 6 kXB bf16 = 3 kXB floats.  Float32
+// steps (the same bytes): the same three arrays, 3 kMP kLD floats.  Then 256
+// partial sums, alpha and ||W||_1, then W itself (float32, kMP rows of kLD),
+// kept for the whole schedule.
 constexpr int kNsRegion = 3 * kXB;
 static_assert(3 * kMP * kLD <= kNsRegion, "the float32 layout must fit in the split layout's bytes");
-constexpr int kNsLdsFloats = kNsRegion + 260;
+constexpr int kNsWOffset = kNsRegion + 260;
+static_assert(kNsWOffset % 4 == 0, "W must start 16-byte aligned");
+constexpr int kNsLdsFloats = kNsWOffset + kMP * kLD;
 
 // Largest value over the 64 lanes of a wavefront of a non-negative x,
 // returned to every lane: DPP row rotations leave each 16-lane row's
@@ -73,16 +80,20 @@ __device__ __forceinline__ float wave_max_nonneg(float x) {
 }
 
 // In-LDS schedule for m <= 64: one workgroup of four wavefronts per problem,
-// 57 KB of LDS (so it can share a CU with the kernel-matrix stage).
+// 73 KB of LDS (so two fit a CU, as two kernel-matrix workgroups do).
 //
-// Wavefront w owns block row w (rows [16 w, 16 w + 16)) of Q = W X, of
-// S = X Q and of X: each lane holds the 16 entries X[16 w + 4 lk + r]
-// [16 bj + li] (bj, r in [0, 4)) in registers.  A step forms Q's block row
-// (W's rows from registers, X's columns read as rows of X^T), stores it
-// transposed, and after a barrier forms S's block row (X's rows, Q's columns
-// read as rows of Q^T), then writes X_next = 2X - S into both X (row-major)
-// and X^T.  Only wavefront w reads X's block row w, and X^T is read only in
-// the first half of a step, so both are updated in place.
+// Wavefront w owns block column w (columns [16 w, 16 w + 16)) of Q = W X,
+// of S = X Q and of X: each lane holds the 16 entries X[16 bo + 4 lk + r]
+// [16 w + li] (bo, r in [0, 4)) in registers.  A step forms Q's block column
+// (all of W's rows from registers, times X's block column, read from the
+// wavefront's own slab as rows of X^T), puts it into the same slab as rows
+// of Q^T, forms S's block column (all of X's rows, from the shared row-major
+// copy, times Q's block column from the slab), and writes X_next = 2X - S
+// into its slab (as rows of X^T) and into the other row-major copy.  Only
+// the row-major copy is shared between wavefronts, and it alternates between
+// two buffers, so one barrier per step orders everything: a wavefront reads
+// the current copy after every wavefront wrote it, and writes the next copy,
+// which nobody reads until the following barrier.
 //
 // The float32 steps reduce over k in [0, 4 KS), KS = ceil(m / 4), on fp32
 // MFMA 16x16x4; the split steps over k in [0, 32 KB), KB = ceil(m / 32), on
@@ -97,21 +108,14 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
                                          float* __restrict__ lds, unsigned long long* __restrict__ clk) {
   // Debug stamps (clk non-null): start, first step, end, device wall clock.
   const unsigned long long t_start = clk ? (unsigned long long)wall_clock64() : 0ull;
-  constexpr int KLD = D + 4;  // landmark staging stride: 16-byte rows for broadcast reads
-  static_assert(kMP * KLD <= kMP * kLD, "landmark staging must fit in one float32 buffer");
-  // Float32 layout: X, X^T, (W X)^T.
-  float* xf = lds;
-  float* xtf = lds + kMP * kLD;
-  float* qf = lds + 2 * kMP * kLD;
-  // Split layout (same bytes): X, X^T, (W X)^T, each high parts then low parts.
-  __bf16* xb = reinterpret_cast<__bf16*>(lds);
-  __bf16* xtb = xb + 2 * kXB;
-  __bf16* qb = xb + 4 * kXB;
-  // Set-up: W in the float32 (W X)^T buffer, the landmarks in the float32
-  // X^T buffer.  Both are dead once every lane holds its operands in
-  // registers (a barrier before X0 is stored).
-  float* wl = qf;
-  float* kl = xtf;
+  // Float32 layout: the row-major X twice, then the slab array (rows of X^T
+  // or Q^T; wavefront w uses rows [16 w, 16 w + 16)).
+  float* xrf0 = lds;
+  float* tf = lds + 2 * kMP * kLD;
+  // Split layout (same bytes): the same arrays, each high parts then low parts.
+  __bf16* xrb0 = reinterpret_cast<__bf16*>(lds);
+  __bf16* tb = xrb0 + 4 * kXB;
+  float* wl = lds + kNsWOffset;  // W, float32
   float* red = lds + kNsRegion;  // [256] partial column sums, then alpha and ||W||_1
   float& alpha_s = red[256];
   float& norm1_s = red[257];
@@ -120,55 +124,60 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
   // of dependent products is the longer one: its wavefronts take issue
   // priority.
   __builtin_amdgcn_s_setprio(3);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  // Landmark rows into LDS: every load of the (at most 64 x D) block is
-  // issued before the first store, so the staging costs one memory latency.
-  {
-    constexpr int kV = kMP * D / 4 / 256;  // float4 per lane
-    const float4* ktp4 = reinterpret_cast<const float4*>(kt + (size_t)p * m * D);
-    float4 kv[kV];
-#pragma unroll
-    for (int i = 0; i < kV; ++i) {
-      const int e4 = tid + 256 * i;
-      kv[i] = (4 * e4 < m * D) ? ktp4[e4] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int i = 0; i < kV; ++i) {
-      const int e = 4 * (tid + 256 * i);
-      *reinterpret_cast<float4*>(&kl[(e / D) * KLD + (e % D)]) = kv[i];
-    }
-  }
-  __syncthreads();
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const float* ktp = kt + (size_t)p * m * D;
 
   // W = k(K~, K~) + eps I, zero padded.  Lane b holds landmark b in
-  // registers; wavefront w forms rows [16 w, 16 w + 16) four at a time with
-  // the row landmark broadcast from LDS.  Entry (a, b) sums |K~_a - K~_b| over
-  // even and odd features in increasing order, the same sums as entry (b, a),
-  // so W is bit-symmetric.
+  // registers; wavefront w forms rows [16 w, 16 w + 16) four at a time.  The
+  // row landmarks are wave-uniform: they are read with scalar loads into
+  // scalar registers (one wavefront per SIMD issues too slowly to hide LDS
+  // broadcast reads), two 4-feature chunks ahead.  Entry (a, b) sums
+  // |K~_a - K~_b| over even and odd features in increasing order, the same
+  // sums as entry (b, a), so W is bit-symmetric.
   {
+    constexpr int NC = D / 4;  // 4-feature chunks
     const int b = lane;
     float csum = 0.f;  // |W[a][b]| over this wavefront's rows a, in increasing a
     float xb_[D];
+    {
+      const float4* kb4 = reinterpret_cast<const float4*>(ktp + (size_t)min(b, m - 1) * D);
 #pragma unroll
-    for (int t = 0; t < D; ++t) xb_[t] = kl[min(b, m - 1) * KLD + t];
+      for (int c = 0; c < NC; ++c) {
+        const float4 v4 = kb4[c];
+        xb_[4 * c] = v4.x;
+        xb_[4 * c + 1] = v4.y;
+        xb_[4 * c + 2] = v4.z;
+        xb_[4 * c + 3] = v4.w;
+      }
+    }
     for (int a0 = 16 * w; a0 < 16 * w + 16; a0 += 4) {
       if (a0 < m) {
         float s0[4] = {0.f, 0.f, 0.f, 0.f}, s1[4] = {0.f, 0.f, 0.f, 0.f};
         const float* ka[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) ka[u] = kl + min(a0 + u, m - 1) * KLD;
+        for (int u = 0; u < 4; ++u) ka[u] = ktp + (size_t)min(a0 + u, m - 1) * D;
+        float4 kv[3][4];  // ring of three chunks: the current one and the next two
 #pragma unroll
-        for (int t = 0; t < D; t += 4) {
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) kv[c][u] = *reinterpret_cast<const float4*>(ka[u] + 4 * c);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          if (c + 2 < NC) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) kv[(c + 2) % 3][u] = *reinterpret_cast<const float4*>(ka[u] + 4 * (c + 2));
+          }
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const float4 r = *reinterpret_cast<const float4*>(ka[u] + t);
-            s0[u] += fabsf(r.x - xb_[t]);
-            s1[u] += fabsf(r.y - xb_[t + 1]);
-            s0[u] += fabsf(r.z - xb_[t + 2]);
-            s1[u] += fabsf(r.w - xb_[t + 3]);
+            const float4 r = kv[c % 3][u];
+            s0[u] += fabsf(r.x - xb_[4 * c]);
+            s1[u] += fabsf(r.y - xb_[4 * c + 1]);
+            s0[u] += fabsf(r.z - xb_[4 * c + 2]);
+            s1[u] += fabsf(r.w - xb_[4 * c + 3]);
           }
-          // The sums are in/out operands here: each 4-feature chunk's row
-          // values are read just before use (bounded registers).
+          // The sums are in/out operands here, so the loads of a chunk stay
+          // two chunks ahead of its arithmetic (bounded registers).
           asm volatile("" : "+v"(s0[0]), "+v"(s0[1]), "+v"(s0[2]), "+v"(s0[3]), "+v"(s1[0]), "+v"(s1[1]),
                        "+v"(s1[2]), "+v"(s1[3])::"memory");
         }
@@ -195,7 +204,7 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
   // alpha = ||W||_1 ||W||_inf.  W is symmetric, so its largest absolute
   // column sum (the 1-norm) is also its largest row sum (the inf-norm):
   // alpha = (max_b sum_a |W[a][b]|)^2, the column sums merged from the four
-  // wavefronts' partial sums in wavefront order.  W goes out to the
+  // wavefront's partial sums in wavefront order.  W goes out to the
   // workspace.
   float* wp = wout + (size_t)p * kMP * kMP;
   for (int e = tid; e < kMP * kMP; e += 256) wp[e] = wl[(e >> 6) * kLD + (e & 63)];
@@ -211,211 +220,251 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
   __syncthreads();
 
   const int li = lane & 15, lk = lane >> 4;
-  // W's A operands for every step of Q = W X, block row w.  fp32 MFMA
-  // 16x16x4: A[li][lk] of step s = W[16 w + li][4 s + lk], KS = ceil(m / 4)
-  // steps (a template parameter, so the step loops unroll without branches).
-  // bf16 MFMA 16x16x32: A[li][8 lk + e] of step kb = W[16 w + li][32 kb +
-  // 8 lk + e], KB = ceil(m / 32) steps, as high and low parts.
-  constexpr int KB = (4 * KS + 31) / 32;
-  float wreg[KS];
-#pragma unroll
-  for (int st = 0; st < KS; ++st) wreg[st] = wl[(16 * w + li) * kLD + 4 * st + lk];
-  u32x4 wh[KB], wlo[KB];
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float* wr = wl + (16 * w + li) * kLD + 32 * kb + 8 * lk + 2 * i;
-      uint32_t h, l;
-      split2(wr[0], wr[1], h, l);
-      wh[kb][i] = h;
-      wlo[kb][i] = l;
-    }
-
-  // X0 = W^T / alpha.  xr[bj][r] = X[16 w + 4 lk + r][16 bj + li], the
-  // entries this lane produces in every step.
   const int n16 = iters > kFp32Steps ? iters - kFp32Steps : 0;
-  const float alpha = alpha_s, norm1 = norm1_s;
+  // W's A operands for the split steps, every row block: bf16 MFMA 16x16x32,
+  // A[li][8 lk + e] of step kb for row block bi = W[16 bi + li][32 kb + 8 lk
+  // + e], KB = ceil(m / 32) steps, as high and low parts.
+  constexpr int KB = (4 * KS + 31) / 32;
+  u32x4 wh[4][KB], wlo[4][KB];
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float* wr = wl + (16 * bi + li) * kLD + 32 * kb + 8 * lk + 2 * i;
+        uint32_t h, l;
+        split2(wr[0], wr[1], h, l);
+        wh[bi][kb][i] = h;
+        wlo[bi][kb][i] = l;
+      }
+
+  // X0 = W^T / alpha (times the float32 reciprocal of alpha).  xr[bo][r] =
+  // X[16 bo + 4 lk + r][16 w + li], the entries this lane produces in every
+  // step.
+  const float ralpha = 1.f / alpha_s, norm1 = norm1_s;
   float xr[4][4];
 #pragma unroll
-  for (int bj = 0; bj < 4; ++bj)
+  for (int bo = 0; bo < 4; ++bo)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) xr[bj][r] = wl[(16 * bj + li) * kLD + 16 * w + 4 * lk + r] / alpha;
-  __syncthreads();  // every lane has read W and the landmarks: their buffers are free
+    for (int r = 0; r < 4; ++r) xr[bo][r] = wl[(16 * w + li) * kLD + 16 * bo + 4 * lk + r] * ralpha;
+  __syncthreads();  // X0 read before the stores below (W stays in place)
 
-  const int i0 = 16 * w + 4 * lk;  // first row of this lane's entries
-  // This lane's entries of X into the split layout: row-major X (four
-  // 16-bit stores per part) and X^T (four consecutive entries of row
-  // 16 bj + li, one 8-byte store per part).
-  auto store_split = [&]() {
-    uint16_t* xh16 = reinterpret_cast<uint16_t*>(xb);
+  const int jc = 16 * w + li;  // the column of X this lane holds (a row of X^T)
+  // This lane's entries of X into the split layout: row-major copy `buf`
+  // (four 16-bit stores per part and row block) and the slab (four
+  // consecutive entries of row jc of X^T, one 8-byte store per part).
+  auto store_split = [&](int buf) {
+    uint16_t* xh16 = reinterpret_cast<uint16_t*>(xrb0 + buf * 2 * kXB);
     uint16_t* xl16 = xh16 + kXB;
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj) {
+    for (int bo = 0; bo < 4; ++bo) {
       uint32_t h0, l0, h1, l1;
-      split2(xr[bj][0], xr[bj][1], h0, l0);
-      split2(xr[bj][2], xr[bj][3], h1, l1);
-      const int j = 16 * bj + li;
+      split2(xr[bo][0], xr[bo][1], h0, l0);
+      split2(xr[bo][2], xr[bo][3], h1, l1);
+      const int i0 = 16 * bo + 4 * lk;
       const uint32_t hw[4] = {h0 & 0xffffu, h0 >> 16, h1 & 0xffffu, h1 >> 16};
       const uint32_t lw[4] = {l0 & 0xffffu, l0 >> 16, l1 & 0xffffu, l1 >> 16};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        xh16[(i0 + r) * kLB + j] = (uint16_t)hw[r];
-        xl16[(i0 + r) * kLB + j] = (uint16_t)lw[r];
+        xh16[(i0 + r) * kLB + jc] = (uint16_t)hw[r];
+        xl16[(i0 + r) * kLB + jc] = (uint16_t)lw[r];
       }
-      *reinterpret_cast<uint2*>(xtb + j * kLB + i0) = make_uint2(h0, h1);
-      *reinterpret_cast<uint2*>(xtb + kXB + j * kLB + i0) = make_uint2(l0, l1);
+      *reinterpret_cast<uint2*>(tb + jc * kLB + i0) = make_uint2(h0, h1);
+      *reinterpret_cast<uint2*>(tb + kXB + jc * kLB + i0) = make_uint2(l0, l1);
     }
   };
   // The same entries into the float32 layout.
-  auto store_f32 = [&]() {
+  auto store_f32 = [&](int buf) {
+    float* xrf = xrf0 + buf * kMP * kLD;
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj) {
-      const int j = 16 * bj + li;
+    for (int bo = 0; bo < 4; ++bo) {
+      const int i0 = 16 * bo + 4 * lk;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) xf[(i0 + r) * kLD + j] = xr[bj][r];
-      *reinterpret_cast<float4*>(&xtf[j * kLD + i0]) = make_float4(xr[bj][0], xr[bj][1], xr[bj][2], xr[bj][3]);
+      for (int r = 0; r < 4; ++r) xrf[(i0 + r) * kLD + jc] = xr[bo][r];
+      *reinterpret_cast<float4*>(&tf[jc * kLD + i0]) = make_float4(xr[bo][0], xr[bo][1], xr[bo][2], xr[bo][3]);
     }
   };
   if (n16 > 0)
-    store_split();
+    store_split(0);
   else
-    store_f32();
+    store_f32(0);
   __syncthreads();
   const unsigned long long t_steps = clk ? (unsigned long long)wall_clock64() : 0ull;
 
   // ---- split steps ----
-  int it = 0;
+  int it = 0, cur = 0;
   while (it < n16) {
-    // Q = W X, block row w, stored transposed: Q^T[j][i] = Q[i][j].  The B
-    // operand X[32 kb + 8 lk + e][16 bj + li] is row 16 bj + li of X^T.
+    // Q[:, w] = W X[:, w].  B operand X[32 kb + 8 lk + e][jc] = row jc of X^T
+    // in the slab.  Operand loads are issued before the first product.
+    f32x4 acc[4];
     {
-      f32x4 acc[4];
+      bf16x8 bh[KB], bl[KB];
 #pragma unroll
-      for (int bj = 0; bj < 4; ++bj) acc[bj] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < KB; ++kb) {
+        const int o = jc * kLB + 32 * kb + 8 * lk;
+        bh[kb] = *reinterpret_cast<const bf16x8*>(tb + o);
+        bl[kb] = *reinterpret_cast<const bf16x8*>(tb + kXB + o);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) acc[bi] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-        for (int bj = 0; bj < 4; ++bj) {
-          const int o = (16 * bj + li) * kLB + 32 * kb + 8 * lk;
-          const bf16x8 bh = *reinterpret_cast<const bf16x8*>(xtb + o);
-          const bf16x8 bl = *reinterpret_cast<const bf16x8*>(xtb + kXB + o);
-          acc[bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wlo[kb]), bh, acc[bj], 0, 0, 0);
-          acc[bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wh[kb]), bl, acc[bj], 0, 0, 0);
-          acc[bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wh[kb]), bh, acc[bj], 0, 0, 0);
-        }
-      }
-      // acc[bj][r] = Q[16 w + 4 lk + r][16 bj + li]: four consecutive entries
-      // of row 16 bj + li of Q^T.
+        for (int bi = 0; bi < 4; ++bi)
+          acc[bi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wlo[bi][kb]), bh[kb], acc[bi], 0, 0, 0);
 #pragma unroll
-      for (int bj = 0; bj < 4; ++bj) {
-        uint32_t h0, l0, h1, l1;
-        split2(acc[bj][0], acc[bj][1], h0, l0);
-        split2(acc[bj][2], acc[bj][3], h1, l1);
-        const int o = (16 * bj + li) * kLB + i0;
-        *reinterpret_cast<uint2*>(qb + o) = make_uint2(h0, h1);
-        *reinterpret_cast<uint2*>(qb + kXB + o) = make_uint2(l0, l1);
+        for (int bi = 0; bi < 4; ++bi)
+          acc[bi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wh[bi][kb]), bl[kb], acc[bi], 0, 0, 0);
+#pragma unroll
+        for (int bi = 0; bi < 4; ++bi)
+          acc[bi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wh[bi][kb]), bh[kb], acc[bi], 0, 0, 0);
       }
     }
-    __syncthreads();
-    // S = X Q, block row w; X_next = 2 X - S.
-    {
-      f32x4 acc[4];
+    // acc[bi][r] = Q[16 bi + 4 lk + r][jc]: four consecutive entries of row
+    // jc of Q^T, into the slab over X^T (already read above; the products
+    // these stores depend on consumed it).
 #pragma unroll
-      for (int bj = 0; bj < 4; ++bj) acc[bj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int bi = 0; bi < 4; ++bi) {
+      uint32_t h0, l0, h1, l1;
+      split2(acc[bi][0], acc[bi][1], h0, l0);
+      split2(acc[bi][2], acc[bi][3], h1, l1);
+      const int o = jc * kLB + 16 * bi + 4 * lk;
+      *reinterpret_cast<uint2*>(tb + o) = make_uint2(h0, h1);
+      *reinterpret_cast<uint2*>(tb + kXB + o) = make_uint2(l0, l1);
+    }
+    // S[:, w] = X Q[:, w]: A operand X[16 bo + li][32 kb + 8 lk + e] from the
+    // current row-major copy (every wavefront's, written before the last
+    // barrier), B operand Q[32 kb + 8 lk + e][jc] from the slab (this
+    // wavefront's own stores above, earlier in its LDS order).
+    {
+      const __bf16* xh = xrb0 + cur * 2 * kXB;
+      bf16x8 ah[4][KB], al[4][KB], qh[KB], ql[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const int oa = (16 * w + li) * kLB + 32 * kb + 8 * lk;  // X[16 w + li][32 kb + 8 lk + e]
-        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(xb + oa);
-        const bf16x8 al = *reinterpret_cast<const bf16x8*>(xb + kXB + oa);
+        const int ob = jc * kLB + 32 * kb + 8 * lk;
+        qh[kb] = *reinterpret_cast<const bf16x8*>(tb + ob);
+        ql[kb] = *reinterpret_cast<const bf16x8*>(tb + kXB + ob);
 #pragma unroll
-        for (int bj = 0; bj < 4; ++bj) {
-          const int ob = (16 * bj + li) * kLB + 32 * kb + 8 * lk;  // Q[32 kb + 8 lk + e][16 bj + li]
-          const bf16x8 qh = *reinterpret_cast<const bf16x8*>(qb + ob);
-          const bf16x8 ql = *reinterpret_cast<const bf16x8*>(qb + kXB + ob);
-          acc[bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, qh, acc[bj], 0, 0, 0);
-          acc[bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, ql, acc[bj], 0, 0, 0);
-          acc[bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, qh, acc[bj], 0, 0, 0);
+        for (int bo = 0; bo < 4; ++bo) {
+          const int oa = (16 * bo + li) * kLB + 32 * kb + 8 * lk;
+          ah[bo][kb] = *reinterpret_cast<const bf16x8*>(xh + oa);
+          al[bo][kb] = *reinterpret_cast<const bf16x8*>(xh + kXB + oa);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int bo = 0; bo < 4; ++bo) acc[bo] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int bo = 0; bo < 4; ++bo) acc[bo] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[bo][kb], qh[kb], acc[bo], 0, 0, 0);
+#pragma unroll
+        for (int bo = 0; bo < 4; ++bo) acc[bo] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[bo][kb], ql[kb], acc[bo], 0, 0, 0);
+#pragma unroll
+        for (int bo = 0; bo < 4; ++bo) acc[bo] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[bo][kb], qh[kb], acc[bo], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int bo = 0; bo < 4; ++bo)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) xr[bo][r] = 2.f * xr[bo][r] - acc[bo][r];
+    // X_next into the other row-major copy (last read before the previous
+    // barrier) and into the slab over Q^T (consumed above).
+    store_split(cur ^ 1);
+    if (it >= kGuardFrom) {
       float amax = 0.f;
 #pragma unroll
-      for (int bj = 0; bj < 4; ++bj)
+      for (int bo = 0; bo < 4; ++bo)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          xr[bj][r] = 2.f * xr[bj][r] - acc[bj][r];
-          amax = fmaxf(amax, fabsf(xr[bj][r]));
-        }
-      // X's block row w is read by this wavefront only, and its reads above
-      // feed the products these stores depend on; X^T is not read in this
-      // half of the step.
-      store_split();
+        for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(xr[bo][r]));
       amax = wave_max_nonneg(amax);
       if (lane == 0) red[w] = amax;
     }
     __syncthreads();
-    ++it;
+    cur ^= 1;
     // The guard: the same four values in every wavefront, so the decision
-    // is uniform across the workgroup.  red[0..3] is next written after the
-    // next step's first barrier, which every wavefront passes after this read.
-    const float4 mx = *reinterpret_cast<const float4*>(red);
-    if (norm1 * fmaxf(fmaxf(mx.x, mx.y), fmaxf(mx.z, mx.w)) > kSplitGuard) break;
-  }
-  if (n16 > 0) {
-    // Into the float32 layout for the remaining steps (at least kFp32Steps),
-    // from the registers.  The split buffers are dead: every wavefront passed
-    // the last split step's barrier.
-    store_f32();
-    __syncthreads();
+    // is uniform across the workgroup.  red[0..3] is next written after
+    // every wavefront has passed the next barrier, and so this read.
+    if (it >= kGuardFrom) {
+      const float4 mx = *reinterpret_cast<const float4*>(red);
+      if (norm1 * fmaxf(fmaxf(mx.x, mx.y), fmaxf(mx.z, mx.w)) > kSplitGuard) {
+        ++it;
+        break;
+      }
+    }
+    ++it;
   }
 
-  // ---- float32 steps ----
-  for (; it < iters; ++it) {
-    // Q = W X, block row w, stored transposed: qf[j][i] = Q[i][j].  B operand
-    // X[4 st + lk][16 bj + li] = X^T[16 bj + li][4 st + lk].
-    {
+  // ---- float32 steps (n16 < iters whenever iters > 0, so at least kFp32Steps
+  // of them follow the split steps) ----
+  if (it < iters) {
+    if (n16 > 0) {
+      // Into the float32 layout, from the registers.  The split buffers are
+      // dead: every wavefront passed the last split step's barrier.
+      store_f32(0);
+      cur = 0;
+      __syncthreads();
+    }
+    // W's A operands for the float32 steps, every row block: fp32 MFMA
+    // 16x16x4, A[li][lk] of step st for row block bi = W[16 bi + li][4 st + lk].
+    float wreg[4][KS];
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+      for (int st = 0; st < KS; ++st) wreg[bi][st] = wl[(16 * bi + li) * kLD + 4 * st + lk];
+    for (; it < iters; ++it) {
       f32x4 acc[4];
+      {
+        // Q[:, w] = W X[:, w]; B operand X[4 st + lk][jc] = slab row jc.
+        float xv[KS];
 #pragma unroll
-      for (int bj = 0; bj < 4; ++bj) acc[bj] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int st = 0; st < KS; ++st) xv[st] = tf[jc * kLD + 4 * st + lk];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int st = 0; st < KS; ++st) {
+        for (int bi = 0; bi < 4; ++bi) acc[bi] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int bj = 0; bj < 4; ++bj) {
-          const float xv = xtf[(16 * bj + li) * kLD + 4 * st + lk];
-          acc[bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(wreg[st], xv, acc[bj], 0, 0, 0);
-        }
+        for (int st = 0; st < KS; ++st)
+#pragma unroll
+          for (int bi = 0; bi < 4; ++bi) acc[bi] = __builtin_amdgcn_mfma_f32_16x16x4f32(wreg[bi][st], xv[st], acc[bi], 0, 0, 0);
       }
 #pragma unroll
-      for (int bj = 0; bj < 4; ++bj)
-        *reinterpret_cast<float4*>(&qf[(16 * bj + li) * kLD + i0]) =
-            make_float4(acc[bj][0], acc[bj][1], acc[bj][2], acc[bj][3]);
-    }
-    __syncthreads();
-    // S = X Q, block row w; X_next = 2 X - S into X and X^T.
-    {
-      f32x4 acc[4];
+      for (int bi = 0; bi < 4; ++bi)
+        *reinterpret_cast<float4*>(&tf[jc * kLD + 16 * bi + 4 * lk]) =
+            make_float4(acc[bi][0], acc[bi][1], acc[bi][2], acc[bi][3]);
+      {
+        // S[:, w] = X Q[:, w]: A operand X[16 bo + li][4 st + lk] from the
+        // current row-major copy, B operand Q[4 st + lk][jc] from the slab.
+        const float* xrf = xrf0 + cur * kMP * kLD;
+        float xa[4][KS], qv[KS];
 #pragma unroll
-      for (int bj = 0; bj < 4; ++bj) acc[bj] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int st = 0; st < KS; ++st) {
+          qv[st] = tf[jc * kLD + 4 * st + lk];
 #pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        const float xa = xf[(16 * w + li) * kLD + 4 * st + lk];  // X[16 w + li][4 st + lk]
-#pragma unroll
-        for (int bj = 0; bj < 4; ++bj) {
-          const float qv = qf[(16 * bj + li) * kLD + 4 * st + lk];  // Q[4 st + lk][16 bj + li]
-          acc[bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa, qv, acc[bj], 0, 0, 0);
+          for (int bo = 0; bo < 4; ++bo) xa[bo][st] = xrf[(16 * bo + li) * kLD + 4 * st + lk];
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int bo = 0; bo < 4; ++bo) acc[bo] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < KS; ++st)
+#pragma unroll
+          for (int bo = 0; bo < 4; ++bo) acc[bo] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[bo][st], qv[st], acc[bo], 0, 0, 0);
       }
 #pragma unroll
-      for (int bj = 0; bj < 4; ++bj)
+      for (int bo = 0; bo < 4; ++bo)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) xr[bj][r] = 2.f * xr[bj][r] - acc[bj][r];
-      store_f32();
+        for (int r = 0; r < 4; ++r) xr[bo][r] = 2.f * xr[bo][r] - acc[bo][r];
+      store_f32(cur ^ 1);
+      __syncthreads();
+      cur ^= 1;
     }
-    __syncthreads();
   }
 
-  // X (row-major, float32 layout) to the workspace.
+  // X (row-major, float32 layout, copy cur) to the workspace.
   float* xp = xout + (size_t)p * kMP * kMP;
+  const float* xf = xrf0 + cur * kMP * kLD;
   for (int e = tid; e < kMP * kMP; e += 256) xp[e] = xf[(e >> 6) * kLD + (e & 63)];
   if (clk != nullptr && tid == 0) {
     clk[3 * p + 0] = t_start;

@@ -124,28 +124,34 @@ def cpu_model() -> str:
 def cpu_baseline(w, x, budget_s: float):
     """The oracle as it stands over the workload's (batch, head) problems on a
     process pool of one single-threaded worker per available host core (at
-    most 16, the host share of one GPU), in whole rounds over all problems
-    until about budget_s seconds of CPU work are done; scaled to tokens/s.
-    Runs before the GPU is touched (the workers are forked)."""
+    most 16, the host share of one GPU): problems are handed out in order,
+    cycling over the workload as repeated forwards do, until about budget_s
+    seconds of CPU work are done (at least one per worker); scaled to
+    tokens/s over the completed problems.  Runs before the GPU is touched (the workers are forked)."""
     import multiprocessing as mp
     cores = max(1, min(len(os.sched_getaffinity(0)), 16))
     _CPU_JOB.update(w=w, x=x)
     ctx = mp.get_context("fork")
+    done = 0
     with ctx.Pool(cores, initializer=_cpu_worker_init) as pool:
-        rounds = 0
         t0 = time.perf_counter()
-        while True:
-            pool.map(_cpu_problem, range(w.P), chunksize=1)
-            rounds += 1
+        pending = [pool.apply_async(_cpu_problem, (i % w.P,)) for i in range(cores)]
+        issued = len(pending)
+        while pending:
+            pending.pop(0).get()
+            done += 1
             el = time.perf_counter() - t0
-            if el * min(cores, w.P) >= budget_s or rounds >= 1000:
-                break
+            # CPU work so far ~ elapsed x busy workers; keep handing out problems until the budget
+            if el * cores < budget_s and issued < 1000 * cores:
+                pending.append(pool.apply_async(_cpu_problem, (issued % w.P,)))
+                issued += 1
+        el = time.perf_counter() - t0
     _CPU_JOB.clear()
-    return {"value": rounds * w.P * w.N / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": done * w.N / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "cpu_model": cpu_model(),
-            "sample": f"{rounds} round(s) over all {w.P} (batch, head) problems of the same workload "
-                      f"(N={w.N} tokens each), float64 numpy, {cores} worker processes of one thread each "
-                      f"(one problem per task), {el:.2f} s wall"}
+            "sample": f"{done} (batch, head) problems of the same workload, handed out in order over its {w.P} "
+                      f"(N={w.N} tokens each), float64 numpy, {cores} worker processes of one thread "
+                      f"each, {el:.2f} s wall"}
 
 
 def wall_clock_hz() -> float:
@@ -475,6 +481,11 @@ def main(argv=None):
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the bench line: warm and cold single-call times and peak memory over the "
                          "length sweep at m = 256 and the headline workload")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="one bench line per configuration (the five forward workloads, the headline workload and "
+                         "the length-sweep points), the oracle legs first")
+    ap.add_argument("--fill-baseline", default=None,
+                    help="rewrite BASELINE.md section 4 from the bench lines in this file (no GPU)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="after the measurements, run a plain float32 copy kernel of this many MiB three times "
                          "(the known-size reference for HBM traffic counters)")
@@ -491,15 +502,46 @@ def main(argv=None):
         print(f"bench.py measures one GPU: this forward has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         return 2
-    w = WORKLOADS[args.workload]
-    if args.kernel != "laplacian" or args.solver != "ns":
-        import dataclasses
-        w = dataclasses.replace(w, kernel=args.kernel, solver=args.solver)
-    x = make_inputs(w)
+    if args.fill_baseline:
+        return fill_baseline_main(args)
+    if args.all_configs:
+        names = ALL_CONFIGS
+    else:
+        names = [args.workload]
+    ws_ = []
+    for name in names:
+        w = WORKLOADS[name]
+        if args.kernel != "laplacian" or args.solver != "ns":
+            import dataclasses
+            w = dataclasses.replace(w, kernel=args.kernel, solver=args.solver)
+        ws_.append(w)
+    inputs = [make_inputs(w) for w in ws_]
+    # The CPU legs run before the GPU is touched (their workers are forked).
+    cpus = [cpu_baseline(w, x, args.cpu_budget) if args.cpu_budget > 0 else None for w, x in zip(ws_, inputs)]
+    for w, x, cpu in zip(ws_, inputs, cpus):
+        line = gpu_line(w, x, cpu, args)
+        print(json.dumps(line), flush=True)
+    return 0
 
-    # The CPU leg runs before the GPU is touched.
-    cpu = cpu_baseline(w, x, args.cpu_budget) if args.cpu_budget > 0 else None
 
+PRECISION = ("float32 values throughout (bf16 inputs widen exactly); L1 distances, exp, W and whitening statistics "
+             "on the float32 vector ALU (statistics merged in float64, landmarks summed in float64); B V, Z Y and "
+             "the Newton-Schulz steps for m <= 64 (all but the last two) on bf16 MFMA with every float32 operand "
+             "split into bf16 high and low parts, three partial products accumulated in float32; Y = X (B V), the "
+             "last Newton-Schulz steps and the m > 64 solver on fp32 MFMA")
+
+# The configurations the bench lines cover: the five forward workloads, the
+# headline workload (the 56x56 shape with bf16 inputs) and the two smaller
+# points of the length sweep at 256 landmarks.
+ALL_CONFIGS = ["tiny_f32", "stage1_56x56_f32", "stage2_28x28_bf16", "stage3_14x14_bf16", "long_256x256_bf16",
+               HEADLINE, "sweep_64x64_bf16", "sweep_128x128_bf16"]
+CLOCK_WARMUP_S = 0.03  # the GPU reaches its steady clock after ~15 ms of sustained work
+
+
+def gpu_line(w, x, cpu, args):
+    """One bench line for workload w: warm-up, exactly K timed steps, the
+    kernel-matrix kernel's duration from its dispatch timestamps, a per-stage
+    breakdown, the in-launch solver's stamps."""
     import torch
 
     import laplacian_nystr_approximation_amd as L
@@ -521,6 +563,16 @@ def main(argv=None):
     per_step = 2 * LAPNYS_NUM_STAGES
     kern = 2 * LAPNYS_STAGE_KERNEL
 
+    # Clock warm-up (untimed, before the W warm-up steps): forward calls until
+    # CLOCK_WARMUP_S of wall time have passed, so the timed steps run at the
+    # GPU's steady clock whatever W is.
+    clock_steps = 0
+    tw = time.perf_counter()
+    while time.perf_counter() - tw < CLOCK_WARMUP_S:
+        for _ in range(8):
+            L.lapnys_forward_ws(q, k, v, out, params, ws, stream)
+        clock_steps += 8
+        torch.cuda.synchronize()
     for _ in range(W):
         L.lapnys_forward_ws(q, k, v, out, params, ws, stream)
     torch.cuda.synchronize()
@@ -565,6 +617,14 @@ def main(argv=None):
         # events around the launch, give its time.
         solver = solver_timing(w, L, q, k, v, out, params, ws, dev)
         stage_ms.pop("ns", None)
+    elif w.solver == "ns":
+        # The solver's own launches on the side stream: the stage span.
+        flops = 4.0 * (((w.m + 63) // 64) * 64) ** 3 * w.ns_iters * w.P
+        solver = {"source": "events at the first and last solver launch (side stream)", "stage_ms": stage_ms["ns"],
+                  "padded_mfma_flops": flops,
+                  "chip_wide_mfma_frac": flops / (stage_ms["ns"] * 1e-3) / MFMA_F32_FLOPS,
+                  "algorithmic_mfma_frac": 4.0 * w.m ** 3 * w.ns_iters * w.P / (stage_ms["ns"] * 1e-3)
+                                           / MFMA_F32_FLOPS}
 
     # Same work without any stage events.
     torch.cuda.synchronize()
@@ -601,6 +661,8 @@ def main(argv=None):
     else:
         variant = (", Gaussian kernel" if gauss else "") + (", CG solver" if w.solver == "cg" else "")
         metric = f"attention tokens/s ({w.name}{variant})"
+    # Z Y in the output stage: 2 N m d flops per problem (run as three bf16 products)
+    zy_flops = 2.0 * w.N * w.m * w.d * w.P
     line = {
         "metric": metric,
         "value": tokens / (ms_step * 1e-3),
@@ -608,11 +670,13 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
+        "clock_warmup_steps": clock_steps,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32+bf16x3",
+        "precision": PRECISION,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "grid": [w.grid_h, w.grid_w], "N": w.N, "d": w.d,
                    "pool": w.pool, "m": w.m, "input_dtype": w.dtype, "lambda": w.lam, "eps": w.eps,
@@ -622,11 +686,55 @@ def main(argv=None):
         "stage_ms": stage_ms,
         "solver": solver,
         "stage_roofline": stage_rooflines(w, stage_ms),
+        "output_zy_mfma": {"flops": zy_flops, "ms": stage_ms["output"],
+                           "frac_of_fp32_mfma_peak": zy_flops / (stage_ms["output"] * 1e-3) / MFMA_F32_FLOPS,
+                           "note": "algorithmic flops of Z Y over the whole output stage time (HBM-bound stage)"},
         "ms_per_step_without_events": plain_ms,
     }
     if gauss:
         line["kernel_values"] = kernel_value_comparison(w, q, k, v, dev)
-    print(json.dumps(line), flush=True)
+    del q, k, v, out, ws
+    torch.cuda.empty_cache()
+    return line
+
+
+def fill_baseline_main(args):
+    """Rewrite the benchmark spec section 4 from the bench lines recorded in a file
+    (lines starting with '{'), one table row per workload."""
+    rows = []
+    with open(args.fill_baseline) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("{"):
+                rows.append(json.loads(line))
+    out = ["## 4. Results", "",
+           f"Filled by `python bench.py --fill-baseline {os.path.relpath(args.fill_baseline, ROOT)}` from the bench "
+           "lines recorded there (one MI355X, `python bench.py --all-configs`); no value is entered by hand.", "",
+           "| Workload | P | N | m | tokens/s (GPU) | ms per forward | L1+exp VALU frac | NS MFMA frac | "
+           "pool / output HBM frac | oracle tokens/s (cores) |",
+           "|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        c = r["config"]
+        sol = r.get("solver") or {}
+        if "mfma_frac_per_occupied_cu" in sol:
+            ns = f"{sol['mfma_frac_per_occupied_cu']:.2f} per occupied CU ({sol['per_problem_us_mean']:.0f} us per problem)"
+        elif "algorithmic_mfma_frac" in sol:
+            ns = f"{sol['algorithmic_mfma_frac']:.3f} chip-wide ({sol['stage_ms'] * 1e3:.0f} us stage)"
+        else:
+            ns = "-"
+        sr = r.get("stage_roofline", {})
+        hbm = f"{sr['pool']['frac']:.2f} / {sr['output']['frac']:.2f}" if "pool" in sr else "-"
+        cpu = r.get("cpu_baseline") or {}
+        cpus = f"{cpu['value']:.3g} ({cpu['cores']})" if cpu else "-"
+        out.append(f"| `{c['workload']}` | {c['B'] * c['H']} | {c['N']} | {c['m']} | {r['value']:.3g} | "
+                   f"{r['ms_per_step']:.4f} | {r['roofline']['frac']:.2f} | {ns} | {hbm} | {cpus} |")
+    out.append("")
+    path = os.path.join(ROOT, "BASELINE.md")
+    text = open(path).read()
+    i = text.index("## 4. Results")
+    with open(path, "w") as f:
+        f.write(text[:i] + "\n".join(out))
+    print("\n".join(out))
     return 0
 
 

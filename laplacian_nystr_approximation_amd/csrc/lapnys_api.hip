@@ -133,6 +133,8 @@ int make_plan(const lapnys_params* p, Plan* pl) {
   P.off_rs = take(Pn * P.m * f);
   P.off_y = take(Pn * P.m * P.d * f);
   P.off_yt = take(P.fused_ns ? Pn * 2 * P.d * 64 * sizeof(uint16_t) : 0);
+  // m > 64 Newton-Schulz steps: X^T of two iterates.
+  P.off_xt = take(!P.fused_ns && !P.cg ? 2 * Pn * P.mp * P.mp * f : 0);
   P.total = off;
   return LAPNYS_OK;
 }
@@ -174,6 +176,7 @@ lapnys::Work carve(const Plan& pl, void* ws) {
   W.rs = (float*)(b + pl.off_rs);
   W.y = (float*)(b + pl.off_y);
   W.yt = (__bf16*)(b + pl.off_yt);
+  W.xt = (float*)(b + pl.off_xt);
   W.x_final = W.x;
   return W;
 }
@@ -181,7 +184,7 @@ lapnys::Work carve(const Plan& pl, void* ws) {
 // Per-device side stream and the fork/join events, created on first use.
 struct DeviceCtx {
   hipStream_t side = nullptr;
-  hipEvent_t fork = nullptr, pooled = nullptr, join = nullptr;
+  hipEvent_t pooled = nullptr, join = nullptr;
 };
 std::mutex g_ctx_mu;  // also serialises the fork/join sequence of concurrent callers
 std::vector<DeviceCtx> g_ctx;
@@ -199,8 +202,7 @@ int device_ctx(DeviceCtx** out) {
     // The fork/join events order work between two streams of one device: a
     // device-scope release is all they need (no host-visible write-back).
     const unsigned flags = hipEventDisableTiming | hipEventReleaseToDevice;
-    if (!ok(hipEventCreateWithFlags(&c.fork, flags), "hipEventCreateWithFlags") ||
-        !ok(hipEventCreateWithFlags(&c.join, flags), "hipEventCreateWithFlags") ||
+    if (!ok(hipEventCreateWithFlags(&c.join, flags), "hipEventCreateWithFlags") ||
         !ok(hipEventCreateWithFlags(&c.pooled, flags), "hipEventCreateWithFlags"))
       return LAPNYS_ERR_HIP;
   }
@@ -240,22 +242,22 @@ int run(const Plan& pl, const void* q, const void* k, const void* v, float* out,
   }
 
   // Otherwise (m > 64, the Gaussian form, the plain steps, CG): the solver's
-  // launches run on a library-owned stream beside the kernel-matrix stage.  The pool stage runs
-  // on that stream ahead of them and the caller's stream waits for it, so the
-  // solver is dispatched first.
+  // launches run on a library-owned stream beside the kernel-matrix stage,
+  // forked from the caller's stream after the pool stage and joined before
+  // the stages that read the solver's result.  Each stream waits only on an
+  // event recorded last on the other stream before the wait is issued (the
+  // runtime may resolve a wait on an event recorded earlier than the other
+  // stream's latest work no sooner than that latest work).
   std::lock_guard<std::mutex> lock(g_ctx_mu);
   DeviceCtx* dc = nullptr;
   const int st = device_ctx(&dc);
   if (st != LAPNYS_OK) return st;
   hipStream_t side = dc->side;
-  // fork: everything before this call on the caller's stream precedes the side stream's work
-  if (!ok(hipEventRecord(dc->fork, s), "hipEventRecord") || !ok(hipStreamWaitEvent(side, dc->fork, 0), "hipStreamWaitEvent"))
+  if (!ok(lapnys::launch_pool(pl, k, W, s, span(LAPNYS_STAGE_POOL)), "pool launch")) return LAPNYS_ERR_HIP;
+  if (!ok(hipEventRecord(dc->pooled, s), "hipEventRecord") || !ok(hipStreamWaitEvent(side, dc->pooled, 0), "hipStreamWaitEvent"))
     return LAPNYS_ERR_HIP;
-  if (!ok(lapnys::launch_pool(pl, k, W, side, span(LAPNYS_STAGE_POOL)), "pool launch")) return LAPNYS_ERR_HIP;
-  if (!ok(hipEventRecord(dc->pooled, side), "hipEventRecord")) return LAPNYS_ERR_HIP;
   if (!ok(lapnys::launch_ns(pl, W, side, span(LAPNYS_STAGE_NS)), "Newton-Schulz launch")) return LAPNYS_ERR_HIP;
   if (!ok(hipEventRecord(dc->join, side), "hipEventRecord")) return LAPNYS_ERR_HIP;
-  if (!ok(hipStreamWaitEvent(s, dc->pooled, 0), "hipStreamWaitEvent")) return LAPNYS_ERR_HIP;
   const lapnys::Span ks = span(LAPNYS_STAGE_KERNEL);
   if (!ok(pl.gaussian ? lapnys::launch_gauss(pl, q, k, v, W, s, ks) : lapnys::launch_l1exp(pl, q, k, v, W, s, ks),
           "kernel-matrix launch"))

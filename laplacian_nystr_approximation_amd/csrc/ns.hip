@@ -14,8 +14,9 @@
 //    runs inside the kernel-matrix stage's launch (ns_small.hpp, l1exp.hip).
 //  * 64 < m <= 256 (this file): the products are too large for one LDS; W and
 //    the iterates live in the workspace (L2-resident) and each product is one
-//    batched launch of 64 x 64 output tiles, two launches per step.  The same
-//    tile kernel also forms Y = X (B V) for these sizes.
+//    batched launch of 64 x 32 output tiles (ns_tile_kernel), two launches per
+//    step.  A general 64 x 64 tile product (gemm64_kernel) forms Y = X (B V)
+//    for these sizes and the optional correction below.
 //
 // Optional correction (LAPNYS_NS_REFINE, beyond the pages' fixed-count
 // iteration), for either schedule: R = I - W X with float64 accumulation, then
@@ -91,7 +92,8 @@ __global__ __launch_bounds__(256) void wbuild_big_kernel(const float* __restrict
 // its 1-norm and inf-norm are the same largest column sum and W^T = W: alpha
 // = (max column sum)^2 and X0 = W / alpha, read row-major.  Column sums: one
 // lane per column adds the W build's mp / 16 (<= 16) partial sums in block
-// order, all loaded at once.
+// order, all loaded at once.  X0 is symmetric too, so the row-major X0
+// also serves the first step as its own transpose.
 __global__ __launch_bounds__(256) void alpha_x0_kernel(const float* __restrict__ w, const float* __restrict__ part,
                                                        float* __restrict__ x, int mp) {
   __shared__ float red[4];
@@ -208,6 +210,120 @@ __global__ __launch_bounds__(256) void gemm64_kernel(const float* __restrict__ A
   for (int r = 0; r < 16; ++r) {
     const int rr = r0 + 32 * wr + 8 * (r >> 2) + 4 * lk + (r & 3);
     if (rr < crows && cc < ccols) Cp[(size_t)rr * ldc + cc] = mode == 2 ? Ap[(size_t)rr * lda + cc] + acc[r] : acc[r];
+  }
+}
+
+// ---- the Newton-Schulz steps at 64 < m <= 256 ------------------------------
+//
+// Each step X <- X (2I - W X) is two launches of ns_tile_kernel: Q = W X with
+// (2I - Q)^T stored, then X (2I - Q).  A launch of these tiles is short (a few
+// microseconds) and most of it is latency, so each launch stores its result
+// in the layouts the next one reads whole, 16 bytes per lane: row-major where
+// the result is a left operand next, transposed where it is a right one.
+// Every product is float32 on fp32 MFMA.  (Split bf16 products, as in the
+// in-LDS schedule for m <= 64, lose here: while the iteration has not yet
+// converged along W's small eigenvalues, the error of a step is carried to
+// the end at the same relative size instead of being squared away, and at
+// these sizes the float32 products cost little more per launch.)
+constexpr int kTileLd = 260;   // float LDS row stride of the staged B^T (1040-byte rows)
+constexpr int kTileCLd = 33;   // float row stride of the output tile in LDS
+
+// One launch of the step.  Matrices are mp x mp float32 per problem (mp a
+// multiple of 64), problem p at p mp^2; row-major keeps M[r][c] at r mp + c,
+// transposed at c mp + r.
+struct NsTileArgs {
+  const float* a;    // A, row-major
+  const float* bt;   // B, transposed
+  float* o_a;        // result, row-major (mode 1; null: not stored)
+  float* o_bt;       // result, transposed (null: not stored)
+  int mp, kext;      // reduction over [0, kext), a multiple of 32, <= mp
+  int mode;          // 0: C = W X, stores 2I - C; 1: C = X (2I - Q), stores C
+};
+
+// Output tile 64 x 32 (rows blockIdx.x * 64, columns blockIdx.y * 32) of
+// problem blockIdx.z: 4 mp^2 / 2048 workgroups per problem, one per CU at
+// m = 256 and eight problems.  Wavefront w owns rows 16 w + [0, 16) as two
+// 16 x 16 blocks of fp32 MFMA 16x16x4.  B^T's 32 rows, shared by the four
+// wavefronts, are staged in LDS; each lane loads its own A row's operands
+// directly.  MFMA (q, c) takes k = 16 q + 4 lk + c from lane group lk, so
+// both operands are 16-byte reads and the four groups of a row read 64
+// contiguous bytes per load.  Each block accumulates in two chains (even and
+// odd q, added at the end), which keeps four independent MFMA chains in
+// flight per wavefront.  Rows and columns past m hold zeros in every
+// operand; the identity of 2I - Q spans all mp rows, which keeps X zero there.
+__global__ __launch_bounds__(256) void ns_tile_kernel(NsTileArgs g) {
+  __shared__ __align__(16) float stage[32 * kTileLd];
+  __shared__ float ct[64 * kTileCLd];
+  const int p = blockIdx.z, r0 = blockIdx.x * 64, c0 = blockIdx.y * 32;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, lk = lane >> 4;
+  const size_t sq = (size_t)g.mp * g.mp;
+  const int row = r0 + 16 * w + li;
+  const int nq = g.kext >> 4;  // 16-deep chunks of k, even
+  // B^T: 32 rows x kext floats as 16-byte chunks (kext / 4 per row).  Chunks
+  // past kext load the last one again (in bounds) and land in LDS columns
+  // that no product reads.
+  float4 bv[8];
+  const float* btp = g.bt + (size_t)p * sq;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int e = tid + 256 * i, col = e >> 6, kc = min(e & 63, 4 * nq - 1);
+    bv[i] = *reinterpret_cast<const float4*>(btp + (size_t)(c0 + col) * g.mp + 4 * kc);
+  }
+  float4 av[16];
+  const float* ap = g.a + (size_t)p * sq + (size_t)row * g.mp + 4 * lk;
+#pragma unroll
+  for (int q = 0; q < 16; ++q)
+    if (q < nq) av[q] = *reinterpret_cast<const float4*>(ap + 16 * q);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int e = tid + 256 * i, col = e >> 6, kc = e & 63;
+    *reinterpret_cast<float4*>(stage + col * kTileLd + 4 * kc) = bv[i];
+  }
+  __syncthreads();
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) acc[j][0] = acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < 16; ++q)
+    if (q < nq) {
+      const int h = q & 1;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float4 b4 = *reinterpret_cast<const float4*>(stage + (16 * j + li) * kTileLd + 16 * q + 4 * lk);
+        acc[j][h] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q].x, b4.x, acc[j][h], 0, 0, 0);
+        acc[j][h] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q].y, b4.y, acc[j][h], 0, 0, 0);
+        acc[j][h] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q].z, b4.z, acc[j][h], 0, 0, 0);
+        acc[j][h] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q].w, b4.w, acc[j][h], 0, 0, 0);
+      }
+    }
+  // acc[j][.][r] sums to C[16 w + 4 lk + r][16 j + li] of the tile.
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ct[(16 * w + 4 * lk + r) * kTileCLd + 16 * j + li] = acc[j][0][r] + acc[j][1][r];
+  __syncthreads();
+  // Transposed: thread (column tid / 8, rows 8 (tid % 8) + [0, 8)).
+  if (g.o_bt) {
+    const int col = tid >> 3, rr = 8 * (tid & 7);
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = ct[(rr + i) * kTileCLd + col];
+    const int gc = c0 + col, gr = r0 + rr;
+    if (g.mode == 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (gr + i == gc ? 2.f : 0.f) - v[i];
+    }
+    float* d = g.o_bt + (size_t)p * sq + (size_t)gc * g.mp + gr;
+    *reinterpret_cast<float4*>(d) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(d + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+  // Row-major (mode 1): thread (row tid / 4, columns 8 (tid % 4) + [0, 8)).
+  if (g.o_a) {
+    const int rr = tid >> 2, cc = 8 * (tid & 3);
+    float* d = g.o_a + (size_t)p * sq + (size_t)(r0 + rr) * g.mp + c0 + cc;
+    const float* c = ct + rr * kTileCLd + cc;
+    *reinterpret_cast<float4*>(d) = make_float4(c[0], c[1], c[2], c[3]);
+    *reinterpret_cast<float4*>(d + 4) = make_float4(c[4], c[5], c[6], c[7]);
   }
 }
 
@@ -483,27 +599,29 @@ hipError_t launch_ns(const Plan& pl, Work& wk, hipStream_t s, Span t) {
   if (pl.cg) return hipGetLastError();  // the CG solve (cg.hip) needs W only
   // The column-sum partials go to the product buffer, which the steps only
   // write after alpha_x0 has read them.
+  const int T = pl.ns_iters;
   hipExtLaunchKernelGGL(alpha_x0_kernel, dim3(pl.P, 16), dim3(256), 0, s, nullptr,
-                        pl.ns_iters == 0 && !pl.refine ? t.stop : nullptr, 0, wk.w, wk.pm, wk.x, mp);
+                        T == 0 && !pl.refine ? t.stop : nullptr, 0, wk.w, wk.pm, wk.x, mp);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const long long sq = (long long)mp * mp;
-  const dim3 grid(mp / 64, mp / 64, pl.P);
-  float* xc = wk.x;
-  float* xn = wk.x2;
-  for (int it = 0; it < pl.ns_iters; ++it) {
-    hipLaunchKernelGGL(gemm64_kernel, grid, dim3(256), 0, s, wk.w, mp, sq, xc, mp, sq, mp, mp, wk.pm, mp, sq, mp, mp,
-                       kext, 0);
-    hipExtLaunchKernelGGL(gemm64_kernel, grid, dim3(256), 0, s, nullptr,
-                          it + 1 == pl.ns_iters && !pl.refine ? t.stop : nullptr, 0,
-                          xc, mp, sq, wk.pm, mp, sq, mp, mp, xn, mp, sq, mp, mp, kext, 1);
+  // Iterates alternate by step: X_it row-major at xf[it % 2] and transposed
+  // at xtf[it % 2] (X0, symmetric, is its own transpose); (2I - Q)^T in the
+  // product buffer.
+  const size_t n32 = (size_t)pl.P * mp * mp;
+  float* const xf[2] = {wk.x, wk.x2};
+  float* const xtf[2] = {wk.xt, wk.xt + n32};
+  const dim3 grid(mp / 64, mp / 32, pl.P);
+  for (int it = 0; it < T; ++it) {
+    const int c = it & 1, n = c ^ 1;
+    const NsTileArgs q{wk.w, it == 0 ? wk.x : xtf[c], nullptr, wk.pm, mp, kext, 0};
+    hipLaunchKernelGGL(ns_tile_kernel, grid, dim3(256), 0, s, q);
+    const NsTileArgs x{xf[c], wk.pm, xf[n], it + 1 < T ? xtf[n] : nullptr, mp, kext, 1};
+    hipExtLaunchKernelGGL(ns_tile_kernel, grid, dim3(256), 0, s, nullptr, it + 1 == T && !pl.refine ? t.stop : nullptr,
+                          0, x);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    float* t = xc;
-    xc = xn;
-    xn = t;
   }
-  wk.x_final = xc;
+  wk.x_final = xf[T & 1];
   return pl.refine ? launch_refine(pl, wk, s, t.stop) : hipSuccess;
 }
 

@@ -43,7 +43,7 @@ class Workload:
     refine: bool = False  # one float64-residual correction after the Newton-Schulz steps
     kernel: str = "laplacian"  # or "gaussian"
     solver: str = "ns"  # or "cg" (conjugate gradient for W^-1 (B V))
-    ns_plain: bool = False  # m <= 64: the plain float32 Newton-Schulz steps, a launch of their own
+    ns_plain: bool = False  # every Newton-Schulz product in float32 (m <= 64: as a launch of its own)
     # > 0: every odd pooled window of each landmark row of K is replaced by its
     # left neighbour's tokens plus near_dup-scaled normal noise (see
     # make_inputs), so pairs of landmarks nearly coincide and W is close to

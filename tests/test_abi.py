@@ -140,11 +140,15 @@ def test_binding_checks_tensor_sizes():
 
 
 def test_plain_ns_flag():
-    """LAPNYS_NS_PLAIN is a known flag; at m <= 64 it needs no other workspace."""
+    """LAPNYS_NS_PLAIN is a known flag and needs no other workspace at any m:
+    at m <= 64 it moves the float32 steps into a launch of their own, and
+    at m > 64 every step already takes float32 products."""
     pl = _p(ns_plain=True)
     assert pl.flags == B.LAPNYS_WHITEN | B.LAPNYS_NS_PLAIN
     assert L.library().lapnys_landmark_count(ctypes.byref(pl)) == 49
     assert L.lapnys_workspace_size(pl) == L.lapnys_workspace_size(_p())
+    big = dict(grid_h=32, grid_w=32)  # m = 256
+    assert L.lapnys_workspace_size(_p(ns_plain=True, **big)) == L.lapnys_workspace_size(_p(**big))
 
 
 def test_backward_workspace_and_support():

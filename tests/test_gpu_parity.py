@@ -83,13 +83,20 @@ def _ill_conditioned_cases():
         base.with_(name="neardup_1e-3_eps1e-5_T48", near_dup=1e-3, eps=1e-5, ns_iters=48),
         base.with_(name="neardup_1e-4_eps1e-6_T48", near_dup=1e-4, eps=1e-6, ns_iters=48),
         base.with_(name="neardup_1e-3_eps1e-5_T32_bf16", near_dup=1e-3, eps=1e-5, ns_iters=32, dtype="bf16"),
+        # m > 64, the tiled schedule: the guard moves the steps to float32
+        # products once rho = ||W||_1 max|X| passes 64.
+        Workload("neardup_m100_1e-3_eps1e-5_T48", B=1, H=2, grid_h=40, grid_w=40, d=64, pool=4, seed_index=81,
+                 near_dup=1e-3, eps=1e-5, ns_iters=48),
+        Workload("neardup_m256_1e-3_eps1e-5_T48_bf16", B=1, H=2, grid_h=64, grid_w=64, d=64, pool=4,
+                 seed_index=82, near_dup=1e-3, eps=1e-5, ns_iters=48, dtype="bf16"),
     ]
 
 
 @pytest.mark.parametrize("w", _ill_conditioned_cases(), ids=lambda w: w.name)
 def test_ill_conditioned_default_schedule(w):
-    """The default m <= 64 schedule on a nearly singular W against the oracle
-    and against LAPNYS_NS_PLAIN on the same inputs.  Every stage up to B V to
+    """The default schedules (m <= 64 in one launch, m > 64 tiled) on a nearly
+    singular W against the oracle and against LAPNYS_NS_PLAIN on the same
+    inputs.  Every stage up to B V to
     the usual bar; X and Y entry by entry (gates that grow with W's condition
     number); the residual ||W X - I||_F within twice the plain float32
     schedule's (plus 1e-6) and within the float32 floor 8 u cond(W); O within

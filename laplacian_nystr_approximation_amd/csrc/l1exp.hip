@@ -13,13 +13,14 @@
 // The partials are reduced by the finalize stage (finalize.hip).
 //
 // Layout of the work: one lane per token.  A workgroup of 256 lanes takes a
-// tile of 256 consecutive tokens of one problem and a block of landmarks.  A
-// landmark row is spread over the 16 lanes of each DPP row and reaches every
-// lane through a row_newbcast source operand, so the inner loop is pure VALU:
-// one subtract (with the broadcast folded in) and one add with an |.| source
-// modifier per (token, landmark, feature), and one 16-byte load per lane feeds
-// a whole landmark row.  This stage is not a dense contraction; it runs on the
-// vector ALUs, not on MFMA.
+// tile of 256 consecutive tokens of one problem and a block of landmarks,
+// whose rows it stages in LDS.  Every landmark value reaches all 64 lanes of
+// a wavefront as a wave-uniform LDS broadcast read (one 16-byte read gives
+// four features of one landmark, double-buffered one 4-feature chunk ahead),
+// so the inner loop is one subtract and one add with an |.| source modifier
+// per (token, landmark, feature), eight independent sums at a time (four
+// landmarks, even and odd features).  This stage is not a dense contraction;
+// it runs on the vector ALUs, not on MFMA.
 //
 // LDS per workgroup: a tile buffer that holds C as float32 [lb][256 + 4], then
 // B as bf16 high and low parts [lb + 1][264] each (the extra row is zero),

@@ -14,7 +14,9 @@ import os
 from typing import Dict, Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblapnys.so")
+# The in-tree build; LAPNYS_LIBRARY names another build of the same library
+# (the host-sanitized one that the ABI tests also run against).
+LIB_PATH = os.environ.get("LAPNYS_LIBRARY") or os.path.join(_HERE, "liblapnys.so")
 
 LAPNYS_F32 = 0
 LAPNYS_BF16 = 1

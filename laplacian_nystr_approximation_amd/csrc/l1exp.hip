@@ -242,6 +242,26 @@ __global__ __launch_bounds__(kTT) void l1exp_kernel(
                         lds, kclk);
 }
 
+// The same stage without the solver at landmark blocks of at most 32 (m > 64,
+// and the forms whose solver runs beside it), with registers held to three
+// wavefronts per SIMD: the L1 loop issues faster with three than with two,
+// and the 43 KB of LDS of such a block allows three workgroups per CU.  At
+// d = 64 this spills a few registers of the cold path and still runs the
+// m = 256 kernel-matrix stage 16 % faster.  Same parameters as l1exp_kernel.
+template <typename T, int D, int LBB>
+__global__ __launch_bounds__(kTT) __attribute__((amdgpu_waves_per_eu(3))) void l1exp_solo_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ kt,
+    float* __restrict__ ct, float2* __restrict__ stats, float* __restrict__ bvpart, float* __restrict__ bt,
+    float* __restrict__ wout, float* __restrict__ xout, int N, int ldc, int m, int lbmax, int ntiles, int tpg, int groups, int jblocks,
+    float scale, float eps, int iters, int nns, int gap, unsigned long long* __restrict__ nsclk,
+    unsigned long long* __restrict__ kclk) {
+  extern __shared__ __align__(16) float lds[];
+  const int b = blockIdx.x;
+  const int jb = b % jblocks, g = (b / jblocks) % groups, p = b / (jblocks * groups);
+  l1exp_body<T, D, LBB>(q, k, v, kt, ct, stats, bvpart, bt, N, ldc, m, lbmax, ntiles, tpg, groups, scale, jb, g, p,
+                        lds, kclk);
+}
+
 // CUs of the current device (queried once per device; 0 if unknown).
 int cu_count() {
   static int cached[kMaxDevices] = {};
@@ -263,6 +283,7 @@ hipError_t launch_kernel(const Plan& pl, const void* q, const void* k, const voi
   if (KS > 0 && floats < (size_t)ns_detail::kNsLdsFloats) floats = ns_detail::kNsLdsFloats;
   const size_t shmem = floats * sizeof(float);
   auto kern = l1exp_kernel<T, D, LBB, KS>;
+  if constexpr (KS == 0 && LBB <= 2) kern = l1exp_solo_kernel<T, D, LBB>;
   if (shmem > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;

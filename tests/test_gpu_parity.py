@@ -8,8 +8,8 @@ import sys
 import numpy as np
 import pytest
 
-from gpu_harness import (NS_RESIDUAL, O_NORMWISE_F32, U32, check_problem, gpu_available, ns_residual, o_errors,
-                         run_gpu, run_oracle, workload_inputs)
+from gpu_harness import (NS_RESIDUAL, O_NORMWISE_F32, U32, check_problem, device_inputs, gpu_available, ns_residual,
+                         o_errors, run_gpu, run_oracle, torch_mod, workload_inputs)
 import oracle
 from lapnys_inputs import WORKLOADS, Workload, bf16_bits_to_f32, f32_to_bf16_bits
 
@@ -352,3 +352,38 @@ def test_linear_in_v():
     x2.v[...] = f32_to_bf16_bits(2 * bf16_bits_to_f32(x.v))  # doubling is exact
     b = run_gpu(w, x2, debug=False)["O"]
     assert np.array_equal((2 * a).view(np.uint32), b.view(np.uint32))
+
+
+def test_concurrent_streams_match_sequential():
+    """Forwards enqueued alternately on two caller streams without synchronising
+    in between, twice over, each call with its own workspace and output: an
+    m <= 64 problem set (its whole sequence on the caller's stream) on the
+    first stream, and m = 256 problem sets on both (their solver on the
+    library's own stream, forked after pooling and joined by events, so the
+    two callers share that stream).  Every output equals the same call run
+    alone, bit for bit."""
+    torch = torch_mod()
+    import laplacian_nystr_approximation_amd as L
+    wa, wb = WORKLOADS["stage2_28x28_bf16"], WORKLOADS["sweep_64x64_bf16"]
+    wc = wb.with_(seed_index=wb.seed_index + 100)
+    cases = [(wa, workload_inputs(wa)), (wb, workload_inputs(wb)), (wc, workload_inputs(wc))]
+    refs = [run_gpu(w, x, debug=False)["O"] for w, x in cases]
+    bufs = []
+    for w, x in cases:
+        params = L.params_for(w)
+        q, k, v = device_inputs(x, w.dtype)
+        outs = [torch.full((w.B, w.H, w.N, w.d), float("nan"), dtype=torch.float32, device="cuda") for _ in range(2)]
+        wss = [torch.empty(L.lapnys_workspace_size(params), dtype=torch.uint8, device="cuda") for _ in range(2)]
+        bufs.append((params, q, k, v, outs, wss))
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    order = [(0, s1), (1, s2), (2, s1)]
+    for r in range(2):
+        for i, s in order:
+            params, q, k, v, outs, wss = bufs[i]
+            L.lapnys_forward_ws(q, k, v, outs[r], params, wss[r], stream=s)
+    torch.cuda.synchronize()
+    for i, (w, _) in enumerate(cases):
+        for r in range(2):
+            got = bufs[i][4][r].cpu().numpy().reshape(refs[i].shape)
+            assert np.array_equal(got.view(np.uint32), refs[i].view(np.uint32)), f"{w.name} round {r}"

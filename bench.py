@@ -483,7 +483,7 @@ def main(argv=None):
                          "length sweep at m = 256 and the headline workload")
     ap.add_argument("--all-configs", action="store_true",
                     help="one bench line per configuration (the five forward workloads, the headline workload and "
-                         "the length-sweep points), the oracle legs first")
+                         "the length-sweep points), each from a child process running that workload's bench")
     ap.add_argument("--fill-baseline", default=None,
                     help="rewrite BASELINE.md section 4 from the bench lines in this file (no GPU)")
     ap.add_argument("--copy-mb", type=int, default=0,
@@ -505,9 +505,23 @@ def main(argv=None):
     if args.fill_baseline:
         return fill_baseline_main(args)
     if args.all_configs:
-        names = ALL_CONFIGS
-    else:
-        names = [args.workload]
+        # One child process per configuration, each the same command as a
+        # single-workload run (its oracle leg, then its GPU line), so no line
+        # is measured after another configuration's work in the same process.
+        # This process touches no GPU.
+        import subprocess
+        for name in ALL_CONFIGS:
+            cmd = [sys.executable, os.path.abspath(__file__), "--workload", name, "--steps", str(args.steps),
+                   "--warmup", str(args.warmup), "--cpu-budget", str(args.cpu_budget), "--kernel", args.kernel,
+                   "--solver", args.solver]
+            r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
+            if r.returncode != 0:
+                print(f"bench.py --workload {name} failed ({r.returncode})", file=sys.stderr)
+                return r.returncode
+            lines = [line for line in r.stdout.splitlines() if line.startswith("{")]
+            print(lines[-1], flush=True)
+        return 0
+    names = [args.workload]
     ws_ = []
     for name in names:
         w = WORKLOADS[name]

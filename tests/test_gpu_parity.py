@@ -293,6 +293,13 @@ def _edge_cases():
         # blocks of 32, 32 and 2
         Workload("tail_22x12_p2_m66", grid_h=22, grid_w=12, d=64, pool=2, dtype="bf16", **base),
         Workload("tail_18x30_p3_m60", grid_h=18, grid_w=30, d=32, pool=3, dtype="f32", **base),
+        # the tiled Newton-Schulz at a padded size of 192 (3 x 6 tiles of 64 x 32,
+        # reduction over 160) and at 256 with a reduction over 224; and its
+        # zero- and one-step schedules
+        Workload("m144_24x24_p2", grid_h=24, grid_w=24, d=64, pool=2, dtype="f32", **{**base, "ns_iters": 30}),
+        Workload("m210_30x28_p2_d32", grid_h=30, grid_w=28, d=32, pool=2, dtype="bf16", **{**base, "ns_iters": 30}),
+        Workload("ns0_18x18_m81", grid_h=18, grid_w=18, d=64, pool=2, dtype="f32", **{**base, "ns_iters": 0}),
+        Workload("ns1_18x18_m81", grid_h=18, grid_w=18, d=32, pool=2, dtype="bf16", **{**base, "ns_iters": 1}),
     ]
     return cases
 

@@ -133,8 +133,6 @@ int make_plan(const lapnys_params* p, Plan* pl) {
   P.off_rs = take(Pn * P.m * f);
   P.off_y = take(Pn * P.m * P.d * f);
   P.off_yt = take(P.fused_ns ? Pn * 2 * P.d * 64 * sizeof(uint16_t) : 0);
-  // m > 64 Newton-Schulz steps: X^T of two iterates.
-  P.off_xt = take(!P.fused_ns && !P.cg ? 2 * Pn * P.mp * P.mp * f : 0);
   P.total = off;
   return LAPNYS_OK;
 }
@@ -176,7 +174,6 @@ lapnys::Work carve(const Plan& pl, void* ws) {
   W.rs = (float*)(b + pl.off_rs);
   W.y = (float*)(b + pl.off_y);
   W.yt = (__bf16*)(b + pl.off_yt);
-  W.xt = (float*)(b + pl.off_xt);
   W.x_final = W.x;
   return W;
 }

@@ -99,7 +99,7 @@ struct Plan {
   int groups;       // tile groups per problem
   // workspace offsets in bytes
   size_t off_kt, off_w, off_x, off_x2, off_pm, off_ct, off_stats, off_bvpart, off_bv,
-      off_mu, off_sigma, off_rs, off_y, off_yt, off_xt, total;
+      off_mu, off_sigma, off_rs, off_y, off_yt, total;
 };
 
 // Device pointers into one call's workspace.
@@ -108,7 +108,6 @@ struct Work {
   __bf16* yt;          // m <= 64: Y^T as bf16 high and low parts, [P][2][d][64] (yt_index layout)
   float* x_final;      // the Newton-Schulz result (x or x2), set by launch_ns
   float* bt = nullptr; // if set (Laplacian form only): the kernel-matrix stage also stores B as [P][m][N]
-  float* xt = nullptr;  // m > 64 steps: X^T of two iterates, [2][P][mp][mp]
   // If set (debug form): device wall-clock stamps.  nsclk [P][3]: start, first
   // step and end of each problem's in-launch solver workgroup; kclk [2]: the
   // earliest start and latest end over the Laplacian kernel-matrix workgroups

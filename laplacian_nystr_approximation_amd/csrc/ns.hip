@@ -215,116 +215,206 @@ __global__ __launch_bounds__(256) void gemm64_kernel(const float* __restrict__ A
 
 // ---- the Newton-Schulz steps at 64 < m <= 256 ------------------------------
 //
-// Each step X <- X (2I - W X) is two launches of ns_tile_kernel: Q = W X with
-// (2I - Q)^T stored, then X (2I - Q).  A launch of these tiles is short (a few
-// microseconds) and most of it is latency, so each launch stores its result
-// in the layouts the next one reads whole, 16 bytes per lane: row-major where
-// the result is a left operand next, transposed where it is a right one.
-// Every product is float32 on fp32 MFMA.  (Split bf16 products, as in the
-// in-LDS schedule for m <= 64, lose here: while the iteration has not yet
+// One launch per step.  Column block c (16 columns) of the next iterate,
+//   X'[:, c] = X (2 E_c - W X[:, c]),    E_c the same columns of I,
+// needs W, X and that block of X only, so a workgroup forms it from the
+// previous iterate alone: Q_c = W X[:, c] (mp x 16), T_c = 2 E_c - Q_c, then
+// X T_c for its share of the rows.  Column by column this is the step
+// X (2I - W X) itself, so the iteration keeps its self-correction of the
+// residual I - W X.  (The row-block form (2I - X W) X corrects I - X W
+// instead; emulated in float32 at m = 256 it left W X - I ten times larger.)
+// A workgroup that forms only part of the rows of X T_c repeats Q_c, which the
+// other parts of its column block form too: at m = 256 and eight problems two
+// parts of 128 rows give 256 workgroups, one per CU, for 1.5 times the
+// step's flops (pick_step weighs this against the number of workgroups).
+//
+// Every product is float32 on fp32 MFMA 16x16x4.  (Split bf16 products, as in
+// the in-LDS schedule for m <= 64, lose here: while the iteration has not yet
 // converged along W's small eigenvalues, the error of a step is carried to
-// the end at the same relative size instead of being squared away, and at
-// these sizes the float32 products cost little more per launch.)
-constexpr int kTileLd = 260;   // float LDS row stride of the staged B^T (1040-byte rows)
-constexpr int kTileCLd = 33;   // float row stride of the output tile in LDS
+// the end at the same relative size instead of being squared away.)  MFMA
+// (q, c) takes k = 16 q + 4 lk + c from lane group lk, so every operand is a
+// 16-byte read.  W's rows and X's rows come from global memory (each element
+// read once per workgroup; L2-resident), kStepPD chunks of k ahead of the
+// products; X[:, c] and T_c sit transposed in LDS.  Workgroup b takes problem
+// b % P: when P is a multiple of 8 all workgroups of a problem run on one XCD
+// and share its L2.  Rows and columns past m hold zeros in W and X and stay
+// zero (T_c's identity there meets zero columns of X), and a reduction over
+// all mp terms equals the one over m: the added terms are exact zeros.
+constexpr int kStepPD = 2;  // 32-deep chunks of k loaded ahead of the products
 
-// One launch of the step.  Matrices are mp x mp float32 per problem (mp a
-// multiple of 64), problem p at p mp^2; row-major keeps M[r][c] at r mp + c,
-// transposed at c mp + r.
-struct NsTileArgs {
-  const float* a;    // A, row-major
-  const float* bt;   // B, transposed
-  float* o_a;        // result, row-major (mode 1; null: not stored)
-  float* o_bt;       // result, transposed (null: not stored)
-  int mp, kext;      // reduction over [0, kext), a multiple of 32, <= mp
-  int mode;          // 0: C = W X, stores 2I - C; 1: C = X (2I - Q), stores C
+// Eight consecutive k of one row, k = 32 q + [0, 8) from row (the caller
+// adds 8 lk): two adjacent 16-byte loads.  Across the four lane groups each
+// load instruction touches every 128-byte line of a row's chunk, so a row's
+// chunk costs the L2 two line requests, not four.
+struct K8 {
+  float4 lo, hi;
 };
+__device__ __forceinline__ K8 load_k8(const float* row, int q) {
+  const float* a = row + 32 * q;
+  return K8{*reinterpret_cast<const float4*>(a), *reinterpret_cast<const float4*>(a + 4)};
+}
 
-// Output tile 64 x 32 (rows blockIdx.x * 64, columns blockIdx.y * 32) of
-// problem blockIdx.z: 4 mp^2 / 2048 workgroups per problem, one per CU at
-// m = 256 and eight problems.  Wavefront w owns rows 16 w + [0, 16) as two
-// 16 x 16 blocks of fp32 MFMA 16x16x4.  B^T's 32 rows, shared by the four
-// wavefronts, are staged in LDS; each lane loads its own A row's operands
-// directly.  MFMA (q, c) takes k = 16 q + 4 lk + c from lane group lk, so
-// both operands are 16-byte reads and the four groups of a row read 64
-// contiguous bytes per load.  Each block accumulates in two chains (even and
-// odd q, added at the end), which keeps four independent MFMA chains in
-// flight per wavefront.  Rows and columns past m hold zeros in every
-// operand; the identity of 2I - Q spans all mp rows, which keeps X zero there.
-__global__ __launch_bounds__(256) void ns_tile_kernel(NsTileArgs g) {
-  __shared__ __align__(16) float stage[32 * kTileLd];
-  __shared__ float ct[64 * kTileCLd];
-  const int p = blockIdx.z, r0 = blockIdx.x * 64, c0 = blockIdx.y * 32;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, lk = lane >> 4;
-  const size_t sq = (size_t)g.mp * g.mp;
-  const int row = r0 + 16 * w + li;
-  const int nq = g.kext >> 4;  // 16-deep chunks of k, even
-  // B^T: 32 rows x kext floats as 16-byte chunks (kext / 4 per row).  Chunks
-  // past kext load the last one again (in bounds) and land in LDS columns
-  // that no product reads.
-  float4 bv[8];
-  const float* btp = g.bt + (size_t)p * sq;
+// acc += A B over the eight k of a chunk: MFMA c takes k = 32 q + 8 lk + c
+// from lane group lk (A from a, B from b).
+__device__ __forceinline__ f32x4 mfma_k8(const K8& a, const K8& b, f32x4 acc) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.x, b.lo.x, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.y, b.lo.y, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.z, b.lo.z, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.w, b.lo.w, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.x, b.hi.x, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.y, b.hi.y, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.z, b.hi.z, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.w, b.hi.w, acc, 0, 0, 0);
+  return acc;
+}
+
+// Column block blockIdx.x / P % (MP / 16), rows [64 TPW part, +64 TPW) with
+// part = blockIdx.x / P / (MP / 16), of problem blockIdx.x % P, with NW
+// wavefronts (eight give each SIMD two, whose loads and products overlap).
+// Matrices are MP x MP float32 row-major, problem p at p MP^2.  xn must not
+// alias x.
+template <int MP, int TPW, int NW>
+__global__ __launch_bounds__(64 * NW) void ns_step_kernel(const float* __restrict__ w, const float* __restrict__ x,
+                                                          float* __restrict__ xn, int P) {
+  static_assert((MP / 16) % NW == 0 && (4 * TPW) % NW == 0, "row tiles must split evenly over the wavefronts");
+  constexpr int NT = 64 * NW;          // lanes
+  constexpr int NT1 = MP / 16 / NW;    // Q_c row tiles per wavefront
+  constexpr int NT2 = 4 * TPW / NW;    // output row tiles per wavefront
+  constexpr int NCB = MP / 16;  // column blocks
+  constexpr int NQ = MP / 32;   // 32-deep chunks of k
+  constexpr int KS = MP + 4;    // LDS row stride (floats) of the transposed blocks
+  __shared__ __align__(16) float xc[16 * KS];  // xc[j][k] = X[k][c0 + j]
+  __shared__ __align__(16) float tt[16 * KS];  // tt[j][k] = T_c[k][j]
+  const int b = blockIdx.x, p = b % P, rest = b / P;
+  const int c0 = 16 * (rest % NCB), r0 = 64 * TPW * (rest / NCB);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, li = lane & 15, lk = lane >> 4;
+  const size_t sq = (size_t)MP * MP;
+  const float* wp = w + p * sq;
+  const float* xp = x + p * sq;
+
+  // X[:, c0 + [0, 16)): MP rows of four 16-byte loads, transposed into xc.
+  constexpr int kXc = 4 * MP / NT;
+  float4 xv[kXc];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int e = tid + 256 * i, col = e >> 6, kc = min(e & 63, 4 * nq - 1);
-    bv[i] = *reinterpret_cast<const float4*>(btp + (size_t)(c0 + col) * g.mp + 4 * kc);
+  for (int i = 0; i < kXc; ++i) {
+    const int e = tid + NT * i;
+    xv[i] = *reinterpret_cast<const float4*>(xp + (size_t)(e >> 2) * MP + c0 + 4 * (e & 3));
   }
-  float4 av[16];
-  const float* ap = g.a + (size_t)p * sq + (size_t)row * g.mp + 4 * lk;
+  // W rows 16 (wv + NW u) + li of Q_c's row tiles u, the first kStepPD chunks.
+  const float* wrow = wp + (size_t)(16 * wv + li) * MP + 8 * lk;
+  K8 wa[kStepPD][NT1];
 #pragma unroll
-  for (int q = 0; q < 16; ++q)
-    if (q < nq) av[q] = *reinterpret_cast<const float4*>(ap + 16 * q);
+  for (int s = 0; s < kStepPD; ++s)
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int e = tid + 256 * i, col = e >> 6, kc = e & 63;
-    *reinterpret_cast<float4*>(stage + col * kTileLd + 4 * kc) = bv[i];
+    for (int u = 0; u < NT1; ++u) wa[s][u] = load_k8(wrow + (size_t)16 * NW * u * MP, s);
+#pragma unroll
+  for (int i = 0; i < kXc; ++i) {
+    const int e = tid + NT * i, k = e >> 2, j = 4 * (e & 3);
+    xc[j * KS + k] = xv[i].x;
+    xc[(j + 1) * KS + k] = xv[i].y;
+    xc[(j + 2) * KS + k] = xv[i].z;
+    xc[(j + 3) * KS + k] = xv[i].w;
   }
   __syncthreads();
-  f32x4 acc[2][2];
+
+  // Q_c row tiles wv + NW u: acc1[u][q & 1] accumulates chunk q.  Chunk q's
+  // products, then chunk q + 1's LDS operand and chunk q + kStepPD's W loads;
+  // the scheduling barrier keeps the compiler from sinking the loads to
+  // their use, which would expose their latency at every chunk.
+  f32x4 acc1[NT1][2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) acc[j][0] = acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < NT1; ++u) acc1[u][0] = acc1[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float* xcl = xc + li * KS + 8 * lk;
+  K8 bx = load_k8(xcl, 0);
 #pragma unroll
-  for (int q = 0; q < 16; ++q)
-    if (q < nq) {
-      const int h = q & 1;
+  for (int q = 0; q < NQ; ++q) {
+    const int s = q % kStepPD, h = q & 1;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const float4 b4 = *reinterpret_cast<const float4*>(stage + (16 * j + li) * kTileLd + 16 * q + 4 * lk);
-        acc[j][h] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q].x, b4.x, acc[j][h], 0, 0, 0);
-        acc[j][h] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q].y, b4.y, acc[j][h], 0, 0, 0);
-        acc[j][h] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q].z, b4.z, acc[j][h], 0, 0, 0);
-        acc[j][h] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q].w, b4.w, acc[j][h], 0, 0, 0);
-      }
+    for (int u = 0; u < NT1; ++u) acc1[u][h] = mfma_k8(wa[s][u], bx, acc1[u][h]);
+    if (q + 1 < NQ) bx = load_k8(xcl, q + 1);
+    if (q + kStepPD < NQ) {
+#pragma unroll
+      for (int u = 0; u < NT1; ++u) wa[s][u] = load_k8(wrow + (size_t)16 * NW * u * MP, q + kStepPD);
     }
-  // acc[j][.][r] sums to C[16 w + 4 lk + r][16 j + li] of the tile.
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // X rows r0 + 16 (wv + NW v) + li of the output row tiles v, issued before
+  // T_c goes to LDS.
+  const float* xrow = xp + (size_t)(r0 + 16 * wv + li) * MP + 8 * lk;
+  K8 xa[kStepPD][NT2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int s = 0; s < kStepPD; ++s)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ct[(16 * w + 4 * lk + r) * kTileCLd + 16 * j + li] = acc[j][0][r] + acc[j][1][r];
+    for (int v = 0; v < NT2; ++v) xa[s][v] = load_k8(xrow + (size_t)16 * NW * v * MP, s);
+  // acc1[u][.][r] sums to Q[16 (wv + NW u) + 4 lk + r][c0 + li]; T_c = 2 E_c - Q_c.
+#pragma unroll
+  for (int u = 0; u < NT1; ++u) {
+    const int k0 = 16 * (wv + NW * u) + 4 * lk;
+    float t4[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) t4[r] = (k0 + r == c0 + li ? 2.f : 0.f) - (acc1[u][0][r] + acc1[u][1][r]);
+    *reinterpret_cast<float4*>(tt + li * KS + k0) = make_float4(t4[0], t4[1], t4[2], t4[3]);
+  }
   __syncthreads();
-  // Transposed: thread (column tid / 8, rows 8 (tid % 8) + [0, 8)).
-  if (g.o_bt) {
-    const int col = tid >> 3, rr = 8 * (tid & 7);
-    float v[8];
+
+  // X' rows: X T_c, row tiles wv + NW v of this part.
+  f32x4 acc2[NT2][2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = ct[(rr + i) * kTileCLd + col];
-    const int gc = c0 + col, gr = r0 + rr;
-    if (g.mode == 0) {
+  for (int v = 0; v < NT2; ++v) acc2[v][0] = acc2[v][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float* ttl = tt + li * KS + 8 * lk;
+  K8 bt = load_k8(ttl, 0);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = (gr + i == gc ? 2.f : 0.f) - v[i];
+  for (int q = 0; q < NQ; ++q) {
+    const int s = q % kStepPD, h = q & 1;
+#pragma unroll
+    for (int v = 0; v < NT2; ++v) acc2[v][h] = mfma_k8(xa[s][v], bt, acc2[v][h]);
+    if (q + 1 < NQ) bt = load_k8(ttl, q + 1);
+    if (q + kStepPD < NQ) {
+#pragma unroll
+      for (int v = 0; v < NT2; ++v) xa[s][v] = load_k8(xrow + (size_t)16 * NW * v * MP, q + kStepPD);
     }
-    float* d = g.o_bt + (size_t)p * sq + (size_t)gc * g.mp + gr;
-    *reinterpret_cast<float4*>(d) = make_float4(v[0], v[1], v[2], v[3]);
-    *reinterpret_cast<float4*>(d + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  // Row-major (mode 1): thread (row tid / 4, columns 8 (tid % 4) + [0, 8)).
-  if (g.o_a) {
-    const int rr = tid >> 2, cc = 8 * (tid & 3);
-    float* d = g.o_a + (size_t)p * sq + (size_t)(r0 + rr) * g.mp + c0 + cc;
-    const float* c = ct + rr * kTileCLd + cc;
-    *reinterpret_cast<float4*>(d) = make_float4(c[0], c[1], c[2], c[3]);
-    *reinterpret_cast<float4*>(d + 4) = make_float4(c[4], c[5], c[6], c[7]);
+  // acc2[v][.][r] sums to X'[r0 + 16 (wv + NW v) + 4 lk + r][c0 + li]: 16
+  // lanes write 64 contiguous bytes of a row.
+  float* xo = xn + p * sq + c0 + li;
+#pragma unroll
+  for (int v = 0; v < NT2; ++v)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) xo[(size_t)(r0 + 16 * (wv + NW * v) + 4 * lk + r) * MP] = acc2[v][0][r] + acc2[v][1][r];
+}
+
+using StepKernel = void (*)(const float*, const float*, float*, int);
+
+// The step kernel for padded size mp and P problems, its grid and workgroup
+// size.  Row parts of 64 TPW rows: fewer parts repeat Q_c less, more parts
+// give more workgroups; the choice minimises (rounds of 256 workgroups) x
+// (MFMAs per SIMD, proportional to MP / 64 + TPW), ties to fewer workgroups.
+struct StepChoice {
+  StepKernel k;
+  unsigned grid, threads;
+};
+StepChoice pick_step(int mp, int P) {
+  struct Cand { int tpw, nw; StepKernel k; };
+  static const Cand c256[] = {{4, 8, ns_step_kernel<256, 4, 8>}, {2, 8, ns_step_kernel<256, 2, 8>},
+                              {1, 4, ns_step_kernel<256, 1, 4>}};
+  static const Cand c192[] = {{3, 4, ns_step_kernel<192, 3, 4>}, {1, 4, ns_step_kernel<192, 1, 4>}};
+  static const Cand c128[] = {{2, 8, ns_step_kernel<128, 2, 8>}, {1, 4, ns_step_kernel<128, 1, 4>}};
+  StepChoice best{nullptr, 0, 0};
+  if (mp != 128 && mp != 192 && mp != 256) return best;
+  const Cand* c = mp == 256 ? c256 : mp == 192 ? c192 : c128;
+  const int n = mp == 256 ? 3 : 2;
+  long long best_cost = 0;
+  for (int i = 0; i < n; ++i) {
+    const long long wgs = (long long)P * (mp / 16) * (mp / (64 * c[i].tpw));
+    const long long cost = ((wgs + 255) / 256) * (mp / 64 + c[i].tpw);
+    if (!best.k || cost < best_cost) {
+      best = StepChoice{c[i].k, (unsigned)wgs, 64u * c[i].nw};
+      best_cost = cost;
+    }
   }
+  return best;
 }
 
 // The residual R = I - W X of one 32 x 32 tile (blockIdx.x, blockIdx.y) of
@@ -604,20 +694,14 @@ hipError_t launch_ns(const Plan& pl, Work& wk, hipStream_t s, Span t) {
                         T == 0 && !pl.refine ? t.stop : nullptr, 0, wk.w, wk.pm, wk.x, mp);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  // Iterates alternate by step: X_it row-major at xf[it % 2] and transposed
-  // at xtf[it % 2] (X0, symmetric, is its own transpose); (2I - Q)^T in the
-  // product buffer.
-  const size_t n32 = (size_t)pl.P * mp * mp;
+  // Iterates alternate by step between the two buffers.
   float* const xf[2] = {wk.x, wk.x2};
-  float* const xtf[2] = {wk.xt, wk.xt + n32};
-  const dim3 grid(mp / 64, mp / 32, pl.P);
+  const StepChoice step = pick_step(mp, pl.P);
+  if (!step.k) return hipErrorInvalidValue;
   for (int it = 0; it < T; ++it) {
-    const int c = it & 1, n = c ^ 1;
-    const NsTileArgs q{wk.w, it == 0 ? wk.x : xtf[c], nullptr, wk.pm, mp, kext, 0};
-    hipLaunchKernelGGL(ns_tile_kernel, grid, dim3(256), 0, s, q);
-    const NsTileArgs x{xf[c], wk.pm, xf[n], it + 1 < T ? xtf[n] : nullptr, mp, kext, 1};
-    hipExtLaunchKernelGGL(ns_tile_kernel, grid, dim3(256), 0, s, nullptr, it + 1 == T && !pl.refine ? t.stop : nullptr,
-                          0, x);
+    hipExtLaunchKernelGGL(step.k, dim3(step.grid), dim3(step.threads), 0, s, nullptr,
+                          it + 1 == T && !pl.refine ? t.stop : nullptr,
+                          0, (const float*)wk.w, (const float*)xf[it & 1], xf[(it + 1) & 1], pl.P);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

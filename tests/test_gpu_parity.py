@@ -300,6 +300,16 @@ def _edge_cases():
         Workload("m210_30x28_p2_d32", grid_h=30, grid_w=28, d=32, pool=2, dtype="bf16", **{**base, "ns_iters": 30}),
         Workload("ns0_18x18_m81", grid_h=18, grid_w=18, d=64, pool=2, dtype="f32", **{**base, "ns_iters": 0}),
         Workload("ns1_18x18_m81", grid_h=18, grid_w=18, d=32, pool=2, dtype="bf16", **{**base, "ns_iters": 1}),
+        # the m > 64 step kernel's other forms, chosen by the problem count:
+        # all 256 rows in one part, eight wavefronts (16 problems at m = 256);
+        # all 192 rows in one part (8 problems at m = 144); all 128 rows in
+        # one part, eight wavefronts (32 problems at m = 100)
+        Workload("steps_m256_p16", B=16, H=1, grid_h=16, grid_w=16, d=32, pool=1, dtype="f32", lam=4.0, eps=1e-3,
+                 ns_iters=40, seed_index=43),
+        Workload("steps_m144_p8", B=4, H=2, grid_h=24, grid_w=24, d=64, pool=2, dtype="bf16", lam=4.0, eps=1e-3,
+                 ns_iters=30, seed_index=44),
+        Workload("steps_m100_p32", B=8, H=4, grid_h=20, grid_w=20, d=32, pool=2, dtype="f32", lam=4.0, eps=1e-3,
+                 ns_iters=20, seed_index=45),
     ]
     return cases
 

@@ -614,13 +614,14 @@ def gpu_line(w, x, cpu, args):
     ev.close()
 
     # Untimed breakdown: every stage bracketed by events (the extra event
-    # records lengthen these steps slightly).
+    # records lengthen these steps slightly); the median over the K steps, so
+    # that one stalled step does not move a stage of a few microseconds.
     evs = L.HipEvents(per_step * K)
     for i in range(K):
         L.lapnys_forward_profiled(q, k, v, out, params, ws, evs.handles[i * per_step:(i + 1) * per_step], stream)
     torch.cuda.synchronize()
-    stage_ms = {name: float(np.mean([evs.elapsed_ms(i * per_step + 2 * s, i * per_step + 2 * s + 1)
-                                     for i in range(K)]))
+    stage_ms = {name: float(np.median([evs.elapsed_ms(i * per_step + 2 * s, i * per_step + 2 * s + 1)
+                                       for i in range(K)]))
                 for s, name in enumerate(STAGE_NAMES)}
     evs.close()
 

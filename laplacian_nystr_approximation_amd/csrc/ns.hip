@@ -13,10 +13,10 @@
 //  * m <= 64: one workgroup per problem keeps W and the iterates in LDS and
 //    runs inside the kernel-matrix stage's launch (ns_small.hpp, l1exp.hip).
 //  * 64 < m <= 256 (this file): the products are too large for one LDS; W and
-//    the iterates live in the workspace (L2-resident) and each product is one
-//    batched launch of 64 x 32 output tiles (ns_tile_kernel), two launches per
-//    step.  A general 64 x 64 tile product (gemm64_kernel) forms Y = X (B V)
-//    for these sizes and the optional correction below.
+//    the iterates live in the workspace (L2-resident) and each step is one
+//    batched launch (ns_step_kernel) that forms the next iterate column block
+//    by column block.  A general 64 x 64 tile product (gemm64_kernel) forms
+//    Y = X (B V) for these sizes and the optional correction below.
 //
 // Optional correction (LAPNYS_NS_REFINE, beyond the pages' fixed-count
 // iteration), for either schedule: R = I - W X with float64 accumulation, then
@@ -52,9 +52,17 @@ __global__ __launch_bounds__(256) void wbuild_big_kernel(const float* __restrict
     const int e = threadIdx.x + 256 * i;
     kv[i] = ktp[(size_t)min(a0 + e / D, m - 1) * D + e % D];
   }
+  // Column landmark b: D / 4 16-byte loads (rows are 16-byte aligned).
   float xb[D];
+  const float4* kb4 = reinterpret_cast<const float4*>(ktp + (size_t)min(b, m - 1) * D);
 #pragma unroll
-  for (int t = 0; t < D; ++t) xb[t] = ktp[(size_t)min(b, m - 1) * D + t];
+  for (int t = 0; t < D / 4; ++t) {
+    const float4 v4 = kb4[t];
+    xb[4 * t] = v4.x;
+    xb[4 * t + 1] = v4.y;
+    xb[4 * t + 2] = v4.z;
+    xb[4 * t + 3] = v4.w;
+  }
 #pragma unroll
   for (int i = 0; i < kPer; ++i) kl[threadIdx.x + 256 * i] = kv[i];
   __syncthreads();
@@ -232,14 +240,18 @@ __global__ __launch_bounds__(256) void gemm64_kernel(const float* __restrict__ A
 // the in-LDS schedule for m <= 64, lose here: while the iteration has not yet
 // converged along W's small eigenvalues, the error of a step is carried to
 // the end at the same relative size instead of being squared away.)  MFMA
-// (q, c) takes k = 16 q + 4 lk + c from lane group lk, so every operand is a
-// 16-byte read.  W's rows and X's rows come from global memory (each element
-// read once per workgroup; L2-resident), kStepPD chunks of k ahead of the
-// products; X[:, c] and T_c sit transposed in LDS.  Workgroup b takes problem
-// b % P: when P is a multiple of 8 all workgroups of a problem run on one XCD
-// and share its L2.  Rows and columns past m hold zeros in W and X and stay
-// zero (T_c's identity there meets zero columns of X), and a reduction over
-// all mp terms equals the one over m: the added terms are exact zeros.
+// (q, c), c < 8, takes k = 32 q + 8 lk + c from lane group lk, so every
+// operand is a 16-byte read.  W's rows and X's rows come from global memory
+// (each element read once per workgroup; L2-resident), kStepPD chunks of k
+// ahead of the products; X[:, c] and T_c sit transposed in LDS.  Workgroup b
+// takes problem b % P: when P is a multiple of 8 all workgroups of a problem
+// run on one XCD and share its L2.  Measured at m = 256 and eight problems:
+// 11.5 us per launch, bound by the L2-to-CU transfer of the 384 KB each
+// workgroup reads (W whole and its part of X, about 35 GB/s per CU), not by
+// the MFMAs (5.5 us at their issue rate).  Rows and columns past m hold zeros
+// in W and X and stay zero (T_c's identity there meets zero columns of X),
+// and a reduction over all mp terms equals the one over m: the added terms
+// are exact zeros.
 constexpr int kStepPD = 2;  // 32-deep chunks of k loaded ahead of the products
 
 // Eight consecutive k of one row, k = 32 q + [0, 8) from row (the caller

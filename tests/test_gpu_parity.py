@@ -310,6 +310,13 @@ def _edge_cases():
                  ns_iters=30, seed_index=44),
         Workload("steps_m100_p32", B=8, H=4, grid_h=20, grid_w=20, d=32, pool=2, dtype="f32", lam=4.0, eps=1e-3,
                  ns_iters=20, seed_index=45),
+        # odd problem counts (workgroup b takes problem b % P)
+        Workload("steps_m100_p1", B=1, H=1, grid_h=20, grid_w=20, d=64, pool=2, dtype="bf16", lam=4.0, eps=1e-3,
+                 ns_iters=20, seed_index=46),
+        Workload("steps_m81_p3", B=3, H=1, grid_h=18, grid_w=18, d=32, pool=2, dtype="f32", lam=4.0, eps=1e-3,
+                 ns_iters=24, seed_index=47),
+        Workload("steps_m144_p5", B=1, H=5, grid_h=24, grid_w=24, d=64, pool=2, dtype="bf16", lam=4.0, eps=1e-3,
+                 ns_iters=30, seed_index=48),
     ]
     return cases
 

@@ -100,8 +100,7 @@ __global__ __launch_bounds__(256) void wbuild_big_kernel(const float* __restrict
 // its 1-norm and inf-norm are the same largest column sum and W^T = W: alpha
 // = (max column sum)^2 and X0 = W / alpha, read row-major.  Column sums: one
 // lane per column adds the W build's mp / 16 (<= 16) partial sums in block
-// order, all loaded at once.  X0 is symmetric too, so the row-major X0
-// also serves the first step as its own transpose.
+// order, all loaded at once.
 __global__ __launch_bounds__(256) void alpha_x0_kernel(const float* __restrict__ w, const float* __restrict__ part,
                                                        float* __restrict__ x, int mp) {
   __shared__ float red[4];

@@ -51,14 +51,13 @@ constexpr float kSplitGuard = 64.f;  // largest rho = ||W||_1 max|X| for a split
 // First step after which the guard is evaluated: in exact arithmetic rho is
 // at most 2^(k/2) after k steps, at most 64 up to step 12.
 constexpr int kGuardFrom = 11;
-// LDS of one problem's schedule (floats).  Split steps: X twice (the current
-// iterate and the next) and one per-wavefront slab that holds X^T and then
-// (W X)^T, each as high and low parts, 6 kXB bf16 = 3 kXB floats.  Float32
-// steps (the same bytes): the same three arrays, 3 kMP kLD floats.  Then 256
-// partial sums, alpha and ||W||_1, then W itself (float32, kMP rows of kLD),
-// kept for the whole schedule.
-constexpr int kNsRegion = 3 * kXB;
-static_assert(3 * kMP * kLD <= kNsRegion, "the float32 layout must fit in the split layout's bytes");
+// LDS of one problem's schedule (floats).  Split steps: the row-major copy
+// of X twice (the current iterate and the next), each as high and low parts,
+// 4 kXB bf16 = 2 kXB floats.  Float32 steps (the same bytes): the two copies,
+// 2 kMP kLD floats.  Then 256 partial sums, alpha and ||W||_1, then W itself
+// (float32, kMP rows of kLD), kept for the whole schedule.
+constexpr int kNsRegion = 2 * kXB;
+static_assert(2 * kMP * kLD <= kNsRegion, "the float32 layout must fit in the split layout's bytes");
 constexpr int kNsWOffset = kNsRegion + 260;
 static_assert(kNsWOffset % 4 == 0, "W must start 16-byte aligned");
 constexpr int kNsLdsFloats = kNsWOffset + kMP * kLD;
@@ -80,20 +79,22 @@ __device__ __forceinline__ float wave_max_nonneg(float x) {
 }
 
 // In-LDS schedule for m <= 64: one workgroup of four wavefronts per problem,
-// 73 KB of LDS (so two fit a CU, as two kernel-matrix workgroups do).
+// 55 KB of LDS.
 //
 // Wavefront w owns block column w (columns [16 w, 16 w + 16)) of Q = W X,
 // of S = X Q and of X: each lane holds the 16 entries X[16 bo + 4 lk + r]
-// [16 w + li] (bo, r in [0, 4)) in registers.  A step forms Q's block column
-// (all of W's rows from registers, times X's block column, read from the
-// wavefront's own slab as rows of X^T), puts it into the same slab as rows
-// of Q^T, forms S's block column (all of X's rows, from the shared row-major
-// copy, times Q's block column from the slab), and writes X_next = 2X - S
-// into its slab (as rows of X^T) and into the other row-major copy.  Only
-// the row-major copy is shared between wavefronts, and it alternates between
-// two buffers, so one barrier per step orders everything: a wavefront reads
-// the current copy after every wavefront wrote it, and writes the next copy,
-// which nobody reads until the following barrier.
+// [16 w + li] (bo, r in [0, 4)) in registers, the MFMA result layout.  A
+// step forms Q's block column (all of W's rows from registers, times X's
+// block column from registers), then S's block column (all of X's rows,
+// from the shared row-major copy, times Q's block column, still in
+// registers), and writes X_next = 2X - S into the other row-major copy.
+// Both products take their reduction index in the order the result layout
+// holds it (see the step loops), which is what lets a block column feed the
+// next product without going through LDS.  Only the row-major copy is
+// shared between wavefronts, and it alternates between two buffers, so one
+// barrier per step orders everything: a wavefront reads the current copy
+// after every wavefront wrote it, and writes the next copy, which nobody
+// reads until the following barrier.
 //
 // The float32 steps reduce over k in [0, 4 KS), KS = ceil(m / 4), on fp32
 // MFMA 16x16x4; the split steps over k in [0, 32 KB), KB = ceil(m / 32), on
@@ -108,13 +109,11 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
                                          float* __restrict__ lds, unsigned long long* __restrict__ clk) {
   // Debug stamps (clk non-null): start, first step, end, device wall clock.
   const unsigned long long t_start = clk ? (unsigned long long)wall_clock64() : 0ull;
-  // Float32 layout: the row-major X twice, then the slab array (rows of X^T
-  // or Q^T; wavefront w uses rows [16 w, 16 w + 16)).
+  // Float32 layout: the row-major X twice.
   float* xrf0 = lds;
-  float* tf = lds + 2 * kMP * kLD;
-  // Split layout (same bytes): the same arrays, each high parts then low parts.
+  // Split layout (same bytes): the same two copies, each high parts then low
+  // parts, columns in the split steps' reduction order.
   __bf16* xrb0 = reinterpret_cast<__bf16*>(lds);
-  __bf16* tb = xrb0 + 4 * kXB;
   float* wl = lds + kNsWOffset;  // W, float32
   float* red = lds + kNsRegion;  // [256] partial column sums, then alpha and ||W||_1
   float& alpha_s = red[256];
@@ -221,10 +220,18 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
 
   const int li = lane & 15, lk = lane >> 4;
   const int n16 = iters > kFp32Steps ? iters - kFp32Steps : 0;
-  // W's A operands for the split steps, every row block: bf16 MFMA 16x16x32,
-  // A[li][8 lk + e] of step kb for row block bi = W[16 bi + li][32 kb + 8 lk
-  // + e], KB = ceil(m / 32) steps, as high and low parts.
+  // Reduction index of the split steps' products: bf16 MFMA 16x16x32 kb takes
+  // from lane group lk the eight k = 32 kb + 4 lk + r and 32 kb + 16 + 4 lk + r
+  // (r < 4).  Those are the entries a lane holds of a block column in the
+  // MFMA result layout (rows 16 bo + 4 lk + r, bo = 2 kb and 2 kb + 1), so the
+  // block columns of X and Q are B operands straight from registers.  The
+  // shared row-major copy of X keeps its columns in the order kpos(k), which
+  // puts each lane group's eight at 32 kb + 8 lk + [0, 8): one 16-byte read.
   constexpr int KB = (4 * KS + 31) / 32;
+  auto kpos = [](int k) { return (k & ~31) | (((k & 15) >> 2) << 3) | (((k >> 4) & 1) << 2) | (k & 3); };
+  // W's A operands for the split steps, every row block, as high and low
+  // parts: A[li][8 lk + e] of step kb for row block bi = W[16 bi + li][k(kb,
+  // lk, e)] with k as above.
   u32x4 wh[4][KB], wlo[4][KB];
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)
@@ -232,7 +239,7 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float* wr = wl + (16 * bi + li) * kLD + 32 * kb + 8 * lk + 2 * i;
+        const float* wr = wl + (16 * bi + li) * kLD + 32 * kb + 16 * (i >> 1) + 4 * lk + 2 * (i & 1);
         uint32_t h, l;
         split2(wr[0], wr[1], h, l);
         wh[bi][kb][i] = h;
@@ -250,13 +257,13 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
     for (int r = 0; r < 4; ++r) xr[bo][r] = wl[(16 * w + li) * kLD + 16 * bo + 4 * lk + r] * ralpha;
   __syncthreads();  // X0 read before the stores below (W stays in place)
 
-  const int jc = 16 * w + li;  // the column of X this lane holds (a row of X^T)
-  // This lane's entries of X into the split layout: row-major copy `buf`
-  // (four 16-bit stores per part and row block) and the slab (four
-  // consecutive entries of row jc of X^T, one 8-byte store per part).
+  const int jc = 16 * w + li;  // the column of X this lane holds
+  // This lane's entries of X into the split row-major copy `buf`, column jc
+  // at kpos(jc): sixteen 16-bit stores per part.
   auto store_split = [&](int buf) {
     uint16_t* xh16 = reinterpret_cast<uint16_t*>(xrb0 + buf * 2 * kXB);
     uint16_t* xl16 = xh16 + kXB;
+    const int cp = kpos(jc);
 #pragma unroll
     for (int bo = 0; bo < 4; ++bo) {
       uint32_t h0, l0, h1, l1;
@@ -267,14 +274,12 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
       const uint32_t lw[4] = {l0 & 0xffffu, l0 >> 16, l1 & 0xffffu, l1 >> 16};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        xh16[(i0 + r) * kLB + jc] = (uint16_t)hw[r];
-        xl16[(i0 + r) * kLB + jc] = (uint16_t)lw[r];
+        xh16[(i0 + r) * kLB + cp] = (uint16_t)hw[r];
+        xl16[(i0 + r) * kLB + cp] = (uint16_t)lw[r];
       }
-      *reinterpret_cast<uint2*>(tb + jc * kLB + i0) = make_uint2(h0, h1);
-      *reinterpret_cast<uint2*>(tb + kXB + jc * kLB + i0) = make_uint2(l0, l1);
     }
   };
-  // The same entries into the float32 layout.
+  // The same entries into the float32 row-major copy (natural column order).
   auto store_f32 = [&](int buf) {
     float* xrf = xrf0 + buf * kMP * kLD;
 #pragma unroll
@@ -282,7 +287,23 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
       const int i0 = 16 * bo + 4 * lk;
 #pragma unroll
       for (int r = 0; r < 4; ++r) xrf[(i0 + r) * kLD + jc] = xr[bo][r];
-      *reinterpret_cast<float4*>(&tf[jc * kLD + i0]) = make_float4(xr[bo][0], xr[bo][1], xr[bo][2], xr[bo][3]);
+    }
+  };
+  // A block column in the result layout (v[bo][r] = M[16 bo + 4 lk + r][jc])
+  // as the B operands of the split steps' MFMAs kb: high and low parts.
+  auto b_operands = [&](const float (&v)[4][4], bf16x8 (&bh)[KB], bf16x8 (&bl)[KB]) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      u32x4 h, l;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t hh, ll;
+        split2(v[2 * kb + (i >> 1)][2 * (i & 1)], v[2 * kb + (i >> 1)][2 * (i & 1) + 1], hh, ll);
+        h[i] = hh;
+        l[i] = ll;
+      }
+      bh[kb] = __builtin_bit_cast(bf16x8, h);
+      bl[kb] = __builtin_bit_cast(bf16x8, l);
     }
   };
   if (n16 > 0)
@@ -295,18 +316,24 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
   // ---- split steps ----
   int it = 0, cur = 0;
   while (it < n16) {
-    // Q[:, w] = W X[:, w].  B operand X[32 kb + 8 lk + e][jc] = row jc of X^T
-    // in the slab.  Operand loads are issued before the first product.
+    // The A operands of S = X Q[:, w], X[16 bo + li][k] from the current
+    // row-major copy (every wavefront's, written before the last barrier),
+    // are issued first and arrive during the first product.
+    const __bf16* xh = xrb0 + cur * 2 * kXB;
+    bf16x8 ah[4][KB], al[4][KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int bo = 0; bo < 4; ++bo) {
+        const int oa = (16 * bo + li) * kLB + 32 * kb + 8 * lk;
+        ah[bo][kb] = *reinterpret_cast<const bf16x8*>(xh + oa);
+        al[bo][kb] = *reinterpret_cast<const bf16x8*>(xh + kXB + oa);
+      }
+    // Q[:, w] = W X[:, w], the B operand from this lane's entries of X.
     f32x4 acc[4];
     {
       bf16x8 bh[KB], bl[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int o = jc * kLB + 32 * kb + 8 * lk;
-        bh[kb] = *reinterpret_cast<const bf16x8*>(tb + o);
-        bl[kb] = *reinterpret_cast<const bf16x8*>(tb + kXB + o);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      b_operands(xr, bh, bl);
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi) acc[bi] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -322,38 +349,15 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
           acc[bi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wh[bi][kb]), bh[kb], acc[bi], 0, 0, 0);
       }
     }
-    // acc[bi][r] = Q[16 bi + 4 lk + r][jc]: four consecutive entries of row
-    // jc of Q^T, into the slab over X^T (already read above; the products
-    // these stores depend on consumed it).
-#pragma unroll
-    for (int bi = 0; bi < 4; ++bi) {
-      uint32_t h0, l0, h1, l1;
-      split2(acc[bi][0], acc[bi][1], h0, l0);
-      split2(acc[bi][2], acc[bi][3], h1, l1);
-      const int o = jc * kLB + 16 * bi + 4 * lk;
-      *reinterpret_cast<uint2*>(tb + o) = make_uint2(h0, h1);
-      *reinterpret_cast<uint2*>(tb + kXB + o) = make_uint2(l0, l1);
-    }
-    // S[:, w] = X Q[:, w]: A operand X[16 bo + li][32 kb + 8 lk + e] from the
-    // current row-major copy (every wavefront's, written before the last
-    // barrier), B operand Q[32 kb + 8 lk + e][jc] from the slab (this
-    // wavefront's own stores above, earlier in its LDS order).
+    // S[:, w] = X Q[:, w], the B operand from Q's block column in registers.
     {
-      const __bf16* xh = xrb0 + cur * 2 * kXB;
-      bf16x8 ah[4][KB], al[4][KB], qh[KB], ql[KB];
+      float q[4][4];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int ob = jc * kLB + 32 * kb + 8 * lk;
-        qh[kb] = *reinterpret_cast<const bf16x8*>(tb + ob);
-        ql[kb] = *reinterpret_cast<const bf16x8*>(tb + kXB + ob);
+      for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-        for (int bo = 0; bo < 4; ++bo) {
-          const int oa = (16 * bo + li) * kLB + 32 * kb + 8 * lk;
-          ah[bo][kb] = *reinterpret_cast<const bf16x8*>(xh + oa);
-          al[bo][kb] = *reinterpret_cast<const bf16x8*>(xh + kXB + oa);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
+        for (int r = 0; r < 4; ++r) q[bi][r] = acc[bi][r];
+      bf16x8 qh[KB], ql[KB];
+      b_operands(q, qh, ql);
 #pragma unroll
       for (int bo = 0; bo < 4; ++bo) acc[bo] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -371,7 +375,7 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
 #pragma unroll
       for (int r = 0; r < 4; ++r) xr[bo][r] = 2.f * xr[bo][r] - acc[bo][r];
     // X_next into the other row-major copy (last read before the previous
-    // barrier) and into the slab over Q^T (consumed above).
+    // barrier).
     store_split(cur ^ 1);
     if (it >= kGuardFrom) {
       float amax = 0.f;
@@ -407,50 +411,57 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
       cur = 0;
       __syncthreads();
     }
-    // W's A operands for the float32 steps, every row block: fp32 MFMA
-    // 16x16x4, A[li][lk] of step st for row block bi = W[16 bi + li][4 st + lk].
-    float wreg[4][KS];
+    // fp32 MFMA 16x16x4 (bo, r) takes k = 16 bo + 4 lk + r from lane group
+    // lk: the B operands are this lane's entries of a block column (xr, then
+    // Q's), and W's A operands are W[16 bi + li][16 bo + 4 lk + r].  Row
+    // blocks of the reduction past the last landmark are zero and skipped.
+    constexpr int NBO = (4 * KS + 15) / 16;
+    float wreg[4][NBO][4];
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-      for (int st = 0; st < KS; ++st) wreg[bi][st] = wl[(16 * bi + li) * kLD + 4 * st + lk];
+      for (int bo = 0; bo < NBO; ++bo)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wreg[bi][bo][r] = wl[(16 * bi + li) * kLD + 16 * bo + 4 * lk + r];
     for (; it < iters; ++it) {
+      // The A operands of S = X Q[:, w]: X[16 bo + li][16 bk + 4 lk + r] from
+      // the current row-major copy, one 16-byte read per (bo, bk).
+      const float* xrf = xrf0 + cur * kMP * kLD;
+      float4 xa[4][NBO];
+#pragma unroll
+      for (int bo = 0; bo < 4; ++bo)
+#pragma unroll
+        for (int bk = 0; bk < NBO; ++bk)
+          xa[bo][bk] = *reinterpret_cast<const float4*>(xrf + (16 * bo + li) * kLD + 16 * bk + 4 * lk);
+      // Q[:, w] = W X[:, w].
       f32x4 acc[4];
-      {
-        // Q[:, w] = W X[:, w]; B operand X[4 st + lk][jc] = slab row jc.
-        float xv[KS];
 #pragma unroll
-        for (int st = 0; st < KS; ++st) xv[st] = tf[jc * kLD + 4 * st + lk];
-        __builtin_amdgcn_sched_barrier(0);
+      for (int bi = 0; bi < 4; ++bi) acc[bi] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int bi = 0; bi < 4; ++bi) acc[bi] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int bk = 0; bk < NBO; ++bk)
 #pragma unroll
-        for (int st = 0; st < KS; ++st)
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-          for (int bi = 0; bi < 4; ++bi) acc[bi] = __builtin_amdgcn_mfma_f32_16x16x4f32(wreg[bi][st], xv[st], acc[bi], 0, 0, 0);
-      }
+          for (int bi = 0; bi < 4; ++bi)
+            acc[bi] = __builtin_amdgcn_mfma_f32_16x16x4f32(wreg[bi][bk][r], xr[bk][r], acc[bi], 0, 0, 0);
+      float q[4][4];
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi)
-        *reinterpret_cast<float4*>(&tf[jc * kLD + 16 * bi + 4 * lk]) =
-            make_float4(acc[bi][0], acc[bi][1], acc[bi][2], acc[bi][3]);
-      {
-        // S[:, w] = X Q[:, w]: A operand X[16 bo + li][4 st + lk] from the
-        // current row-major copy, B operand Q[4 st + lk][jc] from the slab.
-        const float* xrf = xrf0 + cur * kMP * kLD;
-        float xa[4][KS], qv[KS];
 #pragma unroll
-        for (int st = 0; st < KS; ++st) {
-          qv[st] = tf[jc * kLD + 4 * st + lk];
+        for (int r = 0; r < 4; ++r) q[bi][r] = acc[bi][r];
+      // S[:, w] = X Q[:, w].
 #pragma unroll
-          for (int bo = 0; bo < 4; ++bo) xa[bo][st] = xrf[(16 * bo + li) * kLD + 4 * st + lk];
-        }
-        __builtin_amdgcn_sched_barrier(0);
+      for (int bo = 0; bo < 4; ++bo) acc[bo] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int bo = 0; bo < 4; ++bo) acc[bo] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int bk = 0; bk < NBO; ++bk) {
 #pragma unroll
-        for (int st = 0; st < KS; ++st)
+        for (int bo = 0; bo < 4; ++bo) acc[bo] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[bo][bk].x, q[bk][0], acc[bo], 0, 0, 0);
 #pragma unroll
-          for (int bo = 0; bo < 4; ++bo) acc[bo] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[bo][st], qv[st], acc[bo], 0, 0, 0);
+        for (int bo = 0; bo < 4; ++bo) acc[bo] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[bo][bk].y, q[bk][1], acc[bo], 0, 0, 0);
+#pragma unroll
+        for (int bo = 0; bo < 4; ++bo) acc[bo] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[bo][bk].z, q[bk][2], acc[bo], 0, 0, 0);
+#pragma unroll
+        for (int bo = 0; bo < 4; ++bo) acc[bo] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[bo][bk].w, q[bk][3], acc[bo], 0, 0, 0);
       }
 #pragma unroll
       for (int bo = 0; bo < 4; ++bo)

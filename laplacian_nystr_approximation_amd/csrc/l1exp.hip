@@ -313,20 +313,40 @@ hipError_t launch_kernel(const Plan& pl, const void* q, const void* k, const voi
 }
 
 // m <= 64: the Newton-Schulz step count KS = ceil(m / 4) and the landmark
-// row blocks LBB = ceil(m / 16) are compile-time constants.
-template <typename T, int D, int KS = 1>
+// row blocks LBB are compile-time constants: ceil(m / 16) for one landmark
+// block, ceil(ceil(m / 2) / 16) when HALF splits the landmarks in two.
+template <typename T, int D, bool HALF, int KS = 1>
 hipError_t launch_fused(const Plan& pl, const void* q, const void* k, const void* v, Work& w, hipStream_t s,
                         Span t) {
   if constexpr (KS < 16) {
-    if ((pl.m + 3) / 4 > KS) return launch_fused<T, D, KS + 1>(pl, q, k, v, w, s, t);
+    if ((pl.m + 3) / 4 > KS) return launch_fused<T, D, HALF, KS + 1>(pl, q, k, v, w, s, t);
   }
-  return launch_kernel<T, D, (KS + 3) / 4, KS>(pl, q, k, v, w, s, t);
+  if constexpr (HALF) {
+    if constexpr (KS >= 8) return launch_kernel<T, D, (2 * KS + 15) / 16, KS>(pl, q, k, v, w, s, t);
+    return hipErrorInvalidValue;  // not planned below 29 landmarks
+  } else {
+    return launch_kernel<T, D, (KS + 3) / 4, KS>(pl, q, k, v, w, s, t);
+  }
 }
 
 template <typename T, int D>
 hipError_t launch_typed(const Plan& pl, const void* q, const void* k, const void* v, Work& w, hipStream_t s,
                         Span t) {
-  if (pl.ns_in_launch) return launch_fused<T, D>(pl, q, k, v, w, s, t);
+  if (pl.ns_in_launch) {
+    // When the solver and kernel-matrix workgroups need more than two rounds
+    // of the CUs (two workgroups of either kind fit a CU), the landmarks go
+    // in two blocks: the half-length kernel-matrix workgroups then fill the
+    // slots that free up while the solver workgroups run, instead of a third
+    // round of full-length ones starting only when the first solvers end.
+    const int cus = cu_count();
+    if (cus > 0 && pl.m >= 29 && pl.P + (long long)pl.groups * pl.P > 2LL * cus) {
+      Plan half = pl;
+      half.lb = (pl.m + 1) / 2;
+      half.jblocks = 2;
+      return launch_fused<T, D, true>(half, q, k, v, w, s, t);
+    }
+    return launch_fused<T, D, false>(pl, q, k, v, w, s, t);
+  }
   // The solver runs on its own: one block of m <= 64 landmarks (up to four
   // 16-row blocks), or landmark blocks of at most 32 (two row blocks).
   if (pl.lb > 48) return launch_kernel<T, D, 4, 0>(pl, q, k, v, w, s, t);

@@ -317,6 +317,13 @@ def _edge_cases():
                  ns_iters=24, seed_index=47),
         Workload("steps_m144_p5", B=1, H=5, grid_h=24, grid_w=24, d=64, pool=2, dtype="bf16", lam=4.0, eps=1e-3,
                  ns_iters=30, seed_index=48),
+        # m <= 64 with more problems than two rounds of the CUs hold: the
+        # kernel-matrix stage splits the landmarks in two blocks (64 -> 32 + 32,
+        # 30 -> 15 + 15)
+        Workload("halfblocks_m64_p260", B=260, H=1, grid_h=8, grid_w=8, d=32, pool=1, dtype="f32", lam=4.0, eps=1e-3,
+                 ns_iters=20, seed_index=49),
+        Workload("halfblocks_m30_p272", B=136, H=2, grid_h=12, grid_w=10, d=64, pool=2, dtype="bf16", lam=4.0,
+                 eps=1e-3, ns_iters=20, seed_index=51),
     ]
     return cases
 

@@ -333,13 +333,16 @@ template <typename T, int D>
 hipError_t launch_typed(const Plan& pl, const void* q, const void* k, const void* v, Work& w, hipStream_t s,
                         Span t) {
   if (pl.ns_in_launch) {
-    // When the solver and kernel-matrix workgroups need more than two rounds
-    // of the CUs (two workgroups of either kind fit a CU), the landmarks go
-    // in two blocks: the half-length kernel-matrix workgroups then fill the
-    // slots that free up while the solver workgroups run, instead of a third
-    // round of full-length ones starting only when the first solvers end.
+    // The landmarks go in two blocks when the solver and kernel-matrix
+    // workgroups need more than two rounds of the CUs (two workgroups of
+    // either kind fit a CU): the half-length kernel-matrix workgroups then
+    // fill the slots that free up while the solver workgroups run, instead of
+    // a third round of full-length ones starting only when the first solvers
+    // end.  They also go in two blocks when even then every workgroup has a
+    // CU of its own (a few problems): the halves run side by side.
     const int cus = cu_count();
-    if (cus > 0 && pl.m >= 29 && pl.P + (long long)pl.groups * pl.P > 2LL * cus) {
+    const long long kwg = (long long)pl.groups * pl.P;
+    if (cus > 0 && pl.m >= 29 && (pl.P + kwg > 2LL * cus || pl.P + 2 * kwg <= cus)) {
       Plan half = pl;
       half.lb = (pl.m + 1) / 2;
       half.jblocks = 2;

@@ -26,8 +26,11 @@ PROBE_SRC = os.path.join(PKG, "probe", "valu_probe.hip")
 PROBE_LIB = os.path.join(PKG, "libvaluprobe.so")
 ARCH = "gfx950"
 
-# Packed fp32 instructions are disabled for every device compile.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed fp32 instructions are disabled for every device compile.  MFMA
+# results are allocated in ordinary vector registers (gfx950 accepts either
+# file): the solver's step loops otherwise copy every accumulator out of the
+# accumulation registers before using it (48 copies per step).
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-result"]
 

@@ -127,75 +127,105 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const float* ktp = kt + (size_t)p * m * D;
 
-  // W = k(K~, K~) + eps I, zero padded.  Lane b holds landmark b in
-  // registers; wavefront w forms rows [16 w, 16 w + 16) four at a time.  The
-  // row landmarks are wave-uniform: they are read with scalar loads into
-  // scalar registers (one wavefront per SIMD issues too slowly to hide LDS
-  // broadcast reads), two 4-feature chunks ahead.  Entry (a, b) sums
-  // |K~_a - K~_b| over even and odd features in increasing order, the same
-  // sums as entry (b, a), so W is bit-symmetric.
+  // W = k(K~, K~) + eps I, zero padded.  The landmark rows are staged in
+  // LDS (in the X region, free until the steps start; rows of D + 4 floats,
+  // so lanes reading different rows hit different banks) and W's LDS rows
+  // are cleared.  Entry (b, a) for a = (b + r) mod m is formed once, by lane
+  // b of the wavefront that owns the shift r (r = w, w + 4, ... up to m / 2),
+  // from landmark b in registers and landmark a read from LDS, and written to
+  // both (b, a) and (a, b): W is bit-symmetric by construction.  The sum runs
+  // over even and odd features in increasing order, four entries at a time
+  // (eight independent chains), with the next two 4-feature chunks of their
+  // rows loaded ahead.
   {
-    constexpr int NC = D / 4;  // 4-feature chunks
+    constexpr int NC = D / 4;   // 4-feature chunks
+    constexpr int KSTR = D + 4;  // staged row stride (floats)
+    float* ks = lds;
+    {
+      constexpr int kV = 64 * D / 4 / 256;  // float4 loads per lane, at most
+      const int n4 = m * D / 4;
+      const float4* k4 = reinterpret_cast<const float4*>(ktp);
+      float4 kv[kV];
+#pragma unroll
+      for (int i = 0; i < kV; ++i) kv[i] = k4[min(tid + 256 * i, n4 - 1)];
+#pragma unroll
+      for (int i = 0; i < kV; ++i) {
+        const int e4 = tid + 256 * i;
+        if (e4 < n4) *reinterpret_cast<float4*>(ks + (e4 / NC) * KSTR + 4 * (e4 % NC)) = kv[i];
+      }
+      for (int e = tid; e < kMP * kLD; e += 256) wl[e] = 0.f;
+    }
+    __syncthreads();
     const int b = lane;
-    float csum = 0.f;  // |W[a][b]| over this wavefront's rows a, in increasing a
+    const bool live = b < m;
     float xb_[D];
     {
-      const float4* kb4 = reinterpret_cast<const float4*>(ktp + (size_t)min(b, m - 1) * D);
+      const float* kb = ks + min(b, m - 1) * KSTR;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const float4 v4 = kb4[c];
+        const float4 v4 = *reinterpret_cast<const float4*>(kb + 4 * c);
         xb_[4 * c] = v4.x;
         xb_[4 * c + 1] = v4.y;
         xb_[4 * c + 2] = v4.z;
         xb_[4 * c + 3] = v4.w;
       }
     }
-    for (int a0 = 16 * w; a0 < 16 * w + 16; a0 += 4) {
-      if (a0 < m) {
-        float s0[4] = {0.f, 0.f, 0.f, 0.f}, s1[4] = {0.f, 0.f, 0.f, 0.f};
-        const float* ka[4];
+    const int rmax = m / 2;
+    for (int r0 = w; r0 <= rmax; r0 += 16) {  // shifts r0 + 4 u, u < 4 (wave-uniform)
+      float s0[4] = {0.f, 0.f, 0.f, 0.f}, s1[4] = {0.f, 0.f, 0.f, 0.f};
+      int arow[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) ka[u] = ktp + (size_t)min(a0 + u, m - 1) * D;
-        float4 kv[3][4];  // ring of three chunks: the current one and the next two
+      for (int u = 0; u < 4; ++u) {
+        const int a = b + r0 + 4 * u;
+        arow[u] = min(a >= m ? a - m : a, m - 1);
+      }
+      const float* ka[4];
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+      for (int u = 0; u < 4; ++u) ka[u] = ks + arow[u] * KSTR;
+      float4 kv[3][4];  // ring of three chunks: the current one and the next two
 #pragma unroll
-          for (int u = 0; u < 4; ++u) kv[c][u] = *reinterpret_cast<const float4*>(ka[u] + 4 * c);
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          if (c + 2 < NC) {
+        for (int u = 0; u < 4; ++u) kv[c][u] = *reinterpret_cast<const float4*>(ka[u] + 4 * c);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) kv[(c + 2) % 3][u] = *reinterpret_cast<const float4*>(ka[u] + 4 * (c + 2));
-          }
+      for (int c = 0; c < NC; ++c) {
+        if (c + 2 < NC) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const float4 r = kv[c % 3][u];
-            s0[u] += fabsf(r.x - xb_[4 * c]);
-            s1[u] += fabsf(r.y - xb_[4 * c + 1]);
-            s0[u] += fabsf(r.z - xb_[4 * c + 2]);
-            s1[u] += fabsf(r.w - xb_[4 * c + 3]);
-          }
-          // The sums are in/out operands here, so the loads of a chunk stay
-          // two chunks ahead of its arithmetic (bounded registers).
-          asm volatile("" : "+v"(s0[0]), "+v"(s0[1]), "+v"(s0[2]), "+v"(s0[3]), "+v"(s1[0]), "+v"(s1[1]),
-                       "+v"(s1[2]), "+v"(s1[3])::"memory");
+          for (int u = 0; u < 4; ++u) kv[(c + 2) % 3][u] = *reinterpret_cast<const float4*>(ka[u] + 4 * (c + 2));
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int a = a0 + u;
-          float val = 0.f;
-          if (a < m && b < m) {
-            val = exp2f((s0[u] + s1[u]) * scale);
-            if (a == b) val += eps;
-          }
-          wl[a * kLD + b] = val;
-          csum += val;  // entries are positive
+          const float4 r = kv[c % 3][u];
+          s0[u] += fabsf(r.x - xb_[4 * c]);
+          s1[u] += fabsf(r.y - xb_[4 * c + 1]);
+          s0[u] += fabsf(r.z - xb_[4 * c + 2]);
+          s1[u] += fabsf(r.w - xb_[4 * c + 3]);
         }
-      } else {
+        // The sums are in/out operands here, so the loads of a chunk stay
+        // two chunks ahead of its arithmetic (bounded registers).
+        asm volatile("" : "+v"(s0[0]), "+v"(s0[1]), "+v"(s0[2]), "+v"(s0[3]), "+v"(s1[0]), "+v"(s1[1]),
+                     "+v"(s1[2]), "+v"(s1[3])::"memory");
+      }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) wl[(a0 + u) * kLD + b] = 0.f;
+      for (int u = 0; u < 4; ++u) {
+        const int r = r0 + 4 * u;
+        // At r = m / 2 (m even) lanes b and b + r form the same pair: the
+        // lower one writes it.
+        if (live && r <= rmax && (2 * r != m || b < r)) {
+          const int a = arow[u];
+          float val = exp2f((s0[u] + s1[u]) * scale);
+          if (r == 0) val += eps;
+          wl[b * kLD + a] = val;
+          wl[a * kLD + b] = val;
+        }
       }
     }
+    __syncthreads();
+    // Column sums of this wavefront's rows 16 w + [0, 16), in increasing row
+    // order (entries are positive).
+    float csum = 0.f;
+#pragma unroll
+    for (int a = 0; a < 16; ++a) csum += wl[(16 * w + a) * kLD + b];
     red[w * kMP + b] = csum;
   }
   __syncthreads();
@@ -258,24 +288,40 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
   __syncthreads();  // X0 read before the stores below (W stays in place)
 
   const int jc = 16 * w + li;  // the column of X this lane holds
-  // This lane's entries of X into the split row-major copy `buf`, column jc
-  // at kpos(jc): sixteen 16-bit stores per part.
-  auto store_split = [&](int buf) {
+  // A block column in the result layout (v[bo][r] = M[16 bo + 4 lk + r][jc])
+  // split into bf16 high and low parts, two entries per word: words (bo, 0)
+  // and (bo, 1) hold rows r = 0, 1 and r = 2, 3.
+  auto split_cols = [&](const float (&v)[4][4], uint32_t (&hw)[4][2], uint32_t (&lw)[4][2]) {
+#pragma unroll
+    for (int bo = 0; bo < 4; ++bo) {
+      split2(v[bo][0], v[bo][1], hw[bo][0], lw[bo][0]);
+      split2(v[bo][2], v[bo][3], hw[bo][1], lw[bo][1]);
+    }
+  };
+  // The same words as the B operands of the split steps' MFMAs kb (rows
+  // 32 kb + [0, 32) of the block column: row blocks 2 kb and 2 kb + 1).
+  auto b_words = [&](const uint32_t (&hw)[4][2], const uint32_t (&lw)[4][2], bf16x8 (&bh)[KB], bf16x8 (&bl)[KB]) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      bh[kb] = __builtin_bit_cast(bf16x8, u32x4{hw[2 * kb][0], hw[2 * kb][1], hw[2 * kb + 1][0], hw[2 * kb + 1][1]});
+      bl[kb] = __builtin_bit_cast(bf16x8, u32x4{lw[2 * kb][0], lw[2 * kb][1], lw[2 * kb + 1][0], lw[2 * kb + 1][1]});
+    }
+  };
+  // This lane's entries of X (as split words) into the split row-major copy
+  // `buf`, column jc at kpos(jc): sixteen 16-bit stores per part.
+  auto store_split = [&](int buf, const uint32_t (&hw)[4][2], const uint32_t (&lw)[4][2]) {
     uint16_t* xh16 = reinterpret_cast<uint16_t*>(xrb0 + buf * 2 * kXB);
     uint16_t* xl16 = xh16 + kXB;
     const int cp = kpos(jc);
 #pragma unroll
     for (int bo = 0; bo < 4; ++bo) {
-      uint32_t h0, l0, h1, l1;
-      split2(xr[bo][0], xr[bo][1], h0, l0);
-      split2(xr[bo][2], xr[bo][3], h1, l1);
       const int i0 = 16 * bo + 4 * lk;
-      const uint32_t hw[4] = {h0 & 0xffffu, h0 >> 16, h1 & 0xffffu, h1 >> 16};
-      const uint32_t lw[4] = {l0 & 0xffffu, l0 >> 16, l1 & 0xffffu, l1 >> 16};
+      const uint32_t h4[4] = {hw[bo][0] & 0xffffu, hw[bo][0] >> 16, hw[bo][1] & 0xffffu, hw[bo][1] >> 16};
+      const uint32_t l4[4] = {lw[bo][0] & 0xffffu, lw[bo][0] >> 16, lw[bo][1] & 0xffffu, lw[bo][1] >> 16};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        xh16[(i0 + r) * kLB + cp] = (uint16_t)hw[r];
-        xl16[(i0 + r) * kLB + cp] = (uint16_t)lw[r];
+        xh16[(i0 + r) * kLB + cp] = (uint16_t)h4[r];
+        xl16[(i0 + r) * kLB + cp] = (uint16_t)l4[r];
       }
     }
   };
@@ -289,27 +335,15 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
       for (int r = 0; r < 4; ++r) xrf[(i0 + r) * kLD + jc] = xr[bo][r];
     }
   };
-  // A block column in the result layout (v[bo][r] = M[16 bo + 4 lk + r][jc])
-  // as the B operands of the split steps' MFMAs kb: high and low parts.
-  auto b_operands = [&](const float (&v)[4][4], bf16x8 (&bh)[KB], bf16x8 (&bl)[KB]) {
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      u32x4 h, l;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t hh, ll;
-        split2(v[2 * kb + (i >> 1)][2 * (i & 1)], v[2 * kb + (i >> 1)][2 * (i & 1) + 1], hh, ll);
-        h[i] = hh;
-        l[i] = ll;
-      }
-      bh[kb] = __builtin_bit_cast(bf16x8, h);
-      bl[kb] = __builtin_bit_cast(bf16x8, l);
-    }
-  };
-  if (n16 > 0)
-    store_split(0);
-  else
+  // The split words of this lane's entries of the current iterate: written
+  // to the row-major copy and reused as the next step's B operands.
+  uint32_t xhw[4][2], xlw[4][2];
+  if (n16 > 0) {
+    split_cols(xr, xhw, xlw);
+    store_split(0, xhw, xlw);
+  } else {
     store_f32(0);
+  }
   __syncthreads();
   const unsigned long long t_steps = clk ? (unsigned long long)wall_clock64() : 0ull;
 
@@ -333,7 +367,7 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
     f32x4 acc[4];
     {
       bf16x8 bh[KB], bl[KB];
-      b_operands(xr, bh, bl);
+      b_words(xhw, xlw, bh, bl);
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi) acc[bi] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -356,8 +390,10 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
       for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
         for (int r = 0; r < 4; ++r) q[bi][r] = acc[bi][r];
+      uint32_t qhw[4][2], qlw[4][2];
+      split_cols(q, qhw, qlw);
       bf16x8 qh[KB], ql[KB];
-      b_operands(q, qh, ql);
+      b_words(qhw, qlw, qh, ql);
 #pragma unroll
       for (int bo = 0; bo < 4; ++bo) acc[bo] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -376,7 +412,8 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
       for (int r = 0; r < 4; ++r) xr[bo][r] = 2.f * xr[bo][r] - acc[bo][r];
     // X_next into the other row-major copy (last read before the previous
     // barrier).
-    store_split(cur ^ 1);
+    split_cols(xr, xhw, xlw);
+    store_split(cur ^ 1, xhw, xlw);
     if (it >= kGuardFrom) {
       float amax = 0.f;
 #pragma unroll

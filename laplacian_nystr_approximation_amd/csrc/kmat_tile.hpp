@@ -92,6 +92,30 @@ struct VHalf {
   }
 };
 
+// bf16 V: each pair of consecutive values of a step is loaded straight into
+// the two halves of one register (the packed MFMA operand word), so a half
+// holds 16 registers instead of 32.
+template <int D>
+struct VHalf<uint16_t, D> {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 w[kTT / 16];
+  __device__ __forceinline__ void issue(const uint16_t* __restrict__ vcol, int t0, int lk, int h, int tok_last) {
+#pragma unroll
+    for (int sp = 0; sp < 4; ++sp)
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const int t = t0 + 128 * h + 32 * sp + 8 * lk + 2 * e2;
+        w[4 * sp + e2].x = vcol[min(t, tok_last) * D];
+        w[4 * sp + e2].y = vcol[min(t + 1, tok_last) * D];
+      }
+  }
+  __device__ __forceinline__ void operand(int sp, u32x4& hi, u32x4& lo) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hi[i] = __builtin_bit_cast(uint32_t, w[4 * sp + i]);
+    (void)lo;
+  }
+};
+
 // Column statistics of the tile's C (float32 rows of stride kTP at tl) and
 // the C^T store.  Lane l takes tokens 4 l + [0, 4) of the tile: one 16-byte
 // LDS read and one 16-byte store of the C^T row per landmark.  Wavefront w

@@ -124,8 +124,11 @@ __device__ __forceinline__ void kernel_row(const float (&x)[D], const float* __r
 // One workgroup's share of the stage: landmark block jb (lb <= lbmax
 // landmarks from j0 = jb * lbmax), tile group g, problem p.  LBB = 16-row
 // blocks per landmark block (lbmax rounded up to 16, over 16).  tl: the
-// workgroup's LDS, (lbmax + 1) * kTileRow + lbmax * D floats.
-template <typename T, int D, int LBB>
+// workgroup's LDS, (lbmax + 1) * kTileRow + lbmax * D floats.  PART 0 forms
+// both C and B of each tile; PART 1 only C (statistics and the C^T store),
+// PART 2 only B (the B V partial; its V operands are then issued after the B
+// rows, so they do not hold registers during them).
+template <typename T, int D, int LBB, int PART = 0>
 __device__ __forceinline__ void l1exp_body(const T* __restrict__ q, const T* __restrict__ k,
                                            const T* __restrict__ v, const float* __restrict__ kt,
                                            float* __restrict__ ct, float2* __restrict__ stats,
@@ -175,20 +178,26 @@ __device__ __forceinline__ void l1exp_body(const T* __restrict__ q, const T* __r
     const size_t row = prob + (size_t)(t0 + (valid ? tid : 0)) * D;
 
     // ---- C = k(Q, K~) ----
-    issue_row<T, D>(q + row, valid, raw);
-    widen_row<D>(raw, x);
-    __syncthreads();  // tile buffer free (previous tile's MFMA reads done)
-    kernel_row<D, false>(x, kl, kg, lb, scale, tl, lbmax + 1, tid, valid);
-    __syncthreads();
+    if constexpr (PART != 2) {
+      issue_row<T, D>(q + row, valid, raw);
+      widen_row<D>(raw, x);
+      __syncthreads();  // tile buffer free (previous tile's MFMA reads done)
+      kernel_row<D, false>(x, kl, kg, lb, scale, tl, lbmax + 1, tid, valid);
+      __syncthreads();
+    }
+    if constexpr (PART == 1) {
+      tile_stats_store(tl, stats, ct, p, ntiles, tile, m, j0, lb, ldc, t0, nvalid, lane, w);
+      continue;
+    }
 
     // The key row and this lane's V operands are issued now and arrive while
     // the statistics pass runs.
     issue_row<T, D>(k + row, valid, raw);
     VHalf<T, D> v0;
-    v0.issue(vcol, t0, bv.lk, 0, tok_last);
+    if constexpr (PART == 0) v0.issue(vcol, t0, bv.lk, 0, tok_last);
 
     // ---- column statistics of C over the tile, and the C^T store ----
-    tile_stats_store(tl, stats, ct, p, ntiles, tile, m, j0, lb, ldc, t0, nvalid, lane, w);
+    if constexpr (PART == 0) tile_stats_store(tl, stats, ct, p, ntiles, tile, m, j0, lb, ldc, t0, nvalid, lane, w);
 
     // ---- B = k(K~, K), kept on chip ----
     widen_row<D>(raw, x);
@@ -198,13 +207,14 @@ __device__ __forceinline__ void l1exp_body(const T* __restrict__ q, const T* __r
     __syncthreads();
 
     // ---- B V partial: acc[landmark][feature] += sum over the tile's tokens ----
+    if constexpr (PART == 2) v0.issue(vcol, t0, bv.lk, 0, tok_last);
     VHalf<T, D> v1;
     v1.issue(vcol, t0, bv.lk, 1, tok_last);
     bv.accumulate(bh, bl, v0, v1);
   }
 
   // Partial B V of this tile group: rows j0 + [0, lb) of bvpart[p][g].
-  bv.store(bvpart + ((size_t)p * groups + g) * m * D, j0, lb);
+  if constexpr (PART != 1) bv.store(bvpart + ((size_t)p * groups + g) * m * D, j0, lb);
   if (kclk != nullptr && threadIdx.x == 0) atomicMax(kclk + 1, (unsigned long long)wall_clock64());
 }
 
@@ -242,6 +252,45 @@ __global__ __launch_bounds__(kTT) void l1exp_kernel(
                         lds, kclk);
 }
 
+// The same launch with the work of each (landmark block, tile group) in two
+// workgroups: one forms C (with its statistics and the C^T store), the other
+// B (with the B V partial, its V operands loaded after the B rows).  Neither
+// holds the other's registers, so the launch fits three wavefronts per SIMD
+// (162 registers, the solver's; 53 KB of LDS with the landmarks in two
+// blocks), for shapes where the unsplit workgroups would leave most CUs a
+// single one (see launch_typed).  Grid: nns + 8 S ceil(units / 8) workgroups
+// (plus nns empty ones), S = 2 jblocks, unit u = g + groups p: workgroup b =
+// (u / 8) 8 S + 8 sub + u % 8 takes sub = jb + jblocks part of unit u, so
+// the S workgroups of a unit run on one XCD and share its L2.
+template <typename T, int D, int LBB, int KS>
+__global__ __launch_bounds__(kTT) void l1exp_split_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ kt,
+    float* __restrict__ ct, float2* __restrict__ stats, float* __restrict__ bvpart, float* __restrict__ bt,
+    float* __restrict__ wout, float* __restrict__ xout, int N, int ldc, int m, int lbmax, int ntiles, int tpg, int groups, int jblocks,
+    float scale, float eps, int iters, int nns, int gap, unsigned long long* __restrict__ nsclk,
+    unsigned long long* __restrict__ kclk) {
+  extern __shared__ __align__(16) float lds[];
+  int b = blockIdx.x;
+  if constexpr (KS > 0) {
+    if (b < nns) {
+      ns_detail::ns_small<D, KS>(kt, wout, xout, m, scale, eps, iters, b, lds, nsclk);
+      return;
+    }
+    if (b >= gap && b < gap + nns) return;
+    b -= b >= gap ? 2 * nns : nns;
+  }
+  const int S = 2 * jblocks;
+  const int u = (b / (8 * S)) * 8 + b % 8, sub = (b / 8) % S;
+  if (u >= groups * nns) return;
+  const int jb = sub % jblocks, part = sub / jblocks, g = u % groups, p = u / groups;
+  if (part == 0)
+    l1exp_body<T, D, LBB, 1>(q, k, v, kt, ct, stats, bvpart, bt, N, ldc, m, lbmax, ntiles, tpg, groups, scale, jb, g,
+                             p, lds, kclk);
+  else
+    l1exp_body<T, D, LBB, 2>(q, k, v, kt, ct, stats, bvpart, bt, N, ldc, m, lbmax, ntiles, tpg, groups, scale, jb, g,
+                             p, lds, kclk);
+}
+
 // The same stage without the solver at landmark blocks of at most 32 (m > 64,
 // and the forms whose solver runs beside it), with registers held to three
 // wavefronts per SIMD: the L1 loop issues faster with three than with two,
@@ -275,15 +324,17 @@ int cu_count() {
   return cached[dev];
 }
 
-template <typename T, int D, int LBB, int KS>
+template <typename T, int D, int LBB, int KS, bool SPLIT = false>
 hipError_t launch_kernel(const Plan& pl, const void* q, const void* k, const void* v, Work& w, hipStream_t s,
                          Span t) {
+  static_assert(!SPLIT || KS > 0, "the split launch carries the solver");
   const int lbmax = pl.lb;
   size_t floats = (size_t)(lbmax + 1) * kTileRow + (size_t)lbmax * D;
   if (KS > 0 && floats < (size_t)ns_detail::kNsLdsFloats) floats = ns_detail::kNsLdsFloats;
   const size_t shmem = floats * sizeof(float);
   auto kern = l1exp_kernel<T, D, LBB, KS>;
   if constexpr (KS == 0 && LBB <= 2) kern = l1exp_solo_kernel<T, D, LBB>;
+  if constexpr (SPLIT) kern = l1exp_split_kernel<T, D, LBB, KS>;
   if (shmem > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
@@ -296,6 +347,7 @@ hipError_t launch_kernel(const Plan& pl, const void* q, const void* k, const voi
   // only the balance changes.)
   const int nns = KS > 0 ? pl.P : 0;
   long long grid = (long long)nns + (long long)pl.jblocks * pl.groups * pl.P;
+  if (SPLIT) grid = (long long)nns + ((long long)pl.groups * pl.P + 7) / 8 * 8 * 2 * pl.jblocks;
   int gap = 0x7fffffff;
   if (nns > 0) {
     const int cus = cu_count();
@@ -315,14 +367,14 @@ hipError_t launch_kernel(const Plan& pl, const void* q, const void* k, const voi
 // m <= 64: the Newton-Schulz step count KS = ceil(m / 4) and the landmark
 // row blocks LBB are compile-time constants: ceil(m / 16) for one landmark
 // block, ceil(ceil(m / 2) / 16) when HALF splits the landmarks in two.
-template <typename T, int D, bool HALF, int KS = 1>
+template <typename T, int D, bool HALF, bool SPLIT = false, int KS = 1>
 hipError_t launch_fused(const Plan& pl, const void* q, const void* k, const void* v, Work& w, hipStream_t s,
                         Span t) {
   if constexpr (KS < 16) {
-    if ((pl.m + 3) / 4 > KS) return launch_fused<T, D, HALF, KS + 1>(pl, q, k, v, w, s, t);
+    if ((pl.m + 3) / 4 > KS) return launch_fused<T, D, HALF, SPLIT, KS + 1>(pl, q, k, v, w, s, t);
   }
   if constexpr (HALF) {
-    if constexpr (KS >= 8) return launch_kernel<T, D, (2 * KS + 15) / 16, KS>(pl, q, k, v, w, s, t);
+    if constexpr (KS >= 8) return launch_kernel<T, D, (2 * KS + 15) / 16, KS, SPLIT>(pl, q, k, v, w, s, t);
     return hipErrorInvalidValue;  // not planned below 29 landmarks
   } else {
     return launch_kernel<T, D, (KS + 3) / 4, KS>(pl, q, k, v, w, s, t);
@@ -339,14 +391,21 @@ hipError_t launch_typed(const Plan& pl, const void* q, const void* k, const void
     // fill the slots that free up while the solver workgroups run, instead of
     // a third round of full-length ones starting only when the first solvers
     // end.  They also go in two blocks when even then every workgroup has a
-    // CU of its own (a few problems): the halves run side by side.
+    // CU of its own (a few problems): the halves run side by side.  In
+    // between, when the unsplit workgroups would average at most 1.5 per CU
+    // the solvers leave free (most of those CUs then run one workgroup, one
+    // wavefront per SIMD), the two blocks' C and B halves run as separate
+    // workgroups at three wavefronts per SIMD (l1exp_split_kernel): the
+    // 28x28 workload (64 problems) went from 68.6 to 62.9 us; at the 56x56
+    // workloads (1.86 per free CU) the split was slower (80.3 against 71.9).
     const int cus = cu_count();
     const long long kwg = (long long)pl.groups * pl.P;
-    if (cus > 0 && pl.m >= 29 && (pl.P + kwg > 2LL * cus || pl.P + 2 * kwg <= cus)) {
+    if (cus > 0 && pl.m >= 29) {
       Plan half = pl;
       half.lb = (pl.m + 1) / 2;
       half.jblocks = 2;
-      return launch_fused<T, D, true>(half, q, k, v, w, s, t);
+      if (pl.P + kwg > 2LL * cus || pl.P + 2 * kwg <= cus) return launch_fused<T, D, true>(half, q, k, v, w, s, t);
+      if (pl.P < cus && 2 * kwg <= 3LL * (cus - pl.P)) return launch_fused<T, D, true, true>(half, q, k, v, w, s, t);
     }
     return launch_fused<T, D, false>(pl, q, k, v, w, s, t);
   }

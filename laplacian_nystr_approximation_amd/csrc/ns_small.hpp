@@ -54,11 +54,17 @@ constexpr int kGuardFrom = 11;
 // LDS of one problem's schedule (floats).  Split steps: the row-major copy
 // of X twice (the current iterate and the next), each as high and low parts,
 // 4 kXB bf16 = 2 kXB floats.  Float32 steps (the same bytes): the two copies,
-// 2 kMP kLD floats.  Then 256 partial sums, alpha and ||W||_1, then W itself
-// (float32, kMP rows of kLD), kept for the whole schedule.
+// 2 kMP kLD floats.  Before the steps the same region holds the staged
+// landmark rows (kMP rows of D + 4 floats), then 256 partial column sums,
+// alpha and ||W||_1 (at kNsRed).  Then W itself (float32, kMP rows of kLD),
+// kept for the whole schedule; its padding columns 64..67 of row 0 carry the
+// four wavefronts' max|X| for the guard.  54272 bytes in all: three such
+// workgroups fit in a CU's 160 KB.
 constexpr int kNsRegion = 2 * kXB;
 static_assert(2 * kMP * kLD <= kNsRegion, "the float32 layout must fit in the split layout's bytes");
-constexpr int kNsWOffset = kNsRegion + 260;
+constexpr int kNsRed = kMP * (64 + 4);
+static_assert(kNsRed + 260 <= kNsRegion, "the set-up sums must fit beside the staged landmarks");
+constexpr int kNsWOffset = kNsRegion;
 static_assert(kNsWOffset % 4 == 0, "W must start 16-byte aligned");
 constexpr int kNsLdsFloats = kNsWOffset + kMP * kLD;
 
@@ -115,9 +121,10 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
   // parts, columns in the split steps' reduction order.
   __bf16* xrb0 = reinterpret_cast<__bf16*>(lds);
   float* wl = lds + kNsWOffset;  // W, float32
-  float* red = lds + kNsRegion;  // [256] partial column sums, then alpha and ||W||_1
+  float* red = lds + kNsRed;     // [256] partial column sums, then alpha and ||W||_1
   float& alpha_s = red[256];
   float& norm1_s = red[257];
+  float* gmax = wl + kMP;        // the guard's four max|X| (W's row 0 padding)
 
   // Beside the kernel-matrix workgroups on the same CUs, the solver's chain
   // of dependent products is the longer one: its wavefronts take issue
@@ -421,15 +428,15 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
 #pragma unroll
         for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(xr[bo][r]));
       amax = wave_max_nonneg(amax);
-      if (lane == 0) red[w] = amax;
+      if (lane == 0) gmax[w] = amax;
     }
     __syncthreads();
     cur ^= 1;
     // The guard: the same four values in every wavefront, so the decision
-    // is uniform across the workgroup.  red[0..3] is next written after
+    // is uniform across the workgroup.  gmax[0..3] is next written after
     // every wavefront has passed the next barrier, and so this read.
     if (it >= kGuardFrom) {
-      const float4 mx = *reinterpret_cast<const float4*>(red);
+      const float4 mx = *reinterpret_cast<const float4*>(gmax);
       if (norm1 * fmaxf(fmaxf(mx.x, mx.y), fmaxf(mx.z, mx.w)) > kSplitGuard) {
         ++it;
         break;

@@ -29,6 +29,8 @@ def _cases():
         (Workload("bwd_single_landmark_6x6", grid_h=6, grid_w=6, d=64, pool=6, dtype="f32", **base), None),
         (WORKLOADS["stage3_14x14_bf16"], [0, 7, 319]),
         (WORKLOADS["stage1_56x56_f32"], [0, 31]),
+        # the kernel-matrix stage's C and B halves in separate workgroups
+        (WORKLOADS["stage2_28x28_bf16"], [0, 37, 63]),
         (dataclasses.replace(WORKLOADS["tiny_f32"], name="tiny_f32_plain", ns_plain=True), None),
         # the tiled solver's sizes: m = 81, 100 and 256
         (Workload("bwd_m81_18x18_p2", grid_h=18, grid_w=18, d=64, pool=2, dtype="f32", **base), None),

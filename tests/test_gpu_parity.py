@@ -324,6 +324,13 @@ def _edge_cases():
                  ns_iters=20, seed_index=49),
         Workload("halfblocks_m30_p272", B=136, H=2, grid_h=12, grid_w=10, d=64, pool=2, dtype="bf16", lam=4.0,
                  eps=1e-3, ns_iters=20, seed_index=51),
+        # m <= 64 with the unsplit workgroups at most 1.5 per CU the solvers
+        # leave: the C and B halves of the two landmark blocks run as separate
+        # workgroups (float32 d = 32 with a 16-token last tile; bf16 m = 36)
+        Workload("cbsplit_f32_d32_p48", B=48, H=1, grid_h=28, grid_w=28, d=32, pool=4, dtype="f32", lam=4.0,
+                 eps=1e-3, ns_iters=20, seed_index=52),
+        Workload("cbsplit_bf16_m36_p64", B=32, H=2, grid_h=24, grid_w=24, d=64, pool=4, dtype="bf16", lam=4.0,
+                 eps=1e-3, ns_iters=20, seed_index=53),
     ]
     return cases
 

@@ -540,7 +540,7 @@ def main(argv=None):
 
 PRECISION = ("float32 values throughout (bf16 inputs widen exactly); L1 distances, exp, W and whitening statistics "
              "on the float32 vector ALU (statistics merged in float64, landmarks summed in float64); B V, Z Y and "
-             "the Newton-Schulz steps for m <= 64 (all but the last two) on bf16 MFMA with every float32 operand "
+             "the Newton-Schulz steps for m <= 64 (all but the last) on bf16 MFMA with every float32 operand "
              "split into bf16 high and low parts, three partial products accumulated in float32; Y = X (B V), the "
              "last Newton-Schulz steps and the m > 64 solver on fp32 MFMA")
 

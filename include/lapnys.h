@@ -32,7 +32,7 @@
  * run on bf16 MFMA with every float32 operand split into a bf16 high part and
  * a bf16 low part and three of the four partial products (hi*hi, hi*lo,
  * lo*hi) accumulated in float32: each product keeps all but about 2^-16 of
- * its value.  The last Newton-Schulz steps (at least two, and every step once
+ * its value.  The last Newton-Schulz steps (at least one, and every step once
  * ||W||_1 max|X| exceeds 64), Y = X (B V), the m > 64 solver and the CG
  * solver use float32 products (fp32 MFMA).  Measured against the float64
  * oracle the output stays within 1e-4 of max|O| (normwise) for float32 and

@@ -227,8 +227,8 @@ __device__ __forceinline__ void l1exp_body(const T* __restrict__ q, const T* __r
 // the kernel-matrix ones numbered landmark block fastest, then tile group,
 // then problem.
 // Dynamic LDS: the larger of the two parts' needs, 16-byte aligned.  The
-// register budget of the union of both parts is held to three wavefronts per
-// SIMD (the L1 loop needs at least two to dual-issue).
+// union of both parts takes 202 registers at d = 64: two wavefronts per SIMD
+// (the L1 loop needs at least two to dual-issue).
 template <typename T, int D, int LBB, int KS>
 __global__ __launch_bounds__(kTT) void l1exp_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ kt,

@@ -89,7 +89,7 @@ __device__ __forceinline__ float wave_max_nonneg(float x) {
 }
 
 // In-LDS schedule for m <= 64: one workgroup of four wavefronts per problem,
-// 55 KB of LDS.
+// 54272 bytes of LDS.
 //
 // Wavefront w owns block column w (columns [16 w, 16 w + 16)) of Q = W X,
 // of S = X Q and of X: each lane holds the 16 entries X[16 bo + 4 lk + r]

@@ -16,7 +16,7 @@
 // tile of 256 consecutive tokens of one problem and a block of landmarks,
 // whose rows it stages in LDS.  Every landmark value reaches all 64 lanes of
 // a wavefront as a wave-uniform LDS broadcast read (one 16-byte read gives
-// four features of one landmark, double-buffered one 4-feature chunk ahead),
+// four features of one landmark, loaded two 4-feature chunks ahead),
 // so the inner loop is one subtract and one add with an |.| source modifier
 // per (token, landmark, feature), eight independent sums at a time (four
 // landmarks, even and odd features).  This stage is not a dense contraction;
@@ -55,9 +55,12 @@ constexpr int kSrc[4] = {kLds, kLds, kLds, kLds};
 // rows of stride kRB, followed by a zero row lb.  kl: the block's landmark
 // rows in LDS; kg: the same rows in global memory.  Four landmarks at a time, each
 // with two partial sums (even / odd features), give eight independent add
-// chains; the operands of the next 4-feature chunk are loaded while the
-// current chunk is summed, and the compiler barriers keep that shape.
-template <int D, bool SPLIT>
+// chains; the operands of the next RING - 1 4-feature chunks are in flight
+// while the current chunk is summed (with one chunk ahead instead of two the
+// 28x28 and 56x56 float32 workloads ran 1-3 % slower; the kernel held to
+// three wavefronts per SIMD keeps one, as two spilled more of its
+// registers), and the compiler barriers keep that shape.
+template <int D, bool SPLIT, int RING = 3>
 __device__ __forceinline__ void kernel_row(const float (&x)[D], const float* __restrict__ kl,
                                            const float* __restrict__ kg, int lb, float scale, float* __restrict__ tl,
                                            int rows, int col, bool valid, float* __restrict__ bout = nullptr,
@@ -77,17 +80,20 @@ __device__ __forceinline__ void kernel_row(const float (&x)[D], const float* __r
   int j = 0;
   for (; j + 4 <= lb; j += 4) {
     float sa[4] = {0.f, 0.f, 0.f, 0.f}, sb[4] = {0.f, 0.f, 0.f, 0.f};
-    float4 kv[2][4];
+    float4 kv[RING][4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      kv[0][u] = *reinterpret_cast<const float4*>((kSrc[u] == kLds ? kl : kg) + (j + u) * D);
+    for (int c0 = 0; c0 < RING - 1; ++c0)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        kv[c0][u] = *reinterpret_cast<const float4*>((kSrc[u] == kLds ? kl : kg) + (j + u) * D + 4 * c0);
 #pragma unroll
     for (int c = 0; c < D / 4; ++c) {
-      const int cur = c & 1;
-      if (c + 1 < D / 4) {
+      const int cur = c % RING;
+      if (c + RING - 1 < D / 4) {
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          kv[cur ^ 1][u] = *reinterpret_cast<const float4*>((kSrc[u] == kLds ? kl : kg) + (j + u) * D + 4 * (c + 1));
+          kv[(c + RING - 1) % RING][u] =
+              *reinterpret_cast<const float4*>((kSrc[u] == kLds ? kl : kg) + (j + u) * D + 4 * (c + RING - 1));
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -128,7 +134,7 @@ __device__ __forceinline__ void kernel_row(const float (&x)[D], const float* __r
 // both C and B of each tile; PART 1 only C (statistics and the C^T store),
 // PART 2 only B (the B V partial; its V operands are then issued after the B
 // rows, so they do not hold registers during them).
-template <typename T, int D, int LBB, int PART = 0>
+template <typename T, int D, int LBB, int PART = 0, int RING = 3>
 __device__ __forceinline__ void l1exp_body(const T* __restrict__ q, const T* __restrict__ k,
                                            const T* __restrict__ v, const float* __restrict__ kt,
                                            float* __restrict__ ct, float2* __restrict__ stats,
@@ -182,7 +188,7 @@ __device__ __forceinline__ void l1exp_body(const T* __restrict__ q, const T* __r
       issue_row<T, D>(q + row, valid, raw);
       widen_row<D>(raw, x);
       __syncthreads();  // tile buffer free (previous tile's MFMA reads done)
-      kernel_row<D, false>(x, kl, kg, lb, scale, tl, lbmax + 1, tid, valid);
+      kernel_row<D, false, RING>(x, kl, kg, lb, scale, tl, lbmax + 1, tid, valid);
       __syncthreads();
     }
     if constexpr (PART == 1) {
@@ -202,7 +208,7 @@ __device__ __forceinline__ void l1exp_body(const T* __restrict__ q, const T* __r
     // ---- B = k(K~, K), kept on chip ----
     widen_row<D>(raw, x);
     __syncthreads();  // statistics pass done with the tile buffer
-    kernel_row<D, true>(x, kl, kg, lb, scale, tl, lbmax + 1, tid, valid,
+    kernel_row<D, true, RING>(x, kl, kg, lb, scale, tl, lbmax + 1, tid, valid,
                         bt != nullptr ? bt + ((size_t)p * m + j0) * N + t0 + tid : nullptr, N);
     __syncthreads();
 
@@ -307,7 +313,7 @@ __global__ __launch_bounds__(kTT) __attribute__((amdgpu_waves_per_eu(3))) void l
   extern __shared__ __align__(16) float lds[];
   const int b = blockIdx.x;
   const int jb = b % jblocks, g = (b / jblocks) % groups, p = b / (jblocks * groups);
-  l1exp_body<T, D, LBB>(q, k, v, kt, ct, stats, bvpart, bt, N, ldc, m, lbmax, ntiles, tpg, groups, scale, jb, g, p,
+  l1exp_body<T, D, LBB, 0, 2>(q, k, v, kt, ct, stats, bvpart, bt, N, ldc, m, lbmax, ntiles, tpg, groups, scale, jb, g, p,
                         lds, kclk);
 }
 

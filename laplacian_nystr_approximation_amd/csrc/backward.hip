@@ -340,6 +340,20 @@ __device__ __forceinline__ void bwd_g_body(float* __restrict__ lds, const float*
     }
     __syncthreads();
     if (16 * w >= jv) continue;
+    // The epilogue's operands are loaded before the products, from clamped
+    // addresses (entries past m or past the tile are not stored), so their
+    // latency overlaps the MFMAs instead of following them one load at a time.
+    float cv[4][kGT / 16], rjv[4], mjv[4], ajv[4], bjv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int jc = min(j0 + 16 * w + 4 * lk + r, m - 1);
+      rjv[r] = rs[p * m + jc];
+      mjv[r] = mu[p * m + jc];
+      ajv[r] = ab[(size_t)p * 2 * m + jc];
+      bjv[r] = ab[(size_t)p * 2 * m + m + jc];
+#pragma unroll
+      for (int bj = 0; bj < kGT / 16; ++bj) cv[r][bj] = ct[((size_t)p * m + jc) * ldc + n0 + min(16 * bj + li, nv - 1)];
+    }
     f32x4 acc[kGT / 16];
 #pragma unroll
     for (int bj = 0; bj < kGT / 16; ++bj) acc[bj] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -355,15 +369,13 @@ __device__ __forceinline__ void bwd_g_body(float* __restrict__ lds, const float*
     for (int r = 0; r < 4; ++r) {
       const int j = j0 + 16 * w + 4 * lk + r;
       if (j >= m) continue;
-      const float rj = rs[p * m + j], mj = mu[p * m + j];
-      const float aj = ab[(size_t)p * 2 * m + j], bj2 = ab[(size_t)p * 2 * m + m + j];
 #pragma unroll
       for (int bj = 0; bj < kGT / 16; ++bj) {
         const int i = 16 * bj + li;
         if (i < nv) {
-          const float c = ct[((size_t)p * m + j) * ldc + n0 + i];
-          const float z = (c - mj) * rj;
-          const float dc = (acc[bj][r] - aj - z * bj2) * rj;
+          const float c = cv[r][bj];
+          const float z = (c - mjv[r]) * rjv[r];
+          const float dc = (acc[bj][r] - ajv[r] - z * bjv[r]) * rjv[r];
           gt[((size_t)p * m + j) * N + n0 + i] = dc * c;
         }
       }

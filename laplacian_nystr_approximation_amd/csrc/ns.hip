@@ -503,9 +503,9 @@ __global__ __launch_bounds__(256) void residual_kernel(const float* __restrict__
 // copies of W (symmetric), X, X^T and T^T.  X is double-buffered (two
 // wavefronts share a block row); X^T and T^T are rewritten only after every
 // wavefront has passed the barrier behind their last reads.
-template <int D, bool GAUSS>
+template <int D, bool GAUSS, int KEXT>
 __global__ __launch_bounds__(512) void ns_plain_kernel(const float* __restrict__ kt, float* __restrict__ w,
-                                                       float* __restrict__ x, int m, float scale, float eps, int kext,
+                                                       float* __restrict__ x, int m, float scale, float eps,
                                                        int iters) {
   constexpr int kS = 68;  // row stride (floats): 16-byte rows, quarter-waves on distinct banks
   constexpr int kN = 64 * kS;
@@ -517,7 +517,10 @@ __global__ __launch_bounds__(512) void ns_plain_kernel(const float* __restrict__
   const int p = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int li = lane & 15, lk = lane >> 4;
   const int br = wv >> 1, bc0 = 2 * (wv & 1);
-  const int S = kext / 4;
+  // The reduction extent is a compile-time constant, so each product's loop
+  // unrolls and its LDS reads are issued ahead of the MFMAs (with a runtime
+  // extent every four k-steps waited for their reads).
+  constexpr int S = KEXT / 4;
   f32x4* w4 = reinterpret_cast<f32x4*>(w + (size_t)p * 64 * 64);
   f32x4* x4 = reinterpret_cast<f32x4*>(x + (size_t)p * 64 * 64);
   {
@@ -606,6 +609,7 @@ __global__ __launch_bounds__(512) void ns_plain_kernel(const float* __restrict__
     // T = 2I - W X, stored transposed
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
     for (int c = 0; c < S; c += 4) {
       const f32x4 a = *reinterpret_cast<const f32x4*>(&ws[arow + c]);
       f32x4 b[2];
@@ -629,6 +633,7 @@ __global__ __launch_bounds__(512) void ns_plain_kernel(const float* __restrict__
     // X_next = X T
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
     for (int c = 0; c < S; c += 4) {
       const f32x4 a = *reinterpret_cast<const f32x4*>(&xc[arow + c]);
       f32x4 b[2];
@@ -680,13 +685,16 @@ hipError_t launch_ns(const Plan& pl, Work& wk, hipStream_t s, Span t) {
     // here.  kext (m rounded up to 32) is a multiple of 16, as the operand
     // reads need.
     if (pl.ns_in_launch) return hipErrorInvalidValue;
-    auto kern = pl.d == 64 ? (pl.gaussian ? ns_plain_kernel<64, true> : ns_plain_kernel<64, false>)
-                           : (pl.gaussian ? ns_plain_kernel<32, true> : ns_plain_kernel<32, false>);
+    auto pick = [&](auto k32, auto k64) { return kext > 32 ? k64 : k32; };
+    auto kern = pl.d == 64 ? (pl.gaussian ? pick(ns_plain_kernel<64, true, 32>, ns_plain_kernel<64, true, 64>)
+                                          : pick(ns_plain_kernel<64, false, 32>, ns_plain_kernel<64, false, 64>))
+                           : (pl.gaussian ? pick(ns_plain_kernel<32, true, 32>, ns_plain_kernel<32, true, 64>)
+                                          : pick(ns_plain_kernel<32, false, 32>, ns_plain_kernel<32, false, 64>));
     hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                          (int)kPlainLds);
     if (err != hipSuccess) return err;
     hipExtLaunchKernelGGL(kern, dim3(pl.P), dim3(512), kPlainLds, s, t.start, pl.refine ? nullptr : t.stop, 0, wk.kt,
-                          wk.w, wk.x, pl.m, pl.scale, pl.eps, kext, pl.ns_iters);
+                          wk.w, wk.x, pl.m, pl.scale, pl.eps, pl.ns_iters);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     wk.x_final = wk.x;

@@ -24,6 +24,7 @@
 // float64 residual lets it reach the float32 representation floor of W^-1
 // where the float32 products of the steps themselves stall above it.
 #include "lapnys_internal.hpp"
+#include "ns_small.hpp"
 
 namespace lapnys {
 
@@ -481,20 +482,17 @@ __global__ __launch_bounds__(256) void residual_kernel(const float* __restrict__
   }
 }
 
-// m <= 64, Gaussian form or the plain steps (LAPNYS_NS_PLAIN): W, alpha, X0
-// and the steps X <- X (2I - W X) of one problem per workgroup, with W and
+// m <= 64, the plain steps (LAPNYS_NS_PLAIN, the Laplacian kernel): W, alpha,
+// X0 and the steps X <- X (2I - W X) of one problem per workgroup, with W and
 // the iterates in LDS (64 x 64, zero padded).  W's entries are formed as in
-// wbuild_big_kernel (squared or absolute differences over even and odd
-// features, in increasing order, so W is bit-symmetric, and the diagonal is
-// 1 + eps) and written out; alpha = (max
-// column sum)^2 and X0 = W / alpha as in alpha_x0_kernel.  The steps take the
-// tiled steps' form: T = 2I - W X in full, then X T, float32 products on fp32
-// MFMA 16x16x4 over k in [0, kext).  (The in-LDS schedule of the Laplacian form keeps X
-// exactly symmetric by mirroring one triangle of X (W X); for an iterate that
-// is still far from converged after the fixed step count, as a Gaussian W
-// often leaves it, the mirrored rounding errors cost about 6x in the output's
-// agreement with the float64 iteration, and for a near-singular W they stall
-// or diverge the iteration, so this form keeps every entry.)
+// wbuild_big_kernel (absolute differences over even and odd features, in
+// increasing order, so W is bit-symmetric, and the diagonal is 1 + eps) and
+// written out; alpha = (max column sum)^2 and X0 = W / alpha as in
+// alpha_x0_kernel.  The steps take the tiled steps' form: T = 2I - W X in
+// full, then X T, float32 products on fp32 MFMA 16x16x4 over k in [0, kext):
+// the reference schedule the default one is compared with (the default forms
+// 2X - X (W X) inside the kernel-matrix launch and takes its early products
+// on bf16-split MFMA).
 //
 // Eight wavefronts: wavefront v forms block row v / 2 and column blocks
 // 2 (v % 2) + [0, 2) of each product.  The reduction index is permuted so
@@ -503,7 +501,7 @@ __global__ __launch_bounds__(256) void residual_kernel(const float* __restrict__
 // copies of W (symmetric), X, X^T and T^T.  X is double-buffered (two
 // wavefronts share a block row); X^T and T^T are rewritten only after every
 // wavefront has passed the barrier behind their last reads.
-template <int D, bool GAUSS, int KEXT>
+template <int D, int KEXT>
 __global__ __launch_bounds__(512) void ns_plain_kernel(const float* __restrict__ kt, float* __restrict__ w,
                                                        float* __restrict__ x, int m, float scale, float eps,
                                                        int iters) {
@@ -554,13 +552,8 @@ __global__ __launch_bounds__(512) void ns_plain_kernel(const float* __restrict__
 #pragma unroll
       for (int t = 0; t < D; t += 2) {
         const float e0 = tt[a * kS + t] - kb[t], e1 = tt[a * kS + t + 1] - kb[t + 1];
-        if constexpr (GAUSS) {
-          s0 = fmaf(e0, e0, s0);
-          s1 = fmaf(e1, e1, s1);
-        } else {
-          s0 += fabsf(e0);
-          s1 += fabsf(e1);
-        }
+        s0 += fabsf(e0);
+        s1 += fabsf(e1);
       }
       float val = 0.f;
       if (a < m && b < m) {
@@ -675,6 +668,31 @@ __global__ __launch_bounds__(256) void extract_square_kernel(const float* __rest
   dst[e] = src[(p * src_ld + a) * src_ld + b];
 }
 
+// The Gaussian kernel's solver for m <= 64: the Laplacian form's in-LDS
+// schedule (ns_small.hpp: each entry of W formed once per pair, the block
+// columns of X in registers, one barrier per step) with W from squared
+// differences and every step on float32 products, as a launch of its own
+// beside the kernel-matrix stage: one workgroup of 256 lanes per problem.
+template <int D, int KS>
+__global__ __launch_bounds__(256) void ns_gauss_kernel(const float* __restrict__ kt, float* __restrict__ w,
+                                                       float* __restrict__ x, int m, float scale, float eps,
+                                                       int iters) {
+  extern __shared__ __align__(16) float lds[];
+  ns_detail::ns_small<D, KS, true>(kt, w, x, m, scale, eps, iters, blockIdx.x, lds, nullptr);
+}
+
+// KS = ceil(m / 4), a compile-time constant of the schedule's loops.
+template <int D, int KS = 1>
+hipError_t launch_ns_gauss(const Plan& pl, Work& wk, hipStream_t s, Span t) {
+  if constexpr (KS < 16) {
+    if ((pl.m + 3) / 4 > KS) return launch_ns_gauss<D, KS + 1>(pl, wk, s, t);
+  }
+  hipExtLaunchKernelGGL((ns_gauss_kernel<D, KS>), dim3(pl.P), dim3(256), ns_detail::kNsLdsFloats * sizeof(float), s,
+                        t.start, pl.refine ? nullptr : t.stop, 0, wk.kt, wk.w, wk.x, pl.m, pl.scale, pl.eps,
+                        pl.ns_iters);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_ns(const Plan& pl, Work& wk, hipStream_t s, Span t) {
@@ -685,11 +703,15 @@ hipError_t launch_ns(const Plan& pl, Work& wk, hipStream_t s, Span t) {
     // here.  kext (m rounded up to 32) is a multiple of 16, as the operand
     // reads need.
     if (pl.ns_in_launch) return hipErrorInvalidValue;
+    if (pl.gaussian) {
+      hipError_t err = pl.d == 64 ? launch_ns_gauss<64>(pl, wk, s, t) : launch_ns_gauss<32>(pl, wk, s, t);
+      if (err != hipSuccess) return err;
+      wk.x_final = wk.x;
+      return pl.refine ? launch_refine(pl, wk, s, t.stop) : hipSuccess;
+    }
     auto pick = [&](auto k32, auto k64) { return kext > 32 ? k64 : k32; };
-    auto kern = pl.d == 64 ? (pl.gaussian ? pick(ns_plain_kernel<64, true, 32>, ns_plain_kernel<64, true, 64>)
-                                          : pick(ns_plain_kernel<64, false, 32>, ns_plain_kernel<64, false, 64>))
-                           : (pl.gaussian ? pick(ns_plain_kernel<32, true, 32>, ns_plain_kernel<32, true, 64>)
-                                          : pick(ns_plain_kernel<32, false, 32>, ns_plain_kernel<32, false, 64>));
+    auto kern = pl.d == 64 ? pick(ns_plain_kernel<64, 32>, ns_plain_kernel<64, 64>)
+                           : pick(ns_plain_kernel<32, 32>, ns_plain_kernel<32, 64>);
     hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                          (int)kPlainLds);
     if (err != hipSuccess) return err;

@@ -113,7 +113,7 @@ __device__ __forceinline__ float wave_max_nonneg(float x) {
 //
 // Problem p's W and X, for one workgroup of 256 lanes.  lds: kNsLdsFloats
 // floats, 16-byte aligned.
-template <int D, int KS>
+template <int D, int KS, bool GAUSS = false>
 __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __restrict__ wout,
                                          float* __restrict__ xout, int m, float scale, float eps, int iters, int p,
                                          float* __restrict__ lds, unsigned long long* __restrict__ clk) {
@@ -207,10 +207,19 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const float4 r = kv[c % 3][u];
-          s0[u] += fabsf(r.x - xb_[4 * c]);
-          s1[u] += fabsf(r.y - xb_[4 * c + 1]);
-          s0[u] += fabsf(r.z - xb_[4 * c + 2]);
-          s1[u] += fabsf(r.w - xb_[4 * c + 3]);
+          if constexpr (GAUSS) {
+            const float e0 = r.x - xb_[4 * c], e1 = r.y - xb_[4 * c + 1];
+            const float e2 = r.z - xb_[4 * c + 2], e3 = r.w - xb_[4 * c + 3];
+            s0[u] = fmaf(e0, e0, s0[u]);
+            s1[u] = fmaf(e1, e1, s1[u]);
+            s0[u] = fmaf(e2, e2, s0[u]);
+            s1[u] = fmaf(e3, e3, s1[u]);
+          } else {
+            s0[u] += fabsf(r.x - xb_[4 * c]);
+            s1[u] += fabsf(r.y - xb_[4 * c + 1]);
+            s0[u] += fabsf(r.z - xb_[4 * c + 2]);
+            s1[u] += fabsf(r.w - xb_[4 * c + 3]);
+          }
         }
         // The sums are in/out operands here, so the loads of a chunk stay
         // two chunks ahead of its arithmetic (bounded registers).
@@ -260,7 +269,10 @@ __device__ __forceinline__ void ns_small(const float* __restrict__ kt, float* __
   __syncthreads();
 
   const int li = lane & 15, lk = lane >> 4;
-  const int n16 = iters > kFp32Steps ? iters - kFp32Steps : 0;
+  // The Gaussian kernel's iterate is usually still far from converged after
+  // the given steps, where a split step's error is carried to the end: every
+  // step of that form takes float32 products.
+  const int n16 = !GAUSS && iters > kFp32Steps ? iters - kFp32Steps : 0;
   // Reduction index of the split steps' products: bf16 MFMA 16x16x32 kb takes
   // from lane group lk the eight k = 32 kb + 4 lk + r and 32 kb + 16 + 4 lk + r
   // (r < 4).  Those are the entries a lane holds of a block column in the

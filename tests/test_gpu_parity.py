@@ -136,6 +136,10 @@ def _refine_cases():
         # one step, then the correction: far from converged, so only parity
         Workload("ns1_12x12_m36_refine", B=1, H=2, grid_h=12, grid_w=12, d=64, pool=2, dtype="f32", ns_iters=1,
                  seed_index=42, refine=True),
+        # the Gaussian form's m <= 64 solver launch followed by the correction
+        # (d = 32, m = 36; parity only, as above)
+        Workload("gauss_ns1_12x12_m36_d32_refine", B=1, H=2, grid_h=12, grid_w=12, d=32, pool=2, dtype="f32",
+                 ns_iters=1, seed_index=54, refine=True, kernel="gaussian"),
     ]
 
 

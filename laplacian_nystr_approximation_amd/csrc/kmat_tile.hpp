@@ -117,46 +117,59 @@ struct VHalf<uint16_t, D> {
 };
 
 // Column statistics of the tile's C (float32 rows of stride kTP at tl) and
-// the C^T store.  Lane l takes tokens 4 l + [0, 4) of the tile: one 16-byte
-// LDS read and one 16-byte store of the C^T row per landmark.  Wavefront w
-// takes landmarks w, w + 4, ..., four of them at a time so that their
-// wavefront reductions overlap.  Tokens past N hold C = 0, so the sums need
-// no mask; the squared deviations do.  The C^T row stride is N rounded up to
-// 4, so a lane's 16-byte store past N stays in the row's padding.
+// the C^T store.
+//   * Statistics: L lanes per landmark (lane L j + q, j < lb; L = 4, 8 or 16
+//     as the block has more than 32, more than 16 or at most 16 landmarks),
+//     lane q summing its 256 / L tokens of row j as 16-byte LDS reads in token
+//     order; the partial sums merge pairwise by lane exchanges ((q0 + q1) +
+//     (q2 + q3) and so on), so all L lanes hold the same tile sum and mean, and
+//     the squared deviations about that mean go the same way.  No
+//     wavefront-wide reduction: the sixteen DPP steps per landmark pair those
+//     took were half of this pass.  Tokens past N hold C = 0, so the sums need
+//     no mask; the squared deviations do.
+//   * C^T: lane l stores tokens 4 l + [0, 4) of each of its wavefront's rows
+//     (w, w + 4, ...) with one 16-byte store.  The C^T row stride is N rounded
+//     up to 4, so a store past N stays in the row's padding.
 __device__ __forceinline__ void tile_stats_store(const float* __restrict__ tl, float2* __restrict__ stats,
                                                  float* __restrict__ ct, int p, int ntiles, int tile, int m, int j0,
                                                  int lb, int ldc, int t0, int nvalid, int lane, int w) {
   const bool full = nvalid == kTT;
   const float inv_n = 1.f / (float)nvalid;  // 1/256 exactly for a full tile
-  for (int jq = w; jq < lb; jq += 4 * kNW) {
-    float4 vals[4];
-    float s[4], m2[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int jj = min(jq + kNW * u, lb - 1);  // rows past lb: read, not stored
-      vals[u] = *reinterpret_cast<const float4*>(tl + jj * kTP + 4 * lane);
-      s[u] = (vals[u].x + vals[u].y) + (vals[u].z + vals[u].w);
+  {
+    // L lanes per landmark (4 up to 64 landmarks, 8 up to 32, 16 up to 16),
+    // so every wavefront takes part however few landmarks the block has;
+    // lane q of landmark j sums tokens SEG q + [0, SEG), SEG = 256 / L.
+    const int lsh = lb > 32 ? 2 : (lb > 16 ? 3 : 4), L = 1 << lsh, seg = kTT >> lsh;
+    const int tid = 64 * w + lane, j = tid >> lsh, q = tid & (L - 1);
+    const float* row = tl + min(j, lb - 1) * kTP + seg * q;  // rows past lb: read, not stored
+    // The row segment is read twice (sum, then deviations) rather than held:
+    // the pass runs beside the next row's loads in flight.
+    float s = 0.f;
+#pragma unroll 4
+    for (int i = 0; i < seg / 4; ++i) {
+      const float4 v = *reinterpret_cast<const float4*>(row + 4 * i);
+      s += (v.x + v.y) + (v.z + v.w);
     }
-    wave_sum_dpp_n<4>(s);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float mean = s[u] * inv_n;
-      float d[4] = {vals[u].x - mean, vals[u].y - mean, vals[u].z - mean, vals[u].w - mean};
+    for (int off = 1; off < L; off <<= 1) s += __shfl_xor(s, off, 64);
+    const float mean = s * inv_n;
+    float m2 = 0.f;
+#pragma unroll 4
+    for (int i = 0; i < seg / 4; ++i) {
+      const float4 v = *reinterpret_cast<const float4*>(row + 4 * i);
+      float d[4] = {v.x - mean, v.y - mean, v.z - mean, v.w - mean};
       if (!full) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) d[i] = (4 * lane + i < nvalid) ? d[i] : 0.f;
+        for (int e = 0; e < 4; ++e) d[e] = (seg * q + 4 * i + e < nvalid) ? d[e] : 0.f;
       }
-      m2[u] = (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
+      m2 += (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
     }
-    wave_sum_dpp_n<4>(m2);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = jq + kNW * u;
-      if (j < lb) {
-        if (lane == 0) stats[((size_t)p * ntiles + tile) * m + j0 + j] = make_float2(s[u], m2[u]);
-        float* crow = ct + ((size_t)p * m + j0 + j) * ldc + t0;
-        if (4 * lane < nvalid) *reinterpret_cast<float4*>(crow + 4 * lane) = vals[u];
-      }
+    for (int off = 1; off < L; off <<= 1) m2 += __shfl_xor(m2, off, 64);
+    if (q == 0 && j < lb) stats[((size_t)p * ntiles + tile) * m + j0 + j] = make_float2(s, m2);
+  }
+  if (4 * lane < nvalid) {
+    for (int j = w; j < lb; j += kNW) {
+      const float4 c4 = *reinterpret_cast<const float4*>(tl + j * kTP + 4 * lane);
+      *reinterpret_cast<float4*>(ct + ((size_t)p * m + j0 + j) * ldc + t0 + 4 * lane) = c4;
     }
   }
 }

@@ -233,7 +233,7 @@ __device__ __forceinline__ void l1exp_body(const T* __restrict__ q, const T* __r
 // the kernel-matrix ones numbered landmark block fastest, then tile group,
 // then problem.
 // Dynamic LDS: the larger of the two parts' needs, 16-byte aligned.  The
-// union of both parts takes 202 registers at d = 64: two wavefronts per SIMD
+// union of both parts takes 212 registers at d = 64: two wavefronts per SIMD
 // (the L1 loop needs at least two to dual-issue).
 template <typename T, int D, int LBB, int KS>
 __global__ __launch_bounds__(kTT) void l1exp_kernel(

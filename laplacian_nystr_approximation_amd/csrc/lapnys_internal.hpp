@@ -35,34 +35,6 @@ __device__ __forceinline__ void split2(float z0, float z1, uint32_t& hi, uint32_
 __device__ __forceinline__ float widen(float x) { return x; }
 __device__ __forceinline__ float widen(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// Sums over the 64 lanes of a wavefront of U independent values at once,
-// each returned to every lane (as a wave-uniform value).  Within each 16-lane
-// row, DPP row rotations by 8, 4, 2 and 1 leave the row sum in every lane;
-// then row_bcast:15 adds row 0's sum into row 1 and row 2's into row 3, and
-// row_bcast:31 adds lane 31's (rows 0 + 1) into row 3, so lane 63 holds
-// (r3 + r2) + (r1 + r0), read once.  VALU only, no LDS round trip; the steps
-// of the U values are interleaved so their latencies overlap, and the order
-// is fixed, so results repeat bit for bit.
-template <int U>
-__device__ __forceinline__ void wave_sum_dpp_n(float (&x)[U]) {
-#pragma unroll
-  for (int u = 0; u < U; ++u) x[u] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x[u]), 0x128, 0xf, 0xf, false));
-#pragma unroll
-  for (int u = 0; u < U; ++u) x[u] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x[u]), 0x124, 0xf, 0xf, false));
-#pragma unroll
-  for (int u = 0; u < U; ++u) x[u] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x[u]), 0x122, 0xf, 0xf, false));
-#pragma unroll
-  for (int u = 0; u < U; ++u) x[u] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x[u]), 0x121, 0xf, 0xf, false));
-#pragma unroll
-  for (int u = 0; u < U; ++u)  // row_bcast:15 into rows 1 and 3
-    x[u] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x[u]), 0x142, 0xa, 0xf, false));
-#pragma unroll
-  for (int u = 0; u < U; ++u)  // row_bcast:31 into rows 2 and 3
-    x[u] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x[u]), 0x143, 0xc, 0xf, false));
-#pragma unroll
-  for (int u = 0; u < U; ++u) x[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[u]), 63));
-}
-
 // Landmark block handled by one workgroup of the fused kernel-matrix stage.
 constexpr int kLandmarkBlock = 64;
 // Largest landmark count the fused single-workgroup Newton-Schulz handles.

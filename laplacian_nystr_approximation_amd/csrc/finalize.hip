@@ -127,19 +127,26 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float2* __restrict__ 
 // problem p's B V in group order, forms the same columns of Y = X (B V) (X
 // zero padded to 64 x 64, rows of B V past m zero) on fp32 MFMA 16x16x4, and
 // stores them into Y^T high and low parts; workgroup c = D / 16 merges the
-// statistics, beside them.
+// statistics, beside them.  Workgroups are handed to the XCDs in turn by
+// index, and each XCD has its own L2: the index b = (p / 8) 8 (D / 16 + 1) +
+// 8 c + p % 8 keeps all of a problem's workgroups on one XCD, so X and the
+// B V partials come from HBM once per problem instead of once per slice
+// (at 320 problems the launch took 9.4 us with the slices on four XCDs).
+// Problems past P (the grid rounds P up to a multiple of 8) exit at once.
 template <int D>
 __global__ __launch_bounds__(256) void finalize_fused_kernel(const float2* __restrict__ stats,
                                                              const float* __restrict__ bvpart,
                                                              const float* __restrict__ x, float* __restrict__ bv,
                                                              float* __restrict__ mu, float* __restrict__ sigma,
                                                              float* __restrict__ rs, __bf16* __restrict__ yt, int N,
-                                                             int m, int ntiles, int tt, int groups, int whiten) {
+                                                             int m, int ntiles, int tt, int groups, int whiten, int P) {
   constexpr int DB = D / 16;
   constexpr int kXS = 68;  // X row stride in LDS: the A-operand column reads hit distinct banks
   __shared__ __align__(16) float xs[64 * kXS];
   __shared__ __align__(16) float bs[64 * 16];  // the B V column slice, [landmark][16]
-  const int c = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int p = (b / (8 * (DB + 1))) * 8 + b % 8, c = (b / 8) % (DB + 1);
+  if (p >= P) return;
   if (c == DB) {
     column_stats(stats, mu, sigma, rs, N, m, ntiles, tt, whiten, p, tid);
     return;
@@ -206,9 +213,10 @@ __global__ __launch_bounds__(256) void finalize_fused_kernel(const float2* __res
 hipError_t launch_reduce(const Plan& pl, const Work& w, hipStream_t s, Span t) {
   if (pl.fused_ns) {
     auto kern = pl.d == 64 ? finalize_fused_kernel<64> : finalize_fused_kernel<32>;
-    hipExtLaunchKernelGGL(kern, dim3(pl.d / 16 + 1, pl.P), dim3(256), 0, s, t.start, t.stop, 0,
+    const int grid = (pl.P + 7) / 8 * 8 * (pl.d / 16 + 1);
+    hipExtLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, t.start, t.stop, 0,
                           reinterpret_cast<const float2*>(w.stats), w.bvpart, w.x_final, w.bv, w.mu, w.sigma, w.rs,
-                          w.yt, pl.N, pl.m, pl.ntiles, pl.tt, pl.groups, pl.whiten ? 1 : 0);
+                          w.yt, pl.N, pl.m, pl.ntiles, pl.tt, pl.groups, pl.whiten ? 1 : 0, pl.P);
     return hipGetLastError();
   }
   const int nbv = (pl.m * pl.d + 255) / 256;

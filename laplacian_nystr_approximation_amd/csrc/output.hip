@@ -24,6 +24,14 @@
 //    A lane thus ends up holding D/16 consecutive features of each of its
 //    tokens and writes them with one 16-byte (D = 64) or 8-byte (D = 32)
 //    streaming store.
+//  * Workgroups go to the eight XCDs in turn by index, each XCD with its own
+//    L2.  For m <= 64 with P a multiple of 8 the workgroup index b =
+//    (p / 8) 8 T + 8 tile + p % 8 (T tiles per problem) keeps all of a
+//    problem's tiles on one XCD, so Y^T and the column statistics come from
+//    HBM once per problem (the 56x56 workload's stage: 9.2 -> 8.8 us).
+//    Otherwise tiles are numbered problem-major (b = p T + tile): at m = 256
+//    with 8 problems of 256 tiles the grouping put each problem's whole C
+//    stream behind one XCD and was slower (139 -> 144 us).
 #include "lapnys_internal.hpp"
 
 namespace lapnys {
@@ -47,14 +55,16 @@ template <int D, bool FUSED_Y>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void output_kernel(const float* __restrict__ ct, int ldc,
                                                      const __bf16* __restrict__ yt, const float* __restrict__ y,
                                                      const float* __restrict__ mu, const float* __restrict__ rs,
-                                                     float* __restrict__ out, int N, int m) {
+                                                     float* __restrict__ out, int N, int m, int xcd_group) {
   constexpr int DB = D / 16;
   extern __shared__ __align__(16) float lds[];
   const int rl = FUSED_Y ? 64 : (m + 63) & ~63;  // landmarks per Y^T row; rows past m are zero
   __bf16* yth = reinterpret_cast<__bf16*>(lds);  // [D][rl] high parts
   __bf16* ytl = yth + D * rl;                    // [D][rl] low parts
   float2* mrs = reinterpret_cast<float2*>(ytl + D * rl);  // [rl]: (mu, 1/sigma), zero past m
-  const int tile = blockIdx.x, p = blockIdx.y;
+  const int nt = (N + 255) / 256, b = blockIdx.x;
+  const int tile = xcd_group ? (b / 8) % nt : b % nt;
+  const int p = xcd_group ? (b / (8 * nt)) * 8 + b % 8 : b / nt;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int li = lane & 15, lk = lane >> 4;
   const int tb = tile * 256 + 64 * w;  // first token of this wavefront
@@ -218,8 +228,11 @@ hipError_t launch_typed(const Plan& pl, const Work& wk, float* out, hipStream_t 
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
   }
-  hipExtLaunchKernelGGL(kern, dim3((pl.N + 255) / 256, pl.P), dim3(256), shmem, s, t.start, t.stop, 0, wk.ct, pl.ldc,
-                        wk.yt, wk.y, wk.mu, wk.rs, out, pl.N, pl.m);
+  const int xcd_group = FUSED_Y && pl.P % 8 == 0 ? 1 : 0;
+  const long long grid = (long long)((pl.N + 255) / 256) * pl.P;
+  if (grid * 256 > 0xffffffffLL) return hipErrorInvalidConfiguration;  // one grid axis of 2^32 lanes
+  hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), shmem, s, t.start, t.stop, 0, wk.ct, pl.ldc,
+                        wk.yt, wk.y, wk.mu, wk.rs, out, pl.N, pl.m, xcd_group);
   return hipGetLastError();
 }
 
